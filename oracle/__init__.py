@@ -1,0 +1,201 @@
+"""CPU oracle for the tiered KV-cache hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  It wraps ``liboracle.so`` (plain C, fp64, memcpy loops, brute-force top-k, built
+from ``kvt_oracle.c`` by ``oracle/build.py``) with numpy-in / numpy-out functions.  It shares no
+code with the HIP library in ``hbm_kv_cache_amd``.
+
+Functions and the passages they follow:
+
+* ``sub_block_ptrs``   -- vLLM CPU offloading worker, ``compute_sub_block_ptrs``.
+* ``swap``             -- vLLM CPU offloading worker, ``transfer_async`` / ``swap_blocks_batch``.
+* ``index_scores``, ``topk`` -- QSA KV offload for ExLlamaV3, ``CacheLayer_qsa_offload``
+  docstring (pooled plane scored in full every step, top-k selection).
+* ``gather``           -- QSA KV offload, ``sparse_attend`` (selected K/V rows from host planes).
+* ``stage_tail``       -- llama.cpp PR #319 commit text (used host rows copied to a VRAM buffer).
+* ``attn_decode``      -- QSA KV offload, staged attention (GQA map, softmax normalisation).
+* ``attn_prefill``     -- llama.cpp PR #319 (VRAM head + host tail, same output as all-device).
+
+Every function here has at least one pin in ``tests/test_oracle.py`` that does not restate its
+formula (library routines, closed forms, invariants, worked values).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_double, c_int, c_int32, c_int64, c_uint64, c_void_p
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F16, BF16, Q8_0 = 1, 2, 3
+OK, EINVAL, ERANGE, EOVERLAP = 0, -1, -2, -4
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = c_void_p
+        sig = {
+            "orc_f16_to_f64": (c_double, [ctypes.c_uint16]),
+            "orc_bf16_to_f64": (c_double, [ctypes.c_uint16]),
+            "orc_sub_block_ptrs": (c_int, [c_uint64, c_uint64, c_uint64, P, c_int64, c_int32,
+                                           c_int32, P, c_int64]),
+            "orc_chunks_consumed": (c_int64, [c_int64, c_int32, c_int32]),
+            "orc_check_disjoint": (c_int, [P, P, P, c_int64]),
+            "orc_swap": (c_int, [P, P, P, c_int64, c_int]),
+            "orc_index_scores": (c_int, [P, c_int64, c_int32, P, c_int32, P, c_int]),
+            "orc_topk": (c_int, [P, c_int32, c_int64, c_int32, P]),
+            "orc_gather": (c_int, [P, P, c_int64, c_int32, c_int32, c_int32, c_int64, P, c_int32,
+                                   P, c_int32, P, P]),
+            "orc_stage_tail": (c_int, [P, c_int64, c_int64, c_int64, P]),
+            "orc_attn_decode": (c_int, [P, c_int32, c_int32, c_int32, c_int32, P, P, c_int64, P,
+                                        c_double, P, c_int]),
+            "orc_attn_prefill": (c_int, [P, c_int64, c_int64, c_int32, c_int32, c_int32, P, P,
+                                         c_int64, P, P, c_int64, c_int32, c_int32, c_double,
+                                         c_int64, c_int64, P, c_int]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _threads(n):
+    return int(n) if n else (os.cpu_count() or 1)
+
+
+class OracleError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} returned {code}")
+        self.code = code
+
+
+def _check(fn, rc):
+    if rc != OK:
+        raise OracleError(fn, rc)
+
+
+def f16_to_f64(u16: int) -> float:
+    return _load().orc_f16_to_f64(int(u16))
+
+
+def bf16_to_f64(u16: int) -> float:
+    return _load().orc_bf16_to_f64(int(u16))
+
+
+def sub_block_ptrs(base, row_stride, page_bytes, block_ids, bpc, skip, n_out):
+    ids = np.ascontiguousarray(block_ids, dtype=np.int64)
+    out = np.zeros(n_out, dtype=np.uint64)
+    rc = _load().orc_sub_block_ptrs(int(base), int(row_stride), int(page_bytes), _ptr(ids),
+                                    ids.size, int(bpc), int(skip), _ptr(out), int(n_out))
+    _check("orc_sub_block_ptrs", rc)
+    return out
+
+
+def chunks_consumed(n, skip, bpc):
+    return int(_load().orc_chunks_consumed(int(n), int(skip), int(bpc)))
+
+
+def check_disjoint(src, dst, sizes):
+    src, dst, sizes = (np.ascontiguousarray(x, dtype=np.uint64) for x in (src, dst, sizes))
+    return int(_load().orc_check_disjoint(_ptr(src), _ptr(dst), _ptr(sizes), src.size))
+
+
+def swap(src, dst, sizes, threads=1):
+    """memcpy(dst[i], src[i], sizes[i]) on raw host addresses."""
+    src, dst, sizes = (np.ascontiguousarray(x, dtype=np.uint64) for x in (src, dst, sizes))
+    _check("orc_swap", _load().orc_swap(_ptr(src), _ptr(dst), _ptr(sizes), src.size,
+                                        _threads(threads)))
+
+
+def index_scores(pooled_u16, q_u16, threads=0):
+    """pooled: uint16 fp16 bits [n_blocks][d]; q: uint16 fp16 bits [n_sel][d] -> f64 [n_sel][n_blocks]."""
+    pooled = np.ascontiguousarray(pooled_u16, dtype=np.uint16)
+    q = np.ascontiguousarray(q_u16, dtype=np.uint16)
+    n_blocks, d = pooled.shape
+    n_sel = q.shape[0]
+    assert q.shape[1] == d
+    out = np.empty((n_sel, n_blocks), dtype=np.float64)
+    _check("orc_index_scores", _load().orc_index_scores(_ptr(pooled), n_blocks, d, _ptr(q), n_sel,
+                                                        _ptr(out), _threads(threads)))
+    return out
+
+
+def topk(scores, k):
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    n_sel, n_blocks = s.shape
+    ids = np.empty((n_sel, k), dtype=np.int32)
+    _check("orc_topk", _load().orc_topk(_ptr(s), n_sel, n_blocks, int(k), _ptr(ids)))
+    return ids
+
+
+def gather(k_plane, v_plane, n_tok, kvh, hd, elem_bytes, row_stride, ids, block_tokens,
+           block_table=None, k_out=None, v_out=None):
+    """Planes: uint8 arrays addressed as token*row_stride + head*hd*elem_bytes."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    kk = ids.shape[1]
+    shape = (kvh, kk * block_tokens, hd * elem_bytes)
+    if k_out is None:
+        k_out = np.zeros(shape, dtype=np.uint8)
+    if v_out is None:
+        v_out = np.zeros(shape, dtype=np.uint8)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    _check("orc_gather", _load().orc_gather(_ptr(k_plane), _ptr(v_plane), int(n_tok), kvh, hd,
+                                            elem_bytes, int(row_stride), _ptr(bt),
+                                            int(block_tokens), _ptr(ids), kk, _ptr(k_out),
+                                            _ptr(v_out)))
+    return k_out, v_out
+
+
+def stage_tail(plane, row_bytes, row_begin, row_end, staging=None):
+    if staging is None:
+        staging = np.empty((row_end - row_begin) * row_bytes, dtype=np.uint8)
+    _check("orc_stage_tail", _load().orc_stage_tail(_ptr(plane), int(row_bytes), int(row_begin),
+                                                    int(row_end), _ptr(staging)))
+    return staging
+
+
+def attn_decode(q_u16, k_u16, v_u16, fmt, scale, n_valid=None, threads=0):
+    """q: [n_qh][hd] bits; k, v: [kvh][n_kv][hd] bits (fp16 or bf16) -> f64 [n_qh][hd]."""
+    q = np.ascontiguousarray(q_u16, dtype=np.uint16)
+    k = np.ascontiguousarray(k_u16, dtype=np.uint16)
+    v = np.ascontiguousarray(v_u16, dtype=np.uint16)
+    n_qh, hd = q.shape
+    kvh, n_kv, hd2 = k.shape
+    assert hd2 == hd and v.shape == k.shape
+    nv = None if n_valid is None else np.ascontiguousarray(n_valid, dtype=np.int32)
+    out = np.empty((n_qh, hd), dtype=np.float64)
+    _check("orc_attn_decode", _load().orc_attn_decode(_ptr(q), n_qh, kvh, hd, int(fmt), _ptr(k),
+                                                      _ptr(v), n_kv, _ptr(nv), float(scale),
+                                                      _ptr(out), _threads(threads)))
+    return out
+
+
+def attn_prefill(q_u16, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, fmt, causal,
+                 scale, t_begin=0, t_end=None, threads=0):
+    """q: [n_q][n_qh][hd] fp16 bits; K/V head and tail: uint8 row arrays -> f64 [rows][n_qh][hd]."""
+    q = np.ascontiguousarray(q_u16, dtype=np.uint16)
+    n_q, n_qh, hd = q.shape
+    if t_end is None:
+        t_end = n_q
+    out = np.empty((t_end - t_begin, n_qh, hd), dtype=np.float64)
+    _check("orc_attn_prefill", _load().orc_attn_prefill(
+        _ptr(q), n_q, int(q_pos0), n_qh, kvh, hd, _ptr(k_head), _ptr(v_head), int(n_head),
+        _ptr(k_tail), _ptr(v_tail), int(n_kv), int(fmt), int(bool(causal)), float(scale),
+        int(t_begin), int(t_end), _ptr(out), _threads(threads)))
+    return out
