@@ -1,0 +1,249 @@
+// kvt_copy.hip -- S2 batched block swap and S7 tail staging.
+//
+// vLLM-CPU transfer_async hands a swap function three u64 tables (src, dst, size) and picks
+// either the copy engines or a GPU kernel that dereferences host pointers.  Here:
+//   * KERNEL: each wavefront owns one 8 KiB chunk of one descriptor.  It reads the descriptor,
+//     issues all of its 16-byte loads (up to 8 per lane, 8 KiB in flight per wave) and then
+//     its stores, so thousands of waves keep the host link saturated.  Descriptors whose
+//     addresses are only 8-byte aligned take an 8-byte path, anything else a byte path.
+//   * SDMA: the copy engines, through hipMemcpyBatchAsync (one submission for the batch),
+//     falling back to one hipMemcpyAsync per descriptor where the batch call is unavailable.
+// kvt_stage_tail (llama-T tail staging) is one contiguous range: a single SDMA copy or the
+// same wide-load kernel over one span.
+#include <dlfcn.h>
+
+#include <algorithm>
+#include <atomic>
+
+#include "kvt_internal.h"
+
+namespace {
+
+constexpr int kChunk = 8192;                      // bytes per wave unit
+constexpr int kWavesPerBlock = 4;                 // 256-thread workgroups
+constexpr int kWordsPerLane16 = kChunk / 16 / kvt::kWave;  // 8
+constexpr int kWordsPerLane8 = kChunk / 8 / kvt::kWave;    // 16
+
+// One wave copies bytes [off, off+len) of a single range.  off + len <= range size.
+__device__ __forceinline__ void wave_copy_chunk(uint64_t s, uint64_t d, uint64_t len, int lane)
+{
+    if (((s | d) & 15) == 0) {
+        const u32x4 *sp = reinterpret_cast<const u32x4 *>(s);
+        u32x4 *dp = reinterpret_cast<u32x4 *>(d);
+        const uint32_t nw = (uint32_t)(len >> 4);
+        u32x4 r[kWordsPerLane16];
+#pragma unroll
+        for (int k = 0; k < kWordsPerLane16; k++) {
+            uint32_t w = lane + k * kvt::kWave;
+            if (w < nw)
+                r[k] = __builtin_nontemporal_load(sp + w);
+        }
+#pragma unroll
+        for (int k = 0; k < kWordsPerLane16; k++) {
+            uint32_t w = lane + k * kvt::kWave;
+            if (w < nw)
+                dp[w] = r[k];
+        }
+        uint64_t done = (uint64_t)nw << 4;
+        if (done < len && lane < (int)(len - done)) {  // < 16 trailing bytes
+            reinterpret_cast<uint8_t *>(d)[done + lane] =
+                reinterpret_cast<const uint8_t *>(s)[done + lane];
+        }
+    } else if (((s | d) & 7) == 0) {
+        const u32x2 *sp = reinterpret_cast<const u32x2 *>(s);
+        u32x2 *dp = reinterpret_cast<u32x2 *>(d);
+        const uint32_t nw = (uint32_t)(len >> 3);
+        u32x2 r[kWordsPerLane8];
+#pragma unroll
+        for (int k = 0; k < kWordsPerLane8; k++) {
+            uint32_t w = lane + k * kvt::kWave;
+            if (w < nw)
+                r[k] = __builtin_nontemporal_load(sp + w);
+        }
+#pragma unroll
+        for (int k = 0; k < kWordsPerLane8; k++) {
+            uint32_t w = lane + k * kvt::kWave;
+            if (w < nw)
+                dp[w] = r[k];
+        }
+        uint64_t done = (uint64_t)nw << 3;
+        if (done < len && lane < (int)(len - done)) {
+            reinterpret_cast<uint8_t *>(d)[done + lane] =
+                reinterpret_cast<const uint8_t *>(s)[done + lane];
+        }
+    } else {
+        const uint8_t *sp = reinterpret_cast<const uint8_t *>(s);
+        uint8_t *dp = reinterpret_cast<uint8_t *>(d);
+        for (uint64_t b = lane; b < len; b += kvt::kWave)
+            dp[b] = sp[b];
+    }
+}
+
+// unit u = (descriptor i, chunk c) with u = i*chunks + c; one wave per unit
+__global__ __launch_bounds__(256) void copy_desc_kernel(const uint64_t *__restrict__ src,
+                                                        const uint64_t *__restrict__ dst,
+                                                        const uint64_t *__restrict__ sizes,
+                                                        int64_t n_units, uint32_t chunks)
+{
+    const int lane = threadIdx.x & (kvt::kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (u >= n_units)
+        return;
+    const int64_t i = u / chunks;
+    const uint64_t off = (uint64_t)(u - i * chunks) * kChunk;
+    const uint64_t sz = sizes[i];
+    if (off >= sz)
+        return;
+    const uint64_t len = sz - off < (uint64_t)kChunk ? sz - off : (uint64_t)kChunk;
+    wave_copy_chunk(src[i] + off, dst[i] + off, len, lane);
+}
+
+// one contiguous range, one wave per 8 KiB chunk
+__global__ __launch_bounds__(256) void copy_span_kernel(uint64_t src, uint64_t dst, uint64_t bytes)
+{
+    const int lane = threadIdx.x & (kvt::kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t off = ((uint64_t)blockIdx.x * kWavesPerBlock + wave) * kChunk;
+    if (off >= bytes)
+        return;
+    const uint64_t len = bytes - off < (uint64_t)kChunk ? bytes - off : (uint64_t)kChunk;
+    wave_copy_chunk(src + off, dst + off, len, lane);
+}
+
+// AUTO policy: kernel for pages below the threshold (vLLM-CPU _select_swap_blocks_fn keeps the
+// kernel for small 8-byte-multiple pages and the copy engines otherwise).  Defaults are the
+// crossover measured on MI355X by the small-page sweep; stores default to the copy engines.
+std::atomic<uint64_t> g_threshold[2] = {{1u << 20}, {0}};
+
+// hipMemcpyBatchAsync is resolved at run time from the HIP runtime already in the process (the
+// one that owns the caller's streams); runtimes that predate it get per-copy submission.
+typedef hipError_t (*batch_fn_t)(void **, void **, size_t *, size_t, hipMemcpyAttributes *,
+                                 size_t *, size_t, size_t *, hipStream_t);
+std::atomic<int> g_batch_state{0};  // 0 unknown, 1 usable, 2 unavailable
+std::atomic<batch_fn_t> g_batch_fn{nullptr};
+
+batch_fn_t batch_fn()
+{
+    int st = g_batch_state.load();
+    if (st == 0) {
+        void *h = dlopen("libamdhip64.so.7", RTLD_LAZY | RTLD_NOLOAD);
+        void *f = h ? dlsym(h, "hipMemcpyBatchAsync") : nullptr;
+        g_batch_fn.store(reinterpret_cast<batch_fn_t>(f));
+        st = f ? 1 : 2;
+        g_batch_state.store(st);
+    }
+    return st == 1 ? g_batch_fn.load() : nullptr;
+}
+
+int sdma_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
+                hipStream_t s)
+{
+    if (batch_fn_t f = batch_fn()) {
+        size_t fail_idx = 0;
+        hipError_t e = f(reinterpret_cast<void **>(const_cast<uint64_t *>(dst)),
+                         reinterpret_cast<void **>(const_cast<uint64_t *>(src)),
+                         reinterpret_cast<size_t *>(const_cast<uint64_t *>(sizes)), (size_t)n,
+                         nullptr, nullptr, 0, &fail_idx, s);
+        if (e == hipSuccess)
+            return KVT_OK;
+        (void)hipGetLastError();
+        if (e != hipErrorNotSupported && e != hipErrorInvalidValue)
+            return kvt::fail(KVT_EHIP, "hipMemcpyBatchAsync failed at %zu: %s", fail_idx,
+                             hipGetErrorString(e));
+        g_batch_state.store(2);  // refuses this form: per-copy submission from now on
+    }
+    for (int64_t i = 0; i < n; i++) {
+        if (!sizes[i])
+            continue;
+        KVT_HIP(hipMemcpyAsync(reinterpret_cast<void *>(dst[i]),
+                               reinterpret_cast<const void *>(src[i]), sizes[i],
+                               hipMemcpyDefault, s));
+    }
+    return KVT_OK;
+}
+
+}  // namespace
+
+extern "C" uint64_t kvt_set_copy_threshold(int32_t dir, uint64_t bytes)
+{
+    if (dir != KVT_H2D && dir != KVT_D2H)
+        return 0;
+    return g_threshold[dir].exchange(bytes);
+}
+
+// S2: vLLM-CPU transfer_async -> swap_blocks_batch(src, dst, sizes).
+extern "C" int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
+                               int64_t n, int32_t dir, int32_t mode, void *stream)
+{
+    if (n < 0 || (n && (!src || !dst || !sizes)))
+        return kvt::fail(KVT_EINVAL, "kvt_swap_blocks: n=%lld with null tables", (long long)n);
+    if (dir != KVT_H2D && dir != KVT_D2H)
+        return kvt::fail(KVT_EINVAL, "kvt_swap_blocks: dir=%d", dir);
+    if (mode != KVT_COPY_AUTO && mode != KVT_COPY_KERNEL && mode != KVT_COPY_SDMA)
+        return kvt::fail(KVT_EINVAL, "kvt_swap_blocks: mode=%d", mode);
+    if (n == 0)
+        return KVT_OK;
+    hipStream_t s = kvt::as_stream(stream);
+
+    uint64_t max_size = 0, or_size = 0;
+    for (int64_t i = 0; i < n; i++) {
+        max_size = std::max(max_size, sizes[i]);
+        or_size |= sizes[i];
+    }
+    if (max_size == 0)
+        return KVT_OK;
+    const bool kernel_ok = (or_size & 7) == 0;
+    if (mode == KVT_COPY_KERNEL && !kernel_ok)
+        return kvt::fail(KVT_EALIGN, "kvt_swap_blocks: kernel path needs sizes %% 8 == 0");
+    bool use_kernel = mode == KVT_COPY_KERNEL ||
+                      (mode == KVT_COPY_AUTO && kernel_ok && max_size < g_threshold[dir].load());
+    if (!use_kernel)
+        return sdma_copies(src, dst, sizes, n, s);
+
+    const uint64_t chunks = (max_size + kChunk - 1) / kChunk;
+    if (chunks > 0xffffffffull)
+        return kvt::fail(KVT_ERANGE, "kvt_swap_blocks: page of %llu bytes too large",
+                         (unsigned long long)max_size);
+    const int64_t units = n * (int64_t)chunks;
+    const int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks > 0x7fffffff)
+        return kvt::fail(KVT_ERANGE, "kvt_swap_blocks: %lld wave units exceed one launch",
+                         (long long)units);
+    hipLaunchKernelGGL(copy_desc_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst,
+                       sizes, units, (uint32_t)chunks);
+    KVT_LAUNCHED("copy_desc_kernel");
+    return KVT_OK;
+}
+
+// S7: llama-T tail staging -- rows [row_begin, row_end) of a host-resident plane into HBM.
+extern "C" int kvt_stage_tail(const void *plane, int64_t row_bytes, int64_t row_begin,
+                              int64_t row_end, void *staging, int32_t mode, void *stream)
+{
+    if (row_bytes < 1 || row_begin < 0 || row_end < row_begin)
+        return kvt::fail(KVT_EINVAL, "kvt_stage_tail: row_bytes=%lld rows [%lld, %lld)",
+                         (long long)row_bytes, (long long)row_begin, (long long)row_end);
+    if (mode != KVT_COPY_AUTO && mode != KVT_COPY_KERNEL && mode != KVT_COPY_SDMA)
+        return kvt::fail(KVT_EINVAL, "kvt_stage_tail: mode=%d", mode);
+    const uint64_t bytes = (uint64_t)(row_end - row_begin) * (uint64_t)row_bytes;
+    if (!bytes)
+        return KVT_OK;
+    if (!plane || !staging)
+        return kvt::fail(KVT_EINVAL, "kvt_stage_tail: null plane or staging buffer");
+    hipStream_t s = kvt::as_stream(stream);
+    const uint64_t src = reinterpret_cast<uint64_t>(plane) + (uint64_t)row_begin * row_bytes;
+    const uint64_t dst = reinterpret_cast<uint64_t>(staging);
+    if (mode != KVT_COPY_KERNEL) {
+        KVT_HIP(hipMemcpyAsync(staging, reinterpret_cast<const void *>(src), bytes,
+                               hipMemcpyDefault, s));
+        return KVT_OK;
+    }
+    const uint64_t blocks = (bytes + (uint64_t)kChunk * kWavesPerBlock - 1) /
+                            ((uint64_t)kChunk * kWavesPerBlock);
+    if (blocks > 0x7fffffffull)
+        return kvt::fail(KVT_ERANGE, "kvt_stage_tail: %llu bytes exceed one launch",
+                         (unsigned long long)bytes);
+    hipLaunchKernelGGL(copy_span_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, bytes);
+    KVT_LAUNCHED("copy_span_kernel");
+    return KVT_OK;
+}

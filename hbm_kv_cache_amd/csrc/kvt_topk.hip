@@ -1,0 +1,336 @@
+// kvt_topk.hip -- S3 index scoring + S4 top-k block selection.
+//
+// QSA-KVO keeps the pooled indexer plane in HBM because it is scored in full on every step;
+// the top-k of those scores decides which K/V blocks cross the host link.
+//
+// Kernel 1 (score_local_topk): a workgroup takes kChunkBlocks pooled rows, stages them and the
+//   index queries in LDS, evaluates every (block, head) score in fp64 (each fp16*fp16 product
+//   is exact in fp64 and the sum runs in index order, so the value is fully determined), and
+//   keeps each head's best min(k, kChunkBlocks) candidates, found by a segmented bitonic sort
+//   in LDS.  Candidates go to the workspace as (64-bit rank key, block id).
+// Kernel 2 (merge_topk): per head, segments of up to kMergeMax candidates are sorted again and
+//   cut to k; repeated until one segment per head remains, whose ids are then sorted
+//   ascending and written out (-1 for empty slots).
+//
+// Rank order (a total order, so the result is unique): larger score first, equal scores by
+// lower block id, NaN after every number.  Encoded as a 64-bit key (larger = better) plus id.
+#include <algorithm>
+
+#include "kvt_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunkBlocks = 128;     // pooled rows per scoring workgroup
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeMax = 4096;       // candidates per merge workgroup (power of two)
+constexpr uint32_t kNoId = 0xffffffffu;
+
+__device__ __forceinline__ uint64_t rank_key(double s)
+{
+    uint64_t u = __double_as_longlong(s);
+    if (s != s)
+        return 0;  // NaN: below every number
+    if (s == 0.0)
+        return 0x8000000000000000ull;  // -0 and +0 are the same score
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// a ranks before b
+__device__ __forceinline__ bool better(uint64_t ka, uint32_t ia, uint64_t kb, uint32_t ib)
+{
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// In-place bitonic sort, best first, of n (power of two) entries split into independent
+// segments of `seg` (power of two, seg <= n).  All threads of the block take part.
+__device__ void bitonic_best_first(uint64_t *key, uint32_t *id, int n, int seg)
+{
+    for (int size = 2; size <= seg; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
+                const int i = (p / stride) * 2 * stride + (p % stride);
+                const int j = i + stride;
+                const bool up = size == seg || (i & size) == 0;
+                const uint64_t ka = key[i], kb = key[j];
+                const uint32_t ia = id[i], ib = id[j];
+                const bool swap = up ? better(kb, ib, ka, ia) : better(ka, ia, kb, ib);
+                if (swap) {
+                    key[i] = kb; key[j] = ka;
+                    id[i] = ib; id[j] = ia;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ascending sort of n (power of two) ids, kNoId last
+__device__ void bitonic_ids_ascending(uint32_t *id, int n)
+{
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
+                const int i = (p / stride) * 2 * stride + (p % stride);
+                const int j = i + stride;
+                const bool up = size == n || (i & size) == 0;
+                const uint32_t a = id[i], b = id[j];
+                if (up ? b < a : a < b) {
+                    id[i] = b;
+                    id[j] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__host__ __device__ constexpr int pow2_at_least(int x)
+{
+    int p = 1;
+    while (p < x)
+        p <<= 1;
+    return p;
+}
+
+// grid.x = ceil(n_blocks / kChunkBlocks); dynamic LDS = see score_lds_bytes
+__global__ __launch_bounds__(kThreads) void score_local_topk(
+    const uint16_t *__restrict__ pooled, int64_t n_blocks, int dim,
+    const uint16_t *__restrict__ q_idx, int n_sel, int kk, uint64_t *__restrict__ cand_key,
+    uint32_t *__restrict__ cand_id, double *__restrict__ scores_out)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int pitch = dim * 2 + 16;  // bytes per staged pooled row (padded: no bank conflicts)
+    unsigned char *rows = lds;
+    float *qf = reinterpret_cast<float *>(lds + kChunkBlocks * pitch);
+    uint64_t *skey = reinterpret_cast<uint64_t *>(qf + n_sel * dim);
+    uint32_t *sid = reinterpret_cast<uint32_t *>(skey + n_sel * kChunkBlocks);
+
+    const int64_t b0 = (int64_t)blockIdx.x * kChunkBlocks;
+    const int nrows = (int)std::min<int64_t>(kChunkBlocks, n_blocks - b0);
+    const int words_per_row = dim / 8;
+
+    // stage pooled rows (16-byte words, coalesced) and the index queries (as exact fp32)
+    for (int w = threadIdx.x; w < nrows * words_per_row; w += kThreads) {
+        const int r = w / words_per_row, c = w % words_per_row;
+        const uint4 v = *reinterpret_cast<const uint4 *>(pooled + (b0 + r) * dim + c * 8);
+        *reinterpret_cast<uint4 *>(rows + r * pitch + c * 16) = v;
+    }
+    for (int e = threadIdx.x; e < n_sel * dim; e += kThreads)
+        qf[e] = f16_bits_to_f32(q_idx[e]);
+    __syncthreads();
+
+    // scores: pair p = h*kChunkBlocks + r; four independent fp64 chains per thread
+    const int npairs = n_sel * kChunkBlocks;
+    for (int p0 = threadIdx.x; p0 < npairs; p0 += 4 * kThreads) {
+        int r[4], h[4];
+        double acc[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int p = min(p0 + u * kThreads, npairs - 1);
+            h[u] = p / kChunkBlocks;
+            r[u] = p % kChunkBlocks;
+            if (r[u] >= nrows)
+                r[u] = 0;
+            acc[u] = 0.0;
+        }
+        for (int c = 0; c < words_per_row; c++) {
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(rows + r[u] * pitch + c * 16);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                const float *qh = qf + h[u] * dim + c * 8;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const uint16_t bits = (uint16_t)(w4[e >> 1] >> ((e & 1) * 16));
+                    const double pv = (double)f16_bits_to_f32(bits);
+                    acc[u] = fma((double)qh[e], pv, acc[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int p = p0 + u * kThreads;
+            if (p >= npairs)
+                continue;
+            const int hh = p / kChunkBlocks, rr = p % kChunkBlocks;
+            if (rr < nrows) {
+                skey[p] = rank_key(acc[u]);
+                sid[p] = (uint32_t)(b0 + rr);
+                if (scores_out)
+                    scores_out[(int64_t)hh * n_blocks + b0 + rr] = acc[u];
+            } else {
+                skey[p] = 0;
+                sid[p] = kNoId;
+            }
+        }
+    }
+    __syncthreads();
+
+    bitonic_best_first(skey, sid, npairs, kChunkBlocks);
+
+    // best kk of each head's segment -> candidates [h][blockIdx][kk]
+    for (int e = threadIdx.x; e < n_sel * kk; e += kThreads) {
+        const int hh = e / kk, i = e % kk;
+        const int64_t o = ((int64_t)hh * gridDim.x + blockIdx.x) * kk + i;
+        cand_key[o] = skey[hh * kChunkBlocks + i];
+        cand_id[o] = sid[hh * kChunkBlocks + i];
+    }
+}
+
+// grid = (n_seg_out, n_sel).  Input per head: n_in candidates; segment s covers
+// [s*kMergeMax, ...).  Output per head: n_seg_out*k candidates, or (final) k ids.
+__global__ __launch_bounds__(kMergeThreads) void merge_topk(
+    const uint64_t *__restrict__ in_key, const uint32_t *__restrict__ in_id, int64_t n_in,
+    int k, uint64_t *__restrict__ out_key, uint32_t *__restrict__ out_id,
+    int32_t *__restrict__ ids_final)
+{
+    __shared__ uint64_t skey[kMergeMax];
+    __shared__ uint32_t sid[kMergeMax];
+    const int h = blockIdx.y;
+    const int64_t s0 = (int64_t)blockIdx.x * kMergeMax;
+    const int cnt = (int)std::min<int64_t>(kMergeMax, n_in - s0);
+    const int n = pow2_at_least(std::max(cnt, k));
+    for (int i = threadIdx.x; i < n; i += kMergeThreads) {
+        if (i < cnt) {
+            skey[i] = in_key[h * n_in + s0 + i];
+            sid[i] = in_id[h * n_in + s0 + i];
+        } else {
+            skey[i] = 0;
+            sid[i] = kNoId;
+        }
+    }
+    __syncthreads();
+    bitonic_best_first(skey, sid, n, n);
+    if (!ids_final) {
+        for (int i = threadIdx.x; i < k; i += kMergeThreads) {
+            const int64_t o = ((int64_t)h * gridDim.x + blockIdx.x) * k + i;
+            out_key[o] = skey[i];
+            out_id[o] = sid[i];
+        }
+        return;
+    }
+    // final: the k selected ids in ascending order, empty slots (kNoId) last as -1
+    const int m = pow2_at_least(k);
+    for (int i = threadIdx.x; i < m; i += kMergeThreads)
+        if (i >= k)
+            sid[i] = kNoId;
+    __syncthreads();
+    bitonic_ids_ascending(sid, m);
+    for (int i = threadIdx.x; i < k; i += kMergeThreads)
+        ids_final[h * k + i] = sid[i] == kNoId ? -1 : (int32_t)sid[i];
+}
+
+size_t score_lds_bytes(int dim, int n_sel)
+{
+    return (size_t)kChunkBlocks * (dim * 2 + 16) + (size_t)n_sel * dim * 4 +
+           (size_t)n_sel * kChunkBlocks * 12;
+}
+
+struct Plan {
+    int64_t n_wg;        // scoring workgroups
+    int kk;              // candidates each keeps per head
+    int64_t level0;      // candidates per head after scoring
+    int64_t buf_a, buf_b;  // entries per head of the two ping-pong candidate buffers
+};
+
+Plan make_plan(int64_t n_blocks, int k)
+{
+    Plan p;
+    p.n_wg = (n_blocks + kChunkBlocks - 1) / kChunkBlocks;
+    p.kk = std::min(k, kChunkBlocks);
+    p.level0 = p.n_wg * p.kk;
+    p.buf_a = p.level0;
+    int64_t n = p.level0, b = 0;
+    bool to_b = true;
+    while (n > kMergeMax) {  // intermediate merge levels
+        const int64_t segs = (n + kMergeMax - 1) / kMergeMax;
+        n = segs * k;
+        if (to_b)
+            b = std::max(b, n);
+        to_b = !to_b;
+    }
+    p.buf_b = b;
+    return p;
+}
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" size_t kvt_index_topk_ws_bytes(int64_t n_blocks, int32_t n_sel, int32_t k)
+{
+    if (n_blocks < 0 || n_sel < 1 || k < 1)
+        return 0;
+    const Plan p = make_plan(std::max<int64_t>(n_blocks, 1), k);
+    const size_t a = (size_t)n_sel * p.buf_a, b = (size_t)n_sel * p.buf_b;
+    return round_up(a * 8, 256) + round_up(a * 4, 256) + round_up(b * 8, 256) +
+           round_up(b * 4, 256) + 256;
+}
+
+// S3+S4: QSA-KVO pooled-plane scoring and top-k block selection.
+extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
+                              const void *q_idx, int32_t n_sel, int32_t k, int32_t *ids,
+                              double *scores, void *ws, size_t ws_bytes, void *stream)
+{
+    if (n_blocks < 0 || n_blocks > 0x7fffffffll || dim < 8 || dim > 256 || dim % 8 ||
+        n_sel < 1 || n_sel > 32 || k < 1 || k > 256)
+        return kvt::fail(KVT_EINVAL,
+                         "kvt_index_topk: n_blocks=%lld dim=%d n_sel=%d k=%d outside limits",
+                         (long long)n_blocks, dim, n_sel, k);
+    if (!ids || !q_idx || (n_blocks && !pooled))
+        return kvt::fail(KVT_EINVAL, "kvt_index_topk: null pointer");
+    if (!kvt::aligned(pooled, 16))
+        return kvt::fail(KVT_EALIGN, "kvt_index_topk: pooled plane must be 16-byte aligned");
+    const size_t need = kvt_index_topk_ws_bytes(n_blocks, n_sel, k);
+    if (!ws || ws_bytes < need)
+        return kvt::fail(KVT_EINVAL, "kvt_index_topk: workspace of %zu bytes, need %zu",
+                         ws_bytes, need);
+    hipStream_t s = kvt::as_stream(stream);
+    const Plan p = make_plan(std::max<int64_t>(n_blocks, 1), k);
+
+    // carve the workspace (256-byte aligned pieces)
+    uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
+    const size_t a = (size_t)n_sel * p.buf_a, b = (size_t)n_sel * p.buf_b;
+    uint64_t *a_key = reinterpret_cast<uint64_t *>(w); w += round_up(a * 8, 256);
+    uint32_t *a_id = reinterpret_cast<uint32_t *>(w); w += round_up(a * 4, 256);
+    uint64_t *b_key = reinterpret_cast<uint64_t *>(w); w += round_up(b * 8, 256);
+    uint32_t *b_id = reinterpret_cast<uint32_t *>(w);
+
+    if (n_blocks == 0) {
+        // nothing to rank: every slot is empty.  One merge over a single empty segment.
+        hipLaunchKernelGGL(merge_topk, dim3(1, n_sel), dim3(kMergeThreads), 0, s, a_key, a_id,
+                           (int64_t)0, k, nullptr, nullptr, ids);
+        KVT_LAUNCHED("merge_topk");
+        return KVT_OK;
+    }
+    const size_t lds = score_lds_bytes(dim, n_sel);
+    if (lds > 160 * 1024)
+        return kvt::fail(KVT_EINVAL, "kvt_index_topk: dim=%d n_sel=%d need %zu bytes of LDS",
+                         dim, n_sel, lds);
+    hipLaunchKernelGGL(score_local_topk, dim3((unsigned)p.n_wg), dim3(kThreads), lds, s,
+                       static_cast<const uint16_t *>(pooled), n_blocks, dim,
+                       static_cast<const uint16_t *>(q_idx), n_sel, p.kk, a_key, a_id, scores);
+    KVT_LAUNCHED("score_local_topk");
+
+    int64_t n = p.level0;
+    bool in_a = true;
+    while (true) {
+        const int64_t segs = (n + kMergeMax - 1) / kMergeMax;
+        const uint64_t *ik = in_a ? a_key : b_key;
+        const uint32_t *ii = in_a ? a_id : b_id;
+        if (segs == 1) {
+            hipLaunchKernelGGL(merge_topk, dim3(1, n_sel), dim3(kMergeThreads), 0, s, ik, ii, n,
+                               k, nullptr, nullptr, ids);
+            KVT_LAUNCHED("merge_topk");
+            return KVT_OK;
+        }
+        uint64_t *ok = in_a ? b_key : a_key;
+        uint32_t *oi = in_a ? b_id : a_id;
+        hipLaunchKernelGGL(merge_topk, dim3((unsigned)segs, n_sel), dim3(kMergeThreads), 0, s,
+                           ik, ii, n, k, ok, oi, nullptr);
+        KVT_LAUNCHED("merge_topk");
+        n = segs * k;
+        in_a = !in_a;
+    }
+}

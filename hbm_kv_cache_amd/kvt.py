@@ -1,0 +1,213 @@
+"""ctypes binding for libkvt.so -- argument marshalling only, same names as include/kvt.h.
+
+Every pointer argument accepts an int address, a torch tensor (its data_ptr()), a numpy array
+(its data address) or None (NULL).  Stream arguments accept a torch stream, a raw handle (int)
+or None, which means torch's current stream on the current device.  Each call returns nothing
+and raises ``KvtError`` (carrying the status code and the library's message) on failure.
+
+There is no fallback: if libkvt.so is missing or does not load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_uint, c_uint64, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvt.so")
+
+OK, EINVAL, ERANGE, EALIGN, EOVERLAP, ENOMEM, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+H2D, D2H = 0, 1
+COPY_AUTO, COPY_KERNEL, COPY_SDMA = 0, 1, 2
+F16, BF16, Q8_0 = 1, 2, 3
+HOST_COHERENT, HOST_NONCOHERENT, HOST_WRITECOMBINED = 0, 1, 2
+
+_P = c_void_p
+_SIGNATURES = {
+    "kvt_abi_version": (c_int, []),
+    "kvt_last_error": (ctypes.c_char_p, []),
+    "kvt_host_alloc": (c_int, [c_size_t, c_uint, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p)]),
+    "kvt_host_free": (c_int, [_P]),
+    "kvt_sub_block_ptrs": (c_int, [c_uint64, c_uint64, c_uint64, _P, c_int64, c_int32, c_int32,
+                                   _P, c_int64]),
+    "kvt_chunks_consumed": (c_int64, [c_int64, c_int32, c_int32]),
+    "kvt_swap_blocks": (c_int, [_P, _P, _P, c_int64, c_int32, c_int32, _P]),
+    "kvt_set_copy_threshold": (c_uint64, [c_int32, c_uint64]),
+    "kvt_index_topk_ws_bytes": (c_size_t, [c_int64, c_int32, c_int32]),
+    "kvt_index_topk": (c_int, [_P, c_int64, c_int32, _P, c_int32, c_int32, _P, _P, _P, c_size_t,
+                               _P]),
+    "kvt_gather_blocks": (c_int, [_P, _P, c_int64, c_int32, c_int32, c_int32, c_int64, _P,
+                                  c_int32, _P, c_int32, _P, _P, _P]),
+    "kvt_stage_tail": (c_int, [_P, c_int64, c_int64, c_int64, _P, c_int32, _P]),
+    "kvt_attn_decode_ws_bytes": (c_size_t, [c_int32, c_int32, c_int64]),
+    "kvt_attn_decode": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, _P, _P, c_int64, _P,
+                                c_float, _P, _P, c_size_t, _P]),
+    "kvt_attn_prefill": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P, c_int64,
+                                 _P, _P, c_int64, c_int32, c_int32, c_float, _P, _P]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class KvtError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+def load():
+    """Load libkvt.so (once).  Raises if it is missing: there is no other implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m hbm_kv_cache_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x).__name__}")
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(fn, rc):
+    if rc != OK:
+        msg = load().kvt_last_error()
+        raise KvtError(fn, rc, msg.decode() if msg else "")
+
+
+def kvt_abi_version() -> int:
+    return load().kvt_abi_version()
+
+
+def kvt_last_error() -> str:
+    m = load().kvt_last_error()
+    return m.decode() if m else ""
+
+
+def kvt_host_alloc(nbytes: int, flags: int = HOST_COHERENT):
+    """Returns (host_address, device_address) of a zeroed pinned, device-mapped slab."""
+    h, d = c_void_p(), c_void_p()
+    _check("kvt_host_alloc", load().kvt_host_alloc(int(nbytes), int(flags), ctypes.byref(h),
+                                                   ctypes.byref(d)))
+    return h.value, d.value
+
+
+def kvt_host_free(host_ptr: int) -> None:
+    _check("kvt_host_free", load().kvt_host_free(host_ptr))
+
+
+def kvt_sub_block_ptrs(base, row_stride, page_bytes, block_ids, n_ids, bpc, skip, out, n_out):
+    _check("kvt_sub_block_ptrs", load().kvt_sub_block_ptrs(
+        int(base), int(row_stride), int(page_bytes), _ptr(block_ids), int(n_ids), int(bpc),
+        int(skip), _ptr(out), int(n_out)))
+
+
+def kvt_chunks_consumed(n, skip, bpc) -> int:
+    return int(load().kvt_chunks_consumed(int(n), int(skip), int(bpc)))
+
+
+def kvt_swap_blocks(src, dst, sizes, n, direction, mode=COPY_AUTO, stream=None):
+    _check("kvt_swap_blocks", load().kvt_swap_blocks(_ptr(src), _ptr(dst), _ptr(sizes), int(n),
+                                                     int(direction), int(mode), _stream(stream)))
+
+
+def kvt_set_copy_threshold(direction, nbytes) -> int:
+    return int(load().kvt_set_copy_threshold(int(direction), int(nbytes)))
+
+
+def kvt_index_topk_ws_bytes(n_blocks, n_sel, k) -> int:
+    return int(load().kvt_index_topk_ws_bytes(int(n_blocks), int(n_sel), int(k)))
+
+
+def kvt_index_topk(pooled, n_blocks, dim, q_idx, n_sel, k, ids, scores, ws, ws_bytes,
+                   stream=None):
+    _check("kvt_index_topk", load().kvt_index_topk(
+        _ptr(pooled), int(n_blocks), int(dim), _ptr(q_idx), int(n_sel), int(k), _ptr(ids),
+        _ptr(scores), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def kvt_gather_blocks(k_plane, v_plane, n_tok, kvh, hd, elem_bytes, row_stride, block_table, bt,
+                      ids, k, k_out, v_out, stream=None):
+    _check("kvt_gather_blocks", load().kvt_gather_blocks(
+        _ptr(k_plane), _ptr(v_plane), int(n_tok), int(kvh), int(hd), int(elem_bytes),
+        int(row_stride), _ptr(block_table), int(bt), _ptr(ids), int(k), _ptr(k_out), _ptr(v_out),
+        _stream(stream)))
+
+
+def kvt_stage_tail(plane, row_bytes, row_begin, row_end, staging, mode=COPY_AUTO, stream=None):
+    _check("kvt_stage_tail", load().kvt_stage_tail(_ptr(plane), int(row_bytes), int(row_begin),
+                                                   int(row_end), _ptr(staging), int(mode),
+                                                   _stream(stream)))
+
+
+def kvt_attn_decode_ws_bytes(n_qh, hd, n_kv) -> int:
+    return int(load().kvt_attn_decode_ws_bytes(int(n_qh), int(hd), int(n_kv)))
+
+
+def kvt_attn_decode(q, n_qh, kvh, hd, dtype, k, v, n_kv, n_valid, scale, out, ws, ws_bytes,
+                    stream=None):
+    _check("kvt_attn_decode", load().kvt_attn_decode(
+        _ptr(q), int(n_qh), int(kvh), int(hd), int(dtype), _ptr(k), _ptr(v), int(n_kv),
+        _ptr(n_valid), float(scale), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def kvt_attn_prefill(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_tail, v_tail, n_kv,
+                     kv_format, causal, scale, out, stream=None):
+    _check("kvt_attn_prefill", load().kvt_attn_prefill(
+        _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
+        int(n_head), _ptr(k_tail), _ptr(v_tail), int(n_kv), int(kv_format), int(bool(causal)),
+        float(scale), _ptr(out), _stream(stream)))
+
+
+class HostBuffer:
+    """Owner of one pinned, device-mapped host slab from kvt_host_alloc.
+
+    ``.host`` / ``.dev`` are the two addresses; ``.numpy(dtype, shape)`` views the host side;
+    ``.free()`` (or garbage collection) releases it -- drop every view first, and make sure no
+    queued GPU work still reads it."""
+
+    def __init__(self, nbytes: int, flags: int = HOST_COHERENT):
+        self.nbytes = int(nbytes)
+        self.host, self.dev = kvt_host_alloc(self.nbytes, flags)
+
+    def numpy(self, dtype="uint8", shape=None):
+        import numpy as np
+        dt = np.dtype(dtype)
+        buf = (ctypes.c_char * self.nbytes).from_address(self.host)
+        a = np.frombuffer(buf, dtype=dt, count=self.nbytes // dt.itemsize)
+        return a if shape is None else a.reshape(shape)
+
+    def free(self):
+        if self.host:
+            kvt_host_free(self.host)
+            self.host = self.dev = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

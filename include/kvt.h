@@ -1,0 +1,211 @@
+/*
+ * kvt.h -- C ABI of libkvt: the tiered KV-cache hot path on MI355X (gfx950).
+ *
+ * Paged K/V lives partly in pinned, device-mapped host memory and partly in HBM.  The library
+ * moves blocks between the tiers and runs attention over them:
+ *
+ *   kvt_sub_block_ptrs   build src/dst/size pointer tables        (host, pure)
+ *   kvt_swap_blocks      batched block copy driven by those tables (host<->HBM)
+ *   kvt_index_topk       score a pooled indexer plane in HBM, select the top-k blocks
+ *   kvt_gather_blocks    copy only the selected blocks' K/V rows host -> HBM
+ *   kvt_stage_tail       copy a sequence's host-resident rows into an HBM staging buffer
+ *   kvt_attn_decode      GQA decode attention over gathered K/V
+ *   kvt_attn_prefill     causal (or full) prefill attention over an HBM head + tail
+ *
+ * Sources (page titles; each entry point names the section it follows):
+ *   [vLLM-CPU] vLLM fork, "v1/kv_offload/cpu/gpu_worker.py" (CPU offloading worker)
+ *   [QSA-KVO]  "QSA KV cache host-RAM offload for ExLlamaV3" (qsa-kv-offload.patch)
+ *   [llama-T]  "llama/cuda: tiered KV cache (--kv-vram-cells)", llama.cpp PR #319
+ *
+ * Conventions (all entry points):
+ *   - The caller owns every buffer.  The library allocates nothing on the hot path; where an
+ *     op needs scratch, the caller passes a workspace sized by the matching *_ws_bytes call.
+ *   - "device pointer" = an address a gfx950 kernel may dereference: HBM from hipMalloc /
+ *     torch, or pinned host memory from kvt_host_alloc (its device alias).  "host-mapped"
+ *     planes are such device aliases of pinned host memory; kernels read them over PCIe.
+ *   - Every compute entry point only ENQUEUES work on `stream` (a hipStream_t; NULL = the
+ *     legacy default stream) and returns.  Inputs, tables and outputs must stay valid, and
+ *     must not be written by anyone else, until the stream has passed the op.  Ordering against
+ *     other streams (e.g. a store must wait for the writes it reads) is the caller's job.
+ *   - Errors: argument checks happen on the host before anything is enqueued; a failing check
+ *     returns a negative status and enqueues nothing.  Nothing aborts or throws across the
+ *     ABI.  kvt_last_error() returns a message for the last failure on the calling thread.
+ *   - ABI evolution is append-only: new parameters go into new entry points, and
+ *     kvt_abi_version() is bumped on any addition.
+ */
+#ifndef KVT_H
+#define KVT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVT_ABI_VERSION 1
+
+/* status codes */
+#define KVT_OK 0
+#define KVT_EINVAL (-1)       /* bad argument (shape, count, null pointer, skip >= bpc ...) */
+#define KVT_ERANGE (-2)       /* an index or count outside what the buffers hold */
+#define KVT_EALIGN (-3)       /* an address or size misaligned for the requested path */
+#define KVT_EOVERLAP (-4)     /* overlapping copy ranges (only when validation is asked for) */
+#define KVT_ENOMEM (-5)       /* pinned host allocation failed */
+#define KVT_EUNSUPPORTED (-6) /* a valid request this build does not implement */
+#define KVT_EHIP (-7)         /* a HIP runtime call failed; kvt_last_error() has its text */
+
+/* copy direction and mechanism */
+#define KVT_H2D 0
+#define KVT_D2H 1
+#define KVT_COPY_AUTO 0   /* kernel below the page-size threshold when 8-byte aligned, else SDMA */
+#define KVT_COPY_KERNEL 1 /* wavefront loads/stores through the host mapping */
+#define KVT_COPY_SDMA 2   /* the copy engines (hipMemcpyBatchAsync) */
+
+/* element formats */
+#define KVT_F16 1
+#define KVT_BF16 2
+#define KVT_Q8_0 3 /* 32-value blocks: fp16 scale (2 bytes, little-endian) + 32 int8; x = scale*q */
+
+/* kvt_host_alloc flags */
+#define KVT_HOST_COHERENT 0u       /* fine-grained: GPU reads bypass caching of host data */
+#define KVT_HOST_NONCOHERENT 1u    /* coarse-grained mapping */
+#define KVT_HOST_WRITECOMBINED 2u  /* write-combined on the CPU side (host writes, GPU reads) */
+
+int kvt_abi_version(void);
+const char *kvt_last_error(void);
+
+/* ----------------------------------------------------------------------------------------
+ * Host tier.  [QSA-KVO] CacheLayer_qsa_offload.alloc/free: K/V planes live in pinned,
+ * device-mapped host memory that kernels reach through a device alias.  The page registers
+ * an anonymous mapping; this library allocates pinned memory instead (registering memory
+ * that already exists is not available on every ROCm host), with the same result: one slab,
+ * zero-filled, usable by host code through *host_ptr and by kernels through *dev_ptr.
+ *   bytes    > 0
+ *   flags    KVT_HOST_* (one of)
+ *   host_ptr receives the host address; dev_ptr the device alias (equal on ROCm with UVA).
+ * Returns KVT_ENOMEM when the allocation fails (the page's fallback rule: the caller may
+ * then keep the data in pageable memory and use SDMA copies).
+ * kvt_host_free releases a slab from kvt_host_alloc; every device use must have completed.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_host_alloc(size_t bytes, unsigned flags, void **host_ptr, void **dev_ptr);
+int kvt_host_free(void *host_ptr);
+
+/* ----------------------------------------------------------------------------------------
+ * S1  pointer tables.  [vLLM-CPU] compute_sub_block_ptrs, _fill_direct_ops, transfer_async.
+ * A tensor row (block) b holds `bpc` sub-blocks ("pages") of page_bytes each; sub-block j of
+ * block b starts at  base + b*row_stride + j*page_bytes.  The pointers of block_ids[0..n_ids)
+ * are listed block-major and the run [skip, skip + n_out) is written to out[0..n_out).
+ *   bpc >= 1, 0 <= skip < bpc, n_out <= n_ids*bpc - skip, block_ids[i] >= 0.
+ * With bpc == 1 (the GPU side of a transfer) out[i] = base + block_ids[i]*row_stride.
+ * Pure host code: touches no device.  Errors: KVT_EINVAL, KVT_ERANGE.
+ * kvt_chunks_consumed(n, skip, bpc) = ceil((n + skip) / bpc): how many chunk-side blocks a
+ * run of n sub-blocks starting `skip` into its first block uses.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_sub_block_ptrs(uint64_t base, uint64_t row_stride, uint64_t page_bytes,
+                       const int64_t *block_ids, int64_t n_ids, int32_t bpc, int32_t skip,
+                       uint64_t *out, int64_t n_out);
+int64_t kvt_chunks_consumed(int64_t n, int32_t skip, int32_t bpc);
+
+/* ----------------------------------------------------------------------------------------
+ * S2  batched swap.  [vLLM-CPU] transfer_async -> swap_blocks_batch(src, dst, sizes):
+ *   for i < n: copy sizes[i] bytes from address src[i] to address dst[i].
+ * src, dst, sizes: u64 tables of n entries in pinned host memory from kvt_host_alloc (the
+ *   SDMA path reads them on the host, the kernel path through their device alias; pass the
+ *   host pointer -- it is the same address on ROCm).  Table entries are device addresses.
+ * dir:  KVT_H2D (load) or KVT_D2H (store); only steers KVT_COPY_AUTO (stores go to SDMA,
+ *   as the page does, unless measured otherwise with kvt_set_copy_threshold).
+ * mode: KVT_COPY_AUTO / KERNEL / SDMA.  The kernel path needs every size to be a multiple
+ *   of 8 and 8-byte aligned addresses (else KVT_EALIGN); 16-byte alignment takes the wide path.
+ * Destination ranges must be pairwise disjoint and disjoint from all sources; the order of
+ * the copies is unspecified.  Zero sizes are no-ops.  n == 0 enqueues nothing.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
+                    int32_t dir, int32_t mode, void *stream);
+/* AUTO switches to SDMA at pages >= threshold bytes (per direction); returns the old value. */
+uint64_t kvt_set_copy_threshold(int32_t dir, uint64_t bytes);
+
+/* ----------------------------------------------------------------------------------------
+ * S3+S4  index scoring and top-k selection.  [QSA-KVO] CacheLayer_qsa_offload docstring and
+ * InferParams.qsa_kv_offload: the pooled indexer plane stays in HBM and is scored in full on
+ * every step; a top-k selection of blocks decides which K/V rows are read from host memory.
+ *   pooled  device fp16 [n_blocks][dim]  (one pooled key per KV block)
+ *   q_idx   device fp16 [n_sel][dim]     (one index query per selection head)
+ *   score s[h][b] = sum_{d=0..dim-1} q_idx[h][d]*pooled[b][d], evaluated in fp64 in index
+ *   order (each fp16 product is exact in fp64, so the value is fully determined).
+ *   ids     device int32 [n_sel][k]: per head the k best blocks -- larger score first, equal
+ *           scores by lower block id, NaN after every number -- written in ascending id
+ *           order; when k > n_blocks the trailing slots hold -1.
+ *   scores  optional device fp64 [n_sel][n_blocks] copy of every score (NULL to skip).
+ *   ws      device workspace of kvt_index_topk_ws_bytes(n_blocks, n_sel, k) bytes.
+ * Limits: 1 <= k <= 256, dim a multiple of 8 and <= 256, 1 <= n_sel <= 64.
+ * ---------------------------------------------------------------------------------------- */
+size_t kvt_index_topk_ws_bytes(int64_t n_blocks, int32_t n_sel, int32_t k);
+int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim, const void *q_idx,
+                   int32_t n_sel, int32_t k, int32_t *ids, double *scores, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S5  top-k gather.  [QSA-KVO] sparse_attend / CacheLayer_qsa_offload: only the selected
+ * blocks' K/V rows cross the host link, so the bytes read per step do not depend on context.
+ *   k_plane, v_plane  device pointers (normally host-mapped) to token-major planes: token t,
+ *                     head h starts at plane + t*row_stride + h*hd*elem_bytes.
+ *   n_tok             tokens the planes hold; block b covers tokens [b*bt, b*bt + bt) of
+ *                     physical block block_table[b] (identity when block_table is NULL).
+ *   ids               device int32 [kvh][k], e.g. kvt_index_topk's output.
+ *   k_out, v_out      device [kvh][k*bt][hd] elements:  out[h][i*bt + r] = plane[phys*bt + r][h].
+ * Slots with ids < 0, or whose block lies outside the planes, are skipped (left untouched).
+ * hd*elem_bytes and row_stride must be multiples of 16, plane bases 16-byte aligned.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_gather_blocks(const void *k_plane, const void *v_plane, int64_t n_tok, int32_t kvh,
+                      int32_t hd, int32_t elem_bytes, int64_t row_stride,
+                      const int32_t *block_table, int32_t bt, const int32_t *ids, int32_t k,
+                      void *k_out, void *v_out, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S7  tail staging.  [llama-T] commit text: when an attention op reaches the host tail, the
+ * used host rows are copied into a VRAM staging buffer once per op, and the op reads that.
+ *   staging[(r - row_begin)*row_bytes ...] = plane[r*row_bytes ...]  for r in [row_begin, row_end)
+ *   plane: device pointer (host-mapped), staging: device (HBM); mode KVT_COPY_* (AUTO = SDMA).
+ * ---------------------------------------------------------------------------------------- */
+int kvt_stage_tail(const void *plane, int64_t row_bytes, int64_t row_begin, int64_t row_end,
+                   void *staging, int32_t mode, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S6  decode attention.  [QSA-KVO] qsa_sparse_attend_rows_staged: q head i reads KV head
+ * i / (n_qh/kvh); softmax over the head's keys; partial (o, m, l) folded with the online-
+ * softmax rule.
+ *   q      device [n_qh][hd], dtype KVT_BF16 or KVT_F16
+ *   k, v   device [kvh][n_kv][hd], same dtype (kvt_gather_blocks' layout)
+ *   n_valid optional device int32 [kvh]: keys j < n_valid[h] take part (NULL = all n_kv)
+ *   out    device fp32 [n_qh][hd]:  o_i = sum_j e^(l_j - m) v_j / sum_j e^(l_j - m),
+ *          l_j = scale * q_i.k_j; a head with no valid key gets 0.
+ *   ws     device workspace of kvt_attn_decode_ws_bytes(n_qh, hd, n_kv) bytes.
+ * Limits: hd == 128, n_qh/kvh <= 16.  Deterministic: fixed split and merge order.
+ * ---------------------------------------------------------------------------------------- */
+size_t kvt_attn_decode_ws_bytes(int32_t n_qh, int32_t hd, int64_t n_kv);
+int kvt_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd, int32_t dtype,
+                    const void *k, const void *v, int64_t n_kv, const int32_t *n_valid,
+                    float scale, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S8  prefill attention over a tiered cache.  [llama-T]: cells [0, n_head) live in HBM, the
+ * rest in host memory (read in place, or staged into HBM first by kvt_stage_tail); the output
+ * is the same, bit for bit, whichever way the tail is reached.
+ *   q      device fp16 [n_q][n_qh][hd]; query row t is at position q_pos0 + t
+ *   row r of K (and V) lives at k_head + r*row_bytes for r < n_head, else at
+ *          k_tail + (r - n_head)*row_bytes; a row is kvh heads x hd values in kv_format
+ *          (KVT_Q8_0: hd/32 blocks of 34 bytes per head, head-major)
+ *   causal nonzero: row t sees keys j <= q_pos0 + t (j < n_kv); zero: all n_kv keys
+ *   out    device fp32 [n_q][n_qh][hd]
+ * Limits: kv_format KVT_Q8_0, hd == 128, n_qh/kvh in {1, 2, 4, 8}.  Deterministic.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh,
+                     int32_t hd, const void *k_head, const void *v_head, int64_t n_head,
+                     const void *k_tail, const void *v_tail, int64_t n_kv, int32_t kv_format,
+                     int32_t causal, float scale, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVT_H */

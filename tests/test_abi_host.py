@@ -1,0 +1,114 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point include/kvt.h
+declares, and its host-side logic (pointer tables, argument validation) is right.  No call here
+reaches a device: every one either is pure host code or fails its argument check first."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from hbm_kv_cache_amd import kvt, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_all_exported():
+    lib = kvt.load()
+    names = _declared()
+    assert len(names) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", kvt.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(kvt_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        assert hasattr(lib, n)
+    assert set(kvt.EXPORTED) == set(names)
+
+
+def test_abi_version():
+    assert kvt.kvt_abi_version() == 1
+
+
+def test_library_has_gfx950_code_object():
+    out = subprocess.run(["strings", kvt.LIB_PATH], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+
+
+@pytest.mark.parametrize("bpc,skip", [(1, 0), (4, 0), (4, 3), (2, 1), (8, 7)])
+def test_sub_block_ptrs_equal_oracle(bpc, skip):
+    g = synth.rng(0, synth.P_MISC, 100 + bpc * 10 + skip)
+    ids = g.permutation(1000)[:50].astype(np.int64)
+    n_out = 50 * bpc - skip - g.integers(0, bpc)
+    base, stride, page = 0x7F00_0000_1000, 135168, 32768
+    got = np.zeros(n_out, dtype=np.uint64)
+    kvt.kvt_sub_block_ptrs(base, stride, page, ids, ids.size, bpc, skip, got, n_out)
+    ref = oracle.sub_block_ptrs(base, stride, page, ids, bpc, skip, n_out)
+    assert np.array_equal(got, ref)
+
+
+def test_sub_block_ptrs_errors_match_oracle_rules():
+    out = np.zeros(8, dtype=np.uint64)
+    ids = np.array([1, 2], dtype=np.int64)
+    for bpc, skip, n, code in [(4, 4, 1, kvt.EINVAL), (4, -1, 1, kvt.EINVAL), (0, 0, 1, kvt.EINVAL),
+                               (4, 1, 8, kvt.ERANGE)]:
+        with pytest.raises(kvt.KvtError) as e:
+            kvt.kvt_sub_block_ptrs(0, 64, 16, ids, 2, bpc, skip, out, n)
+        assert e.value.code == code
+    neg = np.array([3, -1], dtype=np.int64)
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_sub_block_ptrs(0, 64, 16, neg, 2, 1, 0, out, 2)
+    assert e.value.code == kvt.ERANGE
+
+
+def test_chunks_consumed_equal_oracle():
+    for bpc in (1, 2, 4, 8):
+        for skip in range(bpc):
+            for n in range(0, 30):
+                assert kvt.kvt_chunks_consumed(n, skip, bpc) == oracle.chunks_consumed(n, skip, bpc)
+
+
+def test_argument_errors_return_before_any_device_work():
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_swap_blocks(None, None, None, 4, kvt.H2D, kvt.COPY_KERNEL, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_swap_blocks(None, None, None, 0, 7, kvt.COPY_KERNEL, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_index_topk(16, 100, 128, 16, 8, 0, 16, None, 16, 1 << 20, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:   # workspace too small
+        kvt.kvt_index_topk(16, 100, 128, 16, 8, 32, 16, None, 16, 8, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_gather_blocks(16, 16, 128, 8, 128, 2, 100, None, 64, 16, 32, 16, 16, stream=0)
+    assert e.value.code == kvt.EALIGN
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_decode(16, 64, 8, 64, kvt.BF16, 16, 16, 10, None, 0.1, 16, 16, 1 << 20,
+                            stream=0)
+    assert e.value.code == kvt.EUNSUPPORTED
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_decode(16, 63, 8, 128, kvt.BF16, 16, 16, 10, None, 0.1, 16, 16, 1 << 20,
+                            stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_stage_tail(16, 0, 0, 10, 16, kvt.COPY_AUTO, stream=0)
+    assert e.value.code == kvt.EINVAL
+    kvt.kvt_stage_tail(16, 34, 10, 10, 16, kvt.COPY_AUTO, stream=0)   # empty range: no-op
+
+
+def test_workspace_sizes_are_monotone_and_cover_candidates():
+    a = kvt.kvt_index_topk_ws_bytes(4096, 8, 32)
+    b = kvt.kvt_index_topk_ws_bytes(16384, 8, 32)
+    c = kvt.kvt_index_topk_ws_bytes(1 << 20, 8, 32)     # needs intermediate merge levels
+    assert 0 < a < b < c
+    assert b >= 8 * (16384 // 128) * 32 * 12
+    assert kvt.kvt_attn_decode_ws_bytes(64, 128, 2048) == 64 * 32 * 130 * 4

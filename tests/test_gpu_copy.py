@@ -1,0 +1,192 @@
+"""GPU parity of the batched swap (kvt_swap_blocks) and tail staging (kvt_stage_tail) against
+the oracle's memcpy loops: bit-exact, round trips are the identity, canaries stay untouched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hbm_kv_cache_amd import kvt, synth
+
+pytestmark = pytest.mark.gpu
+
+MODES = [kvt.COPY_KERNEL, kvt.COPY_SDMA, kvt.COPY_AUTO]
+MODE_NAMES = {kvt.COPY_KERNEL: "kernel", kvt.COPY_SDMA: "sdma", kvt.COPY_AUTO: "auto"}
+
+
+def _tables(n):
+    hb = kvt.HostBuffer(max(24 * n, 24))
+    assert hb.host == hb.dev, "pinned host memory must share its address with its device alias"
+    t = hb.numpy(np.uint64, None)[:3 * n].reshape(3, n)
+    return hb, t
+
+
+def _dev_addr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: MODE_NAMES[m])
+def test_swap_one_layer_load_store_round_trip(gpu, mode):
+    """One layer: K and V planes of 256 blocks x (16 tok x 8 heads x 128 dim fp16) = 32 KiB
+    pages in pinned host memory; 64 seeded block ids host -> random HBM slots, then back."""
+    nb, page, n = 256, 16 * 8 * 128 * 2, 64
+    host = kvt.HostBuffer(2 * nb * page)
+    hv = host.numpy(np.uint16, (2, nb, page // 2))
+    hv[0] = synth.f16_normal(synth.rng(1, synth.P_K), (nb, page // 2))
+    hv[1] = synth.f16_normal(synth.rng(1, synth.P_V), (nb, page // 2))
+    dev = torch.full((2, nb, page), 0xA5, dtype=torch.uint8, device=gpu)
+    src_ids = synth.permutation(synth.rng(1, synth.P_PERM_SRC), nb)[:n]
+    dst_ids = synth.permutation(synth.rng(1, synth.P_PERM_DST), nb)[:n]
+
+    tb, t = _tables(2 * n)
+    for p in range(2):
+        kvt.kvt_sub_block_ptrs(host.dev + p * nb * page, page, page, src_ids, n, 1, 0,
+                               t[0, p * n:], n)
+        kvt.kvt_sub_block_ptrs(_dev_addr(dev) + p * nb * page, page, page, dst_ids, n, 1, 0,
+                               t[1, p * n:], n)
+    t[2] = page
+    kvt.kvt_swap_blocks(t[0], t[1], t[2], 2 * n, kvt.H2D, mode)
+    torch.cuda.synchronize()
+
+    # oracle: its own tables over the host bytes, into a canary replica of HBM
+    hbytes = host.numpy(np.uint8, (2, nb, page))
+    ref = np.full((2, nb, page), 0xA5, dtype=np.uint8)
+    for p in range(2):
+        s = oracle.sub_block_ptrs(hbytes[p].ctypes.data, page, page, src_ids, 1, 0, n)
+        d = oracle.sub_block_ptrs(ref[p].ctypes.data, page, page, dst_ids, 1, 0, n)
+        oracle.swap(s, d, np.full(n, page, dtype=np.uint64))
+    assert np.array_equal(dev.cpu().numpy(), ref)
+
+    # store back into a second, canary-filled host plane at the original ids
+    back = kvt.HostBuffer(2 * nb * page)
+    bv = back.numpy(np.uint8, (2, nb, page))
+    bv[:] = 0x5A
+    t2b, t2 = _tables(2 * n)
+    t2[0], t2[1], t2[2] = t[1], 0, page
+    for p in range(2):
+        kvt.kvt_sub_block_ptrs(back.dev + p * nb * page, page, page, src_ids, n, 1, 0,
+                               t2[1, p * n:], n)
+    kvt.kvt_swap_blocks(t2[0], t2[1], t2[2], 2 * n, kvt.D2H, mode)
+    torch.cuda.synchronize()
+    assert np.array_equal(bv[:, src_ids], hbytes[:, src_ids])
+    rest = np.setdiff1d(np.arange(nb), src_ids)
+    assert (bv[:, rest] == 0x5A).all()
+    del hv, hbytes, bv
+    host.free(); back.free(); tb.free(); t2b.free()
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: MODE_NAMES[m])
+def test_swap_chunked_strided_layers_with_skip(gpu, mode):
+    """The 32-layer geometry, fewer layers and blocks: host rows of 4 x 32 KiB pages + 4 KiB of
+    padding (bpc = 4), HBM blocks of one page, a seeded skip on the first host chunk, the same
+    id lists for every tensor; uniform random 16-bit payload; padding canaries untouched."""
+    tensors, gpu_blocks, bpc, page, pad = 6, 512, 4, 32768, 4096
+    host_rows = gpu_blocks // bpc
+    stride = bpc * page + pad
+    g = synth.rng(2, synth.P_SKIP)
+    for trial in range(2):
+        skip = int(g.integers(0, bpc))
+        n = 300 + trial * 17
+        n_chunks = kvt.kvt_chunks_consumed(n, skip, bpc)
+        host = kvt.HostBuffer(tensors * host_rows * stride)
+        hb = host.numpy(np.uint8, (tensors, host_rows, stride))
+        synth.fill_random_bytes(synth.rng(2, synth.P_K, trial), hb)
+        canary_pad = hb[:, :, bpc * page:].copy()
+        dev = torch.full((tensors, gpu_blocks, page), 0x33, dtype=torch.uint8, device=gpu)
+        chunks = synth.permutation(synth.rng(2, synth.P_PERM_SRC, trial), host_rows)[:n_chunks]
+        gids = synth.permutation(synth.rng(2, synth.P_PERM_DST, trial), gpu_blocks)[:n]
+
+        # load: host (chunked, skip) -> HBM (bpc 1)
+        tb, t = _tables(tensors * n)
+        for x in range(tensors):
+            kvt.kvt_sub_block_ptrs(host.dev + x * host_rows * stride, stride, page, chunks,
+                                   n_chunks, bpc, skip, t[0, x * n:], n)
+            kvt.kvt_sub_block_ptrs(_dev_addr(dev) + x * gpu_blocks * page, page, page, gids, n,
+                                   1, 0, t[1, x * n:], n)
+        t[2] = page
+        kvt.kvt_swap_blocks(t[0], t[1], t[2], tensors * n, kvt.H2D, mode)
+        torch.cuda.synchronize()
+        ref = np.full((tensors, gpu_blocks, page), 0x33, dtype=np.uint8)
+        for x in range(tensors):
+            s = oracle.sub_block_ptrs(hb[x].ctypes.data, stride, page, chunks, bpc, skip, n)
+            d = oracle.sub_block_ptrs(ref[x].ctypes.data, page, page, gids, 1, 0, n)
+            oracle.swap(s, d, np.full(n, page, dtype=np.uint64))
+        assert np.array_equal(dev.cpu().numpy(), ref), f"load trial {trial} skip {skip}"
+
+        # store: HBM -> the same host chunks after zeroing their pages (round trip identity)
+        before = hb.copy()
+        for x in range(tensors):
+            for o in range(n):
+                c, j = divmod(o + skip, bpc)
+                hb[x, chunks[c], j * page:(j + 1) * page] = 0
+        t[0], t[1] = t[1].copy(), t[0].copy()
+        kvt.kvt_swap_blocks(t[0], t[1], t[2], tensors * n, kvt.D2H, mode)
+        torch.cuda.synchronize()
+        assert np.array_equal(hb, before), f"round trip trial {trial}"
+        assert np.array_equal(hb[:, :, bpc * page:], canary_pad)
+        del hb, before
+        host.free(); tb.free()
+
+
+@pytest.mark.parametrize("page,offset", [(512, 0), (2048, 0), (2048, 8), (8192, 0), (1000, 8)])
+@pytest.mark.parametrize("mode", [kvt.COPY_KERNEL, kvt.COPY_SDMA])
+def test_swap_small_pages_scattered(gpu, page, offset, mode):
+    """Many small pages in random scattered order host -> HBM; offset 8 puts the host page bases
+    at 8 mod 16 (the 8-byte path); page 1000 is 8-byte aligned but not a multiple of 16."""
+    n = 65536 if page <= 2048 else 8192
+    stride = page + offset
+    host = kvt.HostBuffer(n * stride + 64)
+    hb = host.numpy(np.uint8, None)[offset:offset + n * stride].reshape(n, stride)
+    synth.fill_random_bytes(synth.rng(3, synth.P_K, page), hb)
+    dev = torch.zeros((n, page), dtype=torch.uint8, device=gpu)
+    src = synth.permutation(synth.rng(3, synth.P_PERM_SRC, page), n)
+    dst = synth.permutation(synth.rng(3, synth.P_PERM_DST, page), n)
+    tb, t = _tables(n)
+    kvt.kvt_sub_block_ptrs(host.dev + offset, stride, page, src, n, 1, 0, t[0], n)
+    kvt.kvt_sub_block_ptrs(_dev_addr(dev), page, page, dst, n, 1, 0, t[1], n)
+    t[2] = page
+    kvt.kvt_swap_blocks(t[0], t[1], t[2], n, kvt.H2D, mode)
+    torch.cuda.synchronize()
+    ref = np.zeros((n, page), dtype=np.uint8)
+    ref[dst] = hb[src, :page]
+    assert np.array_equal(dev.cpu().numpy(), ref)
+    del hb
+    host.free(); tb.free()
+
+
+def test_swap_zero_sizes_and_empty(gpu):
+    host = kvt.HostBuffer(4096)
+    dev = torch.full((4096,), 7, dtype=torch.uint8, device=gpu)
+    tb, t = _tables(4)
+    t[0] = [host.dev, host.dev + 16, host.dev + 32, host.dev + 48]
+    t[1] = [dev.data_ptr(), dev.data_ptr() + 100, dev.data_ptr() + 200, dev.data_ptr() + 300]
+    t[2] = 0
+    for mode in MODES:
+        kvt.kvt_swap_blocks(t[0], t[1], t[2], 4, kvt.H2D, mode)
+        kvt.kvt_swap_blocks(t[0], t[1], t[2], 0, kvt.H2D, mode)
+    torch.cuda.synchronize()
+    assert (dev.cpu() == 7).all()
+    with pytest.raises(kvt.KvtError) as e:
+        t[2] = [8, 8, 12, 8]
+        kvt.kvt_swap_blocks(t[0], t[1], t[2], 4, kvt.H2D, kvt.COPY_KERNEL)
+    assert e.value.code == kvt.EALIGN
+    host.free(); tb.free()
+
+
+@pytest.mark.parametrize("mode", MODES, ids=lambda m: MODE_NAMES[m])
+def test_stage_tail_q8_0_rows(gpu, mode):
+    """Tail staging: rows [n_head, n_kv) of a q8_0 plane (1088-byte rows) into HBM."""
+    kvh, hd, n_kv, n_head = 8, 128, 20000, 9413
+    rows = synth.q8_0_rows(synth.rng(5, synth.P_K), n_kv, kvh, hd)
+    row_bytes = rows.shape[1]
+    host = kvt.HostBuffer(rows.nbytes)
+    hp = host.numpy(np.uint8, rows.shape)
+    hp[:] = rows
+    staging = torch.full(((n_kv - n_head) * row_bytes + 64,), 0xCC, dtype=torch.uint8, device=gpu)
+    kvt.kvt_stage_tail(host.dev, row_bytes, n_head, n_kv, staging, mode)
+    torch.cuda.synchronize()
+    ref = oracle.stage_tail(rows, row_bytes, n_head, n_kv)
+    got = staging.cpu().numpy()
+    assert np.array_equal(got[:ref.size], ref)
+    assert (got[ref.size:] == 0xCC).all()
+    del hp
+    host.free()

@@ -1,0 +1,206 @@
+"""GPU parity of the top-k decode path: index scoring + top-k (bit-exact ids and fp64 scores),
+the host -> HBM gather (bit-exact), decode attention (<= 2e-3 max-abs vs the fp64 oracle), and
+one whole decode step at the 262,144-token geometry."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hbm_kv_cache_amd import kvt, synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _u16(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+
+
+def _run_topk(pooled, q_idx, k, dev, want_scores=True):
+    n_blocks, dim = pooled.shape
+    n_sel = q_idx.shape[0]
+    ws_bytes = kvt.kvt_index_topk_ws_bytes(n_blocks, n_sel, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ids = torch.full((n_sel, k), -7, dtype=torch.int32, device=dev)
+    scores = torch.empty((n_sel, max(n_blocks, 1)), dtype=torch.float64, device=dev)
+    pd = _u16(pooled, dev) if n_blocks else torch.empty(8, dtype=torch.int16, device=dev)
+    kvt.kvt_index_topk(pd, n_blocks, dim, _u16(q_idx, dev), n_sel, k, ids,
+                       scores if want_scores else None, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), scores.cpu().numpy()[:, :n_blocks]
+
+
+@pytest.mark.parametrize("n_blocks,k", [(4096, 32), (16384, 32), (5000, 32), (129, 32), (100, 32),
+                                        (1, 32), (32, 32), (70000, 32), (3000, 200), (5, 1)])
+def test_index_topk_bit_exact(gpu, n_blocks, k):
+    g = synth.rng(4, synth.P_POOLED, n_blocks + k)
+    pooled = synth.f16_normal(g, (n_blocks, 128))
+    q_idx = synth.f16_normal(synth.rng(4, synth.P_QIDX, n_blocks), (8, 128))
+    ids, scores = _run_topk(pooled, q_idx, k, gpu)
+    ref_scores = oracle.index_scores(pooled, q_idx)
+    assert np.array_equal(scores, ref_scores)        # fp64, index order: identical values
+    assert np.array_equal(ids, oracle.topk(ref_scores, k))
+
+
+def test_index_topk_ties_nans_and_duplicates(gpu):
+    g = synth.rng(4, synth.P_MISC, 1)
+    n_blocks = 3000
+    pooled = synth.f16_normal(g, (n_blocks, 128))
+    pooled[1000:1100] = pooled[7]                    # 101 identical keys -> exact score ties
+    pooled[2000:2010, 3] = 0x7E00                    # NaN in the key -> NaN scores
+    q_idx = synth.f16_normal(g, (8, 128))
+    q_idx[5] = 0                                     # every score 0 for head 5 (ties everywhere)
+    q_idx[6] = 0x8000                                # -0.0: products are signed zeros
+    ids, scores = _run_topk(pooled, q_idx, 32, gpu)
+    ref = oracle.index_scores(pooled, q_idx)
+    same = (scores == ref) | (np.isnan(scores) & np.isnan(ref))
+    assert same.all()
+    assert np.array_equal(ids, oracle.topk(ref, 32))
+    assert ids[5].tolist() == list(range(32))        # all ties: lowest ids
+    assert ids[6].tolist() == list(range(32))
+
+
+def test_index_topk_empty_and_oversized_k(gpu):
+    ids, _ = _run_topk(np.zeros((0, 128), np.uint16), np.zeros((8, 128), np.uint16), 16, gpu,
+                       want_scores=False)
+    assert (ids == -1).all()
+    pooled = synth.f16_normal(synth.rng(4, synth.P_MISC, 2), (7, 128))
+    q_idx = synth.f16_normal(synth.rng(4, synth.P_MISC, 3), (3, 128))
+    ids, _ = _run_topk(pooled, q_idx, 20, gpu)
+    ref = oracle.topk(oracle.index_scores(pooled, q_idx), 20)
+    assert np.array_equal(ids, ref)
+    assert (ids[:, 7:] == -1).all()
+
+
+def _host_planes(n_tok, kvh, hd, cfg, step=0):
+    """Pinned K and V planes [n_tok][kvh][hd] bf16 N(0,1)."""
+    row = kvh * hd * 2
+    buf = kvt.HostBuffer(2 * n_tok * row)
+    planes = buf.numpy(np.uint16, (2, n_tok, kvh, hd))
+    step_rows = 1 << 16
+    for p, purpose in enumerate((synth.P_K, synth.P_V)):
+        g = synth.rng(cfg, purpose, step)
+        for t0 in range(0, n_tok, step_rows):
+            t1 = min(n_tok, t0 + step_rows)
+            planes[p, t0:t1] = synth.bf16_normal(g, (t1 - t0, kvh, hd))
+    return buf, planes
+
+
+def test_gather_blocks_bit_exact_with_table_and_negative_ids(gpu):
+    n_tok, kvh, hd, bt, k = 64 * 300, 8, 128, 64, 32
+    buf, planes = _host_planes(n_tok, kvh, hd, 4, 11)
+    n_blocks = n_tok // bt
+    g = synth.rng(4, synth.P_MISC, 12)
+    ids = np.stack([np.sort(g.permutation(n_blocks)[:k]) for _ in range(kvh)]).astype(np.int32)
+    ids[3, 20:] = -1
+    ids[4, 31] = n_blocks + 5                        # outside the planes: skipped
+    table = g.permutation(n_blocks).astype(np.int32)
+    for tab in (None, table):
+        out = torch.full((2, kvh, k * bt, hd), 0x1234, dtype=torch.int16, device=gpu)
+        kvt.kvt_gather_blocks(buf.dev, buf.dev + n_tok * kvh * hd * 2, n_tok, kvh, hd, 2,
+                              kvh * hd * 2, None if tab is None else torch.from_numpy(tab).to(gpu),
+                              bt, torch.from_numpy(ids).to(gpu), k, out[0], out[1])
+        torch.cuda.synchronize()
+        ids_o = ids.copy()
+        ids_o[4, 31] = -1
+        canary = np.full((kvh, k * bt, hd * 2), 0, dtype=np.uint8)
+        canary.view(np.uint16)[:] = 0x1234
+        ko, vo = oracle.gather(planes[0].view(np.uint8), planes[1].view(np.uint8), n_tok, kvh,
+                               hd, 2, kvh * hd * 2, ids_o, bt, block_table=tab,
+                               k_out=canary.copy(), v_out=canary.copy())
+        got = out.cpu().numpy().view(np.uint8).reshape(2, kvh, k * bt, hd * 2)
+        assert np.array_equal(got[0], ko) and np.array_equal(got[1], vo)
+    del planes
+    buf.free()
+
+
+def _decode_inputs(n_qh, kvh, n_kv, fmt, seed):
+    g = synth.rng(4, synth.P_Q, seed)
+    gen = synth.bf16_normal if fmt == kvt.BF16 else synth.f16_normal
+    return gen(g, (n_qh, 128)), gen(g, (kvh, n_kv, 128)), gen(g, (kvh, n_kv, 128))
+
+
+def _run_decode(q, k, v, fmt, dev, n_valid=None, scale=None):
+    n_qh, hd = q.shape
+    kvh, n_kv, _ = k.shape
+    scale = 1 / math.sqrt(hd) if scale is None else scale
+    out = torch.full((n_qh, hd), float("nan"), dtype=torch.float32, device=dev)
+    ws_bytes = kvt.kvt_attn_decode_ws_bytes(n_qh, hd, n_kv)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    nv = None if n_valid is None else torch.tensor(n_valid, dtype=torch.int32, device=dev)
+    kvt.kvt_attn_decode(_u16(q, dev), n_qh, kvh, hd, fmt, _u16(k, dev), _u16(v, dev), n_kv, nv,
+                        scale, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    ref = oracle.attn_decode(q, k, v, oracle.BF16 if fmt == kvt.BF16 else oracle.F16, scale,
+                             n_valid=n_valid)
+    return out.cpu().numpy().astype(np.float64), ref
+
+
+@pytest.mark.parametrize("n_qh,kvh,n_kv,fmt", [(64, 8, 2048, kvt.BF16), (64, 8, 2000, kvt.BF16),
+                                               (64, 8, 2048, kvt.F16), (8, 8, 300, kvt.BF16),
+                                               (32, 2, 1000, kvt.F16), (12, 4, 64, kvt.BF16),
+                                               (16, 1, 4096, kvt.BF16)])
+def test_decode_attention_within_tolerance(gpu, n_qh, kvh, n_kv, fmt):
+    q, k, v = _decode_inputs(n_qh, kvh, n_kv, fmt, n_qh * 7 + n_kv)
+    got, ref = _run_decode(q, k, v, fmt, gpu)
+    err = np.max(np.abs(got - ref))
+    assert err <= TOL, err
+
+
+def test_decode_attention_valid_counts_and_degenerate_cases(gpu):
+    q, k, v = _decode_inputs(64, 8, 2048, kvt.BF16, 99)
+    nv = [2048, 1280, 0, 1, 63, 64, 65, 2047]
+    got, ref = _run_decode(q, k, v, kvt.BF16, gpu, n_valid=nv)
+    assert np.max(np.abs(got - ref)) <= TOL
+    assert (got[16:24] == 0).all()                           # head with no valid key
+    assert np.array_equal(got[24:32], np.repeat(ref[24:25], 8, 0))   # one key: that value row
+    # all keys equal -> mean of V; a peaked softmax (large scale) still within tolerance
+    k_eq = np.repeat(k[:, :1], 2048, axis=1)
+    got, ref = _run_decode(q, k_eq, v, kvt.BF16, gpu)
+    assert np.max(np.abs(got - ref)) <= TOL
+    got, ref = _run_decode(q, k, v, kvt.BF16, gpu, scale=2.0)
+    assert np.max(np.abs(got - ref)) <= TOL
+    got, ref = _run_decode(q, k[:, :0], v[:, :0], kvt.BF16, gpu)     # no keys at all
+    assert (got == 0).all() and (ref == 0).all()
+
+
+@pytest.mark.parametrize("ctx", [262144, 1048576])
+def test_decode_step_full_geometry(gpu, ctx):
+    """One decode step at full size: pooled plane in HBM, K/V planes in pinned host memory,
+    score + top-32 per KV head, gather host -> HBM, GQA attention with 64 query heads.
+    Ids and gathered bytes bit-exact; attention within 2e-3 of the fp64 oracle."""
+    kvh, hd, bt, k, n_qh = 8, 128, 64, 32, 64
+    n_blocks = ctx // bt
+    buf, planes = _host_planes(ctx, kvh, hd, 4, ctx)
+    pooled = synth.f16_normal(synth.rng(4, synth.P_POOLED, ctx), (n_blocks, 128))
+    q_idx = synth.f16_normal(synth.rng(4, synth.P_QIDX, ctx), (kvh, 128))
+    q = synth.bf16_normal(synth.rng(4, synth.P_Q, ctx), (n_qh, hd))
+
+    ws_t = kvt.kvt_index_topk_ws_bytes(n_blocks, kvh, k)
+    ws_d = kvt.kvt_attn_decode_ws_bytes(n_qh, hd, k * bt)
+    ws = torch.empty(ws_t + ws_d, dtype=torch.uint8, device=gpu)
+    ids = torch.empty((kvh, k), dtype=torch.int32, device=gpu)
+    kg = torch.empty((2, kvh, k * bt, hd), dtype=torch.int16, device=gpu)
+    out = torch.empty((n_qh, hd), dtype=torch.float32, device=gpu)
+    kvt.kvt_index_topk(_u16(pooled, gpu), n_blocks, 128, _u16(q_idx, gpu), kvh, k, ids, None,
+                       ws, ws_t)
+    kvt.kvt_gather_blocks(buf.dev, buf.dev + ctx * kvh * hd * 2, ctx, kvh, hd, 2, kvh * hd * 2,
+                          None, bt, ids, k, kg[0], kg[1])
+    kvt.kvt_attn_decode(_u16(q, gpu), n_qh, kvh, hd, kvt.BF16, kg[0], kg[1], k * bt, None,
+                        1 / math.sqrt(hd), out, ws[ws_t:], ws_d)
+    torch.cuda.synchronize()
+
+    ref_ids = oracle.topk(oracle.index_scores(pooled, q_idx), k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ko, vo = oracle.gather(planes[0].view(np.uint8), planes[1].view(np.uint8), ctx, kvh, hd, 2,
+                           kvh * hd * 2, ref_ids, bt)
+    got = kg.cpu().numpy().view(np.uint8).reshape(2, kvh, k * bt, hd * 2)
+    assert np.array_equal(got[0], ko) and np.array_equal(got[1], vo)
+    ref = oracle.attn_decode(q, ko.view(np.uint16).reshape(kvh, k * bt, hd),
+                             vo.view(np.uint16).reshape(kvh, k * bt, hd), oracle.BF16,
+                             1 / math.sqrt(hd))
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
+    del planes
+    buf.free()
