@@ -1,0 +1,497 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiered KV-cache hot path on one MI355X.
+
+Headline workload: one top-k sparse decode step at 262,144 tokens of context, batch 1 --
+score the pooled indexer plane (fp16 [4096][128], HBM) for 8 KV heads, select the top 32
+blocks per head, gather their K/V rows (8 KV heads x 128 dim bf16, 64-token blocks) from pinned
+host planes into HBM, and run GQA decode attention for 64 query heads.  Every step uses a fresh
+query pair, hence a fresh selection (no host data can be served from GPU caches).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--ctx 262144] [--suite]
+
+Prints ONE JSON line.  ``value`` = host->HBM KV gather GB/s over whole steps (8,388,608 bytes
+gathered per step / step time).  ``roofline`` is the gather kernel itself (HIP events on the
+launch stream) against the PCIe Gen5 x16 per-direction peak; ``cpu_baseline`` is the CPU
+oracle running the same step on the host cores.  ``--suite`` adds the other workloads
+(one-layer and 32-layer swaps, the small-page kernel/SDMA sweep, tiered prefill).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+GB = 1e9
+PCIE5_X16_PEAK_GBS = 64.0   # AMD: PCIe 5.0 x16, 128 GB/s bidirectional -> 64 GB/s per direction
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--ctx", type=int, default=262144)
+    p.add_argument("--layout", default="block_head_major",
+                   choices=["block_head_major", "token_major"],
+                   help="host K/V plane layout (block-local head-major, or token-major)")
+    p.add_argument("--suite", action="store_true", help="also measure the other workloads")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="bound on the CPU-oracle baseline's wall time")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on the stream the work is launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record(self.stream)
+
+    def stop_ms(self):
+        self.b.record(self.stream)
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def measure_link_peaks(torch, kvt, dev, host_buf, nbytes, reps=5):
+    """Best-of-reps SDMA copy of nbytes between pinned host memory and HBM, both directions."""
+    stream = torch.cuda.current_stream()
+    hbm = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    t = Timer(torch, stream)
+    best_h2d = best_d2h = 0.0
+    tb = kvt.HostBuffer(24)
+    import numpy as np
+    tab = tb.numpy(np.uint64, (3, 1))
+    for _ in range(reps):
+        t.start()
+        kvt.kvt_stage_tail(host_buf.dev, nbytes, 0, 1, hbm, kvt.COPY_SDMA)
+        best_h2d = max(best_h2d, nbytes / (t.stop_ms() * 1e-3) / GB)
+    tab[0, 0], tab[1, 0], tab[2, 0] = hbm.data_ptr(), host_buf.dev, nbytes
+    for _ in range(reps):
+        t.start()
+        kvt.kvt_swap_blocks(tab[0], tab[1], tab[2], 1, kvt.D2H, kvt.COPY_SDMA)
+        best_d2h = max(best_d2h, nbytes / (t.stop_ms() * 1e-3) / GB)
+    # HBM: device-to-device copy of the same buffer size (reads + writes count)
+    other = torch.empty_like(hbm)
+    best_hbm = 0.0
+    for _ in range(reps):
+        t.start()
+        other.copy_(hbm)
+        best_hbm = max(best_hbm, 2 * nbytes / (t.stop_ms() * 1e-3) / GB)
+    del hbm, other
+    tb.free()
+    return {"h2d_sdma_gbs": round(best_h2d, 2), "d2h_sdma_gbs": round(best_d2h, 2),
+            "hbm_copy_gbs": round(best_hbm, 1), "bytes": nbytes}
+
+
+class DecodeWorkload:
+    """Top-k sparse decode at one context length: all inputs resident before timing starts."""
+
+    KVH, HD, BT, K, NQH = 8, 128, 64, 32, 64
+
+    # (block, head, token) byte strides of the host planes, per layout
+    LAYOUTS = {
+        # [block][head][token][dim]: each (block, head) is one contiguous 16 KiB run
+        "block_head_major": lambda kvh, hd, bt: (kvh * bt * hd * 2, bt * hd * 2, hd * 2),
+        # [token][head][dim], the pages' layout: 256-byte runs at a 2 KiB stride
+        "token_major": lambda kvh, hd, bt: (bt * kvh * hd * 2, hd * 2, kvh * hd * 2),
+    }
+
+    def __init__(self, torch, kvt, synth, dev, ctx, n_sets, layout="block_head_major"):
+        import numpy as np
+        self.torch, self.kvt, self.dev, self.ctx = torch, kvt, dev, ctx
+        kvh, hd, bt, k = self.KVH, self.HD, self.BT, self.K
+        self.n_blocks = ctx // bt
+        self.row = kvh * hd * 2
+        self.layout = layout
+        self.strides = self.LAYOUTS[layout](kvh, hd, bt)
+        t0 = time.time()
+        self.host = kvt.HostBuffer(2 * ctx * self.row)
+        planes = self.host.numpy(np.uint16, (2, ctx, kvh, hd))
+        for p, purpose in enumerate((synth.P_K, synth.P_V)):
+            g = synth.rng(4, purpose, ctx)
+            for t0_ in range(0, ctx, 1 << 16):
+                t1_ = min(ctx, t0_ + (1 << 16))
+                planes[p, t0_:t1_] = synth.bf16_normal(g, (t1_ - t0_, kvh, hd))
+        self.planes = planes
+        log(f"ctx={ctx}: host K/V planes {2 * ctx * self.row / 2**30:.2f} GiB pinned "
+            f"in {time.time() - t0:.1f}s")
+        self.pooled_np = synth.f16_normal(synth.rng(4, synth.P_POOLED, ctx), (self.n_blocks, 128))
+        self.pooled = torch.from_numpy(self.pooled_np.view(np.int16)).to(dev)
+        self.n_sets = n_sets
+        self.qidx_np = synth.f16_normal(synth.rng(4, synth.P_QIDX, ctx), (n_sets, kvh, 128))
+        self.q_np = synth.bf16_normal(synth.rng(4, synth.P_Q, ctx), (n_sets, self.NQH, hd))
+        self.qidx = torch.from_numpy(self.qidx_np.view(np.int16)).to(dev)
+        self.q = torch.from_numpy(self.q_np.view(np.int16)).to(dev)
+        self.ws_t = kvt.kvt_index_topk_ws_bytes(self.n_blocks, kvh, k)
+        self.ws_d = kvt.kvt_attn_decode_ws_bytes(self.NQH, hd, k * bt)
+        self.ws = torch.empty(self.ws_t + self.ws_d + 256, dtype=torch.uint8, device=dev)
+        self.ids = torch.empty((kvh, k), dtype=torch.int32, device=dev)
+        self.kv = torch.empty((2, kvh, k * bt, hd), dtype=torch.int16, device=dev)
+        self.out = torch.empty((self.NQH, hd), dtype=torch.float32, device=dev)
+        self.scale = 1.0 / math.sqrt(hd)
+        self.gather_bytes = 2 * kvh * k * bt * hd * 2   # K and V: 8,388,608 at these shapes
+
+    def topk(self, i):
+        kvt = self.kvt
+        kvt.kvt_index_topk(self.pooled, self.n_blocks, 128, self.qidx[i % self.n_sets], self.KVH,
+                           self.K, self.ids, None, self.ws, self.ws_t)
+
+    def gather(self):
+        kvt = self.kvt
+        kvt.kvt_gather_blocks(self.host.dev, self.host.dev + self.ctx * self.row, self.n_blocks,
+                              self.KVH, self.HD, 2, *self.strides, None, self.BT, self.ids, self.K,
+                              self.kv[0], self.kv[1])
+
+    def attend(self, i):
+        kvt = self.kvt
+        kvt.kvt_attn_decode(self.q[i % self.n_sets], self.NQH, self.KVH, self.HD, kvt.BF16,
+                            self.kv[0], self.kv[1], self.K * self.BT, None, self.scale, self.out,
+                            self.ws[self.ws_t + 128:], self.ws_d)
+
+    def step(self, i):
+        self.topk(i)
+        self.gather()
+        self.attend(i)
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        # whole-step timing: host clock and events around exactly `steps` steps
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            self.step(warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = ev0.elapsed_time(ev1)
+        # per-kernel timing pass: events bracketing each launch on the same stream
+        parts = {"topk": [], "gather": [], "attn": []}
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for i in range(steps):
+            e = evs[i]
+            e[0].record(stream)
+            self.topk(warmup + steps + i)
+            e[1].record(stream)
+            self.gather()
+            e[2].record(stream)
+            self.attend(warmup + steps + i)
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        for e in evs:
+            parts["topk"].append(e[0].elapsed_time(e[1]))
+            parts["gather"].append(e[1].elapsed_time(e[2]))
+            parts["attn"].append(e[2].elapsed_time(e[3]))
+        avg = {k: sum(v) / len(v) for k, v in parts.items()}
+        return {"wall_s": wall, "event_ms": ev_ms, "ms_per_step": max(wall * 1e3, ev_ms) / steps,
+                "part_ms": avg}
+
+    def free(self):
+        self.planes = None
+        self.host.free()
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle's decode step (fp64 scoring, full-sort top-k, memcpy gather from the same
+    pinned host planes, fp64 attention) on the host cores, for a bounded wall time."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    threads = min(threads, os.cpu_count() or threads)
+    kvh, hd, bt, k = wl.KVH, wl.HD, wl.BT, wl.K
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        i = n % wl.n_sets
+        s = oracle.index_scores(wl.pooled_np, wl.qidx_np[i], threads=threads)
+        ids = oracle.topk(s, k)
+        ko, vo = oracle.gather(wl.planes[0].view(np.uint8), wl.planes[1].view(np.uint8),
+                               wl.n_blocks, kvh, hd, 2, wl.strides, ids, bt)
+        oracle.attn_decode(wl.q_np[i], ko.view(np.uint16).reshape(kvh, k * bt, hd),
+                           vo.view(np.uint16).reshape(kvh, k * bt, hd), oracle.BF16, wl.scale,
+                           threads=threads)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or (n >= 3 and el * (n + 1) / n > seconds * 1.5):
+            break
+    steps_s = n / el
+    return {"value": round(wl.gather_bytes * steps_s / GB, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "steps_per_s": round(steps_s, 3),
+            "sample": f"{n} oracle decode steps at {wl.ctx} ctx (fp64 scoring of {wl.n_blocks} "
+                      f"blocks x 8 heads, full-sort top-32, memcpy gather of 8 MiB, fp64 GQA "
+                      f"attention over 2048 keys x 64 heads) in {el:.1f}s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by layer or KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from hbm_kv_cache_amd import kvt, synth
+    kvt.load()    # no fallback: the HIP library must be there
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    dev = torch.device("cuda:0")
+    log("device", torch.cuda.get_device_name(0))
+
+    n_sets = args.warmup + 2 * args.steps
+    wl = DecodeWorkload(torch, kvt, synth, dev, args.ctx, n_sets, args.layout)
+    peaks = measure_link_peaks(torch, kvt, dev, wl.host, 1 << 30)
+    log("link peaks", peaks)
+    r = wl.run(args.steps, args.warmup)
+    log("decode", r)
+    # the same planes read through the other layout's strides: context for the layout choice
+    other = "token_major" if args.layout == "block_head_major" else "block_head_major"
+    keep = wl.strides
+    wl.strides = wl.LAYOUTS[other](wl.KVH, wl.HD, wl.BT)
+    r_other = wl.run(max(20, args.steps // 4), 5)
+    wl.strides = keep
+    log(f"decode with {other} host planes", r_other)
+
+    ms = r["ms_per_step"]
+    gather_ms = r["part_ms"]["gather"]
+    achieved = wl.gather_bytes / (gather_ms * 1e-3) / GB
+    value = wl.gather_bytes / (ms * 1e-3) / GB
+    line = {
+        "metric": "host->HBM KV gather GB/s (% PCIe peak); tiered decode tok/s at 262k ctx",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V in pinned host memory, fp16 pooled plane)",
+        "config": {"workload": f"top-k sparse decode step, batch 1, ctx {args.ctx}: score "
+                               f"{wl.n_blocks} pooled blocks x 8 KV heads, top-32 per head, "
+                               "gather K/V (8 heads x 128 bf16, 64-token blocks) host->HBM, "
+                               "GQA attention 64 q heads",
+                   "ctx": args.ctx, "kv_heads": 8, "head_dim": 128, "q_heads": 64,
+                   "block_tokens": 64, "topk": 32, "gather_bytes_per_step": wl.gather_bytes,
+                   "host_layout": args.layout},
+        "decode_tok_s": round(1e3 / ms, 2),
+        f"{other}_host_layout": {
+            "ms_per_step": round(r_other["ms_per_step"], 5),
+            "decode_tok_s": round(1e3 / r_other["ms_per_step"], 2),
+            "gather_kernel_gbs": round(wl.gather_bytes / (r_other["part_ms"]["gather"] * 1e-3) / GB, 3)},
+        "pct_pcie_peak": round(100 * value / PCIE5_X16_PEAK_GBS, 2),
+        "pct_measured_h2d_peak": round(100 * value / peaks["h2d_sdma_gbs"], 2),
+        "part_ms": {k: round(v, 5) for k, v in r["part_ms"].items()},
+        "link_peaks": peaks,
+        "roofline": {"bound": "pcie", "kernel": "gather_kernel", "achieved": round(achieved, 3),
+                     "peak": PCIE5_X16_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PCIE5_X16_PEAK_GBS, 4),
+                     "peak_measured_h2d": peaks["h2d_sdma_gbs"],
+                     "frac_measured": round(achieved / peaks["h2d_sdma_gbs"], 4),
+                     "bytes_per_launch": wl.gather_bytes, "avg_launch_ms": round(gather_ms, 5),
+                     "traffic": None},
+    }
+    if args.suite:
+        line["suite"] = run_suite(torch, kvt, synth, dev, wl, args, peaks)
+    if not args.no_cpu:
+        log("cpu baseline ...")
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    wl.free()
+    print(json.dumps(line), flush=True)
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def _swap_rate(torch, kvt, t, tab, n, direction, mode, nbytes):
+    t.start()
+    kvt.kvt_swap_blocks(tab[0], tab[1], tab[2], n, direction, mode)
+    ms = t.stop_ms()
+    return nbytes / (ms * 1e-3) / GB, ms
+
+
+def suite_one_layer(torch, kvt, synth, dev, peaks, reps=20):
+    """One layer: K and V planes of 256 x 32 KiB pages in pinned memory; 64 fresh random block
+    ids per rep, host -> HBM (load) and HBM -> host (store), kernel and SDMA."""
+    import numpy as np
+    nb, page, n = 256, 16 * 8 * 128 * 2, 64
+    host = kvt.HostBuffer(2 * nb * page)
+    hv = host.numpy(np.uint16, (2, nb, page // 2))
+    hv[0] = synth.f16_normal(synth.rng(1, synth.P_K), (nb, page // 2))
+    hv[1] = synth.f16_normal(synth.rng(1, synth.P_V), (nb, page // 2))
+    hbm = torch.empty((2, nb, page), dtype=torch.uint8, device=dev)
+    tb = kvt.HostBuffer(3 * 8 * 2 * n)
+    tab = tb.numpy(np.uint64, (3, 2 * n))
+    t = Timer(torch, torch.cuda.current_stream())
+    out = {}
+    for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma")):
+        for direction, dname in ((kvt.H2D, "h2d"), (kvt.D2H, "d2h")):
+            rates = []
+            for r in range(reps):
+                hid = synth.permutation(synth.rng(1, synth.P_PERM_SRC, r), nb)[:n]
+                gid = synth.permutation(synth.rng(1, synth.P_PERM_DST, r), nb)[:n]
+                for p in range(2):
+                    hs = tab[0 if direction == kvt.H2D else 1, p * n:]
+                    gs = tab[1 if direction == kvt.H2D else 0, p * n:]
+                    kvt.kvt_sub_block_ptrs(host.dev + p * nb * page, page, page, hid, n, 1, 0, hs, n)
+                    kvt.kvt_sub_block_ptrs(hbm.data_ptr() + p * nb * page, page, page, gid, n, 1, 0,
+                                           gs, n)
+                tab[2] = page
+                rates.append(_swap_rate(torch, kvt, t, tab, 2 * n, direction, mode, 2 * n * page)[0])
+            peak = peaks["h2d_sdma_gbs"] if direction == kvt.H2D else peaks["d2h_sdma_gbs"]
+            out[f"{dname}_{mname}_gbs"] = round(_median(rates), 2)
+            out[f"{dname}_{mname}_pct_measured_peak"] = round(100 * _median(rates) / peak, 1)
+    out["bytes_per_direction"] = 2 * n * page
+    del hv
+    host.free()
+    tb.free()
+    return out
+
+
+def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
+    """32 layers x (K, V) = 64 tensors: HBM [8192][32 KiB] each; host rows of 4 pages + 4 KiB
+    pad (2048 rows, 135,168 B stride); 4096 random blocks per tensor with a random skip on the
+    first host chunk (blocks_per_chunk 4): 8 GiB per direction."""
+    import numpy as np
+    tensors, gblocks, bpc, page, pad, n = 64, 8192, 4, 32768, 4096, 4096
+    hrows = gblocks // bpc
+    stride = bpc * page + pad
+    t0 = time.time()
+    host = kvt.HostBuffer(tensors * hrows * stride)
+    hb = host.numpy(np.uint8, (tensors * hrows * stride,))
+    seed_block = np.empty(1 << 28, dtype=np.uint8)
+    synth.fill_random_bytes(synth.rng(2, synth.P_K), seed_block)
+    for o in range(0, hb.size, seed_block.size):
+        m = min(seed_block.size, hb.size - o)
+        hb[o:o + m] = seed_block[:m]
+    del seed_block
+    hbm = torch.empty((tensors, gblocks, page), dtype=torch.uint8, device=dev)
+    log(f"32-layer planes: {host.nbytes / 2**30:.1f} GiB pinned + {hbm.numel() / 2**30:.1f} GiB HBM "
+        f"in {time.time() - t0:.1f}s")
+    tb = kvt.HostBuffer(3 * 8 * tensors * n)
+    tab = tb.numpy(np.uint64, (3, tensors * n))
+    t = Timer(torch, torch.cuda.current_stream())
+    out = {}
+    g = synth.rng(2, synth.P_SKIP)
+    for direction, dname in ((kvt.H2D, "h2d"), (kvt.D2H, "d2h")):
+        for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma")):
+            rates = []
+            for r in range(reps):
+                skip = int(g.integers(0, bpc))
+                nch = kvt.kvt_chunks_consumed(n, skip, bpc)
+                chunks = synth.permutation(synth.rng(2, synth.P_PERM_SRC, r), hrows)[:nch]
+                gids = synth.permutation(synth.rng(2, synth.P_PERM_DST, r), gblocks)[:n]
+                hrow = tab[0 if direction == kvt.H2D else 1]
+                grow = tab[1 if direction == kvt.H2D else 0]
+                for x in range(tensors):
+                    kvt.kvt_sub_block_ptrs(host.dev + x * hrows * stride, stride, page, chunks, nch,
+                                           bpc, skip, hrow[x * n:], n)
+                    kvt.kvt_sub_block_ptrs(hbm.data_ptr() + x * gblocks * page, page, page, gids,
+                                           n, 1, 0, grow[x * n:], n)
+                tab[2] = page
+                rate, ms = _swap_rate(torch, kvt, t, tab, tensors * n, direction, mode,
+                                      tensors * n * page)
+                rates.append(rate)
+                log(f"  32-layer {dname} {mname} rep {r}: {rate:.2f} GB/s ({ms:.1f} ms)")
+            peak = peaks["h2d_sdma_gbs"] if direction == kvt.H2D else peaks["d2h_sdma_gbs"]
+            out[f"{dname}_{mname}_gbs"] = round(_median(rates), 2)
+            out[f"{dname}_{mname}_pct_measured_peak"] = round(100 * _median(rates) / peak, 1)
+    out["bytes_per_direction"] = tensors * n * page
+    del hb
+    del hbm
+    host.free()
+    tb.free()
+    torch.cuda.empty_cache()
+    return out
+
+
+def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
+    """65,536 pages in random scattered order host -> HBM, page sizes 512 B .. 64 KiB, kernel
+    loads vs the copy engines; plus 2 KiB pages at 8 mod 16 alignment."""
+    import numpy as np
+    n = 65536
+    sizes = [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536]
+    host = kvt.HostBuffer(n * sizes[-1] + 64)
+    hb = host.numpy(np.uint8)
+    synth.fill_random_bytes(synth.rng(3, synth.P_K), hb[:1 << 28])
+    for o in range(1 << 28, hb.size, 1 << 28):
+        m = min(1 << 28, hb.size - o)
+        hb[o:o + m] = hb[:m]
+    hbm = torch.empty(n * sizes[-1], dtype=torch.uint8, device=dev)
+    tb = kvt.HostBuffer(3 * 8 * n)
+    tab = tb.numpy(np.uint64, (3, n))
+    t = Timer(torch, torch.cuda.current_stream())
+    out = {"pages": n, "sweep": []}
+    cross = None
+    for size in sizes + [2048]:
+        off = 8 if (size == 2048 and len(out["sweep"]) == len(sizes)) else 0
+        row = {"page_bytes": size, "host_offset_mod16": off}
+        for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma")):
+            rates = []
+            for r in range(reps):
+                src = synth.permutation(synth.rng(3, synth.P_PERM_SRC, r), n)
+                dst = synth.permutation(synth.rng(3, synth.P_PERM_DST, r), n)
+                kvt.kvt_sub_block_ptrs(host.dev + off, size + (8 if off else 0), size, src, n, 1, 0,
+                                       tab[0], n)
+                kvt.kvt_sub_block_ptrs(hbm.data_ptr(), size, size, dst, n, 1, 0, tab[1], n)
+                tab[2] = size
+                rates.append(_swap_rate(torch, kvt, t, tab, n, kvt.H2D, mode, n * size)[0])
+            row[f"{mname}_gbs"] = round(_median(rates), 2)
+        log(f"  small pages {row}")
+        out["sweep"].append(row)
+        if not off and cross is None and row["sdma_gbs"] >= row["kernel_gbs"]:
+            cross = size
+    out["h2d_crossover_bytes"] = cross
+    del hb
+    del hbm
+    host.free()
+    tb.free()
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_suite(torch, kvt, synth, dev, wl, args, peaks):
+    out = {}
+    log("suite: one-layer swap")
+    out["swap_1_layer"] = suite_one_layer(torch, kvt, synth, dev, peaks)
+    log("suite: small pages")
+    out["small_pages"] = suite_small_pages(torch, kvt, synth, dev, peaks)
+    log("suite: 32-layer swap")
+    out["swap_32_layers"] = suite_32_layers(torch, kvt, synth, dev, peaks)
+    log("suite: decode at 1,048,576")
+    w1m = DecodeWorkload(torch, kvt, synth, dev, 1 << 20, args.warmup + 2 * args.steps)
+    r = w1m.run(args.steps, args.warmup)
+    out["decode_1m"] = {"ms_per_step": round(r["ms_per_step"], 5),
+                        "decode_tok_s": round(1e3 / r["ms_per_step"], 2),
+                        "gather_gbs_whole_step": round(w1m.gather_bytes / (r["ms_per_step"] * 1e-3) / GB, 3),
+                        "part_ms": {k: round(v, 5) for k, v in r["part_ms"].items()}}
+    w1m.free()
+    return out
+
+
+if __name__ == "__main__":
+    main()

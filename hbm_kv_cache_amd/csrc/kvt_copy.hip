@@ -111,10 +111,13 @@ __global__ __launch_bounds__(256) void copy_span_kernel(uint64_t src, uint64_t d
     wave_copy_chunk(src + off, dst + off, len, lane);
 }
 
-// AUTO policy: kernel for pages below the threshold (vLLM-CPU _select_swap_blocks_fn keeps the
-// kernel for small 8-byte-multiple pages and the copy engines otherwise).  Defaults are the
-// crossover measured on MI355X by the small-page sweep; stores default to the copy engines.
-std::atomic<uint64_t> g_threshold[2] = {{1u << 20}, {0}};
+// AUTO policy: vLLM-CPU _select_swap_blocks_fn keeps a kernel for small 8-byte-multiple pages
+// and the copy engines otherwise.  On MI355X the kernel path measured at or above the copy
+// engines at every page size from 512 B to 64 KiB and in both directions (56.9 GB/s host->HBM
+// and 55.1 GB/s HBM->host on 32 KiB pages; per-descriptor SDMA submission costs microseconds
+// each), so AUTO takes the kernel whenever it is eligible.  kvt_set_copy_threshold moves the
+// switch point per direction.
+std::atomic<uint64_t> g_threshold[2] = {{~0ull}, {~0ull}};
 
 // hipMemcpyBatchAsync is resolved at run time from the HIP runtime already in the process (the
 // one that owns the caller's streams); runtimes that predate it get per-copy submission.

@@ -10,7 +10,8 @@
 //   products are exact in fp32, accumulation is fp32.  Softmax and P*V stay in fp32 on the
 //   vector ALUs: with at most 16 query rows per KV head the PV product is tiny, and keeping
 //   the probabilities in fp32 avoids rounding them to 16 bits.
-// decode_merge: one thread per (query head, dim) folds the chunks in index order.
+// decode_merge: one thread per (query head, dim) folds the chunks in index order: the global
+//   max first, then every chunk rescaled by e^(m_c - max) -- the same fold, one rescale each.
 #include <cmath>
 
 #include "kvt_internal.h"
@@ -50,41 +51,43 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
                                                      float scale_log2, float *__restrict__ part)
 {
     __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
-    __shared__ float ps[16][kKeys + 1];
+    __shared__ __align__(16) float ps[kKeys][16];   // probabilities, key-major
     const int lane = threadIdx.x;
     const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x;
     const int64_t key0 = (int64_t)c * kKeys;
-    int64_t nv = n_valid ? (int64_t)n_valid[h] : n_kv;
-    nv = nv < n_kv ? nv : n_kv;
     const int g = lane >> 4, col = lane & 15;
 
-    // A operands: query rows (row = col), d = ks*32 + 8g .. +7 ; rows >= group are zero
+    // Every load below is unconditional, from a clamped (always valid) address, so all of them
+    // are in flight together; out-of-range rows are zeroed or masked afterwards.
+    const int qrow = col < group ? col : group - 1;
+    const uint16_t *qh = q + ((int64_t)h * group + qrow) * kHd + 8 * g;
     uint4 qa[4];
-    const uint16_t *qh = q + ((int64_t)h * group + col) * kHd;
 #pragma unroll
     for (int ks = 0; ks < 4; ks++)
-        qa[ks] = col < group ? *reinterpret_cast<const uint4 *>(qh + ks * 32 + 8 * g)
-                             : make_uint4(0, 0, 0, 0);
-
-    // B operands: key row key0 + nt*16 + col, d = ks*32 + 8g .. +7
+        qa[ks] = *reinterpret_cast<const uint4 *>(qh + ks * 32);
     const uint16_t *kh = k + (int64_t)h * n_kv * kHd;
     uint4 kb[4][4];
 #pragma unroll
     for (int nt = 0; nt < 4; nt++) {
-        const int64_t key = key0 + nt * 16 + col;
+        const int64_t key = min(key0 + nt * 16 + col, n_kv - 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
-            kb[nt][ks] = key < n_kv ? *reinterpret_cast<const uint4 *>(kh + key * kHd + ks * 32 + 8 * g)
-                                    : make_uint4(0, 0, 0, 0);
+            kb[nt][ks] = *reinterpret_cast<const uint4 *>(kh + key * kHd + ks * 32 + 8 * g);
     }
-    // V chunk -> LDS: 64 rows x 16 words of 16 bytes
     const uint16_t *vh = v + (int64_t)h * n_kv * kHd;
     uint4 vr[16];
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
-        vr[j] = key0 + row < n_kv ? *reinterpret_cast<const uint4 *>(vh + (key0 + row) * kHd + cw * 8)
-                                  : make_uint4(0, 0, 0, 0);
+        const int64_t key = min(key0 + row, n_kv - 1);
+        vr[j] = *reinterpret_cast<const uint4 *>(vh + key * kHd + cw * 8);
+    }
+    int64_t nv = n_valid ? (int64_t)n_valid[h] : n_kv;
+    nv = nv < n_kv ? nv : n_kv;
+    if (col >= group) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            qa[ks] = make_uint4(0, 0, 0, 0);
     }
 
     f32x4 s[4];
@@ -95,10 +98,13 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
         for (int ks = 0; ks < 4; ks++)
             s[nt] = mfma16x16x32<kBf16>(qa[ks], kb[nt][ks], s[nt]);
     }
+    // V rows of keys that take no part are zeroed: their probability is 0, but 0 * NaN is not
+    // (rows past n_valid may hold anything, e.g. slots a gather skipped)
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
-        *reinterpret_cast<uint4 *>(vs + row * kVPitch + cw * 16) = vr[j];
+        const uint4 val = key0 + row < nv ? vr[j] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(vs + row * kVPitch + cw * 16) = val;
     }
 
     // lane holds S[row 4g+i][key nt*16 + col]; scale into the log2 domain, mask invalid keys
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
 #pragma unroll
         for (int nt = 0; nt < 4; nt++) {
             const float p = m[i] == -INFINITY ? 0.f : exp2f(s[nt][i] - m[i]);
-            ps[4 * g + i][nt * 16 + col] = p;
+            ps[nt * 16 + col][4 * g + i] = p;
             l[i] += p;
         }
     }
@@ -141,26 +147,30 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
 #pragma unroll
     for (int r = 0; r < 16; r++)
         o[r][0] = o[r][1] = 0.f;
+    const int nq4 = (group + 3) >> 2;   // float4 groups of probabilities actually used
+#pragma unroll 4
     for (int key = 0; key < kKeys; key++) {
         const uint32_t pair = *reinterpret_cast<const uint32_t *>(vs + key * kVPitch + lane * 4);
         const float v0 = to_f32((uint16_t)(pair & 0xffff), kBf16);
         const float v1 = to_f32((uint16_t)(pair >> 16), kBf16);
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            if (r < group) {
-                const float p = ps[r][key];
-                o[r][0] = fmaf(p, v0, o[r][0]);
-                o[r][1] = fmaf(p, v1, o[r][1]);
+        for (int q4 = 0; q4 < 4; q4++) {
+            if (q4 < nq4) {
+                const float4 p = *reinterpret_cast<const float4 *>(&ps[key][4 * q4]);
+                const float pr[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    o[4 * q4 + e][0] = fmaf(pr[e], v0, o[4 * q4 + e][0]);
+                    o[4 * q4 + e][1] = fmaf(pr[e], v1, o[4 * q4 + e][1]);
+                }
             }
         }
     }
     float *pb = part + ((int64_t)h * n_chunks + c) * group * (kHd + 2);
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-        if (r < group) {
-            pb[r * (kHd + 2) + 2 * lane] = o[r][0];
-            pb[r * (kHd + 2) + 2 * lane + 1] = o[r][1];
-        }
+        if (r < group)
+            *reinterpret_cast<float2 *>(pb + r * (kHd + 2) + 2 * lane) = make_float2(o[r][0], o[r][1]);
     }
     if (col == 0) {
 #pragma unroll
@@ -174,24 +184,29 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
     }
 }
 
-// grid = n_qh, block = kHd
+// grid = n_qh, block = kHd.  Two passes over the chunks (global max, then the weighted sums),
+// each with independent loads, in chunk order: deterministic.
 __global__ __launch_bounds__(kHd) void decode_merge(const float *__restrict__ part, int group,
                                                     int n_chunks, float *__restrict__ out)
 {
     const int qh = blockIdx.x, d = threadIdx.x;
     const int h = qh / group, r = qh % group;
-    float m = -INFINITY, l = 0.f, acc = 0.f;
-    for (int c = 0; c < n_chunks; c++) {
-        const float *pb = part + (((int64_t)h * n_chunks + c) * group + r) * (kHd + 2);
-        const float mc = pb[kHd];
-        if (mc == -INFINITY)
-            continue;
-        const float mn = fmaxf(m, mc);
-        const float a = m == -INFINITY ? 0.f : exp2f(m - mn);
-        const float b = exp2f(mc - mn);
-        acc = acc * a + pb[d] * b;
-        l = l * a + pb[kHd + 1] * b;
-        m = mn;
+    const float *base = part + ((int64_t)h * n_chunks * group + r) * (kHd + 2);
+    const int64_t cstride = (int64_t)group * (kHd + 2);
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int c = 0; c < n_chunks; c++)
+        M = fmaxf(M, base[c * cstride + kHd]);
+    float acc = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+        for (int c = 0; c < n_chunks; c++) {
+            const float *pb = base + c * cstride;
+            const float mc = pb[kHd];
+            const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
+            acc = fmaf(pb[d], w, acc);
+            l = fmaf(pb[kHd + 1], w, l);
+        }
     }
     out[(int64_t)qh * kHd + d] = l > 0.f ? acc / l : 0.f;
 }

@@ -3,14 +3,22 @@
 // QSA-KVO keeps the pooled indexer plane in HBM because it is scored in full on every step;
 // the top-k of those scores decides which K/V blocks cross the host link.
 //
-// Kernel 1 (score_local_topk): a workgroup takes kChunkBlocks pooled rows, stages them and the
-//   index queries in LDS, evaluates every (block, head) score in fp64 (each fp16*fp16 product
-//   is exact in fp64 and the sum runs in index order, so the value is fully determined), and
-//   keeps each head's best min(k, kChunkBlocks) candidates, found by a segmented bitonic sort
-//   in LDS.  Candidates go to the workspace as (64-bit rank key, block id).
-// Kernel 2 (merge_topk): per head, segments of up to kMergeMax candidates are sorted again and
-//   cut to k; repeated until one segment per head remains, whose ids are then sorted
-//   ascending and written out (-1 for empty slots).
+// Every score is evaluated in fp64 in index order: each fp16*fp16 product is exact in fp64,
+// so the value is fully determined and the selection is reproducible bit for bit.
+//
+// Wavefront path (k <= 32, the decode case):
+//   score_wave_topk -- a workgroup stages 64 pooled rows and the index queries in LDS; lane l
+//     of a wave scores row l for one head, so a head's 64 candidates sit one per lane and a
+//     64-lane bitonic sort over cross-lane shuffles (no LDS, no barriers) leaves the best k in
+//     lanes 0..k-1, written out as a sorted candidate list.
+//   merge_wave_topk -- one workgroup per head; each wave folds candidate lists into its running
+//     best-32 (the running list in lanes 0..31, the incoming list reversed in lanes 32..63:
+//     a bitonic sequence, cleaned in six shuffle steps), then the 16 waves fold pairwise
+//     through LDS, and the winners' ids are sorted ascending by one more lane sort.
+// Generic path (k up to 256):
+//   score_local_topk -- the same scoring over 128-row chunks, candidates cut to min(k, 128) by
+//     a segmented bitonic sort in LDS;  merge_topk -- segments of up to 4096 candidates sorted
+//     in LDS and cut to k, repeated until one segment per head remains.
 //
 // Rank order (a total order, so the result is unique): larger score first, equal scores by
 // lower block id, NaN after every number.  Encoded as a 64-bit key (larger = better) plus id.
@@ -25,6 +33,8 @@ constexpr int kChunkBlocks = 128;     // pooled rows per scoring workgroup
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeMax = 4096;       // candidates per merge workgroup (power of two)
 constexpr uint32_t kNoId = 0xffffffffu;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 __device__ __forceinline__ uint64_t rank_key(double s)
 {
@@ -221,6 +231,198 @@ __global__ __launch_bounds__(kMergeThreads) void merge_topk(
         ids_final[h * k + i] = sid[i] == kNoId ? -1 : (int32_t)sid[i];
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// wavefront path
+// ---------------------------------------------------------------------------------------------
+constexpr int kWaveRows = 64;        // pooled rows per scoring workgroup: one per lane
+constexpr int kWaveK = 32;           // largest k of this path
+constexpr int kMergeWaves = 16;
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src)
+{
+    const uint32_t lo = __shfl((uint32_t)v, src, 64), hi = __shfl((uint32_t)(v >> 32), src, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// compare-exchange with the lane `stride` away; `up` = this pair ends best-first
+__device__ __forceinline__ void wave_cx(uint64_t &key, uint32_t &id, int lane, int stride, bool up)
+{
+    const uint64_t pk = shfl_u64(key, lane ^ stride);
+    const uint32_t pi = __shfl(id, lane ^ stride, 64);
+    const bool lower = (lane & stride) == 0;
+    const bool mine_better = better(key, id, pk, pi);
+    if ((lower == up) != mine_better) {
+        key = pk;
+        id = pi;
+    }
+}
+
+// bitonic sort of the wave's 64 (key, id) pairs, best first
+__device__ __forceinline__ void wave_sort_best_first(uint64_t &key, uint32_t &id, int lane)
+{
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+            wave_cx(key, id, lane, stride, size == 64 || (lane & size) == 0);
+}
+
+// running best-32 (lanes 0..31, best first) merged with a list (lanes 0..31, best first)
+__device__ __forceinline__ void wave_merge32(uint64_t &ck, uint32_t &ci, uint64_t lk, uint32_t li,
+                                             int lane)
+{
+    const uint64_t rk = shfl_u64(lk, 63 - lane);
+    const uint32_t ri = __shfl(li, 63 - lane, 64);
+    if (lane >= 32) {
+        ck = rk;
+        ci = ri;
+    }
+#pragma unroll
+    for (int stride = 32; stride > 0; stride >>= 1)
+        wave_cx(ck, ci, lane, stride, true);
+}
+
+// grid.x = ceil(n_blocks / 64), 256 threads.  LDS: 64 padded rows + queries as fp64.
+__global__ __launch_bounds__(kThreads) void score_wave_topk(
+    const uint16_t *__restrict__ pooled, int64_t n_blocks, int dim,
+    const uint16_t *__restrict__ q_idx, int n_sel, int k, uint64_t *__restrict__ cand_key,
+    uint32_t *__restrict__ cand_id, double *__restrict__ scores_out)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int pitch = dim * 2 + 16;
+    unsigned char *rows = lds;
+    double *qd = reinterpret_cast<double *>(lds + kWaveRows * pitch);
+    const int64_t b0 = (int64_t)blockIdx.x * kWaveRows;
+    const int nrows = (int)std::min<int64_t>(kWaveRows, n_blocks - b0);
+    const int wpr = dim / 8;
+
+    // every load is issued unconditionally (tail rows re-read the last valid row)
+    constexpr int kMaxWordsPerThread = kWaveRows * (256 / 8) / kThreads;   // 8
+    u32x4 v[kMaxWordsPerThread];
+#pragma unroll
+    for (int u = 0; u < kMaxWordsPerThread; u++) {
+        const int w = threadIdx.x + u * kThreads;
+        const int r = min(w / wpr, nrows - 1), c = w % wpr;
+        if (w < kWaveRows * wpr)
+            v[u] = *reinterpret_cast<const u32x4 *>(pooled + (b0 + r) * dim + c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxWordsPerThread; u++) {
+        const int w = threadIdx.x + u * kThreads;
+        if (w < kWaveRows * wpr)
+            *reinterpret_cast<u32x4 *>(rows + (w / wpr) * pitch + (w % wpr) * 16) = v[u];
+    }
+    for (int e = threadIdx.x; e < n_sel * dim; e += kThreads)
+        qd[e] = (double)f16_bits_to_f32(q_idx[e]);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool valid = lane < nrows;
+    const unsigned char *my_row = rows + lane * pitch;
+    // heads h0 and h0 + 4 together: two independent fp64 chains per lane
+    for (int h0 = wave; h0 < n_sel; h0 += 8) {
+        const int h1 = h0 + 4;
+        const bool two = h1 < n_sel;
+        const double *q0 = qd + h0 * dim;
+        const double *q1 = qd + (two ? h1 : h0) * dim;
+        double a0 = 0.0, a1 = 0.0;
+        for (int c = 0; c < wpr; c++) {
+            const u32x4 w4 = *reinterpret_cast<const u32x4 *>(my_row + c * 16);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const uint16_t bits = (uint16_t)(w4[e >> 1] >> ((e & 1) * 16));
+                const double pv = (double)f16_bits_to_f32(bits);
+                a0 = fma(q0[c * 8 + e], pv, a0);
+                a1 = fma(q1[c * 8 + e], pv, a1);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            if (t == 1 && !two)
+                break;
+            const int h = t ? h1 : h0;
+            const double acc = t ? a1 : a0;
+            uint64_t key = valid ? rank_key(acc) : 0;
+            uint32_t id = valid ? (uint32_t)(b0 + lane) : kNoId;
+            if (scores_out && valid)
+                scores_out[(int64_t)h * n_blocks + b0 + lane] = acc;
+            wave_sort_best_first(key, id, lane);
+            if (lane < k) {
+                const int64_t o = ((int64_t)h * gridDim.x + blockIdx.x) * k + lane;
+                cand_key[o] = key;
+                cand_id[o] = id;
+            }
+        }
+    }
+}
+
+// grid.x = n_sel, kMergeWaves*64 threads.  Lists of k sorted candidates: [h][n_lists][k].
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
+    const uint64_t *__restrict__ cand_key, const uint32_t *__restrict__ cand_id, int n_lists,
+    int k, int32_t *__restrict__ ids)
+{
+    __shared__ uint64_t skey[kMergeWaves][kWaveK];
+    __shared__ uint32_t sid[kMergeWaves][kWaveK];
+    const int h = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t *hk = cand_key + (int64_t)h * n_lists * k;
+    const uint32_t *hi = cand_id + (int64_t)h * n_lists * k;
+    const int li = min(lane, k - 1);
+    uint64_t ck = 0;
+    uint32_t ci = kNoId;
+    // prefetch one list ahead: the loads of list L+16 are in flight while L merges
+    int L = wave;
+    uint64_t nk = 0;
+    uint32_t ni = kNoId;
+    if (L < n_lists) {
+        nk = hk[(int64_t)L * k + li];
+        ni = hi[(int64_t)L * k + li];
+    }
+    while (L < n_lists) {
+        uint64_t lk = lane < k ? nk : 0;
+        uint32_t lid = lane < k ? ni : kNoId;
+        const int Ln = L + kMergeWaves;
+        if (Ln < n_lists) {
+            nk = hk[(int64_t)Ln * k + li];
+            ni = hi[(int64_t)Ln * k + li];
+        }
+        wave_merge32(ck, ci, lk, lid, lane);
+        L = Ln;
+    }
+    // pairwise fold of the waves' lists through LDS
+    for (int active = kMergeWaves / 2; active >= 1; active >>= 1) {
+        if (wave >= active && wave < 2 * active && lane < kWaveK) {
+            skey[wave][lane] = ck;
+            sid[wave][lane] = ci;
+        }
+        __syncthreads();
+        if (wave < active) {
+            const uint64_t lk = skey[wave + active][lane & 31];
+            const uint32_t lid = sid[wave + active][lane & 31];
+            wave_merge32(ck, ci, lane < kWaveK ? lk : 0, lane < kWaveK ? lid : kNoId, lane);
+        }
+        __syncthreads();
+    }
+    if (wave == 0) {
+        // the k winners' ids in ascending order; empty slots (kNoId) sort last and become -1
+        uint32_t id = lane < k ? ci : kNoId;
+#pragma unroll
+        for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const uint32_t p = __shfl(id, lane ^ stride, 64);
+                const bool lower = (lane & stride) == 0;
+                const bool up = size == 64 || (lane & size) == 0;
+                const bool mine_first = id < p;
+                if ((lower == up) != mine_first && id != p)
+                    id = p;
+            }
+        if (lane < k)
+            ids[h * k + lane] = id == kNoId ? -1 : (int32_t)id;
+    }
+}
+
 size_t score_lds_bytes(int dim, int n_sel)
 {
     return (size_t)kChunkBlocks * (dim * 2 + 16) + (size_t)n_sel * dim * 4 +
@@ -254,14 +456,16 @@ Plan make_plan(int64_t n_blocks, int k)
     return p;
 }
 
-inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
 }  // namespace
 
 extern "C" size_t kvt_index_topk_ws_bytes(int64_t n_blocks, int32_t n_sel, int32_t k)
 {
     if (n_blocks < 0 || n_sel < 1 || k < 1)
         return 0;
+    if (k <= kWaveK) {
+        const size_t c = (size_t)n_sel * (size_t)std::max<int64_t>((n_blocks + kWaveRows - 1) / kWaveRows, 1) * k;
+        return round_up(c * 8, 256) + round_up(c * 4, 256) + 256;
+    }
     const Plan p = make_plan(std::max<int64_t>(n_blocks, 1), k);
     const size_t a = (size_t)n_sel * p.buf_a, b = (size_t)n_sel * p.buf_b;
     return round_up(a * 8, 256) + round_up(a * 4, 256) + round_up(b * 8, 256) +
@@ -287,6 +491,24 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
         return kvt::fail(KVT_EINVAL, "kvt_index_topk: workspace of %zu bytes, need %zu",
                          ws_bytes, need);
     hipStream_t s = kvt::as_stream(stream);
+    if (k <= kWaveK) {
+        const int64_t n_wg = (n_blocks + kWaveRows - 1) / kWaveRows;
+        const size_t c = (size_t)n_sel * (size_t)std::max<int64_t>(n_wg, 1) * k;
+        uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
+        uint64_t *ck = reinterpret_cast<uint64_t *>(w);
+        uint32_t *ci = reinterpret_cast<uint32_t *>(w + round_up(c * 8, 256));
+        if (n_wg > 0) {
+            const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)n_sel * dim * 8;
+            hipLaunchKernelGGL(score_wave_topk, dim3((unsigned)n_wg), dim3(kThreads), lds, s,
+                               static_cast<const uint16_t *>(pooled), n_blocks, dim,
+                               static_cast<const uint16_t *>(q_idx), n_sel, k, ck, ci, scores);
+            KVT_LAUNCHED("score_wave_topk");
+        }
+        hipLaunchKernelGGL(merge_wave_topk, dim3(n_sel), dim3(kMergeWaves * 64), 0, s, ck, ci,
+                           (int)n_wg, k, ids);
+        KVT_LAUNCHED("merge_wave_topk");
+        return KVT_OK;
+    }
     const Plan p = make_plan(std::max<int64_t>(n_blocks, 1), k);
 
     // carve the workspace (256-byte aligned pieces)

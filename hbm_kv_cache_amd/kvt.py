@@ -36,8 +36,8 @@ _SIGNATURES = {
     "kvt_index_topk_ws_bytes": (c_size_t, [c_int64, c_int32, c_int32]),
     "kvt_index_topk": (c_int, [_P, c_int64, c_int32, _P, c_int32, c_int32, _P, _P, _P, c_size_t,
                                _P]),
-    "kvt_gather_blocks": (c_int, [_P, _P, c_int64, c_int32, c_int32, c_int32, c_int64, _P,
-                                  c_int32, _P, c_int32, _P, _P, _P]),
+    "kvt_gather_blocks": (c_int, [_P, _P, c_int64, c_int32, c_int32, c_int32, c_int64, c_int64,
+                                  c_int64, _P, c_int32, _P, c_int32, _P, _P, _P]),
     "kvt_stage_tail": (c_int, [_P, c_int64, c_int64, c_int64, _P, c_int32, _P]),
     "kvt_attn_decode_ws_bytes": (c_size_t, [c_int32, c_int32, c_int64]),
     "kvt_attn_decode": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, _P, _P, c_int64, _P,
@@ -150,12 +150,13 @@ def kvt_index_topk(pooled, n_blocks, dim, q_idx, n_sel, k, ids, scores, ws, ws_b
         _ptr(scores), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
-def kvt_gather_blocks(k_plane, v_plane, n_tok, kvh, hd, elem_bytes, row_stride, block_table, bt,
-                      ids, k, k_out, v_out, stream=None):
+def kvt_gather_blocks(k_plane, v_plane, n_blocks, kvh, hd, elem_bytes, block_stride,
+                      head_stride, token_stride, block_table, bt, ids, k, k_out, v_out,
+                      stream=None):
     _check("kvt_gather_blocks", load().kvt_gather_blocks(
-        _ptr(k_plane), _ptr(v_plane), int(n_tok), int(kvh), int(hd), int(elem_bytes),
-        int(row_stride), _ptr(block_table), int(bt), _ptr(ids), int(k), _ptr(k_out), _ptr(v_out),
-        _stream(stream)))
+        _ptr(k_plane), _ptr(v_plane), int(n_blocks), int(kvh), int(hd), int(elem_bytes),
+        int(block_stride), int(head_stride), int(token_stride), _ptr(block_table), int(bt),
+        _ptr(ids), int(k), _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
 def kvt_stage_tail(plane, row_bytes, row_begin, row_end, staging, mode=COPY_AUTO, stream=None):

@@ -58,7 +58,8 @@ extern "C" {
 /* copy direction and mechanism */
 #define KVT_H2D 0
 #define KVT_D2H 1
-#define KVT_COPY_AUTO 0   /* kernel below the page-size threshold when 8-byte aligned, else SDMA */
+#define KVT_COPY_AUTO 0   /* the kernel when sizes are multiples of 8 and pages are below the
+                            threshold (default: no limit), else SDMA */
 #define KVT_COPY_KERNEL 1 /* wavefront loads/stores through the host mapping */
 #define KVT_COPY_SDMA 2   /* the copy engines (hipMemcpyBatchAsync) */
 
@@ -113,10 +114,10 @@ int64_t kvt_chunks_consumed(int64_t n, int32_t skip, int32_t bpc);
  * src, dst, sizes: u64 tables of n entries in pinned host memory from kvt_host_alloc (the
  *   SDMA path reads them on the host, the kernel path through their device alias; pass the
  *   host pointer -- it is the same address on ROCm).  Table entries are device addresses.
- * dir:  KVT_H2D (load) or KVT_D2H (store); only steers KVT_COPY_AUTO (stores go to SDMA,
- *   as the page does, unless measured otherwise with kvt_set_copy_threshold).
+ * dir:  KVT_H2D (load) or KVT_D2H (store); selects which AUTO threshold applies.
  * mode: KVT_COPY_AUTO / KERNEL / SDMA.  The kernel path needs every size to be a multiple
- *   of 8 and 8-byte aligned addresses (else KVT_EALIGN); 16-byte alignment takes the wide path.
+ *   of 8 (else KVT_EALIGN); 16-byte aligned addresses take the wide path, 8-byte aligned ones
+ *   an 8-byte path, anything else a byte path.
  * Destination ranges must be pairwise disjoint and disjoint from all sources; the order of
  * the copies is unspecified.  Zero sizes are no-ops.  n == 0 enqueues nothing.
  * ---------------------------------------------------------------------------------------- */
@@ -147,20 +148,26 @@ int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim, const void
 
 /* ----------------------------------------------------------------------------------------
  * S5  top-k gather.  [QSA-KVO] sparse_attend / CacheLayer_qsa_offload: only the selected
- * blocks' K/V rows cross the host link, so the bytes read per step do not depend on context.
- *   k_plane, v_plane  device pointers (normally host-mapped) to token-major planes: token t,
- *                     head h starts at plane + t*row_stride + h*hd*elem_bytes.
- *   n_tok             tokens the planes hold; block b covers tokens [b*bt, b*bt + bt) of
- *                     physical block block_table[b] (identity when block_table is NULL).
+ * blocks' K/V rows cross the host link, so the bytes read per step do not depend on context;
+ * the gather reaches the planes through a base pointer plus computed offsets.
+ *   k_plane, v_plane  device pointers (normally host-mapped).  Token r (0 <= r < bt) of
+ *                     physical block p, head h, starts at
+ *                         plane + p*block_stride + h*head_stride + r*token_stride   (bytes)
+ *                     and holds hd elements of elem_bytes.  Token-major [token][head][dim]:
+ *                     (bt*kvh*hd*eb, hd*eb, kvh*hd*eb); block-local head-major
+ *                     [block][head][token][dim]: (kvh*bt*hd*eb, bt*hd*eb, hd*eb).
+ *   n_blocks          physical blocks the planes hold; logical block b lives in physical block
+ *                     block_table[b] (identity when block_table is NULL).
  *   ids               device int32 [kvh][k], e.g. kvt_index_topk's output.
- *   k_out, v_out      device [kvh][k*bt][hd] elements:  out[h][i*bt + r] = plane[phys*bt + r][h].
- * Slots with ids < 0, or whose block lies outside the planes, are skipped (left untouched).
- * hd*elem_bytes and row_stride must be multiples of 16, plane bases 16-byte aligned.
+ *   k_out, v_out      device [kvh][k*bt][hd] elements: out[h][i*bt + r] = token r of block
+ *                     phys(ids[h][i]), head h.
+ * Slots with ids < 0, or whose block lies outside [0, n_blocks), are skipped (left untouched).
+ * hd*elem_bytes and the three strides must be multiples of 16, bases 16-byte aligned.
  * ---------------------------------------------------------------------------------------- */
-int kvt_gather_blocks(const void *k_plane, const void *v_plane, int64_t n_tok, int32_t kvh,
-                      int32_t hd, int32_t elem_bytes, int64_t row_stride,
-                      const int32_t *block_table, int32_t bt, const int32_t *ids, int32_t k,
-                      void *k_out, void *v_out, void *stream);
+int kvt_gather_blocks(const void *k_plane, const void *v_plane, int64_t n_blocks, int32_t kvh,
+                      int32_t hd, int32_t elem_bytes, int64_t block_stride, int64_t head_stride,
+                      int64_t token_stride, const int32_t *block_table, int32_t bt,
+                      const int32_t *ids, int32_t k, void *k_out, void *v_out, void *stream);
 
 /* ----------------------------------------------------------------------------------------
  * S7  tail staging.  [llama-T] commit text: when an attention op reaches the host tail, the

@@ -54,8 +54,8 @@ def _load():
             "orc_swap": (c_int, [P, P, P, c_int64, c_int]),
             "orc_index_scores": (c_int, [P, c_int64, c_int32, P, c_int32, P, c_int]),
             "orc_topk": (c_int, [P, c_int32, c_int64, c_int32, P]),
-            "orc_gather": (c_int, [P, P, c_int64, c_int32, c_int32, c_int32, c_int64, P, c_int32,
-                                   P, c_int32, P, P]),
+            "orc_gather": (c_int, [P, P, c_int64, c_int32, c_int32, c_int32, c_int64, c_int64,
+                                   c_int64, P, c_int32, P, c_int32, P, P]),
             "orc_stage_tail": (c_int, [P, c_int64, c_int64, c_int64, P]),
             "orc_attn_decode": (c_int, [P, c_int32, c_int32, c_int32, c_int32, P, P, c_int64, P,
                                         c_double, P, c_int]),
@@ -144,9 +144,20 @@ def topk(scores, k):
     return ids
 
 
-def gather(k_plane, v_plane, n_tok, kvh, hd, elem_bytes, row_stride, ids, block_tokens,
+def token_major_strides(kvh, hd, elem_bytes, block_tokens, row_stride=None):
+    """(block, head, token) byte strides of the token-major layout [token][head][dim]."""
+    row = kvh * hd * elem_bytes if row_stride is None else row_stride
+    return block_tokens * row, hd * elem_bytes, row
+
+
+def block_head_major_strides(kvh, hd, elem_bytes, block_tokens):
+    """(block, head, token) byte strides of the layout [block][head][token][dim]."""
+    return kvh * block_tokens * hd * elem_bytes, block_tokens * hd * elem_bytes, hd * elem_bytes
+
+
+def gather(k_plane, v_plane, n_blocks, kvh, hd, elem_bytes, strides, ids, block_tokens,
            block_table=None, k_out=None, v_out=None):
-    """Planes: uint8 arrays addressed as token*row_stride + head*hd*elem_bytes."""
+    """Planes: uint8 arrays addressed through (block, head, token) byte strides."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     kk = ids.shape[1]
     shape = (kvh, kk * block_tokens, hd * elem_bytes)
@@ -155,10 +166,10 @@ def gather(k_plane, v_plane, n_tok, kvh, hd, elem_bytes, row_stride, ids, block_
     if v_out is None:
         v_out = np.zeros(shape, dtype=np.uint8)
     bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
-    _check("orc_gather", _load().orc_gather(_ptr(k_plane), _ptr(v_plane), int(n_tok), kvh, hd,
-                                            elem_bytes, int(row_stride), _ptr(bt),
-                                            int(block_tokens), _ptr(ids), kk, _ptr(k_out),
-                                            _ptr(v_out)))
+    bs, hs, ts = (int(x) for x in strides)
+    _check("orc_gather", _load().orc_gather(_ptr(k_plane), _ptr(v_plane), int(n_blocks), kvh, hd,
+                                            elem_bytes, bs, hs, ts, _ptr(bt), int(block_tokens),
+                                            _ptr(ids), kk, _ptr(k_out), _ptr(v_out)))
     return k_out, v_out
 
 

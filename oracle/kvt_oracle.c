@@ -226,16 +226,20 @@ int orc_topk(const double *scores, int32_t n_sel, int64_t n_blocks, int32_t k, i
 /* ------------------------------------------------------------------------------------------ */
 /* O4  top-k gather                        [QSA-KVO] sparse_attend / CacheLayer_qsa_offload   */
 /* ------------------------------------------------------------------------------------------ */
-/* Planes are token-major: token t, head h starts at plane + t*row_stride + h*hd*elem_bytes.
- * A logical block b covers tokens [b*bt, b*bt + bt) of physical block table[b] (identity when
- * the table is NULL).  For head h and selection slot i with id b >= 0:
- *   out[h][i*bt + r][:] = plane[phys(b)*bt + r][h][:]   for r < bt.
- * Slots with id < 0 are left untouched. */
-int orc_gather(const uint8_t *k_plane, const uint8_t *v_plane, int64_t n_tok, int32_t kvh,
-               int32_t hd, int32_t elem_bytes, int64_t row_stride, const int32_t *block_table,
-               int32_t bt, const int32_t *ids, int32_t k, uint8_t *k_out, uint8_t *v_out)
+/* A plane is addressed through byte strides ("a base pointer plus computed offsets"): token r
+ * of physical block p, head h starts at  plane + p*block_stride + h*head_stride + r*token_stride
+ * and holds hd elements of elem_bytes.  The pages' token-major layout [token][head][dim] is
+ * block_stride = bt*kvh*hd*eb, head_stride = hd*eb, token_stride = kvh*hd*eb.
+ * Logical block b lives in physical block table[b] (identity when the table is NULL).
+ * For head h and selection slot i with id b >= 0:
+ *   out[h][i*bt + r][:] = the hd elements of token r of block phys(b), head h,  r < bt.
+ * Slots with id < 0 are left untouched; a block outside [0, n_blocks) is an error. */
+int orc_gather(const uint8_t *k_plane, const uint8_t *v_plane, int64_t n_blocks, int32_t kvh,
+               int32_t hd, int32_t elem_bytes, int64_t block_stride, int64_t head_stride,
+               int64_t token_stride, const int32_t *block_table, int32_t bt, const int32_t *ids,
+               int32_t k, uint8_t *k_out, uint8_t *v_out)
 {
-    if (kvh < 1 || hd < 1 || elem_bytes < 1 || bt < 1 || k < 1 || n_tok < 0)
+    if (kvh < 1 || hd < 1 || elem_bytes < 1 || bt < 1 || k < 1 || n_blocks < 0)
         return ORC_EINVAL;
     size_t slice = (size_t)hd * elem_bytes;
     for (int32_t h = 0; h < kvh; h++) {
@@ -244,11 +248,11 @@ int orc_gather(const uint8_t *k_plane, const uint8_t *v_plane, int64_t n_tok, in
             if (b < 0)
                 continue;
             int64_t pb = block_table ? block_table[b] : b;
-            if (pb < 0 || (pb + 1) * (int64_t)bt > n_tok)
+            if (pb < 0 || pb >= n_blocks)
                 return ORC_ERANGE;
             for (int32_t r = 0; r < bt; r++) {
-                int64_t t = pb * bt + r;
-                size_t src_off = (size_t)t * row_stride + (size_t)h * slice;
+                size_t src_off = (size_t)(pb * block_stride + (int64_t)h * head_stride +
+                                          (int64_t)r * token_stride);
                 size_t dst_off = ((size_t)h * k * bt + (size_t)i * bt + r) * slice;
                 memcpy(k_out + dst_off, k_plane + src_off, slice);
                 memcpy(v_out + dst_off, v_plane + src_off, slice);

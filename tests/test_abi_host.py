@@ -89,7 +89,8 @@ def test_argument_errors_return_before_any_device_work():
         kvt.kvt_index_topk(16, 100, 128, 16, 8, 32, 16, None, 16, 8, stream=0)
     assert e.value.code == kvt.EINVAL
     with pytest.raises(kvt.KvtError) as e:
-        kvt.kvt_gather_blocks(16, 16, 128, 8, 128, 2, 100, None, 64, 16, 32, 16, 16, stream=0)
+        kvt.kvt_gather_blocks(16, 16, 2, 8, 128, 2, 64 * 100, 256, 100, None, 64, 16, 32, 16, 16,
+                              stream=0)
     assert e.value.code == kvt.EALIGN
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_attn_decode(16, 64, 8, 64, kvt.BF16, 16, 16, 10, None, 0.1, 16, 16, 1 << 20,

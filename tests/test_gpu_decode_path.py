@@ -88,10 +88,16 @@ def _host_planes(n_tok, kvh, hd, cfg, step=0):
     return buf, planes
 
 
-def test_gather_blocks_bit_exact_with_table_and_negative_ids(gpu):
+LAYOUTS = {"token_major": oracle.token_major_strides,
+           "block_head_major": oracle.block_head_major_strides}
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+def test_gather_blocks_bit_exact_with_table_and_negative_ids(gpu, layout):
     n_tok, kvh, hd, bt, k = 64 * 300, 8, 128, 64, 32
     buf, planes = _host_planes(n_tok, kvh, hd, 4, 11)
     n_blocks = n_tok // bt
+    strides = LAYOUTS[layout](kvh, hd, 2, bt)
     g = synth.rng(4, synth.P_MISC, 12)
     ids = np.stack([np.sort(g.permutation(n_blocks)[:k]) for _ in range(kvh)]).astype(np.int32)
     ids[3, 20:] = -1
@@ -99,16 +105,16 @@ def test_gather_blocks_bit_exact_with_table_and_negative_ids(gpu):
     table = g.permutation(n_blocks).astype(np.int32)
     for tab in (None, table):
         out = torch.full((2, kvh, k * bt, hd), 0x1234, dtype=torch.int16, device=gpu)
-        kvt.kvt_gather_blocks(buf.dev, buf.dev + n_tok * kvh * hd * 2, n_tok, kvh, hd, 2,
-                              kvh * hd * 2, None if tab is None else torch.from_numpy(tab).to(gpu),
+        kvt.kvt_gather_blocks(buf.dev, buf.dev + n_tok * kvh * hd * 2, n_blocks, kvh, hd, 2,
+                              *strides, None if tab is None else torch.from_numpy(tab).to(gpu),
                               bt, torch.from_numpy(ids).to(gpu), k, out[0], out[1])
         torch.cuda.synchronize()
         ids_o = ids.copy()
         ids_o[4, 31] = -1
         canary = np.full((kvh, k * bt, hd * 2), 0, dtype=np.uint8)
         canary.view(np.uint16)[:] = 0x1234
-        ko, vo = oracle.gather(planes[0].view(np.uint8), planes[1].view(np.uint8), n_tok, kvh,
-                               hd, 2, kvh * hd * 2, ids_o, bt, block_table=tab,
+        ko, vo = oracle.gather(planes[0].view(np.uint8), planes[1].view(np.uint8), n_blocks, kvh,
+                               hd, 2, strides, ids_o, bt, block_table=tab,
                                k_out=canary.copy(), v_out=canary.copy())
         got = out.cpu().numpy().view(np.uint8).reshape(2, kvh, k * bt, hd * 2)
         assert np.array_equal(got[0], ko) and np.array_equal(got[1], vo)
@@ -162,12 +168,19 @@ def test_decode_attention_valid_counts_and_degenerate_cases(gpu):
     assert np.max(np.abs(got - ref)) <= TOL
     got, ref = _run_decode(q, k, v, kvt.BF16, gpu, scale=2.0)
     assert np.max(np.abs(got - ref)) <= TOL
+    # rows past n_valid hold NaN patterns (as slots a gather skipped may): they take no part
+    k_nan, v_nan = k.copy(), v.copy()
+    k_nan[:, 1500:] = 0x7FC0
+    v_nan[:, 1500:] = 0x7FC0
+    got, ref = _run_decode(q, k_nan, v_nan, kvt.BF16, gpu, n_valid=[1500] * 8)
+    assert np.isfinite(got).all() and np.max(np.abs(got - ref)) <= TOL
     got, ref = _run_decode(q, k[:, :0], v[:, :0], kvt.BF16, gpu)     # no keys at all
     assert (got == 0).all() and (ref == 0).all()
 
 
-@pytest.mark.parametrize("ctx", [262144, 1048576])
-def test_decode_step_full_geometry(gpu, ctx):
+@pytest.mark.parametrize("ctx,layout", [(262144, "block_head_major"), (262144, "token_major"),
+                                        (1048576, "block_head_major")])
+def test_decode_step_full_geometry(gpu, ctx, layout):
     """One decode step at full size: pooled plane in HBM, K/V planes in pinned host memory,
     score + top-32 per KV head, gather host -> HBM, GQA attention with 64 query heads.
     Ids and gathered bytes bit-exact; attention within 2e-3 of the fp64 oracle."""
@@ -186,7 +199,8 @@ def test_decode_step_full_geometry(gpu, ctx):
     out = torch.empty((n_qh, hd), dtype=torch.float32, device=gpu)
     kvt.kvt_index_topk(_u16(pooled, gpu), n_blocks, 128, _u16(q_idx, gpu), kvh, k, ids, None,
                        ws, ws_t)
-    kvt.kvt_gather_blocks(buf.dev, buf.dev + ctx * kvh * hd * 2, ctx, kvh, hd, 2, kvh * hd * 2,
+    strides = LAYOUTS[layout](kvh, hd, 2, bt)
+    kvt.kvt_gather_blocks(buf.dev, buf.dev + ctx * kvh * hd * 2, n_blocks, kvh, hd, 2, *strides,
                           None, bt, ids, k, kg[0], kg[1])
     kvt.kvt_attn_decode(_u16(q, gpu), n_qh, kvh, hd, kvt.BF16, kg[0], kg[1], k * bt, None,
                         1 / math.sqrt(hd), out, ws[ws_t:], ws_d)
@@ -194,8 +208,8 @@ def test_decode_step_full_geometry(gpu, ctx):
 
     ref_ids = oracle.topk(oracle.index_scores(pooled, q_idx), k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
-    ko, vo = oracle.gather(planes[0].view(np.uint8), planes[1].view(np.uint8), ctx, kvh, hd, 2,
-                           kvh * hd * 2, ref_ids, bt)
+    ko, vo = oracle.gather(planes[0].view(np.uint8), planes[1].view(np.uint8), n_blocks, kvh,
+                           hd, 2, strides, ref_ids, bt)
     got = kg.cpu().numpy().view(np.uint8).reshape(2, kvh, k * bt, hd * 2)
     assert np.array_equal(got[0], ko) and np.array_equal(got[1], vo)
     ref = oracle.attn_decode(q, ko.view(np.uint16).reshape(kvh, k * bt, hd),

@@ -233,15 +233,32 @@ def test_topk_tie_rule_prefers_lower_id():
 # ------------------------------------------------------------------------------------------
 
 def test_gather_all_blocks_is_head_major_transpose():
+    """Token-major planes: gathering every block in order is numpy's transpose to head-major."""
     g = synth.rng(0, synth.P_MISC, 11)
     n_tok, kvh, hd, bt = 256, 4, 16, 64
     k = synth.random_u16(g, (n_tok, kvh, hd))
     v = synth.random_u16(g, (n_tok, kvh, hd))
     ids = np.tile(np.arange(n_tok // bt, dtype=np.int32), (kvh, 1))
-    ko, vo = oracle.gather(k.view(np.uint8), v.view(np.uint8), n_tok, kvh, hd, 2,
-                           kvh * hd * 2, ids, bt)
+    ko, vo = oracle.gather(k.view(np.uint8), v.view(np.uint8), n_tok // bt, kvh, hd, 2,
+                           oracle.token_major_strides(kvh, hd, 2, bt), ids, bt)
     assert np.array_equal(ko.view(np.uint16).reshape(kvh, n_tok, hd), k.transpose(1, 0, 2))
     assert np.array_equal(vo.view(np.uint16).reshape(kvh, n_tok, hd), v.transpose(1, 0, 2))
+
+
+def test_gather_block_head_major_layout_is_numpy_transpose():
+    """[block][head][token][dim] planes: gathering every block in order is numpy's transpose."""
+    g = synth.rng(0, synth.P_MISC, 19)
+    nb, kvh, hd, bt = 5, 3, 16, 8
+    k = synth.random_u16(g, (nb, kvh, bt, hd))
+    ids = np.tile(np.arange(nb, dtype=np.int32), (kvh, 1))
+    ko, _ = oracle.gather(k.view(np.uint8), k.view(np.uint8), nb, kvh, hd, 2,
+                          oracle.block_head_major_strides(kvh, hd, 2, bt), ids, bt)
+    assert np.array_equal(ko.view(np.uint16).reshape(kvh, nb * bt, hd),
+                          k.transpose(1, 0, 2, 3).reshape(kvh, nb * bt, hd))
+    # the same bytes viewed token-major vs head-major give different gathers unless kvh == 1
+    tm, _ = oracle.gather(k.view(np.uint8), k.view(np.uint8), nb, kvh, hd, 2,
+                          oracle.token_major_strides(kvh, hd, 2, bt), ids, bt)
+    assert not np.array_equal(tm, ko)
 
 
 def test_gather_random_ids_padded_rows_and_block_table():
@@ -255,8 +272,9 @@ def test_gather_random_ids_padded_rows_and_block_table():
     ids = np.stack([np.sort(g.permutation(n_blocks)[:5]) for _ in range(kvh)]).astype(np.int32)
     ids[1, 3:] = -1
     canary = np.full((kvh, 5 * bt, hd * 2), 0xEE, dtype=np.uint8)
-    ko, vo = oracle.gather(kbuf, vbuf, n_tok, kvh, hd, 2, row + pad, ids, bt, block_table=table,
-                           k_out=canary.copy(), v_out=canary.copy())
+    ko, vo = oracle.gather(kbuf, vbuf, n_blocks, kvh, hd, 2,
+                           oracle.token_major_strides(kvh, hd, 2, bt, row + pad), ids, bt,
+                           block_table=table, k_out=canary.copy(), v_out=canary.copy())
     k4 = kbuf[:, :row].reshape(n_blocks, bt, kvh, hd * 2)
     v4 = vbuf[:, :row].reshape(n_blocks, bt, kvh, hd * 2)
     for h in range(kvh):
@@ -272,7 +290,8 @@ def test_gather_random_ids_padded_rows_and_block_table():
 def test_gather_out_of_range_block_is_an_error():
     k = np.zeros(64 * 16, dtype=np.uint8)
     with pytest.raises(oracle.OracleError) as e:
-        oracle.gather(k, k, 64, 1, 8, 2, 16, np.array([[1]]), 64)
+        oracle.gather(k, k, 1, 1, 8, 2, oracle.token_major_strides(1, 8, 2, 64),
+                      np.array([[1]]), 64)
     assert e.value.code == oracle.ERANGE
 
 
