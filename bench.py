@@ -474,8 +474,96 @@ def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
     return out
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16
+
+
+def prefill_flops(n_q, q_pos0, n_qh, hd, n_kv, causal=True):
+    """QK^T and PV multiply-adds, 2 flops each: 4*hd*n_qh per (query, visible key) pair."""
+    if causal:
+        keys = sum(min(q_pos0 + t + 1, n_kv) for t in range(n_q))
+    else:
+        keys = n_q * n_kv
+    return 4 * hd * n_qh * keys
+
+
+def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
+    """Tiered prefill: 180,000-token q8_0 cache (8 KV heads x 128), cells [0, 94208) in HBM and
+    the rest in pinned host memory; a 2048-query causal chunk at the tail with 32 query heads.
+    Stage the used host rows into HBM once, then flash attention over head + staging."""
+    import numpy as np
+    n_kv, n_head, n_q, n_qh, kvh, hd = 180000, 94208, 2048, 32, 8, 128
+    n_tail = n_kv - n_head
+    t0 = time.time()
+    k = synth.q8_0_rows(synth.rng(5, synth.P_K, n_kv), n_kv, kvh, hd)
+    v = synth.q8_0_rows(synth.rng(5, synth.P_V, n_kv), n_kv, kvh, hd)
+    row = k.shape[1]
+    q = torch.from_numpy(synth.f16_normal(synth.rng(5, synth.P_Q, n_kv),
+                                          (n_q, n_qh, hd)).view(np.int16)).to(dev)
+    k_all = torch.from_numpy(k).to(dev)
+    v_all = torch.from_numpy(v).to(dev)
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    del k, v
+    stage = torch.empty((2, n_tail, row), dtype=torch.uint8, device=dev)
+    out = torch.empty((n_q, n_qh, hd), dtype=torch.float32, device=dev)
+    log(f"prefill inputs ready in {time.time() - t0:.1f}s")
+    t = Timer(torch, torch.cuda.current_stream())
+    q_pos0 = n_kv - n_q
+    scale = 1 / math.sqrt(hd)
+    flops = prefill_flops(n_q, q_pos0, n_qh, hd, n_kv)
+    stage_bytes = 2 * n_tail * row
+
+    def stage_ms(mode):
+        ms = []
+        for _ in range(reps):
+            t.start()
+            kvt.kvt_stage_tail(host.dev, row, 0, n_tail, stage[0], mode)
+            kvt.kvt_stage_tail(host.dev + n_tail * row, row, 0, n_tail, stage[1], mode)
+            ms.append(t.stop_ms())
+        return _median(ms)
+
+    def attn_ms(kh, vh, nh, kt, vt):
+        ms = []
+        for _ in range(reps):
+            t.start()
+            kvt.kvt_attn_prefill(q, n_q, q_pos0, n_qh, kvh, hd, kh, vh, nh, kt, vt, n_kv,
+                                 kvt.Q8_0, 1, scale, out)
+            ms.append(t.stop_ms())
+        return _median(ms)
+
+    st_sdma = stage_ms(kvt.COPY_SDMA)
+    st_kernel = stage_ms(kvt.COPY_KERNEL)
+    a_staged = attn_ms(k_all, v_all, n_head, stage[0], stage[1])
+    a_inplace = attn_ms(k_all, v_all, n_head, host.dev, host.dev + n_tail * row)
+    a_hbm = attn_ms(k_all, v_all, n_kv, None, None)
+    st = min(st_sdma, st_kernel)
+    res = {
+        "n_kv": n_kv, "n_head": n_head, "n_q": n_q, "q_heads": n_qh, "kv_heads": kvh,
+        "stage_bytes": stage_bytes, "flops": flops,
+        "stage_sdma_ms": round(st_sdma, 4), "stage_kernel_ms": round(st_kernel, 4),
+        "stage_gbs": round(stage_bytes / (st * 1e-3) / GB, 2),
+        "stage_pct_measured_h2d_peak": round(100 * stage_bytes / (st * 1e-3) / GB / peaks["h2d_sdma_gbs"], 1),
+        "attn_staged_ms": round(a_staged, 4),
+        "attn_tflops": round(flops / (a_staged * 1e-3) / 1e12, 1),
+        "attn_pct_mfma_fp16_peak": round(100 * flops / (a_staged * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 2),
+        "attn_tail_in_host_ms": round(a_inplace, 4),
+        "attn_all_hbm_ms": round(a_hbm, 4),
+        "prefill_tok_s_staged": round(n_q / ((st + a_staged) * 1e-3), 1),
+        "prefill_tok_s_staging_off": round(n_q / (a_inplace * 1e-3), 1),
+    }
+    log("prefill", res)
+    del ht
+    host.free()
+    del k_all, v_all, stage, out, q
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     out = {}
+    log("suite: tiered prefill")
+    out["tiered_prefill"] = suite_prefill(torch, kvt, synth, dev, peaks)
     log("suite: one-layer swap")
     out["swap_1_layer"] = suite_one_layer(torch, kvt, synth, dev, peaks)
     log("suite: small pages")

@@ -49,25 +49,34 @@ def fill_random_bytes(g: np.random.Generator, out: np.ndarray, chunk: int = 1 <<
         flat[o:o + n] = g.integers(0, 256, size=n, dtype=np.uint8)
 
 
+def q8_0_encode(x: np.ndarray) -> np.ndarray:
+    """Encode float data [n][nb][32] as q8_0 blocks: scale = fp16(max|x| / 127) as 2
+    little-endian bytes, then q = clamp(rint(x / scale), -127, 127) as 32 int8.  Returns uint8
+    [n][nb][34].  (Input generation only: consumers read the stored bytes.)"""
+    x = np.asarray(x, dtype=np.float32)
+    n, nb, _ = x.shape
+    out = np.empty((n, nb, 34), dtype=np.uint8)
+    amax = np.abs(x).max(axis=2)
+    d16 = (amax / np.float32(127.0)).astype(np.float16)
+    d = d16.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qf = np.where(d[..., None] > 0, x / d[..., None], 0.0)
+    q = np.clip(np.rint(qf), -127, 127).astype(np.int8)
+    out[:, :, 0:2] = d16.view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:] = q.view(np.uint8)
+    return out
+
+
 def q8_0_rows(g: np.random.Generator, n_rows: int, kvh: int, hd: int) -> np.ndarray:
-    """q8_0 cache rows of N(0,1) data: per 32-value block, scale = fp16(max|x| / 127) stored as
-    2 little-endian bytes, then q = clamp(rint(x / scale), -127, 127) as 32 int8.  A row is
-    kvh heads x hd/32 blocks, head-major: kvh * hd/32 * 34 bytes.  Returns uint8 [n_rows][row]."""
+    """q8_0 cache rows of N(0,1) data (see q8_0_encode).  A row is kvh heads x hd/32 blocks,
+    head-major: kvh * hd/32 * 34 bytes.  Returns uint8 [n_rows][row]."""
     assert hd % 32 == 0
     nb = kvh * (hd // 32)
     out = np.empty((n_rows, nb, 34), dtype=np.uint8)
     step = 1 << 16
     for r0 in range(0, n_rows, step):
         r1 = min(n_rows, r0 + step)
-        x = g.standard_normal((r1 - r0, nb, 32), dtype=np.float32)
-        amax = np.abs(x).max(axis=2)
-        d16 = (amax / np.float32(127.0)).astype(np.float16)
-        d = d16.astype(np.float32)
-        with np.errstate(divide="ignore", invalid="ignore"):
-            qf = np.where(d[..., None] > 0, x / d[..., None], 0.0)
-        q = np.clip(np.rint(qf), -127, 127).astype(np.int8)
-        out[r0:r1, :, 0:2] = d16.view(np.uint8).reshape(r1 - r0, nb, 2)
-        out[r0:r1, :, 2:] = q.view(np.uint8)
+        out[r0:r1] = q8_0_encode(g.standard_normal((r1 - r0, nb, 32), dtype=np.float32))
     return out.reshape(n_rows, nb * 34)
 
 

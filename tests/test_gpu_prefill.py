@@ -1,0 +1,159 @@
+"""GPU parity of the tiered prefill path: tail staging + flash attention over a q8_0 cache.
+
+* within 2e-3 max-abs of the fp64 oracle (every element at small sizes, sampled query rows at
+  the full 180,000-token geometry);
+* bit-identical output whether the cache is all in HBM, split into an HBM head plus a staged
+  tail, or split with the tail read in place from host memory (staging off)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hbm_kv_cache_amd import kvt, synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _cache(n_kv, kvh, seed):
+    k = synth.q8_0_rows(synth.rng(5, synth.P_K, seed), n_kv, kvh, 128)
+    v = synth.q8_0_rows(synth.rng(5, synth.P_V, seed), n_kv, kvh, 128)
+    return k, v
+
+
+def _prefill(q_np, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, causal, dev):
+    n_q, n_qh, hd = q_np.shape
+    q = torch.from_numpy(q_np.view(np.int16)).to(dev)
+    out = torch.full((n_q, n_qh, hd), float("nan"), dtype=torch.float32, device=dev)
+    kvt.kvt_attn_prefill(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_tail, v_tail,
+                         n_kv, kvt.Q8_0, causal, 1 / math.sqrt(hd), out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+@pytest.mark.parametrize("n_kv,n_q,n_qh,kvh,causal,n_head", [
+    (1000, 77, 32, 8, True, 400),       # ragged queries and keys, split mid-tile
+    (2048, 64, 16, 4, True, 2048),      # all in HBM
+    (1500, 100, 8, 8, True, 0),         # all in the tail
+    (700, 33, 8, 4, False, 350),        # non-causal, group 2
+    (333, 40, 4, 4, True, 64),          # group 1
+    (130, 130, 8, 2, True, 65),         # queries from position 0: first row sees one key
+])
+def test_prefill_matches_oracle(gpu, n_kv, n_q, n_qh, kvh, causal, n_head):
+    k, v = _cache(n_kv, kvh, n_kv + n_q)
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, n_kv), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    got = _prefill(q, q_pos0, kvh, kd, vd, n_head, kd[n_head:], vd[n_head:], n_kv, causal, gpu)
+    ref = oracle.attn_prefill(q, q_pos0, kvh, k, v, n_head, k[n_head:], v[n_head:], n_kv,
+                              oracle.Q8_0, causal, 1 / math.sqrt(128))
+    err = np.max(np.abs(got - ref))
+    assert np.isfinite(got).all() and err <= TOL, err
+
+
+def test_prefill_peaked_softmax_within_tolerance(gpu):
+    """For every query row, one visible key is the (q8_0-quantised) query itself, so its logit
+    (about |q|^2 / sqrt(128), ~11) dominates the others (~N(0,1)): most of the weight sits on
+    one key and the rounding of the probabilities and of V matters most.  Still within 2e-3.
+    (The bound holds at the usual 1/sqrt(head_dim) scale; the fp16 rounding of dequantised K
+    perturbs each logit by up to scale * sum|q k| * 2^-11, which grows with the scale.)"""
+    n_kv, n_q, n_qh, kvh = 512, 16, 4, 4
+    k, v = _cache(n_kv, kvh, 7)
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, 7), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    rows = k.reshape(n_kv, kvh * 4, 34).copy()
+    for t in range(n_q):
+        j = q_pos0 + t - 3 * (t % 5)                  # a visible key for row t
+        x = q[t].view(np.float16).astype(np.float32).reshape(kvh * 4, 32)   # head h -> kv h
+        rows[j] = synth.q8_0_encode(x[None])[0]
+    k = rows.reshape(n_kv, -1)
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    got = _prefill(q, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    ref = oracle.attn_prefill(q, q_pos0, kvh, k, v, n_kv, None, None, n_kv, oracle.Q8_0, True,
+                              1 / math.sqrt(128))
+    assert np.max(np.abs(got - ref)) <= TOL
+
+
+def test_prefill_three_way_bit_identity(gpu):
+    """All-HBM cache == HBM head + staged tail == HBM head + tail read from host memory."""
+    n_kv, n_q, n_qh, kvh, n_head = 5000, 300, 32, 8, 2100
+    k, v = _cache(n_kv, kvh, 11)
+    row = k.shape[1]
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, 11), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    host = kvt.HostBuffer(2 * (n_kv - n_head) * row)
+    ht = host.numpy(np.uint8, (2, n_kv - n_head, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    all_hbm = _prefill(q, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    stage = torch.empty((2, n_kv - n_head, row), dtype=torch.uint8, device=gpu)
+    for mode in (kvt.COPY_SDMA, kvt.COPY_KERNEL):
+        stage.zero_()
+        kvt.kvt_stage_tail(host.dev, row, 0, n_kv - n_head, stage[0], mode)
+        kvt.kvt_stage_tail(host.dev + (n_kv - n_head) * row, row, 0, n_kv - n_head, stage[1], mode)
+        staged = _prefill(q, q_pos0, kvh, kd, vd, n_head, stage[0], stage[1], n_kv, True, gpu)
+        assert np.array_equal(staged.view(np.uint32), all_hbm.view(np.uint32))
+    in_place = _prefill(q, q_pos0, kvh, kd, vd, n_head, host.dev,
+                        host.dev + (n_kv - n_head) * row, n_kv, True, gpu)
+    assert np.array_equal(in_place.view(np.uint32), all_hbm.view(np.uint32))
+    del ht
+    host.free()
+
+
+def test_prefill_full_geometry_sampled_rows(gpu):
+    """180,000-token context, cells [0, 94208) in HBM and the rest in host memory, q8_0 K/V
+    (8 KV heads x 128), a 2048-query causal chunk at the tail with 32 query heads: stage the
+    host rows into HBM once, run the attention, compare sampled query rows (all heads, all
+    dims) with the fp64 oracle; staging on/off and all-HBM agree bit for bit."""
+    n_kv, n_head, n_q, n_qh, kvh = 180000, 94208, 2048, 32, 8
+    k, v = _cache(n_kv, kvh, 180000)
+    row = k.shape[1]
+    n_tail = n_kv - n_head
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, 180000), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k[:n_head], gpu), _dev(v[:n_head], gpu)
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    stage = torch.empty((2, n_tail, row), dtype=torch.uint8, device=gpu)
+    kvt.kvt_stage_tail(host.dev, row, 0, n_tail, stage[0], kvt.COPY_AUTO)
+    kvt.kvt_stage_tail(host.dev + n_tail * row, row, 0, n_tail, stage[1], kvt.COPY_AUTO)
+    staged = _prefill(q, q_pos0, kvh, kd, vd, n_head, stage[0], stage[1], n_kv, True, gpu)
+    assert np.array_equal(stage.cpu().numpy().reshape(2, n_tail, row), ht)
+    for rows in ((0, 2), (1023, 1025), (2046, 2048)):
+        ref = oracle.attn_prefill(q, q_pos0, kvh, k, v, n_kv, None, None, n_kv, oracle.Q8_0, True,
+                                  1 / math.sqrt(128), t_begin=rows[0], t_end=rows[1])
+        err = np.max(np.abs(staged[rows[0]:rows[1]] - ref))
+        assert err <= TOL, (rows, err)
+    in_place = _prefill(q, q_pos0, kvh, kd, vd, n_head, host.dev, host.dev + n_tail * row, n_kv,
+                        True, gpu)
+    assert np.array_equal(in_place.view(np.uint32), staged.view(np.uint32))
+    kall, vall = _dev(k, gpu), _dev(v, gpu)
+    all_hbm = _prefill(q, q_pos0, kvh, kall, vall, n_kv, None, None, n_kv, True, gpu)
+    assert np.array_equal(all_hbm.view(np.uint32), staged.view(np.uint32))
+    del ht
+    host.free()
+
+
+def test_prefill_argument_errors(gpu):
+    q = torch.zeros((4, 8, 128), dtype=torch.float16, device=gpu)
+    out = torch.empty((4, 8, 128), dtype=torch.float32, device=gpu)
+    k = torch.zeros((10, 8 * 136), dtype=torch.uint8, device=gpu)
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 10, None, None, 10, kvt.F16, 1, 0.1, out)
+    assert e.value.code == kvt.EUNSUPPORTED
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_prefill(q, 4, 0, 8, 1, 128, k, k, 10, None, None, 10, kvt.Q8_0, 1, 0.1, out)
+    assert e.value.code == kvt.EUNSUPPORTED            # group 8
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 11, None, None, 10, kvt.Q8_0, 1, 0.1, out)
+    assert e.value.code == kvt.EINVAL                  # n_head > n_kv
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 5, None, None, 10, kvt.Q8_0, 1, 0.1, out)
+    assert e.value.code == kvt.EINVAL                  # tail rows without tail pointers
