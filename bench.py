@@ -42,7 +42,9 @@ def parse():
     p.add_argument("--layout", default="block_head_major",
                    choices=["block_head_major", "token_major"],
                    help="host K/V plane layout (block-local head-major, or token-major)")
-    p.add_argument("--suite", action="store_true", help="also measure the other workloads")
+    p.add_argument("--suite", nargs="?", const="all", default=None,
+                   help="also measure the other workloads: all, or a comma list of "
+                        "prefill, swap1, small, swap32, decode1m")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the CPU-oracle baseline's wall time")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -561,23 +563,31 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
 
 
 def run_suite(torch, kvt, synth, dev, wl, args, peaks):
+    want = set(args.suite.split(",")) if args.suite != "all" else {
+        "prefill", "swap1", "small", "swap32", "decode1m"}
     out = {}
-    log("suite: tiered prefill")
-    out["tiered_prefill"] = suite_prefill(torch, kvt, synth, dev, peaks)
-    log("suite: one-layer swap")
-    out["swap_1_layer"] = suite_one_layer(torch, kvt, synth, dev, peaks)
-    log("suite: small pages")
-    out["small_pages"] = suite_small_pages(torch, kvt, synth, dev, peaks)
-    log("suite: 32-layer swap")
-    out["swap_32_layers"] = suite_32_layers(torch, kvt, synth, dev, peaks)
-    log("suite: decode at 1,048,576")
-    w1m = DecodeWorkload(torch, kvt, synth, dev, 1 << 20, args.warmup + 2 * args.steps)
-    r = w1m.run(args.steps, args.warmup)
-    out["decode_1m"] = {"ms_per_step": round(r["ms_per_step"], 5),
-                        "decode_tok_s": round(1e3 / r["ms_per_step"], 2),
-                        "gather_gbs_whole_step": round(w1m.gather_bytes / (r["ms_per_step"] * 1e-3) / GB, 3),
-                        "part_ms": {k: round(v, 5) for k, v in r["part_ms"].items()}}
-    w1m.free()
+    if "prefill" in want:
+        log("suite: tiered prefill")
+        out["tiered_prefill"] = suite_prefill(torch, kvt, synth, dev, peaks)
+    if "swap1" in want:
+        log("suite: one-layer swap")
+        out["swap_1_layer"] = suite_one_layer(torch, kvt, synth, dev, peaks)
+    if "small" in want:
+        log("suite: small pages")
+        out["small_pages"] = suite_small_pages(torch, kvt, synth, dev, peaks)
+    if "swap32" in want:
+        log("suite: 32-layer swap")
+        out["swap_32_layers"] = suite_32_layers(torch, kvt, synth, dev, peaks)
+    if "decode1m" in want:
+        log("suite: decode at 1,048,576")
+        w1m = DecodeWorkload(torch, kvt, synth, dev, 1 << 20, args.warmup + 2 * args.steps)
+        r = w1m.run(args.steps, args.warmup)
+        out["decode_1m"] = {"ms_per_step": round(r["ms_per_step"], 5),
+                            "decode_tok_s": round(1e3 / r["ms_per_step"], 2),
+                            "gather_gbs_whole_step":
+                                round(w1m.gather_bytes / (r["ms_per_step"] * 1e-3) / GB, 3),
+                            "part_ms": {k: round(v, 5) for k, v in r["part_ms"].items()}}
+        w1m.free()
     return out
 
 

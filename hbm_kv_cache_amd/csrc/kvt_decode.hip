@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
         l[i] = 0.f;
 #pragma unroll
         for (int nt = 0; nt < 4; nt++) {
-            const float p = m[i] == -INFINITY ? 0.f : exp2f(s[nt][i] - m[i]);
+            const float p = m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[nt][i] - m[i]);
             ps[nt * 16 + col][4 * g + i] = p;
             l[i] += p;
         }
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kHd) void decode_merge(const float *__restrict__ pa
         for (int c = 0; c < n_chunks; c++) {
             const float *pb = base + c * cstride;
             const float mc = pb[kHd];
-            const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
+            const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
             acc = fmaf(pb[d], w, acc);
             l = fmaf(pb[kHd + 1], w, l);
         }

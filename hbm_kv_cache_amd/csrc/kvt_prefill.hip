@@ -8,16 +8,22 @@
 // is staged, read in place from host memory, or the whole cache is in HBM.
 //
 // Per workgroup: one KV head (blockIdx.x % kvh, so on an 8-XCD part with kvh = 8 each XCD
-// streams one head's K/V through its own L2) and 128 query rows (32 queries x 4 query heads of
-// the group for G = 4), one wave per 32 rows.  Per 64-key tile:
-//   * each thread loads one q8_0 block (key = lane, block = wave) of K and of V -- the loads of
-//     tile t+1 are issued before tile t is computed -- and dequantises it to fp16 with a
-//     magic-number conversion (int8 -> 1024 + 128 + q in fp16, subtract 1152 exactly, times
-//     the block scale: one rounding, to nearest): K as rows [key][d], V transposed [d][key];
+// streams one head's K/V through its own L2) and 256 query rows -- for G = 4, 64 queries x the
+// 4 query heads of the group -- one wave per 32 rows.  Per 64-key tile:
+//   * the tile's raw q8_0 head slices (64 keys x 136 bytes per plane, 1088 bytes apart in the
+//     cache rows) are read with coalesced 8-byte loads -- consecutive lanes on consecutive words
+//     of one slice, so a load instruction touches a handful of cache lines rather than one per
+//     lane -- and parked in LDS;
+//   * every thread then owns one q8_0 block of the tile (plane K or V, key = lane, block 0..3)
+//     and dequantises it to fp16 with a magic-number conversion (the int8 byte under 0x64 is
+//     1024 + 128 + q in fp16; subtracting 1152 is exact; times the block scale is the one
+//     rounding, to nearest): K as rows [key][d], V transposed [d][key].  Raw and fp16 tiles
+//     are double buffered: tile t+1 is dequantised while tile t is multiplied, one barrier per
+//     tile, with the loads of tiles t+2 and t+3 in flight;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (K from LDS, Q held in registers);
-//   * online softmax in fp32 (log2 domain, scale folded into one multiply), probabilities
-//     rounded to fp16 -- and the row sums taken over the rounded values, so each output row is
-//     an exact convex combination of V rows with those weights;
+//   * online softmax in fp32 in the log2 domain: p = exp2(s*c - m*c) with the scale c folded
+//     into one FMA and the exponential on the bare v_exp_f32 (results below 2^-126 flush to
+//     zero, which no probability sum notices); probabilities rounded to fp16 in pairs;
 //   * O^T += V^T P^T on the same MFMA.  Computing S transposed leaves every lane holding the
 //     16 probabilities of one query row in the MFMA B-operand layout, so P needs no shuffle:
 //     the k-slots of a PV step are the keys {16s + 4g + 0..3, 16s + 8 + 4g + 0..3} (g = lane/32)
@@ -31,7 +37,7 @@ namespace {
 
 constexpr int kHd = 128;
 constexpr int kKT = 64;                        // keys per tile
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlk = 34;                       // q8_0 block: fp16 scale + 32 int8
 constexpr int kHeadBytes = (kHd / 32) * kBlk;  // one head's slice of a row: 136 bytes
@@ -39,26 +45,23 @@ constexpr int kKPitch = kHd * 2 + 16;          // LDS bytes per dequantised K ro
 constexpr int kVtPitch = kKT * 2 + 8;          // LDS bytes per dequantised V^T row (136)
 constexpr int kLdsK = kKT * kKPitch;
 constexpr int kLdsV = kHd * kVtPitch;
+constexpr int kLdsBuf = kLdsK + kLdsV;         // one tile, K and V^T
+constexpr int kRawPlane = kKT * kHeadBytes;    // one plane's head slices of a tile (8704 B)
+constexpr int kRawBytes = 2 * kRawPlane;       // K and V
+constexpr int kRawWords = kRawBytes / 8;       // 8-byte words per tile (2176)
+constexpr int kRawPerThread = (kRawWords + kThreads - 1) / kThreads;
 constexpr int kOutPitch = 33;                  // floats per row of the output transpose buffer
-static_assert(kWaves * 32 * kOutPitch * 4 <= kLdsK, "output staging reuses the K tile");
+static_assert(kWaves * 32 * kOutPitch * 4 <= 2 * kLdsBuf, "output staging reuses the tiles");
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// The 9 dwords that cover q8_0 block b of a head slice (36 bytes from byte 4*floor(34b/4)).
-__device__ __forceinline__ void load_block(const unsigned char *row, int b, uint32_t w[9])
-{
-    const uint32_t *p = reinterpret_cast<const uint32_t *>(row + 4 * ((kBlk * b) >> 2));
-#pragma unroll
-    for (int k = 0; k < 9; k++)
-        w[k] = __builtin_nontemporal_load(p + k);
 }
 
 // q8_0 block -> 32 fp16 values (16 dwords, element order).  odd: the block starts 2 bytes
@@ -82,6 +85,75 @@ __device__ __forceinline__ void dequant_block(const uint32_t w[9], bool odd, uin
     }
 }
 
+
+// Coalesced 8-byte loads of tile `tile`: word f is plane f / 1088, key (f % 1088) / 17,
+// byte 8 * (f % 17) of that key's 136-byte head slice.
+// k_head ... v_tail already point at this workgroup's head slice (offset h * 136 added).
+__device__ __forceinline__ void load_raw(const unsigned char *k_head, const unsigned char *v_head,
+                                         const unsigned char *k_tail, const unsigned char *v_tail,
+                                         int64_t n_head, int64_t n_kv, int64_t row_bytes, int tile,
+                                         uint64_t (&rq)[kRawPerThread])
+{
+#pragma unroll
+    for (int u = 0; u < kRawPerThread; u++) {
+        const int f = threadIdx.x + u * kThreads;
+        if (f < kRawWords) {
+            const int plane = f >= kRawWords / 2;
+            const int rem = f - plane * (kRawWords / 2);
+            const int kin = rem / (kHeadBytes / 8), w = rem - kin * (kHeadBytes / 8);
+            int64_t key = (int64_t)tile * kKT + kin;
+            key = key < n_kv ? key : n_kv - 1;
+            const bool in_head = key < n_head;
+            const unsigned char *hb = plane ? v_head : k_head;
+            const unsigned char *tb = plane ? v_tail : k_tail;
+            const unsigned char *rowp = in_head ? hb + key * row_bytes
+                                                : tb + (key - n_head) * row_bytes;
+            rq[u] = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(rowp + 8 * w));
+        }
+    }
+}
+
+// Word f goes to byte 8*f: the raw tile in LDS is [plane][key][136 bytes].
+__device__ __forceinline__ void store_raw(unsigned char *rawbuf, const uint64_t (&rq)[kRawPerThread])
+{
+#pragma unroll
+    for (int u = 0; u < kRawPerThread; u++) {
+        const int f = threadIdx.x + u * kThreads;
+        if (f < kRawWords)
+            *reinterpret_cast<uint64_t *>(rawbuf + 8 * f) = rq[u];
+    }
+}
+
+// Thread (plane = wave / 4, block = wave % 4, key = lane) dequantises its q8_0 block of the raw
+// tile into the fp16 tile: K as rows [key][d], V transposed [d][key].
+__device__ __forceinline__ void dequant_tile(const unsigned char *rawbuf, unsigned char *buf,
+                                             int wave, int lane)
+{
+    const bool is_v = wave >= 4;
+    const int blk = wave & 3;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(
+        rawbuf + (is_v ? kRawPlane : 0) + lane * kHeadBytes + 4 * ((kBlk * blk) >> 2));
+    uint32_t w[9];
+#pragma unroll
+    for (int k = 0; k < 9; k++)
+        w[k] = src[k];
+    uint32_t d[16];
+    dequant_block(w, blk & 1, d);
+    if (!is_v) {
+        unsigned char *kdst = buf + lane * kKPitch + blk * 64;
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+            *reinterpret_cast<u32x4 *>(kdst + 16 * c) =
+                u32x4{d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]};
+    } else {
+        unsigned char *vdst = buf + kLdsK + (blk * 32) * kVtPitch + lane * 2;
+#pragma unroll
+        for (int e = 0; e < 32; e++)
+            *reinterpret_cast<uint16_t *>(vdst + e * kVtPitch) =
+                (uint16_t)(d[e >> 1] >> ((e & 1) * 16));
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     const _Float16 *__restrict__ q, int64_t n_q, int64_t q_pos0, int n_qh, int kvh, int group,
     const unsigned char *__restrict__ k_head, const unsigned char *__restrict__ v_head,
@@ -89,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     const unsigned char *__restrict__ v_tail, int64_t n_kv, int causal, float scale_log2,
     float *__restrict__ out)
 {
-    __shared__ __align__(16) unsigned char lds_k[kLdsK];
-    __shared__ __align__(16) unsigned char lds_v[kLdsV];
+    __shared__ __align__(16) unsigned char lds[2 * kLdsBuf + 2 * kRawBytes];
+    unsigned char *const lds_raw = lds + 2 * kLdsBuf;   // two raw (q8_0) tiles
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, i = lane & 31;
@@ -128,46 +200,36 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
 #pragma unroll
     for (int dt = 0; dt < 4; dt++)
         o[dt] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f;   // running max (raw logits) and sum
 
-    // this thread's q8_0 block in the dequantisation: key = lane of the tile, block = wave
-    const int blk = wave;
-    const bool odd = blk & 1;
-    uint32_t rk[9], rv[9];
-    auto load_tile = [&](int tile) {
-        int64_t key = (int64_t)tile * kKT + lane;
-        key = key < n_kv ? key : n_kv - 1;
-        const bool in_head = key < n_head;
-        const int64_t r = in_head ? key : key - n_head;
-        const unsigned char *kr = (in_head ? k_head : k_tail) + r * row_bytes + h * kHeadBytes;
-        const unsigned char *vr = (in_head ? v_head : v_tail) + r * row_bytes + h * kHeadBytes;
-        load_block(kr, blk, rk);
-        load_block(vr, blk, rv);
-    };
-    if (n_tiles > 0)
-        load_tile(0);
+    // the four cache bases, moved to this workgroup's head slice
+    const unsigned char *kh = k_head + h * kHeadBytes, *vh = v_head + h * kHeadBytes;
+    const unsigned char *kt = k_tail + h * kHeadBytes, *vt = v_tail + h * kHeadBytes;
+    uint64_t rq[kRawPerThread];
 
+    // prologue: raw tile 0 -> LDS; fp16 tile 0 and raw tile 1 ready; loads of tile 2 in flight
+    if (n_tiles > 0) {
+        load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, 0, rq);
+        store_raw(lds_raw, rq);
+        if (n_tiles > 1)
+            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, 1, rq);
+    }
+    __syncthreads();
+    if (n_tiles > 0) {
+        dequant_tile(lds_raw, lds, wave, lane);
+        if (n_tiles > 1)
+            store_raw(lds_raw + kRawBytes, rq);
+        if (n_tiles > 2)
+            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, 2, rq);
+    }
+    __syncthreads();
+
+    // per tile: multiply fp16 buffer (tile & 1); dequantise raw tile+1 into the other fp16
+    // buffer; move the registers of tile+2 into the raw buffer tile+1 just left; one barrier;
+    // then issue the loads of tile+3
     for (int tile = 0; tile < n_tiles; tile++) {
-        // dequantise this tile into LDS: K rows [key][d], V transposed [d][key]
-        {
-            uint32_t dk[16], dv[16];
-            dequant_block(rk, odd, dk);
-            dequant_block(rv, odd, dv);
-            unsigned char *kdst = lds_k + lane * kKPitch + blk * 64;
-#pragma unroll
-            for (int c = 0; c < 4; c++)
-                *reinterpret_cast<u32x4 *>(kdst + 16 * c) =
-                    u32x4{dk[4 * c], dk[4 * c + 1], dk[4 * c + 2], dk[4 * c + 3]};
-            unsigned char *vdst = lds_v + (blk * 32) * kVtPitch + lane * 2;
-#pragma unroll
-            for (int e = 0; e < 32; e++)
-                *reinterpret_cast<uint16_t *>(vdst + e * kVtPitch) =
-                    (uint16_t)(dv[e >> 1] >> ((e & 1) * 16));
-        }
-        __syncthreads();
-        if (tile + 1 < n_tiles)
-            load_tile(tile + 1);
-
+        const unsigned char *lk = lds + (tile & 1) * kLdsBuf;
+        const unsigned char *lv = lk + kLdsK;
         const int64_t key0 = (int64_t)tile * kKT;
         if (key0 <= wave_last) {
             // S^T tile: rows = keys 32*st + (lane & 31), columns = this wave's 32 query rows
@@ -177,42 +239,47 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
 #pragma unroll
                 for (int st = 0; st < 2; st++) {
                     const f16x8 a = *reinterpret_cast<const f16x8 *>(
-                        lds_k + (32 * st + i) * kKPitch + (16 * kd + 8 * g) * 2);
+                        lk + (32 * st + i) * kKPitch + (16 * kd + 8 * g) * 2);
                     s[st] = mfma32(a, qb[kd], s[st]);
                 }
             }
             // lane holds S[query i][key0 + 32*st + 8*(r/4) + 4*g + r%4] in s[st][r]
             const bool need_mask = key0 + kKT - 1 > (causal ? pos_first : n_kv - 1) ||
                                    key0 + kKT > n_kv;
+            if (need_mask) {
+                // last visible key of this lane's query, relative to the tile, in [-1, 64]
+                int64_t lim = (causal && pos_i < n_kv - 1 ? pos_i : n_kv - 1) - key0;
+                lim = lim < -1 ? -1 : (lim > kKT ? kKT : lim);
+                const int lim32 = (int)lim;
+#pragma unroll
+                for (int st = 0; st < 2; st++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++)
+                        if (32 * st + 8 * (r >> 2) + 4 * g + (r & 3) > lim32)
+                            s[st][r] = -INFINITY;
+            }
             float mt = -INFINITY;
 #pragma unroll
-            for (int st = 0; st < 2; st++) {
+            for (int st = 0; st < 2; st++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    float x = s[st][r] * scale_log2;
-                    if (need_mask) {
-                        const int64_t key = key0 + 32 * st + 8 * (r >> 2) + 4 * g + (r & 3);
-                        if (key >= n_kv || (causal && key > pos_i))
-                            x = -INFINITY;
-                    }
-                    s[st][r] = x;
-                    mt = fmaxf(mt, x);
-                }
-            }
+                for (int r = 0; r < 16; r++)
+                    mt = fmaxf(mt, s[st][r]);
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
             const float m_new = fmaxf(m, mt);
-            const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+            // every logit is scaled by c > 0, so the max commutes with the scaling
+            const float mc = m_new == -INFINITY ? 0.f : m_new * scale_log2;
+            const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m * scale_log2 - mc);
             uint32_t pk[2][8];   // fp16 probabilities, packed in pairs
             float psum = 0.f;
 #pragma unroll
             for (int st = 0; st < 2; st++) {
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
-                    const float p0 = m_new == -INFINITY ? 0.f : exp2f(s[st][r] - m_new);
-                    const float p1 = m_new == -INFINITY ? 0.f : exp2f(s[st][r + 1] - m_new);
-                    const h2 ph = {(_Float16)p0, (_Float16)p1};
-                    psum += (float)ph[0] + (float)ph[1];
-                    pk[st][r >> 1] = __builtin_bit_cast(uint32_t, ph);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][r], scale_log2, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][r + 1], scale_log2, -mc));
+                    psum += p0 + p1;
+                    pk[st][r >> 1] =
+                        __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, h2));
                 }
             }
             psum += __shfl_xor(psum, 32, 64);
@@ -233,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
                     f16x8, u32x4{pk[st][r0], pk[st][r0 + 1], pk[st][r0 + 2], pk[st][r0 + 3]});
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++) {
-                    const unsigned char *vrow = lds_v + (32 * dt + i) * kVtPitch;
+                    const unsigned char *vrow = lv + (32 * dt + i) * kVtPitch;
                     const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + 2 * (16 * ks + 4 * g));
                     const f16x4 hi =
                         *reinterpret_cast<const f16x4 *>(vrow + 2 * (16 * ks + 8 + 4 * g));
@@ -242,12 +309,19 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
                 }
             }
         }
+        if (tile + 1 < n_tiles)
+            dequant_tile(lds_raw + ((tile + 1) & 1) * kRawBytes, lds + ((tile + 1) & 1) * kLdsBuf,
+                         wave, lane);
+        if (tile + 2 < n_tiles)
+            store_raw(lds_raw + (tile & 1) * kRawBytes, rq);
         __syncthreads();
+        if (tile + 3 < n_tiles)
+            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 3, rq);
     }
 
-    // normalise and write O[query][qh][d] through LDS (reusing the K tile), 32 d at a time
+    // normalise and write O[query][qh][d] through LDS (reusing the tiles), 32 d at a time
     const float inv_l = l > 0.f ? 1.f / l : 0.f;
-    float *buf = reinterpret_cast<float *>(lds_k) + wave * 32 * kOutPitch;
+    float *buf = reinterpret_cast<float *>(lds) + wave * 32 * kOutPitch;
 #pragma unroll
     for (int dt = 0; dt < 4; dt++) {
 #pragma unroll
@@ -283,9 +357,11 @@ extern "C" int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int3
     if (kvh < 1 || n_qh < 1 || n_qh % kvh)
         return kvt::fail(KVT_EINVAL, "kvt_attn_prefill: n_qh=%d kvh=%d", n_qh, kvh);
     const int group = n_qh / kvh;
-    if (group != 1 && group != 2 && group != 4)
-        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_prefill: group %d (this build: 1, 2, 4)",
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_prefill: group %d (this build: 1, 2, 4, 8)",
                          group);
+    if (!(scale > 0.f))
+        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill: scale must be positive");
     if (n_q < 0 || q_pos0 < 0 || n_kv < 0 || n_head < 0 || n_head > n_kv)
         return kvt::fail(KVT_EINVAL, "kvt_attn_prefill: n_q=%lld q_pos0=%lld n_head=%lld n_kv=%lld",
                          (long long)n_q, (long long)q_pos0, (long long)n_head, (long long)n_kv);
@@ -294,9 +370,9 @@ extern "C" int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int3
     if (!q || !out || (n_head > 0 && (!k_head || !v_head)) ||
         (n_kv > n_head && (!k_tail || !v_tail)))
         return kvt::fail(KVT_EINVAL, "kvt_attn_prefill: null pointer");
-    if (!kvt::aligned(q, 16) || !kvt::aligned(out, 16) || !kvt::aligned(k_head, 4) ||
-        !kvt::aligned(v_head, 4) || !kvt::aligned(k_tail, 4) || !kvt::aligned(v_tail, 4))
-        return kvt::fail(KVT_EALIGN, "kvt_attn_prefill: q/out need 16-byte, K/V 4-byte alignment");
+    if (!kvt::aligned(q, 16) || !kvt::aligned(out, 16) || !kvt::aligned(k_head, 8) ||
+        !kvt::aligned(v_head, 8) || !kvt::aligned(k_tail, 8) || !kvt::aligned(v_tail, 8))
+        return kvt::fail(KVT_EALIGN, "kvt_attn_prefill: q/out need 16-byte, K/V 8-byte alignment");
     const int qpw = 32 * (kWaves / group);
     const int64_t q_tiles = (n_q + qpw - 1) / qpw;
     if (q_tiles * kvh > 0x7fffffffll)

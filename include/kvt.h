@@ -205,8 +205,8 @@ int kvt_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd, int32_
  *          (KVT_Q8_0: hd/32 blocks of 34 bytes per head, head-major)
  *   causal nonzero: row t sees keys j <= q_pos0 + t (j < n_kv); zero: all n_kv keys
  *   out    device fp32 [n_q][n_qh][hd]
- * Limits: kv_format KVT_Q8_0, hd == 128, n_qh/kvh in {1, 2, 4}; q and out 16-byte aligned,
- * K/V pointers 4-byte aligned.  Deterministic: the same inputs give the same bits, however
+ * Limits: kv_format KVT_Q8_0, hd == 128, n_qh/kvh in {1, 2, 4, 8}, scale > 0; q and out 16-byte aligned,
+ * K/V pointers 8-byte aligned.  Deterministic: the same inputs give the same bits, however
  * the rows are split between head and tail.
  * ---------------------------------------------------------------------------------------- */
 int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh,

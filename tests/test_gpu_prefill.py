@@ -44,6 +44,7 @@ def _dev(a, dev):
     (700, 33, 8, 4, False, 350),        # non-causal, group 2
     (333, 40, 4, 4, True, 64),          # group 1
     (130, 130, 8, 2, True, 65),         # queries from position 0: first row sees one key
+    (600, 50, 16, 2, True, 300),        # group 8
 ])
 def test_prefill_matches_oracle(gpu, n_kv, n_q, n_qh, kvh, causal, n_head):
     k, v = _cache(n_kv, kvh, n_kv + n_q)
@@ -149,8 +150,11 @@ def test_prefill_argument_errors(gpu):
         kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 10, None, None, 10, kvt.F16, 1, 0.1, out)
     assert e.value.code == kvt.EUNSUPPORTED
     with pytest.raises(kvt.KvtError) as e:
-        kvt.kvt_attn_prefill(q, 4, 0, 8, 1, 128, k, k, 10, None, None, 10, kvt.Q8_0, 1, 0.1, out)
-    assert e.value.code == kvt.EUNSUPPORTED            # group 8
+        kvt.kvt_attn_prefill(q, 4, 0, 16, 1, 128, k, k, 10, None, None, 10, kvt.Q8_0, 1, 0.1, out)
+    assert e.value.code == kvt.EUNSUPPORTED            # group 16
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 10, None, None, 10, kvt.Q8_0, 1, 0.0, out)
+    assert e.value.code == kvt.EINVAL                  # scale must be positive
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 11, None, None, 10, kvt.Q8_0, 1, 0.1, out)
     assert e.value.code == kvt.EINVAL                  # n_head > n_kv
