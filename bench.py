@@ -86,6 +86,14 @@ def measure_link_peaks(torch, kvt, dev, host_buf, nbytes, reps=5):
         t.start()
         kvt.kvt_swap_blocks(tab[0], tab[1], tab[2], 1, kvt.D2H, kvt.COPY_SDMA)
         best_d2h = max(best_d2h, nbytes / (t.stop_ms() * 1e-3) / GB)
+    # the copy kernel over a span of the gather's per-step size (host -> HBM): it is also the
+    # plain copy of known size that scales the gather kernel's FETCH_SIZE / WRITE_SIZE counters
+    span = 8 << 20
+    best_h2d_k = 0.0
+    for _ in range(reps):
+        t.start()
+        kvt.kvt_stage_tail(host_buf.dev, span, 0, 1, hbm, kvt.COPY_KERNEL)
+        best_h2d_k = max(best_h2d_k, span / (t.stop_ms() * 1e-3) / GB)
     # HBM: device-to-device copy of the same buffer size (reads + writes count)
     other = torch.empty_like(hbm)
     best_hbm = 0.0
@@ -96,6 +104,7 @@ def measure_link_peaks(torch, kvt, dev, host_buf, nbytes, reps=5):
     del hbm, other
     tb.free()
     return {"h2d_sdma_gbs": round(best_h2d, 2), "d2h_sdma_gbs": round(best_d2h, 2),
+            "h2d_copy_kernel_8mib_gbs": round(best_h2d_k, 2),
             "hbm_copy_gbs": round(best_hbm, 1), "bytes": nbytes}
 
 
@@ -112,9 +121,11 @@ class DecodeWorkload:
         "token_major": lambda kvh, hd, bt: (bt * kvh * hd * 2, hd * 2, kvh * hd * 2),
     }
 
-    def __init__(self, torch, kvt, synth, dev, ctx, n_sets, layout="block_head_major"):
+    def __init__(self, torch, kvt, synth, dev, ctx, n_sets, layout="block_head_major",
+                 mode="fused"):
         import numpy as np
         self.torch, self.kvt, self.dev, self.ctx = torch, kvt, dev, ctx
+        self.mode = mode   # "fused": gather + attention in one pass; "staged": three kernels
         kvh, hd, bt, k = self.KVH, self.HD, self.BT, self.K
         self.n_blocks = ctx // bt
         self.row = kvh * hd * 2
@@ -164,15 +175,35 @@ class DecodeWorkload:
                             self.kv[0], self.kv[1], self.K * self.BT, None, self.scale, self.out,
                             self.ws[self.ws_t + 128:], self.ws_d)
 
+    def fused(self, i):
+        kvt = self.kvt
+        kvt.kvt_gather_attn_decode(self.q[i % self.n_sets], self.NQH, self.KVH, self.HD, kvt.BF16,
+                                   self.host.dev, self.host.dev + self.ctx * self.row,
+                                   self.n_blocks, *self.strides, None, self.BT, self.ids, self.K,
+                                   self.kv[0], self.kv[1], self.scale, self.out,
+                                   self.ws[self.ws_t + 128:], self.ws_d)
+
     def step(self, i):
         self.topk(i)
-        self.gather()
-        self.attend(i)
+        if self.mode == "fused":
+            self.fused(i)
+        else:
+            self.gather()
+            self.attend(i)
 
-    def run(self, steps, warmup):
+    def parts(self, i):
+        """The step's launches as (name, callable) pairs, for per-part event timing."""
+        if self.mode == "fused":
+            return [("topk", lambda: self.topk(i)), ("gather_attn", lambda: self.fused(i))]
+        return [("topk", lambda: self.topk(i)), ("gather", self.gather),
+                ("attn", lambda: self.attend(i))]
+
+    def run(self, steps, warmup, base=0):
+        """warmup + 2*steps steps on query sets base, base+1, ..."""
         torch = self.torch
         stream = torch.cuda.current_stream()
-        for i in range(warmup):
+        warmup += base   # query-set indices below run from base on
+        for i in range(base, warmup):
             self.step(i)
         torch.cuda.synchronize()
         # whole-step timing: host clock and events around exactly `steps` steps
@@ -187,23 +218,21 @@ class DecodeWorkload:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ev_ms = ev0.elapsed_time(ev1)
-        # per-kernel timing pass: events bracketing each launch on the same stream
-        parts = {"topk": [], "gather": [], "attn": []}
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        # per-part timing pass: events bracketing each launch on the same stream
+        names = [n for n, _ in self.parts(0)]
+        parts = {n: [] for n in names}
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+               for _ in range(steps)]
         for i in range(steps):
             e = evs[i]
             e[0].record(stream)
-            self.topk(warmup + steps + i)
-            e[1].record(stream)
-            self.gather()
-            e[2].record(stream)
-            self.attend(warmup + steps + i)
-            e[3].record(stream)
+            for j, (_, fn) in enumerate(self.parts(warmup + steps + i)):
+                fn()
+                e[j + 1].record(stream)
         torch.cuda.synchronize()
         for e in evs:
-            parts["topk"].append(e[0].elapsed_time(e[1]))
-            parts["gather"].append(e[1].elapsed_time(e[2]))
-            parts["attn"].append(e[2].elapsed_time(e[3]))
+            for j, n in enumerate(names):
+                parts[n].append(e[j].elapsed_time(e[j + 1]))
         avg = {k: sum(v) / len(v) for k, v in parts.items()}
         return {"wall_s": wall, "event_ms": ev_ms, "ms_per_step": max(wall * 1e3, ev_ms) / steps,
                 "part_ms": avg}
@@ -211,6 +240,25 @@ class DecodeWorkload:
     def free(self):
         self.planes = None
         self.host.free()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PMC_RECORD = os.path.join(ROOT, "profiles", "decode_step_262k_pmc.json")
+
+
+def kernel_traffic(kernel):
+    """Bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE record, each
+    counter scaled by what it read for a plain copy kernel of known size.  None when there is
+    no record, or it was taken on another version of the kernel's source file."""
+    import hashlib
+    try:
+        rec = json.load(open(PMC_RECORD))["kernels"][kernel]
+        src = hashlib.sha256(open(os.path.join(ROOT, rec["source"]), "rb").read()).hexdigest()
+    except (OSError, ValueError, KeyError, TypeError):
+        return None
+    if rec.get("source_sha256") != src:
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(wl, seconds):
@@ -260,23 +308,32 @@ def main():
     dev = torch.device("cuda:0")
     log("device", torch.cuda.get_device_name(0))
 
-    n_sets = args.warmup + 2 * args.steps
-    wl = DecodeWorkload(torch, kvt, synth, dev, args.ctx, n_sets, args.layout)
+    n_run = args.warmup + 2 * args.steps
+    n_other = 5 + 2 * max(20, args.steps // 4)
+    wl = DecodeWorkload(torch, kvt, synth, dev, args.ctx, 2 * n_run + n_other, args.layout)
     peaks = measure_link_peaks(torch, kvt, dev, wl.host, 1 << 30)
     log("link peaks", peaks)
-    r = wl.run(args.steps, args.warmup)
-    log("decode", r)
+    # every run draws its own queries (hence its own selections): no host rows are re-read
+    r = wl.run(args.steps, args.warmup, base=0)
+    log("decode (fused gather + attention)", r)
+    wl.mode = "staged"
+    r_staged = wl.run(args.steps, args.warmup, base=n_run)
+    wl.mode = "fused"
+    log("decode (gather, then attention)", r_staged)
     # the same planes read through the other layout's strides: context for the layout choice
     other = "token_major" if args.layout == "block_head_major" else "block_head_major"
     keep = wl.strides
     wl.strides = wl.LAYOUTS[other](wl.KVH, wl.HD, wl.BT)
-    r_other = wl.run(max(20, args.steps // 4), 5)
+    r_other = wl.run(max(20, args.steps // 4), 5, base=2 * n_run)
     wl.strides = keep
     log(f"decode with {other} host planes", r_other)
 
+    def gbs(ms_):
+        return round(wl.gather_bytes / (ms_ * 1e-3) / GB, 3)
+
     ms = r["ms_per_step"]
-    gather_ms = r["part_ms"]["gather"]
-    achieved = wl.gather_bytes / (gather_ms * 1e-3) / GB
+    kern_ms = r["part_ms"]["gather_attn"]
+    achieved = wl.gather_bytes / (kern_ms * 1e-3) / GB
     value = wl.gather_bytes / (ms * 1e-3) / GB
     line = {
         "metric": "host->HBM KV gather GB/s (% PCIe peak); tiered decode tok/s at 262k ctx",
@@ -293,27 +350,39 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 K/V in pinned host memory, fp16 pooled plane)",
         "config": {"workload": f"top-k sparse decode step, batch 1, ctx {args.ctx}: score "
                                f"{wl.n_blocks} pooled blocks x 8 KV heads, top-32 per head, "
-                               "gather K/V (8 heads x 128 bf16, 64-token blocks) host->HBM, "
-                               "GQA attention 64 q heads",
+                               "gather K/V (8 heads x 128 bf16, 64-token blocks) host->HBM "
+                               "and GQA attention (64 q heads) over them in one pass",
                    "ctx": args.ctx, "kv_heads": 8, "head_dim": 128, "q_heads": 64,
                    "block_tokens": 64, "topk": 32, "gather_bytes_per_step": wl.gather_bytes,
                    "host_layout": args.layout},
         "decode_tok_s": round(1e3 / ms, 2),
-        f"{other}_host_layout": {
-            "ms_per_step": round(r_other["ms_per_step"], 5),
-            "decode_tok_s": round(1e3 / r_other["ms_per_step"], 2),
-            "gather_kernel_gbs": round(wl.gather_bytes / (r_other["part_ms"]["gather"] * 1e-3) / GB, 3)},
         "pct_pcie_peak": round(100 * value / PCIE5_X16_PEAK_GBS, 2),
         "pct_measured_h2d_peak": round(100 * value / peaks["h2d_sdma_gbs"], 2),
         "part_ms": {k: round(v, 5) for k, v in r["part_ms"].items()},
+        "staged_path": {
+            "what": "index_topk, gather_blocks, attn_decode as three launches",
+            "value": gbs(r_staged["ms_per_step"]),
+            "ms_per_step": round(r_staged["ms_per_step"], 5),
+            "decode_tok_s": round(1e3 / r_staged["ms_per_step"], 2),
+            "part_ms": {k: round(v, 5) for k, v in r_staged["part_ms"].items()},
+            "gather_kernel_gbs": gbs(r_staged["part_ms"]["gather"])},
+        f"{other}_host_layout": {
+            "value": gbs(r_other["ms_per_step"]),
+            "ms_per_step": round(r_other["ms_per_step"], 5),
+            "decode_tok_s": round(1e3 / r_other["ms_per_step"], 2),
+            "gather_attn_gbs": gbs(r_other["part_ms"]["gather_attn"])},
         "link_peaks": peaks,
-        "roofline": {"bound": "pcie", "kernel": "gather_kernel", "achieved": round(achieved, 3),
+        "roofline": {"bound": "pcie",
+                     "kernel": "gather_decode_partial (timed with its decode_merge: "
+                               "kvt_gather_attn_decode)",
+                     "achieved": round(achieved, 3),
                      "peak": PCIE5_X16_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PCIE5_X16_PEAK_GBS, 4),
                      "peak_measured_h2d": peaks["h2d_sdma_gbs"],
                      "frac_measured": round(achieved / peaks["h2d_sdma_gbs"], 4),
-                     "bytes_per_launch": wl.gather_bytes, "avg_launch_ms": round(gather_ms, 5),
-                     "traffic": None},
+                     "bytes_per_launch": wl.gather_bytes, "avg_launch_ms": round(kern_ms, 5),
+                     "traffic": kernel_traffic("gather_decode_partial"),
+                     "traffic_unit": "bytes per launch"},
     }
     if args.suite:
         line["suite"] = run_suite(torch, kvt, synth, dev, wl, args, peaks)

@@ -21,6 +21,7 @@ namespace {
 constexpr int kHd = 128;
 constexpr int kKeys = 64;   // keys per chunk (4 MFMA column tiles of 16)
 constexpr int kVPitch = kHd * 2 + 4;  // bytes per staged V row (padded)
+constexpr int kKPitch = kHd * 2 + 16; // bytes per staged K row (padded, 16-byte aligned)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -42,54 +43,17 @@ __device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c)
                                                        __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// part layout: [kvh][n_chunks][group][kHd + 2]  (o[kHd], m, l); m, l in the log2 domain
+// Scores, softmax and P*V of one 64-key chunk for one KV head, once the chunk's K operands are
+// in registers and its V rows are in LDS (rows of keys that take no part zeroed).
+// valid: bit j set = key j of the chunk takes part.  Writes the chunk's partial (o, m, l) for
+// the group's query heads to pb.
 template <bool kBf16>
-__global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict__ q, int group,
-                                                     const uint16_t *__restrict__ k,
-                                                     const uint16_t *__restrict__ v, int64_t n_kv,
-                                                     const int32_t *__restrict__ n_valid,
-                                                     float scale_log2, float *__restrict__ part)
+__device__ __forceinline__ void chunk_attend(const uint4 (&qa)[4], const uint4 (&kb)[4][4],
+                                             uint64_t valid, int group, float scale_log2,
+                                             const unsigned char *vs, float (*ps)[16], float *pb,
+                                             int lane)
 {
-    __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
-    __shared__ __align__(16) float ps[kKeys][16];   // probabilities, key-major
-    const int lane = threadIdx.x;
-    const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x;
-    const int64_t key0 = (int64_t)c * kKeys;
     const int g = lane >> 4, col = lane & 15;
-
-    // Every load below is unconditional, from a clamped (always valid) address, so all of them
-    // are in flight together; out-of-range rows are zeroed or masked afterwards.
-    const int qrow = col < group ? col : group - 1;
-    const uint16_t *qh = q + ((int64_t)h * group + qrow) * kHd + 8 * g;
-    uint4 qa[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++)
-        qa[ks] = *reinterpret_cast<const uint4 *>(qh + ks * 32);
-    const uint16_t *kh = k + (int64_t)h * n_kv * kHd;
-    uint4 kb[4][4];
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++) {
-        const int64_t key = min(key0 + nt * 16 + col, n_kv - 1);
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-            kb[nt][ks] = *reinterpret_cast<const uint4 *>(kh + key * kHd + ks * 32 + 8 * g);
-    }
-    const uint16_t *vh = v + (int64_t)h * n_kv * kHd;
-    uint4 vr[16];
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
-        const int64_t key = min(key0 + row, n_kv - 1);
-        vr[j] = *reinterpret_cast<const uint4 *>(vh + key * kHd + cw * 8);
-    }
-    int64_t nv = n_valid ? (int64_t)n_valid[h] : n_kv;
-    nv = nv < n_kv ? nv : n_kv;
-    if (col >= group) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-            qa[ks] = make_uint4(0, 0, 0, 0);
-    }
-
     f32x4 s[4];
 #pragma unroll
     for (int nt = 0; nt < 4; nt++) {
@@ -98,15 +62,6 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
         for (int ks = 0; ks < 4; ks++)
             s[nt] = mfma16x16x32<kBf16>(qa[ks], kb[nt][ks], s[nt]);
     }
-    // V rows of keys that take no part are zeroed: their probability is 0, but 0 * NaN is not
-    // (rows past n_valid may hold anything, e.g. slots a gather skipped)
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
-        const uint4 val = key0 + row < nv ? vr[j] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(vs + row * kVPitch + cw * 16) = val;
-    }
-
     // lane holds S[row 4g+i][key nt*16 + col]; scale into the log2 domain, mask invalid keys
     float m[4], l[4];
 #pragma unroll
@@ -114,7 +69,7 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
         m[i] = -INFINITY;
 #pragma unroll
         for (int nt = 0; nt < 4; nt++) {
-            const bool ok = key0 + nt * 16 + col < nv;
+            const bool ok = (valid >> (nt * 16 + col)) & 1;
             s[nt][i] = ok ? s[nt][i] * scale_log2 : -INFINITY;
             m[i] = fmaxf(m[i], s[nt][i]);
         }
@@ -166,7 +121,6 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
             }
         }
     }
-    float *pb = part + ((int64_t)h * n_chunks + c) * group * (kHd + 2);
 #pragma unroll
     for (int r = 0; r < 16; r++) {
         if (r < group)
@@ -182,6 +136,179 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
             }
         }
     }
+}
+
+// The group's query rows as MFMA A operands (row col of the 16-row tile; rows >= group zero).
+__device__ __forceinline__ void load_q(const uint16_t *__restrict__ q, int h, int group, int lane,
+                                       uint4 (&qa)[4])
+{
+    const int g = lane >> 4, col = lane & 15;
+    const int qrow = col < group ? col : group - 1;
+    const uint16_t *qh = q + ((int64_t)h * group + qrow) * kHd + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+        qa[ks] = *reinterpret_cast<const uint4 *>(qh + ks * 32);
+}
+
+// part layout: [kvh][n_chunks][group][kHd + 2]  (o[kHd], m, l); m, l in the log2 domain
+template <bool kBf16>
+__global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict__ q, int group,
+                                                     const uint16_t *__restrict__ k,
+                                                     const uint16_t *__restrict__ v, int64_t n_kv,
+                                                     const int32_t *__restrict__ n_valid,
+                                                     float scale_log2, float *__restrict__ part)
+{
+    __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
+    __shared__ __align__(16) float ps[kKeys][16];   // probabilities, key-major
+    const int lane = threadIdx.x;
+    const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x;
+    const int64_t key0 = (int64_t)c * kKeys;
+    const int g = lane >> 4, col = lane & 15;
+
+    // Every load below is unconditional, from a clamped (always valid) address, so all of them
+    // are in flight together; out-of-range rows are zeroed or masked afterwards.
+    uint4 qa[4];
+    load_q(q, h, group, lane, qa);
+    const uint16_t *kh = k + (int64_t)h * n_kv * kHd;
+    uint4 kb[4][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) {
+        const int64_t key = min(key0 + nt * 16 + col, n_kv - 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            kb[nt][ks] = *reinterpret_cast<const uint4 *>(kh + key * kHd + ks * 32 + 8 * g);
+    }
+    const uint16_t *vh = v + (int64_t)h * n_kv * kHd;
+    uint4 vr[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
+        const int64_t key = min(key0 + row, n_kv - 1);
+        vr[j] = *reinterpret_cast<const uint4 *>(vh + key * kHd + cw * 8);
+    }
+    int64_t nv = n_valid ? (int64_t)n_valid[h] : n_kv;
+    nv = nv < n_kv ? nv : n_kv;
+    if (col >= group) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            qa[ks] = make_uint4(0, 0, 0, 0);
+    }
+    // V rows of keys that take no part are zeroed: their probability is 0, but 0 * NaN is not
+    // (rows past n_valid may hold anything, e.g. slots a gather skipped)
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
+        const uint4 val = key0 + row < nv ? vr[j] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(vs + row * kVPitch + cw * 16) = val;
+    }
+    const int64_t nvc = nv - key0;   // keys of this chunk that take part: the first nvc
+    const uint64_t valid = nvc >= kKeys ? ~0ull : nvc <= 0 ? 0ull : (1ull << nvc) - 1;
+    float *pb = part + ((int64_t)h * n_chunks + c) * group * (kHd + 2);
+    chunk_attend<kBf16>(qa, kb, valid, group, scale_log2, vs, ps, pb, lane);
+}
+
+// Gather and attend in one pass: the chunk's K/V rows are read straight from the (host-mapped)
+// planes of the selected blocks, optionally written to the HBM gather buffers, and attended.
+// Key j of head h (j < k*bt) is token j % bt of selected slot j / bt.  Each lane owns the
+// 16-byte word cw = lane % 16 of rows lane/16 + 4*jj (jj < 16): every group of 16 lanes reads
+// one contiguous 256-byte row slice, and all 32 loads of a lane are in flight together.
+template <bool kBf16>
+__global__ __launch_bounds__(64) void gather_decode_partial(
+    const uint16_t *__restrict__ q, int group, const unsigned char *__restrict__ kp,
+    const unsigned char *__restrict__ vp, int64_t n_blocks, int64_t block_stride,
+    int64_t head_stride, int64_t token_stride, const int32_t *__restrict__ table, int bt,
+    const int32_t *__restrict__ ids, int kk, uint16_t *__restrict__ k_out,
+    uint16_t *__restrict__ v_out, float scale_log2, float *__restrict__ part)
+{
+    __shared__ __align__(16) unsigned char ksm[kKeys * kKPitch];
+    __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
+    __shared__ __align__(16) float ps[kKeys][16];
+    const int lane = threadIdx.x;
+    const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x;
+    const int n_kv = kk * bt;   // < 2^31, checked by the host
+    const int key0 = c * kKeys;
+    const int rg = lane >> 4, cw = lane & 15;
+    const int32_t *hid = ids + (int64_t)h * kk;
+    const int64_t hoff = (int64_t)h * head_stride + cw * 16;
+
+    // the query rows first: their loads must not queue behind the host reads
+    uint4 qa[4];
+    load_q(q, h, group, lane, qa);
+    // The chunk's keys span at most 64 slots: lane L resolves slot s0 + L (id, then table) to
+    // the byte offset of its block, or -1 when the slot takes no part.
+    const int s0 = (int)((uint32_t)key0 / (uint32_t)bt);
+    int64_t blk = hid[min(s0 + lane, kk - 1)];
+    bool sok = blk >= 0 && blk < n_blocks;
+    if (table) {
+        blk = table[sok ? blk : 0];
+        sok = sok && blk >= 0 && blk < n_blocks;
+    }
+    const int64_t sbase = sok ? blk * block_stride : -1;
+    // byte offsets of this lane's 16 rows (cw*16 -- always a valid address -- for keys that
+    // take no part); bit jj of okb = row rg + 4*jj takes part
+    int slot[16];
+    int64_t base[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; jj++) {
+        const int key = key0 + rg + 4 * jj;
+        slot[jj] = (int)((uint32_t)(key < n_kv ? key : n_kv - 1) / (uint32_t)bt);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; jj++)
+        base[jj] = __shfl(sbase, slot[jj] - s0, 64);
+    int64_t off[16];
+    uint32_t okb = 0;
+#pragma unroll
+    for (int jj = 0; jj < 16; jj++) {
+        const int key = key0 + rg + 4 * jj;
+        const int r = (key < n_kv ? key : n_kv - 1) - slot[jj] * bt;
+        const bool ok = key < n_kv && base[jj] >= 0;
+        off[jj] = ok ? base[jj] + hoff + (int64_t)r * token_stride : (int64_t)cw * 16;
+        okb |= (uint32_t)ok << jj;
+    }
+    // keys that take part, as a chunk bit mask (lanes 0, 16, 32, 48 own rows 4jj + 0..3)
+    uint64_t valid = 0;
+#pragma unroll
+    for (int jj = 0; jj < 16; jj++) {
+        const uint64_t bal = __ballot((okb >> jj) & 1);
+        valid |= ((bal & 1) | ((bal >> 15) & 2) | ((bal >> 30) & 4) | ((bal >> 45) & 8)) << (4 * jj);
+    }
+    // The rows cross the link one K and one V wave-load at a time per wave: with every load of
+    // the step issued at once the link runs ~20% slower (see kvt_gather.hip).  Each pair goes
+    // to LDS -- K as read, V zeroed where the key takes no part -- and, when asked, to the
+    // HBM gather buffers in kvt_gather_blocks' layout (rows of skipped slots untouched).
+#pragma unroll
+    for (int jj = 0; jj < 16; jj++) {
+        const u32x4 kr = *reinterpret_cast<const u32x4 *>(kp + off[jj]);
+        const u32x4 vr = *reinterpret_cast<const u32x4 *>(vp + off[jj]);
+        const int row = rg + 4 * jj;
+        const bool ok = (okb >> jj) & 1;
+        *reinterpret_cast<u32x4 *>(ksm + row * kKPitch + cw * 16) = kr;
+        *reinterpret_cast<u32x4 *>(vs + row * kVPitch + cw * 16) = ok ? vr : u32x4{0, 0, 0, 0};
+        if (k_out && ok) {
+            const int64_t e = ((int64_t)h * n_kv + key0 + row) * kHd + cw * 8;
+            *reinterpret_cast<u32x4 *>(k_out + e) = kr;
+            *reinterpret_cast<u32x4 *>(v_out + e) = vr;
+        }
+        __asm__ volatile("" ::: "memory");   // keep the next pair behind this one
+    }
+    __syncthreads();
+    if ((lane & 15) >= group) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            qa[ks] = make_uint4(0, 0, 0, 0);
+    }
+    // K as MFMA B operands: lane (g, col) takes key nt*16 + col, dims ks*32 + 8g .. +7
+    const int g = lane >> 4, col = lane & 15;
+    uint4 kb[4][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++)
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+            kb[nt][ks] = *reinterpret_cast<const uint4 *>(ksm + (nt * 16 + col) * kKPitch +
+                                                          ks * 64 + 16 * g);
+    float *pb = part + ((int64_t)h * n_chunks + c) * group * (kHd + 2);
+    chunk_attend<kBf16>(qa, kb, valid, group, scale_log2, vs, ps, pb, lane);
 }
 
 // grid = n_qh, block = kHd.  Two passes over the chunks (global max, then the weighted sums),
@@ -262,6 +389,70 @@ extern "C" int kvt_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t
                                n_kv, n_valid, scale_log2, part);
         KVT_LAUNCHED("decode_partial");
     }
+    hipLaunchKernelGGL(decode_merge, dim3(n_qh), dim3(kHd), 0, s, part, group, (int)chunks, out);
+    KVT_LAUNCHED("decode_merge");
+    return KVT_OK;
+}
+
+// S5+S6 in one pass: QSA-KVO's decode reads the selected K/V blocks through base pointers and
+// computed offsets; here each chunk's rows cross the host link straight into the wave that
+// attends them (and, when k_out/v_out are given, into the HBM gather buffers as well).
+extern "C" int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd,
+                                      int32_t dtype, const void *k_plane, const void *v_plane,
+                                      int64_t n_blocks, int64_t block_stride, int64_t head_stride,
+                                      int64_t token_stride, const int32_t *block_table, int32_t bt,
+                                      const int32_t *ids, int32_t k, void *k_out, void *v_out,
+                                      float scale, float *out, void *ws, size_t ws_bytes,
+                                      void *stream)
+{
+    if (hd != kHd)
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_gather_attn_decode: hd=%d (this build: 128)", hd);
+    if (dtype != KVT_BF16 && dtype != KVT_F16)
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_gather_attn_decode: dtype=%d", dtype);
+    if (n_qh < 1 || kvh < 1 || n_qh % kvh || n_qh / kvh > 16 || kvh > 65535 || bt < 1 || k < 1 ||
+        n_blocks < 1)
+        return kvt::fail(KVT_EINVAL,
+                         "kvt_gather_attn_decode: n_qh=%d kvh=%d bt=%d k=%d n_blocks=%lld", n_qh,
+                         kvh, bt, k, (long long)n_blocks);
+    if ((int64_t)k * bt > 0x7fffffffll - kKeys)
+        return kvt::fail(KVT_ERANGE, "kvt_gather_attn_decode: k*bt too large");
+    if (block_stride % 16 || head_stride % 16 || token_stride % 16 || block_stride < 0 ||
+        head_stride < 0 || token_stride < 0)
+        return kvt::fail(KVT_EALIGN,
+                         "kvt_gather_attn_decode: strides (%lld, %lld, %lld) must be non-negative "
+                         "multiples of 16",
+                         (long long)block_stride, (long long)head_stride, (long long)token_stride);
+    if (!q || !out || !k_plane || !v_plane || !ids || (!k_out) != (!v_out))
+        return kvt::fail(KVT_EINVAL, "kvt_gather_attn_decode: null pointer (k_out and v_out "
+                                     "are both given or both NULL)");
+    if (!kvt::aligned(q, 16) || !kvt::aligned(k_plane, 16) || !kvt::aligned(v_plane, 16) ||
+        !kvt::aligned(k_out, 16) || !kvt::aligned(v_out, 16))
+        return kvt::fail(KVT_EALIGN, "kvt_gather_attn_decode: q, planes and outputs must be "
+                                     "16-byte aligned");
+    const int64_t n_kv = (int64_t)k * bt;
+    const size_t need = kvt_attn_decode_ws_bytes(n_qh, hd, n_kv);
+    if (!ws || ws_bytes < need)
+        return kvt::fail(KVT_EINVAL, "kvt_gather_attn_decode: workspace of %zu bytes, need %zu",
+                         ws_bytes, need);
+    const int64_t chunks = (n_kv + kKeys - 1) / kKeys;
+    hipStream_t s = kvt::as_stream(stream);
+    const int group = n_qh / kvh;
+    float *part = static_cast<float *>(ws);
+    const float scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)chunks, kvh), dim3(64), 0, s,
+                           static_cast<const uint16_t *>(q), group,
+                           static_cast<const unsigned char *>(k_plane),
+                           static_cast<const unsigned char *>(v_plane), n_blocks, block_stride,
+                           head_stride, token_stride, block_table, (int)bt, ids, (int)k,
+                           static_cast<uint16_t *>(k_out), static_cast<uint16_t *>(v_out),
+                           scale_log2, part);
+    };
+    if (dtype == KVT_BF16)
+        launch(gather_decode_partial<true>);
+    else
+        launch(gather_decode_partial<false>);
+    KVT_LAUNCHED("gather_decode_partial");
     hipLaunchKernelGGL(decode_merge, dim3(n_qh), dim3(kHd), 0, s, part, group, (int)chunks, out);
     KVT_LAUNCHED("decode_merge");
     return KVT_OK;

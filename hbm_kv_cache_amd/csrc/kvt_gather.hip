@@ -4,57 +4,73 @@
 // host link, so the bytes read per decode step do not grow with context.  The planes are
 // reached through a base pointer plus computed offsets -- token r of block p, head h lives at
 // plane + p*block_stride + h*head_stride + r*token_stride -- so any layout of the host tier
-// works.  Per (plane, head, slot) one workgroup copies the block's bt rows of hd*elem_bytes;
-// every thread issues all of its 16-byte loads before its first store, so each workgroup keeps
-// its whole block in flight on the link, and the HBM side is one contiguous [bt][hd] run.
+// works.  Each (plane, head, slot) unit is the block's bt rows of hd*elem_bytes, and its HBM
+// side is one contiguous [bt][hd] run.
 //
-// The host-link rate depends on how long the contiguous runs are: a token-major plane gives
-// 256-byte runs (one head of one token), a block-local head-major plane [block][head][token]
-// gives one run of bt*hd*elem_bytes (16 KiB) per unit.
+// Pacing, measured on MI355X for 8 MiB per step: issuing every 16-byte load of the selection
+// at once (all 8 MiB requested within microseconds) moves it at 43 GB/s, whatever the launch
+// shape, load flavour or host layout; the same bytes with at most ~0.25-2 MiB in flight --
+// each wave moving one 1 KiB wave-load at a time -- move at 54-55 GB/s, the link's rate for a
+// transfer of that size.  So a grid of at most kMaxWaves wavefronts strides over 8 KiB pieces of
+// the (slot, head, plane) units and each wave copies its piece one wave-load at a time.
+#include <algorithm>
+
 #include "kvt_internal.h"
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = kWavesPerGroup * kvt::kWave;
+constexpr int kMaxWaves = 1024;           // ~1 MiB in flight at one 1 KiB wave-load each
+constexpr int kPieceWords = 512;          // 16-byte words per piece (8 KiB)
 
-// grid = (k, kvh, 2): x = selection slot, y = head, z = plane (0 = K, 1 = V)
+// One piece: words [p0, p0 + n) of a unit whose rows are wpr words long.
+__device__ __forceinline__ void copy_piece(const unsigned char *__restrict__ src,
+                                           unsigned char *__restrict__ dst, int64_t token_stride,
+                                           int wpr, int p0, int n, int lane)
+{
+#pragma unroll 1
+    for (int w = p0 + lane; w < p0 + n; w += kvt::kWave) {
+        const int row = w / wpr, col = w - row * wpr;
+        const u32x4 v = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(src + row * token_stride) + col);
+        reinterpret_cast<u32x4 *>(dst)[w] = v;
+        __asm__ volatile("" ::: "memory");   // keep the next load behind this one
+    }
+}
+
+// unit u = (plane * kvh + h) * k + i; piece c of ceil(bt*wpr / kPieceWords) per unit
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const unsigned char *__restrict__ k_plane, const unsigned char *__restrict__ v_plane,
     int64_t n_blocks, int64_t block_stride, int64_t head_stride, int64_t token_stride,
     int slice_bytes, const int32_t *__restrict__ table, int bt, const int32_t *__restrict__ ids,
-    int k, unsigned char *__restrict__ k_out, unsigned char *__restrict__ v_out)
+    int k, int kvh, int pieces_per_unit, int64_t n_pieces, unsigned char *__restrict__ k_out,
+    unsigned char *__restrict__ v_out)
 {
-    const int i = blockIdx.x, h = blockIdx.y;
-    const int b = ids[h * k + i];
-    if (b < 0 || b >= n_blocks)
-        return;
-    const int64_t phys = table ? table[b] : b;
-    if (phys < 0 || phys >= n_blocks)
-        return;
-    const unsigned char *src = (blockIdx.z ? v_plane : k_plane) + phys * block_stride +
-                               (int64_t)h * head_stride;
-    unsigned char *dst = (blockIdx.z ? v_out : k_out) +
-                         ((int64_t)h * k + i) * (int64_t)bt * slice_bytes;
-    const int wpr = slice_bytes >> 4;  // 16-byte words per row slice
-    const int nw = bt * wpr;
-    for (int w0 = threadIdx.x; w0 < nw; w0 += kUnroll * kThreads) {
-        u32x4 r[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int w = w0 + u * kThreads;
-            if (w < nw) {
-                const int row = w / wpr, col = w - row * wpr;
-                r[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4 *>(src + row * token_stride) + col);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int w = w0 + u * kThreads;
-            if (w < nw)
-                reinterpret_cast<u32x4 *>(dst)[w] = r[u];
-        }
+    const int lane = threadIdx.x & (kvt::kWave - 1);
+    const int wpr = slice_bytes >> 4;
+    const int unit_words = bt * wpr;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerGroup;
+    for (int64_t pc = (int64_t)blockIdx.x * kWavesPerGroup +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         pc < n_pieces; pc += stride) {
+        const int64_t u = pc / pieces_per_unit;
+        const int c = (int)(pc - u * pieces_per_unit);
+        const int plane = (int)(u / ((int64_t)kvh * k));
+        const int hu = (int)(u - (int64_t)plane * kvh * k);   // h * k + i
+        const int h = hu / k;
+        const int b = ids[hu];
+        if (b < 0 || b >= n_blocks)
+            continue;
+        const int64_t phys = table ? table[b] : b;
+        if (phys < 0 || phys >= n_blocks)
+            continue;
+        const unsigned char *src = (plane ? v_plane : k_plane) + phys * block_stride +
+                                   (int64_t)h * head_stride;
+        unsigned char *dst = (plane ? v_out : k_out) + (int64_t)hu * bt * slice_bytes;
+        const int p0 = c * kPieceWords;
+        const int n = min(kPieceWords, unit_words - p0);
+        copy_piece(src, dst, token_stride, wpr, p0, n, lane);
     }
 }
 
@@ -83,14 +99,20 @@ extern "C" int kvt_gather_blocks(const void *k_plane, const void *v_plane, int64
     if (!kvt::aligned(k_plane, 16) || !kvt::aligned(v_plane, 16) || !kvt::aligned(k_out, 16) ||
         !kvt::aligned(v_out, 16))
         return kvt::fail(KVT_EALIGN, "kvt_gather_blocks: planes and outputs must be 16-byte aligned");
-    if (slice * bt > (1ll << 30) || k > 0x7fffffff)
+    if (slice * bt > (1ll << 30) || (int64_t)kvh * k > 0x3fffffff)
         return kvt::fail(KVT_ERANGE, "kvt_gather_blocks: block of %lld bytes too large",
                          (long long)(slice * bt));
-    hipLaunchKernelGGL(gather_kernel, dim3(k, kvh, 2), dim3(kThreads), 0, kvt::as_stream(stream),
+    const int64_t unit_words = slice / 16 * bt;
+    const int pieces_per_unit = (int)((unit_words + kPieceWords - 1) / kPieceWords);
+    const int64_t n_pieces = (int64_t)pieces_per_unit * kvh * k * 2;
+    const int64_t waves = std::min<int64_t>(n_pieces, kMaxWaves);
+    const unsigned groups = (unsigned)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
+    hipLaunchKernelGGL(gather_kernel, dim3(groups), dim3(kThreads), 0, kvt::as_stream(stream),
                        static_cast<const unsigned char *>(k_plane),
                        static_cast<const unsigned char *>(v_plane), n_blocks, block_stride,
-                       head_stride, token_stride, (int)slice, block_table, bt, ids, k,
-                       static_cast<unsigned char *>(k_out), static_cast<unsigned char *>(v_out));
+                       head_stride, token_stride, (int)slice, block_table, bt, ids, k, kvh,
+                       pieces_per_unit, n_pieces, static_cast<unsigned char *>(k_out),
+                       static_cast<unsigned char *>(v_out));
     KVT_LAUNCHED("gather_kernel");
     return KVT_OK;
 }

@@ -42,6 +42,9 @@ _SIGNATURES = {
     "kvt_attn_decode_ws_bytes": (c_size_t, [c_int32, c_int32, c_int64]),
     "kvt_attn_decode": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, _P, _P, c_int64, _P,
                                 c_float, _P, _P, c_size_t, _P]),
+    "kvt_gather_attn_decode": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, _P, _P, c_int64,
+                                       c_int64, c_int64, c_int64, _P, c_int32, _P, c_int32, _P, _P,
+                                       c_float, _P, _P, c_size_t, _P]),
     "kvt_attn_prefill": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P, c_int64,
                                  _P, _P, c_int64, c_int32, c_int32, c_float, _P, _P]),
 }
@@ -174,6 +177,16 @@ def kvt_attn_decode(q, n_qh, kvh, hd, dtype, k, v, n_kv, n_valid, scale, out, ws
     _check("kvt_attn_decode", load().kvt_attn_decode(
         _ptr(q), int(n_qh), int(kvh), int(hd), int(dtype), _ptr(k), _ptr(v), int(n_kv),
         _ptr(n_valid), float(scale), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def kvt_gather_attn_decode(q, n_qh, kvh, hd, dtype, k_plane, v_plane, n_blocks, block_stride,
+                           head_stride, token_stride, block_table, bt, ids, k, k_out, v_out, scale,
+                           out, ws, ws_bytes, stream=None):
+    _check("kvt_gather_attn_decode", load().kvt_gather_attn_decode(
+        _ptr(q), int(n_qh), int(kvh), int(hd), int(dtype), _ptr(k_plane), _ptr(v_plane),
+        int(n_blocks), int(block_stride), int(head_stride), int(token_stride), _ptr(block_table),
+        int(bt), _ptr(ids), int(k), _ptr(k_out), _ptr(v_out), float(scale), _ptr(out), _ptr(ws),
+        int(ws_bytes), _stream(stream)))
 
 
 def kvt_attn_prefill(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_tail, v_tail, n_kv,

@@ -10,6 +10,7 @@
  *   kvt_gather_blocks    copy only the selected blocks' K/V rows host -> HBM
  *   kvt_stage_tail       copy a sequence's host-resident rows into an HBM staging buffer
  *   kvt_attn_decode      GQA decode attention over gathered K/V
+ *   kvt_gather_attn_decode  the gather and the decode attention in one pass
  *   kvt_attn_prefill     causal (or full) prefill attention over an HBM head + tail
  *
  * Sources (page titles; each entry point names the section it follows):
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 1
+#define KVT_ABI_VERSION 2
 
 /* status codes */
 #define KVT_OK 0
@@ -194,6 +195,31 @@ size_t kvt_attn_decode_ws_bytes(int32_t n_qh, int32_t hd, int64_t n_kv);
 int kvt_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd, int32_t dtype,
                     const void *k, const void *v, int64_t n_kv, const int32_t *n_valid,
                     float scale, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S5+S6 in one pass.  [QSA-KVO] sparse_attend / qsa_sparse_attend_rows_staged: decode reads
+ * the selected blocks' K/V through base pointers and computed offsets.  Each 64-key chunk's
+ * rows cross the host link straight into the wavefront that attends them, so the attention
+ * runs under the transfer instead of after it.
+ *   q, n_qh, kvh, hd, dtype, scale, out, ws   as kvt_attn_decode, with n_kv = k*bt
+ *                     (ws: kvt_attn_decode_ws_bytes(n_qh, hd, k*bt) bytes)
+ *   k_plane ... k     as kvt_gather_blocks, with elem_bytes = 2: key j (j < k*bt) of head h
+ *                     is token j % bt of slot j / bt of that head's selection
+ *   k_out, v_out      optional device [kvh][k*bt][hd] (both or neither): when given they
+ *                     receive exactly what kvt_gather_blocks writes (skipped slots untouched)
+ * Keys of slots that kvt_gather_blocks skips (id < 0, block outside [0, n_blocks)) take no
+ * part.  With such slots only at the end of each head's list, out is bit-identical to
+ * kvt_gather_blocks followed by kvt_attn_decode with n_valid[h] = bt * (valid slots of h):
+ * the same chunks, the same arithmetic, the same merge.
+ * Limits: hd == 128, n_qh/kvh <= 16, n_blocks >= 1, k*bt < 2^31 - 64; strides multiples of
+ * 16, q, planes and outputs 16-byte aligned.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd, int32_t dtype,
+                           const void *k_plane, const void *v_plane, int64_t n_blocks,
+                           int64_t block_stride, int64_t head_stride, int64_t token_stride,
+                           const int32_t *block_table, int32_t bt, const int32_t *ids, int32_t k,
+                           void *k_out, void *v_out, float scale, float *out, void *ws,
+                           size_t ws_bytes, void *stream);
 
 /* ----------------------------------------------------------------------------------------
  * S8  prefill attention over a tiered cache.  [llama-T]: cells [0, n_head) live in HBM, the

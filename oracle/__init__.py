@@ -197,6 +197,36 @@ def attn_decode(q_u16, k_u16, v_u16, fmt, scale, n_valid=None, threads=0):
     return out
 
 
+def gather_attn_decode(q_u16, k_plane, v_plane, n_blocks, kvh, hd, fmt, strides, ids,
+                       block_tokens, scale, block_table=None, threads=0):
+    """Decode attention over the selected blocks' rows (elements of 2 bytes) read through the
+    plane strides: per KV head, the keys are the tokens of its selected slots, and a slot
+    whose id lies outside [0, n_blocks) -- or whose table entry does -- contributes no key.
+    Written as the two definitions above: the valid slots gathered first, then attention with
+    n_valid = block_tokens * (valid slots).  Returns (out f64 [n_qh][hd], k_rows, v_rows), the
+    rows as uint8 [kvh][k*block_tokens][hd*2] with the valid slots first."""
+    ids = np.array(ids, dtype=np.int64)
+    valid = (ids >= 0) & (ids < n_blocks)
+    if block_table is not None:
+        tab = np.asarray(block_table, dtype=np.int64)
+        phys = np.where(valid, tab[np.clip(ids, 0, max(n_blocks - 1, 0))], -1)
+        valid &= (phys >= 0) & (phys < n_blocks)
+    kk = ids.shape[1]
+    packed = np.full((kvh, kk), -1, dtype=np.int32)
+    n_valid = np.zeros(kvh, dtype=np.int32)
+    for h in range(kvh):
+        sel = ids[h][valid[h]]
+        packed[h, :sel.size] = sel
+        n_valid[h] = sel.size * block_tokens
+    ko, vo = gather(k_plane, v_plane, n_blocks, kvh, hd, 2, strides, packed, block_tokens,
+                    block_table=block_table)
+    n_kv = kk * block_tokens
+    out = attn_decode(q_u16, ko.view(np.uint16).reshape(kvh, n_kv, hd),
+                      vo.view(np.uint16).reshape(kvh, n_kv, hd), fmt, scale, n_valid=n_valid,
+                      threads=threads)
+    return out, ko, vo
+
+
 def attn_prefill(q_u16, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, fmt, causal,
                  scale, t_begin=0, t_end=None, threads=0):
     """q: [n_q][n_qh][hd] fp16 bits; K/V head and tail: uint8 row arrays -> f64 [rows][n_qh][hd]."""

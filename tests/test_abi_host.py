@@ -34,7 +34,7 @@ def test_header_declarations_all_exported():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 1
+    assert kvt.kvt_abi_version() == 2
 
 
 def test_library_has_gfx950_code_object():
@@ -100,6 +100,18 @@ def test_argument_errors_return_before_any_device_work():
         kvt.kvt_attn_decode(16, 63, 8, 128, kvt.BF16, 16, 16, 10, None, 0.1, 16, 16, 1 << 20,
                             stream=0)
     assert e.value.code == kvt.EINVAL
+    fused = dict(q=16, n_qh=64, kvh=8, hd=128, dtype=kvt.BF16, k_plane=16, v_plane=16,
+                 n_blocks=100, block_stride=16384 * 8, head_stride=16384, token_stride=256,
+                 block_table=None, bt=64, ids=16, k=32, k_out=16, v_out=16, scale=0.1, out=16,
+                 ws=16, ws_bytes=1 << 20, stream=0)
+    for change, code in [(dict(hd=64), kvt.EUNSUPPORTED), (dict(dtype=kvt.Q8_0), kvt.EUNSUPPORTED),
+                         (dict(v_out=None), kvt.EINVAL), (dict(n_blocks=0), kvt.EINVAL),
+                         (dict(n_qh=63), kvt.EINVAL), (dict(token_stride=264), kvt.EALIGN),
+                         (dict(k_plane=24), kvt.EALIGN), (dict(ws_bytes=100), kvt.EINVAL),
+                         (dict(k=1 << 26, bt=64), kvt.ERANGE), (dict(ids=None), kvt.EINVAL)]:
+        with pytest.raises(kvt.KvtError) as e:
+            kvt.kvt_gather_attn_decode(**{**fused, **change})
+        assert e.value.code == code, change
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_stage_tail(16, 0, 0, 10, 16, kvt.COPY_AUTO, stream=0)
     assert e.value.code == kvt.EINVAL

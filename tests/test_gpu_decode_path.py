@@ -218,3 +218,151 @@ def test_decode_step_full_geometry(gpu, ctx, layout):
     assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
     del planes
     buf.free()
+
+
+def _run_fused(buf, n_tok, kvh, hd, bt, n_blocks, strides, ids, q, fmt, dev, table=None,
+               with_out=True, canary=0x1234):
+    n_qh = q.shape[0]
+    k = ids.shape[1]
+    n_kv = k * bt
+    out = torch.full((n_qh, hd), float("nan"), dtype=torch.float32, device=dev)
+    ws_bytes = kvt.kvt_attn_decode_ws_bytes(n_qh, hd, n_kv)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    kv = torch.full((2, kvh, n_kv, hd), canary, dtype=torch.int16, device=dev)
+    kvt.kvt_gather_attn_decode(_u16(q, dev), n_qh, kvh, hd, fmt, buf.dev,
+                               buf.dev + n_tok * kvh * hd * 2, n_blocks, *strides,
+                               None if table is None else torch.from_numpy(table).to(dev), bt,
+                               torch.from_numpy(ids).to(dev), k,
+                               kv[0] if with_out else None, kv[1] if with_out else None,
+                               1 / math.sqrt(hd), out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), kv.cpu().numpy().view(np.uint8).reshape(
+        2, kvh, n_kv, hd * 2)
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+@pytest.mark.parametrize("bt,k,n_qh", [(64, 32, 64), (16, 20, 64), (48, 5, 16), (100, 7, 8),
+                                       (1, 70, 32), (64, 1, 64)])
+def test_gather_attn_decode_matches_oracle(gpu, layout, bt, k, n_qh):
+    """Fused gather + attention: out within 2e-3 of the oracle, the HBM copy of the rows
+    bit-exact (skipped slots untouched), with a block table and with ids that are -1, repeated,
+    or outside the planes, and block sizes that do and do not divide the 64-key chunks."""
+    kvh, hd = 8, 128
+    n_blocks = 300
+    n_tok = n_blocks * bt
+    buf, planes = _host_planes(n_tok, kvh, hd, 4, 100 + bt)
+    strides = LAYOUTS[layout](kvh, hd, 2, bt)
+    g = synth.rng(4, synth.P_MISC, 200 + bt * 3 + k)
+    ids = np.stack([np.sort(g.permutation(n_blocks)[:k]) for _ in range(kvh)]).astype(np.int32)
+    ids[2, k // 2] = -1                              # a hole in the middle
+    ids[5, -1] = n_blocks + 3                        # outside the planes
+    ids[6, :] = -1                                   # a head with nothing selected
+    if k > 1:
+        ids[7, 1] = ids[7, 0]                        # the same block twice
+    table = g.permutation(n_blocks).astype(np.int32)
+    q = synth.bf16_normal(synth.rng(4, synth.P_Q, bt + k), (n_qh, hd))
+    for tab in (None, table):
+        got, kv = _run_fused(buf, n_tok, kvh, hd, bt, n_blocks, strides, ids, q, kvt.BF16, gpu,
+                             table=tab)
+        ref, _, _ = oracle.gather_attn_decode(q, planes[0].view(np.uint8),
+                                              planes[1].view(np.uint8), n_blocks, kvh, hd,
+                                              oracle.BF16, strides, ids, bt, 1 / math.sqrt(hd),
+                                              block_table=tab)
+        assert np.isfinite(got).all()
+        assert np.max(np.abs(got - ref)) <= TOL
+        G = n_qh // kvh
+        assert (got[6 * G:7 * G] == 0).all()
+        ids_o = np.where((ids >= 0) & (ids < n_blocks), ids, -1).astype(np.int32)
+        can = np.zeros((kvh, k * bt, hd * 2), dtype=np.uint8)
+        can.view(np.uint16)[:] = 0x1234
+        ko, vo = oracle.gather(planes[0].view(np.uint8), planes[1].view(np.uint8), n_blocks, kvh,
+                               hd, 2, strides, ids_o, bt, block_table=tab, k_out=can.copy(),
+                               v_out=can.copy())
+        assert np.array_equal(kv[0], ko) and np.array_equal(kv[1], vo)
+    del planes
+    buf.free()
+
+
+@pytest.mark.parametrize("fmt", [kvt.BF16, kvt.F16])
+def test_gather_attn_decode_bit_identical_to_gather_then_decode(gpu, fmt):
+    """Trailing skipped slots: the fused op equals kvt_gather_blocks + kvt_attn_decode with
+    n_valid bit for bit (same chunks, same arithmetic, same merge); without k_out/v_out the
+    attention output is the same."""
+    kvh, hd, bt, k, n_qh = 8, 128, 64, 32, 64
+    n_blocks = 500
+    n_tok = n_blocks * bt
+    buf, planes = _host_planes(n_tok, kvh, hd, 4, 77)
+    if fmt == kvt.F16:                               # reinterpret the plane as N(0,1) fp16
+        g = synth.rng(4, synth.P_K, 78)
+        for p in range(2):
+            for t0 in range(0, n_tok, 1 << 14):
+                planes[p, t0:t0 + (1 << 14)] = synth.f16_normal(g, (min(1 << 14, n_tok - t0),
+                                                                    kvh, hd))
+    strides = oracle.block_head_major_strides(kvh, hd, 2, bt)
+    g = synth.rng(4, synth.P_MISC, 79)
+    ids = np.stack([np.sort(g.permutation(n_blocks)[:k]) for _ in range(kvh)]).astype(np.int32)
+    ids[1, 25:] = -1
+    ids[3, 1:] = -1
+    gen = synth.bf16_normal if fmt == kvt.BF16 else synth.f16_normal
+    q = gen(synth.rng(4, synth.P_Q, 80), (n_qh, hd))
+    fused, kv = _run_fused(buf, n_tok, kvh, hd, bt, n_blocks, strides, ids, q, fmt, gpu)
+    fused_noout, kv2 = _run_fused(buf, n_tok, kvh, hd, bt, n_blocks, strides, ids, q, fmt, gpu,
+                                  with_out=False)
+    assert np.array_equal(fused, fused_noout)
+    assert (kv2.view(np.uint16) == 0x1234).all()     # nothing written without outputs
+
+    staged = torch.full((2, kvh, k * bt, hd), 0x1234, dtype=torch.int16, device=gpu)
+    ids_d = torch.from_numpy(ids).to(gpu)
+    kvt.kvt_gather_blocks(buf.dev, buf.dev + n_tok * kvh * hd * 2, n_blocks, kvh, hd, 2, *strides,
+                          None, bt, ids_d, k, staged[0], staged[1])
+    n_valid = torch.from_numpy(((ids >= 0).sum(1) * bt).astype(np.int32)).to(gpu)
+    out = torch.empty((n_qh, hd), dtype=torch.float32, device=gpu)
+    ws_bytes = kvt.kvt_attn_decode_ws_bytes(n_qh, hd, k * bt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=gpu)
+    kvt.kvt_attn_decode(_u16(q, gpu), n_qh, kvh, hd, fmt, staged[0], staged[1], k * bt, n_valid,
+                        1 / math.sqrt(hd), out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), fused)
+    assert np.array_equal(staged.cpu().numpy().view(np.uint8).reshape(kv.shape), kv)
+    ofmt = oracle.BF16 if fmt == kvt.BF16 else oracle.F16
+    ref, _, _ = oracle.gather_attn_decode(q, planes[0].view(np.uint8), planes[1].view(np.uint8),
+                                          n_blocks, kvh, hd, ofmt, strides, ids, bt,
+                                          1 / math.sqrt(hd))
+    assert np.max(np.abs(fused - ref)) <= TOL
+    del planes
+    buf.free()
+
+
+@pytest.mark.parametrize("ctx", [262144, 1048576])
+def test_fused_decode_step_full_geometry(gpu, ctx):
+    """The decode step with the fused gather + attention at full size (block-local head-major
+    host planes): ids bit-exact, the HBM rows bit-exact, attention within 2e-3."""
+    kvh, hd, bt, k, n_qh = 8, 128, 64, 32, 64
+    n_blocks = ctx // bt
+    buf, planes = _host_planes(ctx, kvh, hd, 4, ctx + 1)
+    pooled = synth.f16_normal(synth.rng(4, synth.P_POOLED, ctx + 1), (n_blocks, 128))
+    q_idx = synth.f16_normal(synth.rng(4, synth.P_QIDX, ctx + 1), (kvh, 128))
+    q = synth.bf16_normal(synth.rng(4, synth.P_Q, ctx + 1), (n_qh, hd))
+    strides = oracle.block_head_major_strides(kvh, hd, 2, bt)
+    ws_t = kvt.kvt_index_topk_ws_bytes(n_blocks, kvh, k)
+    ws_d = kvt.kvt_attn_decode_ws_bytes(n_qh, hd, k * bt)
+    ws = torch.empty(ws_t + ws_d, dtype=torch.uint8, device=gpu)
+    ids = torch.empty((kvh, k), dtype=torch.int32, device=gpu)
+    kg = torch.empty((2, kvh, k * bt, hd), dtype=torch.int16, device=gpu)
+    out = torch.empty((n_qh, hd), dtype=torch.float32, device=gpu)
+    kvt.kvt_index_topk(_u16(pooled, gpu), n_blocks, 128, _u16(q_idx, gpu), kvh, k, ids, None,
+                       ws, ws_t)
+    kvt.kvt_gather_attn_decode(_u16(q, gpu), n_qh, kvh, hd, kvt.BF16, buf.dev,
+                               buf.dev + ctx * kvh * hd * 2, n_blocks, *strides, None, bt, ids, k,
+                               kg[0], kg[1], 1 / math.sqrt(hd), out, ws[ws_t:], ws_d)
+    torch.cuda.synchronize()
+    ref_ids = oracle.topk(oracle.index_scores(pooled, q_idx), k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref, ko, vo = oracle.gather_attn_decode(q, planes[0].view(np.uint8), planes[1].view(np.uint8),
+                                            n_blocks, kvh, hd, oracle.BF16, strides, ref_ids, bt,
+                                            1 / math.sqrt(hd))
+    got = kg.cpu().numpy().view(np.uint8).reshape(2, kvh, k * bt, hd * 2)
+    assert np.array_equal(got[0], ko) and np.array_equal(got[1], vo)
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
+    del planes
+    buf.free()

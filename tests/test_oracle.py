@@ -356,6 +356,39 @@ def test_decode_special_cases():
     assert np.max(np.abs(a - b)) < 1e-13
 
 
+@pytest.mark.parametrize("with_table", [False, True])
+def test_gather_attn_decode_is_sdpa_over_valid_slots(with_table):
+    """The selected blocks' tokens read by numpy fancy indexing from a token-major plane, slots
+    with ids outside [0, n_blocks) (or table entries outside it) dropped, torch SDPA in fp64."""
+    g = synth.rng(0, synth.P_MISC, 40 + with_table)
+    kvh, hd, bt, n_blocks, kk, G = 2, 32, 4, 10, 5, 3
+    planes = synth.bf16_normal(g, (2, n_blocks * bt, kvh, hd))
+    q = synth.bf16_normal(g, (kvh * G, hd))
+    ids = np.array([[3, -1, 7, 12, 0], [9, 2, 2, -5, 6]], dtype=np.int32)
+    table = None
+    if with_table:
+        table = g.permutation(n_blocks).astype(np.int32)
+        table[6] = n_blocks + 1                      # a table entry outside the planes
+    strides = oracle.token_major_strides(kvh, hd, 2, bt)
+    out, _, _ = oracle.gather_attn_decode(q, planes[0].view(np.uint8), planes[1].view(np.uint8),
+                                          n_blocks, kvh, hd, oracle.BF16, strides, ids, bt, 0.3,
+                                          block_table=table)
+    for h in range(kvh):
+        toks = []
+        for b in ids[h]:
+            if not 0 <= b < n_blocks:
+                continue
+            p = b if table is None else table[b]
+            if not 0 <= p < n_blocks:
+                continue
+            toks += list(range(p * bt, p * bt + bt))
+        kk_ = _to_f64(planes[0][toks, h], oracle.BF16)[None]
+        vv_ = _to_f64(planes[1][toks, h], oracle.BF16)[None]
+        qq = _to_f64(q[h * G:(h + 1) * G], oracle.BF16)[None]
+        ref = _sdpa(qq, kk_, vv_, 0.3)[0].numpy()
+        assert np.max(np.abs(out[h * G:(h + 1) * G] - ref)) < 1e-12
+
+
 def _dequant_q8_0_numpy(rows, kvh, hd):
     """Independent decode of q8_0 rows with numpy dtypes: [n][kvh][hd] float64."""
     n = rows.shape[0]
