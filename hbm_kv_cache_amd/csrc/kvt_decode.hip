@@ -43,69 +43,98 @@ __device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c)
                                                        __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Scores, softmax and P*V of one 64-key chunk for one KV head, once the chunk's K operands are
-// in registers and its V rows are in LDS (rows of keys that take no part zeroed).
-// valid: bit j set = key j of the chunk takes part.  Writes the chunk's partial (o, m, l) for
-// the group's query heads to pb.
-template <bool kBf16>
-__device__ __forceinline__ void chunk_attend(const uint4 (&qa)[4], const uint4 (&kb)[4][4],
-                                             uint64_t valid, int group, float scale_log2,
-                                             const unsigned char *vs, float (*ps)[16], float *pb,
-                                             int lane)
+// Online softmax over one 64-key chunk, taken as four 16-key sub-tiles (MFMA column tiles).
+// Per query row r of the group: m = running max (log2 domain), l = running sum of 2^(s - m),
+// o = running sum of 2^(s - m) v over this lane's two dims.  Sub-tile t: S = Q K_t^T on MFMA,
+// keys that take no part masked, m' = max(m, tile max), alpha = 2^(m - m'), then
+// l = alpha l + sum 2^(s - m'), o = alpha o + sum 2^(s - m') v.  The staged and the fused
+// kernels both run exactly this arithmetic, so they agree bit for bit.
+struct ChunkState {
+    float m[4], l[4];   // rows 4g + i (replicated over the 16 lanes of group g)
+    float o[16][2];     // rows 0..15, dims 2*lane, 2*lane + 1
+};
+
+__device__ __forceinline__ void state_init(ChunkState &st)
 {
-    const int g = lane >> 4, col = lane & 15;
-    f32x4 s[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; nt++) {
-        s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-            s[nt] = mfma16x16x32<kBf16>(qa[ks], kb[nt][ks], s[nt]);
-    }
-    // lane holds S[row 4g+i][key nt*16 + col]; scale into the log2 domain, mask invalid keys
-    float m[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        m[i] = -INFINITY;
+        st.m[i] = -INFINITY;
+        st.l[i] = 0.f;
+    }
 #pragma unroll
-        for (int nt = 0; nt < 4; nt++) {
-            const bool ok = (valid >> (nt * 16 + col)) & 1;
-            s[nt][i] = ok ? s[nt][i] * scale_log2 : -INFINITY;
-            m[i] = fmaxf(m[i], s[nt][i]);
-        }
+    for (int r = 0; r < 16; r++)
+        st.o[r][0] = st.o[r][1] = 0.f;
+}
+
+// kb: sub-tile t's K as MFMA B operands (lane (g, col): key 16t + col, dims ks*32 + 8g ..);
+// vs: the chunk's V rows in LDS; ps [16][16] and as [16]: per-sub-tile LDS scratch.
+template <bool kBf16>
+__device__ __forceinline__ void subtile_attend(int t, const uint4 (&qa)[4], const uint4 (&kb)[4],
+                                               uint64_t valid, int group, float scale_log2,
+                                               const unsigned char *vs, float (*ps)[16],
+                                               float *as, ChunkState &st, int lane)
+{
+    const int g = lane >> 4, col = lane & 15;
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+        s = mfma16x16x32<kBf16>(qa[ks], kb[ks], s);
+    // lane holds S[row 4g+i][key 16t + col]
+    const bool ok = (valid >> (16 * t + col)) & 1;
+    float mt[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        s[i] = ok ? s[i] * scale_log2 : -INFINITY;
+        mt[i] = s[i];
     }
     // row max / sum across the 16 lanes of a group (xor offsets stay inside the group)
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1)
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            m[i] = fmaxf(m[i], __shfl_xor(m[i], off, 64));
+            mt[i] = fmaxf(mt[i], __shfl_xor(mt[i], off, 64));
+    float alpha[4], ls[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        l[i] = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < 4; nt++) {
-            const float p = m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[nt][i] - m[i]);
-            ps[nt * 16 + col][4 * g + i] = p;
-            l[i] += p;
-        }
+        const float mn = fmaxf(st.m[i], mt[i]);
+        alpha[i] = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m[i] - mn);
+        const float p = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[i] - mn);
+        ps[col][4 * g + i] = p;
+        ls[i] = p;
+        st.m[i] = mn;
     }
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1)
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            l[i] += __shfl_xor(l[i], off, 64);
-    __syncthreads();
-
-    // O[r][2*lane .. 2*lane+1] = sum_key p[r][key] * V[key][...]
-    float o[16][2];
+            ls[i] += __shfl_xor(ls[i], off, 64);
 #pragma unroll
-    for (int r = 0; r < 16; r++)
-        o[r][0] = o[r][1] = 0.f;
-    const int nq4 = (group + 3) >> 2;   // float4 groups of probabilities actually used
+    for (int i = 0; i < 4; i++)
+        st.l[i] = fmaf(st.l[i], alpha[i], ls[i]);
+    if (col == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            as[4 * g + i] = alpha[i];
+    }
+    __syncthreads();   // ps, as visible to the whole wave
+
+    const int nq4 = (group + 3) >> 2;   // float4 groups of rows actually used
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+        if (q4 < nq4) {
+            const float4 a = *reinterpret_cast<const float4 *>(&as[4 * q4]);
+            const float ar[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                st.o[4 * q4 + e][0] *= ar[e];
+                st.o[4 * q4 + e][1] *= ar[e];
+            }
+        }
+    }
 #pragma unroll 4
-    for (int key = 0; key < kKeys; key++) {
-        const uint32_t pair = *reinterpret_cast<const uint32_t *>(vs + key * kVPitch + lane * 4);
+    for (int key = 0; key < 16; key++) {
+        const uint32_t pair =
+            *reinterpret_cast<const uint32_t *>(vs + (16 * t + key) * kVPitch + lane * 4);
         const float v0 = to_f32((uint16_t)(pair & 0xffff), kBf16);
         const float v1 = to_f32((uint16_t)(pair >> 16), kBf16);
 #pragma unroll
@@ -115,24 +144,32 @@ __device__ __forceinline__ void chunk_attend(const uint4 (&qa)[4], const uint4 (
                 const float pr[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    o[4 * q4 + e][0] = fmaf(pr[e], v0, o[4 * q4 + e][0]);
-                    o[4 * q4 + e][1] = fmaf(pr[e], v1, o[4 * q4 + e][1]);
+                    st.o[4 * q4 + e][0] = fmaf(pr[e], v0, st.o[4 * q4 + e][0]);
+                    st.o[4 * q4 + e][1] = fmaf(pr[e], v1, st.o[4 * q4 + e][1]);
                 }
             }
         }
     }
+}
+
+// the chunk's partial (o, m, l) for the group's query rows
+__device__ __forceinline__ void write_partial(const ChunkState &st, int group, float *pb,
+                                              int lane)
+{
+    const int g = lane >> 4, col = lane & 15;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
         if (r < group)
-            *reinterpret_cast<float2 *>(pb + r * (kHd + 2) + 2 * lane) = make_float2(o[r][0], o[r][1]);
+            *reinterpret_cast<float2 *>(pb + r * (kHd + 2) + 2 * lane) =
+                make_float2(st.o[r][0], st.o[r][1]);
     }
     if (col == 0) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int r = 4 * g + i;
             if (r < group) {
-                pb[r * (kHd + 2) + kHd] = m[i];
-                pb[r * (kHd + 2) + kHd + 1] = l[i];
+                pb[r * (kHd + 2) + kHd] = st.m[i];
+                pb[r * (kHd + 2) + kHd + 1] = st.l[i];
             }
         }
     }
@@ -159,7 +196,8 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
                                                      float scale_log2, float *__restrict__ part)
 {
     __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
-    __shared__ __align__(16) float ps[kKeys][16];   // probabilities, key-major
+    __shared__ __align__(16) float ps[16][16];   // a sub-tile's probabilities, key-major
+    __shared__ __align__(16) float as[16];       // a sub-tile's rescale factors per row
     const int lane = threadIdx.x;
     const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x;
     const int64_t key0 = (int64_t)c * kKeys;
@@ -203,8 +241,14 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
     }
     const int64_t nvc = nv - key0;   // keys of this chunk that take part: the first nvc
     const uint64_t valid = nvc >= kKeys ? ~0ull : nvc <= 0 ? 0ull : (1ull << nvc) - 1;
-    float *pb = part + ((int64_t)h * n_chunks + c) * group * (kHd + 2);
-    chunk_attend<kBf16>(qa, kb, valid, group, scale_log2, vs, ps, pb, lane);
+    ChunkState st;
+    state_init(st);
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        __syncthreads();   // V rows (t = 0) / the previous sub-tile's ps, as reads are done
+        subtile_attend<kBf16>(t, qa, kb[t], valid, group, scale_log2, vs, ps, as, st, lane);
+    }
+    write_partial(st, group, part + ((int64_t)h * n_chunks + c) * group * (kHd + 2), lane);
 }
 
 // Gather and attend in one pass: the chunk's K/V rows are read straight from the (host-mapped)
@@ -222,7 +266,8 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
 {
     __shared__ __align__(16) unsigned char ksm[kKeys * kKPitch];
     __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
-    __shared__ __align__(16) float ps[kKeys][16];
+    __shared__ __align__(16) float ps[16][16];
+    __shared__ __align__(16) float as[16];
     const int lane = threadIdx.x;
     const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x;
     const int n_kv = kk * bt;   // < 2^31, checked by the host
@@ -273,42 +318,53 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
         const uint64_t bal = __ballot((okb >> jj) & 1);
         valid |= ((bal & 1) | ((bal >> 15) & 2) | ((bal >> 30) & 4) | ((bal >> 45) & 8)) << (4 * jj);
     }
-    // The rows cross the link one K and one V wave-load at a time per wave: with every load of
-    // the step issued at once the link runs ~20% slower (see kvt_gather.hip).  Each pair goes
-    // to LDS -- K as read, V zeroed where the key takes no part -- and, when asked, to the
-    // HBM gather buffers in kvt_gather_blocks' layout (rows of skipped slots untouched).
-#pragma unroll
-    for (int jj = 0; jj < 16; jj++) {
-        const u32x4 kr = *reinterpret_cast<const u32x4 *>(kp + off[jj]);
-        const u32x4 vr = *reinterpret_cast<const u32x4 *>(vp + off[jj]);
-        const int row = rg + 4 * jj;
-        const bool ok = (okb >> jj) & 1;
-        *reinterpret_cast<u32x4 *>(ksm + row * kKPitch + cw * 16) = kr;
-        *reinterpret_cast<u32x4 *>(vs + row * kVPitch + cw * 16) = ok ? vr : u32x4{0, 0, 0, 0};
-        if (k_out && ok) {
-            const int64_t e = ((int64_t)h * n_kv + key0 + row) * kHd + cw * 8;
-            *reinterpret_cast<u32x4 *>(k_out + e) = kr;
-            *reinterpret_cast<u32x4 *>(v_out + e) = vr;
-        }
-        __asm__ volatile("" ::: "memory");   // keep the next pair behind this one
-    }
-    __syncthreads();
     if ((lane & 15) >= group) {
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
             qa[ks] = make_uint4(0, 0, 0, 0);
     }
-    // K as MFMA B operands: lane (g, col) takes key nt*16 + col, dims ks*32 + 8g .. +7
-    const int g = lane >> 4, col = lane & 15;
-    uint4 kb[4][4];
+    // The rows cross the link one K and one V wave-load at a time per wave: with every load of
+    // the step issued at once the link runs ~20% slower (see kvt_gather.hip).  Each pair goes
+    // to LDS -- K as read, V zeroed where the key takes no part -- and, when asked, to the
+    // HBM gather buffers in kvt_gather_blocks' layout (rows of skipped slots untouched).  The
+    // pair after a sub-tile's last is issued before that sub-tile is attended, so the
+    // attention runs while the link is busy.
+    ChunkState st;
+    state_init(st);
+    u32x4 kr = *reinterpret_cast<const u32x4 *>(kp + off[0]);
+    u32x4 vr = *reinterpret_cast<const u32x4 *>(vp + off[0]);
 #pragma unroll
-    for (int nt = 0; nt < 4; nt++)
+    for (int t = 0; t < 4; t++) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int jj = 4 * t + u;
+            const int row = rg + 4 * jj;
+            const bool ok = (okb >> jj) & 1;
+            *reinterpret_cast<u32x4 *>(ksm + row * kKPitch + cw * 16) = kr;
+            *reinterpret_cast<u32x4 *>(vs + row * kVPitch + cw * 16) =
+                ok ? vr : u32x4{0, 0, 0, 0};
+            if (k_out && ok) {
+                const int64_t e = ((int64_t)h * n_kv + key0 + row) * kHd + cw * 8;
+                *reinterpret_cast<u32x4 *>(k_out + e) = kr;
+                *reinterpret_cast<u32x4 *>(v_out + e) = vr;
+            }
+            __asm__ volatile("" ::: "memory");   // keep the next pair behind this one
+            if (jj + 1 < 16) {
+                kr = *reinterpret_cast<const u32x4 *>(kp + off[jj + 1]);
+                vr = *reinterpret_cast<const u32x4 *>(vp + off[jj + 1]);
+            }
+        }
+        __syncthreads();   // sub-tile t's K and V rows are in LDS
+        // K as MFMA B operands: lane (g, col) takes key 16t + col, dims ks*32 + 8g .. +7
+        const int g = lane >> 4, col = lane & 15;
+        uint4 kb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
-            kb[nt][ks] = *reinterpret_cast<const uint4 *>(ksm + (nt * 16 + col) * kKPitch +
-                                                          ks * 64 + 16 * g);
-    float *pb = part + ((int64_t)h * n_chunks + c) * group * (kHd + 2);
-    chunk_attend<kBf16>(qa, kb, valid, group, scale_log2, vs, ps, pb, lane);
+            kb[ks] = *reinterpret_cast<const uint4 *>(ksm + (16 * t + col) * kKPitch + ks * 64 +
+                                                      16 * g);
+        subtile_attend<kBf16>(t, qa, kb, valid, group, scale_log2, vs, ps, as, st, lane);
+    }
+    write_partial(st, group, part + ((int64_t)h * n_chunks + c) * group * (kHd + 2), lane);
 }
 
 // grid = n_qh, block = kHd.  Two passes over the chunks (global max, then the weighted sums),
