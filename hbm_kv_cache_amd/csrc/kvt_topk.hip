@@ -245,16 +245,65 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src)
     return ((uint64_t)hi << 32) | lo;
 }
 
-// compare-exchange with the lane `stride` away; `up` = this pair ends best-first
-__device__ __forceinline__ void wave_cx(uint64_t &key, uint32_t &id, int lane, int stride, bool up)
+// The value lane ^ S holds, on the cheapest cross-lane path for S: DPP quad permutes for 1
+// and 2, DPP row shifts (up or down by S inside a row of 16) for 4 and 8, a bit-mode
+// ds_swizzle for 16, ds_bpermute only for 32.
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane)
 {
-    const uint64_t pk = shfl_u64(key, lane ^ stride);
-    const uint32_t pi = __shfl(id, lane ^ stride, 64);
-    const bool lower = (lane & stride) == 0;
+    const int x = (int)v;
+    if constexpr (S == 1)
+        return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+    else if constexpr (S == 2)
+        return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+    else if constexpr (S == 4 || S == 8) {
+        const int from_above = __builtin_amdgcn_update_dpp(x, x, 0x100 + S, 0xF, 0xF, false);
+        const int from_below = __builtin_amdgcn_update_dpp(x, x, 0x110 + S, 0xF, 0xF, false);
+        return (uint32_t)((lane & S) ? from_below : from_above);
+    } else if constexpr (S == 16)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);   // and 0x1f, xor 0x10
+    else
+        return (uint32_t)__shfl_xor(x, S, 64);
+}
+
+template <int S>
+__device__ __forceinline__ void wave_cx_s(uint64_t &key, uint32_t &id, int lane, bool up)
+{
+    const uint32_t lo = xor_lane<S>((uint32_t)key, lane);
+    const uint32_t hi = xor_lane<S>((uint32_t)(key >> 32), lane);
+    const uint32_t pi = xor_lane<S>(id, lane);
+    const uint64_t pk = ((uint64_t)hi << 32) | lo;
+    const bool lower = (lane & S) == 0;
     const bool mine_better = better(key, id, pk, pi);
     if ((lower == up) != mine_better) {
         key = pk;
         id = pi;
+    }
+}
+
+// compare-exchange with the lane `stride` away; `up` = this pair ends best-first.  Every call
+// site has a compile-time stride once its loop is unrolled, so the switch folds away.
+__device__ __forceinline__ void wave_cx(uint64_t &key, uint32_t &id, int lane, int stride, bool up)
+{
+    switch (stride) {
+    case 1: wave_cx_s<1>(key, id, lane, up); break;
+    case 2: wave_cx_s<2>(key, id, lane, up); break;
+    case 4: wave_cx_s<4>(key, id, lane, up); break;
+    case 8: wave_cx_s<8>(key, id, lane, up); break;
+    case 16: wave_cx_s<16>(key, id, lane, up); break;
+    default: wave_cx_s<32>(key, id, lane, up); break;
+    }
+}
+
+__device__ __forceinline__ uint32_t xor_lane_dyn(uint32_t v, int lane, int stride)
+{
+    switch (stride) {
+    case 1: return xor_lane<1>(v, lane);
+    case 2: return xor_lane<2>(v, lane);
+    case 4: return xor_lane<4>(v, lane);
+    case 8: return xor_lane<8>(v, lane);
+    case 16: return xor_lane<16>(v, lane);
+    default: return xor_lane<32>(v, lane);
     }
 }
 
@@ -283,8 +332,10 @@ __device__ __forceinline__ void wave_merge32(uint64_t &ck, uint32_t &ci, uint64_
         wave_cx(ck, ci, lane, stride, true);
 }
 
-// grid.x = ceil(n_blocks / 64), 256 threads.  LDS: 64 padded rows + queries as fp64.
-__global__ __launch_bounds__(kThreads) void score_wave_topk(
+// grid.x = ceil(n_blocks / 64), kWaveThreads threads (a wave per head).  LDS: 64 padded rows
+// + queries as fp64.
+constexpr int kWaveThreads = 512;
+__global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
     const uint16_t *__restrict__ pooled, int64_t n_blocks, int dim,
     const uint16_t *__restrict__ q_idx, int n_sel, int k, uint64_t *__restrict__ cand_key,
     uint32_t *__restrict__ cand_id, double *__restrict__ scores_out)
@@ -298,61 +349,49 @@ __global__ __launch_bounds__(kThreads) void score_wave_topk(
     const int wpr = dim / 8;
 
     // every load is issued unconditionally (tail rows re-read the last valid row)
-    constexpr int kMaxWordsPerThread = kWaveRows * (256 / 8) / kThreads;   // 8
+    constexpr int kMaxWordsPerThread = kWaveRows * (256 / 8) / kWaveThreads;   // 4
     u32x4 v[kMaxWordsPerThread];
 #pragma unroll
     for (int u = 0; u < kMaxWordsPerThread; u++) {
-        const int w = threadIdx.x + u * kThreads;
+        const int w = threadIdx.x + u * kWaveThreads;
         const int r = min(w / wpr, nrows - 1), c = w % wpr;
         if (w < kWaveRows * wpr)
             v[u] = *reinterpret_cast<const u32x4 *>(pooled + (b0 + r) * dim + c * 8);
     }
 #pragma unroll
     for (int u = 0; u < kMaxWordsPerThread; u++) {
-        const int w = threadIdx.x + u * kThreads;
+        const int w = threadIdx.x + u * kWaveThreads;
         if (w < kWaveRows * wpr)
             *reinterpret_cast<u32x4 *>(rows + (w / wpr) * pitch + (w % wpr) * 16) = v[u];
     }
-    for (int e = threadIdx.x; e < n_sel * dim; e += kThreads)
+    for (int e = threadIdx.x; e < n_sel * dim; e += kWaveThreads)
         qd[e] = (double)f16_bits_to_f32(q_idx[e]);
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool valid = lane < nrows;
     const unsigned char *my_row = rows + lane * pitch;
-    // heads h0 and h0 + 4 together: two independent fp64 chains per lane
-    for (int h0 = wave; h0 < n_sel; h0 += 8) {
-        const int h1 = h0 + 4;
-        const bool two = h1 < n_sel;
-        const double *q0 = qd + h0 * dim;
-        const double *q1 = qd + (two ? h1 : h0) * dim;
-        double a0 = 0.0, a1 = 0.0;
+    // one head per wave: lane l scores row l, one fp64 chain in index order
+    for (int h = wave; h < n_sel; h += kWaveThreads / 64) {
+        const double *qh = qd + h * dim;
+        double acc = 0.0;
         for (int c = 0; c < wpr; c++) {
             const u32x4 w4 = *reinterpret_cast<const u32x4 *>(my_row + c * 16);
 #pragma unroll
             for (int e = 0; e < 8; e++) {
                 const uint16_t bits = (uint16_t)(w4[e >> 1] >> ((e & 1) * 16));
-                const double pv = (double)f16_bits_to_f32(bits);
-                a0 = fma(q0[c * 8 + e], pv, a0);
-                a1 = fma(q1[c * 8 + e], pv, a1);
+                acc = fma(qh[c * 8 + e], (double)f16_bits_to_f32(bits), acc);
             }
         }
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-            if (t == 1 && !two)
-                break;
-            const int h = t ? h1 : h0;
-            const double acc = t ? a1 : a0;
-            uint64_t key = valid ? rank_key(acc) : 0;
-            uint32_t id = valid ? (uint32_t)(b0 + lane) : kNoId;
-            if (scores_out && valid)
-                scores_out[(int64_t)h * n_blocks + b0 + lane] = acc;
-            wave_sort_best_first(key, id, lane);
-            if (lane < k) {
-                const int64_t o = ((int64_t)h * gridDim.x + blockIdx.x) * k + lane;
-                cand_key[o] = key;
-                cand_id[o] = id;
-            }
+        uint64_t key = valid ? rank_key(acc) : 0;
+        uint32_t id = valid ? (uint32_t)(b0 + lane) : kNoId;
+        if (scores_out && valid)
+            scores_out[(int64_t)h * n_blocks + b0 + lane] = acc;
+        wave_sort_best_first(key, id, lane);
+        if (lane < k) {
+            const int64_t o = ((int64_t)h * gridDim.x + blockIdx.x) * k + lane;
+            cand_key[o] = key;
+            cand_id[o] = id;
         }
     }
 }
@@ -411,7 +450,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
         for (int size = 2; size <= 64; size <<= 1)
 #pragma unroll
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                const uint32_t p = __shfl(id, lane ^ stride, 64);
+                const uint32_t p = xor_lane_dyn(id, lane, stride);
                 const bool lower = (lane & stride) == 0;
                 const bool up = size == 64 || (lane & size) == 0;
                 const bool mine_first = id < p;
@@ -499,7 +538,7 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
         uint32_t *ci = reinterpret_cast<uint32_t *>(w + round_up(c * 8, 256));
         if (n_wg > 0) {
             const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)n_sel * dim * 8;
-            hipLaunchKernelGGL(score_wave_topk, dim3((unsigned)n_wg), dim3(kThreads), lds, s,
+            hipLaunchKernelGGL(score_wave_topk, dim3((unsigned)n_wg), dim3(kWaveThreads), lds, s,
                                static_cast<const uint16_t *>(pooled), n_blocks, dim,
                                static_cast<const uint16_t *>(q_idx), n_sel, k, ck, ci, scores);
             KVT_LAUNCHED("score_wave_topk");

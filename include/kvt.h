@@ -140,7 +140,7 @@ uint64_t kvt_set_copy_threshold(int32_t dir, uint64_t bytes);
  *           order; when k > n_blocks the trailing slots hold -1.
  *   scores  optional device fp64 [n_sel][n_blocks] copy of every score (NULL to skip).
  *   ws      device workspace of kvt_index_topk_ws_bytes(n_blocks, n_sel, k) bytes.
- * Limits: 1 <= k <= 256, dim a multiple of 8 and <= 256, 1 <= n_sel <= 64.
+ * Limits: 1 <= k <= 256, dim a multiple of 8 and <= 256, 1 <= n_sel <= 32.
  * ---------------------------------------------------------------------------------------- */
 size_t kvt_index_topk_ws_bytes(int64_t n_blocks, int32_t n_sel, int32_t k);
 int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim, const void *q_idx,
