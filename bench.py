@@ -365,7 +365,8 @@ def main():
             "ms_per_step": round(r_staged["ms_per_step"], 5),
             "decode_tok_s": round(1e3 / r_staged["ms_per_step"], 2),
             "part_ms": {k: round(v, 5) for k, v in r_staged["part_ms"].items()},
-            "gather_kernel_gbs": gbs(r_staged["part_ms"]["gather"])},
+            "gather_kernel_gbs": gbs(r_staged["part_ms"]["gather"]),
+            "gather_kernel_traffic": kernel_traffic("gather_kernel")},
         f"{other}_host_layout": {
             "value": gbs(r_other["ms_per_step"]),
             "ms_per_step": round(r_other["ms_per_step"], 5),
