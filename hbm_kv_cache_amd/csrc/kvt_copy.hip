@@ -2,9 +2,9 @@
 //
 // vLLM-CPU transfer_async hands a swap function three u64 tables (src, dst, size) and picks
 // either the copy engines or a GPU kernel that dereferences host pointers.  Here:
-//   * KERNEL: each wavefront owns one 8 KiB chunk of one descriptor.  It reads the descriptor,
-//     issues all of its 16-byte loads (up to 8 per lane, 8 KiB in flight per wave) and then
-//     its stores, so thousands of waves keep the host link saturated.  Descriptors whose
+//   * KERNEL: each wavefront owns one 8 KiB chunk of one descriptor.  It reads the descriptor
+//     and reads the chunk one 1 KiB wave-load at a time (16 bytes per lane), then stores it,
+//     so thousands of waves keep ~1 MiB or more in flight without flooding the link.  Descriptors whose
 //     addresses are only 8-byte aligned take an 8-byte path, anything else a byte path.
 //   * SDMA: the copy engines, through hipMemcpyBatchAsync (one submission for the batch),
 //     falling back to one hipMemcpyAsync per descriptor where the batch call is unavailable.
@@ -21,51 +21,51 @@ namespace {
 
 constexpr int kChunk = 8192;                      // bytes per wave unit
 constexpr int kWavesPerBlock = 4;                 // 256-thread workgroups
+
 constexpr int kWordsPerLane16 = kChunk / 16 / kvt::kWave;  // 8
 constexpr int kWordsPerLane8 = kChunk / 8 / kvt::kWave;    // 16
 
-// One wave copies bytes [off, off+len) of a single range.  off + len <= range size.
+// One wave copies bytes [off, off+len) of a single range.  off + len <= range size.  The wave
+// has one wave-load (64 lanes x 16 or 8 bytes) in flight at a time -- the empty asm that takes
+// each loaded value makes the wave wait for it before the next load issues -- and stores the
+// chunk after its last load, so no load waits behind a store.  Host reads with every load of a
+// transfer in flight at once ran ~20% below the link rate on MI355X (see kvt_gather.hip);
+// thousands of waves with one wave-load each keep enough in flight.
+template <typename W, int N>
+__device__ __forceinline__ void wave_copy_words(const W *sp, W *dp, uint32_t nw, int lane)
+{
+    W r[N];
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+        const uint32_t w = lane + k * kvt::kWave;
+        if (w < nw) {
+            r[k] = __builtin_nontemporal_load(sp + w);
+            __asm__ volatile("" : : "v"(r[k]) : "memory");
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+        const uint32_t w = lane + k * kvt::kWave;
+        if (w < nw)
+            dp[w] = r[k];
+    }
+}
+
 __device__ __forceinline__ void wave_copy_chunk(uint64_t s, uint64_t d, uint64_t len, int lane)
 {
     if (((s | d) & 15) == 0) {
-        const u32x4 *sp = reinterpret_cast<const u32x4 *>(s);
-        u32x4 *dp = reinterpret_cast<u32x4 *>(d);
         const uint32_t nw = (uint32_t)(len >> 4);
-        u32x4 r[kWordsPerLane16];
-#pragma unroll
-        for (int k = 0; k < kWordsPerLane16; k++) {
-            uint32_t w = lane + k * kvt::kWave;
-            if (w < nw)
-                r[k] = __builtin_nontemporal_load(sp + w);
-        }
-#pragma unroll
-        for (int k = 0; k < kWordsPerLane16; k++) {
-            uint32_t w = lane + k * kvt::kWave;
-            if (w < nw)
-                dp[w] = r[k];
-        }
+        wave_copy_words<u32x4, kWordsPerLane16>(reinterpret_cast<const u32x4 *>(s),
+                                                reinterpret_cast<u32x4 *>(d), nw, lane);
         uint64_t done = (uint64_t)nw << 4;
         if (done < len && lane < (int)(len - done)) {  // < 16 trailing bytes
             reinterpret_cast<uint8_t *>(d)[done + lane] =
                 reinterpret_cast<const uint8_t *>(s)[done + lane];
         }
     } else if (((s | d) & 7) == 0) {
-        const u32x2 *sp = reinterpret_cast<const u32x2 *>(s);
-        u32x2 *dp = reinterpret_cast<u32x2 *>(d);
         const uint32_t nw = (uint32_t)(len >> 3);
-        u32x2 r[kWordsPerLane8];
-#pragma unroll
-        for (int k = 0; k < kWordsPerLane8; k++) {
-            uint32_t w = lane + k * kvt::kWave;
-            if (w < nw)
-                r[k] = __builtin_nontemporal_load(sp + w);
-        }
-#pragma unroll
-        for (int k = 0; k < kWordsPerLane8; k++) {
-            uint32_t w = lane + k * kvt::kWave;
-            if (w < nw)
-                dp[w] = r[k];
-        }
+        wave_copy_words<u32x2, kWordsPerLane8>(reinterpret_cast<const u32x2 *>(s),
+                                               reinterpret_cast<u32x2 *>(d), nw, lane);
         uint64_t done = (uint64_t)nw << 3;
         if (done < len && lane < (int)(len - done)) {
             reinterpret_cast<uint8_t *>(d)[done + lane] =
