@@ -604,11 +604,30 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
             ms.append(t.stop_ms())
         return _median(ms)
 
+    state_b = kvt.kvt_attn_prefill_state_bytes(n_q, n_qh, kvh)
+    state = torch.empty(state_b, dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
+
+    def pipe_ms(arena_rows):
+        arena = torch.empty((2, arena_rows, row), dtype=torch.uint8, device=dev)
+        ms = []
+        for _ in range(reps):
+            t.start()
+            kvt.kvt_attn_prefill_pipelined(q, n_q, q_pos0, n_qh, kvh, hd, k_all, v_all, n_head,
+                                           host.dev, host.dev + n_tail * row, n_kv, kvt.Q8_0, 1,
+                                           scale, arena[0], arena[1], arena_rows, state, state_b,
+                                           out, copy_stream=copy_stream)
+            ms.append(t.stop_ms())
+        del arena
+        return _median(ms)
+
     st_sdma = stage_ms(kvt.COPY_SDMA)
     st_kernel = stage_ms(kvt.COPY_KERNEL)
     a_staged = attn_ms(k_all, v_all, n_head, stage[0], stage[1])
     a_inplace = attn_ms(k_all, v_all, n_head, host.dev, host.dev + n_tail * row)
     a_hbm = attn_ms(k_all, v_all, n_kv, None, None)
+    p_one = pipe_ms(2 * n_tail)          # the whole tail in one bucket
+    p_arena = pipe_ms(2 * 16384)         # bounded arena: buckets of 16,384 rows (17.8 MB/plane)
     st = min(st_sdma, st_kernel)
     res = {
         "n_kv": n_kv, "n_head": n_head, "n_q": n_q, "q_heads": n_qh, "kv_heads": kvh,
@@ -623,11 +642,14 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
         "attn_all_hbm_ms": round(a_hbm, 4),
         "prefill_tok_s_staged": round(n_q / ((st + a_staged) * 1e-3), 1),
         "prefill_tok_s_staging_off": round(n_q / (a_inplace * 1e-3), 1),
+        "pipelined_one_bucket_ms": round(p_one, 4),
+        "pipelined_arena_16384_ms": round(p_arena, 4),
+        "prefill_tok_s_pipelined": round(n_q / (min(p_one, p_arena) * 1e-3), 1),
     }
     log("prefill", res)
     del ht
     host.free()
-    del k_all, v_all, stage, out, q
+    del k_all, v_all, stage, out, q, state
     torch.cuda.empty_cache()
     return res
 

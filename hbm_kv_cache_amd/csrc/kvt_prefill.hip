@@ -159,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     const unsigned char *__restrict__ k_head, const unsigned char *__restrict__ v_head,
     int64_t n_head, const unsigned char *__restrict__ k_tail,
     const unsigned char *__restrict__ v_tail, int64_t n_kv, int causal, float scale_log2,
+    int tile_begin, int tile_cap, float *__restrict__ state, int first, int last,
     float *__restrict__ out)
 {
     __shared__ __align__(16) unsigned char lds[2 * kLdsBuf + 2 * kRawBytes];
@@ -187,7 +188,9 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     const int64_t wave_last = t_first < n_q ? last_key_for(t_first + 31) : -1;
     const int64_t pos_first = q_pos0 + t_first;
     const int64_t pos_i = q_pos0 + t_i;
-    const int n_tiles = wg_last < 0 ? 0 : (int)((wg_last + kKT) / kKT);
+    const int n_tiles_all = wg_last < 0 ? 0 : (int)((wg_last + kKT) / kKT);
+    // this call's tiles: [tile_begin, n_tiles) (a key range of a resumable pass)
+    const int n_tiles = n_tiles_all < tile_cap ? n_tiles_all : tile_cap;
 
     // Q^T as MFMA B operands: column i = query row, k = d = 16*kd + 8*g + 0..7
     f16x8 qb[8];
@@ -197,37 +200,51 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
         qb[kd] = *reinterpret_cast<const f16x8 *>(qrow + 16 * kd);
 
     f32x16 o[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; dt++)
-        o[dt] = f32x16{};
     float m = -INFINITY, l = 0.f;   // running max (raw logits) and sum
+    // resumable passes keep (o, m, l) per lane: [workgroup][wave][66][lane], exact fp32
+    float *st = state ? state + ((int64_t)blockIdx.x * kWaves + wave) * 66 * 64 + lane : nullptr;
+    if (first) {
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+            o[dt] = f32x16{};
+    } else {
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                o[dt][r] = st[(16 * dt + r) * 64];
+        m = st[64 * 64];
+        l = st[65 * 64];
+    }
 
     // the four cache bases, moved to this workgroup's head slice
     const unsigned char *kh = k_head + h * kHeadBytes, *vh = v_head + h * kHeadBytes;
     const unsigned char *kt = k_tail + h * kHeadBytes, *vt = v_tail + h * kHeadBytes;
     uint64_t rq[kRawPerThread];
 
-    // prologue: raw tile 0 -> LDS; fp16 tile 0 and raw tile 1 ready; loads of tile 2 in flight
-    if (n_tiles > 0) {
-        load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, 0, rq);
-        store_raw(lds_raw, rq);
-        if (n_tiles > 1)
-            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, 1, rq);
+    // prologue: raw tile b -> LDS; fp16 tile b and raw tile b+1 ready; loads of b+2 in flight
+    // (b = tile_begin; buffers are indexed by tile & 1)
+    const int b0 = tile_begin;
+    if (n_tiles > b0) {
+        load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
+        store_raw(lds_raw + (b0 & 1) * kRawBytes, rq);
+        if (n_tiles > b0 + 1)
+            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
     }
     __syncthreads();
-    if (n_tiles > 0) {
-        dequant_tile(lds_raw, lds, wave, lane);
-        if (n_tiles > 1)
-            store_raw(lds_raw + kRawBytes, rq);
-        if (n_tiles > 2)
-            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, 2, rq);
+    if (n_tiles > b0) {
+        dequant_tile(lds_raw + (b0 & 1) * kRawBytes, lds + (b0 & 1) * kLdsBuf, wave, lane);
+        if (n_tiles > b0 + 1)
+            store_raw(lds_raw + ((b0 + 1) & 1) * kRawBytes, rq);
+        if (n_tiles > b0 + 2)
+            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 2, rq);
     }
     __syncthreads();
 
     // per tile: multiply fp16 buffer (tile & 1); dequantise raw tile+1 into the other fp16
     // buffer; move the registers of tile+2 into the raw buffer tile+1 just left; one barrier;
     // then issue the loads of tile+3
-    for (int tile = 0; tile < n_tiles; tile++) {
+    for (int tile = b0; tile < n_tiles; tile++) {
         const unsigned char *lk = lds + (tile & 1) * kLdsBuf;
         const unsigned char *lv = lk + kLdsK;
         const int64_t key0 = (int64_t)tile * kKT;
@@ -319,6 +336,16 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
             load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 3, rq);
     }
 
+    if (!last) {   // hand the state to the next pass
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                st[(16 * dt + r) * 64] = o[dt][r];
+        st[64 * 64] = m;
+        st[65 * 64] = l;
+        return;
+    }
     // normalise and write O[query][qh][d] through LDS (reusing the tiles), 32 d at a time
     const float inv_l = l > 0.f ? 1.f / l : 0.f;
     float *buf = reinterpret_cast<float *>(lds) + wave * 32 * kOutPitch;
@@ -340,6 +367,89 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     }
 }
 
+// Argument checks shared by the prefill entry points; fills group and q_tiles.
+int check_prefill(const char *fn, const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                  int32_t kvh, int32_t hd, const void *k_head, const void *v_head, int64_t n_head,
+                  const void *k_tail, const void *v_tail, int64_t n_kv, int32_t kv_format,
+                  float scale, const float *out, int &group, int64_t &q_tiles)
+{
+    if (kv_format != KVT_Q8_0)
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: kv_format=%d (this build: Q8_0)", fn, kv_format);
+    if (hd != kHd)
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: hd=%d (this build: 128)", fn, hd);
+    if (kvh < 1 || n_qh < 1 || n_qh % kvh)
+        return kvt::fail(KVT_EINVAL, "%s: n_qh=%d kvh=%d", fn, n_qh, kvh);
+    group = n_qh / kvh;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: group %d (this build: 1, 2, 4, 8)", fn, group);
+    if (!(scale > 0.f))
+        return kvt::fail(KVT_EINVAL, "%s: scale must be positive", fn);
+    if (n_q < 0 || q_pos0 < 0 || n_kv < 0 || n_head < 0 || n_head > n_kv)
+        return kvt::fail(KVT_EINVAL, "%s: n_q=%lld q_pos0=%lld n_head=%lld n_kv=%lld", fn,
+                         (long long)n_q, (long long)q_pos0, (long long)n_head, (long long)n_kv);
+    if (n_q > 0 && (!q || !out || (n_head > 0 && (!k_head || !v_head)) ||
+                    (n_kv > n_head && (!k_tail || !v_tail))))
+        return kvt::fail(KVT_EINVAL, "%s: null pointer", fn);
+    if (!kvt::aligned(q, 16) || !kvt::aligned(out, 16) || !kvt::aligned(k_head, 8) ||
+        !kvt::aligned(v_head, 8) || !kvt::aligned(k_tail, 8) || !kvt::aligned(v_tail, 8))
+        return kvt::fail(KVT_EALIGN, "%s: q/out need 16-byte, K/V 8-byte alignment", fn);
+    const int qpw = 32 * (kWaves / group);
+    q_tiles = (n_q + qpw - 1) / qpw;
+    if (q_tiles * kvh > 0x7fffffffll || n_kv / kKT > 0x7ffffff0ll)
+        return kvt::fail(KVT_ERANGE, "%s: too many query or key tiles", fn);
+    return KVT_OK;
+}
+
+size_t state_bytes(int64_t q_tiles, int32_t kvh)
+{
+    return (size_t)q_tiles * (size_t)kvh * kWaves * 66 * 64 * sizeof(float);
+}
+
+void launch_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh,
+                    int group, int64_t q_tiles, const void *k_head, const void *v_head,
+                    int64_t n_head, const void *k_tail, const void *v_tail, int64_t n_kv,
+                    int causal, float scale, int64_t key_begin, int64_t key_end, float *state,
+                    int first, int last, float *out, hipStream_t s)
+{
+    const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+    const int tile_begin = (int)(key_begin / kKT);
+    const int tile_cap = (int)((key_end + kKT - 1) / kKT);
+    hipLaunchKernelGGL(prefill_q8_0, dim3((unsigned)(q_tiles * kvh)), dim3(kThreads), 0, s,
+                       static_cast<const _Float16 *>(q), n_q, q_pos0, n_qh, kvh, group,
+                       static_cast<const unsigned char *>(k_head),
+                       static_cast<const unsigned char *>(v_head), n_head,
+                       static_cast<const unsigned char *>(k_tail),
+                       static_cast<const unsigned char *>(v_tail), n_kv, causal, scale_log2,
+                       tile_begin, tile_cap, state, first, last, out);
+}
+
+// Events of the pipelined entry point, created once per thread and device and then reused:
+// [0] start, [1 + slot] slot filled, [3 + slot] slot free.
+struct PipeEvents {
+    int device = -1;
+    hipEvent_t e[5] = {};
+};
+thread_local PipeEvents t_pipe;
+
+int pipe_events(hipEvent_t *&ev)
+{
+    int dev = 0;
+    KVT_HIP(hipGetDevice(&dev));
+    if (t_pipe.device != dev) {
+        for (hipEvent_t &x : t_pipe.e) {
+            if (x)
+                (void)hipEventDestroy(x);
+            x = nullptr;
+        }
+        t_pipe.device = -1;
+        for (hipEvent_t &x : t_pipe.e)
+            KVT_HIP(hipEventCreateWithFlags(&x, hipEventDisableTiming));
+        t_pipe.device = dev;
+    }
+    ev = t_pipe.e;
+    return KVT_OK;
+}
+
 }  // namespace
 
 // S8: llama-T tiered prefill attention (HBM head + staged or host-resident tail).
@@ -349,41 +459,159 @@ extern "C" int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int3
                                 int64_t n_kv, int32_t kv_format, int32_t causal, float scale,
                                 float *out, void *stream)
 {
-    if (kv_format != KVT_Q8_0)
-        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_prefill: kv_format=%d (this build: Q8_0)",
-                         kv_format);
-    if (hd != kHd)
-        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_prefill: hd=%d (this build: 128)", hd);
-    if (kvh < 1 || n_qh < 1 || n_qh % kvh)
-        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill: n_qh=%d kvh=%d", n_qh, kvh);
+    int group = 0;
+    int64_t q_tiles = 0;
+    const int rc = check_prefill("kvt_attn_prefill", q, n_q, q_pos0, n_qh, kvh, hd, k_head,
+                                 v_head, n_head, k_tail, v_tail, n_kv, kv_format, scale, out,
+                                 group, q_tiles);
+    if (rc != KVT_OK || n_q == 0)
+        return rc;
+    launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head, k_tail,
+                   v_tail, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out,
+                   kvt::as_stream(stream));
+    KVT_LAUNCHED("prefill_q8_0");
+    return KVT_OK;
+}
+
+extern "C" size_t kvt_attn_prefill_state_bytes(int64_t n_q, int32_t n_qh, int32_t kvh)
+{
+    if (n_q < 0 || kvh < 1 || n_qh < kvh || n_qh % kvh)
+        return 0;
     const int group = n_qh / kvh;
     if (group != 1 && group != 2 && group != 4 && group != 8)
-        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_prefill: group %d (this build: 1, 2, 4, 8)",
-                         group);
-    if (!(scale > 0.f))
-        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill: scale must be positive");
-    if (n_q < 0 || q_pos0 < 0 || n_kv < 0 || n_head < 0 || n_head > n_kv)
-        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill: n_q=%lld q_pos0=%lld n_head=%lld n_kv=%lld",
-                         (long long)n_q, (long long)q_pos0, (long long)n_head, (long long)n_kv);
+        return 0;
+    const int qpw = 32 * (kWaves / group);
+    return state_bytes((n_q + qpw - 1) / qpw, kvh);
+}
+
+// S8 as resumable passes over key ranges (the online-softmax fold over buckets of the pages'
+// bounded staging arena).
+extern "C" int kvt_attn_prefill_range(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                                      int32_t kvh, int32_t hd, const void *k_head,
+                                      const void *v_head, int64_t n_head, const void *k_tail,
+                                      const void *v_tail, int64_t n_kv, int32_t kv_format,
+                                      int32_t causal, float scale, int64_t key_begin,
+                                      int64_t key_end, void *state, size_t state_bytes_,
+                                      float *out, void *stream)
+{
+    int group = 0;
+    int64_t q_tiles = 0;
+    const int rc = check_prefill("kvt_attn_prefill_range", q, n_q, q_pos0, n_qh, kvh, hd,
+                                 k_head, v_head, n_head, k_tail, v_tail, n_kv, kv_format, scale,
+                                 out, group, q_tiles);
+    if (rc != KVT_OK)
+        return rc;
+    if (key_begin < 0 || key_end < key_begin || key_end > n_kv || key_begin % kKT ||
+        (key_end % kKT && key_end != n_kv))
+        return kvt::fail(KVT_EINVAL,
+                         "kvt_attn_prefill_range: keys [%lld, %lld) of %lld: the bounds must be "
+                         "multiples of 64 (the end may be n_kv)",
+                         (long long)key_begin, (long long)key_end, (long long)n_kv);
+    const int first = key_begin == 0, last = key_end == n_kv;
+    if (!(first && last)) {
+        if (!state || state_bytes_ < state_bytes(q_tiles, kvh) || !kvt::aligned(state, 4))
+            return kvt::fail(KVT_EINVAL, "kvt_attn_prefill_range: state of %zu bytes, need %zu",
+                             state_bytes_, state_bytes(q_tiles, kvh));
+    }
     if (n_q == 0)
         return KVT_OK;
-    if (!q || !out || (n_head > 0 && (!k_head || !v_head)) ||
-        (n_kv > n_head && (!k_tail || !v_tail)))
-        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill: null pointer");
-    if (!kvt::aligned(q, 16) || !kvt::aligned(out, 16) || !kvt::aligned(k_head, 8) ||
-        !kvt::aligned(v_head, 8) || !kvt::aligned(k_tail, 8) || !kvt::aligned(v_tail, 8))
-        return kvt::fail(KVT_EALIGN, "kvt_attn_prefill: q/out need 16-byte, K/V 8-byte alignment");
-    const int qpw = 32 * (kWaves / group);
-    const int64_t q_tiles = (n_q + qpw - 1) / qpw;
-    if (q_tiles * kvh > 0x7fffffffll)
-        return kvt::fail(KVT_ERANGE, "kvt_attn_prefill: too many query tiles");
-    const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    hipLaunchKernelGGL(prefill_q8_0, dim3((unsigned)(q_tiles * kvh)), dim3(kThreads), 0,
-                       kvt::as_stream(stream), static_cast<const _Float16 *>(q), n_q, q_pos0,
-                       n_qh, kvh, group, static_cast<const unsigned char *>(k_head),
-                       static_cast<const unsigned char *>(v_head), n_head,
-                       static_cast<const unsigned char *>(k_tail),
-                       static_cast<const unsigned char *>(v_tail), n_kv, causal, scale_log2, out);
+    launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head, k_tail,
+                   v_tail, n_kv, causal, scale, key_begin, key_end, static_cast<float *>(state),
+                   first, last, out, kvt::as_stream(stream));
     KVT_LAUNCHED("prefill_q8_0");
+    return KVT_OK;
+}
+
+// S7+S8 overlapped: the host tail crosses the link in arena-sized buckets on copy_stream while
+// stream attends the HBM head and then each staged bucket (llama-T staging, with the pages'
+// bounded arena and online-softmax fold over buckets).
+extern "C" int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_pos0,
+                                          int32_t n_qh, int32_t kvh, int32_t hd,
+                                          const void *k_head, const void *v_head, int64_t n_head,
+                                          const void *k_host, const void *v_host, int64_t n_kv,
+                                          int32_t kv_format, int32_t causal, float scale,
+                                          void *arena_k, void *arena_v, int64_t arena_rows,
+                                          void *state, size_t state_bytes_, float *out,
+                                          void *stream, void *copy_stream)
+{
+    int group = 0;
+    int64_t q_tiles = 0;
+    const int rc = check_prefill("kvt_attn_prefill_pipelined", q, n_q, q_pos0, n_qh, kvh, hd,
+                                 k_head, v_head, n_head, k_host, v_host, n_kv, kv_format, scale,
+                                 out, group, q_tiles);
+    if (rc != KVT_OK)
+        return rc;
+    hipStream_t s = kvt::as_stream(stream), cs = kvt::as_stream(copy_stream);
+    if (n_q == 0)
+        return KVT_OK;
+    if (n_head == n_kv) {   // nothing in host memory
+        launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
+                       nullptr, nullptr, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out, s);
+        KVT_LAUNCHED("prefill_q8_0");
+        return KVT_OK;
+    }
+    const int64_t slot_keys = arena_rows / 2 / kKT * kKT;
+    if (slot_keys < kKT || !arena_k || !arena_v || !kvt::aligned(arena_k, 8) ||
+        !kvt::aligned(arena_v, 8))
+        return kvt::fail(KVT_EINVAL,
+                         "kvt_attn_prefill_pipelined: arena of %lld rows (need >= 128, 8-byte "
+                         "aligned K and V)",
+                         (long long)arena_rows);
+    if (cs == s)
+        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill_pipelined: copy_stream must differ from "
+                                     "stream");
+    if (!state || state_bytes_ < state_bytes(q_tiles, kvh) || !kvt::aligned(state, 4))
+        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill_pipelined: state of %zu bytes, need %zu",
+                         state_bytes_, state_bytes(q_tiles, kvh));
+    hipEvent_t *ev = nullptr;
+    if (pipe_events(ev) != KVT_OK)
+        return KVT_EHIP;
+    const int64_t row_bytes = (int64_t)kvh * kHeadBytes;
+    const uintptr_t ak = reinterpret_cast<uintptr_t>(arena_k);
+    const uintptr_t av = reinterpret_cast<uintptr_t>(arena_v);
+    const uintptr_t hk = reinterpret_cast<uintptr_t>(k_host);
+    const uintptr_t hv = reinterpret_cast<uintptr_t>(v_host);
+    float *stf = static_cast<float *>(state);
+
+    // the copies start after everything already on `stream` (the tail's producers, and the
+    // previous call's passes over the arena)
+    KVT_HIP(hipEventRecord(ev[0], s));
+    KVT_HIP(hipStreamWaitEvent(cs, ev[0], 0));
+    const int64_t hb = n_head / kKT * kKT;   // head keys in whole tiles; the rest by bucket
+    bool started = false;
+    if (hb > 0) {
+        launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
+                       nullptr, nullptr, n_kv, causal, scale, 0, hb, stf, 1, 0, out, s);
+        KVT_LAUNCHED("prefill_q8_0");
+        started = true;
+    }
+    int b = 0;
+    for (int64_t kb = hb; kb < n_kv; kb += slot_keys, b++) {
+        const int64_t ke = kb + slot_keys < n_kv ? kb + slot_keys : n_kv;
+        const int slot = b & 1;
+        const int64_t r0 = kb > n_head ? kb : n_head;   // first host row of the bucket
+        const size_t bytes = (size_t)(ke - r0) * (size_t)row_bytes;
+        const uintptr_t sk = ak + (uintptr_t)(slot * slot_keys * row_bytes);
+        const uintptr_t sv = av + (uintptr_t)(slot * slot_keys * row_bytes);
+        if (b >= 2)
+            KVT_HIP(hipStreamWaitEvent(cs, ev[3 + slot], 0));
+        KVT_HIP(hipMemcpyAsync(reinterpret_cast<void *>(sk),
+                               reinterpret_cast<const void *>(hk + (r0 - n_head) * row_bytes),
+                               bytes, hipMemcpyDefault, cs));
+        KVT_HIP(hipMemcpyAsync(reinterpret_cast<void *>(sv),
+                               reinterpret_cast<const void *>(hv + (r0 - n_head) * row_bytes),
+                               bytes, hipMemcpyDefault, cs));
+        KVT_HIP(hipEventRecord(ev[1 + slot], cs));
+        KVT_HIP(hipStreamWaitEvent(s, ev[1 + slot], 0));
+        // the kernel reads row r >= n_head at tail + (r - n_head)*row_bytes: aim it at the slot
+        const uintptr_t shift = (uintptr_t)((r0 - n_head) * row_bytes);
+        launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
+                       reinterpret_cast<const void *>(sk - shift),
+                       reinterpret_cast<const void *>(sv - shift), n_kv, causal, scale, kb, ke,
+                       stf, started ? 0 : 1, ke == n_kv ? 1 : 0, out, s);
+        KVT_LAUNCHED("prefill_q8_0");
+        started = true;
+        KVT_HIP(hipEventRecord(ev[3 + slot], s));
+    }
     return KVT_OK;
 }

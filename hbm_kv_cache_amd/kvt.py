@@ -47,6 +47,13 @@ _SIGNATURES = {
                                        c_float, _P, _P, c_size_t, _P]),
     "kvt_attn_prefill": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P, c_int64,
                                  _P, _P, c_int64, c_int32, c_int32, c_float, _P, _P]),
+    "kvt_attn_prefill_state_bytes": (c_size_t, [c_int64, c_int32, c_int32]),
+    "kvt_attn_prefill_range": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P,
+                                       c_int64, _P, _P, c_int64, c_int32, c_int32, c_float,
+                                       c_int64, c_int64, _P, c_size_t, _P, _P]),
+    "kvt_attn_prefill_pipelined": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P,
+                                           _P, c_int64, _P, _P, c_int64, c_int32, c_int32,
+                                           c_float, _P, _P, c_int64, _P, c_size_t, _P, _P, _P]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -225,3 +232,29 @@ class HostBuffer:
             self.free()
         except Exception:
             pass
+
+
+def kvt_attn_prefill_state_bytes(n_q, n_qh, kvh) -> int:
+    return int(load().kvt_attn_prefill_state_bytes(int(n_q), int(n_qh), int(kvh)))
+
+
+def kvt_attn_prefill_range(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_tail, v_tail,
+                           n_kv, kv_format, causal, scale, key_begin, key_end, state,
+                           state_bytes, out, stream=None):
+    _check("kvt_attn_prefill_range", load().kvt_attn_prefill_range(
+        _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
+        int(n_head), _ptr(k_tail), _ptr(v_tail), int(n_kv), int(kv_format), int(bool(causal)),
+        float(scale), int(key_begin), int(key_end), _ptr(state), int(state_bytes), _ptr(out),
+        _stream(stream)))
+
+
+def kvt_attn_prefill_pipelined(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_host,
+                               v_host, n_kv, kv_format, causal, scale, arena_k, arena_v,
+                               arena_rows, state, state_bytes, out, stream=None,
+                               copy_stream=None):
+    """copy_stream: a hipStream_t handle or torch Stream; it must differ from `stream`."""
+    _check("kvt_attn_prefill_pipelined", load().kvt_attn_prefill_pipelined(
+        _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
+        int(n_head), _ptr(k_host), _ptr(v_host), int(n_kv), int(kv_format), int(bool(causal)),
+        float(scale), _ptr(arena_k), _ptr(arena_v), int(arena_rows), _ptr(state),
+        int(state_bytes), _ptr(out), _stream(stream), _stream(copy_stream)))

@@ -12,6 +12,8 @@
  *   kvt_attn_decode      GQA decode attention over gathered K/V
  *   kvt_gather_attn_decode  the gather and the decode attention in one pass
  *   kvt_attn_prefill     causal (or full) prefill attention over an HBM head + tail
+ *   kvt_attn_prefill_range      the same attention as resumable passes over key ranges
+ *   kvt_attn_prefill_pipelined  tail staging in arena buckets overlapped with the attention
  *
  * Sources (page titles; each entry point names the section it follows):
  *   [vLLM-CPU] vLLM fork, "v1/kv_offload/cpu/gpu_worker.py" (CPU offloading worker)
@@ -44,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 2
+#define KVT_ABI_VERSION 3
 
 /* status codes */
 #define KVT_OK 0
@@ -239,6 +241,55 @@ int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, i
                      int32_t hd, const void *k_head, const void *v_head, int64_t n_head,
                      const void *k_tail, const void *v_tail, int64_t n_kv, int32_t kv_format,
                      int32_t causal, float scale, float *out, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S8 as resumable passes.  [QSA-KVO] staged attention folds bucket partials with the online-
+ * softmax rule; here a pass over keys [key_begin, key_end) continues from the running
+ * (o, m, l) of the previous pass, kept in `state` in exact fp32, so any split into passes
+ * gives the same bits as kvt_attn_prefill (the tiles, their order and the arithmetic are the
+ * same).  Arguments as kvt_attn_prefill, plus:
+ *   key_begin, key_end  multiples of 64 (key_end may be n_kv); passes must cover [0, n_kv) in
+ *                       order, each starting where the last ended.  The first pass
+ *                       (key_begin == 0) starts a fresh state; the last (key_end == n_kv)
+ *                       writes `out`, the others write only `state`.
+ *   state               device, kvt_attn_prefill_state_bytes(n_q, n_qh, kvh) bytes, owned by
+ *                       the caller; opaque layout; may be NULL for a single pass [0, n_kv).
+ * Rows a pass reads through k_tail/v_tail must be valid during that pass only: a pass over
+ * [key_begin, key_end) touches no row outside that range.
+ * ---------------------------------------------------------------------------------------- */
+size_t kvt_attn_prefill_state_bytes(int64_t n_q, int32_t n_qh, int32_t kvh);
+int kvt_attn_prefill_range(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                           int32_t kvh, int32_t hd, const void *k_head, const void *v_head,
+                           int64_t n_head, const void *k_tail, const void *v_tail, int64_t n_kv,
+                           int32_t kv_format, int32_t causal, float scale, int64_t key_begin,
+                           int64_t key_end, void *state, size_t state_bytes, float *out,
+                           void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S7+S8 overlapped.  [llama-T] stages the used host rows into VRAM once per op; [QSA-KVO]
+ * stages in arena-sized buckets and overlaps the copy of one bucket with attention on the
+ * previous.  Here: `stream` attends the HBM head (whole 64-key tiles) while `copy_stream`
+ * copies the first bucket of host rows into one half of the arena; then each bucket is
+ * attended from its arena half while the next bucket is copied into the other half.
+ *   k_host, v_host      device aliases of the host tail: row r >= n_head at
+ *                       k_host + (r - n_head)*row_bytes (row_bytes = kvh*136 for q8_0, hd 128)
+ *   arena_k, arena_v    device (HBM), arena_rows rows each (>= 128); buckets are
+ *                       floor(arena_rows/2 / 64)*64 keys
+ *   state               as kvt_attn_prefill_range (required)
+ *   stream, copy_stream two different streams; the copies wait for everything enqueued on
+ *                       `stream` before the call, and `stream` waits for each copy it reads,
+ *                       so the op is ordered on `stream` like any other call.
+ * The output equals kvt_attn_prefill's bit for bit.  The library keeps five events per host
+ * thread (created on the first call on a device, then reused); calls from one thread are
+ * ordered through them, so two calls on one thread must use the same `stream`.
+ * Limits: as kvt_attn_prefill.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                               int32_t kvh, int32_t hd, const void *k_head, const void *v_head,
+                               int64_t n_head, const void *k_host, const void *v_host,
+                               int64_t n_kv, int32_t kv_format, int32_t causal, float scale,
+                               void *arena_k, void *arena_v, int64_t arena_rows, void *state,
+                               size_t state_bytes, float *out, void *stream, void *copy_stream);
 
 #ifdef __cplusplus
 }

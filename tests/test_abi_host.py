@@ -34,7 +34,7 @@ def test_header_declarations_all_exported():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 2
+    assert kvt.kvt_abi_version() == 3
 
 
 def test_library_has_gfx950_code_object():
@@ -112,6 +112,24 @@ def test_argument_errors_return_before_any_device_work():
         with pytest.raises(kvt.KvtError) as e:
             kvt.kvt_gather_attn_decode(**{**fused, **change})
         assert e.value.code == code, change
+    pre = dict(q=16, n_q=4, q_pos0=0, n_qh=8, kvh=8, hd=128, k_head=16, v_head=16, n_head=100,
+               k_tail=16, v_tail=16, n_kv=1000, kv_format=kvt.Q8_0, causal=1, scale=0.1,
+               key_begin=0, key_end=128, state=16, state_bytes=1 << 30, out=16, stream=0)
+    for change in (dict(key_begin=10), dict(key_end=100), dict(key_end=1001),
+                   dict(state_bytes=16), dict(state=None)):
+        with pytest.raises(kvt.KvtError) as e:
+            kvt.kvt_attn_prefill_range(**{**pre, **change})
+        assert e.value.code == kvt.EINVAL, change
+    pipe = {k_: v_ for k_, v_ in pre.items() if k_ not in ("key_begin", "key_end", "k_tail",
+                                                           "v_tail")}
+    pipe.update(k_host=16, v_host=16, arena_k=16, arena_v=16, arena_rows=4096, copy_stream=8)
+    for change in (dict(arena_rows=100), dict(copy_stream=0), dict(state_bytes=16),
+                   dict(arena_k=None)):
+        with pytest.raises(kvt.KvtError) as e:
+            kvt.kvt_attn_prefill_pipelined(**{**pipe, **change})
+        assert e.value.code == kvt.EINVAL, change
+    assert kvt.kvt_attn_prefill_state_bytes(2048, 32, 8) == 32 * 8 * 8 * 66 * 64 * 4
+    assert kvt.kvt_attn_prefill_state_bytes(10, 12, 1) == 0      # group 12: unsupported
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_stage_tail(16, 0, 0, 10, 16, kvt.COPY_AUTO, stream=0)
     assert e.value.code == kvt.EINVAL

@@ -107,6 +107,88 @@ def test_prefill_three_way_bit_identity(gpu):
     host.free()
 
 
+def _pipelined(q_np, q_pos0, kvh, k_head, v_head, n_head, host, n_kv, arena_rows, dev,
+               causal=True):
+    """kvt_attn_prefill_pipelined with the host tail in `host` (K rows then V rows)."""
+    n_q, n_qh, hd = q_np.shape
+    row = kvh * 136
+    n_tail = n_kv - n_head
+    q = torch.from_numpy(q_np.view(np.int16)).to(dev)
+    out = torch.full((n_q, n_qh, hd), float("nan"), dtype=torch.float32, device=dev)
+    arena = torch.full((2, arena_rows, row), 0xA5, dtype=torch.uint8, device=dev)
+    sb = kvt.kvt_attn_prefill_state_bytes(n_q, n_qh, kvh)
+    state = torch.empty(sb, dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
+    kvt.kvt_attn_prefill_pipelined(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head,
+                                   host.dev, host.dev + n_tail * row, n_kv, kvt.Q8_0, causal,
+                                   1 / math.sqrt(hd), arena[0], arena[1], arena_rows, state, sb,
+                                   out, copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_prefill_range_passes_bit_identical(gpu):
+    """The attention as resumable passes over key ranges -- including an empty pass and a pass
+    that starts mid-head and ends in the tail -- gives the single pass's bits."""
+    n_kv, n_q, n_qh, kvh, n_head = 1000, 77, 32, 8, 400
+    k, v = _cache(n_kv, kvh, 21)
+    q_np = synth.f16_normal(synth.rng(5, synth.P_Q, 21), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    one = _prefill(q_np, q_pos0, kvh, kd, vd, n_head, kd[n_head:], vd[n_head:], n_kv, True, gpu)
+    q = torch.from_numpy(q_np.view(np.int16)).to(gpu)
+    sb = kvt.kvt_attn_prefill_state_bytes(n_q, n_qh, kvh)
+    state = torch.empty(sb, dtype=torch.uint8, device=gpu)
+    for cuts in ([0, 128, 128, 512, 1000], [0, 64, 448, 960, 1000], [0, 1000]):
+        out = torch.full((n_q, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            kvt.kvt_attn_prefill_range(q, n_q, q_pos0, n_qh, kvh, 128, kd, vd, n_head,
+                                       kd[n_head:], vd[n_head:], n_kv, kvt.Q8_0, True,
+                                       1 / math.sqrt(128), a, b, state, sb, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), one.view(np.uint32)), cuts
+    with pytest.raises(kvt.KvtError) as e:                 # bounds must be whole tiles
+        kvt.kvt_attn_prefill_range(q, n_q, q_pos0, n_qh, kvh, 128, kd, vd, n_head, kd[n_head:],
+                                   vd[n_head:], n_kv, kvt.Q8_0, True, 0.1, 0, 100, state, sb, out)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:                 # a split pass needs the state
+        kvt.kvt_attn_prefill_range(q, n_q, q_pos0, n_qh, kvh, 128, kd, vd, n_head, kd[n_head:],
+                                   vd[n_head:], n_kv, kvt.Q8_0, True, 0.1, 0, 128, state, 16, out)
+    assert e.value.code == kvt.EINVAL
+
+
+@pytest.mark.parametrize("n_kv,n_head,arena_rows,n_qh,kvh", [
+    (5000, 2100, 128, 32, 8),      # 64-key buckets, head split mid-tile
+    (5000, 2048, 1000, 32, 8),     # head on a tile boundary, buckets of 448 keys
+    (5000, 0, 3000, 16, 4),        # no head: buckets from key 0
+    (5000, 4999, 256, 8, 8),       # one host row
+    (3000, 1500, 100000, 32, 8),   # the whole tail in one bucket
+    (2000, 2000, 128, 32, 8),      # nothing in host memory
+])
+def test_prefill_pipelined_bit_identical(gpu, n_kv, n_head, arena_rows, n_qh, kvh):
+    """Tail staged in arena buckets on a second stream while the head and earlier buckets are
+    attended: the same bits as the single pass over an all-HBM cache, on two calls in a row
+    (the second reuses the library's events and the arena)."""
+    n_q = 300
+    k, v = _cache(n_kv, kvh, n_kv + n_head)
+    row = k.shape[1]
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, n_head + 7), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    all_hbm = _prefill(q, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    n_tail = n_kv - n_head
+    host = kvt.HostBuffer(max(2 * n_tail * row, 16))
+    if n_tail:
+        ht = host.numpy(np.uint8, (2, n_tail, row))
+        ht[0], ht[1] = k[n_head:], v[n_head:]
+        del ht
+    for _ in range(2):
+        got = _pipelined(q, q_pos0, kvh, kd[:max(n_head, 1)], vd[:max(n_head, 1)], n_head, host,
+                         n_kv, arena_rows, gpu)
+        assert np.array_equal(got.view(np.uint32), all_hbm.view(np.uint32))
+    host.free()
+
+
 def test_prefill_full_geometry_sampled_rows(gpu):
     """180,000-token context, cells [0, 94208) in HBM and the rest in host memory, q8_0 K/V
     (8 KV heads x 128), a 2048-query causal chunk at the tail with 32 query heads: stage the
@@ -138,6 +220,9 @@ def test_prefill_full_geometry_sampled_rows(gpu):
     kall, vall = _dev(k, gpu), _dev(v, gpu)
     all_hbm = _prefill(q, q_pos0, kvh, kall, vall, n_kv, None, None, n_kv, True, gpu)
     assert np.array_equal(all_hbm.view(np.uint32), staged.view(np.uint32))
+    del kall, vall
+    pipelined = _pipelined(q, q_pos0, kvh, kd, vd, n_head, host, n_kv, 32768, gpu)
+    assert np.array_equal(pipelined.view(np.uint32), staged.view(np.uint32))
     del ht
     host.free()
 
