@@ -244,10 +244,17 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     // per tile: multiply fp16 buffer (tile & 1); dequantise raw tile+1 into the other fp16
     // buffer; move the registers of tile+2 into the raw buffer tile+1 just left; one barrier;
     // then issue the loads of tile+3
+    const bool dequant_first = wave >= 4;
     for (int tile = b0; tile < n_tiles; tile++) {
         const unsigned char *lk = lds + (tile & 1) * kLdsBuf;
         const unsigned char *lv = lk + kLdsK;
         const int64_t key0 = (int64_t)tile * kKT;
+        // Waves w and w + 4 share a SIMD.  The upper four dequantise the next tile before they
+        // multiply this one and the lower four after, so on every SIMD one wave's MFMA work
+        // meets the other's VALU work.
+        if (dequant_first && tile + 1 < n_tiles)
+            dequant_tile(lds_raw + ((tile + 1) & 1) * kRawBytes, lds + ((tile + 1) & 1) * kLdsBuf,
+                         wave, lane);
         if (key0 <= wave_last) {
             // S^T tile: rows = keys 32*st + (lane & 31), columns = this wave's 32 query rows
             f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -326,10 +333,10 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
                 }
             }
         }
-        if (tile + 1 < n_tiles)
+        if (!dequant_first && tile + 1 < n_tiles)
             dequant_tile(lds_raw + ((tile + 1) & 1) * kRawBytes, lds + ((tile + 1) & 1) * kLdsBuf,
                          wave, lane);
-        if (tile + 2 < n_tiles)
+        if (tile + 2 < n_tiles)   // last, so the loads of tile + 2 have had the whole tile
             store_raw(lds_raw + (tile & 1) * kRawBytes, rq);
         __syncthreads();
         if (tile + 3 < n_tiles)
