@@ -44,7 +44,7 @@ def parse():
                    help="host K/V plane layout (block-local head-major, or token-major)")
     p.add_argument("--suite", nargs="?", const="all", default=None,
                    help="also measure the other workloads: all, or a comma list of "
-                        "prefill, swap1, small, swap32, decode1m")
+                        "prefill, swap1, small, swap32, qsa, decode1m")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the CPU-oracle baseline's wall time")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -654,9 +654,77 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
     return res
 
 
+def suite_qsa(torch, kvt, synth, dev, wl, args, reps=None):
+    """The QSA indexer's own selection geometry on the headline's host planes: pooled keys over
+    4-token blocks, top-512 per KV head, token positions plus the write head's tail padded to
+    K_pad = 2080, then the fused gather + attention over those tokens (token-major addressing).
+    262,143 tokens: 65,535 complete pooled blocks and a 3-token tail."""
+    import numpy as np
+    kvh, hd, n_qh, cr, k = wl.KVH, wl.HD, wl.NQH, 4, 512
+    n_tok = wl.ctx - 1
+    n_blocks = n_tok // cr
+    k_pad = -(-(k * cr + cr - 1) // 32) * 32
+    row = kvh * hd * 2
+    n_sets = args.warmup + args.steps
+    pooled = torch.from_numpy(synth.f16_normal(synth.rng(4, synth.P_POOLED, n_tok),
+                                               (n_blocks, 128)).view(np.int16)).to(dev)
+    qidx = torch.from_numpy(synth.f16_normal(synth.rng(4, synth.P_QIDX, n_tok),
+                                             (n_sets, kvh, 128)).view(np.int16)).to(dev)
+    ws_t = kvt.kvt_index_topk_ws_bytes(n_blocks, kvh, k)
+    ws_d = kvt.kvt_attn_decode_ws_bytes(n_qh, hd, k_pad)
+    ws = torch.empty(ws_t + ws_d + 256, dtype=torch.uint8, device=dev)
+    ids = torch.empty((kvh, k), dtype=torch.int32, device=dev)
+    pos = torch.empty((kvh, k_pad), dtype=torch.int32, device=dev)
+    kv = torch.empty((2, kvh, k_pad, hd), dtype=torch.int16, device=dev)
+    out = torch.empty((n_qh, hd), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def parts(i):
+        return [("topk", lambda: kvt.kvt_index_topk(pooled, n_blocks, 128, qidx[i % n_sets], kvh,
+                                                     k, ids, None, ws, ws_t)),
+                ("positions", lambda: kvt.kvt_select_positions(ids, kvh, k, cr, n_tok, k_pad,
+                                                                pos)),
+                ("gather_attn", lambda: kvt.kvt_gather_attn_decode(
+                    wl.q[i % wl.n_sets], n_qh, kvh, hd, kvt.BF16, wl.host.dev,
+                    wl.host.dev + wl.ctx * wl.row, n_tok, row, hd * 2, row, None, 1, pos, k_pad,
+                    kv[0], kv[1], wl.scale, out, ws[ws_t + 128:], ws_d))]
+
+    for i in range(args.warmup):
+        for _, fn in parts(i):
+            fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        for _, fn in parts(args.warmup + i):
+            fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    names = [n for n, _ in parts(0)]
+    acc = {n: 0.0 for n in names}
+    for i in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        evs[0].record(stream)
+        for j, (_, fn) in enumerate(parts(args.warmup + i)):
+            fn()
+            evs[j + 1].record(stream)
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            acc[n] += evs[j].elapsed_time(evs[j + 1]) / args.steps
+    host_bytes = kvh * (k * cr + n_tok % cr) * hd * 2 * 2
+    res = {"n_tok": n_tok, "cr": cr, "block_topk": k, "k_pad": k_pad, "pooled_blocks": n_blocks,
+           "ms_per_step": round(ms, 5), "decode_tok_s": round(1e3 / ms, 2),
+           "host_bytes_per_step": host_bytes,
+           "gather_gbs_whole_step": round(host_bytes / (ms * 1e-3) / GB, 3),
+           "part_ms": {n_: round(v, 5) for n_, v in acc.items()}}
+    log("qsa geometry", res)
+    return res
+
+
 def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     want = set(args.suite.split(",")) if args.suite != "all" else {
-        "prefill", "swap1", "small", "swap32", "decode1m"}
+        "prefill", "swap1", "small", "swap32", "qsa", "decode1m"}
     out = {}
     if "prefill" in want:
         log("suite: tiered prefill")
@@ -670,6 +738,9 @@ def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     if "swap32" in want:
         log("suite: 32-layer swap")
         out["swap_32_layers"] = suite_32_layers(torch, kvt, synth, dev, peaks)
+    if "qsa" in want:
+        log("suite: QSA selection geometry")
+        out["qsa_geometry"] = suite_qsa(torch, kvt, synth, dev, wl, args)
     if "decode1m" in want:
         log("suite: decode at 1,048,576")
         w1m = DecodeWorkload(torch, kvt, synth, dev, 1 << 20, args.warmup + 2 * args.steps)

@@ -15,7 +15,7 @@
 //     best-32 (the running list in lanes 0..31, the incoming list reversed in lanes 32..63:
 //     a bitonic sequence, cleaned in six shuffle steps), then the 16 waves fold pairwise
 //     through LDS, and the winners' ids are sorted ascending by one more lane sort.
-// Generic path (k up to 256):
+// Generic path (k up to kMergeMax / 2 = 2048: each merge level at least halves the candidates):
 //   score_local_topk -- the same scoring over 128-row chunks, candidates cut to min(k, 128) by
 //     a segmented bitonic sort in LDS;  merge_topk -- segments of up to 4096 candidates sorted
 //     in LDS and cut to k, repeated until one segment per head remains.
@@ -59,7 +59,8 @@ __device__ void bitonic_best_first(uint64_t *key, uint32_t *id, int n, int seg)
     for (int size = 2; size <= seg; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
-                const int i = (p / stride) * 2 * stride + (p % stride);
+                // stride is a power of two: i = (p / stride) * 2 * stride + p % stride
+                const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
                 const int j = i + stride;
                 const bool up = size == seg || (i & size) == 0;
                 const uint64_t ka = key[i], kb = key[j];
@@ -81,7 +82,7 @@ __device__ void bitonic_ids_ascending(uint32_t *id, int n)
     for (int size = 2; size <= n; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
-                const int i = (p / stride) * 2 * stride + (p % stride);
+                const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
                 const int j = i + stride;
                 const bool up = size == n || (i & size) == 0;
                 const uint32_t a = id[i], b = id[j];
@@ -517,7 +518,7 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
                               double *scores, void *ws, size_t ws_bytes, void *stream)
 {
     if (n_blocks < 0 || n_blocks > 0x7fffffffll || dim < 8 || dim > 256 || dim % 8 ||
-        n_sel < 1 || n_sel > 32 || k < 1 || k > 256)
+        n_sel < 1 || n_sel > 32 || k < 1 || k > kMergeMax / 2)
         return kvt::fail(KVT_EINVAL,
                          "kvt_index_topk: n_blocks=%lld dim=%d n_sel=%d k=%d outside limits",
                          (long long)n_blocks, dim, n_sel, k);
@@ -594,4 +595,60 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
         n = segs * k;
         in_a = !in_a;
     }
+}
+
+namespace {
+
+// grid = n_sel, 256 threads.  ids[h] ascending, -1 only at the end (kvt_index_topk's output).
+__global__ __launch_bounds__(256) void select_positions_kernel(const int32_t *__restrict__ ids,
+                                                               int k, int cr, int64_t n_tok,
+                                                               int k_pad,
+                                                               int32_t *__restrict__ positions)
+{
+    const int h = blockIdx.x;
+    const int32_t *hid = ids + (int64_t)h * k;
+    // valid ids form a prefix: find its length by bisection on "id >= 0"
+    int lo = 0, hi = k;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (hid[mid] >= 0)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    const int64_t n_sel_tok = (int64_t)lo * cr;
+    const int64_t tail0 = n_tok / cr * cr;           // first token not in a complete block
+    const int64_t n_tail = n_tok - tail0;
+    int32_t *out = positions + (int64_t)h * k_pad;
+    for (int j = threadIdx.x; j < k_pad; j += 256) {
+        int64_t p = -1;
+        if (j < n_sel_tok)
+            p = (int64_t)hid[j / cr] * cr + j % cr;
+        else if (j - n_sel_tok < n_tail)
+            p = tail0 + (j - n_sel_tok);
+        out[j] = (int32_t)p;
+    }
+}
+
+}  // namespace
+
+// QSA-KVO selection geometry: the indexer selects pooled blocks of cr tokens; a row attends their
+// positions plus the write head's tail (the < cr newest tokens no complete block covers),
+// padded with -1 to K_pad = ceil((block_topk*cr + cr - 1) / 32) * 32.
+extern "C" int kvt_select_positions(const int32_t *ids, int32_t n_sel, int32_t k, int32_t cr,
+                                    int64_t n_tok, int32_t k_pad, int32_t *positions,
+                                    void *stream)
+{
+    if (n_sel < 1 || k < 1 || cr < 1 || n_tok < 0 || n_tok > 0x7fffffffll ||
+        (int64_t)k * cr + cr - 1 > k_pad)
+        return kvt::fail(KVT_EINVAL,
+                         "kvt_select_positions: n_sel=%d k=%d cr=%d n_tok=%lld k_pad=%d (need "
+                         "k_pad >= k*cr + cr - 1)",
+                         n_sel, k, cr, (long long)n_tok, k_pad);
+    if (!ids || !positions)
+        return kvt::fail(KVT_EINVAL, "kvt_select_positions: null pointer");
+    hipLaunchKernelGGL(select_positions_kernel, dim3(n_sel), dim3(256), 0, kvt::as_stream(stream),
+                       ids, k, cr, n_tok, k_pad, positions);
+    KVT_LAUNCHED("select_positions_kernel");
+    return KVT_OK;
 }

@@ -36,6 +36,7 @@ _SIGNATURES = {
     "kvt_index_topk_ws_bytes": (c_size_t, [c_int64, c_int32, c_int32]),
     "kvt_index_topk": (c_int, [_P, c_int64, c_int32, _P, c_int32, c_int32, _P, _P, _P, c_size_t,
                                _P]),
+    "kvt_select_positions": (c_int, [_P, c_int32, c_int32, c_int32, c_int64, c_int32, _P, _P]),
     "kvt_gather_blocks": (c_int, [_P, _P, c_int64, c_int32, c_int32, c_int32, c_int64, c_int64,
                                   c_int64, _P, c_int32, _P, c_int32, _P, _P, _P]),
     "kvt_stage_tail": (c_int, [_P, c_int64, c_int64, c_int64, _P, c_int32, _P]),
@@ -158,6 +159,12 @@ def kvt_index_topk(pooled, n_blocks, dim, q_idx, n_sel, k, ids, scores, ws, ws_b
     _check("kvt_index_topk", load().kvt_index_topk(
         _ptr(pooled), int(n_blocks), int(dim), _ptr(q_idx), int(n_sel), int(k), _ptr(ids),
         _ptr(scores), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def kvt_select_positions(ids, n_sel, k, cr, n_tok, k_pad, positions, stream=None):
+    _check("kvt_select_positions", load().kvt_select_positions(
+        _ptr(ids), int(n_sel), int(k), int(cr), int(n_tok), int(k_pad), _ptr(positions),
+        _stream(stream)))
 
 
 def kvt_gather_blocks(k_plane, v_plane, n_blocks, kvh, hd, elem_bytes, block_stride,

@@ -7,6 +7,7 @@
  *   kvt_sub_block_ptrs   build src/dst/size pointer tables        (host, pure)
  *   kvt_swap_blocks      batched block copy driven by those tables (host<->HBM)
  *   kvt_index_topk       score a pooled indexer plane in HBM, select the top-k blocks
+ *   kvt_select_positions expand selected pooled blocks into token positions (+ write-head tail)
  *   kvt_gather_blocks    copy only the selected blocks' K/V rows host -> HBM
  *   kvt_stage_tail       copy a sequence's host-resident rows into an HBM staging buffer
  *   kvt_attn_decode      GQA decode attention over gathered K/V
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 3
+#define KVT_ABI_VERSION 4
 
 /* status codes */
 #define KVT_OK 0
@@ -142,12 +143,27 @@ uint64_t kvt_set_copy_threshold(int32_t dir, uint64_t bytes);
  *           order; when k > n_blocks the trailing slots hold -1.
  *   scores  optional device fp64 [n_sel][n_blocks] copy of every score (NULL to skip).
  *   ws      device workspace of kvt_index_topk_ws_bytes(n_blocks, n_sel, k) bytes.
- * Limits: 1 <= k <= 256, dim a multiple of 8 and <= 256, 1 <= n_sel <= 32.
+ * Limits: 1 <= k <= 2048, dim a multiple of 8 and <= 256, 1 <= n_sel <= 32.
  * ---------------------------------------------------------------------------------------- */
 size_t kvt_index_topk_ws_bytes(int64_t n_blocks, int32_t n_sel, int32_t k);
 int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim, const void *q_idx,
                    int32_t n_sel, int32_t k, int32_t *ids, double *scores, void *ws,
                    size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S4 selection geometry.  [QSA-KVO] indexer: each pooled key covers cr tokens, a row selects
+ * block_topk pooled blocks, and reads their cr*block_topk token positions plus the tokens at
+ * the write head that no complete pooled block covers yet, -1 padded to
+ * K_pad = ceil((block_topk*cr + cr - 1) / 32) * 32 (2080 for block_topk 512, cr 4).
+ *   ids        device int32 [n_sel][k]: selected pooled-block ids, ascending, -1 only at the end
+ *              (kvt_index_topk's output over the n_tok / cr complete blocks)
+ *   positions  device int32 [n_sel][k_pad]: for the v valid ids, positions id*cr + 0..cr-1 in
+ *              order; then cr*floor(n_tok/cr) .. n_tok-1; then -1.  Ascending up to the first -1.
+ * Limits: k_pad >= k*cr + cr - 1, n_tok < 2^31.  Feed positions to kvt_gather_attn_decode (or
+ * kvt_gather_blocks) with bt = 1, k = k_pad, n_blocks = n_tok and per-token strides.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_select_positions(const int32_t *ids, int32_t n_sel, int32_t k, int32_t cr, int64_t n_tok,
+                         int32_t k_pad, int32_t *positions, void *stream);
 
 /* ----------------------------------------------------------------------------------------
  * S5  top-k gather.  [QSA-KVO] sparse_attend / CacheLayer_qsa_offload: only the selected

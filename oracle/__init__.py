@@ -197,6 +197,31 @@ def attn_decode(q_u16, k_u16, v_u16, fmt, scale, n_valid=None, threads=0):
     return out
 
 
+def qsa_k_pad(block_topk, cr):
+    """Selection width of the QSA indexer: block_topk*cr positions plus up to cr - 1 tail
+    positions, rounded up to a multiple of 32."""
+    return -(-(block_topk * cr + cr - 1) // 32) * 32
+
+
+def select_positions(ids, cr, n_tok, k_pad):
+    """Token positions of the selected pooled blocks (each covers cr tokens), in id order, then
+    the write head's tail (tokens cr*floor(n_tok/cr) .. n_tok-1), then -1 up to k_pad.
+    ids: int [n_sel][k], ascending with -1 only at the end."""
+    ids = np.asarray(ids)
+    out = np.full((ids.shape[0], k_pad), -1, dtype=np.int32)
+    tail = list(range(n_tok // cr * cr, n_tok))
+    for h in range(ids.shape[0]):
+        pos = []
+        for b in ids[h]:
+            if b < 0:
+                break
+            pos.extend(int(b) * cr + r for r in range(cr))
+        pos.extend(tail)
+        assert len(pos) <= k_pad
+        out[h, :len(pos)] = pos
+    return out
+
+
 def gather_attn_decode(q_u16, k_plane, v_plane, n_blocks, kvh, hd, fmt, strides, ids,
                        block_tokens, scale, block_table=None, threads=0):
     """Decode attention over the selected blocks' rows (elements of 2 bytes) read through the

@@ -33,7 +33,8 @@ def _run_topk(pooled, q_idx, k, dev, want_scores=True):
 
 
 @pytest.mark.parametrize("n_blocks,k", [(4096, 32), (16384, 32), (5000, 32), (129, 32), (100, 32),
-                                        (1, 32), (32, 32), (70000, 32), (3000, 200), (5, 1)])
+                                        (1, 32), (32, 32), (70000, 32), (3000, 200), (5, 1),
+                                        (65536, 512), (70000, 1000), (5000, 2048), (300, 512)])
 def test_index_topk_bit_exact(gpu, n_blocks, k):
     g = synth.rng(4, synth.P_POOLED, n_blocks + k)
     pooled = synth.f16_normal(g, (n_blocks, 128))
@@ -364,5 +365,72 @@ def test_fused_decode_step_full_geometry(gpu, ctx):
     got = kg.cpu().numpy().view(np.uint8).reshape(2, kvh, k * bt, hd * 2)
     assert np.array_equal(got[0], ko) and np.array_equal(got[1], vo)
     assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
+    del planes
+    buf.free()
+
+
+@pytest.mark.parametrize("cr,n_tok,k", [(4, 1003, 40), (4, 1000, 40), (1, 77, 10), (64, 1285, 7),
+                                        (4, 3, 8)])
+def test_select_positions_bit_exact(gpu, cr, n_tok, k):
+    g = synth.rng(4, synth.P_MISC, cr * 1000 + n_tok)
+    n_blocks = n_tok // cr
+    rows = [np.sort(g.permutation(n_blocks)[:min(k, n_blocks)]) for _ in range(3)]
+    ids = np.full((3, k), -1, dtype=np.int32)
+    for h, r in enumerate(rows):
+        ids[h, :r.size] = r
+    ids[1, k // 2:] = -1
+    k_pad = oracle.qsa_k_pad(k, cr)
+    pos = torch.full((3, k_pad), 12345, dtype=torch.int32, device=gpu)
+    kvt.kvt_select_positions(torch.from_numpy(ids).to(gpu), 3, k, cr, n_tok, k_pad, pos)
+    torch.cuda.synchronize()
+    assert np.array_equal(pos.cpu().numpy(), oracle.select_positions(ids, cr, n_tok, k_pad))
+    if cr > 1:
+        with pytest.raises(kvt.KvtError) as e:              # no room for a full tail
+            kvt.kvt_select_positions(torch.from_numpy(ids).to(gpu), 3, k, cr, n_tok,
+                                     k * cr + cr - 2, pos)
+        assert e.value.code == kvt.EINVAL
+
+
+def test_qsa_geometry_decode_step(gpu):
+    """The page's selection geometry at 262,147 tokens: pooled keys over 4-token blocks
+    (65,536 complete blocks), top-512 per KV head, positions + the 3-token write-head tail padded
+    to 2080, then the fused gather + attention over those tokens (64 query heads, token-major host
+    planes).  Ids, positions and gathered rows bit-exact; attention within 2e-3."""
+    kvh, hd, n_qh, cr, k = 8, 128, 64, 4, 512
+    n_tok = 262144 + 3
+    n_blocks = n_tok // cr
+    k_pad = oracle.qsa_k_pad(k, cr)
+    buf, planes = _host_planes(n_tok, kvh, hd, 4, 7)
+    pooled = synth.f16_normal(synth.rng(4, synth.P_POOLED, 7), (n_blocks, 128))
+    q_idx = synth.f16_normal(synth.rng(4, synth.P_QIDX, 7), (kvh, 128))
+    q = synth.bf16_normal(synth.rng(4, synth.P_Q, 7), (n_qh, hd))
+    ids, _ = _run_topk(pooled, q_idx, k, gpu, want_scores=False)
+    ref_ids = oracle.topk(oracle.index_scores(pooled, q_idx), k)
+    assert np.array_equal(ids, ref_ids)
+    pos = torch.empty((kvh, k_pad), dtype=torch.int32, device=gpu)
+    kvt.kvt_select_positions(torch.from_numpy(ids).to(gpu), kvh, k, cr, n_tok, k_pad, pos)
+    ref_pos = oracle.select_positions(ref_ids, cr, n_tok, k_pad)
+    torch.cuda.synchronize()
+    assert np.array_equal(pos.cpu().numpy(), ref_pos)
+    row = kvh * hd * 2
+    strides = (row, hd * 2, row)   # a "block" is one token of the token-major plane
+    ws_bytes = kvt.kvt_attn_decode_ws_bytes(n_qh, hd, k_pad)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=gpu)
+    kv = torch.full((2, kvh, k_pad, hd), 0x1234, dtype=torch.int16, device=gpu)
+    out = torch.empty((n_qh, hd), dtype=torch.float32, device=gpu)
+    kvt.kvt_gather_attn_decode(_u16(q, gpu), n_qh, kvh, hd, kvt.BF16, buf.dev,
+                               buf.dev + n_tok * row, n_tok, *strides, None, 1, pos, k_pad,
+                               kv[0], kv[1], 1 / math.sqrt(hd), out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.gather_attn_decode(q, planes[0].view(np.uint8), planes[1].view(np.uint8),
+                                          n_tok, kvh, hd, oracle.BF16, strides, ref_pos, 1,
+                                          1 / math.sqrt(hd))
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
+    can = np.zeros((kvh, k_pad, hd * 2), dtype=np.uint8)
+    can.view(np.uint16)[:] = 0x1234
+    ko, vo = oracle.gather(planes[0].view(np.uint8), planes[1].view(np.uint8), n_tok, kvh, hd, 2,
+                           strides, ref_pos, 1, k_out=can.copy(), v_out=can.copy())
+    got = kv.cpu().numpy().view(np.uint8).reshape(2, kvh, k_pad, hd * 2)
+    assert np.array_equal(got[0], ko) and np.array_equal(got[1], vo)
     del planes
     buf.free()

@@ -389,6 +389,35 @@ def test_gather_attn_decode_is_sdpa_over_valid_slots(with_table):
         assert np.max(np.abs(out[h * G:(h + 1) * G] - ref)) < 1e-12
 
 
+def test_qsa_selection_geometry_worked_values():
+    """K_pad and the expanded positions against values worked from the page's definitions."""
+    g = json.load(open(os.path.join(GOLDEN, "qsa_positions_worked.json")))
+    for c in g["k_pad_cases"]:
+        assert oracle.qsa_k_pad(c["block_topk"], c["cr"]) == c["k_pad"]
+    c = g["positions_case"]
+    got = oracle.select_positions(np.array(c["ids"]), c["cr"], c["n_tok"], c["k_pad"])
+    assert got.tolist() == c["expected"]
+
+
+def test_select_positions_properties():
+    """Random selections: valid positions are exactly the union of the blocks' token ranges and
+    the tail, strictly ascending, each below n_tok; the rest is -1."""
+    g = synth.rng(0, synth.P_MISC, 50)
+    for cr, n_tok, k in [(4, 1003, 40), (4, 1000, 40), (1, 77, 10), (64, 64 * 20 + 5, 7)]:
+        n_blocks = n_tok // cr
+        ids = np.stack([np.sort(g.permutation(n_blocks)[:min(k, n_blocks)]) for _ in range(3)])
+        ids = np.concatenate([ids, np.full((3, k - ids.shape[1]), -1)], axis=1)
+        ids[1, k // 2:] = -1                                   # fewer valid blocks
+        k_pad = oracle.qsa_k_pad(k, cr)
+        pos = oracle.select_positions(ids, cr, n_tok, k_pad)
+        for h in range(3):
+            want = sorted({int(b) * cr + r for b in ids[h] if b >= 0 for r in range(cr)} |
+                          set(range(n_tok // cr * cr, n_tok)))
+            v = pos[h][pos[h] >= 0]
+            assert v.tolist() == want
+            assert (pos[h][len(v):] == -1).all() and (v < n_tok).all()
+
+
 def _dequant_q8_0_numpy(rows, kvh, hd):
     """Independent decode of q8_0 rows with numpy dtypes: [n][kvh][hd] float64."""
     n = rows.shape[0]
