@@ -15,10 +15,10 @@
 //     best-32 (the running list in lanes 0..31, the incoming list reversed in lanes 32..63:
 //     a bitonic sequence, cleaned in six shuffle steps), then the 16 waves fold pairwise
 //     through LDS, and the winners' ids are sorted ascending by one more lane sort.
-// Generic path (k up to kMergeMax / 2 = 2048: each merge level at least halves the candidates):
-//   score_local_topk -- the same scoring over 128-row chunks, candidates cut to min(k, 128) by
-//     a segmented bitonic sort in LDS;  merge_topk -- segments of up to 4096 candidates sorted
-//     in LDS and cut to k, repeated until one segment per head remains.
+// Selection path (32 < k <= 2048):
+//   score_wave_topk<true> -- the same scoring, writing every rank key;  select_level -- exact
+//     selection by bisection over the (key, id) composite, per segment of up to 4096 keys, then
+//     once more over the survivors (up to 8192), whose output is already in id order.
 //
 // Rank order (a total order, so the result is unique): larger score first, equal scores by
 // lower block id, NaN after every number.  Encoded as a 64-bit key (larger = better) plus id.
@@ -28,10 +28,6 @@
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunkBlocks = 128;     // pooled rows per scoring workgroup
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeMax = 4096;       // candidates per merge workgroup (power of two)
 constexpr uint32_t kNoId = 0xffffffffu;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -51,187 +47,6 @@ __device__ __forceinline__ bool better(uint64_t ka, uint32_t ia, uint64_t kb, ui
 {
     return ka > kb || (ka == kb && ia < ib);
 }
-
-// In-place bitonic sort, best first, of n (power of two) entries split into independent
-// segments of `seg` (power of two, seg <= n).  All threads of the block take part.
-__device__ void bitonic_best_first(uint64_t *key, uint32_t *id, int n, int seg)
-{
-    for (int size = 2; size <= seg; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
-                // stride is a power of two: i = (p / stride) * 2 * stride + p % stride
-                const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
-                const int j = i + stride;
-                const bool up = size == seg || (i & size) == 0;
-                const uint64_t ka = key[i], kb = key[j];
-                const uint32_t ia = id[i], ib = id[j];
-                const bool swap = up ? better(kb, ib, ka, ia) : better(ka, ia, kb, ib);
-                if (swap) {
-                    key[i] = kb; key[j] = ka;
-                    id[i] = ib; id[j] = ia;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// ascending sort of n (power of two) ids, kNoId last
-__device__ void bitonic_ids_ascending(uint32_t *id, int n)
-{
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int p = threadIdx.x; p < (n >> 1); p += blockDim.x) {
-                const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
-                const int j = i + stride;
-                const bool up = size == n || (i & size) == 0;
-                const uint32_t a = id[i], b = id[j];
-                if (up ? b < a : a < b) {
-                    id[i] = b;
-                    id[j] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-__host__ __device__ constexpr int pow2_at_least(int x)
-{
-    int p = 1;
-    while (p < x)
-        p <<= 1;
-    return p;
-}
-
-// grid.x = ceil(n_blocks / kChunkBlocks); dynamic LDS = see score_lds_bytes
-__global__ __launch_bounds__(kThreads) void score_local_topk(
-    const uint16_t *__restrict__ pooled, int64_t n_blocks, int dim,
-    const uint16_t *__restrict__ q_idx, int n_sel, int kk, uint64_t *__restrict__ cand_key,
-    uint32_t *__restrict__ cand_id, double *__restrict__ scores_out)
-{
-    extern __shared__ __align__(16) unsigned char lds[];
-    const int pitch = dim * 2 + 16;  // bytes per staged pooled row (padded: no bank conflicts)
-    unsigned char *rows = lds;
-    float *qf = reinterpret_cast<float *>(lds + kChunkBlocks * pitch);
-    uint64_t *skey = reinterpret_cast<uint64_t *>(qf + n_sel * dim);
-    uint32_t *sid = reinterpret_cast<uint32_t *>(skey + n_sel * kChunkBlocks);
-
-    const int64_t b0 = (int64_t)blockIdx.x * kChunkBlocks;
-    const int nrows = (int)std::min<int64_t>(kChunkBlocks, n_blocks - b0);
-    const int words_per_row = dim / 8;
-
-    // stage pooled rows (16-byte words, coalesced) and the index queries (as exact fp32)
-    for (int w = threadIdx.x; w < nrows * words_per_row; w += kThreads) {
-        const int r = w / words_per_row, c = w % words_per_row;
-        const uint4 v = *reinterpret_cast<const uint4 *>(pooled + (b0 + r) * dim + c * 8);
-        *reinterpret_cast<uint4 *>(rows + r * pitch + c * 16) = v;
-    }
-    for (int e = threadIdx.x; e < n_sel * dim; e += kThreads)
-        qf[e] = f16_bits_to_f32(q_idx[e]);
-    __syncthreads();
-
-    // scores: pair p = h*kChunkBlocks + r; four independent fp64 chains per thread
-    const int npairs = n_sel * kChunkBlocks;
-    for (int p0 = threadIdx.x; p0 < npairs; p0 += 4 * kThreads) {
-        int r[4], h[4];
-        double acc[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int p = min(p0 + u * kThreads, npairs - 1);
-            h[u] = p / kChunkBlocks;
-            r[u] = p % kChunkBlocks;
-            if (r[u] >= nrows)
-                r[u] = 0;
-            acc[u] = 0.0;
-        }
-        for (int c = 0; c < words_per_row; c++) {
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(rows + r[u] * pitch + c * 16);
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                const float *qh = qf + h[u] * dim + c * 8;
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const uint16_t bits = (uint16_t)(w4[e >> 1] >> ((e & 1) * 16));
-                    const double pv = (double)f16_bits_to_f32(bits);
-                    acc[u] = fma((double)qh[e], pv, acc[u]);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int p = p0 + u * kThreads;
-            if (p >= npairs)
-                continue;
-            const int hh = p / kChunkBlocks, rr = p % kChunkBlocks;
-            if (rr < nrows) {
-                skey[p] = rank_key(acc[u]);
-                sid[p] = (uint32_t)(b0 + rr);
-                if (scores_out)
-                    scores_out[(int64_t)hh * n_blocks + b0 + rr] = acc[u];
-            } else {
-                skey[p] = 0;
-                sid[p] = kNoId;
-            }
-        }
-    }
-    __syncthreads();
-
-    bitonic_best_first(skey, sid, npairs, kChunkBlocks);
-
-    // best kk of each head's segment -> candidates [h][blockIdx][kk]
-    for (int e = threadIdx.x; e < n_sel * kk; e += kThreads) {
-        const int hh = e / kk, i = e % kk;
-        const int64_t o = ((int64_t)hh * gridDim.x + blockIdx.x) * kk + i;
-        cand_key[o] = skey[hh * kChunkBlocks + i];
-        cand_id[o] = sid[hh * kChunkBlocks + i];
-    }
-}
-
-// grid = (n_seg_out, n_sel).  Input per head: n_in candidates; segment s covers
-// [s*kMergeMax, ...).  Output per head: n_seg_out*k candidates, or (final) k ids.
-__global__ __launch_bounds__(kMergeThreads) void merge_topk(
-    const uint64_t *__restrict__ in_key, const uint32_t *__restrict__ in_id, int64_t n_in,
-    int k, uint64_t *__restrict__ out_key, uint32_t *__restrict__ out_id,
-    int32_t *__restrict__ ids_final)
-{
-    __shared__ uint64_t skey[kMergeMax];
-    __shared__ uint32_t sid[kMergeMax];
-    const int h = blockIdx.y;
-    const int64_t s0 = (int64_t)blockIdx.x * kMergeMax;
-    const int cnt = (int)std::min<int64_t>(kMergeMax, n_in - s0);
-    const int n = pow2_at_least(std::max(cnt, k));
-    for (int i = threadIdx.x; i < n; i += kMergeThreads) {
-        if (i < cnt) {
-            skey[i] = in_key[h * n_in + s0 + i];
-            sid[i] = in_id[h * n_in + s0 + i];
-        } else {
-            skey[i] = 0;
-            sid[i] = kNoId;
-        }
-    }
-    __syncthreads();
-    bitonic_best_first(skey, sid, n, n);
-    if (!ids_final) {
-        for (int i = threadIdx.x; i < k; i += kMergeThreads) {
-            const int64_t o = ((int64_t)h * gridDim.x + blockIdx.x) * k + i;
-            out_key[o] = skey[i];
-            out_id[o] = sid[i];
-        }
-        return;
-    }
-    // final: the k selected ids in ascending order, empty slots (kNoId) last as -1
-    const int m = pow2_at_least(k);
-    for (int i = threadIdx.x; i < m; i += kMergeThreads)
-        if (i >= k)
-            sid[i] = kNoId;
-    __syncthreads();
-    bitonic_ids_ascending(sid, m);
-    for (int i = threadIdx.x; i < k; i += kMergeThreads)
-        ids_final[h * k + i] = sid[i] == kNoId ? -1 : (int32_t)sid[i];
-}
-
 
 // ---------------------------------------------------------------------------------------------
 // wavefront path
@@ -336,6 +151,9 @@ __device__ __forceinline__ void wave_merge32(uint64_t &ck, uint32_t &ci, uint64_
 // grid.x = ceil(n_blocks / 64), kWaveThreads threads (a wave per head).  LDS: 64 padded rows
 // + queries as fp64.
 constexpr int kWaveThreads = 512;
+// kKeysOnly: write every row's rank key to cand_key[h][n_blocks] (ids implicit) instead of the
+// sorted best-k candidate lists -- the input of the selection path.
+template <bool kKeysOnly>
 __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
     const uint16_t *__restrict__ pooled, int64_t n_blocks, int dim,
     const uint16_t *__restrict__ q_idx, int n_sel, int k, uint64_t *__restrict__ cand_key,
@@ -388,6 +206,11 @@ __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
         uint32_t id = valid ? (uint32_t)(b0 + lane) : kNoId;
         if (scores_out && valid)
             scores_out[(int64_t)h * n_blocks + b0 + lane] = acc;
+        if (kKeysOnly) {
+            if (valid)
+                cand_key[(int64_t)h * n_blocks + b0 + lane] = key;
+            continue;
+        }
         wave_sort_best_first(key, id, lane);
         if (lane < k) {
             const int64_t o = ((int64_t)h * gridDim.x + blockIdx.x) * k + lane;
@@ -463,37 +286,180 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
     }
 }
 
-size_t score_lds_bytes(int dim, int n_sel)
+// ---------------------------------------------------------------------------------------------
+// selection path (32 < k <= 2048)
+// ---------------------------------------------------------------------------------------------
+// Every element is ranked by the composite (rank key, ~id): 96 bits, larger = better, unique, so
+// the top k are exactly the elements at or above the k-th largest composite T.  A workgroup
+// holds one segment of a head's list in registers (element i = e*1024 + thread), finds T by
+// bisection over the 96 bits -- each step counts the elements at or above a candidate with
+// ballots and one barrier, and stops early once the count is exactly k -- and writes the
+// elements >= T in element order.  Level 0 reads the rank keys of the scoring pass (ids =
+// positions, ascending); every level keeps its output in id order, so the last level's output
+// is the answer already sorted by id.  Empty slots (key 0, id kNoId) rank below every element.
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelSegE = 4;                         // intermediate levels: 4096 per segment
+constexpr int kSelFinalE = 8;                       // the last level: up to 8192 candidates
+
+// the workgroup's sum of one count per wave (one barrier; red is used by this call only)
+__device__ __forceinline__ int block_sum(int c, int *red, int wave, int lane)
 {
-    return (size_t)kChunkBlocks * (dim * 2 + 16) + (size_t)n_sel * dim * 4 +
-           (size_t)n_sel * kChunkBlocks * 12;
+    if (lane == 0)
+        red[wave] = c;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; w++)
+        tot += red[w];
+    return __builtin_amdgcn_readfirstlane(tot);
 }
 
-struct Plan {
-    int64_t n_wg;        // scoring workgroups
-    int kk;              // candidates each keeps per head
-    int64_t level0;      // candidates per head after scoring
-    int64_t buf_a, buf_b;  // entries per head of the two ping-pong candidate buffers
-};
-
-Plan make_plan(int64_t n_blocks, int k)
+// elements with key >= t (the composite test for a candidate whose id part is 0)
+template <int E>
+__device__ __forceinline__ int wave_count_key_ge(const uint64_t (&key)[E], uint64_t t)
 {
-    Plan p;
-    p.n_wg = (n_blocks + kChunkBlocks - 1) / kChunkBlocks;
-    p.kk = std::min(k, kChunkBlocks);
-    p.level0 = p.n_wg * p.kk;
-    p.buf_a = p.level0;
-    int64_t n = p.level0, b = 0;
-    bool to_b = true;
-    while (n > kMergeMax) {  // intermediate merge levels
-        const int64_t segs = (n + kMergeMax - 1) / kMergeMax;
-        n = segs * k;
-        if (to_b)
-            b = std::max(b, n);
-        to_b = !to_b;
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; e++)
+        c += __popcll(__ballot(key[e] >= t));
+    return c;
+}
+
+// elements with composite (key, lo) >= (tk, tl)
+template <int E>
+__device__ __forceinline__ int wave_count_ge(const uint64_t (&key)[E], const uint32_t (&lo)[E],
+                                             uint64_t tk, uint32_t tl)
+{
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; e++)
+        c += __popcll(__ballot(key[e] > tk || (key[e] == tk && lo[e] >= tl)));
+    return c;
+}
+
+// grid = (segments, n_sel).  in_id NULL: ids are the element positions.  Output: per segment
+// k slots (the selected elements in order, then empty slots), or with ids_final the head's k
+// ids, -1 for empty slots.
+template <int E>
+__global__ __launch_bounds__(kSelThreads) void select_level(
+    const uint64_t *__restrict__ in_key, const uint32_t *__restrict__ in_id, int64_t n_in, int k,
+    uint64_t *__restrict__ out_key, uint32_t *__restrict__ out_id, int32_t *__restrict__ ids_final)
+{
+    constexpr int kSlots = E * kSelWaves;   // (element slab, wave) counts, <= 128
+    __shared__ int red[2][kSelWaves];
+    __shared__ int off[kSlots + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = blockIdx.y;
+    const int64_t s0 = (int64_t)blockIdx.x * (E * kSelThreads);
+    const uint64_t *hk = in_key + (int64_t)h * n_in;
+    const uint32_t *hi = in_id ? in_id + (int64_t)h * n_in : nullptr;
+    uint64_t key[E];
+    uint32_t lo[E];
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        const int64_t i = s0 + e * kSelThreads + tid;
+        const bool in = i < n_in;
+        const int64_t ic = in ? i : 0;
+        const uint64_t kv = hk[ic];
+        const uint32_t id = hi ? hi[ic] : (uint32_t)ic;
+        key[e] = in ? kv : 0;
+        lo[e] = in ? ~id : 0;     // an empty slot (id kNoId) also ranks 0
     }
-    p.buf_b = b;
-    return p;
+    // T = the largest composite with count(>= T) >= k; stays 0 with fewer than k elements.
+    // The 64 key bits first: while the candidate's id part is 0, (key, lo) >= (c, 0) is just
+    // key >= c.  The id bits are needed only when the k-th and (k+1)-th keys are equal.
+    uint64_t tk = 0;
+    uint32_t tl = 0;
+    int it = 0;
+    bool done = false;
+    for (int bit = 63; bit >= 0; bit--, it++) {
+        const uint64_t ck = tk | (1ull << bit);
+        const int cnt = block_sum(wave_count_key_ge<E>(key, ck), red[it & 1], wave, lane);
+        if (cnt >= k) {
+            tk = ck;
+            if (cnt == k) {
+                done = true;
+                break;
+            }
+        }
+    }
+    if (!done) {
+        for (int bit = 31; bit >= 0; bit--, it++) {
+            const uint32_t cl = tl | (1u << bit);
+            const int cnt = block_sum(wave_count_ge<E>(key, lo, tk, cl), red[it & 1], wave, lane);
+            if (cnt >= k) {
+                tl = cl;
+                if (cnt == k)
+                    break;
+            }
+        }
+    }
+    // selected: composite >= T, and not an empty slot (composite 0)
+    bool sel[E];
+    uint64_t bal[E];
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        sel[e] = (key[e] > tk || (key[e] == tk && lo[e] >= tl)) && (key[e] | lo[e]) != 0;
+        bal[e] = __ballot(sel[e]);
+        if (lane == 0)
+            off[e * kSelWaves + wave] = __popcll(bal[e]);
+    }
+    __syncthreads();
+    // exclusive offsets in element order (slab e major, then wave), and the total at off[kSlots]
+    if (wave == 0) {
+        const int c0 = lane < kSlots ? off[lane] : 0;
+        const int c1 = lane + 64 < kSlots ? off[lane + 64] : 0;
+        int s_0 = c0, s_1 = c1;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t0 = __shfl_up(s_0, d, 64), t1 = __shfl_up(s_1, d, 64);
+            if (lane >= d) {
+                s_0 += t0;
+                s_1 += t1;
+            }
+        }
+        const int tot0 = __shfl(s_0, 63, 64), tot1 = __shfl(s_1, 63, 64);
+        if (lane < kSlots)
+            off[lane] = s_0 - c0;
+        if (lane + 64 < kSlots)
+            off[lane + 64] = tot0 + s_1 - c1;
+        if (lane == 0)
+            off[kSlots] = tot0 + tot1;
+    }
+    __syncthreads();
+    const int total = off[kSlots];
+    const int64_t o_base = ids_final ? (int64_t)h * k : ((int64_t)h * gridDim.x + blockIdx.x) * k;
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        if (sel[e]) {
+            const int pos = off[e * kSelWaves + wave] +
+                            (int)__builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(bal[e] >> 32),
+                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal[e], 0u));
+            const uint32_t id = ~lo[e];
+            if (ids_final) {
+                ids_final[o_base + pos] = (int32_t)id;
+            } else {
+                out_key[o_base + pos] = key[e];
+                out_id[o_base + pos] = id;
+            }
+        }
+    }
+    for (int pos = total + tid; pos < k; pos += kSelThreads) {
+        if (ids_final) {
+            ids_final[o_base + pos] = -1;
+        } else {
+            out_key[o_base + pos] = 0;
+            out_id[o_base + pos] = kNoId;
+        }
+    }
+}
+
+// Candidate entries per head after each selection level, for n input elements.
+inline int64_t sel_level_out(int64_t n, int k)
+{
+    return (n + kSelSegE * kSelThreads - 1) / (kSelSegE * kSelThreads) * k;
 }
 
 }  // namespace
@@ -506,10 +472,13 @@ extern "C" size_t kvt_index_topk_ws_bytes(int64_t n_blocks, int32_t n_sel, int32
         const size_t c = (size_t)n_sel * (size_t)std::max<int64_t>((n_blocks + kWaveRows - 1) / kWaveRows, 1) * k;
         return round_up(c * 8, 256) + round_up(c * 4, 256) + 256;
     }
-    const Plan p = make_plan(std::max<int64_t>(n_blocks, 1), k);
-    const size_t a = (size_t)n_sel * p.buf_a, b = (size_t)n_sel * p.buf_b;
-    return round_up(a * 8, 256) + round_up(a * 4, 256) + round_up(b * 8, 256) +
-           round_up(b * 4, 256) + 256;
+    // rank keys of every block, then two ping-pong candidate buffers (key + id)
+    const size_t keys = (size_t)n_sel * (size_t)std::max<int64_t>(n_blocks, 1);
+    const int64_t a = n_blocks > kSelFinalE * kSelThreads ? sel_level_out(n_blocks, k) : 0;
+    const int64_t b = a > kSelFinalE * kSelThreads ? sel_level_out(a, k) : 0;
+    const size_t ca = (size_t)n_sel * (size_t)a, cb = (size_t)n_sel * (size_t)b;
+    return round_up(keys * 8, 256) + round_up(ca * 8, 256) + round_up(ca * 4, 256) +
+           round_up(cb * 8, 256) + round_up(cb * 4, 256) + 256;
 }
 
 // S3+S4: QSA-KVO pooled-plane scoring and top-k block selection.
@@ -518,7 +487,7 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
                               double *scores, void *ws, size_t ws_bytes, void *stream)
 {
     if (n_blocks < 0 || n_blocks > 0x7fffffffll || dim < 8 || dim > 256 || dim % 8 ||
-        n_sel < 1 || n_sel > 32 || k < 1 || k > kMergeMax / 2)
+        n_sel < 1 || n_sel > 32 || k < 1 || k > 2048)
         return kvt::fail(KVT_EINVAL,
                          "kvt_index_topk: n_blocks=%lld dim=%d n_sel=%d k=%d outside limits",
                          (long long)n_blocks, dim, n_sel, k);
@@ -539,7 +508,7 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
         uint32_t *ci = reinterpret_cast<uint32_t *>(w + round_up(c * 8, 256));
         if (n_wg > 0) {
             const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)n_sel * dim * 8;
-            hipLaunchKernelGGL(score_wave_topk, dim3((unsigned)n_wg), dim3(kWaveThreads), lds, s,
+            hipLaunchKernelGGL(score_wave_topk<false>, dim3((unsigned)n_wg), dim3(kWaveThreads), lds, s,
                                static_cast<const uint16_t *>(pooled), n_blocks, dim,
                                static_cast<const uint16_t *>(q_idx), n_sel, k, ck, ci, scores);
             KVT_LAUNCHED("score_wave_topk");
@@ -549,52 +518,45 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
         KVT_LAUNCHED("merge_wave_topk");
         return KVT_OK;
     }
-    const Plan p = make_plan(std::max<int64_t>(n_blocks, 1), k);
-
-    // carve the workspace (256-byte aligned pieces)
+    // selection path: every rank key, then exact selection levels
     uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
-    const size_t a = (size_t)n_sel * p.buf_a, b = (size_t)n_sel * p.buf_b;
-    uint64_t *a_key = reinterpret_cast<uint64_t *>(w); w += round_up(a * 8, 256);
-    uint32_t *a_id = reinterpret_cast<uint32_t *>(w); w += round_up(a * 4, 256);
-    uint64_t *b_key = reinterpret_cast<uint64_t *>(w); w += round_up(b * 8, 256);
+    const size_t keys = (size_t)n_sel * (size_t)std::max<int64_t>(n_blocks, 1);
+    const int64_t na = n_blocks > kSelFinalE * kSelThreads ? sel_level_out(n_blocks, k) : 0;
+    const int64_t nb = na > kSelFinalE * kSelThreads ? sel_level_out(na, k) : 0;
+    uint64_t *all_key = reinterpret_cast<uint64_t *>(w); w += round_up(keys * 8, 256);
+    uint64_t *a_key = reinterpret_cast<uint64_t *>(w); w += round_up((size_t)n_sel * na * 8, 256);
+    uint32_t *a_id = reinterpret_cast<uint32_t *>(w); w += round_up((size_t)n_sel * na * 4, 256);
+    uint64_t *b_key = reinterpret_cast<uint64_t *>(w); w += round_up((size_t)n_sel * nb * 8, 256);
     uint32_t *b_id = reinterpret_cast<uint32_t *>(w);
-
-    if (n_blocks == 0) {
-        // nothing to rank: every slot is empty.  One merge over a single empty segment.
-        hipLaunchKernelGGL(merge_topk, dim3(1, n_sel), dim3(kMergeThreads), 0, s, a_key, a_id,
-                           (int64_t)0, k, nullptr, nullptr, ids);
-        KVT_LAUNCHED("merge_topk");
-        return KVT_OK;
+    if (n_blocks > 0) {
+        const int64_t n_wg = (n_blocks + kWaveRows - 1) / kWaveRows;
+        const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)n_sel * dim * 8;
+        hipLaunchKernelGGL(score_wave_topk<true>, dim3((unsigned)n_wg), dim3(kWaveThreads), lds, s,
+                           static_cast<const uint16_t *>(pooled), n_blocks, dim,
+                           static_cast<const uint16_t *>(q_idx), n_sel, k, all_key, nullptr,
+                           scores);
+        KVT_LAUNCHED("score_wave_topk");
     }
-    const size_t lds = score_lds_bytes(dim, n_sel);
-    if (lds > 160 * 1024)
-        return kvt::fail(KVT_EINVAL, "kvt_index_topk: dim=%d n_sel=%d need %zu bytes of LDS",
-                         dim, n_sel, lds);
-    hipLaunchKernelGGL(score_local_topk, dim3((unsigned)p.n_wg), dim3(kThreads), lds, s,
-                       static_cast<const uint16_t *>(pooled), n_blocks, dim,
-                       static_cast<const uint16_t *>(q_idx), n_sel, p.kk, a_key, a_id, scores);
-    KVT_LAUNCHED("score_local_topk");
-
-    int64_t n = p.level0;
-    bool in_a = true;
-    while (true) {
-        const int64_t segs = (n + kMergeMax - 1) / kMergeMax;
-        const uint64_t *ik = in_a ? a_key : b_key;
-        const uint32_t *ii = in_a ? a_id : b_id;
-        if (segs == 1) {
-            hipLaunchKernelGGL(merge_topk, dim3(1, n_sel), dim3(kMergeThreads), 0, s, ik, ii, n,
-                               k, nullptr, nullptr, ids);
-            KVT_LAUNCHED("merge_topk");
-            return KVT_OK;
-        }
-        uint64_t *ok = in_a ? b_key : a_key;
-        uint32_t *oi = in_a ? b_id : a_id;
-        hipLaunchKernelGGL(merge_topk, dim3((unsigned)segs, n_sel), dim3(kMergeThreads), 0, s,
-                           ik, ii, n, k, ok, oi, nullptr);
-        KVT_LAUNCHED("merge_topk");
+    const uint64_t *in_key = all_key;
+    const uint32_t *in_id = nullptr;
+    int64_t n = n_blocks;
+    bool to_a = true;
+    while (n > kSelFinalE * kSelThreads) {
+        const int64_t segs = (n + kSelSegE * kSelThreads - 1) / (kSelSegE * kSelThreads);
+        uint64_t *ok = to_a ? a_key : b_key;
+        uint32_t *oi = to_a ? a_id : b_id;
+        hipLaunchKernelGGL(select_level<kSelSegE>, dim3((unsigned)segs, n_sel), dim3(kSelThreads),
+                           0, s, in_key, in_id, n, k, ok, oi, nullptr);
+        KVT_LAUNCHED("select_level");
+        in_key = ok;
+        in_id = oi;
         n = segs * k;
-        in_a = !in_a;
+        to_a = !to_a;
     }
+    hipLaunchKernelGGL(select_level<kSelFinalE>, dim3(1, n_sel), dim3(kSelThreads), 0, s, in_key,
+                       in_id, n, k, nullptr, nullptr, ids);
+    KVT_LAUNCHED("select_level");
+    return KVT_OK;
 }
 
 namespace {

@@ -63,6 +63,28 @@ def test_index_topk_ties_nans_and_duplicates(gpu):
     assert ids[6].tolist() == list(range(32))
 
 
+@pytest.mark.parametrize("k", [100, 700])
+def test_index_topk_selection_path_ties_nans_and_small_inputs(gpu, k):
+    """k > 32 (the selection path): exact ties, NaN scores, signed zeros; fewer blocks than k;
+    no blocks at all."""
+    g = synth.rng(4, synth.P_MISC, 60 + k)
+    n_blocks = 9000
+    pooled = synth.f16_normal(g, (n_blocks, 128))
+    pooled[1000:1900] = pooled[7]                    # 901 identical keys -> exact score ties
+    pooled[2000:2010, 3] = 0x7E00                    # NaN scores
+    q_idx = synth.f16_normal(g, (8, 128))
+    q_idx[5] = 0                                     # every score 0 for head 5
+    q_idx[6] = 0x8000                                # -0.0
+    ids, scores = _run_topk(pooled, q_idx, k, gpu)
+    ref = oracle.index_scores(pooled, q_idx)
+    assert np.array_equal(ids, oracle.topk(ref, k))
+    assert ids[5].tolist() == list(range(k))
+    for nb in (0, 7, k - 1, k):
+        pl = pooled[:nb] if nb else np.zeros((0, 128), np.uint16)
+        ids, _ = _run_topk(pl, q_idx, k, gpu, want_scores=False)
+        assert np.array_equal(ids, oracle.topk(oracle.index_scores(pl, q_idx), k)), nb
+
+
 def test_index_topk_empty_and_oversized_k(gpu):
     ids, _ = _run_topk(np.zeros((0, 128), np.uint16), np.zeros((8, 128), np.uint16), 16, gpu,
                        want_scores=False)
