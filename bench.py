@@ -44,7 +44,7 @@ def parse():
                    help="host K/V plane layout (block-local head-major, or token-major)")
     p.add_argument("--suite", nargs="?", const="all", default=None,
                    help="also measure the other workloads: all, or a comma list of "
-                        "prefill, swap1, small, swap32, qsa, decode1m")
+                        "prefill, swap1, small, swap32, qsa, decode1m, worker")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the CPU-oracle baseline's wall time")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -722,9 +722,128 @@ def suite_qsa(torch, kvt, synth, dev, wl, args, reps=None):
     return res
 
 
+def suite_worker(torch, kvt, synth, dev, wl, peaks, jobs=16, pages_per_job=4096):
+    """The transfer worker: `jobs` jobs of 4096 random 32 KiB pages (128 MiB, the 32-layer
+    geometry's 64 tensors x 64 blocks) loaded host -> HBM through one worker; the same tables
+    as one direct kvt_swap_blocks call; a load worker and a store worker running at once (both
+    link directions); and the decode step replayed from HIP graphs against eager launches.
+    Payload bytes are the zero fill of fresh pinned/HBM memory (a copy's rate does not depend
+    on the bytes it moves)."""
+    import numpy as np
+    page = 32768
+    n_pages = jobs * pages_per_job
+    hosts = [kvt.HostBuffer(n_pages * page) for _ in range(2)]
+    hbm = torch.zeros((2, n_pages, page), dtype=torch.uint8, device=dev)
+    tabs = []
+    for side in range(2):   # side 0: loads host[0] -> hbm[0]; side 1: stores hbm[1] -> host[1]
+        perm_h = synth.permutation(synth.rng(11, synth.P_PERM_SRC, side), n_pages)
+        perm_g = synth.permutation(synth.rng(11, synth.P_PERM_DST, side), n_pages)
+        hs = np.empty(n_pages, np.uint64)
+        gs = np.empty(n_pages, np.uint64)
+        kvt.kvt_sub_block_ptrs(hosts[side].dev, page, page, perm_h, n_pages, 1, 0, hs, n_pages)
+        kvt.kvt_sub_block_ptrs(hbm[side].data_ptr(), page, page, perm_g, n_pages, 1, 0, gs,
+                               n_pages)
+        tabs.append((hs, gs) if side == 0 else (gs, hs))
+    sizes = np.full(n_pages, page, np.uint64)
+    job_bytes = pages_per_job * page
+    out = {"job_bytes": job_bytes, "jobs": jobs}
+
+    def run_jobs(workers, reps=3):
+        """Submit every job to each worker (one direction each); host-clock GB/s over all."""
+        best = None
+        for r in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            sub = 0.0
+            for j in range(jobs):
+                for side, w in workers:
+                    a, b = tabs[side]
+                    lo, hi = j * pages_per_job, (j + 1) * pages_per_job
+                    ts = time.perf_counter()
+                    kvt.kvt_worker_submit(w, r * jobs + j, a[lo:hi], b[lo:hi], sizes[lo:hi],
+                                          pages_per_job)
+                    sub += time.perf_counter() - ts
+            for side, w in workers:
+                kvt.kvt_worker_wait(w, r * jobs + jobs - 1)
+            wall = time.perf_counter() - t0
+            per_job = []
+            for side, w in workers:
+                done = kvt.kvt_worker_get_finished(w, jobs)
+                assert [d[0] for d in done] == [r * jobs + j for j in range(jobs)]
+                per_job += [d[1] / d[2] / GB for d in done]
+            res = {"gbs": len(workers) * jobs * job_bytes / wall / GB,
+                   "job_event_gbs_median": _median(per_job),
+                   "submit_us_per_job": sub / (jobs * len(workers)) * 1e6}
+            if best is None or res["gbs"] > best["gbs"]:
+                best = res
+        return {k: round(v, 2) for k, v in best.items()}
+
+    for mode, mname in ((kvt.COPY_SDMA, "sdma"), (kvt.COPY_KERNEL, "kernel")):
+        wl_ = kvt.kvt_worker_create(kvt.H2D, mode)
+        ws_ = kvt.kvt_worker_create(kvt.D2H, mode)
+        kvt.kvt_worker_reserve(wl_, jobs, pages_per_job)
+        kvt.kvt_worker_reserve(ws_, jobs, pages_per_job)
+        run_jobs([(0, wl_)], reps=1)   # warm-up
+        out[f"load_{mname}"] = run_jobs([(0, wl_)])
+        out[f"load_store_{mname}"] = run_jobs([(0, wl_), (1, ws_)])
+        kvt.kvt_worker_destroy(wl_)
+        kvt.kvt_worker_destroy(ws_)
+        # the same tables as one direct call on the current stream
+        tb = kvt.HostBuffer(3 * 8 * n_pages)
+        tab = tb.numpy(np.uint64, (3, n_pages))
+        tab[0], tab[1], tab[2] = tabs[0][0], tabs[0][1], sizes
+        t = Timer(torch, torch.cuda.current_stream())
+        rates = [_swap_rate(torch, kvt, t, tab, n_pages, kvt.H2D, mode, n_pages * page)[0]
+                 for _ in range(3)]
+        out[f"direct_load_{mname}_gbs"] = round(max(rates), 2)
+        del tab
+        tb.free()
+    log("worker", out)
+    del hbm
+    for h in hosts:
+        h.free()
+    torch.cuda.empty_cache()
+
+    # the decode step from HIP graphs: one graph per query set, replayed in turn
+    n_sets, steps = 8, 200
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n_sets):
+            wl.step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(n_sets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            wl.step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        for i in range(n_sets):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i % n_sets)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    eager = min(timed(wl.step) for _ in range(3))
+    graph = min(timed(lambda i: graphs[i].replay()) for _ in range(3))
+    out["decode_step_eager_ms"] = round(eager, 5)
+    out["decode_step_graph_ms"] = round(graph, 5)
+    del graphs
+    torch.cuda.synchronize()
+    log("decode graph", {"eager_ms": eager, "graph_ms": graph})
+    return out
+
+
 def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     want = set(args.suite.split(",")) if args.suite != "all" else {
-        "prefill", "swap1", "small", "swap32", "qsa", "decode1m"}
+        "prefill", "swap1", "small", "swap32", "qsa", "decode1m", "worker"}
     out = {}
     if "prefill" in want:
         log("suite: tiered prefill")
@@ -741,6 +860,9 @@ def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     if "qsa" in want:
         log("suite: QSA selection geometry")
         out["qsa_geometry"] = suite_qsa(torch, kvt, synth, dev, wl, args)
+    if "worker" in want:
+        log("suite: transfer worker and graph replay")
+        out["worker"] = suite_worker(torch, kvt, synth, dev, wl, peaks)
     if "decode1m" in want:
         log("suite: decode at 1,048,576")
         w1m = DecodeWorkload(torch, kvt, synth, dev, 1 << 20, args.warmup + 2 * args.steps)

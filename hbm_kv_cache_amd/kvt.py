@@ -55,6 +55,13 @@ _SIGNATURES = {
     "kvt_attn_prefill_pipelined": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P,
                                            _P, c_int64, _P, _P, c_int64, c_int32, c_int32,
                                            c_float, _P, _P, c_int64, _P, c_size_t, _P, _P, _P]),
+    "kvt_worker_create": (c_int, [c_int32, c_int32, ctypes.POINTER(c_void_p)]),
+    "kvt_worker_reserve": (c_int, [_P, c_int32, c_int64]),
+    "kvt_worker_submit": (c_int, [_P, c_int64, _P, _P, _P, c_int64, _P]),
+    "kvt_worker_get_finished": (c_int, [_P, _P, _P, _P, c_int32, ctypes.POINTER(c_int32)]),
+    "kvt_worker_wait": (c_int, [_P, _P, c_int32]),
+    "kvt_worker_pending": (c_int, [_P]),
+    "kvt_worker_destroy": (c_int, [_P]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -265,3 +272,50 @@ def kvt_attn_prefill_pipelined(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_
         int(n_head), _ptr(k_host), _ptr(v_host), int(n_kv), int(kv_format), int(bool(causal)),
         float(scale), _ptr(arena_k), _ptr(arena_v), int(arena_rows), _ptr(state),
         int(state_bytes), _ptr(out), _stream(stream), _stream(copy_stream)))
+
+
+def kvt_worker_create(direction, mode=COPY_AUTO) -> int:
+    """Returns the worker handle (an int address)."""
+    h = c_void_p()
+    _check("kvt_worker_create", load().kvt_worker_create(int(direction), int(mode),
+                                                         ctypes.byref(h)))
+    return h.value
+
+
+def kvt_worker_reserve(w, jobs, entries) -> None:
+    _check("kvt_worker_reserve", load().kvt_worker_reserve(w, int(jobs), int(entries)))
+
+
+def kvt_worker_submit(w, job_id, src, dst, sizes, n, compute_stream=None) -> None:
+    """src/dst/sizes: u64 tables in host memory (numpy arrays or addresses); copied at submit."""
+    _check("kvt_worker_submit", load().kvt_worker_submit(
+        w, int(job_id), _ptr(src), _ptr(dst), _ptr(sizes), int(n), _stream(compute_stream)))
+
+
+def kvt_worker_get_finished(w, max_jobs=256):
+    """Returns [(job_id, bytes, seconds), ...] for finished jobs, oldest first."""
+    ids = (c_int64 * max(1, int(max_jobs)))()
+    nb = (c_uint64 * max(1, int(max_jobs)))()
+    secs = (c_double * max(1, int(max_jobs)))()
+    n = c_int32()
+    _check("kvt_worker_get_finished", load().kvt_worker_get_finished(
+        w, ids, nb, secs, int(max_jobs), ctypes.byref(n)))
+    return [(ids[i], nb[i], secs[i]) for i in range(n.value)]
+
+
+def kvt_worker_wait(w, job_ids) -> None:
+    """job_ids: one id or an iterable of ids."""
+    ids = [int(j) for j in job_ids] if hasattr(job_ids, "__iter__") else [int(job_ids)]
+    arr = (c_int64 * max(1, len(ids)))(*ids)
+    _check("kvt_worker_wait", load().kvt_worker_wait(w, arr, len(ids)))
+
+
+def kvt_worker_pending(w) -> int:
+    rc = load().kvt_worker_pending(w)
+    if rc < 0:
+        _check("kvt_worker_pending", rc)
+    return rc
+
+
+def kvt_worker_destroy(w) -> None:
+    _check("kvt_worker_destroy", load().kvt_worker_destroy(w))

@@ -15,6 +15,7 @@
  *   kvt_attn_prefill     causal (or full) prefill attention over an HBM head + tail
  *   kvt_attn_prefill_range      the same attention as resumable passes over key ranges
  *   kvt_attn_prefill_pipelined  tail staging in arena buckets overlapped with the attention
+ *   kvt_worker_*         an ordered, event-timed asynchronous transfer queue around the swap
  *
  * Sources (page titles; each entry point names the section it follows):
  *   [vLLM-CPU] vLLM fork, "v1/kv_offload/cpu/gpu_worker.py" (CPU offloading worker)
@@ -24,6 +25,8 @@
  * Conventions (all entry points):
  *   - The caller owns every buffer.  The library allocates nothing on the hot path; where an
  *     op needs scratch, the caller passes a workspace sized by the matching *_ws_bytes call.
+ *     (The transfer worker is the exception: it owns pools of streams, events and pinned
+ *     descriptor tables, which grow on first need or up front through kvt_worker_reserve.)
  *   - "device pointer" = an address a gfx950 kernel may dereference: HBM from hipMalloc /
  *     torch, or pinned host memory from kvt_host_alloc (its device alias).  "host-mapped"
  *     planes are such device aliases of pinned host memory; kernels read them over PCIe.
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 4
+#define KVT_ABI_VERSION 5
 
 /* status codes */
 #define KVT_OK 0
@@ -306,6 +309,45 @@ int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_pos0, int32
                                int64_t n_kv, int32_t kv_format, int32_t causal, float scale,
                                void *arena_k, void *arena_v, int64_t arena_rows, void *state,
                                size_t state_bytes, float *out, void *stream, void *copy_stream);
+
+/* ----------------------------------------------------------------------------------------
+ * Transfer worker.  [vLLM-CPU] SingleDirectionOffloadingHandler: transfer_async,
+ * get_finished, wait, shutdown.  One worker per direction (KVT_H2D loads, KVT_D2H stores)
+ * keeps the transfers submitted to it in order:
+ *   - kvt_worker_submit copies the caller's src/dst/sizes tables (host memory, any kind) into
+ *     a pooled pinned buffer, so the caller may reuse its tables as soon as it returns; takes
+ *     a stream and two timing events from the worker's pools; makes that stream wait for all
+ *     work enqueued so far on `compute_stream` (NULL = legacy default stream) and for the end
+ *     of the previous transfer of this worker; then enqueues start event, kvt_swap_blocks
+ *     (mode from create; same table rules) and end event.  job_id is the caller's tag and
+ *     must not match a job still pending in this worker (KVT_EINVAL).  n == 0 is allowed
+ *     (an ordering-only job of 0 bytes).
+ *   - kvt_worker_get_finished reports, oldest first, up to `max` jobs whose end event has
+ *     passed, stopping at the first one still running (completion is reported in submission
+ *     order): job_ids[i], bytes[i] (sum of its sizes) and seconds[i] (start->end event time).
+ *     bytes / seconds may be NULL.  A reported job's stream, events and buffer return to the
+ *     pools.  *n_out receives the count.
+ *   - kvt_worker_wait blocks the calling thread until the transfers of job_ids[0..n) have
+ *     finished; ids that are unknown or already reported are skipped.  It reports nothing.
+ *   - kvt_worker_pending returns how many jobs are submitted and not yet reported (or < 0).
+ *   - kvt_worker_reserve grows the pools to hold `jobs` transfers in flight whose tables have
+ *     up to `entries` rows each, so later submits within that allocate nothing.
+ *   - kvt_worker_destroy (shutdown) waits for the pending jobs in order, releases the pools
+ *     and frees the worker.  If a wait fails, the later jobs are not waited for and that
+ *     error is returned (the worker is freed all the same).
+ * A worker belongs to the device current at create; its calls are thread-safe.  Errors:
+ * KVT_EINVAL (arguments), KVT_ENOMEM (pinned allocation), KVT_EHIP, or kvt_swap_blocks's own.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct kvt_worker kvt_worker;
+int kvt_worker_create(int32_t dir, int32_t mode, kvt_worker **out);
+int kvt_worker_reserve(kvt_worker *w, int32_t jobs, int64_t entries);
+int kvt_worker_submit(kvt_worker *w, int64_t job_id, const uint64_t *src, const uint64_t *dst,
+                      const uint64_t *sizes, int64_t n, void *compute_stream);
+int kvt_worker_get_finished(kvt_worker *w, int64_t *job_ids, uint64_t *bytes, double *seconds,
+                            int32_t max, int32_t *n_out);
+int kvt_worker_wait(kvt_worker *w, const int64_t *job_ids, int32_t n);
+int kvt_worker_pending(kvt_worker *w);
+int kvt_worker_destroy(kvt_worker *w);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,7 @@
 """CPU-only checks of the C ABI: the library loads, exports every entry point include/kvt.h
 declares, and its host-side logic (pointer tables, argument validation) is right.  No call here
 reaches a device: every one either is pure host code or fails its argument check first."""
+import ctypes
 import os
 import re
 import subprocess
@@ -34,7 +35,7 @@ def test_header_declarations_all_exported():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 4
+    assert kvt.kvt_abi_version() == 5
 
 
 def test_library_has_gfx950_code_object():
@@ -143,3 +144,24 @@ def test_workspace_sizes_are_monotone_and_cover_candidates():
     assert 0 < a < b < c
     assert b >= 8 * (16384 // 128) * 32 * 12
     assert kvt.kvt_attn_decode_ws_bytes(64, 128, 2048) == 64 * 32 * 130 * 4
+
+
+def test_worker_argument_errors_touch_no_device():
+    lib = kvt.load()
+    h = ctypes.c_void_p()
+    assert lib.kvt_worker_create(2, kvt.COPY_AUTO, ctypes.byref(h)) == kvt.EINVAL
+    assert lib.kvt_worker_create(kvt.H2D, 7, ctypes.byref(h)) == kvt.EINVAL
+    assert lib.kvt_worker_create(kvt.D2H, kvt.COPY_SDMA, None) == kvt.EINVAL
+    assert h.value is None
+    n = ctypes.c_int32(-1)
+    t = np.zeros(4, np.uint64)
+    assert lib.kvt_worker_submit(None, 1, t.ctypes.data, t.ctypes.data, t.ctypes.data, 4,
+                                 None) == kvt.EINVAL
+    assert lib.kvt_worker_get_finished(None, None, None, None, 0, ctypes.byref(n)) == kvt.EINVAL
+    assert lib.kvt_worker_wait(None, None, 0) == kvt.EINVAL
+    assert lib.kvt_worker_pending(None) == kvt.EINVAL
+    assert lib.kvt_worker_reserve(None, 1, 1) == kvt.EINVAL
+    assert lib.kvt_worker_destroy(None) == kvt.OK
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_worker_create(5)
+    assert e.value.code == kvt.EINVAL and "dir=5" in str(e.value)
