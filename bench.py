@@ -44,7 +44,7 @@ def parse():
                    help="host K/V plane layout (block-local head-major, or token-major)")
     p.add_argument("--suite", nargs="?", const="all", default=None,
                    help="also measure the other workloads: all, or a comma list of "
-                        "prefill, swap1, small, swap32, qsa, decode1m, worker")
+                        "prefill, swap1, small, swap32, qsa, decode1m, worker, upkeep")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the CPU-oracle baseline's wall time")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -841,9 +841,57 @@ def suite_worker(torch, kvt, synth, dev, wl, peaks, jobs=16, pages_per_job=4096)
     return out
 
 
+def suite_upkeep(torch, kvt, synth, dev, peaks, reps=20):
+    """The write side: a 2048-token prefill chunk appended to host pages (K and V rows of
+    8 heads x 128 bf16, raw keys of 128 fp16; 256-token pages at random page ids) and one
+    decode token appended, both through kvt_paged_write; then copy_page of a full page (host
+    memcpy of the three planes after draining the stream, pooled rows on the device)."""
+    import numpy as np
+    ps, n_pages, cr = 256, 1024, 4
+    rbs = [8 * 128 * 2, 8 * 128 * 2, 128 * 2]
+    bufs = [kvt.HostBuffer(n_pages * ps * rb) for rb in rbs]
+    pooled = torch.zeros((n_pages, ps // cr, 256), dtype=torch.uint8, device=dev)
+    pps = n_pages
+    table = torch.from_numpy(synth.permutation(synth.rng(13, synth.P_PERM_DST), n_pages)
+                             .astype(np.int32)[None]).to(dev)
+    out = {}
+    t = Timer(torch, torch.cuda.current_stream())
+    for seq, name in ((2048, "prefill_chunk_2048"), (1, "decode_token")):
+        src = [torch.randint(0, 256, (1, seq, rb), dtype=torch.uint8, device=dev) for rb in rbs]
+        times = []
+        for r in range(reps):
+            lens = torch.tensor([(r * 4099) % (n_pages * ps - seq)], dtype=torch.int32,
+                                device=dev)
+            t.start()
+            kvt.kvt_paged_write(src, [b.dev for b in bufs], rbs, 1, seq, lens, table, pps, ps,
+                                n_pages)
+            times.append(t.stop_ms())
+        ms = _median(times)
+        nbytes = seq * sum(rbs)
+        out[name] = {"bytes": nbytes, "us": round(ms * 1e3, 2),
+                     "gbs": round(nbytes / (ms * 1e-3) / GB, 2),
+                     "pct_measured_d2h": round(100 * nbytes / (ms * 1e-3) / GB /
+                                               peaks["d2h_sdma_gbs"], 1)}
+    host_ms = []
+    for r in range(reps):
+        t0 = time.perf_counter()
+        kvt.kvt_copy_page([b.host for b in bufs], [b.host for b in bufs], rbs, 2 * r, 2 * r + 1,
+                          ps, ps, pooled, pooled, 256, cr)
+        host_ms.append((time.perf_counter() - t0) * 1e3)
+    torch.cuda.synchronize()
+    page_bytes = ps * sum(rbs)
+    ms = _median(host_ms)
+    out["copy_page_full"] = {"host_bytes": page_bytes, "us": round(ms * 1e3, 2),
+                             "host_memcpy_gbs": round(page_bytes / (ms * 1e-3) / GB, 2)}
+    log("upkeep", out)
+    for b in bufs:
+        b.free()
+    return out
+
+
 def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     want = set(args.suite.split(",")) if args.suite != "all" else {
-        "prefill", "swap1", "small", "swap32", "qsa", "decode1m", "worker"}
+        "prefill", "swap1", "small", "swap32", "qsa", "decode1m", "worker", "upkeep"}
     out = {}
     if "prefill" in want:
         log("suite: tiered prefill")
@@ -863,6 +911,9 @@ def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     if "worker" in want:
         log("suite: transfer worker and graph replay")
         out["worker"] = suite_worker(torch, kvt, synth, dev, wl, peaks)
+    if "upkeep" in want:
+        log("suite: paged writes and copy_page")
+        out["upkeep"] = suite_upkeep(torch, kvt, synth, dev, peaks)
     if "decode1m" in want:
         log("suite: decode at 1,048,576")
         w1m = DecodeWorkload(torch, kvt, synth, dev, 1 << 20, args.warmup + 2 * args.steps)

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libkvt.so")
 ARCH = "gfx950"
 
 SOURCES = ["kvt_host.hip", "kvt_copy.hip", "kvt_topk.hip", "kvt_gather.hip", "kvt_decode.hip",
-           "kvt_prefill.hip", "kvt_worker.hip"]
+           "kvt_prefill.hip", "kvt_worker.hip", "kvt_paged.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE, "-I", CSRC]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

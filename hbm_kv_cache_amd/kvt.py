@@ -62,6 +62,10 @@ _SIGNATURES = {
     "kvt_worker_wait": (c_int, [_P, _P, c_int32]),
     "kvt_worker_pending": (c_int, [_P]),
     "kvt_worker_destroy": (c_int, [_P]),
+    "kvt_paged_write": (c_int, [_P, _P, _P, c_int32, c_int32, c_int32, _P, _P, c_int32, c_int32,
+                                c_int64, _P]),
+    "kvt_copy_page": (c_int, [_P, _P, _P, c_int32, c_int64, c_int64, c_int32, c_int32, _P, _P,
+                              c_int64, c_int32, _P]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -319,3 +323,30 @@ def kvt_worker_pending(w) -> int:
 
 def kvt_worker_destroy(w) -> None:
     _check("kvt_worker_destroy", load().kvt_worker_destroy(w))
+
+
+def _plane_arrays(srcs, dsts, row_bytes):
+    n = len(srcs)
+    if len(dsts) != n or len(row_bytes) != n:
+        raise ValueError("plane lists differ in length")
+    a = (c_void_p * max(1, n))(*[_ptr(x) for x in srcs])
+    b = (c_void_p * max(1, n))(*[_ptr(x) for x in dsts])
+    c = (c_int64 * max(1, n))(*[int(x) for x in row_bytes])
+    return a, b, c, n
+
+
+def kvt_paged_write(srcs, dsts, row_bytes, bsz, seq, cache_seqlens, block_table, pages_per_seq,
+                    page_size, n_pages, stream=None):
+    """srcs / dsts / row_bytes: per-plane lists (K, V, raw keys ...)."""
+    a, b, c, n = _plane_arrays(srcs, dsts, row_bytes)
+    _check("kvt_paged_write", load().kvt_paged_write(
+        a, b, c, n, int(bsz), int(seq), _ptr(cache_seqlens), _ptr(block_table),
+        int(pages_per_seq), int(page_size), int(n_pages), _stream(stream)))
+
+
+def kvt_copy_page(src_hosts, dst_hosts, row_bytes, from_page, to_page, page_size, num_tokens,
+                  src_pooled=None, dst_pooled=None, pooled_row_bytes=0, cr=1, stream=None):
+    a, b, c, n = _plane_arrays(src_hosts, dst_hosts, row_bytes)
+    _check("kvt_copy_page", load().kvt_copy_page(
+        a, b, c, n, int(from_page), int(to_page), int(page_size), int(num_tokens),
+        _ptr(src_pooled), _ptr(dst_pooled), int(pooled_row_bytes), int(cr), _stream(stream)))

@@ -16,6 +16,8 @@
  *   kvt_attn_prefill_range      the same attention as resumable passes over key ranges
  *   kvt_attn_prefill_pipelined  tail staging in arena buckets overlapped with the attention
  *   kvt_worker_*         an ordered, event-timed asynchronous transfer queue around the swap
+ *   kvt_paged_write      append new K/V (and raw key) rows into paged planes via a block table
+ *   kvt_copy_page        duplicate a page's first rows (host planes on the CPU, pooled on device)
  *
  * Sources (page titles; each entry point names the section it follows):
  *   [vLLM-CPU] vLLM fork, "v1/kv_offload/cpu/gpu_worker.py" (CPU offloading worker)
@@ -50,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 5
+#define KVT_ABI_VERSION 6
 
 /* status codes */
 #define KVT_OK 0
@@ -348,6 +350,44 @@ int kvt_worker_get_finished(kvt_worker *w, int64_t *job_ids, uint64_t *bytes, do
 int kvt_worker_wait(kvt_worker *w, const int64_t *job_ids, int32_t n);
 int kvt_worker_pending(kvt_worker *w);
 int kvt_worker_destroy(kvt_worker *w);
+
+/* ----------------------------------------------------------------------------------------
+ * Paged writes.  [QSA-KVO] CacheLayer_qsa_offload docstring: new tokens reach the host-
+ * resident K/V planes (and the indexer's raw key plane) through the paged cache update, which
+ * addresses them by base pointer plus offsets.  The update's source is not on the page; this
+ * is the plain paged-cache rule.  Each plane is dense pages [n_pages][page_size][row_bytes];
+ * token t of sequence b (position p = cache_seqlens[b] + t) goes to row p % page_size of page
+ * block_table[b*pages_per_seq + p / page_size]:
+ *   dst[i] + (page*page_size + p % page_size)*row_bytes[i]  <-  src[i] + (b*seq + t)*row_bytes[i]
+ *   src, dst, row_bytes: host arrays of n_planes (1..4) entries.  src[i]: device rows
+ *     [bsz][seq][row_bytes[i]] (HBM); dst[i]: device pointer of the plane (host-mapped or HBM).
+ *   cache_seqlens: device int32 [bsz] (the tokens each sequence holds before this write);
+ *   block_table: device int32 [bsz][pages_per_seq].
+ * Rows whose sequence length is negative, whose page slot is >= pages_per_seq or whose page
+ * id lies outside [0, n_pages) are skipped.  Two tokens must not map to the same row.
+ * row_bytes % 16 == 0, planes 16-byte aligned.  Errors: KVT_EINVAL, KVT_EALIGN, KVT_ERANGE.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_paged_write(const void *const *src, void *const *dst, const int64_t *row_bytes,
+                    int32_t n_planes, int32_t bsz, int32_t seq, const int32_t *cache_seqlens,
+                    const int32_t *block_table, int32_t pages_per_seq, int32_t page_size,
+                    int64_t n_pages, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * Page copy.  [QSA-KVO] CacheLayer_qsa_offload.copy_page: after draining `stream` (a page
+ * being read may still wait on a queued write, and one being written may still be under a
+ * read), the first num_tokens rows of page from_page of each host plane are copied to page
+ * to_page on the CPU (memmove), leaving the host link to the attention gather; then the
+ * page's first ceil(num_tokens / cr) pooled rows are copied on the device, enqueued on stream.
+ *   src_host, dst_host, row_bytes: host arrays of n_planes (0..4) entries; planes are dense
+ *     pages [n_pages][page_size][row_bytes[i]] given by their host addresses.
+ *   src_pooled, dst_pooled: device planes [n_pages][page_size/cr][pooled_row_bytes], or both
+ *     NULL to skip.  cr must divide page_size.
+ * Blocks the calling thread until the stream is idle; not for use under graph capture.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_copy_page(const void *const *src_host, void *const *dst_host, const int64_t *row_bytes,
+                  int32_t n_planes, int64_t from_page, int64_t to_page, int32_t page_size,
+                  int32_t num_tokens, const void *src_pooled, void *dst_pooled,
+                  int64_t pooled_row_bytes, int32_t cr, void *stream);
 
 #ifdef __cplusplus
 }

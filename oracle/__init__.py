@@ -15,6 +15,9 @@ Functions and the passages they follow:
 * ``stage_tail``       -- llama.cpp PR #319 commit text (used host rows copied to a VRAM buffer).
 * ``attn_decode``      -- QSA KV offload, staged attention (GQA map, softmax normalisation).
 * ``attn_prefill``     -- llama.cpp PR #319 (VRAM head + host tail, same output as all-device).
+* ``paged_write``      -- QSA KV offload, ``CacheLayer_qsa_offload`` docstring (new rows reach
+  the host pages through the paged cache update; the plain block-table rule).
+* ``copy_page``        -- QSA KV offload, ``CacheLayer_qsa_offload.copy_page``.
 
 Every function here has at least one pin in ``tests/test_oracle.py`` that does not restate its
 formula (library routines, closed forms, invariants, worked values).
@@ -250,6 +253,40 @@ def gather_attn_decode(q_u16, k_plane, v_plane, n_blocks, kvh, hd, fmt, strides,
                       vo.view(np.uint16).reshape(kvh, n_kv, hd), fmt, scale, n_valid=n_valid,
                       threads=threads)
     return out, ko, vo
+
+
+def paged_write(planes, new_rows, cache_seqlens, block_table, page_size):
+    """Append token rows to paged planes.  planes: list of uint8 arrays [n_pages][page_size][rb]
+    (modified in place); new_rows: matching list of uint8 arrays [bsz][seq][rb];
+    cache_seqlens: int [bsz]; block_table: int [bsz][pages_per_seq].  Token t of sequence b sits
+    at position cache_seqlens[b] + t of that sequence: logical page p // page_size, row
+    p % page_size.  Rows that fall outside the table or on an invalid page are dropped."""
+    table = np.asarray(block_table)
+    for plane, rows in zip(planes, new_rows):
+        n_pages = plane.shape[0]
+        bsz, seq = rows.shape[:2]
+        for b in range(bsz):
+            if cache_seqlens[b] < 0:
+                continue
+            for t in range(seq):
+                p = int(cache_seqlens[b]) + t
+                slot = p // page_size
+                if slot >= table.shape[1]:
+                    continue
+                page = int(table[b, slot])
+                if 0 <= page < n_pages:
+                    plane[page, p % page_size] = rows[b, t]
+
+
+def copy_page(src_planes, dst_planes, from_page, to_page, num_tokens, src_pooled=None,
+              dst_pooled=None, cr=1):
+    """The first num_tokens rows of page from_page of each plane -> page to_page; pooled planes
+    [n_pages][page_size/cr][..]: the first ceil(num_tokens / cr) rows likewise."""
+    for s_, d_ in zip(src_planes, dst_planes):
+        d_[to_page, :num_tokens] = s_[from_page, :num_tokens].copy()
+    if src_pooled is not None:
+        nb = -(-num_tokens // cr)
+        dst_pooled[to_page, :nb] = src_pooled[from_page, :nb].copy()
 
 
 def attn_prefill(q_u16, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, fmt, causal,

@@ -35,7 +35,7 @@ def test_header_declarations_all_exported():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 5
+    assert kvt.kvt_abi_version() == 6
 
 
 def test_library_has_gfx950_code_object():
@@ -165,3 +165,34 @@ def test_worker_argument_errors_touch_no_device():
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_worker_create(5)
     assert e.value.code == kvt.EINVAL and "dir=5" in str(e.value)
+
+
+def test_paged_write_and_copy_page_argument_errors():
+    a = np.zeros(64, np.uint8)
+    p = a.ctypes.data
+    lens = np.zeros(1, np.int32)
+    tab = np.zeros(4, np.int32)
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_paged_write([], [], [], 1, 1, lens, tab, 4, 16, 4, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_paged_write([p], [p], [24], 1, 1, lens, tab, 4, 16, 4, stream=0)
+    assert e.value.code == kvt.EALIGN
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_paged_write([p], [p], [32], 1, 1, None, tab, 4, 16, 4, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_paged_write([p], [p], [32], 1, 1, lens, tab, 0, 16, 4, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_paged_write([p] * 5, [p] * 5, [32] * 5, 1, 1, lens, tab, 4, 16, 4, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_copy_page([p], [p], [32], 0, 1, 16, 17, stream=0)     # more tokens than a page
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_copy_page([p], [p], [32], 0, 1, 16, 4, p, p, 16, 3, stream=0)   # 3 !| 16
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_copy_page([p], [p], [32], 0, 1, 16, 4, p, None, 16, 4, stream=0)
+    assert e.value.code == kvt.EINVAL

@@ -502,3 +502,45 @@ def test_prefill_single_query_reduces_to_decode():
     dec = oracle.attn_decode(q[0], kb[:p + 1].transpose(1, 0, 2), vb[:p + 1].transpose(1, 0, 2),
                              oracle.F16, 0.3)
     assert np.max(np.abs(pre[0] - dec)) < 1e-14
+
+
+def test_paged_write_worked_example():
+    """Row placement through the block table against a hand-worked example."""
+    g = json.load(open(os.path.join(GOLDEN, "paged_write_worked.json")))
+    ps, n_pages, seq = g["page_size"], g["n_pages"], g["seq"]
+    lens = g["cache_seqlens"]
+    bsz = len(lens)
+    plane = np.zeros((n_pages, ps, 1), np.uint8)
+    rows = np.array([[[10 * b + t + 1] for t in range(seq)] for b in range(bsz)], np.uint8)
+    oracle.paged_write([plane], [rows], lens, np.array(g["block_table"]), ps)
+    assert plane[:, :, 0].tolist() == g["expected_pages"]
+
+
+def test_paged_write_identity_table_is_contiguous_append():
+    """With page i of sequence b at table[b][i] = b*pps + i, a sequence's pages are one
+    contiguous array, and the write is a plain slice assignment at its length."""
+    g = synth.rng(0, synth.P_MISC, 60)
+    ps, pps, bsz, rb = 16, 5, 3, 8
+    plane = g.integers(0, 256, size=(bsz * pps, ps, rb), dtype=np.uint8)
+    lens = np.array([0, 17, 40])
+    seq = 23
+    rows = g.integers(0, 256, size=(bsz, seq, rb), dtype=np.uint8)
+    want = plane.reshape(bsz, pps * ps, rb).copy()
+    for b in range(bsz):
+        want[b, lens[b]:lens[b] + seq] = rows[b]
+    table = np.arange(bsz * pps).reshape(bsz, pps)
+    oracle.paged_write([plane], [rows], lens, table, ps)
+    assert np.array_equal(plane.reshape(bsz, pps * ps, rb), want)
+
+
+def test_copy_page_counts_and_untouched_rows():
+    """copy_page moves rows [0, n) of each plane and ceil(n / cr) pooled rows; the rest of
+    the target page and every other page stay as they were."""
+    g = synth.rng(0, synth.P_MISC, 61)
+    k = g.integers(0, 256, size=(4, 8, 6), dtype=np.uint8)
+    pooled = g.integers(0, 256, size=(4, 4, 3), dtype=np.uint8)      # cr = 2: 4 rows per page
+    k0, p0 = k.copy(), pooled.copy()
+    oracle.copy_page([k], [k], 1, 3, 5, pooled, pooled, cr=2)
+    assert np.array_equal(k[3, :5], k0[1, :5]) and np.array_equal(k[3, 5:], k0[3, 5:])
+    assert np.array_equal(pooled[3, :3], p0[1, :3]) and np.array_equal(pooled[3, 3:], p0[3, 3:])
+    assert np.array_equal(k[:3], k0[:3]) and np.array_equal(pooled[:3], p0[:3])
