@@ -44,7 +44,7 @@ def parse():
                    help="host K/V plane layout (block-local head-major, or token-major)")
     p.add_argument("--suite", nargs="?", const="all", default=None,
                    help="also measure the other workloads: all, or a comma list of "
-                        "prefill, swap1, small, swap32, qsa, decode1m, worker, upkeep")
+                        "prefill, swap1, small, swap32, qsa, decode1m, worker, upkeep, rows")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the CPU-oracle baseline's wall time")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -889,9 +889,97 @@ def suite_upkeep(torch, kvt, synth, dev, peaks, reps=20):
     return out
 
 
+def suite_rows(torch, kvt, synth, dev, wl, peaks, row_counts=(1, 16, 64, 128, 256, 512, 2048)):
+    """Sparse attention over per-row selections at 262,144 tokens: pages of 256 token rows
+    (8 KV heads x 128 bf16) in pinned host memory under a random block table, 64 query heads,
+    2080 positions per row (512 pooled blocks of 4 tokens + a 3-token tail, the QSA geometry).
+    For each row count: the direct path (every row reads its selection over the link), the
+    staged path (the 1024 used pages copied to HBM once, then the rows attend the copy), and
+    what the staging rule picks.  The planes are the decode workload's host planes, read as
+    [token][head][dim]."""
+    import numpy as np
+    ps, kvh, hd, n_qh, k_pad = 256, 8, 128, 64, 2080
+    ctx = wl.ctx
+    n_pages = ctx // ps
+    row = kvh * hd * 2
+    g = synth.rng(15, synth.P_PERM_DST)
+    table = torch.from_numpy(synth.permutation(g, n_pages).astype(np.int32)).to(dev)
+    r_max = max(row_counts)
+    gp = synth.rng(15, synth.P_MISC)
+    pos = np.full((r_max, k_pad), -1, np.int32)
+    n_pool = ctx // 4
+    for r in range(r_max):
+        blocks = np.sort(gp.choice(n_pool - 1, size=512, replace=False))
+        pos[r, :2048] = (blocks[:, None] * 4 + np.arange(4)).reshape(-1)
+        pos[r, 2048:2051] = ctx - 3 + np.arange(3)
+    pos_d = torch.from_numpy(pos).to(dev)
+    q = torch.randn((r_max, n_qh, hd), device=dev).to(torch.bfloat16).view(torch.int16)
+    out = torch.empty((r_max, n_qh, hd), dtype=torch.float32, device=dev)
+    ws_b = kvt.kvt_sparse_attend_rows_ws_bytes(r_max, n_qh, kvh, k_pad)
+    ws_b = max(ws_b, kvt.kvt_sparse_attend_rows_ws_bytes(1, n_qh, kvh, k_pad))
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    stage_bytes = n_pages * ps * row
+    sk = torch.empty(stage_bytes, dtype=torch.uint8, device=dev)
+    sv = torch.empty(stage_bytes, dtype=torch.uint8, device=dev)
+    kp, vp = wl.host.dev, wl.host.dev + ctx * row
+    t = Timer(torch, torch.cuda.current_stream())
+    res = {"k_pad": k_pad, "pages": n_pages, "page_size": ps, "rows": {}}
+
+    def direct(R):
+        kvt.kvt_sparse_attend_rows(q, R, n_qh, kvh, hd, kvt.BF16, kp, vp, ctx, row, hd * 2,
+                                   table, n_pages, 0, ps, pos_d, k_pad, 1 / math.sqrt(hd), out,
+                                   ws, ws_b)
+
+    def staged(R):
+        kvt.kvt_sparse_attend_rows_auto(q, R, n_qh, kvh, hd, kvt.BF16, kp, vp, ctx, row, hd * 2,
+                                        table, n_pages, ps, pos_d, k_pad, 1 / math.sqrt(hd), out,
+                                        ws, ws_b, sk, sv, stage_bytes)
+
+    for R in row_counts:
+        reps = 5 if R <= 256 else 2
+        d_ms, s_ms = [], []
+        for _ in range(reps):
+            t.start()
+            direct(R)
+            d_ms.append(t.stop_ms())
+        rule = kvt.kvt_staging_worthwhile(R, k_pad, n_pages, ps)
+        if rule:
+            for _ in range(reps):
+                t.start()
+                staged(R)
+                s_ms.append(t.stop_ms())
+        else:
+            # the rule says direct: time the staged form explicitly, stage then attend
+            for _ in range(reps):
+                t.start()
+                kvt.kvt_stage_pages(kp, vp, ps * row, table, n_pages, n_pages, sk, sv)
+                kvt.kvt_sparse_attend_rows(q, R, n_qh, kvh, hd, kvt.BF16, sk, sv, ctx, row,
+                                           hd * 2, None, 0, 0, 1, pos_d, k_pad,
+                                           1 / math.sqrt(hd), out, ws, ws_b)
+                s_ms.append(t.stop_ms())
+        d, st_ = _median(d_ms), _median(s_ms)
+        res["rows"][str(R)] = {"direct_ms": round(d, 4), "staged_ms": round(st_, 4),
+                               "rule_stages": bool(rule), "faster": "staged" if st_ < d else "direct",
+                               "direct_gbs": round(R * k_pad * row * 2 / (d * 1e-3) / GB, 2)}
+        log(f"rows {R}: direct {d:.3f} ms, staged {st_:.3f} ms, rule "
+            f"{'stage' if rule else 'direct'}")
+    # the staging copy alone
+    ms = []
+    for _ in range(3):
+        t.start()
+        kvt.kvt_stage_pages(kp, vp, ps * row, table, n_pages, n_pages, sk, sv)
+        ms.append(t.stop_ms())
+    res["stage_pages_ms"] = round(_median(ms), 3)
+    res["stage_pages_gbs"] = round(2 * stage_bytes / (_median(ms) * 1e-3) / GB, 2)
+    log("rows", res)
+    del sk, sv, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     want = set(args.suite.split(",")) if args.suite != "all" else {
-        "prefill", "swap1", "small", "swap32", "qsa", "decode1m", "worker", "upkeep"}
+        "prefill", "swap1", "small", "swap32", "qsa", "decode1m", "worker", "upkeep", "rows"}
     out = {}
     if "prefill" in want:
         log("suite: tiered prefill")
@@ -914,6 +1002,9 @@ def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     if "upkeep" in want:
         log("suite: paged writes and copy_page")
         out["upkeep"] = suite_upkeep(torch, kvt, synth, dev, peaks)
+    if "rows" in want:
+        log("suite: sparse attention over per-row selections")
+        out["sparse_rows"] = suite_rows(torch, kvt, synth, dev, wl, peaks)
     if "decode1m" in want:
         log("suite: decode at 1,048,576")
         w1m = DecodeWorkload(torch, kvt, synth, dev, 1 << 20, args.warmup + 2 * args.steps)

@@ -12,6 +12,7 @@
 //   the probabilities in fp32 avoids rounding them to 16 bits.
 // decode_merge: one thread per (query head, dim) folds the chunks in index order: the global
 //   max first, then every chunk rescaled by e^(m_c - max) -- the same fold, one rescale each.
+#include <algorithm>
 #include <cmath>
 
 #include "kvt_internal.h"
@@ -251,44 +252,54 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
     write_partial(st, group, part + ((int64_t)h * n_chunks + c) * group * (kHd + 2), lane);
 }
 
-// Gather and attend in one pass: the chunk's K/V rows are read straight from the (host-mapped)
-// planes of the selected blocks, optionally written to the HBM gather buffers, and attended.
-// Key j of head h (j < k*bt) is token j % bt of selected slot j / bt.  Each lane owns the
-// 16-byte word cw = lane % 16 of rows lane/16 + 4*jj (jj < 16): every group of 16 lanes reads
-// one contiguous 256-byte row slice, and all 32 loads of a lane are in flight together.
-template <bool kBf16>
-__global__ __launch_bounds__(64) void gather_decode_partial(
-    const uint16_t *__restrict__ q, int group, const unsigned char *__restrict__ kp,
-    const unsigned char *__restrict__ vp, int64_t n_blocks, int64_t block_stride,
-    int64_t head_stride, int64_t token_stride, const int32_t *__restrict__ table, int bt,
-    const int32_t *__restrict__ ids, int kk, uint16_t *__restrict__ k_out,
-    uint16_t *__restrict__ v_out, float scale_log2, float *__restrict__ part)
-{
-    __shared__ __align__(16) unsigned char ksm[kKeys * kKPitch];
-    __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
-    __shared__ __align__(16) float ps[16][16];
-    __shared__ __align__(16) float as[16];
-    const int lane = threadIdx.x;
-    const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x;
-    const int n_kv = kk * bt;   // < 2^31, checked by the host
-    const int key0 = c * kKeys;
-    const int rg = lane >> 4, cw = lane & 15;
-    const int32_t *hid = ids + (int64_t)h * kk;
-    const int64_t hoff = (int64_t)h * head_stride + cw * 16;
+// How a selected slot id becomes the byte offset of its block (token_stride apart rows).
+struct SlotMap {
+    const int32_t *table;   // NULL: slot id = block index
+    int64_t n_ids;          // ids lie in [0, n_ids)
+    int64_t n_phys;         // mapped blocks lie in [0, n_phys)
+    int64_t block_stride;
+    int table_page;         // slots per table entry
+    int table_cols;         // entries of the table (row)
+    int logical;            // nonzero: the table only validates; the block index stays the id
+};
 
-    // the query rows first: their loads must not queue behind the host reads
-    uint4 qa[4];
-    load_q(q, h, group, lane, qa);
-    // The chunk's keys span at most 64 slots: lane L resolves slot s0 + L (id, then table) to
-    // the byte offset of its block, or -1 when the slot takes no part.
-    const int s0 = (int)((uint32_t)key0 / (uint32_t)bt);
-    int64_t blk = hid[min(s0 + lane, kk - 1)];
-    bool sok = blk >= 0 && blk < n_blocks;
-    if (table) {
-        blk = table[sok ? blk : 0];
-        sok = sok && blk >= 0 && blk < n_blocks;
+// lane's slot id -> block byte offset, or -1 when the slot takes no part
+__device__ __forceinline__ int64_t slot_offset(int64_t id, const SlotMap &sm)
+{
+    bool ok = id >= 0 && id < sm.n_ids;
+    if (sm.table) {
+        const uint32_t u = ok ? (uint32_t)id : 0u;
+        const uint32_t pg = u / (uint32_t)sm.table_page;
+        ok = ok && (int)pg < sm.table_cols;
+        const int64_t phys = sm.table[ok ? pg : 0];
+        ok = ok && phys >= 0;
+        const int64_t blk = phys * sm.table_page + (int64_t)(u - pg * (uint32_t)sm.table_page);
+        ok = ok && blk < sm.n_phys;
+        if (!sm.logical)
+            id = blk;
     }
-    const int64_t sbase = sok ? blk * block_stride : -1;
+    return ok ? id * sm.block_stride : -1;
+}
+
+// Gather and attend one 64-key chunk: the chunk's K/V rows are read straight from the
+// (host-mapped) planes of the selected slots, optionally written to the HBM gather buffers,
+// and folded into st.  Key j (j < kk*bt) is token j % bt of selected slot j / bt.  Each lane
+// owns the 16-byte word cw = lane % 16 of rows lane/16 + 4*jj (jj < 16): every group of 16
+// lanes reads one contiguous 256-byte row slice.
+template <bool kBf16, bool kPaced>
+__device__ __forceinline__ void gather_chunk(
+    const unsigned char *__restrict__ kp, const unsigned char *__restrict__ vp,
+    const SlotMap &sm, int64_t hoff, int64_t token_stride, int bt,
+    const int32_t *__restrict__ hid, int kk, int key0, uint16_t *__restrict__ k_out,
+    uint16_t *__restrict__ v_out, int64_t out_key0, uint4 (&qa)[4], int group,
+    float scale_log2, unsigned char *ksm, unsigned char *vs, float (*ps)[16], float *as,
+    ChunkState &st, int lane)
+{
+    const int n_kv = kk * bt;   // < 2^31, checked by the host
+    const int rg = lane >> 4, cw = lane & 15;
+    // The chunk's keys span at most 64 slots: lane L resolves slot s0 + L.
+    const int s0 = (int)((uint32_t)key0 / (uint32_t)bt);
+    const int64_t sbase = slot_offset(hid[min(s0 + lane, kk - 1)], sm);
     // byte offsets of this lane's 16 rows (cw*16 -- always a valid address -- for keys that
     // take no part); bit jj of okb = row rg + 4*jj takes part
     int slot[16];
@@ -318,21 +329,31 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
         const uint64_t bal = __ballot((okb >> jj) & 1);
         valid |= ((bal & 1) | ((bal >> 15) & 2) | ((bal >> 30) & 4) | ((bal >> 45) & 8)) << (4 * jj);
     }
+    // query rows past the group are zero (here, not at their load: that would make the id and
+    // row loads above wait for the query loads)
     if ((lane & 15) >= group) {
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
             qa[ks] = make_uint4(0, 0, 0, 0);
     }
-    // The rows cross the link one K and one V wave-load at a time per wave: with every load of
-    // the step issued at once the link runs ~20% slower (see kvt_gather.hip).  Each pair goes
-    // to LDS -- K as read, V zeroed where the key takes no part -- and, when asked, to the
-    // HBM gather buffers in kvt_gather_blocks' layout (rows of skipped slots untouched).  The
-    // pair after a sub-tile's last is issued before that sub-tile is attended, so the
-    // attention runs while the link is busy.
-    ChunkState st;
-    state_init(st);
-    u32x4 kr = *reinterpret_cast<const u32x4 *>(kp + off[0]);
-    u32x4 vr = *reinterpret_cast<const u32x4 *>(vp + off[0]);
+    // Paced (planes across the host link): the rows cross the link one K and one V wave-load
+    // at a time per wave -- with every load of the step issued at once the link runs ~20%
+    // slower (see kvt_gather.hip) -- and the pair after a sub-tile's last is issued before
+    // that sub-tile is attended, so the attention runs while the link is busy.  Unpaced
+    // (planes in HBM): all 16 pairs are issued at once.  Each pair goes to LDS -- K as read, V
+    // zeroed where the key takes no part -- and, when asked, to the HBM gather buffers in
+    // kvt_gather_blocks' layout (rows of skipped slots untouched).
+    u32x4 kr[kPaced ? 1 : 16], vr[kPaced ? 1 : 16];
+    if constexpr (kPaced) {
+        kr[0] = *reinterpret_cast<const u32x4 *>(kp + off[0]);
+        vr[0] = *reinterpret_cast<const u32x4 *>(vp + off[0]);
+    } else {
+#pragma unroll
+        for (int jj = 0; jj < 16; jj++) {
+            kr[jj] = *reinterpret_cast<const u32x4 *>(kp + off[jj]);
+            vr[jj] = *reinterpret_cast<const u32x4 *>(vp + off[jj]);
+        }
+    }
 #pragma unroll
     for (int t = 0; t < 4; t++) {
 #pragma unroll
@@ -340,18 +361,21 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
             const int jj = 4 * t + u;
             const int row = rg + 4 * jj;
             const bool ok = (okb >> jj) & 1;
-            *reinterpret_cast<u32x4 *>(ksm + row * kKPitch + cw * 16) = kr;
+            const u32x4 kx = kr[kPaced ? 0 : jj], vx = vr[kPaced ? 0 : jj];
+            *reinterpret_cast<u32x4 *>(ksm + row * kKPitch + cw * 16) = kx;
             *reinterpret_cast<u32x4 *>(vs + row * kVPitch + cw * 16) =
-                ok ? vr : u32x4{0, 0, 0, 0};
+                ok ? vx : u32x4{0, 0, 0, 0};
             if (k_out && ok) {
-                const int64_t e = ((int64_t)h * n_kv + key0 + row) * kHd + cw * 8;
-                *reinterpret_cast<u32x4 *>(k_out + e) = kr;
-                *reinterpret_cast<u32x4 *>(v_out + e) = vr;
+                const int64_t e = (out_key0 + key0 + row) * kHd + cw * 8;
+                *reinterpret_cast<u32x4 *>(k_out + e) = kx;
+                *reinterpret_cast<u32x4 *>(v_out + e) = vx;
             }
-            __asm__ volatile("" ::: "memory");   // keep the next pair behind this one
-            if (jj + 1 < 16) {
-                kr = *reinterpret_cast<const u32x4 *>(kp + off[jj + 1]);
-                vr = *reinterpret_cast<const u32x4 *>(vp + off[jj + 1]);
+            if constexpr (kPaced) {
+                __asm__ volatile("" ::: "memory");   // keep the next pair behind this one
+                if (jj + 1 < 16) {
+                    kr[0] = *reinterpret_cast<const u32x4 *>(kp + off[jj + 1]);
+                    vr[0] = *reinterpret_cast<const u32x4 *>(vp + off[jj + 1]);
+                }
             }
         }
         __syncthreads();   // sub-tile t's K and V rows are in LDS
@@ -364,16 +388,69 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
                                                       16 * g);
         subtile_attend<kBf16>(t, qa, kb, valid, group, scale_log2, vs, ps, as, st, lane);
     }
-    write_partial(st, group, part + ((int64_t)h * n_chunks + c) * group * (kHd + 2), lane);
 }
 
-// grid = n_qh, block = kHd.  Two passes over the chunks (global max, then the weighted sums),
-// each with independent loads, in chunk order: deterministic.
+// grid = (splits, kvh, rows); split x of row z, KV head y folds chunks
+// [x*chunks_per_wg, min((x+1)*chunks_per_wg, n_chunks)) of that row's keys.
+//   q: [rows][kvh*group][kHd];  ids of (row, head): ids + row*ids_row_stride + h*ids_head_stride;
+//   table (row): sm.table + row*table_row_stride;  part: [rows][kvh][splits][group][kHd + 2].
+// kLoop false: one chunk per workgroup (chunks_per_wg == 1), straight-line code -- the decode
+// step, the only form that writes k_out/v_out.  kPaced: see gather_chunk.
+template <bool kBf16, bool kLoop, bool kPaced>
+__global__ __launch_bounds__(64) void gather_decode_partial(
+    const uint16_t *__restrict__ q, int group, const unsigned char *__restrict__ kp,
+    const unsigned char *__restrict__ vp, SlotMap sm, int64_t head_stride, int64_t token_stride,
+    int64_t table_row_stride, int bt, const int32_t *__restrict__ ids, int64_t ids_row_stride,
+    int ids_head_stride, int kk, int chunks_per_wg, uint16_t *__restrict__ k_out,
+    uint16_t *__restrict__ v_out, float scale_log2, float *__restrict__ part)
+{
+    __shared__ __align__(16) unsigned char ksm[kKeys * kKPitch];
+    __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
+    __shared__ __align__(16) float ps[16][16];
+    __shared__ __align__(16) float as[16];
+    const int lane = threadIdx.x;
+    const int x = blockIdx.x, h = blockIdx.y, row = blockIdx.z, n_split = gridDim.x;
+    const int kvh = gridDim.y;
+    const int n_chunks = (kk * bt + kKeys - 1) / kKeys;
+    const int cw = lane & 15;
+
+    // the query rows first: their loads must not queue behind the host reads
+    uint4 qa[4];
+    load_q(q + (int64_t)row * kvh * group * kHd, h, group, lane, qa);
+    const int32_t *hid = ids + (int64_t)row * ids_row_stride + (int64_t)h * ids_head_stride;
+    SlotMap rsm = sm;
+    if (rsm.table)
+        rsm.table += (int64_t)row * table_row_stride;
+    const int64_t hoff = (int64_t)h * head_stride + cw * 16;
+    ChunkState st;
+    state_init(st);
+    if constexpr (kLoop) {
+        const int c0 = x * chunks_per_wg, c1 = min(c0 + chunks_per_wg, n_chunks);
+        for (int c = c0; c < c1; c++) {
+            if (c != c0)
+                __syncthreads();   // the previous chunk's LDS rows are no longer read
+            gather_chunk<kBf16, kPaced>(kp, vp, rsm, hoff, token_stride, bt, hid, kk,
+                                        c * kKeys, nullptr, nullptr, 0, qa, group, scale_log2, ksm, vs, ps, as, st,
+                                lane);
+        }
+    } else {
+        gather_chunk<kBf16, kPaced>(kp, vp, rsm, hoff, token_stride, bt, hid, kk, x * kKeys, k_out,
+                            v_out, (int64_t)h * kk * bt, qa, group, scale_log2, ksm, vs, ps, as,
+                            st, lane);
+    }
+    write_partial(st, group,
+                  part + (((int64_t)row * kvh + h) * n_split + x) * group * (kHd + 2), lane);
+}
+
+// grid = (n_qh, rows), block = kHd.  Two passes over the chunks (global max, then the weighted
+// sums), each with independent loads, in chunk order: deterministic.
 __global__ __launch_bounds__(kHd) void decode_merge(const float *__restrict__ part, int group,
                                                     int n_chunks, float *__restrict__ out)
 {
-    const int qh = blockIdx.x, d = threadIdx.x;
+    const int qh = blockIdx.x, d = threadIdx.x, n_qh = gridDim.x;
     const int h = qh / group, r = qh % group;
+    part += (int64_t)blockIdx.y * n_qh * n_chunks * (kHd + 2);
+    out += (int64_t)blockIdx.y * n_qh * kHd;
     const float *base = part + ((int64_t)h * n_chunks * group + r) * (kHd + 2);
     const int64_t cstride = (int64_t)group * (kHd + 2);
     float M = -INFINITY;
@@ -495,21 +572,235 @@ extern "C" int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, 
     const int group = n_qh / kvh;
     float *part = static_cast<float *>(ws);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    const SlotMap sm{block_table, n_blocks, n_blocks, block_stride, 1,
+                     (int)std::min<int64_t>(n_blocks, 0x7fffffff), 0};
     auto launch = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)chunks, kvh), dim3(64), 0, s,
+        hipLaunchKernelGGL(kern, dim3((unsigned)chunks, kvh, 1), dim3(64), 0, s,
                            static_cast<const uint16_t *>(q), group,
                            static_cast<const unsigned char *>(k_plane),
-                           static_cast<const unsigned char *>(v_plane), n_blocks, block_stride,
-                           head_stride, token_stride, block_table, (int)bt, ids, (int)k,
+                           static_cast<const unsigned char *>(v_plane), sm, head_stride,
+                           token_stride, (int64_t)0, (int)bt, ids, (int64_t)0, (int)k, (int)k, 1,
                            static_cast<uint16_t *>(k_out), static_cast<uint16_t *>(v_out),
                            scale_log2, part);
     };
     if (dtype == KVT_BF16)
-        launch(gather_decode_partial<true>);
+        launch(gather_decode_partial<true, false, true>);
     else
-        launch(gather_decode_partial<false>);
+        launch(gather_decode_partial<false, false, true>);
     KVT_LAUNCHED("gather_decode_partial");
     hipLaunchKernelGGL(decode_merge, dim3(n_qh), dim3(kHd), 0, s, part, group, (int)chunks, out);
     KVT_LAUNCHED("decode_merge");
     return KVT_OK;
+}
+
+// [QSA-KVO] qsa_staging_worthwhile: the direct path reads rows * k_pad positions over the link
+// (each row its own selection, overlapping heavily); staging reads each used page once.
+extern "C" int kvt_staging_worthwhile(int64_t rows, int64_t k_pad, int64_t pages_used,
+                                      int64_t page_size)
+{
+    if (rows < 0 || k_pad < 0 || pages_used < 0 || page_size < 0)
+        return 0;
+    return (double)rows * (double)k_pad > 2.0 * (double)pages_used * (double)page_size ? 1 : 0;
+}
+
+namespace {
+
+constexpr int kRowsTargetGroups = 2048;   // workgroups to aim for: 8 per CU
+
+// chunks per workgroup and splits for `rows` rows of k_pad positions
+void rows_split(int64_t rows, int kvh, int64_t k_pad, int &chunks_per_wg, int &splits)
+{
+    const int64_t chunks = std::max<int64_t>(1, (k_pad + kKeys - 1) / kKeys);
+    int64_t want = (kRowsTargetGroups + rows * kvh - 1) / std::max<int64_t>(1, rows * kvh);
+    want = std::max<int64_t>(1, std::min(want, chunks));
+    chunks_per_wg = (int)((chunks + want - 1) / want);
+    splits = (int)((chunks + chunks_per_wg - 1) / chunks_per_wg);
+}
+
+// Both planes in device memory (HBM)?  Reads across the host link are paced; HBM reads are not.
+bool in_hbm(const void *a, const void *b)
+{
+    for (const void *p : {a, b}) {
+        hipPointerAttribute_t at;
+        if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+        if (at.type != hipMemoryTypeDevice)
+            return false;
+    }
+    return true;
+}
+
+struct RowsArgs {
+    const void *q;
+    int32_t rows, n_qh, kvh, hd, dtype;
+    const void *k_plane, *v_plane;
+    int64_t n_rows, row_stride, head_stride;
+    const int32_t *table;
+    int32_t table_cols;
+    int64_t table_row_stride;
+    int32_t page_size;
+    const int32_t *positions;
+    int32_t k_pad;
+    float scale;
+    float *out;
+    void *ws;
+    size_t ws_bytes;
+};
+
+int check_rows(const char *fn, const RowsArgs &a)
+{
+    if (a.hd != kHd)
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: hd=%d (this build: 128)", fn, a.hd);
+    if (a.dtype != KVT_BF16 && a.dtype != KVT_F16)
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: dtype=%d", fn, a.dtype);
+    if (a.rows < 0 || a.rows > 65535 || a.n_qh < 1 || a.kvh < 1 || a.n_qh % a.kvh ||
+        a.n_qh / a.kvh > 16 || a.kvh > 65535 || a.k_pad < 1 || a.k_pad > 0x7fffffff - kKeys ||
+        a.n_rows < 1 || a.n_rows > 0x7fffffffll)
+        return kvt::fail(KVT_EINVAL, "%s: rows=%d n_qh=%d kvh=%d k_pad=%d n_rows=%lld", fn,
+                         a.rows, a.n_qh, a.kvh, a.k_pad, (long long)a.n_rows);
+    if (a.table && (a.page_size < 1 || a.table_cols < 1 || a.table_row_stride < 0))
+        return kvt::fail(KVT_EINVAL, "%s: page_size=%d table_cols=%d table_row_stride=%lld", fn,
+                         a.page_size, a.table_cols, (long long)a.table_row_stride);
+    if (a.row_stride % 16 || a.head_stride % 16 || a.row_stride < 0 || a.head_stride < 0)
+        return kvt::fail(KVT_EALIGN, "%s: strides (%lld, %lld) must be non-negative multiples "
+                         "of 16", fn, (long long)a.row_stride, (long long)a.head_stride);
+    if (a.head_stride * (a.kvh - 1) + (int64_t)a.hd * 2 > a.row_stride)
+        return kvt::fail(KVT_EINVAL, "%s: %d heads at stride %lld do not fit a row of %lld bytes",
+                         fn, a.kvh, (long long)a.head_stride, (long long)a.row_stride);
+    if (!a.q || !a.out || !a.k_plane || !a.v_plane || !a.positions)
+        return kvt::fail(KVT_EINVAL, "%s: null pointer", fn);
+    if (!kvt::aligned(a.q, 16) || !kvt::aligned(a.k_plane, 16) || !kvt::aligned(a.v_plane, 16))
+        return kvt::fail(KVT_EALIGN, "%s: q and planes must be 16-byte aligned", fn);
+    const size_t need = kvt_sparse_attend_rows_ws_bytes(a.rows, a.n_qh, a.kvh, a.k_pad);
+    if (!a.ws || a.ws_bytes < need)
+        return kvt::fail(KVT_EINVAL, "%s: workspace of %zu bytes, need %zu", fn, a.ws_bytes,
+                         need);
+    return KVT_OK;
+}
+
+// the attention over the rows' positions; sm says where a position's row lives
+int launch_rows(const char *fn, const RowsArgs &a, const void *kp, const void *vp,
+                const SlotMap &sm, bool paced, void *stream)
+{
+    if (a.rows == 0)
+        return KVT_OK;
+    int cpw = 1, splits = 1;
+    rows_split(a.rows, a.kvh, a.k_pad, cpw, splits);
+    hipStream_t s = kvt::as_stream(stream);
+    const int group = a.n_qh / a.kvh;
+    float *part = static_cast<float *>(a.ws);
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);  // log2(e)
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)splits, a.kvh, a.rows), dim3(64), 0, s,
+                           static_cast<const uint16_t *>(a.q), group,
+                           static_cast<const unsigned char *>(kp),
+                           static_cast<const unsigned char *>(vp), sm, a.head_stride,
+                           (int64_t)0, a.table_row_stride, 1, a.positions, (int64_t)a.k_pad, 0,
+                           (int)a.k_pad, cpw, (uint16_t *)nullptr, (uint16_t *)nullptr,
+                           scale_log2, part);
+    };
+    const bool bf = a.dtype == KVT_BF16;
+    if (paced) {
+        if (cpw == 1)
+            bf ? launch(gather_decode_partial<true, false, true>)
+               : launch(gather_decode_partial<false, false, true>);
+        else
+            bf ? launch(gather_decode_partial<true, true, true>)
+               : launch(gather_decode_partial<false, true, true>);
+    } else {
+        if (cpw == 1)
+            bf ? launch(gather_decode_partial<true, false, false>)
+               : launch(gather_decode_partial<false, false, false>);
+        else
+            bf ? launch(gather_decode_partial<true, true, false>)
+               : launch(gather_decode_partial<false, true, false>);
+    }
+    KVT_LAUNCHED("gather_decode_partial");
+    hipLaunchKernelGGL(decode_merge, dim3(a.n_qh, a.rows), dim3(kHd), 0, s, part, group, splits,
+                       a.out);
+    KVT_LAUNCHED("decode_merge");
+    (void)fn;
+    return KVT_OK;
+}
+
+}  // namespace
+
+extern "C" size_t kvt_sparse_attend_rows_ws_bytes(int32_t rows, int32_t n_qh, int32_t kvh,
+                                                  int32_t k_pad)
+{
+    if (rows < 0 || n_qh < 1 || kvh < 1 || k_pad < 1)
+        return 0;
+    int cpw = 1, splits = 1;
+    rows_split(std::max(rows, 1), kvh, k_pad, cpw, splits);
+    return (size_t)std::max(rows, 1) * (size_t)n_qh * (size_t)splits * (kHd + 2) * sizeof(float);
+}
+
+// [QSA-KVO] qsa_sparse_attend_rows: each query row attends its own selection of cache
+// positions, read in place (host-mapped or HBM planes) through the row's page table.
+extern "C" int kvt_sparse_attend_rows(const void *q, int32_t rows, int32_t n_qh, int32_t kvh,
+                                      int32_t hd, int32_t dtype, const void *k_plane,
+                                      const void *v_plane, int64_t n_rows, int64_t row_stride,
+                                      int64_t head_stride, const int32_t *block_table,
+                                      int32_t table_cols, int64_t table_row_stride,
+                                      int32_t page_size, const int32_t *positions, int32_t k_pad,
+                                      float scale, float *out, void *ws, size_t ws_bytes,
+                                      void *stream)
+{
+    const RowsArgs a{q, rows, n_qh, kvh, hd, dtype, k_plane, v_plane, n_rows, row_stride,
+                     head_stride, block_table, table_cols, table_row_stride, page_size,
+                     positions, k_pad, scale, out, ws, ws_bytes};
+    int rc = check_rows("kvt_sparse_attend_rows", a);
+    if (rc != KVT_OK)
+        return rc;
+    const int64_t n_ids = block_table ? (int64_t)table_cols * page_size : n_rows;
+    const SlotMap sm{block_table, n_ids, n_rows, row_stride, block_table ? page_size : 1,
+                     block_table ? table_cols : 0x7fffffff, 0};
+    return launch_rows("kvt_sparse_attend_rows", a, k_plane, v_plane, sm, !in_hbm(k_plane, v_plane),
+                       stream);
+}
+
+// [QSA-KVO] qsa_sparse_attend_rows_staged behind qsa_staging_worthwhile: when the rule holds
+// and the staging buffers can take the used pages, the pages are copied into HBM once, in
+// logical order, and the rows attend the staged copy; otherwise they read in place.  The
+// validity of a position (its page inside the first pages_used, its table entry a page of the
+// pool) is the same either way, so both give the same bits.
+extern "C" int kvt_sparse_attend_rows_auto(
+    const void *q, int32_t rows, int32_t n_qh, int32_t kvh, int32_t hd, int32_t dtype,
+    const void *k_plane, const void *v_plane, int64_t n_rows, int64_t row_stride,
+    int64_t head_stride, const int32_t *block_table, int32_t pages_used, int32_t page_size,
+    const int32_t *positions, int32_t k_pad, float scale, float *out, void *ws, size_t ws_bytes,
+    void *staging_k, void *staging_v, size_t staging_bytes, int32_t *staged, void *stream)
+{
+    const RowsArgs a{q, rows, n_qh, kvh, hd, dtype, k_plane, v_plane, n_rows, row_stride,
+                     head_stride, block_table, pages_used, 0, page_size, positions, k_pad,
+                     scale, out, ws, ws_bytes};
+    if (!block_table || pages_used < 1 || page_size < 1 || n_rows % page_size)
+        return kvt::fail(KVT_EINVAL, "kvt_sparse_attend_rows_auto: needs a block table, "
+                         "pages_used=%d >= 1 and n_rows=%lld a multiple of page_size=%d",
+                         pages_used, (long long)n_rows, page_size);
+    int rc = check_rows("kvt_sparse_attend_rows_auto", a);
+    if (rc != KVT_OK)
+        return rc;
+    const int64_t page_bytes = (int64_t)page_size * row_stride;
+    const bool fits = staging_k && staging_v && kvt::aligned(staging_k, 16) &&
+                      kvt::aligned(staging_v, 16) &&
+                      staging_bytes >= (size_t)pages_used * (size_t)page_bytes;
+    const bool stage = fits && kvt_staging_worthwhile(rows, k_pad, pages_used, page_size);
+    if (staged)
+        *staged = stage ? 1 : 0;
+    const int64_t n_ids = (int64_t)pages_used * page_size;
+    if (!stage) {
+        const SlotMap sm{block_table, n_ids, n_rows, row_stride, page_size, pages_used, 0};
+        return launch_rows("kvt_sparse_attend_rows_auto", a, k_plane, v_plane, sm,
+                           !in_hbm(k_plane, v_plane), stream);
+    }
+    rc = kvt_stage_pages(k_plane, v_plane, page_bytes, block_table, pages_used,
+                         n_rows / page_size, staging_k, staging_v, stream);
+    if (rc != KVT_OK)
+        return rc;
+    const SlotMap sm{block_table, n_ids, n_rows, row_stride, page_size, pages_used, 1};
+    return launch_rows("kvt_sparse_attend_rows_auto", a, staging_k, staging_v, sm,
+                       !in_hbm(staging_k, staging_v), stream);
 }

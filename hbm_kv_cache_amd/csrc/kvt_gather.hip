@@ -74,7 +74,66 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     }
 }
 
+// unit u = plane * n_used + p: page table[p] of that plane -> staged page p, in pieces of
+// kPieceWords words; pages whose table entry lies outside [0, n_pages) are left as they are
+__global__ __launch_bounds__(kThreads) void stage_pages_kernel(
+    const unsigned char *__restrict__ k_plane, const unsigned char *__restrict__ v_plane,
+    int64_t page_bytes, const int32_t *__restrict__ table, int n_used, int64_t n_pages,
+    int64_t pieces_per_unit, int64_t n_pieces, unsigned char *__restrict__ k_out,
+    unsigned char *__restrict__ v_out)
+{
+    const int lane = threadIdx.x & (kvt::kWave - 1);
+    const int64_t words = page_bytes >> 4;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerGroup;
+    for (int64_t pc = (int64_t)blockIdx.x * kWavesPerGroup +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         pc < n_pieces; pc += stride) {
+        const int64_t u = pc / pieces_per_unit;
+        const int64_t c = pc - u * pieces_per_unit;
+        const int plane = (int)(u / n_used);
+        const int p = (int)(u - (int64_t)plane * n_used);
+        const int64_t phys = table[p];
+        if (phys < 0 || phys >= n_pages)
+            continue;
+        const int64_t w0 = c * kPieceWords;
+        const int n = (int)min<int64_t>(kPieceWords, words - w0);
+        const unsigned char *src = (plane ? v_plane : k_plane) + phys * page_bytes + w0 * 16;
+        unsigned char *dst = (plane ? v_out : k_out) + (int64_t)p * page_bytes + w0 * 16;
+        copy_piece(src, dst, 0, n, 0, n, lane);
+    }
+}
+
 }  // namespace
+
+// QSA-KVO qsa_sparse_attend_rows_staged: the used pages copied into HBM once, in logical order.
+extern "C" int kvt_stage_pages(const void *k_plane, const void *v_plane, int64_t page_bytes,
+                               const int32_t *block_table, int32_t n_used, int64_t n_pages,
+                               void *k_out, void *v_out, void *stream)
+{
+    if (page_bytes < 16 || page_bytes % 16 || n_used < 0 || n_pages < 0)
+        return kvt::fail(KVT_EINVAL, "kvt_stage_pages: page_bytes=%lld n_used=%d n_pages=%lld",
+                         (long long)page_bytes, n_used, (long long)n_pages);
+    if (!k_plane || !k_out || !block_table || (!v_plane) != (!v_out))
+        return kvt::fail(KVT_EINVAL, "kvt_stage_pages: null pointer (v_plane and v_out are "
+                                     "both given or both NULL)");
+    if (!kvt::aligned(k_plane, 16) || !kvt::aligned(k_out, 16) || !kvt::aligned(v_plane, 16) ||
+        !kvt::aligned(v_out, 16))
+        return kvt::fail(KVT_EALIGN, "kvt_stage_pages: planes and outputs must be 16-byte aligned");
+    if (n_used == 0)
+        return KVT_OK;
+    const int planes = v_plane ? 2 : 1;
+    const int64_t pieces_per_unit = (page_bytes / 16 + kPieceWords - 1) / kPieceWords;
+    const int64_t n_pieces = pieces_per_unit * n_used * planes;
+    const int64_t waves = std::min<int64_t>(n_pieces, kMaxWaves);
+    const unsigned groups = (unsigned)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
+    hipLaunchKernelGGL(stage_pages_kernel, dim3(groups), dim3(kThreads), 0,
+                       kvt::as_stream(stream), static_cast<const unsigned char *>(k_plane),
+                       static_cast<const unsigned char *>(v_plane), page_bytes, block_table,
+                       (int)n_used, n_pages, pieces_per_unit, n_pieces,
+                       static_cast<unsigned char *>(k_out), static_cast<unsigned char *>(v_out));
+    KVT_LAUNCHED("stage_pages_kernel");
+    return KVT_OK;
+}
 
 // S5: QSA-KVO top-k gather (selected blocks' rows, host -> HBM).
 extern "C" int kvt_gather_blocks(const void *k_plane, const void *v_plane, int64_t n_blocks,

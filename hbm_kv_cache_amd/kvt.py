@@ -62,6 +62,16 @@ _SIGNATURES = {
     "kvt_worker_wait": (c_int, [_P, _P, c_int32]),
     "kvt_worker_pending": (c_int, [_P]),
     "kvt_worker_destroy": (c_int, [_P]),
+    "kvt_sparse_attend_rows_ws_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+    "kvt_sparse_attend_rows": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, _P, _P,
+                                       c_int64, c_int64, c_int64, _P, c_int32, c_int64, c_int32,
+                                       _P, c_int32, c_float, _P, _P, c_size_t, _P]),
+    "kvt_staging_worthwhile": (c_int, [c_int64, c_int64, c_int64, c_int64]),
+    "kvt_stage_pages": (c_int, [_P, _P, c_int64, _P, c_int32, c_int64, _P, _P, _P]),
+    "kvt_sparse_attend_rows_auto": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, _P,
+                                            _P, c_int64, c_int64, c_int64, _P, c_int32, c_int32,
+                                            _P, c_int32, c_float, _P, _P, c_size_t, _P, _P,
+                                            c_size_t, ctypes.POINTER(c_int32), _P]),
     "kvt_paged_write": (c_int, [_P, _P, _P, c_int32, c_int32, c_int32, _P, _P, c_int32, c_int32,
                                 c_int64, _P]),
     "kvt_copy_page": (c_int, [_P, _P, _P, c_int32, c_int64, c_int64, c_int32, c_int32, _P, _P,
@@ -350,3 +360,44 @@ def kvt_copy_page(src_hosts, dst_hosts, row_bytes, from_page, to_page, page_size
     _check("kvt_copy_page", load().kvt_copy_page(
         a, b, c, n, int(from_page), int(to_page), int(page_size), int(num_tokens),
         _ptr(src_pooled), _ptr(dst_pooled), int(pooled_row_bytes), int(cr), _stream(stream)))
+
+
+def kvt_sparse_attend_rows_ws_bytes(rows, n_qh, kvh, k_pad) -> int:
+    return int(load().kvt_sparse_attend_rows_ws_bytes(int(rows), int(n_qh), int(kvh), int(k_pad)))
+
+
+def kvt_sparse_attend_rows(q, rows, n_qh, kvh, hd, dtype, k_plane, v_plane, n_rows, row_stride,
+                           head_stride, block_table, table_cols, table_row_stride, page_size,
+                           positions, k_pad, scale, out, ws, ws_bytes, stream=None):
+    _check("kvt_sparse_attend_rows", load().kvt_sparse_attend_rows(
+        _ptr(q), int(rows), int(n_qh), int(kvh), int(hd), int(dtype), _ptr(k_plane),
+        _ptr(v_plane), int(n_rows), int(row_stride), int(head_stride), _ptr(block_table),
+        int(table_cols), int(table_row_stride), int(page_size), _ptr(positions), int(k_pad),
+        float(scale), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def kvt_staging_worthwhile(rows, k_pad, pages_used, page_size) -> bool:
+    return bool(load().kvt_staging_worthwhile(int(rows), int(k_pad), int(pages_used),
+                                              int(page_size)))
+
+
+def kvt_stage_pages(k_plane, v_plane, page_bytes, block_table, n_used, n_pages, k_out, v_out,
+                    stream=None):
+    _check("kvt_stage_pages", load().kvt_stage_pages(
+        _ptr(k_plane), _ptr(v_plane), int(page_bytes), _ptr(block_table), int(n_used),
+        int(n_pages), _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def kvt_sparse_attend_rows_auto(q, rows, n_qh, kvh, hd, dtype, k_plane, v_plane, n_rows,
+                                row_stride, head_stride, block_table, pages_used, page_size,
+                                positions, k_pad, scale, out, ws, ws_bytes, staging_k=None,
+                                staging_v=None, staging_bytes=0, stream=None) -> bool:
+    """Returns True when the pages were staged into HBM first."""
+    staged = c_int32(-1)
+    _check("kvt_sparse_attend_rows_auto", load().kvt_sparse_attend_rows_auto(
+        _ptr(q), int(rows), int(n_qh), int(kvh), int(hd), int(dtype), _ptr(k_plane),
+        _ptr(v_plane), int(n_rows), int(row_stride), int(head_stride), _ptr(block_table),
+        int(pages_used), int(page_size), _ptr(positions), int(k_pad), float(scale), _ptr(out),
+        _ptr(ws), int(ws_bytes), _ptr(staging_k), _ptr(staging_v), int(staging_bytes),
+        ctypes.byref(staged), _stream(stream)))
+    return bool(staged.value)

@@ -12,6 +12,9 @@
  *   kvt_stage_tail       copy a sequence's host-resident rows into an HBM staging buffer
  *   kvt_attn_decode      GQA decode attention over gathered K/V
  *   kvt_gather_attn_decode  the gather and the decode attention in one pass
+ *   kvt_sparse_attend_rows  many query rows, each over its own selection of cache positions
+ *   kvt_sparse_attend_rows_auto  the same, staging the used pages first when that reads less
+ *   kvt_stage_pages      copy a sequence's pages (via its block table) into HBM in logical order
  *   kvt_attn_prefill     causal (or full) prefill attention over an HBM head + tail
  *   kvt_attn_prefill_range      the same attention as resumable passes over key ranges
  *   kvt_attn_prefill_pipelined  tail staging in arena buckets overlapped with the attention
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 6
+#define KVT_ABI_VERSION 7
 
 /* status codes */
 #define KVT_OK 0
@@ -243,6 +246,57 @@ int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd,
                            const int32_t *block_table, int32_t bt, const int32_t *ids, int32_t k,
                            void *k_out, void *v_out, float scale, float *out, void *ws,
                            size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * Sparse attention over per-row selections.  [QSA-KVO] qsa_sparse_attend_rows: query row r
+ * (R rows of n_qh heads, e.g. the tokens of a prefill chunk) attends the cache positions
+ * positions[r][0..k_pad) (logical token positions; -1 pads), the same selection for every
+ * head; query head i reads KV head i / (n_qh/kvh).  Each row's result is the decode
+ * attention of kvt_attn_decode over its valid positions, in the same fp32 arithmetic.
+ *   q       device [rows][n_qh][hd], dtype KVT_BF16 / KVT_F16;  out: device fp32, same shape
+ *   planes  k_plane, v_plane: device pointers (host-mapped or HBM) of n_rows token rows;
+ *           head h of physical row x at plane + x*row_stride + h*head_stride
+ *           (head_stride*(kvh-1) + hd*2 <= row_stride; strides multiples of 16)
+ *   block_table  NULL: positions are physical rows.  Else device int32, row r's entries at
+ *           block_table + r*table_row_stride (0 = one table for all rows), table_cols of
+ *           them; position p -> physical row block_table[p / page_size]*page_size + p % page_size
+ *   A position takes part when it is >= 0, below table_cols*page_size (n_rows without a
+ *   table), its table entry is >= 0 and the physical row is below n_rows.
+ *   ws      device workspace of kvt_sparse_attend_rows_ws_bytes(rows, n_qh, kvh, k_pad)
+ * Limits: hd == 128, n_qh/kvh <= 16, rows <= 65535, n_rows < 2^31.  Deterministic.
+ *
+ * kvt_staging_worthwhile: [QSA-KVO] qsa_staging_worthwhile -- nonzero when
+ *   rows * k_pad > 2 * pages_used * page_size (the direct reads would exceed twice the history).
+ * kvt_stage_pages: page block_table[p] of k_plane (and v_plane) -> page p of k_out (v_out),
+ *   p < n_used, pages of page_bytes (a multiple of 16); entries outside [0, n_pages) leave
+ *   their page untouched.  v_plane and v_out both given or both NULL.
+ * kvt_sparse_attend_rows_auto: one sequence (one block table for every row), dense pages of
+ *   page_size rows (n_rows a multiple of page_size), positions below pages_used*page_size.
+ *   When kvt_staging_worthwhile(rows, k_pad, pages_used, page_size) holds and staging_k and
+ *   staging_v (device, staging_bytes each) hold pages_used pages, the pages are staged with
+ *   kvt_stage_pages and the rows attend the HBM copy; otherwise they read in place.  The
+ *   output is bit-identical either way.  *staged (optional, host) receives which was taken.
+ * ---------------------------------------------------------------------------------------- */
+size_t kvt_sparse_attend_rows_ws_bytes(int32_t rows, int32_t n_qh, int32_t kvh, int32_t k_pad);
+int kvt_sparse_attend_rows(const void *q, int32_t rows, int32_t n_qh, int32_t kvh, int32_t hd,
+                           int32_t dtype, const void *k_plane, const void *v_plane,
+                           int64_t n_rows, int64_t row_stride, int64_t head_stride,
+                           const int32_t *block_table, int32_t table_cols,
+                           int64_t table_row_stride, int32_t page_size, const int32_t *positions,
+                           int32_t k_pad, float scale, float *out, void *ws, size_t ws_bytes,
+                           void *stream);
+int kvt_staging_worthwhile(int64_t rows, int64_t k_pad, int64_t pages_used, int64_t page_size);
+int kvt_stage_pages(const void *k_plane, const void *v_plane, int64_t page_bytes,
+                    const int32_t *block_table, int32_t n_used, int64_t n_pages, void *k_out,
+                    void *v_out, void *stream);
+int kvt_sparse_attend_rows_auto(const void *q, int32_t rows, int32_t n_qh, int32_t kvh,
+                                int32_t hd, int32_t dtype, const void *k_plane,
+                                const void *v_plane, int64_t n_rows, int64_t row_stride,
+                                int64_t head_stride, const int32_t *block_table,
+                                int32_t pages_used, int32_t page_size, const int32_t *positions,
+                                int32_t k_pad, float scale, float *out, void *ws,
+                                size_t ws_bytes, void *staging_k, void *staging_v,
+                                size_t staging_bytes, int32_t *staged, void *stream);
 
 /* ----------------------------------------------------------------------------------------
  * S8  prefill attention over a tiered cache.  [llama-T]: cells [0, n_head) live in HBM, the

@@ -15,6 +15,9 @@ Functions and the passages they follow:
 * ``stage_tail``       -- llama.cpp PR #319 commit text (used host rows copied to a VRAM buffer).
 * ``attn_decode``      -- QSA KV offload, staged attention (GQA map, softmax normalisation).
 * ``attn_prefill``     -- llama.cpp PR #319 (VRAM head + host tail, same output as all-device).
+* ``sparse_attend_rows`` -- QSA KV offload, ``qsa_sparse_attend_rows`` (each query row over its
+  own selection of cache positions, mapped through the row's page table).
+* ``staging_worthwhile`` -- QSA KV offload, ``qsa_staging_worthwhile``.
 * ``paged_write``      -- QSA KV offload, ``CacheLayer_qsa_offload`` docstring (new rows reach
   the host pages through the paged cache update; the plain block-table rule).
 * ``copy_page``        -- QSA KV offload, ``CacheLayer_qsa_offload.copy_page``.
@@ -253,6 +256,57 @@ def gather_attn_decode(q_u16, k_plane, v_plane, n_blocks, kvh, hd, fmt, strides,
                       vo.view(np.uint16).reshape(kvh, n_kv, hd), fmt, scale, n_valid=n_valid,
                       threads=threads)
     return out, ko, vo
+
+
+def sparse_attend_rows(q_u16, k_plane, v_plane, n_rows, row_stride, head_stride, kvh, fmt,
+                       positions, scale, block_table=None, page_size=1, table_cols=None,
+                       threads=0):
+    """q: [R][n_qh][hd] bits; planes: uint8 arrays of n_rows rows of row_stride bytes (head h
+    of a row at byte h*head_stride); positions: int [R][k_pad] logical positions, -1 = none;
+    block_table: None (positions are physical rows) or int [R or 1][cols].  A position takes
+    part when it is >= 0, below table_cols*page_size (n_rows without a table), its page's
+    table entry is >= 0 and the physical row is below n_rows.  Row r's output is attn_decode
+    over the rows of its valid positions in order.  Returns f64 [R][n_qh][hd]."""
+    q = np.ascontiguousarray(q_u16, dtype=np.uint16)
+    n_r, n_qh, hd = q.shape
+    kp = np.ascontiguousarray(k_plane).reshape(-1).view(np.uint8)
+    vp = np.ascontiguousarray(v_plane).reshape(-1).view(np.uint8)
+    tab = None if block_table is None else np.asarray(block_table, dtype=np.int64)
+    if tab is not None and table_cols is None:
+        table_cols = tab.shape[1]
+    out = np.empty((n_r, n_qh, hd), dtype=np.float64)
+    for r in range(n_r):
+        phys = []
+        for p in np.asarray(positions[r]).tolist():
+            if p < 0:
+                continue
+            if tab is None:
+                if p < n_rows:
+                    phys.append(p)
+                continue
+            pg, off = divmod(p, page_size)
+            if pg >= table_cols:
+                continue
+            e = int(tab[r if tab.shape[0] > 1 else 0, pg])
+            if e >= 0 and e * page_size + off < n_rows:
+                phys.append(e * page_size + off)
+        n = len(phys)
+        k = np.zeros((kvh, max(n, 1), hd), dtype=np.uint16)
+        v = np.zeros((kvh, max(n, 1), hd), dtype=np.uint16)
+        for j, x in enumerate(phys):
+            for h in range(kvh):
+                o = x * row_stride + h * head_stride
+                k[h, j] = kp[o:o + 2 * hd].view(np.uint16)
+                v[h, j] = vp[o:o + 2 * hd].view(np.uint16)
+        out[r] = attn_decode(q[r], k, v, fmt, scale, n_valid=np.full(kvh, n, np.int32),
+                             threads=threads)
+    return out
+
+
+def staging_worthwhile(rows, k_pad, pages_used, page_size):
+    """Staging the used pages reads pages_used*page_size positions once; the direct path reads
+    rows*k_pad.  Stage when the latter exceeds twice the former."""
+    return rows * k_pad > 2 * pages_used * page_size
 
 
 def paged_write(planes, new_rows, cache_seqlens, block_table, page_size):

@@ -35,7 +35,7 @@ def test_header_declarations_all_exported():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 6
+    assert kvt.kvt_abi_version() == 7
 
 
 def test_library_has_gfx950_code_object():
@@ -195,4 +195,36 @@ def test_paged_write_and_copy_page_argument_errors():
     assert e.value.code == kvt.EINVAL
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_copy_page([p], [p], [32], 0, 1, 16, 4, p, None, 16, 4, stream=0)
+    assert e.value.code == kvt.EINVAL
+
+
+def test_staging_rule_equals_oracle_and_rows_argument_errors():
+    g = np.random.default_rng(5)
+    for _ in range(2000):
+        r, k, p, s = (int(x) for x in g.integers(0, 5000, size=4))
+        assert kvt.kvt_staging_worthwhile(r, k, p, s) == oracle.staging_worthwhile(r, k, p, s)
+    assert kvt.kvt_staging_worthwhile(2048, 2080, 4096, 256)
+    assert kvt.kvt_sparse_attend_rows_ws_bytes(1, 64, 8, 2080) == 64 * 33 * 130 * 4
+    assert kvt.kvt_sparse_attend_rows_ws_bytes(2048, 32, 8, 2080) == 2048 * 32 * 1 * 130 * 4
+    a = np.zeros(1 << 16, np.uint8)
+    p = a.ctypes.data
+    ws = kvt.kvt_sparse_attend_rows_ws_bytes(2, 16, 4, 100)
+    base = dict(q=p, rows=2, n_qh=16, kvh=4, hd=128, dtype=kvt.BF16, k_plane=p, v_plane=p,
+                n_rows=64, row_stride=1024, head_stride=256, block_table=None, table_cols=0,
+                table_row_stride=0, page_size=16, positions=p, k_pad=100, scale=0.1, out=p,
+                ws=p, ws_bytes=ws, stream=0)
+    for change, code in [({"hd": 64}, kvt.EUNSUPPORTED), ({"n_qh": 15}, kvt.EINVAL),
+                         ({"k_pad": 0}, kvt.EINVAL), ({"row_stride": 1000}, kvt.EALIGN),
+                         ({"head_stride": 512}, kvt.EINVAL), ({"ws_bytes": ws - 1}, kvt.EINVAL),
+                         ({"rows": 70000}, kvt.EINVAL), ({"positions": None}, kvt.EINVAL),
+                         ({"block_table": p, "table_cols": 0}, kvt.EINVAL)]:
+        with pytest.raises(kvt.KvtError) as e:
+            kvt.kvt_sparse_attend_rows(**{**base, **change})
+        assert e.value.code == code, change
+    with pytest.raises(kvt.KvtError) as e:     # the automatic form needs a table
+        kvt.kvt_sparse_attend_rows_auto(p, 2, 16, 4, 128, kvt.BF16, p, p, 64, 1024, 256, None, 4,
+                                        16, p, 100, 0.1, p, p, ws, stream=0)
+    assert e.value.code == kvt.EINVAL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_stage_pages(p, None, 4096, p, 4, 8, p, p, stream=0)
     assert e.value.code == kvt.EINVAL

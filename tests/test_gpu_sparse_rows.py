@@ -1,0 +1,143 @@
+"""GPU parity of sparse attention over per-row selections (kvt_sparse_attend_rows and its
+staging-rule form) against the oracle: within 2e-3 max-abs, and the staged path equal to the
+direct path bit for bit."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hbm_kv_cache_amd import kvt, synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _setup(gpu, n_pages, ps, kvh, R, n_qh, k_pad, seq_len, fmt, seed, per_row=True):
+    g = synth.rng(14, synth.P_MISC, seed)
+    hd = 128
+    n_rows = n_pages * ps
+    row = kvh * hd * 2
+    host = kvt.HostBuffer(2 * n_rows * row)
+    planes = host.numpy(np.uint16, (2, n_rows, kvh, hd))
+    gen = synth.bf16_normal if fmt == kvt.BF16 else synth.f16_normal
+    for p, purpose in enumerate((synth.P_K, synth.P_V)):
+        planes[p] = gen(synth.rng(14, purpose, seed), (n_rows, kvh, hd))
+    q = gen(synth.rng(14, synth.P_Q, seed), (R, n_qh, hd))
+    cols = -(-seq_len // ps)
+    nt = R if per_row else 1
+    table = np.stack([g.permutation(n_pages)[:cols] for _ in range(nt)]).astype(np.int32)
+    pos = np.full((R, k_pad), -1, np.int32)
+    for r in range(R):
+        n = int(g.integers(k_pad // 2, k_pad + 1))
+        pos[r, :n] = np.sort(g.choice(seq_len, size=min(n, seq_len), replace=False))[:n]
+    return host, planes, q, table, pos, n_rows, row, cols
+
+
+def _run(gpu, host, q, table, pos, n_rows, row, cols, kvh, ps, fmt, table_row_stride=None):
+    R, n_qh, hd = q.shape
+    k_pad = pos.shape[1]
+    ws_b = kvt.kvt_sparse_attend_rows_ws_bytes(R, n_qh, kvh, k_pad)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=gpu)
+    out = torch.full((R, n_qh, hd), float("nan"), dtype=torch.float32, device=gpu)
+    td = torch.from_numpy(table).to(gpu)
+    trs = (cols if table.shape[0] > 1 else 0) if table_row_stride is None else table_row_stride
+    kvt.kvt_sparse_attend_rows(torch.from_numpy(q.view(np.int16)).to(gpu), R, n_qh, kvh, hd, fmt,
+                               host.dev, host.dev + n_rows * row, n_rows, row, hd * 2, td, cols,
+                               trs, ps, torch.from_numpy(pos).to(gpu), k_pad, 1 / math.sqrt(hd),
+                               out, ws, ws_b)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt", [kvt.BF16, kvt.F16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("R,n_qh,kvh,k_pad,per_row", [
+    (6, 16, 4, 160, True),     # per-row tables, ragged k_pad (3 chunks, last partial)
+    (3, 64, 8, 64, False),     # one shared table, one chunk
+    (300, 32, 8, 200, True),   # enough rows that each workgroup folds several chunks
+])
+def test_sparse_rows_match_oracle(gpu, fmt, R, n_qh, kvh, k_pad, per_row):
+    ps, n_pages, seq_len = 16, 256, 1500
+    host, planes, q, table, pos, n_rows, row, cols = _setup(
+        gpu, n_pages, ps, kvh, R, n_qh, k_pad, seq_len, fmt, R + k_pad, per_row)
+    table[0, 3] = -1                 # a hole in row 0's pages
+    pos[min(1, R - 1), :] = -1       # a row with no position
+    got = _run(gpu, host, q, table, pos, n_rows, row, cols, kvh, ps, fmt)
+    rows = range(R) if R <= 8 else range(0, R, 37)
+    ofmt = oracle.BF16 if fmt == kvt.BF16 else oracle.F16
+    for r in rows:
+        ref = oracle.sparse_attend_rows(q[r:r + 1], planes[0].view(np.uint8),
+                                        planes[1].view(np.uint8), n_rows, row, 256, kvh, ofmt,
+                                        pos[r:r + 1], 1 / math.sqrt(128),
+                                        block_table=table[r:r + 1] if per_row else table,
+                                        page_size=ps)
+        err = np.max(np.abs(got[r] - ref[0]))
+        assert np.isfinite(got[r]).all() and err <= TOL, (r, err)
+    assert (got[min(1, R - 1)] == 0).all()
+    del planes
+    host.free()
+
+
+def test_sparse_rows_without_table(gpu):
+    kvh, ps, R, n_qh, k_pad = 4, 16, 5, 16, 100
+    host, planes, q, _, pos, n_rows, row, _ = _setup(gpu, 64, ps, kvh, R, n_qh, k_pad, 1024,
+                                                     kvt.BF16, 3)
+    pos[2, 10:20] = n_rows + 7       # past the plane: dropped
+    R_, hd = R, 128
+    ws_b = kvt.kvt_sparse_attend_rows_ws_bytes(R, n_qh, kvh, k_pad)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=gpu)
+    out = torch.empty((R, n_qh, hd), dtype=torch.float32, device=gpu)
+    kvt.kvt_sparse_attend_rows(torch.from_numpy(q.view(np.int16)).to(gpu), R_, n_qh, kvh, hd,
+                               kvt.BF16, host.dev, host.dev + n_rows * row, n_rows, row, hd * 2,
+                               None, 0, 0, 1, torch.from_numpy(pos).to(gpu), k_pad,
+                               1 / math.sqrt(hd), out, ws, ws_b)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_attend_rows(q, planes[0].view(np.uint8), planes[1].view(np.uint8),
+                                    n_rows, row, 256, kvh, oracle.BF16, pos, 1 / math.sqrt(hd))
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
+    del planes
+    host.free()
+
+
+@pytest.mark.parametrize("R,expect_staged", [(400, True), (4, False)])
+def test_auto_staged_equals_direct(gpu, R, expect_staged):
+    """The staging rule picks the path; either way the bits equal the direct call's, and
+    kvt_stage_pages lays the used pages out in logical order."""
+    kvh, n_qh, ps, n_pages, k_pad, seq_len = 8, 32, 16, 128, 256, 1000
+    host, planes, q, table, pos, n_rows, row, cols = _setup(
+        gpu, n_pages, ps, kvh, R, n_qh, k_pad, seq_len, kvt.BF16, 11, per_row=False)
+    table[0, 5] = -1
+    assert kvt.kvt_staging_worthwhile(R, k_pad, cols, ps) == expect_staged
+    direct = _run(gpu, host, q, table, pos, n_rows, row, cols, kvh, ps, kvt.BF16)
+    ws_b = kvt.kvt_sparse_attend_rows_ws_bytes(R, n_qh, kvh, k_pad)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=gpu)
+    out = torch.empty((R, n_qh, 128), dtype=torch.float32, device=gpu)
+    stage_bytes = cols * ps * row
+    sk = torch.full((stage_bytes,), 0x7f, dtype=torch.uint8, device=gpu)
+    sv = torch.full((stage_bytes,), 0x7f, dtype=torch.uint8, device=gpu)
+    td = torch.from_numpy(table).to(gpu)
+    staged = kvt.kvt_sparse_attend_rows_auto(
+        torch.from_numpy(q.view(np.int16)).to(gpu), R, n_qh, kvh, 128, kvt.BF16, host.dev,
+        host.dev + n_rows * row, n_rows, row, 256, td, cols, ps, torch.from_numpy(pos).to(gpu),
+        k_pad, 1 / math.sqrt(128), out, ws, ws_b, sk, sv, stage_bytes)
+    torch.cuda.synchronize()
+    assert staged == expect_staged
+    assert np.array_equal(out.cpu().numpy(), direct)
+    if staged:
+        kb = planes[0].view(np.uint8).reshape(n_pages, ps * row)
+        got = sk.cpu().numpy().reshape(cols, ps * row)
+        for p in range(cols):
+            if table[0, p] >= 0:
+                assert np.array_equal(got[p], kb[table[0, p]]), p
+            else:
+                assert (got[p] == 0x7f).all()
+    # too small a staging buffer: direct, same bits
+    staged = kvt.kvt_sparse_attend_rows_auto(
+        torch.from_numpy(q.view(np.int16)).to(gpu), R, n_qh, kvh, 128, kvt.BF16, host.dev,
+        host.dev + n_rows * row, n_rows, row, 256, td, cols, ps, torch.from_numpy(pos).to(gpu),
+        k_pad, 1 / math.sqrt(128), out, ws, ws_b, sk, sv, stage_bytes - 16)
+    torch.cuda.synchronize()
+    assert not staged and np.array_equal(out.cpu().numpy(), direct)
+    del planes
+    host.free()

@@ -544,3 +544,60 @@ def test_copy_page_counts_and_untouched_rows():
     assert np.array_equal(k[3, :5], k0[1, :5]) and np.array_equal(k[3, 5:], k0[3, 5:])
     assert np.array_equal(pooled[3, :3], p0[1, :3]) and np.array_equal(pooled[3, 3:], p0[3, 3:])
     assert np.array_equal(k[:3], k0[:3]) and np.array_equal(pooled[:3], p0[:3])
+
+
+@pytest.mark.parametrize("table_kind", ["per_row", "shared", "none"])
+def test_sparse_attend_rows_is_sdpa_over_valid_positions(table_kind):
+    """Each row's valid positions mapped to physical rows with numpy array arithmetic (a
+    vectorised mask, not the oracle's per-position loop), the K/V rows picked by fancy
+    indexing from a [row][head][dim] view, torch SDPA in fp64 per row."""
+    g = synth.rng(0, synth.P_MISC, 70 + len(table_kind))
+    kvh, hd, G, ps, n_pages, R, k_pad = 2, 32, 3, 4, 12, 4, 14
+    n_rows = n_pages * ps
+    planes = synth.bf16_normal(g, (2, n_rows, kvh, hd))
+    q = synth.bf16_normal(g, (R, kvh * G, hd))
+    cols = 6
+    if table_kind == "none":
+        table = None
+        pos = g.integers(-3, n_rows + 5, size=(R, k_pad))
+    else:
+        nt = R if table_kind == "per_row" else 1
+        table = np.stack([g.permutation(n_pages)[:cols] for _ in range(nt)]).astype(np.int32)
+        table[0, 2] = -1                       # a hole
+        table[-1, 4] = n_pages + 3             # outside the pool
+        pos = g.integers(-3, cols * ps + 6, size=(R, k_pad))
+    pos[1, 5:] = -1
+    out = oracle.sparse_attend_rows(q, planes[0].view(np.uint8), planes[1].view(np.uint8),
+                                    n_rows, kvh * hd * 2, hd * 2, kvh, oracle.BF16, pos, 0.25,
+                                    block_table=table, page_size=ps)
+    for r in range(R):
+        p = pos[r]
+        if table is None:
+            ok = (p >= 0) & (p < n_rows)
+            phys = p
+        else:
+            t = table[r if table.shape[0] > 1 else 0]
+            pg = np.clip(p // ps, 0, cols - 1)
+            e = t[pg].astype(np.int64)
+            phys = e * ps + p % ps
+            ok = (p >= 0) & (p < cols * ps) & (e >= 0) & (phys < n_rows)
+        sel = phys[ok]
+        for h in range(kvh):
+            kk_ = _to_f64(planes[0][sel, h], oracle.BF16)[None]
+            vv_ = _to_f64(planes[1][sel, h], oracle.BF16)[None]
+            qq = _to_f64(q[r, h * G:(h + 1) * G], oracle.BF16)[None]
+            if sel.size == 0:
+                assert (out[r, h * G:(h + 1) * G] == 0).all()
+                continue
+            ref = _sdpa(qq, kk_, vv_, 0.25)[0].numpy()
+            assert np.max(np.abs(out[r, h * G:(h + 1) * G] - ref)) < 1e-12
+
+
+def test_staging_worthwhile_page_examples():
+    """QSA KV offload, qsa_staging_worthwhile's docstring: a 2048-row prefill chunk with 2080
+    selections per row against a history of ~4096 pages sits on the staging side; a one-row
+    decode does not.  The comparison is strict."""
+    assert oracle.staging_worthwhile(2048, 2080, 4096, 256)
+    assert not oracle.staging_worthwhile(1, 2080, 4096, 256)
+    assert not oracle.staging_worthwhile(1024, 1024, 2048, 256)     # equal: not worthwhile
+    assert oracle.staging_worthwhile(1025, 1024, 2048, 256)
