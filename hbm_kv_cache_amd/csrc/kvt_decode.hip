@@ -263,17 +263,28 @@ struct SlotMap {
     int logical;            // nonzero: the table only validates; the block index stays the id
 };
 
-// lane's slot id -> block byte offset, or -1 when the slot takes no part
-__device__ __forceinline__ int64_t slot_offset(int64_t id, const SlotMap &sm)
+// A slot id's table entry (the load), kept apart from its use so that a loop can issue it
+// early.  in: the id lies in [0, n_ids) and its table page in the table.
+__device__ __forceinline__ int32_t table_entry(int64_t id, const SlotMap &sm, uint32_t &pg,
+                                               bool &in)
 {
-    bool ok = id >= 0 && id < sm.n_ids;
+    in = id >= 0 && id < sm.n_ids;
+    const uint32_t u = in ? (uint32_t)id : 0u;
+    pg = u / (uint32_t)sm.table_page;
+    in = in && (int)pg < sm.table_cols;
+    return sm.table ? sm.table[in ? pg : 0] : 0;
+}
+
+// slot id (+ its table entry) -> block byte offset, or -1 when the slot takes no part
+__device__ __forceinline__ int64_t slot_offset_from(int64_t id, bool in, uint32_t pg,
+                                                    int32_t entry, const SlotMap &sm)
+{
+    bool ok = in;
     if (sm.table) {
-        const uint32_t u = ok ? (uint32_t)id : 0u;
-        const uint32_t pg = u / (uint32_t)sm.table_page;
-        ok = ok && (int)pg < sm.table_cols;
-        const int64_t phys = sm.table[ok ? pg : 0];
+        const int64_t phys = entry;
         ok = ok && phys >= 0;
-        const int64_t blk = phys * sm.table_page + (int64_t)(u - pg * (uint32_t)sm.table_page);
+        const int64_t blk =
+            phys * sm.table_page + (int64_t)((uint32_t)id - pg * (uint32_t)sm.table_page);
         ok = ok && blk < sm.n_phys;
         if (!sm.logical)
             id = blk;
@@ -281,25 +292,32 @@ __device__ __forceinline__ int64_t slot_offset(int64_t id, const SlotMap &sm)
     return ok ? id * sm.block_stride : -1;
 }
 
+__device__ __forceinline__ int64_t slot_offset(int64_t id, const SlotMap &sm)
+{
+    uint32_t pg;
+    bool in;
+    const int32_t e = table_entry(id, sm, pg, in);
+    return slot_offset_from(id, in, pg, e, sm);
+}
+
 // Gather and attend one 64-key chunk: the chunk's K/V rows are read straight from the
 // (host-mapped) planes of the selected slots, optionally written to the HBM gather buffers,
 // and folded into st.  Key j (j < kk*bt) is token j % bt of selected slot j / bt.  Each lane
 // owns the 16-byte word cw = lane % 16 of rows lane/16 + 4*jj (jj < 16): every group of 16
 // lanes reads one contiguous 256-byte row slice.
-template <bool kBf16, bool kPaced>
+//   sbase: lane L's block offset of slot s0 + L (s0 = key0 / bt), from slot_offset;
+//   mid(): called once the chunk's first row loads are issued (a loop prefetches there).
+template <bool kBf16, bool kPaced, typename Mid>
 __device__ __forceinline__ void gather_chunk(
-    const unsigned char *__restrict__ kp, const unsigned char *__restrict__ vp,
-    const SlotMap &sm, int64_t hoff, int64_t token_stride, int bt,
-    const int32_t *__restrict__ hid, int kk, int key0, uint16_t *__restrict__ k_out,
+    const unsigned char *__restrict__ kp, const unsigned char *__restrict__ vp, int64_t sbase,
+    int64_t hoff, int64_t token_stride, int bt, int kk, int key0, uint16_t *__restrict__ k_out,
     uint16_t *__restrict__ v_out, int64_t out_key0, uint4 (&qa)[4], int group,
     float scale_log2, unsigned char *ksm, unsigned char *vs, float (*ps)[16], float *as,
-    ChunkState &st, int lane)
+    ChunkState &st, int lane, Mid mid)
 {
     const int n_kv = kk * bt;   // < 2^31, checked by the host
     const int rg = lane >> 4, cw = lane & 15;
-    // The chunk's keys span at most 64 slots: lane L resolves slot s0 + L.
     const int s0 = (int)((uint32_t)key0 / (uint32_t)bt);
-    const int64_t sbase = slot_offset(hid[min(s0 + lane, kk - 1)], sm);
     // byte offsets of this lane's 16 rows (cw*16 -- always a valid address -- for keys that
     // take no part); bit jj of okb = row rg + 4*jj takes part
     int slot[16];
@@ -339,21 +357,52 @@ __device__ __forceinline__ void gather_chunk(
     // Paced (planes across the host link): the rows cross the link one K and one V wave-load
     // at a time per wave -- with every load of the step issued at once the link runs ~20%
     // slower (see kvt_gather.hip) -- and the pair after a sub-tile's last is issued before
-    // that sub-tile is attended, so the attention runs while the link is busy.  Unpaced
-    // (planes in HBM): all 16 pairs are issued at once.  Each pair goes to LDS -- K as read, V
-    // zeroed where the key takes no part -- and, when asked, to the HBM gather buffers in
-    // kvt_gather_blocks' layout (rows of skipped slots untouched).
-    u32x4 kr[kPaced ? 1 : 16], vr[kPaced ? 1 : 16];
-    if constexpr (kPaced) {
-        kr[0] = *reinterpret_cast<const u32x4 *>(kp + off[0]);
-        vr[0] = *reinterpret_cast<const u32x4 *>(vp + off[0]);
-    } else {
+    // that sub-tile is attended, so the attention runs while the link is busy.  Each pair
+    // goes to LDS -- K as read, V zeroed where the key takes no part -- and, when asked, to
+    // the HBM gather buffers in kvt_gather_blocks' layout (rows of skipped slots untouched).
+    // Unpaced (planes in HBM): every load of the chunk is issued at once.
+    if constexpr (!kPaced) {
+        // HBM planes: K straight into the MFMA B layout (lane (g, col) takes key 16t + col,
+        // dims ks*32 + 8g ..), V rows through LDS as below; no K staging in LDS, so twice as
+        // many waves fit a CU.  A key that takes no part reads the plane's first bytes; its
+        // scores are masked.
+        const int g = lane >> 4, col = lane & 15;
+        const int64_t hk = hoff - cw * 16;   // the head's offset inside a row
+        uint4 kd[4][4];
 #pragma unroll
-        for (int jj = 0; jj < 16; jj++) {
-            kr[jj] = *reinterpret_cast<const u32x4 *>(kp + off[jj]);
-            vr[jj] = *reinterpret_cast<const u32x4 *>(vp + off[jj]);
+        for (int t = 0; t < 4; t++) {
+            const int key = key0 + 16 * t + col;
+            const int kc = key < n_kv ? key : n_kv - 1;
+            const int sl = (int)((uint32_t)kc / (uint32_t)bt);
+            const int64_t b = __shfl(sbase, sl - s0, 64);
+            const bool ok = key < n_kv && b >= 0;
+            const int64_t o = ok ? b + hk + (int64_t)(kc - sl * bt) * token_stride + 16 * g : 0;
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++)
+                kd[t][ks] = *reinterpret_cast<const uint4 *>(kp + o + ks * 64);
         }
+        u32x4 vr[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; jj++)
+            vr[jj] = *reinterpret_cast<const u32x4 *>(vp + off[jj]);
+        mid();
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int jj = 4 * t + u;
+                *reinterpret_cast<u32x4 *>(vs + (rg + 4 * jj) * kVPitch + cw * 16) =
+                    ((okb >> jj) & 1) ? vr[jj] : u32x4{0, 0, 0, 0};
+            }
+            __syncthreads();   // sub-tile t's V rows are in LDS
+            subtile_attend<kBf16>(t, qa, kd[t], valid, group, scale_log2, vs, ps, as, st, lane);
+        }
+        return;
     }
+    u32x4 kr[1], vr[1];
+    kr[0] = *reinterpret_cast<const u32x4 *>(kp + off[0]);
+    vr[0] = *reinterpret_cast<const u32x4 *>(vp + off[0]);
+    mid();
 #pragma unroll
     for (int t = 0; t < 4; t++) {
 #pragma unroll
@@ -361,7 +410,7 @@ __device__ __forceinline__ void gather_chunk(
             const int jj = 4 * t + u;
             const int row = rg + 4 * jj;
             const bool ok = (okb >> jj) & 1;
-            const u32x4 kx = kr[kPaced ? 0 : jj], vx = vr[kPaced ? 0 : jj];
+            const u32x4 kx = kr[0], vx = vr[0];
             *reinterpret_cast<u32x4 *>(ksm + row * kKPitch + cw * 16) = kx;
             *reinterpret_cast<u32x4 *>(vs + row * kVPitch + cw * 16) =
                 ok ? vx : u32x4{0, 0, 0, 0};
@@ -370,12 +419,10 @@ __device__ __forceinline__ void gather_chunk(
                 *reinterpret_cast<u32x4 *>(k_out + e) = kx;
                 *reinterpret_cast<u32x4 *>(v_out + e) = vx;
             }
-            if constexpr (kPaced) {
-                __asm__ volatile("" ::: "memory");   // keep the next pair behind this one
-                if (jj + 1 < 16) {
-                    kr[0] = *reinterpret_cast<const u32x4 *>(kp + off[jj + 1]);
-                    vr[0] = *reinterpret_cast<const u32x4 *>(vp + off[jj + 1]);
-                }
+            __asm__ volatile("" ::: "memory");   // keep the next pair behind this one
+            if (jj + 1 < 16) {
+                kr[0] = *reinterpret_cast<const u32x4 *>(kp + off[jj + 1]);
+                vr[0] = *reinterpret_cast<const u32x4 *>(vp + off[jj + 1]);
             }
         }
         __syncthreads();   // sub-tile t's K and V rows are in LDS
@@ -404,7 +451,7 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
     int ids_head_stride, int kk, int chunks_per_wg, uint16_t *__restrict__ k_out,
     uint16_t *__restrict__ v_out, float scale_log2, float *__restrict__ part)
 {
-    __shared__ __align__(16) unsigned char ksm[kKeys * kKPitch];
+    __shared__ __align__(16) unsigned char ksm[kPaced ? kKeys * kKPitch : 16];   // unpaced: unused
     __shared__ __align__(16) unsigned char vs[kKeys * kVPitch];
     __shared__ __align__(16) float ps[16][16];
     __shared__ __align__(16) float as[16];
@@ -425,18 +472,41 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
     ChunkState st;
     state_init(st);
     if constexpr (kLoop) {
+        // Chunk c + 1's ids are loaded before chunk c's rows and its table entries right after
+        // them, so neither lookup waits in line in front of the next chunk's row loads.
         const int c0 = x * chunks_per_wg, c1 = min(c0 + chunks_per_wg, n_chunks);
+        const int n_kv = kk * bt;
+        int64_t id = hid[min((int)((uint32_t)(c0 * kKeys) / (uint32_t)bt) + lane, kk - 1)];
+        uint32_t pg;
+        bool in;
+        int32_t ent = table_entry(id, rsm, pg, in);
         for (int c = c0; c < c1; c++) {
             if (c != c0)
                 __syncthreads();   // the previous chunk's LDS rows are no longer read
-            gather_chunk<kBf16, kPaced>(kp, vp, rsm, hoff, token_stride, bt, hid, kk,
-                                        c * kKeys, nullptr, nullptr, 0, qa, group, scale_log2, ksm, vs, ps, as, st,
-                                lane);
+            const int64_t sbase = slot_offset_from(id, in, pg, ent, rsm);
+            const bool more = c + 1 < c1;
+            const int s1 = (int)((uint32_t)min((c + 1) * kKeys, n_kv - 1) / (uint32_t)bt);
+            const int64_t id_n = hid[min(s1 + lane, kk - 1)];
+            uint32_t pg_n = 0;
+            bool in_n = false;
+            int32_t ent_n = 0;
+            gather_chunk<kBf16, kPaced>(kp, vp, sbase, hoff, token_stride, bt, kk, c * kKeys,
+                                        nullptr, nullptr, 0, qa, group, scale_log2, ksm, vs, ps,
+                                        as, st, lane, [&] {
+                                            if (more)
+                                                ent_n = table_entry(id_n, rsm, pg_n, in_n);
+                                        });
+            id = id_n;
+            pg = pg_n;
+            in = in_n;
+            ent = ent_n;
         }
     } else {
-        gather_chunk<kBf16, kPaced>(kp, vp, rsm, hoff, token_stride, bt, hid, kk, x * kKeys, k_out,
-                            v_out, (int64_t)h * kk * bt, qa, group, scale_log2, ksm, vs, ps, as,
-                            st, lane);
+        const int s0 = (int)((uint32_t)(x * kKeys) / (uint32_t)bt);
+        const int64_t sbase = slot_offset(hid[min(s0 + lane, kk - 1)], rsm);
+        gather_chunk<kBf16, kPaced>(kp, vp, sbase, hoff, token_stride, bt, kk, x * kKeys, k_out,
+                                    v_out, (int64_t)h * kk * bt, qa, group, scale_log2, ksm, vs,
+                                    ps, as, st, lane, [] {});
     }
     write_partial(st, group,
                   part + (((int64_t)row * kvh + h) * n_split + x) * group * (kHd + 2), lane);
