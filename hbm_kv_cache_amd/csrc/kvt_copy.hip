@@ -5,7 +5,9 @@
 //   * KERNEL: each wavefront owns one 8 KiB chunk of one descriptor.  It reads the descriptor
 //     and reads the chunk one 1 KiB wave-load at a time (16 bytes per lane), then stores it,
 //     so thousands of waves keep ~1 MiB or more in flight without flooding the link.  Descriptors whose
-//     addresses are only 8-byte aligned take an 8-byte path, anything else a byte path.
+//     addresses are only 8-byte aligned take an 8-byte path, anything else a byte path.  When
+//     no page exceeds a chunk, a wave takes eight consecutive descriptors instead, read with
+//     one load (copy_small_kernel).
 //   * SDMA: the copy engines, through hipMemcpyBatchAsync (one submission for the batch),
 //     falling back to one hipMemcpyAsync per descriptor where the batch call is unavailable.
 // kvt_stage_tail (llama-T tail staging) is one contiguous range: a single SDMA copy or the
@@ -97,6 +99,39 @@ __global__ __launch_bounds__(256) void copy_desc_kernel(const uint64_t *__restri
         return;
     const uint64_t len = sz - off < (uint64_t)kChunk ? sz - off : (uint64_t)kChunk;
     wave_copy_chunk(src[i] + off, dst[i] + off, len, lane);
+}
+
+// Pages of at most one chunk: one wave per group of kGroup consecutive descriptors.  Lanes
+// 0..23 read the group's src, dst and size entries with one load instruction -- three
+// 64-byte lines of each table instead of a line per descriptor and table, which for 512-byte
+// pages would cost the link a third of the payload again -- and the wave then copies the
+// group's pages one after another, taking each descriptor from those lanes.
+constexpr int kGroup = 8;
+
+__global__ __launch_bounds__(256) void copy_small_kernel(const uint64_t *__restrict__ src,
+                                                         const uint64_t *__restrict__ dst,
+                                                         const uint64_t *__restrict__ sizes,
+                                                         int64_t n)
+{
+    const int lane = threadIdx.x & (kvt::kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t i0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kGroup;
+    if (i0 >= n)
+        return;
+    const int tab = lane / kGroup, j = lane % kGroup;
+    uint64_t v = 0;
+    if (tab < 3 && i0 + j < n)
+        v = (tab == 0 ? src : tab == 1 ? dst : sizes)[i0 + j];
+    // lane L's 64-bit value, in scalar registers (the builtin returns a signed int: each half
+    // is taken as uint32_t before widening, so no half is sign-extended into the other)
+    auto lane_u64 = [&](int L) -> uint64_t {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, L);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), L);
+        return ((uint64_t)hi << 32) | (uint64_t)lo;
+    };
+    const int m = n - i0 < kGroup ? (int)(n - i0) : kGroup;
+    for (int k = 0; k < m; k++)
+        wave_copy_chunk(lane_u64(k), lane_u64(kGroup + k), lane_u64(2 * kGroup + k), lane);
 }
 
 // one contiguous range, one wave per 8 KiB chunk
@@ -204,6 +239,17 @@ extern "C" int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const u
     if (!use_kernel)
         return sdma_copies(src, dst, sizes, n, s);
 
+    if (max_size <= (uint64_t)kChunk) {
+        const int64_t groups = (n + kGroup - 1) / kGroup;
+        const int64_t blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (blocks > 0x7fffffff)
+            return kvt::fail(KVT_ERANGE, "kvt_swap_blocks: %lld descriptors exceed one launch",
+                             (long long)n);
+        hipLaunchKernelGGL(copy_small_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst,
+                           sizes, n);
+        KVT_LAUNCHED("copy_small_kernel");
+        return KVT_OK;
+    }
     const uint64_t chunks = (max_size + kChunk - 1) / kChunk;
     if (chunks > 0xffffffffull)
         return kvt::fail(KVT_ERANGE, "kvt_swap_blocks: page of %llu bytes too large",
