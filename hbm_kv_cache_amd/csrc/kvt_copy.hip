@@ -23,33 +23,40 @@ namespace {
 
 constexpr int kChunk = 8192;                      // bytes per wave unit
 constexpr int kWavesPerBlock = 4;                 // 256-thread workgroups
+constexpr int kCopyWaves = 1024;                  // one wave per SIMD: ~1 MiB in flight
+constexpr int kSmallWaves = 2048;                 // small pages: 512 B-8 KiB per wave-load step
 
 constexpr int kWordsPerLane16 = kChunk / 16 / kvt::kWave;  // 8
 constexpr int kWordsPerLane8 = kChunk / 8 / kvt::kWave;    // 16
 
 // One wave copies bytes [off, off+len) of a single range.  off + len <= range size.  The wave
 // has one wave-load (64 lanes x 16 or 8 bytes) in flight at a time -- the empty asm that takes
-// each loaded value makes the wave wait for it before the next load issues -- and stores the
-// chunk after its last load, so no load waits behind a store.  Host reads with every load of a
-// transfer in flight at once ran ~20% below the link rate on MI355X (see kvt_gather.hip);
-// thousands of waves with one wave-load each keep enough in flight.
+// each loaded value makes the wave wait for it before the next load issues.  A whole chunk is
+// stored after its last load, so no load waits behind a store; part of a chunk is copied load,
+// wait, store.  How much is in flight across the chip is set by the number of waves: the
+// kernels below stride a fixed grid over their work (kCopyWaves), as kvt_gather.hip does --
+// host reads with every load of a transfer in flight at once ran ~20% below the link rate on
+// MI355X, and a grid of one wave per SIMD keeps ~1 MiB in flight, which holds the link rate.
 template <typename W, int N>
 __device__ __forceinline__ void wave_copy_words(const W *sp, W *dp, uint32_t nw, int lane)
 {
-    W r[N];
+    if (nw == (uint32_t)N * kvt::kWave) {
+        W r[N];
 #pragma unroll
-    for (int k = 0; k < N; k++) {
-        const uint32_t w = lane + k * kvt::kWave;
-        if (w < nw) {
-            r[k] = __builtin_nontemporal_load(sp + w);
+        for (int k = 0; k < N; k++) {
+            r[k] = __builtin_nontemporal_load(sp + lane + k * kvt::kWave);
             __asm__ volatile("" : : "v"(r[k]) : "memory");
         }
-    }
 #pragma unroll
-    for (int k = 0; k < N; k++) {
-        const uint32_t w = lane + k * kvt::kWave;
-        if (w < nw)
-            dp[w] = r[k];
+        for (int k = 0; k < N; k++)
+            dp[lane + k * kvt::kWave] = r[k];
+    } else {
+#pragma unroll 1
+        for (uint32_t w = lane; w < nw; w += kvt::kWave) {
+            const W v = __builtin_nontemporal_load(sp + w);
+            __asm__ volatile("" : : "v"(v) : "memory");
+            dp[w] = v;
+        }
     }
 }
 
@@ -81,7 +88,7 @@ __device__ __forceinline__ void wave_copy_chunk(uint64_t s, uint64_t d, uint64_t
     }
 }
 
-// unit u = (descriptor i, chunk c) with u = i*chunks + c; one wave per unit
+// unit u = (descriptor i, chunk c) with u = i*chunks + c; each wave strides over units
 __global__ __launch_bounds__(256) void copy_desc_kernel(const uint64_t *__restrict__ src,
                                                         const uint64_t *__restrict__ dst,
                                                         const uint64_t *__restrict__ sizes,
@@ -89,23 +96,22 @@ __global__ __launch_bounds__(256) void copy_desc_kernel(const uint64_t *__restri
 {
     const int lane = threadIdx.x & (kvt::kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    if (u >= n_units)
-        return;
-    const int64_t i = u / chunks;
-    const uint64_t off = (uint64_t)(u - i * chunks) * kChunk;
-    const uint64_t sz = sizes[i];
-    if (off >= sz)
-        return;
-    const uint64_t len = sz - off < (uint64_t)kChunk ? sz - off : (uint64_t)kChunk;
-    wave_copy_chunk(src[i] + off, dst[i] + off, len, lane);
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + wave; u < n_units; u += stride) {
+        const int64_t i = u / chunks;
+        const uint64_t off = (uint64_t)(u - i * chunks) * kChunk;
+        const uint64_t sz = sizes[i];
+        if (off >= sz)
+            continue;
+        const uint64_t len = sz - off < (uint64_t)kChunk ? sz - off : (uint64_t)kChunk;
+        wave_copy_chunk(src[i] + off, dst[i] + off, len, lane);
+    }
 }
 
-// Pages of at most one chunk: one wave per group of kGroup consecutive descriptors.  Lanes
-// 0..23 read the group's src, dst and size entries with one load instruction -- three
-// 64-byte lines of each table instead of a line per descriptor and table, which for 512-byte
-// pages would cost the link a third of the payload again -- and the wave then copies the
-// group's pages one after another, taking each descriptor from those lanes.
+// Pages of at most one chunk: a wave takes kGroup consecutive descriptors at a time.  Lanes
+// 0..23 read the group's src, dst and size entries with one load instruction -- three 64-byte
+// lines of the tables instead of a line per descriptor and table -- and the wave then copies
+// the group's pages one after another, taking each descriptor from those lanes.
 constexpr int kGroup = 8;
 
 __global__ __launch_bounds__(256) void copy_small_kernel(const uint64_t *__restrict__ src,
@@ -115,35 +121,44 @@ __global__ __launch_bounds__(256) void copy_small_kernel(const uint64_t *__restr
 {
     const int lane = threadIdx.x & (kvt::kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t i0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kGroup;
-    if (i0 >= n)
-        return;
     const int tab = lane / kGroup, j = lane % kGroup;
-    uint64_t v = 0;
-    if (tab < 3 && i0 + j < n)
-        v = (tab == 0 ? src : tab == 1 ? dst : sizes)[i0 + j];
-    // lane L's 64-bit value, in scalar registers (the builtin returns a signed int: each half
-    // is taken as uint32_t before widening, so no half is sign-extended into the other)
-    auto lane_u64 = [&](int L) -> uint64_t {
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, L);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), L);
-        return ((uint64_t)hi << 32) | (uint64_t)lo;
-    };
-    const int m = n - i0 < kGroup ? (int)(n - i0) : kGroup;
-    for (int k = 0; k < m; k++)
-        wave_copy_chunk(lane_u64(k), lane_u64(kGroup + k), lane_u64(2 * kGroup + k), lane);
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock * kGroup;
+    for (int64_t i0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave) * kGroup; i0 < n;
+         i0 += stride) {
+        uint64_t v = 0;
+        if (tab < 3 && i0 + j < n)
+            v = (tab == 0 ? src : tab == 1 ? dst : sizes)[i0 + j];
+        // lane L's 64-bit value, in scalar registers (the builtin returns a signed int: each
+        // half is taken as uint32_t before widening, so no half is sign-extended into the other)
+        auto lane_u64 = [&](int L) -> uint64_t {
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, L);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), L);
+            return ((uint64_t)hi << 32) | (uint64_t)lo;
+        };
+        const int m = n - i0 < kGroup ? (int)(n - i0) : kGroup;
+        for (int k = 0; k < m; k++)
+            wave_copy_chunk(lane_u64(k), lane_u64(kGroup + k), lane_u64(2 * kGroup + k), lane);
+    }
 }
 
-// one contiguous range, one wave per 8 KiB chunk
+// one contiguous range, 8 KiB chunks; each wave strides over chunks
 __global__ __launch_bounds__(256) void copy_span_kernel(uint64_t src, uint64_t dst, uint64_t bytes)
 {
     const int lane = threadIdx.x & (kvt::kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint64_t off = ((uint64_t)blockIdx.x * kWavesPerBlock + wave) * kChunk;
-    if (off >= bytes)
-        return;
-    const uint64_t len = bytes - off < (uint64_t)kChunk ? bytes - off : (uint64_t)kChunk;
-    wave_copy_chunk(src + off, dst + off, len, lane);
+    const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock * kChunk;
+    for (uint64_t off = ((uint64_t)blockIdx.x * kWavesPerBlock + wave) * kChunk; off < bytes;
+         off += stride) {
+        const uint64_t len = bytes - off < (uint64_t)kChunk ? bytes - off : (uint64_t)kChunk;
+        wave_copy_chunk(src + off, dst + off, len, lane);
+    }
+}
+
+// workgroups for `units` wave units, at most `cap` waves
+unsigned copy_groups(uint64_t units, int cap)
+{
+    const uint64_t waves = units < (uint64_t)cap ? units : (uint64_t)cap;
+    return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
 // AUTO policy: vLLM-CPU _select_swap_blocks_fn keeps a kernel for small 8-byte-multiple pages
@@ -240,13 +255,9 @@ extern "C" int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const u
         return sdma_copies(src, dst, sizes, n, s);
 
     if (max_size <= (uint64_t)kChunk) {
-        const int64_t groups = (n + kGroup - 1) / kGroup;
-        const int64_t blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
-        if (blocks > 0x7fffffff)
-            return kvt::fail(KVT_ERANGE, "kvt_swap_blocks: %lld descriptors exceed one launch",
-                             (long long)n);
-        hipLaunchKernelGGL(copy_small_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst,
-                           sizes, n);
+        const uint64_t groups = (uint64_t)(n + kGroup - 1) / kGroup;
+        hipLaunchKernelGGL(copy_small_kernel, dim3(copy_groups(groups, kSmallWaves)), dim3(256),
+                           0, s, src, dst, sizes, n);
         KVT_LAUNCHED("copy_small_kernel");
         return KVT_OK;
     }
@@ -255,12 +266,11 @@ extern "C" int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const u
         return kvt::fail(KVT_ERANGE, "kvt_swap_blocks: page of %llu bytes too large",
                          (unsigned long long)max_size);
     const int64_t units = n * (int64_t)chunks;
-    const int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks > 0x7fffffff)
-        return kvt::fail(KVT_ERANGE, "kvt_swap_blocks: %lld wave units exceed one launch",
-                         (long long)units);
-    hipLaunchKernelGGL(copy_desc_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst,
-                       sizes, units, (uint32_t)chunks);
+    if (units / (int64_t)chunks != n)
+        return kvt::fail(KVT_ERANGE, "kvt_swap_blocks: %lld descriptors of %llu chunks overflow",
+                         (long long)n, (unsigned long long)chunks);
+    hipLaunchKernelGGL(copy_desc_kernel, dim3(copy_groups((uint64_t)units, kCopyWaves)),
+                       dim3(256), 0, s, src, dst, sizes, units, (uint32_t)chunks);
     KVT_LAUNCHED("copy_desc_kernel");
     return KVT_OK;
 }
@@ -287,12 +297,8 @@ extern "C" int kvt_stage_tail(const void *plane, int64_t row_bytes, int64_t row_
                                hipMemcpyDefault, s));
         return KVT_OK;
     }
-    const uint64_t blocks = (bytes + (uint64_t)kChunk * kWavesPerBlock - 1) /
-                            ((uint64_t)kChunk * kWavesPerBlock);
-    if (blocks > 0x7fffffffull)
-        return kvt::fail(KVT_ERANGE, "kvt_stage_tail: %llu bytes exceed one launch",
-                         (unsigned long long)bytes);
-    hipLaunchKernelGGL(copy_span_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, bytes);
+    hipLaunchKernelGGL(copy_span_kernel, dim3(copy_groups((bytes + kChunk - 1) / kChunk, kCopyWaves)),
+                       dim3(256), 0, s, src, dst, bytes);
     KVT_LAUNCHED("copy_span_kernel");
     return KVT_OK;
 }
