@@ -94,21 +94,25 @@ __device__ __forceinline__ void load_raw(const unsigned char *k_head, const unsi
                                          int64_t n_head, int64_t n_kv, int64_t row_bytes, int tile,
                                          uint64_t (&rq)[kRawPerThread])
 {
+    // the tile's first key in each tier, as scalar bases; per word only a 32-bit row offset
+    const int64_t key0 = (int64_t)tile * kKT;
+    const int kmax = (int)((n_kv - 1 - key0) < kKT - 1 ? (n_kv - 1 - key0) : kKT - 1);
+    const int khead = (int)((n_head - key0) < kKT ? (n_head - key0) : kKT);   // keys < khead: head
+    const unsigned char *hk = k_head + key0 * row_bytes, *hv = v_head + key0 * row_bytes;
+    const unsigned char *tk = k_tail + (key0 - n_head) * row_bytes;
+    const unsigned char *tv = v_tail + (key0 - n_head) * row_bytes;
 #pragma unroll
     for (int u = 0; u < kRawPerThread; u++) {
         const int f = threadIdx.x + u * kThreads;
         if (f < kRawWords) {
             const int plane = f >= kRawWords / 2;
             const int rem = f - plane * (kRawWords / 2);
-            const int kin = rem / (kHeadBytes / 8), w = rem - kin * (kHeadBytes / 8);
-            int64_t key = (int64_t)tile * kKT + kin;
-            key = key < n_kv ? key : n_kv - 1;
-            const bool in_head = key < n_head;
-            const unsigned char *hb = plane ? v_head : k_head;
-            const unsigned char *tb = plane ? v_tail : k_tail;
-            const unsigned char *rowp = in_head ? hb + key * row_bytes
-                                                : tb + (key - n_head) * row_bytes;
-            rq[u] = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(rowp + 8 * w));
+            int kin = rem / (kHeadBytes / 8);
+            const int w = rem - kin * (kHeadBytes / 8);
+            kin = kin < kmax ? kin : kmax;
+            const unsigned char *base = kin < khead ? (plane ? hv : hk) : (plane ? tv : tk);
+            const uint32_t off = (uint32_t)kin * (uint32_t)row_bytes + 8u * (uint32_t)w;
+            rq[u] = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(base + off));
         }
     }
 }
