@@ -558,7 +558,7 @@ extern "C" int kvt_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t
                                size_t ws_bytes, void *stream)
 {
     if (hd != kHd)
-        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_decode: hd=%d (this build: 128)", hd);
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_decode: hd=%d (supported: 128)", hd);
     if (n_qh < 1 || kvh < 1 || n_qh % kvh || n_qh / kvh > 16 || kvh > 65535 || n_kv < 0)
         return kvt::fail(KVT_EINVAL, "kvt_attn_decode: n_qh=%d kvh=%d n_kv=%lld", n_qh, kvh,
                          (long long)n_kv);
@@ -609,7 +609,7 @@ extern "C" int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, 
                                       void *stream)
 {
     if (hd != kHd)
-        return kvt::fail(KVT_EUNSUPPORTED, "kvt_gather_attn_decode: hd=%d (this build: 128)", hd);
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_gather_attn_decode: hd=%d (supported: 128)", hd);
     if (dtype != KVT_BF16 && dtype != KVT_F16)
         return kvt::fail(KVT_EUNSUPPORTED, "kvt_gather_attn_decode: dtype=%d", dtype);
     if (n_qh < 1 || kvh < 1 || n_qh % kvh || n_qh / kvh > 16 || kvh > 65535 || bt < 1 || k < 1 ||
@@ -722,7 +722,7 @@ struct RowsArgs {
 int check_rows(const char *fn, const RowsArgs &a)
 {
     if (a.hd != kHd)
-        return kvt::fail(KVT_EUNSUPPORTED, "%s: hd=%d (this build: 128)", fn, a.hd);
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: hd=%d (supported: 128)", fn, a.hd);
     if (a.dtype != KVT_BF16 && a.dtype != KVT_F16)
         return kvt::fail(KVT_EUNSUPPORTED, "%s: dtype=%d", fn, a.dtype);
     if (a.rows < 0 || a.rows > 65535 || a.n_qh < 1 || a.kvh < 1 || a.n_qh % a.kvh ||

@@ -385,14 +385,14 @@ int check_prefill(const char *fn, const void *q, int64_t n_q, int64_t q_pos0, in
                   float scale, const float *out, int &group, int64_t &q_tiles)
 {
     if (kv_format != KVT_Q8_0)
-        return kvt::fail(KVT_EUNSUPPORTED, "%s: kv_format=%d (this build: Q8_0)", fn, kv_format);
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: kv_format=%d (supported: Q8_0)", fn, kv_format);
     if (hd != kHd)
-        return kvt::fail(KVT_EUNSUPPORTED, "%s: hd=%d (this build: 128)", fn, hd);
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: hd=%d (supported: 128)", fn, hd);
     if (kvh < 1 || n_qh < 1 || n_qh % kvh)
         return kvt::fail(KVT_EINVAL, "%s: n_qh=%d kvh=%d", fn, n_qh, kvh);
     group = n_qh / kvh;
     if (group != 1 && group != 2 && group != 4 && group != 8)
-        return kvt::fail(KVT_EUNSUPPORTED, "%s: group %d (this build: 1, 2, 4, 8)", fn, group);
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: group %d (supported: 1, 2, 4, 8)", fn, group);
     if (!(scale > 0.f))
         return kvt::fail(KVT_EINVAL, "%s: scale must be positive", fn);
     if (n_q < 0 || q_pos0 < 0 || n_kv < 0 || n_head < 0 || n_head > n_kv)

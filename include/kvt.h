@@ -64,7 +64,7 @@ extern "C" {
 #define KVT_EALIGN (-3)       /* an address or size misaligned for the requested path */
 #define KVT_EOVERLAP (-4)     /* overlapping copy ranges (only when validation is asked for) */
 #define KVT_ENOMEM (-5)       /* pinned host allocation failed */
-#define KVT_EUNSUPPORTED (-6) /* a valid request this build does not implement */
+#define KVT_EUNSUPPORTED (-6) /* a valid request the library does not implement */
 #define KVT_EHIP (-7)         /* a HIP runtime call failed; kvt_last_error() has its text */
 
 /* copy direction and mechanism */
