@@ -296,7 +296,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by layer or KV head with no exchange; see the design notes)",
+              "(each GPU would run its own layers or KV heads over its own host link, with no "
+              "exchange inside this path)",
               file=sys.stderr)
         sys.exit(2)
     import torch
