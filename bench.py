@@ -630,6 +630,21 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
     p_one = pipe_ms(2 * n_tail)          # the whole tail in one bucket
     p_arena = pipe_ms(2 * 16384)         # bounded arena: buckets of 16,384 rows (17.8 MB/plane)
     st = min(st_sdma, st_kernel)
+    # the same op over fp16 and bf16 caches (N(0,1) values, 2 bytes each), whole cache in HBM
+    fp_ms = {}
+    for fmt, name, dt in ((kvt.F16, "f16", torch.float16), (kvt.BF16, "bf16", torch.bfloat16)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        kf = torch.randn((n_kv, kvh * hd), generator=g, device=dev).to(dt)
+        vf = torch.randn((n_kv, kvh * hd), generator=g, device=dev).to(dt)
+        ms = []
+        for _ in range(reps):
+            t.start()
+            kvt.kvt_attn_prefill(q, n_q, q_pos0, n_qh, kvh, hd, kf, vf, n_kv, None, None, n_kv,
+                                 fmt, 1, scale, out)
+            ms.append(t.stop_ms())
+        fp_ms[name] = _median(ms)
+        del kf, vf
     res = {
         "n_kv": n_kv, "n_head": n_head, "n_q": n_q, "q_heads": n_qh, "kv_heads": kvh,
         "stage_bytes": stage_bytes, "flops": flops,
@@ -646,6 +661,8 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
         "pipelined_one_bucket_ms": round(p_one, 4),
         "pipelined_arena_16384_ms": round(p_arena, 4),
         "prefill_tok_s_pipelined": round(n_q / (min(p_one, p_arena) * 1e-3), 1),
+        "attn_all_hbm_f16_cache_ms": round(fp_ms["f16"], 4),
+        "attn_all_hbm_bf16_cache_ms": round(fp_ms["bf16"], 4),
     }
     log("prefill", res)
     del ht

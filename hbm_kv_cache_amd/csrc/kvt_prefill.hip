@@ -40,16 +40,22 @@ constexpr int kKT = 64;                        // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlk = 34;                       // q8_0 block: fp16 scale + 32 int8
-constexpr int kHeadBytes = (kHd / 32) * kBlk;  // one head's slice of a row: 136 bytes
 constexpr int kKPitch = kHd * 2 + 16;          // LDS bytes per dequantised K row (272)
 constexpr int kVtPitch = kKT * 2 + 8;          // LDS bytes per dequantised V^T row (136)
 constexpr int kLdsK = kKT * kKPitch;
 constexpr int kLdsV = kHd * kVtPitch;
 constexpr int kLdsBuf = kLdsK + kLdsV;         // one tile, K and V^T
-constexpr int kRawPlane = kKT * kHeadBytes;    // one plane's head slices of a tile (8704 B)
-constexpr int kRawBytes = 2 * kRawPlane;       // K and V
-constexpr int kRawWords = kRawBytes / 8;       // 8-byte words per tile (2176)
-constexpr int kRawPerThread = (kRawWords + kThreads - 1) / kThreads;
+// The raw (as stored) tile per cache format: one head's slice of a row is four q8_0 blocks
+// (136 bytes) or 128 fp16 / bf16 values (256 bytes).
+constexpr int head_bytes(int fmt) { return fmt == KVT_Q8_0 ? (kHd / 32) * kBlk : kHd * 2; }
+template <int F>
+struct Raw {
+    static constexpr int kHeadBytes = head_bytes(F);
+    static constexpr int kPlane = kKT * kHeadBytes;                  // one plane's slices of a tile
+    static constexpr int kBytes = 2 * kPlane;                        // K and V
+    static constexpr int kWords = kBytes / 8;                        // 8-byte words per tile
+    static constexpr int kPerThread = (kWords + kThreads - 1) / kThreads;
+};
 constexpr int kOutPitch = 33;                  // floats per row of the output transpose buffer
 static_assert(kWaves * 32 * kOutPitch * 4 <= 2 * kLdsBuf, "output staging reuses the tiles");
 
@@ -89,11 +95,13 @@ __device__ __forceinline__ void dequant_block(const uint32_t w[9], bool odd, uin
 // Coalesced 8-byte loads of tile `tile`: word f is plane f / 1088, key (f % 1088) / 17,
 // byte 8 * (f % 17) of that key's 136-byte head slice.
 // k_head ... v_tail already point at this workgroup's head slice (offset h * 136 added).
+template <int F>
 __device__ __forceinline__ void load_raw(const unsigned char *k_head, const unsigned char *v_head,
                                          const unsigned char *k_tail, const unsigned char *v_tail,
                                          int64_t n_head, int64_t n_kv, int64_t row_bytes, int tile,
-                                         uint64_t (&rq)[kRawPerThread])
+                                         uint64_t (&rq)[Raw<F>::kPerThread])
 {
+    using R = Raw<F>;
     // the tile's first key in each tier, as scalar bases; per word only a 32-bit row offset
     const int64_t key0 = (int64_t)tile * kKT;
     const int kmax = (int)((n_kv - 1 - key0) < kKT - 1 ? (n_kv - 1 - key0) : kKT - 1);
@@ -102,13 +110,13 @@ __device__ __forceinline__ void load_raw(const unsigned char *k_head, const unsi
     const unsigned char *tk = k_tail + (key0 - n_head) * row_bytes;
     const unsigned char *tv = v_tail + (key0 - n_head) * row_bytes;
 #pragma unroll
-    for (int u = 0; u < kRawPerThread; u++) {
+    for (int u = 0; u < R::kPerThread; u++) {
         const int f = threadIdx.x + u * kThreads;
-        if (f < kRawWords) {
-            const int plane = f >= kRawWords / 2;
-            const int rem = f - plane * (kRawWords / 2);
-            int kin = rem / (kHeadBytes / 8);
-            const int w = rem - kin * (kHeadBytes / 8);
+        if (f < R::kWords) {
+            const int plane = f >= R::kWords / 2;
+            const int rem = f - plane * (R::kWords / 2);
+            int kin = rem / (R::kHeadBytes / 8);
+            const int w = rem - kin * (R::kHeadBytes / 8);
             kin = kin < kmax ? kin : kmax;
             const unsigned char *base = kin < khead ? (plane ? hv : hk) : (plane ? tv : tk);
             const uint32_t off = (uint32_t)kin * (uint32_t)row_bytes + 8u * (uint32_t)w;
@@ -118,31 +126,58 @@ __device__ __forceinline__ void load_raw(const unsigned char *k_head, const unsi
 }
 
 // Word f goes to byte 8*f: the raw tile in LDS is [plane][key][136 bytes].
-__device__ __forceinline__ void store_raw(unsigned char *rawbuf, const uint64_t (&rq)[kRawPerThread])
+template <int F>
+__device__ __forceinline__ void store_raw(unsigned char *rawbuf,
+                                          const uint64_t (&rq)[Raw<F>::kPerThread])
 {
 #pragma unroll
-    for (int u = 0; u < kRawPerThread; u++) {
+    for (int u = 0; u < Raw<F>::kPerThread; u++) {
         const int f = threadIdx.x + u * kThreads;
-        if (f < kRawWords)
+        if (f < Raw<F>::kWords)
             *reinterpret_cast<uint64_t *>(rawbuf + 8 * f) = rq[u];
     }
 }
 
-// Thread (plane = wave / 4, block = wave % 4, key = lane) dequantises its q8_0 block of the raw
-// tile into the fp16 tile: K as rows [key][d], V transposed [d][key].
+// Thread (plane = wave / 4, block = wave % 4, key = lane) turns its 32 values of the raw tile
+// into fp16 in the tile used by the MFMA: K as rows [key][d], V transposed [d][key].  q8_0:
+// the block's dequantisation; fp16: the values as stored; bf16: each value converted to fp16,
+// which is exact for magnitudes in [2^-17, 65504] (bf16 carries 8 significant bits; below 2^-17
+// the fp16 subnormal spacing of 2^-24 rounds, and beyond 65504 the result is infinite).
+template <int F>
 __device__ __forceinline__ void dequant_tile(const unsigned char *rawbuf, unsigned char *buf,
                                              int wave, int lane)
 {
+    using R = Raw<F>;
     const bool is_v = wave >= 4;
     const int blk = wave & 3;
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(
-        rawbuf + (is_v ? kRawPlane : 0) + lane * kHeadBytes + 4 * ((kBlk * blk) >> 2));
-    uint32_t w[9];
-#pragma unroll
-    for (int k = 0; k < 9; k++)
-        w[k] = src[k];
     uint32_t d[16];
-    dequant_block(w, blk & 1, d);
+    if constexpr (F == KVT_Q8_0) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(
+            rawbuf + (is_v ? R::kPlane : 0) + lane * R::kHeadBytes + 4 * ((kBlk * blk) >> 2));
+        uint32_t w[9];
+#pragma unroll
+        for (int k = 0; k < 9; k++)
+            w[k] = src[k];
+        dequant_block(w, blk & 1, d);
+    } else {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(
+            rawbuf + (is_v ? R::kPlane : 0) + lane * R::kHeadBytes + blk * 64);
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const u32x4 x = src[c];
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                d[4 * c + e] = x[e];
+        }
+        if constexpr (F == KVT_BF16) {
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                const float lo = __builtin_bit_cast(float, d[k] << 16);
+                const float hi = __builtin_bit_cast(float, d[k] & 0xffff0000u);
+                d[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, h2));
+            }
+        }
+    }
     if (!is_v) {
         unsigned char *kdst = buf + lane * kKPitch + blk * 64;
 #pragma unroll
@@ -158,7 +193,8 @@ __device__ __forceinline__ void dequant_tile(const unsigned char *rawbuf, unsign
     }
 }
 
-__global__ __launch_bounds__(kThreads) void prefill_q8_0(
+template <int F>
+__global__ __launch_bounds__(kThreads) void prefill_attn(
     const _Float16 *__restrict__ q, int64_t n_q, int64_t q_pos0, int n_qh, int kvh, int group,
     const unsigned char *__restrict__ k_head, const unsigned char *__restrict__ v_head,
     int64_t n_head, const unsigned char *__restrict__ k_tail,
@@ -166,8 +202,9 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     int tile_begin, int tile_cap, float *__restrict__ state, int first, int last,
     float *__restrict__ out)
 {
-    __shared__ __align__(16) unsigned char lds[2 * kLdsBuf + 2 * kRawBytes];
-    unsigned char *const lds_raw = lds + 2 * kLdsBuf;   // two raw (q8_0) tiles
+    using R = Raw<F>;
+    __shared__ __align__(16) unsigned char lds[2 * kLdsBuf + 2 * R::kBytes];
+    unsigned char *const lds_raw = lds + 2 * kLdsBuf;   // two raw (as stored) tiles
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, i = lane & 31;
@@ -179,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     const int64_t t_first = q_base + 32 * (wave / group);
     const int64_t t_i = t_first + i;                // this lane's query row
     const int64_t t_ld = t_i < n_q ? t_i : n_q - 1;
-    const int64_t row_bytes = (int64_t)kvh * kHeadBytes;
+    const int64_t row_bytes = (int64_t)kvh * R::kHeadBytes;
 
     // last key any query of the workgroup / of this wave may see
     auto last_key_for = [&](int64_t t_last) -> int64_t {
@@ -222,26 +259,26 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
     }
 
     // the four cache bases, moved to this workgroup's head slice
-    const unsigned char *kh = k_head + h * kHeadBytes, *vh = v_head + h * kHeadBytes;
-    const unsigned char *kt = k_tail + h * kHeadBytes, *vt = v_tail + h * kHeadBytes;
-    uint64_t rq[kRawPerThread];
+    const unsigned char *kh = k_head + h * R::kHeadBytes, *vh = v_head + h * R::kHeadBytes;
+    const unsigned char *kt = k_tail + h * R::kHeadBytes, *vt = v_tail + h * R::kHeadBytes;
+    uint64_t rq[R::kPerThread];
 
     // prologue: raw tile b -> LDS; fp16 tile b and raw tile b+1 ready; loads of b+2 in flight
     // (b = tile_begin; buffers are indexed by tile & 1)
     const int b0 = tile_begin;
     if (n_tiles > b0) {
-        load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
-        store_raw(lds_raw + (b0 & 1) * kRawBytes, rq);
+        load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
+        store_raw<F>(lds_raw + (b0 & 1) * R::kBytes, rq);
         if (n_tiles > b0 + 1)
-            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
+            load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
     }
     __syncthreads();
     if (n_tiles > b0) {
-        dequant_tile(lds_raw + (b0 & 1) * kRawBytes, lds + (b0 & 1) * kLdsBuf, wave, lane);
+        dequant_tile<F>(lds_raw + (b0 & 1) * R::kBytes, lds + (b0 & 1) * kLdsBuf, wave, lane);
         if (n_tiles > b0 + 1)
-            store_raw(lds_raw + ((b0 + 1) & 1) * kRawBytes, rq);
+            store_raw<F>(lds_raw + ((b0 + 1) & 1) * R::kBytes, rq);
         if (n_tiles > b0 + 2)
-            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 2, rq);
+            load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 2, rq);
     }
     __syncthreads();
 
@@ -257,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
         // multiply this one and the lower four after, so on every SIMD one wave's MFMA work
         // meets the other's VALU work.
         if (dequant_first && tile + 1 < n_tiles)
-            dequant_tile(lds_raw + ((tile + 1) & 1) * kRawBytes, lds + ((tile + 1) & 1) * kLdsBuf,
+            dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kLdsBuf,
                          wave, lane);
         if (key0 <= wave_last) {
             // S^T tile: rows = keys 32*st + (lane & 31), columns = this wave's 32 query rows
@@ -338,13 +375,13 @@ __global__ __launch_bounds__(kThreads) void prefill_q8_0(
             }
         }
         if (!dequant_first && tile + 1 < n_tiles)
-            dequant_tile(lds_raw + ((tile + 1) & 1) * kRawBytes, lds + ((tile + 1) & 1) * kLdsBuf,
+            dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kLdsBuf,
                          wave, lane);
         if (tile + 2 < n_tiles)   // last, so the loads of tile + 2 have had the whole tile
-            store_raw(lds_raw + (tile & 1) * kRawBytes, rq);
+            store_raw<F>(lds_raw + (tile & 1) * R::kBytes, rq);
         __syncthreads();
         if (tile + 3 < n_tiles)
-            load_raw(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 3, rq);
+            load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 3, rq);
     }
 
     if (!last) {   // hand the state to the next pass
@@ -384,8 +421,9 @@ int check_prefill(const char *fn, const void *q, int64_t n_q, int64_t q_pos0, in
                   const void *k_tail, const void *v_tail, int64_t n_kv, int32_t kv_format,
                   float scale, const float *out, int &group, int64_t &q_tiles)
 {
-    if (kv_format != KVT_Q8_0)
-        return kvt::fail(KVT_EUNSUPPORTED, "%s: kv_format=%d (supported: Q8_0)", fn, kv_format);
+    if (kv_format != KVT_Q8_0 && kv_format != KVT_F16 && kv_format != KVT_BF16)
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: kv_format=%d (supported: Q8_0, F16, BF16)", fn,
+                         kv_format);
     if (hd != kHd)
         return kvt::fail(KVT_EUNSUPPORTED, "%s: hd=%d (supported: 128)", fn, hd);
     if (kvh < 1 || n_qh < 1 || n_qh % kvh)
@@ -420,18 +458,26 @@ void launch_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, in
                     int group, int64_t q_tiles, const void *k_head, const void *v_head,
                     int64_t n_head, const void *k_tail, const void *v_tail, int64_t n_kv,
                     int causal, float scale, int64_t key_begin, int64_t key_end, float *state,
-                    int first, int last, float *out, hipStream_t s)
+                    int first, int last, float *out, int32_t kv_format, hipStream_t s)
 {
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     const int tile_begin = (int)(key_begin / kKT);
     const int tile_cap = (int)((key_end + kKT - 1) / kKT);
-    hipLaunchKernelGGL(prefill_q8_0, dim3((unsigned)(q_tiles * kvh)), dim3(kThreads), 0, s,
-                       static_cast<const _Float16 *>(q), n_q, q_pos0, n_qh, kvh, group,
-                       static_cast<const unsigned char *>(k_head),
-                       static_cast<const unsigned char *>(v_head), n_head,
-                       static_cast<const unsigned char *>(k_tail),
-                       static_cast<const unsigned char *>(v_tail), n_kv, causal, scale_log2,
-                       tile_begin, tile_cap, state, first, last, out);
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)(q_tiles * kvh)), dim3(kThreads), 0, s,
+                           static_cast<const _Float16 *>(q), n_q, q_pos0, n_qh, kvh, group,
+                           static_cast<const unsigned char *>(k_head),
+                           static_cast<const unsigned char *>(v_head), n_head,
+                           static_cast<const unsigned char *>(k_tail),
+                           static_cast<const unsigned char *>(v_tail), n_kv, causal, scale_log2,
+                           tile_begin, tile_cap, state, first, last, out);
+    };
+    if (kv_format == KVT_Q8_0)
+        launch(prefill_attn<KVT_Q8_0>);
+    else if (kv_format == KVT_F16)
+        launch(prefill_attn<KVT_F16>);
+    else
+        launch(prefill_attn<KVT_BF16>);
 }
 
 // Events of the pipelined entry point, created once per thread and device and then reused:
@@ -478,9 +524,9 @@ extern "C" int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int3
     if (rc != KVT_OK || n_q == 0)
         return rc;
     launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head, k_tail,
-                   v_tail, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out,
+                   v_tail, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out, kv_format,
                    kvt::as_stream(stream));
-    KVT_LAUNCHED("prefill_q8_0");
+    KVT_LAUNCHED("prefill_attn");
     return KVT_OK;
 }
 
@@ -528,8 +574,8 @@ extern "C" int kvt_attn_prefill_range(const void *q, int64_t n_q, int64_t q_pos0
         return KVT_OK;
     launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head, k_tail,
                    v_tail, n_kv, causal, scale, key_begin, key_end, static_cast<float *>(state),
-                   first, last, out, kvt::as_stream(stream));
-    KVT_LAUNCHED("prefill_q8_0");
+                   first, last, out, kv_format, kvt::as_stream(stream));
+    KVT_LAUNCHED("prefill_attn");
     return KVT_OK;
 }
 
@@ -557,8 +603,9 @@ extern "C" int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_
         return KVT_OK;
     if (n_head == n_kv) {   // nothing in host memory
         launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
-                       nullptr, nullptr, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out, s);
-        KVT_LAUNCHED("prefill_q8_0");
+                       nullptr, nullptr, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out,
+                       kv_format, s);
+        KVT_LAUNCHED("prefill_attn");
         return KVT_OK;
     }
     const int64_t slot_keys = arena_rows / 2 / kKT * kKT;
@@ -577,7 +624,7 @@ extern "C" int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_
     hipEvent_t *ev = nullptr;
     if (pipe_events(ev) != KVT_OK)
         return KVT_EHIP;
-    const int64_t row_bytes = (int64_t)kvh * kHeadBytes;
+    const int64_t row_bytes = (int64_t)kvh * head_bytes(kv_format);
     const uintptr_t ak = reinterpret_cast<uintptr_t>(arena_k);
     const uintptr_t av = reinterpret_cast<uintptr_t>(arena_v);
     const uintptr_t hk = reinterpret_cast<uintptr_t>(k_host);
@@ -592,8 +639,9 @@ extern "C" int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_
     bool started = false;
     if (hb > 0) {
         launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
-                       nullptr, nullptr, n_kv, causal, scale, 0, hb, stf, 1, 0, out, s);
-        KVT_LAUNCHED("prefill_q8_0");
+                       nullptr, nullptr, n_kv, causal, scale, 0, hb, stf, 1, 0, out, kv_format,
+                       s);
+        KVT_LAUNCHED("prefill_attn");
         started = true;
     }
     int b = 0;
@@ -619,8 +667,8 @@ extern "C" int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_
         launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
                        reinterpret_cast<const void *>(sk - shift),
                        reinterpret_cast<const void *>(sv - shift), n_kv, causal, scale, kb, ke,
-                       stf, started ? 0 : 1, ke == n_kv ? 1 : 0, out, s);
-        KVT_LAUNCHED("prefill_q8_0");
+                       stf, started ? 0 : 1, ke == n_kv ? 1 : 0, out, kv_format, s);
+        KVT_LAUNCHED("prefill_attn");
         started = true;
         KVT_HIP(hipEventRecord(ev[3 + slot], s));
     }

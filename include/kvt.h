@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 7
+#define KVT_ABI_VERSION 8
 
 /* status codes */
 #define KVT_OK 0
@@ -308,7 +308,10 @@ int kvt_sparse_attend_rows_auto(const void *q, int32_t rows, int32_t n_qh, int32
  *          (KVT_Q8_0: hd/32 blocks of 34 bytes per head, head-major)
  *   causal nonzero: row t sees keys j <= q_pos0 + t (j < n_kv); zero: all n_kv keys
  *   out    device fp32 [n_q][n_qh][hd]
- * Limits: kv_format KVT_Q8_0, hd == 128, n_qh/kvh in {1, 2, 4, 8}, scale > 0; q and out 16-byte aligned,
+ *   kv_format KVT_Q8_0, KVT_F16 or KVT_BF16.  Products run on fp16 MFMA: q8_0 values are
+ *          dequantised to fp16 (one rounding), fp16 values are used as stored, bf16 values are
+ *          converted to fp16 (exact for magnitudes in [2^-17, 65504]; larger ones overflow).
+ * Limits: hd == 128, n_qh/kvh in {1, 2, 4, 8}, scale > 0; q and out 16-byte aligned,
  * K/V pointers 8-byte aligned.  Deterministic: the same inputs give the same bits, however
  * the rows are split between head and tail.
  * ---------------------------------------------------------------------------------------- */
@@ -347,7 +350,8 @@ int kvt_attn_prefill_range(const void *q, int64_t n_q, int64_t q_pos0, int32_t n
  * copies the first bucket of host rows into one half of the arena; then each bucket is
  * attended from its arena half while the next bucket is copied into the other half.
  *   k_host, v_host      device aliases of the host tail: row r >= n_head at
- *                       k_host + (r - n_head)*row_bytes (row_bytes = kvh*136 for q8_0, hd 128)
+ *                       k_host + (r - n_head)*row_bytes (row_bytes = kvh*136 for q8_0 and
+ *                       kvh*256 for fp16 / bf16, at hd 128)
  *   arena_k, arena_v    device (HBM), arena_rows rows each (>= 128); buckets are
  *                       floor(arena_rows/2 / 64)*64 keys
  *   state               as kvt_attn_prefill_range (required)

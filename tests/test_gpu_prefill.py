@@ -17,18 +17,29 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _cache(n_kv, kvh, seed):
-    k = synth.q8_0_rows(synth.rng(5, synth.P_K, seed), n_kv, kvh, 128)
-    v = synth.q8_0_rows(synth.rng(5, synth.P_V, seed), n_kv, kvh, 128)
+ORACLE_FMT = {kvt.Q8_0: oracle.Q8_0, kvt.F16: oracle.F16, kvt.BF16: oracle.BF16}
+FMT_IDS = {kvt.Q8_0: "q8_0", kvt.F16: "f16", kvt.BF16: "bf16"}
+
+
+def _cache(n_kv, kvh, seed, fmt=kvt.Q8_0):
+    """K and V rows as uint8 [n_kv][row bytes]: q8_0 blocks, or N(0,1) fp16 / bf16 values."""
+    if fmt == kvt.Q8_0:
+        k = synth.q8_0_rows(synth.rng(5, synth.P_K, seed), n_kv, kvh, 128)
+        v = synth.q8_0_rows(synth.rng(5, synth.P_V, seed), n_kv, kvh, 128)
+        return k, v
+    gen = synth.f16_normal if fmt == kvt.F16 else synth.bf16_normal
+    k = gen(synth.rng(5, synth.P_K, seed), (n_kv, kvh * 128)).view(np.uint8)
+    v = gen(synth.rng(5, synth.P_V, seed), (n_kv, kvh * 128)).view(np.uint8)
     return k, v
 
 
-def _prefill(q_np, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, causal, dev):
+def _prefill(q_np, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, causal, dev,
+             fmt=kvt.Q8_0):
     n_q, n_qh, hd = q_np.shape
     q = torch.from_numpy(q_np.view(np.int16)).to(dev)
     out = torch.full((n_q, n_qh, hd), float("nan"), dtype=torch.float32, device=dev)
     kvt.kvt_attn_prefill(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_tail, v_tail,
-                         n_kv, kvt.Q8_0, causal, 1 / math.sqrt(hd), out)
+                         n_kv, fmt, causal, 1 / math.sqrt(hd), out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -81,10 +92,11 @@ def test_prefill_peaked_softmax_within_tolerance(gpu):
     assert np.max(np.abs(got - ref)) <= TOL
 
 
-def test_prefill_three_way_bit_identity(gpu):
+@pytest.mark.parametrize("fmt", [kvt.Q8_0, kvt.F16, kvt.BF16], ids=FMT_IDS.get)
+def test_prefill_three_way_bit_identity(gpu, fmt):
     """All-HBM cache == HBM head + staged tail == HBM head + tail read from host memory."""
     n_kv, n_q, n_qh, kvh, n_head = 5000, 300, 32, 8, 2100
-    k, v = _cache(n_kv, kvh, 11)
+    k, v = _cache(n_kv, kvh, 11, fmt)
     row = k.shape[1]
     q = synth.f16_normal(synth.rng(5, synth.P_Q, 11), (n_q, n_qh, 128))
     q_pos0 = n_kv - n_q
@@ -92,26 +104,27 @@ def test_prefill_three_way_bit_identity(gpu):
     host = kvt.HostBuffer(2 * (n_kv - n_head) * row)
     ht = host.numpy(np.uint8, (2, n_kv - n_head, row))
     ht[0], ht[1] = k[n_head:], v[n_head:]
-    all_hbm = _prefill(q, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    all_hbm = _prefill(q, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu, fmt)
     stage = torch.empty((2, n_kv - n_head, row), dtype=torch.uint8, device=gpu)
     for mode in (kvt.COPY_SDMA, kvt.COPY_KERNEL):
         stage.zero_()
         kvt.kvt_stage_tail(host.dev, row, 0, n_kv - n_head, stage[0], mode)
         kvt.kvt_stage_tail(host.dev + (n_kv - n_head) * row, row, 0, n_kv - n_head, stage[1], mode)
-        staged = _prefill(q, q_pos0, kvh, kd, vd, n_head, stage[0], stage[1], n_kv, True, gpu)
+        staged = _prefill(q, q_pos0, kvh, kd, vd, n_head, stage[0], stage[1], n_kv, True, gpu,
+                          fmt)
         assert np.array_equal(staged.view(np.uint32), all_hbm.view(np.uint32))
     in_place = _prefill(q, q_pos0, kvh, kd, vd, n_head, host.dev,
-                        host.dev + (n_kv - n_head) * row, n_kv, True, gpu)
+                        host.dev + (n_kv - n_head) * row, n_kv, True, gpu, fmt)
     assert np.array_equal(in_place.view(np.uint32), all_hbm.view(np.uint32))
     del ht
     host.free()
 
 
 def _pipelined(q_np, q_pos0, kvh, k_head, v_head, n_head, host, n_kv, arena_rows, dev,
-               causal=True):
+               causal=True, fmt=kvt.Q8_0):
     """kvt_attn_prefill_pipelined with the host tail in `host` (K rows then V rows)."""
     n_q, n_qh, hd = q_np.shape
-    row = kvh * 136
+    row = kvh * (136 if fmt == kvt.Q8_0 else 256)
     n_tail = n_kv - n_head
     q = torch.from_numpy(q_np.view(np.int16)).to(dev)
     out = torch.full((n_q, n_qh, hd), float("nan"), dtype=torch.float32, device=dev)
@@ -120,7 +133,7 @@ def _pipelined(q_np, q_pos0, kvh, k_head, v_head, n_head, host, n_kv, arena_rows
     state = torch.empty(sb, dtype=torch.uint8, device=dev)
     copy_stream = torch.cuda.Stream()
     kvt.kvt_attn_prefill_pipelined(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head,
-                                   host.dev, host.dev + n_tail * row, n_kv, kvt.Q8_0, causal,
+                                   host.dev, host.dev + n_tail * row, n_kv, fmt, causal,
                                    1 / math.sqrt(hd), arena[0], arena[1], arena_rows, state, sb,
                                    out, copy_stream=copy_stream)
     torch.cuda.synchronize()
@@ -232,8 +245,8 @@ def test_prefill_argument_errors(gpu):
     out = torch.empty((4, 8, 128), dtype=torch.float32, device=gpu)
     k = torch.zeros((10, 8 * 136), dtype=torch.uint8, device=gpu)
     with pytest.raises(kvt.KvtError) as e:
-        kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 10, None, None, 10, kvt.F16, 1, 0.1, out)
-    assert e.value.code == kvt.EUNSUPPORTED
+        kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 10, None, None, 10, 7, 1, 0.1, out)
+    assert e.value.code == kvt.EUNSUPPORTED            # not a cache format
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_attn_prefill(q, 4, 0, 16, 1, 128, k, k, 10, None, None, 10, kvt.Q8_0, 1, 0.1, out)
     assert e.value.code == kvt.EUNSUPPORTED            # group 16
@@ -246,3 +259,46 @@ def test_prefill_argument_errors(gpu):
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_attn_prefill(q, 4, 0, 8, 8, 128, k, k, 5, None, None, 10, kvt.Q8_0, 1, 0.1, out)
     assert e.value.code == kvt.EINVAL                  # tail rows without tail pointers
+
+
+@pytest.mark.parametrize("fmt", [kvt.F16, kvt.BF16], ids=FMT_IDS.get)
+@pytest.mark.parametrize("n_kv,n_q,n_qh,kvh,causal,n_head", [
+    (1000, 77, 32, 8, True, 400),       # ragged queries and keys, split mid-tile
+    (700, 33, 8, 4, False, 350),        # non-causal, group 2
+    (600, 50, 16, 2, True, 0),          # group 8, all in the tail
+])
+def test_prefill_fp_caches_match_oracle(gpu, fmt, n_kv, n_q, n_qh, kvh, causal, n_head):
+    """fp16 and bf16 caches: the values as stored (bf16 converted to fp16, exact at these
+    magnitudes) on the same MFMA path; within 2e-3 of the fp64 oracle."""
+    k, v = _cache(n_kv, kvh, n_kv + n_q + fmt, fmt)
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, n_kv + fmt), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    got = _prefill(q, q_pos0, kvh, kd, vd, n_head, kd[n_head:], vd[n_head:], n_kv, causal, gpu,
+                   fmt)
+    ref = oracle.attn_prefill(q, q_pos0, kvh, k, v, n_head, k[n_head:], v[n_head:], n_kv,
+                              ORACLE_FMT[fmt], causal, 1 / math.sqrt(128))
+    err = np.max(np.abs(got - ref))
+    assert np.isfinite(got).all() and err <= TOL, err
+
+
+@pytest.mark.parametrize("fmt", [kvt.F16, kvt.BF16], ids=FMT_IDS.get)
+def test_prefill_pipelined_fp_caches_bit_identical(gpu, fmt):
+    """The pipelined staging with fp16 / bf16 rows (256-byte head slices) gives the single
+    pass's bits over an all-HBM cache."""
+    n_kv, n_head, n_q, n_qh, kvh, arena_rows = 4000, 1500, 200, 32, 8, 512
+    k, v = _cache(n_kv, kvh, 99 + fmt, fmt)
+    row = k.shape[1]
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, 99 + fmt), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    all_hbm = _prefill(q, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu, fmt)
+    n_tail = n_kv - n_head
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    del ht
+    got = _pipelined(q, q_pos0, kvh, kd[:n_head], vd[:n_head], n_head, host, n_kv, arena_rows,
+                     gpu, fmt=fmt)
+    assert np.array_equal(got.view(np.uint32), all_hbm.view(np.uint32))
+    host.free()

@@ -441,7 +441,7 @@ def test_q8_0_hand_built_block():
     assert zero_q.sum() == 0
 
 
-@pytest.mark.parametrize("fmt", [oracle.Q8_0, oracle.F16])
+@pytest.mark.parametrize("fmt", [oracle.Q8_0, oracle.F16, oracle.BF16])
 def test_prefill_matches_torch_sdpa_with_bottom_right_causal_mask(fmt):
     g = synth.rng(0, synth.P_MISC, 16)
     kvh, n_qh, hd, n_kv, n_q = 2, 8, 64, 300, 37
@@ -450,11 +450,16 @@ def test_prefill_matches_torch_sdpa_with_bottom_right_causal_mask(fmt):
         k = synth.q8_0_rows(g, n_kv, kvh, hd)
         v = synth.q8_0_rows(g, n_kv, kvh, hd)
         kd, vd = _dequant_q8_0_numpy(k, kvh, hd), _dequant_q8_0_numpy(v, kvh, hd)
-    else:
+    elif fmt == oracle.F16:
         k = synth.f16_normal(g, (n_kv, kvh * hd)).view(np.uint8).reshape(n_kv, -1)
         v = synth.f16_normal(g, (n_kv, kvh * hd)).view(np.uint8).reshape(n_kv, -1)
         kd = k.view(np.float16).astype(np.float64).reshape(n_kv, kvh, hd)
         vd = v.view(np.float16).astype(np.float64).reshape(n_kv, kvh, hd)
+    else:
+        k = synth.bf16_normal(g, (n_kv, kvh * hd)).view(np.uint8).reshape(n_kv, -1)
+        v = synth.bf16_normal(g, (n_kv, kvh * hd)).view(np.uint8).reshape(n_kv, -1)
+        kd = _to_f64(k.view(np.uint16), oracle.BF16).numpy().reshape(n_kv, kvh, hd)
+        vd = _to_f64(v.view(np.uint16), oracle.BF16).numpy().reshape(n_kv, kvh, hd)
     q = synth.f16_normal(g, (n_q, n_qh, hd))
     scale = 1 / math.sqrt(hd)
     n_head = 123
