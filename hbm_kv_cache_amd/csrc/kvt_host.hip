@@ -117,3 +117,44 @@ extern "C" int64_t kvt_chunks_consumed(int64_t n, int32_t skip, int32_t bpc)
         return -1;
     return (n + skip + bpc - 1) / bpc;
 }
+
+// Workspace sizes by operation: a dispatcher over the per-op size functions.
+extern "C" size_t kvt_workspace_bytes(int32_t op, const int64_t *dims, int32_t n_dims)
+{
+    static const int32_t want[] = {-1, 3, 3, 4, 3};   // dims per op (NONE_NEEDED: any)
+    if (op < KVT_OP_NONE_NEEDED || op > KVT_OP_PREFILL_STATE) {
+        kvt::fail(KVT_EINVAL, "kvt_workspace_bytes: op=%d", op);
+        return 0;
+    }
+    if (op == KVT_OP_NONE_NEEDED)
+        return 0;
+    if (!dims || n_dims != want[op]) {
+        kvt::fail(KVT_EINVAL, "kvt_workspace_bytes: op %d takes %d dims, got %d", op, want[op],
+                  dims ? n_dims : 0);
+        return 0;
+    }
+    // every dimension but the 64-bit ones (n_blocks, n_kv, n_q) must fit int32
+    auto i32 = [&](int i) { return dims[i] >= INT32_MIN && dims[i] <= INT32_MAX; };
+    bool ok = true;
+    switch (op) {
+    case KVT_OP_INDEX_TOPK: ok = i32(1) && i32(2); break;
+    case KVT_OP_ATTN_DECODE: ok = i32(0) && i32(1); break;
+    case KVT_OP_SPARSE_ROWS: ok = i32(0) && i32(1) && i32(2) && i32(3); break;
+    case KVT_OP_PREFILL_STATE: ok = i32(1) && i32(2); break;
+    }
+    if (!ok) {
+        kvt::fail(KVT_ERANGE, "kvt_workspace_bytes: op %d: a dimension exceeds int32", op);
+        return 0;
+    }
+    switch (op) {
+    case KVT_OP_INDEX_TOPK:
+        return kvt_index_topk_ws_bytes(dims[0], (int32_t)dims[1], (int32_t)dims[2]);
+    case KVT_OP_ATTN_DECODE:
+        return kvt_attn_decode_ws_bytes((int32_t)dims[0], (int32_t)dims[1], dims[2]);
+    case KVT_OP_SPARSE_ROWS:
+        return kvt_sparse_attend_rows_ws_bytes((int32_t)dims[0], (int32_t)dims[1],
+                                               (int32_t)dims[2], (int32_t)dims[3]);
+    default:
+        return kvt_attn_prefill_state_bytes(dims[0], (int32_t)dims[1], (int32_t)dims[2]);
+    }
+}

@@ -21,6 +21,7 @@ H2D, D2H = 0, 1
 COPY_AUTO, COPY_KERNEL, COPY_SDMA = 0, 1, 2
 F16, BF16, Q8_0 = 1, 2, 3
 HOST_COHERENT, HOST_NONCOHERENT, HOST_WRITECOMBINED = 0, 1, 2
+OP_NONE_NEEDED, OP_INDEX_TOPK, OP_ATTN_DECODE, OP_SPARSE_ROWS, OP_PREFILL_STATE = 0, 1, 2, 3, 4
 
 _P = c_void_p
 _SIGNATURES = {
@@ -72,6 +73,7 @@ _SIGNATURES = {
                                             _P, c_int64, c_int64, c_int64, _P, c_int32, c_int32,
                                             _P, c_int32, c_float, _P, _P, c_size_t, _P, _P,
                                             c_size_t, ctypes.POINTER(c_int32), _P]),
+    "kvt_workspace_bytes": (c_size_t, [c_int32, _P, c_int32]),
     "kvt_paged_write": (c_int, [_P, _P, _P, c_int32, c_int32, c_int32, _P, _P, c_int32, c_int32,
                                 c_int64, _P]),
     "kvt_copy_page": (c_int, [_P, _P, _P, c_int32, c_int64, c_int64, c_int32, c_int32, _P, _P,
@@ -401,3 +403,8 @@ def kvt_sparse_attend_rows_auto(q, rows, n_qh, kvh, hd, dtype, k_plane, v_plane,
         _ptr(ws), int(ws_bytes), _ptr(staging_k), _ptr(staging_v), int(staging_bytes),
         ctypes.byref(staged), _stream(stream)))
     return bool(staged.value)
+
+
+def kvt_workspace_bytes(op, dims) -> int:
+    arr = (c_int64 * max(1, len(dims)))(*[int(d) for d in dims])
+    return int(load().kvt_workspace_bytes(int(op), arr, len(dims)))

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 8
+#define KVT_ABI_VERSION 9
 
 /* status codes */
 #define KVT_OK 0
@@ -446,6 +446,26 @@ int kvt_copy_page(const void *const *src_host, void *const *dst_host, const int6
                   int32_t n_planes, int64_t from_page, int64_t to_page, int32_t page_size,
                   int32_t num_tokens, const void *src_pooled, void *dst_pooled,
                   int64_t pooled_row_bytes, int32_t cr, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * Workspace sizes by operation: one entry point over the *_ws_bytes / *_state_bytes calls
+ * above, for callers that size buffers generically.  dims per op:
+ *   KVT_OP_INDEX_TOPK     {n_blocks, n_sel, k}          = kvt_index_topk_ws_bytes
+ *   KVT_OP_ATTN_DECODE    {n_qh, hd, n_kv}              = kvt_attn_decode_ws_bytes (also the
+ *                                                          fused pass, with n_kv = k * bt)
+ *   KVT_OP_SPARSE_ROWS    {rows, n_qh, kvh, k_pad}      = kvt_sparse_attend_rows_ws_bytes
+ *   KVT_OP_PREFILL_STATE  {n_q, n_qh, kvh}              = kvt_attn_prefill_state_bytes
+ *   KVT_OP_NONE_NEEDED    any dims                      = 0 (swap, gather, staging, single-pass
+ *                                                          prefill take no workspace)
+ * Returns 0 as well for an unknown op, a wrong dims count or a dimension outside its type;
+ * kvt_last_error() then names the problem.
+ * ---------------------------------------------------------------------------------------- */
+#define KVT_OP_NONE_NEEDED 0
+#define KVT_OP_INDEX_TOPK 1
+#define KVT_OP_ATTN_DECODE 2
+#define KVT_OP_SPARSE_ROWS 3
+#define KVT_OP_PREFILL_STATE 4
+size_t kvt_workspace_bytes(int32_t op, const int64_t *dims, int32_t n_dims);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_header_declarations_all_exported():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 8
+    assert kvt.kvt_abi_version() == 9
 
 
 def test_library_has_gfx950_code_object():
@@ -228,3 +228,20 @@ def test_staging_rule_equals_oracle_and_rows_argument_errors():
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_stage_pages(p, None, 4096, p, 4, 8, p, p, stream=0)
     assert e.value.code == kvt.EINVAL
+
+
+def test_workspace_bytes_dispatches_to_the_per_op_sizes():
+    cases = [(kvt.OP_INDEX_TOPK, (4096, 8, 32), kvt.kvt_index_topk_ws_bytes(4096, 8, 32)),
+             (kvt.OP_INDEX_TOPK, (65535, 8, 512), kvt.kvt_index_topk_ws_bytes(65535, 8, 512)),
+             (kvt.OP_ATTN_DECODE, (64, 128, 2048), kvt.kvt_attn_decode_ws_bytes(64, 128, 2048)),
+             (kvt.OP_SPARSE_ROWS, (2048, 64, 8, 2080),
+              kvt.kvt_sparse_attend_rows_ws_bytes(2048, 64, 8, 2080)),
+             (kvt.OP_PREFILL_STATE, (2048, 32, 8), kvt.kvt_attn_prefill_state_bytes(2048, 32, 8)),
+             (kvt.OP_NONE_NEEDED, (), 0)]
+    for op, dims, want in cases:
+        assert kvt.kvt_workspace_bytes(op, dims) == want > 0 or op == kvt.OP_NONE_NEEDED
+    assert kvt.kvt_workspace_bytes(9, (1, 2, 3)) == 0 and "op=9" in kvt.kvt_last_error()
+    assert kvt.kvt_workspace_bytes(kvt.OP_ATTN_DECODE, (64, 128)) == 0
+    assert "takes 3 dims" in kvt.kvt_last_error()
+    assert kvt.kvt_workspace_bytes(kvt.OP_SPARSE_ROWS, (1 << 40, 64, 8, 2080)) == 0
+    assert "int32" in kvt.kvt_last_error()
