@@ -407,6 +407,37 @@ def _swap_rate(torch, kvt, t, tab, n, direction, mode, nbytes):
     return nbytes / (ms * 1e-3) / GB, ms
 
 
+def _cpu_threads():
+    n = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    return min(n, os.cpu_count() or n)
+
+
+def cpu_swap_rates(src, dst_dev, dev_base, sizes, reps=3):
+    """The oracle's memcpy loop over the same source descriptors (pinned host pages), into a
+    host buffer laid out like the device destination (addresses dst - dev_base + buffer):
+    GB/s on one thread and on all host threads.  It is the CPU baseline of a swap."""
+    import numpy as np
+    import oracle
+    src = np.ascontiguousarray(src, dtype=np.uint64)
+    dst_dev = np.ascontiguousarray(dst_dev, dtype=np.uint64)
+    sizes = np.ascontiguousarray(sizes, dtype=np.uint64)
+    span = int((dst_dev - np.uint64(dev_base) + sizes).max())
+    buf = np.zeros(span, dtype=np.uint8)
+    dst = dst_dev - np.uint64(dev_base) + np.uint64(buf.ctypes.data)
+    nbytes = int(sizes.sum())
+    out = {"bytes": nbytes, "kind": "oracle"}
+    for threads, key in ((1, "one_thread_gbs"), (_cpu_threads(), "all_threads_gbs")):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.swap(src, dst, sizes, threads=threads)
+            ts.append(time.perf_counter() - t0)
+        out[key] = round(nbytes / _median(ts) / GB, 2)
+    out["cores"] = _cpu_threads()
+    del buf
+    return out
+
+
 def suite_one_layer(torch, kvt, synth, dev, peaks, reps=20):
     """One layer: K and V planes of 256 x 32 KiB pages in pinned memory; 64 fresh random block
     ids per rep, host -> HBM (load) and HBM -> host (store), kernel and SDMA."""
@@ -439,6 +470,13 @@ def suite_one_layer(torch, kvt, synth, dev, peaks, reps=20):
             out[f"{dname}_{mname}_gbs"] = round(_median(rates), 2)
             out[f"{dname}_{mname}_pct_measured_peak"] = round(100 * _median(rates) / peak, 1)
     out["bytes_per_direction"] = 2 * n * page
+    # CPU baseline: the last load's descriptors (host pages -> a host copy of the HBM planes)
+    for p in range(2):
+        kvt.kvt_sub_block_ptrs(host.dev + p * nb * page, page, page, hid, n, 1, 0, tab[0, p * n:], n)
+        kvt.kvt_sub_block_ptrs(hbm.data_ptr() + p * nb * page, page, page, gid, n, 1, 0,
+                               tab[1, p * n:], n)
+    tab[2] = page
+    out["cpu_baseline"] = cpu_swap_rates(tab[0], tab[1], hbm.data_ptr(), tab[2])
     del hv
     host.free()
     tb.free()
@@ -494,6 +532,12 @@ def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
             out[f"{dname}_{mname}_gbs"] = round(_median(rates), 2)
             out[f"{dname}_{mname}_pct_measured_peak"] = round(100 * _median(rates) / peak, 1)
     out["bytes_per_direction"] = tensors * n * page
+    # CPU baseline on one tensor's load (4096 pages of 32 KiB = 128 MiB), the last ids drawn
+    kvt.kvt_sub_block_ptrs(host.dev, stride, page, chunks, nch, bpc, skip, tab[0], n)
+    kvt.kvt_sub_block_ptrs(hbm.data_ptr(), page, page, gids, n, 1, 0, tab[1], n)
+    tab[2, :n] = page
+    out["cpu_baseline"] = cpu_swap_rates(tab[0, :n], tab[1, :n], hbm.data_ptr(), tab[2, :n])
+    out["cpu_baseline"]["sample"] = "one of the 64 tensors' loads: 4096 pages of 32 KiB"
     del hb
     del hbm
     host.free()
@@ -539,6 +583,16 @@ def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
         if not off and cross is None and row["sdma_gbs"] >= row["kernel_gbs"]:
             cross = size
     out["h2d_crossover_bytes"] = cross
+    # CPU baseline: 512-byte pages (all 65,536) and 64 KiB pages (the first 4096 descriptors)
+    cpu = {}
+    for size, m in ((512, n), (65536, 4096)):
+        src = synth.permutation(synth.rng(3, synth.P_PERM_SRC, 0), n)[:m]
+        dst = np.arange(m, dtype=np.int64)
+        kvt.kvt_sub_block_ptrs(host.dev, size, size, src, m, 1, 0, tab[0], m)
+        kvt.kvt_sub_block_ptrs(hbm.data_ptr(), size, size, dst, m, 1, 0, tab[1], m)
+        tab[2, :m] = size
+        cpu[f"{size}B"] = cpu_swap_rates(tab[0, :m], tab[1, :m], hbm.data_ptr(), tab[2, :m])
+    out["cpu_baseline"] = cpu
     del hb
     del hbm
     host.free()
@@ -570,14 +624,13 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
     k = synth.q8_0_rows(synth.rng(5, synth.P_K, n_kv), n_kv, kvh, hd)
     v = synth.q8_0_rows(synth.rng(5, synth.P_V, n_kv), n_kv, kvh, hd)
     row = k.shape[1]
-    q = torch.from_numpy(synth.f16_normal(synth.rng(5, synth.P_Q, n_kv),
-                                          (n_q, n_qh, hd)).view(np.int16)).to(dev)
+    q_np = synth.f16_normal(synth.rng(5, synth.P_Q, n_kv), (n_q, n_qh, hd))
+    q = torch.from_numpy(q_np.view(np.int16)).to(dev)
     k_all = torch.from_numpy(k).to(dev)
     v_all = torch.from_numpy(v).to(dev)
     host = kvt.HostBuffer(2 * n_tail * row)
     ht = host.numpy(np.uint8, (2, n_tail, row))
     ht[0], ht[1] = k[n_head:], v[n_head:]
-    del k, v
     stage = torch.empty((2, n_tail, row), dtype=torch.uint8, device=dev)
     out = torch.empty((n_q, n_qh, hd), dtype=torch.float32, device=dev)
     log(f"prefill inputs ready in {time.time() - t0:.1f}s")
@@ -663,13 +716,41 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
         "prefill_tok_s_pipelined": round(n_q / (min(p_one, p_arena) * 1e-3), 1),
         "attn_all_hbm_f16_cache_ms": round(fp_ms["f16"], 4),
         "attn_all_hbm_bf16_cache_ms": round(fp_ms["bf16"], 4),
+        "cpu_baseline": cpu_prefill(k, v, ht, q_np, n_head, n_kv, kvh, row, scale, stage_bytes),
     }
     log("prefill", res)
-    del ht
+    del ht, k, v
     host.free()
     del k_all, v_all, stage, out, q, state
     torch.cuda.empty_cache()
     return res
+
+
+def cpu_prefill(k, v, ht, q_np, n_head, n_kv, kvh, row, scale, stage_bytes, budget_s=20.0):
+    """The oracle's staging (memcpy of the host tail) and fp64 prefill attention over a bounded
+    sample of the last query rows (each sees ~180k keys): staging GB/s and attention tok/s."""
+    import oracle
+    threads = _cpu_threads()
+    n_q = q_np.shape[0]
+    n_tail = n_kv - n_head
+    t0 = time.perf_counter()
+    oracle.stage_tail(ht[0], row, 0, n_tail)
+    oracle.stage_tail(ht[1], row, 0, n_tail)
+    st = time.perf_counter() - t0
+    rows, el = 0, 0.0
+    while el < budget_s / 2 and rows < n_q:
+        r = max(1, rows)                      # 1, 1, 2, 4, ... rows per call
+        t0 = time.perf_counter()
+        oracle.attn_prefill(q_np, n_kv - n_q, kvh, k, v, n_head, k[n_head:], v[n_head:], n_kv,
+                            oracle.Q8_0, True, scale, t_begin=n_q - rows - r, t_end=n_q - rows,
+                            threads=threads)
+        el += time.perf_counter() - t0
+        rows += r
+    return {"kind": "oracle", "cores": threads,
+            "stage_gbs": round(stage_bytes / st / GB, 2),
+            "attn_rows_per_s": round(rows / el, 3),
+            "sample": f"staging memcpy of the {n_tail}-row tail; fp64 attention of the last {rows} "
+                      f"of the {n_q} query rows in {el:.1f}s"}
 
 
 def suite_qsa(torch, kvt, synth, dev, wl, args, reps=None):
