@@ -683,6 +683,16 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
     p_one = pipe_ms(2 * n_tail)          # the whole tail in one bucket
     p_arena = pipe_ms(2 * 16384)         # bounded arena: buckets of 16,384 rows (17.8 MB/plane)
     st = min(st_sdma, st_kernel)
+    # an fp16 GEMM probe (hipBLASLt through torch, 8192^3) for the measured MFMA rate
+    a = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
+    b = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
+    gms = []
+    for _ in range(reps + 2):
+        t.start()
+        torch.matmul(a, b)
+        gms.append(t.stop_ms())
+    gemm_tflops = 2 * 8192 ** 3 / (min(gms) * 1e-3) / 1e12
+    del a, b
     # the same op over fp16 and bf16 caches (N(0,1) values, 2 bytes each), whole cache in HBM
     fp_ms = {}
     for fmt, name, dt in ((kvt.F16, "f16", torch.float16), (kvt.BF16, "bf16", torch.bfloat16)):
@@ -707,6 +717,8 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
         "attn_staged_ms": round(a_staged, 4),
         "attn_tflops": round(flops / (a_staged * 1e-3) / 1e12, 1),
         "attn_pct_mfma_fp16_peak": round(100 * flops / (a_staged * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 2),
+        "fp16_gemm_probe_tflops": round(gemm_tflops, 1),
+        "attn_pct_of_gemm_probe": round(100 * flops / (a_staged * 1e-3) / 1e12 / gemm_tflops, 1),
         "attn_tail_in_host_ms": round(a_inplace, 4),
         "attn_all_hbm_ms": round(a_hbm, 4),
         "prefill_tok_s_staged": round(n_q / ((st + a_staged) * 1e-3), 1),
