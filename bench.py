@@ -683,6 +683,45 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
     p_one = pipe_ms(2 * n_tail)          # the whole tail in one bucket
     p_arena = pipe_ms(2 * 16384)         # bounded arena: buckets of 16,384 rows (17.8 MB/plane)
     st = min(st_sdma, st_kernel)
+    # short chunks (one token = a decode step over the tiered cache): the split-K form, staged
+    # (stage + attend) and with the tail read in place, against the single pass -- whether the
+    # staging pays below some chunk length, as the page streaming cold weights keeps chunks
+    # under 65 tokens zero-copy
+    cutoff = {}
+    ws_b = kvt.kvt_attn_prefill_splitk_ws_bytes(1, n_qh, kvh, n_kv)
+    ws_sk = torch.empty(max(ws_b, 16), dtype=torch.uint8, device=dev)
+    for nq in (1, 16, 64, 256, 1024):
+        qs = q[n_q - nq:]
+        outs = out[:nq]
+        wb = kvt.kvt_attn_prefill_splitk_ws_bytes(nq, n_qh, kvh, n_kv)
+        assert wb <= ws_sk.numel()
+
+        def run(kind):
+            ms = []
+            for _ in range(reps):
+                t.start()
+                if kind == "staged":
+                    kvt.kvt_stage_tail(host.dev, row, 0, n_tail, stage[0], kvt.COPY_SDMA)
+                    kvt.kvt_stage_tail(host.dev + n_tail * row, row, 0, n_tail, stage[1],
+                                       kvt.COPY_SDMA)
+                    kt_, vt_ = stage[0], stage[1]
+                else:
+                    kt_, vt_ = host.dev, host.dev + n_tail * row
+                if kind == "single_pass_in_place":
+                    kvt.kvt_attn_prefill(qs, nq, n_kv - nq, n_qh, kvh, hd, k_all, v_all, n_head,
+                                         kt_, vt_, n_kv, kvt.Q8_0, 1, scale, outs)
+                else:
+                    kvt.kvt_attn_prefill_splitk(qs, nq, n_kv - nq, n_qh, kvh, hd, k_all, v_all,
+                                                n_head, kt_, vt_, n_kv, kvt.Q8_0, 1, scale,
+                                                ws_sk, wb, outs)
+                ms.append(t.stop_ms())
+            return _median(ms)
+        cutoff[str(nq)] = {k_: round(run(k_), 3) for k_ in
+                           ("staged", "in_place", "single_pass_in_place")}
+        cutoff[str(nq)]["splits"] = (wb // kvt.kvt_attn_prefill_state_bytes(nq, n_qh, kvh)
+                                     if wb else 1)
+    del ws_sk
+    log("prefill staging cutoff", cutoff)
     # an fp16 GEMM probe (hipBLASLt through torch, 8192^3) for the measured MFMA rate
     a = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
     b = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
@@ -718,6 +757,7 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
         "attn_tflops": round(flops / (a_staged * 1e-3) / 1e12, 1),
         "attn_pct_mfma_fp16_peak": round(100 * flops / (a_staged * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 2),
         "fp16_gemm_probe_tflops": round(gemm_tflops, 1),
+        "staging_cutoff_by_chunk": cutoff,
         "attn_pct_of_gemm_probe": round(100 * flops / (a_staged * 1e-3) / 1e12 / gemm_tflops, 1),
         "attn_tail_in_host_ms": round(a_inplace, 4),
         "attn_all_hbm_ms": round(a_hbm, 4),

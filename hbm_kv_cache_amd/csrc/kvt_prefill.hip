@@ -199,8 +199,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     const unsigned char *__restrict__ k_head, const unsigned char *__restrict__ v_head,
     int64_t n_head, const unsigned char *__restrict__ k_tail,
     const unsigned char *__restrict__ v_tail, int64_t n_kv, int causal, float scale_log2,
-    int tile_begin, int tile_cap, float *__restrict__ state, int first, int last,
-    float *__restrict__ out)
+    int tile_begin, int tile_cap, int n_split, int tiles_per_split, float *__restrict__ state,
+    int first, int last, float *__restrict__ out)
 {
     using R = Raw<F>;
     __shared__ __align__(16) unsigned char lds[2 * kLdsBuf + 2 * R::kBytes];
@@ -208,8 +208,18 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, i = lane & 31;
-    const int h = blockIdx.x % kvh;
-    const int64_t qt = blockIdx.x / kvh;
+    // split-K: gridDim.x = n_split x (query tiles x kvh); split x takes key tiles
+    // [x * tiles_per_split, (x + 1) * tiles_per_split) and hands its state on
+    const int n_wg = gridDim.x / n_split;
+    const int split = blockIdx.x / n_wg;
+    const int wg = blockIdx.x - split * n_wg;
+    const int h = wg % kvh;
+    const int64_t qt = wg / kvh;
+    int tb = tile_begin, tc = tile_cap;
+    if (n_split > 1) {
+        tb = split * tiles_per_split;
+        tc = tb + tiles_per_split < tile_cap ? tb + tiles_per_split : tile_cap;
+    }
     const int qpw = 32 * (kWaves / group);         // queries per workgroup
     const int64_t q_base = qt * qpw;
     const int qh = h * group + wave % group;        // this wave's query head
@@ -230,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     const int64_t pos_first = q_pos0 + t_first;
     const int64_t pos_i = q_pos0 + t_i;
     const int n_tiles_all = wg_last < 0 ? 0 : (int)((wg_last + kKT) / kKT);
-    // this call's tiles: [tile_begin, n_tiles) (a key range of a resumable pass)
-    const int n_tiles = n_tiles_all < tile_cap ? n_tiles_all : tile_cap;
+    // this call's tiles: [tb, n_tiles) (a key range of a resumable pass or a split)
+    const int n_tiles = n_tiles_all < tc ? n_tiles_all : tc;
 
     // Q^T as MFMA B operands: column i = query row, k = d = 16*kd + 8*g + 0..7
     f16x8 qb[8];
@@ -264,8 +274,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     uint64_t rq[R::kPerThread];
 
     // prologue: raw tile b -> LDS; fp16 tile b and raw tile b+1 ready; loads of b+2 in flight
-    // (b = tile_begin; buffers are indexed by tile & 1)
-    const int b0 = tile_begin;
+    // (b = tb; buffers are indexed by tile & 1)
+    const int b0 = tb;
     if (n_tiles > b0) {
         load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
         store_raw<F>(lds_raw + (b0 & 1) * R::kBytes, rq);
@@ -415,6 +425,66 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     }
 }
 
+// Split-K merge: one thread per lane of each (workgroup, wave) of the split launch.  The
+// splits' (o, m, l) -- o and l relative to 2^(m*c) -- fold in split order: M = max m_s, then
+// o = sum o_s 2^((m_s - M) c), l = sum l_s 2^((m_s - M) c); a split that saw no key (m = -inf)
+// weighs 0.  The result, o / l, goes to out[t][qh][d] with the kernel's own lane mapping
+// (query row lane % 32, dims 32*dt + 8*(r/4) + 4*(lane/32) + r%4).
+__global__ __launch_bounds__(64) void prefill_split_merge(const float *__restrict__ state,
+                                                          int n_split, int kvh, int group,
+                                                          int64_t n_q, int n_qh,
+                                                          float scale_log2,
+                                                          float *__restrict__ out)
+{
+    const int lane = threadIdx.x, wave = blockIdx.y, wg = blockIdx.x, n_wg = gridDim.x;
+    const int64_t wstride = (int64_t)kWaves * 66 * 64;   // one workgroup's state
+    const float *base = state + (int64_t)wg * wstride + (int64_t)wave * 66 * 64 + lane;
+    const int64_t sstride = (int64_t)n_wg * wstride;      // one split's state
+    float M = -INFINITY;
+    for (int x = 0; x < n_split; x++)
+        M = fmaxf(M, base[x * sstride + 64 * 64]);
+    float acc[64], L = 0.f;
+#pragma unroll
+    for (int j = 0; j < 64; j++)
+        acc[j] = 0.f;
+    for (int x = 0; x < n_split; x++) {
+        const float *b = base + x * sstride;
+        const float mx = b[64 * 64];
+        const float w = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mx - M) * scale_log2);
+        L = fmaf(b[65 * 64], w, L);
+#pragma unroll
+        for (int j = 0; j < 64; j++)
+            acc[j] = fmaf(b[j * 64], w, acc[j]);
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int h = wg % kvh;
+    const int64_t qt = wg / kvh;
+    const int qpw = 32 * (kWaves / group);
+    const int qh = h * group + wave % group;
+    const int64_t t = qt * qpw + 32 * (wave / group) + (lane & 31);
+    if (t >= n_q)
+        return;
+    float *dst = out + (t * n_qh + qh) * kHd + 4 * (lane >> 5);
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            dst[32 * dt + 8 * (r >> 2) + (r & 3)] = acc[16 * dt + r] * inv;
+}
+
+// splits for a launch of n_wg workgroups over n_tiles key tiles: enough to put about one
+// workgroup on every CU, each split at least 8 tiles
+void split_plan(int64_t n_wg, int64_t n_tiles, int &n_split, int &tiles_per_split)
+{
+    constexpr int64_t kTargetWg = 256;
+    int64_t want = (kTargetWg + n_wg - 1) / n_wg;
+    const int64_t most = n_tiles / 8;
+    want = want < most ? want : most;
+    want = want < 1 ? 1 : want;
+    tiles_per_split = (int)((n_tiles + want - 1) / want);
+    n_split = (int)((n_tiles + tiles_per_split - 1) / tiles_per_split);
+}
+
 // Argument checks shared by the prefill entry points; fills group and q_tiles.
 int check_prefill(const char *fn, const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
                   int32_t kvh, int32_t hd, const void *k_head, const void *v_head, int64_t n_head,
@@ -458,19 +528,21 @@ void launch_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, in
                     int group, int64_t q_tiles, const void *k_head, const void *v_head,
                     int64_t n_head, const void *k_tail, const void *v_tail, int64_t n_kv,
                     int causal, float scale, int64_t key_begin, int64_t key_end, float *state,
-                    int first, int last, float *out, int32_t kv_format, hipStream_t s)
+                    int first, int last, float *out, int32_t kv_format, hipStream_t s,
+                    int n_split = 1, int tiles_per_split = 0)
 {
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     const int tile_begin = (int)(key_begin / kKT);
     const int tile_cap = (int)((key_end + kKT - 1) / kKT);
     auto launch = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)(q_tiles * kvh)), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL(kern, dim3((unsigned)(q_tiles * kvh * n_split)), dim3(kThreads), 0, s,
                            static_cast<const _Float16 *>(q), n_q, q_pos0, n_qh, kvh, group,
                            static_cast<const unsigned char *>(k_head),
                            static_cast<const unsigned char *>(v_head), n_head,
                            static_cast<const unsigned char *>(k_tail),
                            static_cast<const unsigned char *>(v_tail), n_kv, causal, scale_log2,
-                           tile_begin, tile_cap, state, first, last, out);
+                           tile_begin, tile_cap, n_split, tiles_per_split, state, first, last,
+                           out);
     };
     if (kv_format == KVT_Q8_0)
         launch(prefill_attn<KVT_Q8_0>);
@@ -527,6 +599,64 @@ extern "C" int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int3
                    v_tail, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out, kv_format,
                    kvt::as_stream(stream));
     KVT_LAUNCHED("prefill_attn");
+    return KVT_OK;
+}
+
+// S8 for short chunks (down to single-token decode over a tiered cache): the same attention
+// split over the key range when query tiles x KV heads would leave most CUs idle.
+extern "C" size_t kvt_attn_prefill_splitk_ws_bytes(int64_t n_q, int32_t n_qh, int32_t kvh,
+                                                   int64_t n_kv)
+{
+    if (n_q < 1 || n_kv < 1 || kvh < 1 || n_qh < kvh || n_qh % kvh)
+        return 0;
+    const int group = n_qh / kvh;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return 0;
+    const int qpw = 32 * (kWaves / group);
+    const int64_t q_tiles = (n_q + qpw - 1) / qpw;
+    int n_split = 1, tps = 0;
+    split_plan(q_tiles * kvh, (n_kv + kKT - 1) / kKT, n_split, tps);
+    return n_split > 1 ? (size_t)n_split * state_bytes(q_tiles, kvh) : 0;
+}
+
+extern "C" int kvt_attn_prefill_splitk(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                                       int32_t kvh, int32_t hd, const void *k_head,
+                                       const void *v_head, int64_t n_head, const void *k_tail,
+                                       const void *v_tail, int64_t n_kv, int32_t kv_format,
+                                       int32_t causal, float scale, void *ws, size_t ws_bytes,
+                                       float *out, void *stream)
+{
+    int group = 0;
+    int64_t q_tiles = 0;
+    const int rc = check_prefill("kvt_attn_prefill_splitk", q, n_q, q_pos0, n_qh, kvh, hd,
+                                 k_head, v_head, n_head, k_tail, v_tail, n_kv, kv_format, scale,
+                                 out, group, q_tiles);
+    if (rc != KVT_OK || n_q == 0)
+        return rc;
+    hipStream_t s = kvt::as_stream(stream);
+    int n_split = 1, tps = 0;
+    split_plan(q_tiles * kvh, (n_kv + kKT - 1) / kKT, n_split, tps);
+    if (n_split == 1) {   // enough workgroups already: the single pass
+        launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head, k_tail,
+                       v_tail, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out, kv_format, s);
+        KVT_LAUNCHED("prefill_attn");
+        return KVT_OK;
+    }
+    const size_t need = (size_t)n_split * state_bytes(q_tiles, kvh);
+    if (!ws || ws_bytes < need || !kvt::aligned(ws, 4))
+        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill_splitk: workspace of %zu bytes, need %zu",
+                         ws_bytes, need);
+    if (q_tiles * kvh * n_split > 0x7fffffffll)
+        return kvt::fail(KVT_ERANGE, "kvt_attn_prefill_splitk: too many workgroups");
+    float *state = static_cast<float *>(ws);
+    launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head, k_tail,
+                   v_tail, n_kv, causal, scale, 0, n_kv, state, 1, 0, out, kv_format, s, n_split,
+                   tps);
+    KVT_LAUNCHED("prefill_attn");
+    const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+    hipLaunchKernelGGL(prefill_split_merge, dim3((unsigned)(q_tiles * kvh), kWaves), dim3(64), 0,
+                       s, state, n_split, (int)kvh, group, n_q, (int)n_qh, scale_log2, out);
+    KVT_LAUNCHED("prefill_split_merge");
     return KVT_OK;
 }
 

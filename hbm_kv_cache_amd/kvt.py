@@ -74,6 +74,10 @@ _SIGNATURES = {
                                             _P, c_int32, c_float, _P, _P, c_size_t, _P, _P,
                                             c_size_t, ctypes.POINTER(c_int32), _P]),
     "kvt_workspace_bytes": (c_size_t, [c_int32, _P, c_int32]),
+    "kvt_attn_prefill_splitk_ws_bytes": (c_size_t, [c_int64, c_int32, c_int32, c_int64]),
+    "kvt_attn_prefill_splitk": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P,
+                                        c_int64, _P, _P, c_int64, c_int32, c_int32, c_float, _P,
+                                        c_size_t, _P, _P]),
     "kvt_paged_write": (c_int, [_P, _P, _P, c_int32, c_int32, c_int32, _P, _P, c_int32, c_int32,
                                 c_int64, _P]),
     "kvt_copy_page": (c_int, [_P, _P, _P, c_int32, c_int64, c_int64, c_int32, c_int32, _P, _P,
@@ -408,3 +412,16 @@ def kvt_sparse_attend_rows_auto(q, rows, n_qh, kvh, hd, dtype, k_plane, v_plane,
 def kvt_workspace_bytes(op, dims) -> int:
     arr = (c_int64 * max(1, len(dims)))(*[int(d) for d in dims])
     return int(load().kvt_workspace_bytes(int(op), arr, len(dims)))
+
+
+def kvt_attn_prefill_splitk_ws_bytes(n_q, n_qh, kvh, n_kv) -> int:
+    return int(load().kvt_attn_prefill_splitk_ws_bytes(int(n_q), int(n_qh), int(kvh), int(n_kv)))
+
+
+def kvt_attn_prefill_splitk(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_tail,
+                            v_tail, n_kv, kv_format, causal, scale, ws, ws_bytes, out,
+                            stream=None):
+    _check("kvt_attn_prefill_splitk", load().kvt_attn_prefill_splitk(
+        _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
+        int(n_head), _ptr(k_tail), _ptr(v_tail), int(n_kv), int(kv_format), int(bool(causal)),
+        float(scale), _ptr(ws), int(ws_bytes), _ptr(out), _stream(stream)))

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 9
+#define KVT_ABI_VERSION 10
 
 /* status codes */
 #define KVT_OK 0
@@ -319,6 +319,25 @@ int kvt_attn_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, i
                      int32_t hd, const void *k_head, const void *v_head, int64_t n_head,
                      const void *k_tail, const void *v_tail, int64_t n_kv, int32_t kv_format,
                      int32_t causal, float scale, float *out, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S8 for short chunks.  [llama-T] also stages the tail for decode steps in the host tier; a
+ * chunk of few queries (one, for a decode step) gives kvt_attn_prefill only query tiles x kvh
+ * workgroups, each walking the whole key range.  kvt_attn_prefill_splitk computes the same
+ * attention with the key range split across workgroups at fixed 64-key tile boundaries: each
+ * split keeps its (o, m, l) in the workspace and a merge folds the splits in split order.
+ * Arguments as kvt_attn_prefill, plus ws: device workspace of
+ * kvt_attn_prefill_splitk_ws_bytes(n_q, n_qh, kvh, n_kv) bytes (0 when no split is taken).
+ * Splits are chosen to put about one workgroup on every CU (at least 8 tiles each); with one
+ * split the call is kvt_attn_prefill, bit for bit.  Deterministic, and independent of n_head
+ * (head/tail placement) like kvt_attn_prefill.
+ * ---------------------------------------------------------------------------------------- */
+size_t kvt_attn_prefill_splitk_ws_bytes(int64_t n_q, int32_t n_qh, int32_t kvh, int64_t n_kv);
+int kvt_attn_prefill_splitk(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                            int32_t kvh, int32_t hd, const void *k_head, const void *v_head,
+                            int64_t n_head, const void *k_tail, const void *v_tail, int64_t n_kv,
+                            int32_t kv_format, int32_t causal, float scale, void *ws,
+                            size_t ws_bytes, float *out, void *stream);
 
 /* ----------------------------------------------------------------------------------------
  * S8 as resumable passes.  [QSA-KVO] staged attention folds bucket partials with the online-

@@ -35,7 +35,7 @@ def test_header_declarations_all_exported():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 9
+    assert kvt.kvt_abi_version() == 10
 
 
 def test_library_has_gfx950_code_object():

@@ -302,3 +302,92 @@ def test_prefill_pipelined_fp_caches_bit_identical(gpu, fmt):
                      gpu, fmt=fmt)
     assert np.array_equal(got.view(np.uint32), all_hbm.view(np.uint32))
     host.free()
+
+
+def _splitk(q_np, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, causal, dev,
+            fmt=kvt.Q8_0):
+    n_q, n_qh, hd = q_np.shape
+    q = torch.from_numpy(q_np.view(np.int16)).to(dev)
+    out = torch.full((n_q, n_qh, hd), float("nan"), dtype=torch.float32, device=dev)
+    wb = kvt.kvt_attn_prefill_splitk_ws_bytes(n_q, n_qh, kvh, n_kv)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=dev)
+    kvt.kvt_attn_prefill_splitk(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_tail,
+                                v_tail, n_kv, fmt, causal, 1 / math.sqrt(hd), ws, wb, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), wb
+
+
+@pytest.mark.parametrize("n_kv,n_q,n_qh,kvh,causal,n_head", [
+    (5000, 1, 32, 8, True, 2100),      # one decode token: 8 workgroups -> key splits
+    (5000, 7, 64, 8, True, 0),         # a few tokens, group 8, all in the tail
+    (3000, 64, 16, 4, False, 1500),    # non-causal, group 4
+    (2000, 1, 8, 8, True, 350),        # short context: 4 splits of 8 tiles, group 1
+])
+def test_prefill_splitk_matches_oracle(gpu, n_kv, n_q, n_qh, kvh, causal, n_head):
+    k, v = _cache(n_kv, kvh, n_kv + 3 * n_q)
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, n_kv + n_q), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    got, wb = _splitk(q, q_pos0, kvh, kd, vd, n_head, kd[n_head:], vd[n_head:], n_kv, causal, gpu)
+    assert wb > 0, "these shapes take the split path"
+    ref = oracle.attn_prefill(q, q_pos0, kvh, k, v, n_head, k[n_head:], v[n_head:], n_kv,
+                              oracle.Q8_0, causal, 1 / math.sqrt(128))
+    err = np.max(np.abs(got - ref))
+    assert np.isfinite(got).all() and err <= TOL, err
+
+
+def test_prefill_splitk_tiers_bit_identical_and_one_split_is_the_single_pass(gpu):
+    """Key splits sit at fixed tile boundaries, so HBM head + staged tail, the tail read in
+    place and the all-HBM cache give the same bits; a shape that needs no split returns exactly
+    kvt_attn_prefill's output."""
+    n_kv, n_head, kvh, n_qh = 5000, 2100, 8, 32
+    k, v = _cache(n_kv, kvh, 77)
+    row = k.shape[1]
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    q1 = synth.f16_normal(synth.rng(5, synth.P_Q, 77), (1, n_qh, 128))
+    all_hbm, _ = _splitk(q1, n_kv - 1, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    host = kvt.HostBuffer(2 * (n_kv - n_head) * row)
+    ht = host.numpy(np.uint8, (2, n_kv - n_head, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    in_place, _ = _splitk(q1, n_kv - 1, kvh, kd, vd, n_head, host.dev,
+                          host.dev + (n_kv - n_head) * row, n_kv, True, gpu)
+    staged, _ = _splitk(q1, n_kv - 1, kvh, kd, vd, n_head, kd[n_head:], vd[n_head:], n_kv, True,
+                        gpu)
+    assert np.array_equal(in_place.view(np.uint32), all_hbm.view(np.uint32))
+    assert np.array_equal(staged.view(np.uint32), all_hbm.view(np.uint32))
+    del ht
+    host.free()
+    qn = synth.f16_normal(synth.rng(5, synth.P_Q, 78), (2048, n_qh, 128))
+    assert kvt.kvt_attn_prefill_splitk_ws_bytes(2048, n_qh, kvh, n_kv) == 0
+    single = _prefill(qn, n_kv - 2048, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    one_split, _ = _splitk(qn, n_kv - 2048, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    assert np.array_equal(one_split.view(np.uint32), single.view(np.uint32))
+    q = torch.from_numpy(q1.view(np.int16)).to(gpu)
+    out = torch.empty((1, n_qh, 128), dtype=torch.float32, device=gpu)
+    wb = kvt.kvt_attn_prefill_splitk_ws_bytes(1, n_qh, kvh, n_kv)
+    ws = torch.empty(wb, dtype=torch.uint8, device=gpu)
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_prefill_splitk(q, 1, n_kv - 1, n_qh, kvh, 128, kd, vd, n_kv, None, None,
+                                    n_kv, kvt.Q8_0, True, 0.1, ws, wb - 4, out)
+    assert e.value.code == kvt.EINVAL
+
+
+def test_prefill_splitk_decode_token_at_full_geometry(gpu):
+    """One decode token over the 180,000-row tiered q8_0 cache (tail read in place), against
+    the fp64 oracle."""
+    n_kv, n_head, n_qh, kvh = 180000, 94208, 32, 8
+    k, v = _cache(n_kv, kvh, 180001)
+    row = k.shape[1]
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, 180001), (1, n_qh, 128))
+    kd, vd = _dev(k[:n_head], gpu), _dev(v[:n_head], gpu)
+    host = kvt.HostBuffer(2 * (n_kv - n_head) * row)
+    ht = host.numpy(np.uint8, (2, n_kv - n_head, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    got, wb = _splitk(q, n_kv - 1, kvh, kd, vd, n_head, host.dev, host.dev + (n_kv - n_head) * row,
+                      n_kv, True, gpu)
+    assert wb > 0
+    ref = oracle.attn_prefill(q, n_kv - 1, kvh, k, v, n_head, k[n_head:], v[n_head:], n_kv,
+                              oracle.Q8_0, True, 1 / math.sqrt(128))
+    assert np.max(np.abs(got - ref)) <= TOL
+    del ht
+    host.free()
