@@ -282,3 +282,46 @@ def test_graph_decode_step_replays(gpu):
     del g, planes
     torch.cuda.synchronize()
     host.free()
+
+
+def test_worker_concurrent_submitters(gpu):
+    """Two host threads submit to one worker at once (the calls release the GIL): every job is
+    reported exactly once, oldest first in the worker's own order, and every page arrives."""
+    import threading
+    nb, per_job, jobs_per_thread = 256, 16, 8
+    host, hv = _plane(nb, 4)
+    dev = torch.zeros((nb, PAGE), dtype=torch.uint8, device=gpu)
+    w = kvt.kvt_worker_create(kvt.H2D, kvt.COPY_AUTO)
+    errors = []
+
+    def submitter(t):
+        try:
+            for j in range(jobs_per_thread):
+                base = (t * jobs_per_thread + j) * per_job
+                ids = np.arange(base, base + per_job, dtype=np.int64)
+                src, dst, sizes = _load_tables(host, dev, ids, ids)
+                kvt.kvt_worker_submit(w, 1000 * t + j, src, dst, sizes, per_job)
+        except Exception as e:   # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=submitter, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    try:
+        assert not errors, errors
+        want = {1000 * t + j for t in range(2) for j in range(jobs_per_thread)}
+        kvt.kvt_worker_wait(w, want)
+        done = kvt.kvt_worker_get_finished(w, 64)
+        got = [d[0] for d in done]
+        assert sorted(got) == sorted(want) and len(got) == len(want)
+        for t in range(2):   # each thread's jobs keep their own submission order
+            mine = [x for x in got if x // 1000 == t]
+            assert mine == sorted(mine)
+        assert kvt.kvt_worker_pending(w) == 0
+    finally:
+        kvt.kvt_worker_destroy(w)
+    assert np.array_equal(dev.cpu().numpy(), hv)
+    del hv
+    host.free()
