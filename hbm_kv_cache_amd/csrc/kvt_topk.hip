@@ -291,10 +291,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
 // ---------------------------------------------------------------------------------------------
 // Every element is ranked by the composite (rank key, ~id): 96 bits, larger = better, unique, so
 // the top k are exactly the elements at or above the k-th largest composite T.  A workgroup
-// holds one segment of a head's list in registers (element i = e*1024 + thread), finds T by
-// bisection over the 96 bits -- each step counts the elements at or above a candidate with
-// ballots and one barrier, and stops early once the count is exactly k -- and writes the
-// elements >= T in element order.  Level 0 reads the rank keys of the scoring pass (ids =
+// holds one segment of a head's list in registers (element i = e*1024 + thread), finds T a
+// byte at a time from 256-bin LDS histograms -- two barriers a pass, stopping once a bin holds
+// exactly the elements still needed -- and writes the elements >= T in element order.  Level 0 reads the rank keys of the scoring pass (ids =
 // positions, ascending); every level keeps its output in id order, so the last level's output
 // is the answer already sorted by id.  Empty slots (key 0, id kNoId) rank below every element.
 constexpr int kSelThreads = 1024;
@@ -315,29 +314,6 @@ __device__ __forceinline__ int block_sum(int c, int *red, int wave, int lane)
     return __builtin_amdgcn_readfirstlane(tot);
 }
 
-// elements with key >= t (the composite test for a candidate whose id part is 0)
-template <int E>
-__device__ __forceinline__ int wave_count_key_ge(const uint64_t (&key)[E], uint64_t t)
-{
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < E; e++)
-        c += __popcll(__ballot(key[e] >= t));
-    return c;
-}
-
-// elements with composite (key, lo) >= (tk, tl)
-template <int E>
-__device__ __forceinline__ int wave_count_ge(const uint64_t (&key)[E], const uint32_t (&lo)[E],
-                                             uint64_t tk, uint32_t tl)
-{
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < E; e++)
-        c += __popcll(__ballot(key[e] > tk || (key[e] == tk && lo[e] >= tl)));
-    return c;
-}
-
 // grid = (segments, n_sel).  in_id NULL: ids are the element positions.  Output: per segment
 // k slots (the selected elements in order, then empty slots), or with ids_final the head's k
 // ids, -1 for empty slots.
@@ -347,8 +323,10 @@ __global__ __launch_bounds__(kSelThreads) void select_level(
     uint64_t *__restrict__ out_key, uint32_t *__restrict__ out_id, int32_t *__restrict__ ids_final)
 {
     constexpr int kSlots = E * kSelWaves;   // (element slab, wave) counts, <= 128
-    __shared__ int red[2][kSelWaves];
+    __shared__ int red[kSelWaves];
     __shared__ int off[kSlots + 1];
+    __shared__ int hist[256];
+    __shared__ int pick[3];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * (E * kSelThreads);
@@ -366,33 +344,91 @@ __global__ __launch_bounds__(kSelThreads) void select_level(
         key[e] = in ? kv : 0;
         lo[e] = in ? ~id : 0;     // an empty slot (id kNoId) also ranks 0
     }
-    // T = the largest composite with count(>= T) >= k; stays 0 with fewer than k elements.
-    // The 64 key bits first: while the candidate's id part is 0, (key, lo) >= (c, 0) is just
-    // key >= c.  The id bits are needed only when the k-th and (k+1)-th keys are equal.
+    // T = the largest composite with count(>= T) >= k; stays 0 with k or fewer elements.
+    // Radix search, 8 bits a pass: a 256-bin LDS histogram of the next byte over the elements
+    // that still match the bytes chosen so far, then the bin holding the k-th largest.  The
+    // 64 key bits first; the 32 id bits only when the k-th and (k+1)-th keys are equal.  A
+    // pass ends the search when its bin holds exactly the elements still needed.
     uint64_t tk = 0;
     uint32_t tl = 0;
-    int it = 0;
-    bool done = false;
-    for (int bit = 63; bit >= 0; bit--, it++) {
-        const uint64_t ck = tk | (1ull << bit);
-        const int cnt = block_sum(wave_count_key_ge<E>(key, ck), red[it & 1], wave, lane);
-        if (cnt >= k) {
-            tk = ck;
-            if (cnt == k) {
-                done = true;
-                break;
-            }
-        }
+    bool valid[E];
+    int nv = 0;
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+        valid[e] = (key[e] | lo[e]) != 0;
+        nv += __popcll(__ballot(valid[e]));
     }
-    if (!done) {
-        for (int bit = 31; bit >= 0; bit--, it++) {
-            const uint32_t cl = tl | (1u << bit);
-            const int cnt = block_sum(wave_count_ge<E>(key, lo, tk, cl), red[it & 1], wave, lane);
-            if (cnt >= k) {
-                tl = cl;
-                if (cnt == k)
-                    break;
+    nv = block_sum(nv, red, wave, lane);
+    if (nv > k) {
+        int need = k;          // elements still to take from the matching ones
+        bool done = false;
+        for (int pass = 0; pass < 12 && !done; pass++) {   // 8 key bytes, then 4 id bytes
+            const bool on_key = pass < 8;
+            const int shift = on_key ? 56 - 8 * pass : 24 - 8 * (pass - 8);
+            for (int b = tid; b < 256; b += kSelThreads)
+                hist[b] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < E; e++) {
+                bool match;
+                uint32_t digit;
+                if (on_key) {
+                    match = valid[e] && (shift == 56 || (key[e] >> (shift + 8)) == (tk >> (shift + 8)));
+                    digit = (uint32_t)(key[e] >> shift) & 255u;
+                } else {
+                    match = valid[e] && key[e] == tk &&
+                            (shift == 24 || (lo[e] >> (shift + 8)) == (tl >> (shift + 8)));
+                    digit = (lo[e] >> shift) & 255u;
+                }
+                if (match)
+                    atomicAdd(&hist[digit], 1);
             }
+            __syncthreads();
+            // wave 0: bins from the top, the digit whose bin reaches `need`
+            if (wave == 0) {
+                int c[4], loc = 0;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {   // lane L holds bins 255-4L .. 252-4L
+                    c[j] = hist[255 - 4 * lane - j];
+                    loc += c[j];
+                }
+                int incl = loc;                  // inclusive prefix over lanes (from the top)
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int t = __shfl_up(incl, d, 64);
+                    if (lane >= d)
+                        incl += t;
+                }
+                int before = incl - loc;         // elements in higher bins than this lane's
+                int dig = -1, above = 0, inbin = 0;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    if (dig < 0 && before + c[j] >= need) {
+                        dig = 255 - 4 * lane - j;
+                        above = before;
+                        inbin = c[j];
+                    }
+                    before += c[j];
+                }
+                const uint64_t hit = __ballot(dig >= 0);
+                const int src = (int)__builtin_ctzll(hit);   // the first lane from the top
+                dig = __shfl(dig, src, 64);
+                above = __shfl(above, src, 64);
+                inbin = __shfl(inbin, src, 64);
+                if (lane == 0) {
+                    pick[0] = dig;
+                    pick[1] = above;
+                    pick[2] = inbin;
+                }
+            }
+            __syncthreads();
+            const int dig = pick[0];
+            need -= pick[1];
+            if (on_key)
+                tk |= (uint64_t)dig << shift;
+            else
+                tl |= (uint32_t)dig << shift;
+            done = pick[2] == need;   // the whole bin is taken: the rest of T stays 0
         }
     }
     // selected: composite >= T, and not an empty slot (composite 0)
