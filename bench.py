@@ -440,7 +440,8 @@ def cpu_swap_rates(src, dst_dev, dev_base, sizes, reps=3):
 
 def suite_one_layer(torch, kvt, synth, dev, peaks, reps=20):
     """One layer: K and V planes of 256 x 32 KiB pages in pinned memory; 64 fresh random block
-    ids per rep, host -> HBM (load) and HBM -> host (store), kernel and SDMA."""
+    ids per rep, host -> HBM (load) and HBM -> host (store): the kernel, the copy engines and
+    the runtime's copy calls."""
     import numpy as np
     nb, page, n = 256, 16 * 8 * 128 * 2, 64
     host = kvt.HostBuffer(2 * nb * page)
@@ -452,7 +453,7 @@ def suite_one_layer(torch, kvt, synth, dev, peaks, reps=20):
     tab = tb.numpy(np.uint64, (3, 2 * n))
     t = Timer(torch, torch.cuda.current_stream())
     out = {}
-    for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma")):
+    for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma"), (kvt.COPY_RUNTIME, "runtime")):
         for direction, dname in ((kvt.H2D, "h2d"), (kvt.D2H, "d2h")):
             rates = []
             for r in range(reps):
@@ -509,7 +510,7 @@ def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
     out = {}
     g = synth.rng(2, synth.P_SKIP)
     for direction, dname in ((kvt.H2D, "h2d"), (kvt.D2H, "d2h")):
-        for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma")):
+        for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma"), (kvt.COPY_RUNTIME, "runtime")):
             rates = []
             for r in range(reps):
                 skip = int(g.integers(0, bpc))
@@ -548,7 +549,8 @@ def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
 
 def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
     """65,536 pages in random scattered order host -> HBM, page sizes 512 B .. 64 KiB, kernel
-    loads vs the copy engines; plus 2 KiB pages at 8 mod 16 alignment."""
+    loads vs the copy engines and vs the runtime's copy calls; plus 2 KiB pages at 8 mod 16
+    alignment."""
     import numpy as np
     n = 65536
     sizes = [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536]
@@ -563,11 +565,11 @@ def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
     tab = tb.numpy(np.uint64, (3, n))
     t = Timer(torch, torch.cuda.current_stream())
     out = {"pages": n, "sweep": []}
-    cross = None
+    cross = cross_rt = None
     for size in sizes + [2048]:
         off = 8 if (size == 2048 and len(out["sweep"]) == len(sizes)) else 0
         row = {"page_bytes": size, "host_offset_mod16": off}
-        for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma")):
+        for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma"), (kvt.COPY_RUNTIME, "runtime")):
             rates = []
             for r in range(reps):
                 src = synth.permutation(synth.rng(3, synth.P_PERM_SRC, r), n)
@@ -582,7 +584,11 @@ def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
         out["sweep"].append(row)
         if not off and cross is None and row["sdma_gbs"] >= row["kernel_gbs"]:
             cross = size
+        if not off and cross_rt is None and row["runtime_gbs"] >= row["kernel_gbs"]:
+            cross_rt = size
+    # the smallest page at which the copy engines (runtime copy calls) match the kernel
     out["h2d_crossover_bytes"] = cross
+    out["h2d_crossover_bytes_runtime"] = cross_rt
     # CPU baseline: 512-byte pages (all 65,536) and 64 KiB pages (the first 4096 descriptors)
     cpu = {}
     for size, m in ((512, n), (65536, 4096)):
@@ -929,7 +935,8 @@ def suite_worker(torch, kvt, synth, dev, wl, peaks, jobs=16, pages_per_job=4096)
                 best = res
         return {k: round(v, 2) for k, v in best.items()}
 
-    for mode, mname in ((kvt.COPY_SDMA, "sdma"), (kvt.COPY_KERNEL, "kernel")):
+    for mode, mname in ((kvt.COPY_SDMA, "sdma"), (kvt.COPY_RUNTIME, "runtime"),
+                        (kvt.COPY_KERNEL, "kernel")):
         wl_ = kvt.kvt_worker_create(kvt.H2D, mode)
         ws_ = kvt.kvt_worker_create(kvt.D2H, mode)
         kvt.kvt_worker_reserve(wl_, jobs, pages_per_job)

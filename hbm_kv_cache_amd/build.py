@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libkvt.so")
 ARCH = "gfx950"
 
 SOURCES = ["kvt_host.hip", "kvt_copy.hip", "kvt_topk.hip", "kvt_gather.hip", "kvt_decode.hip",
-           "kvt_prefill.hip", "kvt_worker.hip", "kvt_paged.hip"]
+           "kvt_prefill.hip", "kvt_worker.hip", "kvt_paged.hip", "kvt_engine.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE, "-I", CSRC]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
@@ -52,7 +52,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-ldl"]
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-ldl", "-lhsa-runtime64"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -8,10 +8,12 @@
 //     addresses are only 8-byte aligned take an 8-byte path, anything else a byte path.  When
 //     no page exceeds a chunk, a wave takes eight consecutive descriptors instead, read with
 //     one load (copy_small_kernel).
-//   * SDMA: the copy engines, through hipMemcpyBatchAsync (one submission for the batch),
-//     falling back to one hipMemcpyAsync per descriptor where the batch call is unavailable.
-// kvt_stage_tail (llama-T tail staging) is one contiguous range: a single SDMA copy or the
-// same wide-load kernel over one span.
+//   * SDMA: one DMA-engine copy per run of adjacent descriptors, through HSA (kvt_engine.hip).
+//   * RUNTIME: HIP's copy calls -- hipMemcpyBatchAsync (one submission for the batch), else one
+//     hipMemcpyAsync per descriptor -- which choose the engine per copy themselves: a kernel
+//     trace shows page-sized copies running as the runtime's blit kernel.
+// kvt_stage_tail (llama-T tail staging) is one contiguous range: one hipMemcpyAsync, which the
+// runtime runs on a copy engine at staging sizes, or the same wide-load kernel over one span.
 #include <dlfcn.h>
 
 #include <algorithm>
@@ -162,11 +164,13 @@ unsigned copy_groups(uint64_t units, int cap)
 }
 
 // AUTO policy: vLLM-CPU _select_swap_blocks_fn keeps a kernel for small 8-byte-multiple pages
-// and the copy engines otherwise.  On MI355X the kernel path measured at or above the copy
-// engines at every page size from 512 B to 64 KiB and in both directions (56.9 GB/s host->HBM
-// and 55.1 GB/s HBM->host on 32 KiB pages; per-descriptor SDMA submission costs microseconds
-// each), so AUTO takes the kernel whenever it is eligible.  kvt_set_copy_threshold moves the
-// switch point per direction.
+// and the copy engines otherwise.  On MI355X the kernel path measured at or above both the
+// engines and the runtime's copy calls at every page size from 512 B to 64 KiB and in both
+// directions (56.9 GB/s host->HBM and 55.1 GB/s HBM->host on 32 KiB pages; every per-page copy
+// on the engines or through the runtime costs microseconds of submission), so AUTO takes the
+// kernel whenever it is eligible and the runtime's copy calls otherwise (they take any size
+// and alignment, and work under graph capture).  kvt_set_copy_threshold moves the switch point
+// per direction.
 std::atomic<uint64_t> g_threshold[2] = {{~0ull}, {~0ull}};
 
 // hipMemcpyBatchAsync is resolved at run time from the HIP runtime already in the process (the
@@ -189,8 +193,8 @@ batch_fn_t batch_fn()
     return st == 1 ? g_batch_fn.load() : nullptr;
 }
 
-int sdma_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
-                hipStream_t s)
+int runtime_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
+                   hipStream_t s)
 {
     if (batch_fn_t f = batch_fn()) {
         size_t fail_idx = 0;
@@ -233,7 +237,7 @@ extern "C" int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const u
         return kvt::fail(KVT_EINVAL, "kvt_swap_blocks: n=%lld with null tables", (long long)n);
     if (dir != KVT_H2D && dir != KVT_D2H)
         return kvt::fail(KVT_EINVAL, "kvt_swap_blocks: dir=%d", dir);
-    if (mode != KVT_COPY_AUTO && mode != KVT_COPY_KERNEL && mode != KVT_COPY_SDMA)
+    if (mode < KVT_COPY_AUTO || mode > KVT_COPY_RUNTIME)
         return kvt::fail(KVT_EINVAL, "kvt_swap_blocks: mode=%d", mode);
     if (n == 0)
         return KVT_OK;
@@ -251,8 +255,10 @@ extern "C" int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const u
         return kvt::fail(KVT_EALIGN, "kvt_swap_blocks: kernel path needs sizes %% 8 == 0");
     bool use_kernel = mode == KVT_COPY_KERNEL ||
                       (mode == KVT_COPY_AUTO && kernel_ok && max_size < g_threshold[dir].load());
+    if (mode == KVT_COPY_SDMA)
+        return kvt::engine_copies(src, dst, sizes, n, dir, s);
     if (!use_kernel)
-        return sdma_copies(src, dst, sizes, n, s);
+        return runtime_copies(src, dst, sizes, n, s);
 
     if (max_size <= (uint64_t)kChunk) {
         const uint64_t groups = (uint64_t)(n + kGroup - 1) / kGroup;
@@ -282,7 +288,7 @@ extern "C" int kvt_stage_tail(const void *plane, int64_t row_bytes, int64_t row_
     if (row_bytes < 1 || row_begin < 0 || row_end < row_begin)
         return kvt::fail(KVT_EINVAL, "kvt_stage_tail: row_bytes=%lld rows [%lld, %lld)",
                          (long long)row_bytes, (long long)row_begin, (long long)row_end);
-    if (mode != KVT_COPY_AUTO && mode != KVT_COPY_KERNEL && mode != KVT_COPY_SDMA)
+    if (mode < KVT_COPY_AUTO || mode > KVT_COPY_RUNTIME)
         return kvt::fail(KVT_EINVAL, "kvt_stage_tail: mode=%d", mode);
     const uint64_t bytes = (uint64_t)(row_end - row_begin) * (uint64_t)row_bytes;
     if (!bytes)

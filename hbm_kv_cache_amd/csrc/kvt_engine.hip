@@ -1,0 +1,229 @@
+// kvt_engine.hip -- S2 batched swap on the DMA (SDMA) copy engines, driven through HSA.
+//
+// vLLM-CPU chooses between the copy engines and a kernel that reads host pointers.  Through
+// HIP's copy calls that choice is not ours to make: the runtime picks an engine per copy, and
+// on MI355X a kernel trace shows every page-sized pinned<->HBM copy of a batch
+// (hipMemcpyBatchAsync or hipMemcpyAsync) running as one dispatch of the runtime's blit kernel;
+// only large copies reach the DMA engines.  So the SDMA mode of kvt_swap_blocks drives the
+// engines itself.  hsa_amd_memory_async_copy between the GPU agent and a CPU agent is a DMA
+// engine copy; the copies are ordered on the caller's stream by a host function, which runs
+// when the stream reaches it, submits one engine copy per run of adjacent descriptors (a run
+// is contiguous on both sides), waits for them all and returns, after which the stream
+// continues.  A failure inside the host function cannot be returned to the call that queued
+// it: it is kept and returned by the next engine-mode call.
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
+
+#include <atomic>
+#include <cstdio>
+#include <mutex>
+#include <new>
+
+#include "kvt_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct Agents {
+    bool probed = false;
+    int status = KVT_OK;
+    hsa_agent_t gpu{}, cpu{};
+};
+
+std::mutex g_mu;
+bool g_hsa_up = false;
+Agents g_agents[kMaxDevices];
+
+// first failure inside a host function, handed to the next engine-mode call
+std::atomic<int> g_async_status{KVT_OK};
+std::atomic<int> g_async_hsa{0};
+
+struct Probe {
+    uint32_t domain = 0, bus_dev = 0;   // bus_dev = bus << 5 | device (PCI BDF without function)
+    bool have_gpu = false, have_cpu = false;
+    hsa_agent_t gpu{}, cpu{};
+};
+
+hsa_status_t visit_agent(hsa_agent_t a, void *p)
+{
+    Probe *pr = static_cast<Probe *>(p);
+    hsa_device_type_t type;
+    if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &type) != HSA_STATUS_SUCCESS)
+        return HSA_STATUS_SUCCESS;
+    if (type == HSA_DEVICE_TYPE_CPU && !pr->have_cpu) {
+        pr->cpu = a;
+        pr->have_cpu = true;
+    } else if (type == HSA_DEVICE_TYPE_GPU && !pr->have_gpu) {
+        uint32_t bdf = 0, dom = 0;
+        if (hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_BDFID), &bdf) ==
+                HSA_STATUS_SUCCESS &&
+            hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_DOMAIN), &dom) ==
+                HSA_STATUS_SUCCESS &&
+            (bdf >> 3) == pr->bus_dev && dom == pr->domain) {
+            pr->gpu = a;
+            pr->have_gpu = true;
+        }
+    }
+    return HSA_STATUS_SUCCESS;
+}
+
+// The HSA agents of HIP device `dev` (matched by PCI domain, bus and device) and of the CPU
+// nearest to it; probed once per device.
+int agents_for(int dev, Agents *out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return kvt::fail(KVT_EUNSUPPORTED, "engine copies: device %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_mu);
+    Agents &a = g_agents[dev];
+    if (!a.probed) {
+        a.probed = true;
+        a.status = KVT_EUNSUPPORTED;
+        if (!g_hsa_up) {
+            // the HIP runtime has HSA up already; this takes a reference of our own
+            if (hsa_init() != HSA_STATUS_SUCCESS)
+                return kvt::fail(KVT_EUNSUPPORTED, "engine copies: hsa_init failed");
+            g_hsa_up = true;
+        }
+        int bus = 0, devn = 0, dom = 0;
+        if (hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&devn, hipDeviceAttributePciDeviceId, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&dom, hipDeviceAttributePciDomainId, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return kvt::fail(KVT_EUNSUPPORTED, "engine copies: no PCI address for device %d", dev);
+        }
+        Probe pr;
+        pr.domain = (uint32_t)dom;
+        pr.bus_dev = ((uint32_t)bus << 5) | ((uint32_t)devn & 31);
+        if (hsa_iterate_agents(visit_agent, &pr) != HSA_STATUS_SUCCESS || !pr.have_gpu ||
+            !pr.have_cpu)
+            return kvt::fail(KVT_EUNSUPPORTED, "engine copies: no HSA agents for device %d", dev);
+        hsa_agent_t near{};
+        if (hsa_agent_get_info(pr.gpu, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_NEAREST_CPU),
+                               &near) == HSA_STATUS_SUCCESS && near.handle)
+            pr.cpu = near;
+        a.gpu = pr.gpu;
+        a.cpu = pr.cpu;
+        a.status = KVT_OK;
+    }
+    if (a.status != KVT_OK)
+        return kvt::fail(a.status, "engine copies: device %d has no usable HSA agents", dev);
+    *out = a;
+    return KVT_OK;
+}
+
+struct EngineJob {
+    const uint64_t *src, *dst, *sizes;
+    int64_t n;
+    hsa_agent_t dst_agent, src_agent;
+};
+
+// A run: descriptors i..j-1 with every next one starting where the previous ended, on both
+// sides.  Zero-size descriptors are skipped and end no run.
+template <class F>
+void for_each_run(const EngineJob &j, F &&f)
+{
+    int64_t i = 0;
+    while (i < j.n) {
+        if (!j.sizes[i]) {
+            i++;
+            continue;
+        }
+        const uint64_t s0 = j.src[i], d0 = j.dst[i];
+        uint64_t len = j.sizes[i];
+        int64_t k = i + 1;
+        for (; k < j.n; k++) {
+            if (!j.sizes[k])
+                continue;
+            if (j.src[k] != s0 + len || j.dst[k] != d0 + len)
+                break;
+            len += j.sizes[k];
+        }
+        f(s0, d0, len);
+        i = k;
+    }
+}
+
+void record_async(int code, hsa_status_t st)
+{
+    int expected = KVT_OK;
+    if (g_async_status.compare_exchange_strong(expected, code))
+        g_async_hsa.store((int)st);
+}
+
+void run_engine_job(void *p)
+{
+    EngineJob *j = static_cast<EngineJob *>(p);
+    int64_t runs = 0;
+    for_each_run(*j, [&](uint64_t, uint64_t, uint64_t) { runs++; });
+    if (runs) {
+        hsa_signal_t sig;
+        hsa_status_t st = hsa_signal_create(runs, 0, nullptr, &sig);
+        if (st != HSA_STATUS_SUCCESS) {
+            record_async(KVT_EHIP, st);
+        } else {
+            int64_t submitted = 0;
+            bool failed = false;
+            for_each_run(*j, [&](uint64_t s, uint64_t d, uint64_t len) {
+                if (failed)
+                    return;
+                st = hsa_amd_memory_async_copy(reinterpret_cast<void *>(d), j->dst_agent,
+                                               reinterpret_cast<const void *>(s), j->src_agent,
+                                               len, 0, nullptr, sig);
+                if (st != HSA_STATUS_SUCCESS) {
+                    failed = true;
+                    record_async(KVT_EHIP, st);
+                    return;
+                }
+                submitted++;
+            });
+            if (submitted < runs)   // the copies never submitted will never count down
+                hsa_signal_subtract_screlease(sig, runs - submitted);
+            while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_EQ, 0, UINT64_MAX,
+                                             HSA_WAIT_STATE_BLOCKED) != 0) {
+            }
+            hsa_signal_destroy(sig);
+        }
+    }
+    delete j;
+}
+
+}  // namespace
+
+namespace kvt {
+
+// Queue n descriptor copies on the DMA engines, ordered on stream s (see the file comment).
+// dir KVT_H2D: src is host memory, dst device memory; KVT_D2H the reverse.
+int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
+                  int32_t dir, hipStream_t s)
+{
+    const int prev = g_async_status.exchange(KVT_OK);
+    if (prev != KVT_OK)
+        return fail(prev, "kvt_swap_blocks: an earlier engine copy failed (HSA status %d)",
+                    g_async_hsa.load());
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    KVT_HIP(hipStreamIsCapturing(s, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(KVT_EUNSUPPORTED, "kvt_swap_blocks: the SDMA mode cannot be captured in a "
+                                      "graph (its host function is queued per call)");
+    int dev = 0;
+    KVT_HIP(hipStreamGetDevice(s, &dev));
+    Agents a;
+    const int rc = agents_for(dev, &a);
+    if (rc != KVT_OK)
+        return rc;
+    EngineJob *j = new (std::nothrow) EngineJob;
+    if (!j)
+        return fail(KVT_ENOMEM, "kvt_swap_blocks: out of host memory");
+    *j = EngineJob{src, dst, sizes, n, dir == KVT_H2D ? a.gpu : a.cpu,
+                   dir == KVT_H2D ? a.cpu : a.gpu};
+    const hipError_t e = hipLaunchHostFunc(s, run_engine_job, j);
+    if (e != hipSuccess) {
+        delete j;
+        (void)hipGetLastError();
+        return fail(KVT_EHIP, "kvt_swap_blocks: hipLaunchHostFunc: %s", hipGetErrorString(e));
+    }
+    return KVT_OK;
+}
+
+}  // namespace kvt

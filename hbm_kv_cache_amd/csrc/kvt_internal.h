@@ -37,6 +37,11 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
+// kvt_swap_blocks' SDMA mode: n descriptor copies on the DMA engines, ordered on stream s by a
+// host function (kvt_engine.hip).  dir KVT_H2D: src host, dst device; KVT_D2H the reverse.
+int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
+                  int32_t dir, hipStream_t s);
+
 }  // namespace kvt
 
 // native clang vectors (the nontemporal builtins and bit casts want these, not HIP's structs)

@@ -114,7 +114,7 @@ void give_back(kvt_worker *w, kvt_worker::Job &j)
 extern "C" int kvt_worker_create(int32_t dir, int32_t mode, kvt_worker **out)
 {
     if (!out || (dir != KVT_H2D && dir != KVT_D2H) ||
-        (mode != KVT_COPY_AUTO && mode != KVT_COPY_KERNEL && mode != KVT_COPY_SDMA))
+        mode < KVT_COPY_AUTO || mode > KVT_COPY_RUNTIME)
         return kvt::fail(KVT_EINVAL, "kvt_worker_create: dir=%d mode=%d out=%p", dir, mode,
                          (void *)out);
     kvt_worker *w = new (std::nothrow) kvt_worker;

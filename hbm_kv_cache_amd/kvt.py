@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libkvt.so")
 
 OK, EINVAL, ERANGE, EALIGN, EOVERLAP, ENOMEM, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
 H2D, D2H = 0, 1
-COPY_AUTO, COPY_KERNEL, COPY_SDMA = 0, 1, 2
+COPY_AUTO, COPY_KERNEL, COPY_SDMA, COPY_RUNTIME = 0, 1, 2, 3
 F16, BF16, Q8_0 = 1, 2, 3
 HOST_COHERENT, HOST_NONCOHERENT, HOST_WRITECOMBINED = 0, 1, 2
 OP_NONE_NEEDED, OP_INDEX_TOPK, OP_ATTN_DECODE, OP_SPARSE_ROWS, OP_PREFILL_STATE = 0, 1, 2, 3, 4

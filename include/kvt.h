@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 10
+#define KVT_ABI_VERSION 11
 
 /* status codes */
 #define KVT_OK 0
@@ -70,10 +70,14 @@ extern "C" {
 /* copy direction and mechanism */
 #define KVT_H2D 0
 #define KVT_D2H 1
-#define KVT_COPY_AUTO 0   /* the kernel when sizes are multiples of 8 and pages are below the
-                            threshold (default: no limit), else SDMA */
-#define KVT_COPY_KERNEL 1 /* wavefront loads/stores through the host mapping */
-#define KVT_COPY_SDMA 2   /* the copy engines (hipMemcpyBatchAsync) */
+#define KVT_COPY_AUTO 0    /* the kernel when sizes are multiples of 8 and pages are below the
+                             threshold (default: no limit), else RUNTIME */
+#define KVT_COPY_KERNEL 1  /* wavefront loads/stores through the host mapping */
+#define KVT_COPY_SDMA 2    /* the DMA copy engines, one engine copy per run of adjacent
+                             descriptors, driven through HSA (kvt_swap_blocks; see there) */
+#define KVT_COPY_RUNTIME 3 /* HIP's copy calls (hipMemcpyBatchAsync, else hipMemcpyAsync per
+                             descriptor); the runtime picks the engine per copy and serves
+                             page-sized copies with its blit kernel */
 
 /* element formats */
 #define KVT_F16 1
@@ -127,15 +131,22 @@ int64_t kvt_chunks_consumed(int64_t n, int32_t skip, int32_t bpc);
  *   SDMA path reads them on the host, the kernel path through their device alias; pass the
  *   host pointer -- it is the same address on ROCm).  Table entries are device addresses.
  * dir:  KVT_H2D (load) or KVT_D2H (store); selects which AUTO threshold applies.
- * mode: KVT_COPY_AUTO / KERNEL / SDMA.  The kernel path needs every size to be a multiple
- *   of 8 (else KVT_EALIGN); 16-byte aligned addresses take the wide path, 8-byte aligned ones
- *   an 8-byte path, anything else a byte path.
+ * mode: KVT_COPY_AUTO / KERNEL / SDMA / RUNTIME.  The kernel path needs every size to be a
+ *   multiple of 8 (else KVT_EALIGN); 16-byte aligned addresses take the wide path, 8-byte
+ *   aligned ones an 8-byte path, anything else a byte path.
+ *   SDMA: a host function queued on the stream submits the engine copies (descriptors that
+ *   continue the previous one on both sides go as one copy) when the stream reaches it and
+ *   returns once they are done, so later work on the stream sees them; the tables are read
+ *   then, on the host.  Host addresses must be pinned memory from kvt_host_alloc (or
+ *   hipHostMalloc).  Not allowed while the stream is being captured into a graph
+ *   (KVT_EUNSUPPORTED).  A failure inside the host function is returned (KVT_EHIP) by the
+ *   next SDMA-mode call.
  * Destination ranges must be pairwise disjoint and disjoint from all sources; the order of
  * the copies is unspecified.  Zero sizes are no-ops.  n == 0 enqueues nothing.
  * ---------------------------------------------------------------------------------------- */
 int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
                     int32_t dir, int32_t mode, void *stream);
-/* AUTO switches to SDMA at pages >= threshold bytes (per direction); returns the old value. */
+/* AUTO switches to RUNTIME at pages >= threshold bytes (per direction); returns the old value. */
 uint64_t kvt_set_copy_threshold(int32_t dir, uint64_t bytes);
 
 /* ----------------------------------------------------------------------------------------
@@ -200,7 +211,9 @@ int kvt_gather_blocks(const void *k_plane, const void *v_plane, int64_t n_blocks
  * S7  tail staging.  [llama-T] commit text: when an attention op reaches the host tail, the
  * used host rows are copied into a VRAM staging buffer once per op, and the op reads that.
  *   staging[(r - row_begin)*row_bytes ...] = plane[r*row_bytes ...]  for r in [row_begin, row_end)
- *   plane: device pointer (host-mapped), staging: device (HBM); mode KVT_COPY_* (AUTO = SDMA).
+ *   plane: device pointer (host-mapped), staging: device (HBM); mode KVT_COPY_*: KERNEL is
+ *   the wide-load kernel over one span; AUTO, SDMA and RUNTIME are one hipMemcpyAsync, which
+ *   the runtime runs on a copy engine at staging sizes (and which graph capture records).
  * ---------------------------------------------------------------------------------------- */
 int kvt_stage_tail(const void *plane, int64_t row_bytes, int64_t row_begin, int64_t row_end,
                    void *staging, int32_t mode, void *stream);

@@ -35,7 +35,7 @@ def test_header_declarations_all_exported():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 10
+    assert kvt.kvt_abi_version() == 11
 
 
 def test_library_has_gfx950_code_object():
@@ -83,6 +83,15 @@ def test_argument_errors_return_before_any_device_work():
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_swap_blocks(None, None, None, 0, 7, kvt.COPY_KERNEL, stream=0)
     assert e.value.code == kvt.EINVAL
+    for mode in (-1, 4):   # modes are AUTO, KERNEL, SDMA, RUNTIME
+        with pytest.raises(kvt.KvtError) as e:
+            kvt.kvt_swap_blocks(None, None, None, 0, kvt.H2D, mode, stream=0)
+        assert e.value.code == kvt.EINVAL
+        with pytest.raises(kvt.KvtError) as e:
+            kvt.kvt_stage_tail(16, 16, 0, 1, 16, mode, stream=0)
+        assert e.value.code == kvt.EINVAL
+    for mode in (kvt.COPY_AUTO, kvt.COPY_KERNEL, kvt.COPY_SDMA, kvt.COPY_RUNTIME):
+        kvt.kvt_swap_blocks(None, None, None, 0, kvt.H2D, mode, stream=0)   # n = 0: no-op
     with pytest.raises(kvt.KvtError) as e:
         kvt.kvt_index_topk(16, 100, 128, 16, 8, 0, 16, None, 16, 1 << 20, stream=0)
     assert e.value.code == kvt.EINVAL

@@ -9,8 +9,9 @@ from hbm_kv_cache_amd import kvt, synth
 
 pytestmark = pytest.mark.gpu
 
-MODES = [kvt.COPY_KERNEL, kvt.COPY_SDMA, kvt.COPY_AUTO]
-MODE_NAMES = {kvt.COPY_KERNEL: "kernel", kvt.COPY_SDMA: "sdma", kvt.COPY_AUTO: "auto"}
+MODES = [kvt.COPY_KERNEL, kvt.COPY_SDMA, kvt.COPY_RUNTIME, kvt.COPY_AUTO]
+MODE_NAMES = {kvt.COPY_KERNEL: "kernel", kvt.COPY_SDMA: "sdma", kvt.COPY_RUNTIME: "runtime",
+              kvt.COPY_AUTO: "auto"}
 
 
 def _tables(n):
@@ -128,7 +129,8 @@ def test_swap_chunked_strided_layers_with_skip(gpu, mode):
 
 
 @pytest.mark.parametrize("page,offset", [(512, 0), (2048, 0), (2048, 8), (8192, 0), (1000, 8)])
-@pytest.mark.parametrize("mode", [kvt.COPY_KERNEL, kvt.COPY_SDMA])
+@pytest.mark.parametrize("mode", [kvt.COPY_KERNEL, kvt.COPY_SDMA, kvt.COPY_RUNTIME],
+                         ids=lambda m: MODE_NAMES[m])
 def test_swap_small_pages_scattered(gpu, page, offset, mode):
     """Many small pages in random scattered order host -> HBM; offset 8 puts the host page bases
     at 8 mod 16 (the 8-byte path); page 1000 is 8-byte aligned but not a multiple of 16."""
@@ -190,3 +192,109 @@ def test_stage_tail_q8_0_rows(gpu, mode):
     assert (got[ref.size:] == 0xCC).all()
     del hp
     host.free()
+
+
+def test_sdma_runs_of_adjacent_descriptors(gpu):
+    """The engine path merges descriptors that continue the previous one on both sides into one
+    copy; zero sizes inside a run neither end it nor move it.  Mixed runs, singles and zero
+    sizes, in both directions: bit-exact against the oracle's memcpy loop."""
+    page, nb = 4096, 96
+    host = kvt.HostBuffer(nb * page)
+    hb = host.numpy(np.uint8, (nb, page))
+    synth.fill_random_bytes(synth.rng(3, synth.P_K, 77), hb)
+    dev = torch.full((nb, page), 0x11, dtype=torch.uint8, device=gpu)
+    # (src block, dst block, size): a run of 5, a zero inside a run of 3, singles, a run whose
+    # source continues but destination does not, and partial sizes ending a run
+    plan = [(0, 10, page), (1, 11, page), (2, 12, page), (3, 13, page), (4, 14, page),
+            (20, 40, page), (21, 41, 0), (21, 41, page), (22, 42, page),
+            (50, 5, page), (60, 7, 1000),
+            (30, 70, page), (31, 80, page), (32, 81, 512)]
+    n = len(plan)
+    tb, t = _tables(n)
+    for i, (sb, db, sz) in enumerate(plan):
+        t[0, i] = host.dev + sb * page
+        t[1, i] = dev.data_ptr() + db * page
+        t[2, i] = sz
+    kvt.kvt_swap_blocks(t[0], t[1], t[2], n, kvt.H2D, kvt.COPY_SDMA)
+    torch.cuda.synchronize()
+    ref = np.full((nb, page), 0x11, dtype=np.uint8)
+    oracle.swap(np.array([hb.ctypes.data + sb * page for sb, _, _ in plan], np.uint64),
+                np.array([ref.ctypes.data + db * page for _, db, _ in plan], np.uint64),
+                np.array([sz for _, _, sz in plan], np.uint64))
+    assert np.array_equal(dev.cpu().numpy(), ref)
+    # the reverse direction into a canary plane
+    back = kvt.HostBuffer(nb * page)
+    bv = back.numpy(np.uint8, (nb, page))
+    bv[:] = 0x22
+    for i, (sb, db, sz) in enumerate(plan):
+        t[0, i] = dev.data_ptr() + db * page
+        t[1, i] = back.dev + sb * page
+    kvt.kvt_swap_blocks(t[0], t[1], t[2], n, kvt.D2H, kvt.COPY_SDMA)
+    torch.cuda.synchronize()
+    want = np.full((nb, page), 0x22, dtype=np.uint8)
+    oracle.swap(np.array([ref.ctypes.data + db * page for _, db, _ in plan], np.uint64),
+                np.array([want.ctypes.data + sb * page for sb, _, _ in plan], np.uint64),
+                np.array([sz for _, _, sz in plan], np.uint64))
+    assert np.array_equal(bv, want)
+    del hb, bv
+    host.free(); back.free(); tb.free()
+
+
+def test_sdma_is_ordered_on_the_stream(gpu):
+    """Engine copies see the stream's earlier kernels and later kernels see the copies: a fill
+    kernel writes the source, the SDMA store copies it to the host, an SDMA load brings it
+    back, and a copy kernel reads the result -- all queued at once on one stream."""
+    n, page = 256, 8192
+    src = torch.empty((n, page), dtype=torch.uint8, device=gpu)
+    mid = kvt.HostBuffer(n * page)
+    mv = mid.numpy(np.uint8, (n, page))
+    mv[:] = 0
+    dst = torch.zeros((n, page), dtype=torch.uint8, device=gpu)
+    tb, t = _tables(n)
+    tb2, t2 = _tables(n)
+    perm = synth.permutation(synth.rng(3, synth.P_PERM_DST, 5), n)
+    t[0] = [src.data_ptr() + i * page for i in range(n)]
+    t[1] = [mid.dev + int(perm[i]) * page for i in range(n)]
+    t[2] = page
+    t2[0], t2[1], t2[2] = t[1], [dst.data_ptr() + i * page for i in range(n)], page
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for rep in range(3):
+            src.fill_(rep + 1)
+            src[:, :8] = torch.arange(n, dtype=torch.uint8, device=gpu)[:, None]
+            kvt.kvt_swap_blocks(t[0], t[1], t[2], n, kvt.D2H, kvt.COPY_SDMA,
+                                stream=s.cuda_stream)
+            kvt.kvt_swap_blocks(t2[0], t2[1], t2[2], n, kvt.H2D, kvt.COPY_SDMA,
+                                stream=s.cuda_stream)
+            out = dst.clone()
+    s.synchronize()
+    want = np.full((n, page), 3, dtype=np.uint8)
+    want[:, :8] = np.arange(n, dtype=np.uint8)[:, None]
+    assert np.array_equal(out.cpu().numpy(), want)
+    del mv
+    mid.free(); tb.free(); tb2.free()
+
+
+def test_sdma_refused_under_graph_capture(gpu):
+    """The engine path queues a host function per call, so it refuses capture; the runtime's
+    copy path is captured as usual."""
+    host = kvt.HostBuffer(1 << 16)
+    dev = torch.zeros(1 << 16, dtype=torch.uint8, device=gpu)
+    tb, t = _tables(1)
+    t[0], t[1], t[2] = host.dev, dev.data_ptr(), 4096
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    code = None
+    with torch.cuda.graph(g, stream=s):
+        try:
+            kvt.kvt_swap_blocks(t[0], t[1], t[2], 1, kvt.H2D, kvt.COPY_SDMA,
+                                stream=s.cuda_stream)
+        except kvt.KvtError as e:
+            code = e.code
+        dev.add_(1)
+    assert code == kvt.EUNSUPPORTED
+    g.replay()
+    torch.cuda.synchronize()
+    assert (dev.cpu() == 1).all()
+    del g
+    host.free(); tb.free()
