@@ -69,7 +69,8 @@ class Timer:
 
 
 def measure_link_peaks(torch, kvt, dev, host_buf, nbytes, reps=5):
-    """Best-of-reps SDMA copy of nbytes between pinned host memory and HBM, both directions."""
+    """Best-of-reps runtime copy (hipMemcpyAsync, which runs a copy of this size on a DMA
+    engine) of nbytes between pinned host memory and HBM, both directions."""
     stream = torch.cuda.current_stream()
     hbm = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     t = Timer(torch, stream)
@@ -79,12 +80,12 @@ def measure_link_peaks(torch, kvt, dev, host_buf, nbytes, reps=5):
     tab = tb.numpy(np.uint64, (3, 1))
     for _ in range(reps):
         t.start()
-        kvt.kvt_stage_tail(host_buf.dev, nbytes, 0, 1, hbm, kvt.COPY_SDMA)
+        kvt.kvt_stage_tail(host_buf.dev, nbytes, 0, 1, hbm, kvt.COPY_RUNTIME)
         best_h2d = max(best_h2d, nbytes / (t.stop_ms() * 1e-3) / GB)
     tab[0, 0], tab[1, 0], tab[2, 0] = hbm.data_ptr(), host_buf.dev, nbytes
     for _ in range(reps):
         t.start()
-        kvt.kvt_swap_blocks(tab[0], tab[1], tab[2], 1, kvt.D2H, kvt.COPY_SDMA)
+        kvt.kvt_swap_blocks(tab[0], tab[1], tab[2], 1, kvt.D2H, kvt.COPY_RUNTIME)
         best_d2h = max(best_d2h, nbytes / (t.stop_ms() * 1e-3) / GB)
     # the copy kernel over a span of the gather's per-step size (host -> HBM): it is also the
     # plain copy of known size that scales the gather kernel's FETCH_SIZE / WRITE_SIZE counters
@@ -935,8 +936,7 @@ def suite_worker(torch, kvt, synth, dev, wl, peaks, jobs=16, pages_per_job=4096)
                 best = res
         return {k: round(v, 2) for k, v in best.items()}
 
-    for mode, mname in ((kvt.COPY_SDMA, "sdma"), (kvt.COPY_RUNTIME, "runtime"),
-                        (kvt.COPY_KERNEL, "kernel")):
+    for mode, mname in ((kvt.COPY_RUNTIME, "runtime"), (kvt.COPY_KERNEL, "kernel")):
         wl_ = kvt.kvt_worker_create(kvt.H2D, mode)
         ws_ = kvt.kvt_worker_create(kvt.D2H, mode)
         kvt.kvt_worker_reserve(wl_, jobs, pages_per_job)

@@ -5,16 +5,18 @@
 // on MI355X a kernel trace shows every page-sized pinned<->HBM copy of a batch
 // (hipMemcpyBatchAsync or hipMemcpyAsync) running as one dispatch of the runtime's blit kernel;
 // only large copies reach the DMA engines.  So the SDMA mode of kvt_swap_blocks drives the
-// engines itself.  hsa_amd_memory_async_copy between the GPU agent and a CPU agent is a DMA
-// engine copy; the copies are ordered on the caller's stream by a host function, which runs
-// when the stream reaches it, submits one engine copy per run of adjacent descriptors (a run
-// is contiguous on both sides), waits for them all and returns, after which the stream
-// continues.  A failure inside the host function cannot be returned to the call that queued
-// it: it is kept and returned by the next engine-mode call.
+// engines itself: hsa_amd_memory_async_copy between the GPU agent and a CPU agent is a DMA
+// engine copy, one per run of adjacent descriptors (a run is contiguous on both sides).
+//
+// The mode is synchronous with respect to the calling thread: it drains the caller's stream,
+// submits the copies, waits for them on this thread and returns, so work queued on the stream
+// afterwards sees them.  It never waits on a runtime thread: the runtime runs stream host
+// functions on the thread that also serves HSA's asynchronous signal handlers, and a copy whose
+// completion goes through such a handler (a copy tracer installs one) would never complete
+// while that thread is blocked.
 #include <hsa/hsa.h>
 #include <hsa/hsa_ext_amd.h>
 
-#include <atomic>
 #include <cstdio>
 #include <mutex>
 #include <new>
@@ -34,10 +36,6 @@ struct Agents {
 std::mutex g_mu;
 bool g_hsa_up = false;
 Agents g_agents[kMaxDevices];
-
-// first failure inside a host function, handed to the next engine-mode call
-std::atomic<int> g_async_status{KVT_OK};
-std::atomic<int> g_async_hsa{0};
 
 struct Probe {
     uint32_t domain = 0, bus_dev = 0;   // bus_dev = bus << 5 | device (PCI BDF without function)
@@ -112,117 +110,84 @@ int agents_for(int dev, Agents *out)
     return KVT_OK;
 }
 
-struct EngineJob {
-    const uint64_t *src, *dst, *sizes;
-    int64_t n;
-    hsa_agent_t dst_agent, src_agent;
-};
-
 // A run: descriptors i..j-1 with every next one starting where the previous ended, on both
 // sides.  Zero-size descriptors are skipped and end no run.
 template <class F>
-void for_each_run(const EngineJob &j, F &&f)
+void for_each_run(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
+                  F &&f)
 {
     int64_t i = 0;
-    while (i < j.n) {
-        if (!j.sizes[i]) {
+    while (i < n) {
+        if (!sizes[i]) {
             i++;
             continue;
         }
-        const uint64_t s0 = j.src[i], d0 = j.dst[i];
-        uint64_t len = j.sizes[i];
+        const uint64_t s0 = src[i], d0 = dst[i];
+        uint64_t len = sizes[i];
         int64_t k = i + 1;
-        for (; k < j.n; k++) {
-            if (!j.sizes[k])
+        for (; k < n; k++) {
+            if (!sizes[k])
                 continue;
-            if (j.src[k] != s0 + len || j.dst[k] != d0 + len)
+            if (src[k] != s0 + len || dst[k] != d0 + len)
                 break;
-            len += j.sizes[k];
+            len += sizes[k];
         }
         f(s0, d0, len);
         i = k;
     }
 }
 
-void record_async(int code, hsa_status_t st)
-{
-    int expected = KVT_OK;
-    if (g_async_status.compare_exchange_strong(expected, code))
-        g_async_hsa.store((int)st);
-}
-
-void run_engine_job(void *p)
-{
-    EngineJob *j = static_cast<EngineJob *>(p);
-    int64_t runs = 0;
-    for_each_run(*j, [&](uint64_t, uint64_t, uint64_t) { runs++; });
-    if (runs) {
-        hsa_signal_t sig;
-        hsa_status_t st = hsa_signal_create(runs, 0, nullptr, &sig);
-        if (st != HSA_STATUS_SUCCESS) {
-            record_async(KVT_EHIP, st);
-        } else {
-            int64_t submitted = 0;
-            bool failed = false;
-            for_each_run(*j, [&](uint64_t s, uint64_t d, uint64_t len) {
-                if (failed)
-                    return;
-                st = hsa_amd_memory_async_copy(reinterpret_cast<void *>(d), j->dst_agent,
-                                               reinterpret_cast<const void *>(s), j->src_agent,
-                                               len, 0, nullptr, sig);
-                if (st != HSA_STATUS_SUCCESS) {
-                    failed = true;
-                    record_async(KVT_EHIP, st);
-                    return;
-                }
-                submitted++;
-            });
-            if (submitted < runs)   // the copies never submitted will never count down
-                hsa_signal_subtract_screlease(sig, runs - submitted);
-            while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_EQ, 0, UINT64_MAX,
-                                             HSA_WAIT_STATE_BLOCKED) != 0) {
-            }
-            hsa_signal_destroy(sig);
-        }
-    }
-    delete j;
-}
-
 }  // namespace
 
 namespace kvt {
 
-// Queue n descriptor copies on the DMA engines, ordered on stream s (see the file comment).
-// dir KVT_H2D: src is host memory, dst device memory; KVT_D2H the reverse.
+// The n descriptor copies on the DMA engines, after everything queued on stream s; returns
+// once they are done (see the file comment).  dir KVT_H2D: src is host memory, dst device
+// memory; KVT_D2H the reverse.
 int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
                   int32_t dir, hipStream_t s)
 {
-    const int prev = g_async_status.exchange(KVT_OK);
-    if (prev != KVT_OK)
-        return fail(prev, "kvt_swap_blocks: an earlier engine copy failed (HSA status %d)",
-                    g_async_hsa.load());
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     KVT_HIP(hipStreamIsCapturing(s, &cs));
     if (cs != hipStreamCaptureStatusNone)
-        return fail(KVT_EUNSUPPORTED, "kvt_swap_blocks: the SDMA mode cannot be captured in a "
-                                      "graph (its host function is queued per call)");
+        return fail(KVT_EUNSUPPORTED, "kvt_swap_blocks: the SDMA mode waits on the host and "
+                                      "cannot be captured in a graph");
     int dev = 0;
     KVT_HIP(hipStreamGetDevice(s, &dev));
     Agents a;
     const int rc = agents_for(dev, &a);
     if (rc != KVT_OK)
         return rc;
-    EngineJob *j = new (std::nothrow) EngineJob;
-    if (!j)
-        return fail(KVT_ENOMEM, "kvt_swap_blocks: out of host memory");
-    *j = EngineJob{src, dst, sizes, n, dir == KVT_H2D ? a.gpu : a.cpu,
-                   dir == KVT_H2D ? a.cpu : a.gpu};
-    const hipError_t e = hipLaunchHostFunc(s, run_engine_job, j);
-    if (e != hipSuccess) {
-        delete j;
-        (void)hipGetLastError();
-        return fail(KVT_EHIP, "kvt_swap_blocks: hipLaunchHostFunc: %s", hipGetErrorString(e));
+    const hsa_agent_t dst_agent = dir == KVT_H2D ? a.gpu : a.cpu;
+    const hsa_agent_t src_agent = dir == KVT_H2D ? a.cpu : a.gpu;
+    int64_t runs = 0;
+    for_each_run(src, dst, sizes, n, [&](uint64_t, uint64_t, uint64_t) { runs++; });
+    if (!runs)
+        return KVT_OK;
+    KVT_HIP(hipStreamSynchronize(s));   // the copies come after the stream's earlier work
+    hsa_signal_t sig;
+    hsa_status_t st = hsa_signal_create(runs, 0, nullptr, &sig);
+    if (st != HSA_STATUS_SUCCESS)
+        return fail(KVT_EHIP, "kvt_swap_blocks: hsa_signal_create: status %d", (int)st);
+    int64_t submitted = 0;
+    for_each_run(src, dst, sizes, n, [&](uint64_t sa, uint64_t da, uint64_t len) {
+        if (st != HSA_STATUS_SUCCESS)
+            return;
+        st = hsa_amd_memory_async_copy(reinterpret_cast<void *>(da), dst_agent,
+                                       reinterpret_cast<const void *>(sa), src_agent, len, 0,
+                                       nullptr, sig);
+        if (st == HSA_STATUS_SUCCESS)
+            submitted++;
+    });
+    if (submitted < runs)   // copies never submitted will never count the signal down
+        hsa_signal_subtract_screlease(sig, runs - submitted);
+    while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_EQ, 0, UINT64_MAX,
+                                     HSA_WAIT_STATE_BLOCKED) != 0) {
     }
+    hsa_signal_destroy(sig);
+    if (st != HSA_STATUS_SUCCESS)
+        return fail(KVT_EHIP, "kvt_swap_blocks: hsa_amd_memory_async_copy: status %d after %lld "
+                              "of %lld copies", (int)st, (long long)submitted, (long long)runs);
     return KVT_OK;
 }
 

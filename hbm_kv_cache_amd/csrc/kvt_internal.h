@@ -37,8 +37,9 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
-// kvt_swap_blocks' SDMA mode: n descriptor copies on the DMA engines, ordered on stream s by a
-// host function (kvt_engine.hip).  dir KVT_H2D: src host, dst device; KVT_D2H the reverse.
+// kvt_swap_blocks' SDMA mode: n descriptor copies on the DMA engines after the work queued on
+// stream s, waited for on the calling thread (kvt_engine.hip).  dir KVT_H2D: src host, dst
+// device; KVT_D2H the reverse.
 int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
                   int32_t dir, hipStream_t s);
 

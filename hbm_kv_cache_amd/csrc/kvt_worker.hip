@@ -117,6 +117,9 @@ extern "C" int kvt_worker_create(int32_t dir, int32_t mode, kvt_worker **out)
         mode < KVT_COPY_AUTO || mode > KVT_COPY_RUNTIME)
         return kvt::fail(KVT_EINVAL, "kvt_worker_create: dir=%d mode=%d out=%p", dir, mode,
                          (void *)out);
+    if (mode == KVT_COPY_SDMA)   // it waits on the submitting thread; a worker only queues
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_worker_create: the SDMA mode waits on the host; "
+                                           "workers take AUTO, KERNEL or RUNTIME");
     kvt_worker *w = new (std::nothrow) kvt_worker;
     if (!w)
         return kvt::fail(KVT_ENOMEM, "kvt_worker_create: out of host memory");

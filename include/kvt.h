@@ -74,7 +74,8 @@ extern "C" {
                              threshold (default: no limit), else RUNTIME */
 #define KVT_COPY_KERNEL 1  /* wavefront loads/stores through the host mapping */
 #define KVT_COPY_SDMA 2    /* the DMA copy engines, one engine copy per run of adjacent
-                             descriptors, driven through HSA (kvt_swap_blocks; see there) */
+                             descriptors, driven through HSA; waits on the calling thread
+                             (kvt_swap_blocks; see there) */
 #define KVT_COPY_RUNTIME 3 /* HIP's copy calls (hipMemcpyBatchAsync, else hipMemcpyAsync per
                              descriptor); the runtime picks the engine per copy and serves
                              page-sized copies with its blit kernel */
@@ -134,13 +135,13 @@ int64_t kvt_chunks_consumed(int64_t n, int32_t skip, int32_t bpc);
  * mode: KVT_COPY_AUTO / KERNEL / SDMA / RUNTIME.  The kernel path needs every size to be a
  *   multiple of 8 (else KVT_EALIGN); 16-byte aligned addresses take the wide path, 8-byte
  *   aligned ones an 8-byte path, anything else a byte path.
- *   SDMA: a host function queued on the stream submits the engine copies (descriptors that
- *   continue the previous one on both sides go as one copy) when the stream reaches it and
- *   returns once they are done, so later work on the stream sees them; the tables are read
- *   then, on the host.  Host addresses must be pinned memory from kvt_host_alloc (or
+ *   SDMA is synchronous with respect to the calling thread: the call waits for the work
+ *   already queued on the stream, submits the engine copies (descriptors that continue the
+ *   previous one on both sides go as one copy), waits for them and returns, so work queued
+ *   afterwards sees them.  Host addresses must be pinned memory from kvt_host_alloc (or
  *   hipHostMalloc).  Not allowed while the stream is being captured into a graph
- *   (KVT_EUNSUPPORTED).  A failure inside the host function is returned (KVT_EHIP) by the
- *   next SDMA-mode call.
+ *   (KVT_EUNSUPPORTED).  Its copies share one completion signal, which rocprofv3's
+ *   memory-copy trace does not support (the traced process fails); kernel traces are fine.
  * Destination ranges must be pairwise disjoint and disjoint from all sources; the order of
  * the copies is unspecified.  Zero sizes are no-ops.  n == 0 enqueues nothing.
  * ---------------------------------------------------------------------------------------- */
@@ -405,7 +406,8 @@ int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_pos0, int32
 /* ----------------------------------------------------------------------------------------
  * Transfer worker.  [vLLM-CPU] SingleDirectionOffloadingHandler: transfer_async,
  * get_finished, wait, shutdown.  One worker per direction (KVT_H2D loads, KVT_D2H stores)
- * keeps the transfers submitted to it in order:
+ * keeps the transfers submitted to it in order.  kvt_worker_create takes the copy mode AUTO,
+ * KERNEL or RUNTIME (SDMA waits on the host, which a worker never does: KVT_EUNSUPPORTED).
  *   - kvt_worker_submit copies the caller's src/dst/sizes tables (host memory, any kind) into
  *     a pooled pinned buffer, so the caller may reuse its tables as soon as it returns; takes
  *     a stream and two timing events from the worker's pools; makes that stream wait for all

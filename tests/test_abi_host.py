@@ -161,6 +161,9 @@ def test_worker_argument_errors_touch_no_device():
     assert lib.kvt_worker_create(2, kvt.COPY_AUTO, ctypes.byref(h)) == kvt.EINVAL
     assert lib.kvt_worker_create(kvt.H2D, 7, ctypes.byref(h)) == kvt.EINVAL
     assert lib.kvt_worker_create(kvt.D2H, kvt.COPY_SDMA, None) == kvt.EINVAL
+    h2 = ctypes.c_void_p()
+    assert lib.kvt_worker_create(kvt.D2H, kvt.COPY_SDMA, ctypes.byref(h2)) == kvt.EUNSUPPORTED
+    assert not h2.value
     assert h.value is None
     n = ctypes.c_int32(-1)
     t = np.zeros(4, np.uint64)

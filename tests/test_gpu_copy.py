@@ -243,7 +243,8 @@ def test_sdma_runs_of_adjacent_descriptors(gpu):
 def test_sdma_is_ordered_on_the_stream(gpu):
     """Engine copies see the stream's earlier kernels and later kernels see the copies: a fill
     kernel writes the source, the SDMA store copies it to the host, an SDMA load brings it
-    back, and a copy kernel reads the result -- all queued at once on one stream."""
+    back, and a copy kernel reads the result, three times over on one stream.  (The mode
+    drains the stream before its copies and returns after them.)"""
     n, page = 256, 8192
     src = torch.empty((n, page), dtype=torch.uint8, device=gpu)
     mid = kvt.HostBuffer(n * page)
@@ -276,8 +277,8 @@ def test_sdma_is_ordered_on_the_stream(gpu):
 
 
 def test_sdma_refused_under_graph_capture(gpu):
-    """The engine path queues a host function per call, so it refuses capture; the runtime's
-    copy path is captured as usual."""
+    """The engine path waits on the host, so it refuses capture; the rest of the capture goes
+    on as usual."""
     host = kvt.HostBuffer(1 << 16)
     dev = torch.zeros(1 << 16, dtype=torch.uint8, device=gpu)
     tb, t = _tables(1)

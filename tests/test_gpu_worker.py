@@ -39,7 +39,7 @@ def _load_tables(host, dev, src_ids, dst_ids):
     return src, dst, np.full(n, PAGE, np.uint64)
 
 
-@pytest.mark.parametrize("mode", [kvt.COPY_AUTO, kvt.COPY_SDMA], ids=["auto", "sdma"])
+@pytest.mark.parametrize("mode", [kvt.COPY_AUTO, kvt.COPY_RUNTIME], ids=["auto", "runtime"])
 def test_worker_jobs_bit_exact_in_order_and_timed(gpu, mode):
     nb, per_job, jobs = 512, 48, 6
     host, hv = _plane(nb, 1)
