@@ -267,6 +267,14 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
         m = st[64 * 64];
         l = st[65 * 64];
     }
+    // Q (and a resumed state) are in registers before any tile is loaded.  Were their loads
+    // still pending at the loop, the waits before the first uses of Q and O would be placed in
+    // the loop body, and on every later tile they would also wait for the prefetch loads issued
+    // at the end of the tile before.
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
 
     // the four cache bases, moved to this workgroup's head slice
     const unsigned char *kh = k_head + h * R::kHeadBytes, *vh = v_head + h * R::kHeadBytes;
