@@ -299,3 +299,73 @@ def test_sdma_refused_under_graph_capture(gpu):
     assert (dev.cpu() == 1).all()
     del g
     host.free(); tb.free()
+
+
+def test_swap_32_layers_full_geometry_sampled(gpu):
+    """The 32-layer workload at full size in the launch configuration the bench times (kernel
+    mode, 262,144 descriptors per direction): 64 tensors of 8192 HBM blocks; host rows of four
+    32 KiB pages + 4 KiB pad (2048 rows per tensor, 16.5 GiB pinned); 4096 random blocks per
+    tensor with a random skip on the first host chunk.  Every host page carries its own
+    (tensor, row, page) stamp, so a copy from the wrong place cannot match.  Checked on 3000
+    sampled descriptors against the host bytes (the oracle's memcpy, one page at a time),
+    unselected HBM blocks and pads left alone, and the store back as a round trip."""
+    tensors, gblocks, bpc, page, pad, n = 64, 8192, 4, 32768, 4096, 4096
+    hrows = gblocks // bpc
+    stride = bpc * page + pad
+    host = kvt.HostBuffer(tensors * hrows * stride)
+    flat = host.numpy(np.uint8)
+    block = np.empty(1 << 28, dtype=np.uint8)
+    synth.fill_random_bytes(synth.rng(2, synth.P_K, 99), block)
+    for o in range(0, flat.size, block.size):
+        m = min(block.size, flat.size - o)
+        flat[o:o + m] = block[:m]
+    del block
+    hb = flat.reshape(tensors, hrows, stride)
+    stamps = (np.arange(tensors, dtype=np.uint64)[:, None, None] << np.uint64(40)) | \
+             (np.arange(hrows, dtype=np.uint64)[None, :, None] << np.uint64(8)) | \
+             np.arange(bpc, dtype=np.uint64)[None, None, :]
+    hb.view(np.uint64)[:, :, [j * page // 8 for j in range(bpc)]] = stamps
+    hbm = torch.full((tensors, gblocks, page), 0x33, dtype=torch.uint8, device=gpu)
+    g = synth.rng(2, synth.P_SKIP, 99)
+    skip = int(g.integers(0, bpc))
+    nch = kvt.kvt_chunks_consumed(n, skip, bpc)
+    chunks = synth.permutation(synth.rng(2, synth.P_PERM_SRC, 99), hrows)[:nch]
+    gids = synth.permutation(synth.rng(2, synth.P_PERM_DST, 99), gblocks)[:n]
+    tb, t = _tables(tensors * n)
+    for x in range(tensors):
+        kvt.kvt_sub_block_ptrs(host.dev + x * hrows * stride, stride, page, chunks, nch, bpc, skip,
+                               t[0, x * n:], n)
+        kvt.kvt_sub_block_ptrs(hbm.data_ptr() + x * gblocks * page, page, page, gids, n, 1, 0,
+                               t[1, x * n:], n)
+    t[2] = page
+    kvt.kvt_swap_blocks(t[0], t[1], t[2], tensors * n, kvt.H2D, kvt.COPY_KERNEL)
+    torch.cuda.synchronize()
+
+    pick = synth.rng(2, synth.P_MISC, 99).choice(tensors * n, size=3000, replace=False)
+    xs, os_ = pick // n, pick % n
+    rows, js = chunks[(os_ + skip) // bpc], (os_ + skip) % bpc
+    want = np.stack([hb[x, r, j * page:(j + 1) * page] for x, r, j in zip(xs, rows, js)])
+    got = hbm[torch.from_numpy(xs).to(gpu), torch.from_numpy(gids[os_]).to(gpu)].cpu().numpy()
+    assert np.array_equal(got, want), "loaded pages differ from their host pages"
+    rest = np.setdiff1d(np.arange(gblocks), gids)
+    xr = synth.rng(2, synth.P_MISC, 98).integers(0, tensors, 500)
+    br = rest[synth.rng(2, synth.P_MISC, 97).integers(0, rest.size, 500)]
+    assert (hbm[torch.from_numpy(xr).to(gpu), torch.from_numpy(br).to(gpu)] == 0x33).all()
+
+    # store: zero the selected host pages, copy HBM back, compare with the original bytes
+    pads = np.stack([hb[x, r, bpc * page:] for x, r in zip(xs, rows)])
+    sel_rows = chunks[(np.arange(n) + skip) // bpc]
+    sel_js = (np.arange(n) + skip) % bpc
+    for x in range(tensors):
+        for j in range(bpc):
+            hb[x, sel_rows[sel_js == j], j * page:(j + 1) * page] = 0
+    t[0], t[1] = t[1].copy(), t[0].copy()
+    kvt.kvt_swap_blocks(t[0], t[1], t[2], tensors * n, kvt.D2H, kvt.COPY_KERNEL)
+    torch.cuda.synchronize()
+    back = np.stack([hb[x, r, j * page:(j + 1) * page] for x, r, j in zip(xs, rows, js)])
+    assert np.array_equal(back, want), "round trip changed sampled pages"
+    assert np.array_equal(np.stack([hb[x, r, bpc * page:] for x, r in zip(xs, rows)]), pads)
+    del hb, flat, got, want, back
+    del hbm
+    host.free(); tb.free()
+    torch.cuda.empty_cache()
