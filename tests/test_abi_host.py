@@ -34,6 +34,19 @@ def test_header_declarations_all_exported():
     assert set(kvt.EXPORTED) == set(names)
 
 
+def test_binding_constants_equal_the_header():
+    """Every value #define of include/kvt.h (status codes, directions, copy modes, formats, host
+    flags, workspace ops) has the same value in the Python binding, and every signature the
+    binding declares names a function the header declares."""
+    text = open(os.path.join(ROOT, "include", "kvt.h")).read()
+    defs = dict(re.findall(r"^#define KVT_(\w+)\s+\(?(-?\d+)u?\)?", text, re.M))
+    defs.pop("ABI_VERSION")
+    assert {"COPY_RUNTIME", "Q8_0", "OP_PREFILL_STATE", "EHIP"} <= set(defs)
+    for name, value in defs.items():
+        assert getattr(kvt, name) == int(value), name
+    assert set(kvt._SIGNATURES) <= set(_declared())
+
+
 def test_abi_version():
     assert kvt.kvt_abi_version() == 11
 
