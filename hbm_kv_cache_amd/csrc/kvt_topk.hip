@@ -292,8 +292,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
 // Every element is ranked by the composite (rank key, ~id): 96 bits, larger = better, unique, so
 // the top k are exactly the elements at or above the k-th largest composite T.  A workgroup
 // holds one segment of a head's list in registers (element i = e*1024 + thread), finds T a
-// byte at a time from 256-bin LDS histograms -- two barriers a pass, stopping once a bin holds
-// exactly the elements still needed -- and writes the elements >= T in element order.  Level 0 reads the rank keys of the scoring pass (ids =
+// byte at a time from 256-bin LDS histograms -- two barriers a pass, starting at the first byte
+// in which the keys differ, stopping once a bin holds exactly the elements still needed -- and
+// writes the elements >= T in element order.  Level 0 reads the rank keys of the scoring pass (ids =
 // positions, ascending); every level keeps its output in id order, so the last level's output
 // is the answer already sorted by id.  Empty slots (key 0, id kNoId) rank below every element.
 constexpr int kSelThreads = 1024;
@@ -327,6 +328,7 @@ __global__ __launch_bounds__(kSelThreads) void select_level(
     __shared__ int off[kSlots + 1];
     __shared__ int hist[256];
     __shared__ int pick[3];
+    __shared__ uint64_t rmin[kSelWaves], rmax[kSelWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y;
     const int64_t s0 = (int64_t)blockIdx.x * (E * kSelThreads);
@@ -360,9 +362,42 @@ __global__ __launch_bounds__(kSelThreads) void select_level(
     }
     nv = block_sum(nv, red, wave, lane);
     if (nv > k) {
+        // Leading key bytes that every valid element shares (those of the smallest and the
+        // largest key) would each take a pass that puts all elements in one bin: T starts with
+        // them, and the search at the first byte where the keys differ.  Candidate lists (the
+        // levels after the first) hold the top of each head's scores, which share leading
+        // bytes; the first level's raw scores span both signs, so it goes straight to pass 0.
+        int common = 0;
+        if (hi) {
+            uint64_t kmin = ~0ull, kmax = 0;
+#pragma unroll
+            for (int e = 0; e < E; e++)
+                if (valid[e]) {
+                    kmin = key[e] < kmin ? key[e] : kmin;
+                    kmax = key[e] > kmax ? key[e] : kmax;
+                }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) {
+                const uint64_t a = shfl_u64(kmin, lane ^ d), b = shfl_u64(kmax, lane ^ d);
+                kmin = a < kmin ? a : kmin;
+                kmax = b > kmax ? b : kmax;
+            }
+            if (lane == 0) {
+                rmin[wave] = kmin;
+                rmax[wave] = kmax;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < kSelWaves; w++) {
+                kmin = rmin[w] < kmin ? rmin[w] : kmin;
+                kmax = rmax[w] > kmax ? rmax[w] : kmax;
+            }
+            common = kmin == kmax ? 8 : __builtin_clzll(kmin ^ kmax) >> 3;
+            tk = common == 0 ? 0 : common == 8 ? kmin : kmin >> (64 - 8 * common) << (64 - 8 * common);
+        }
         int need = k;          // elements still to take from the matching ones
         bool done = false;
-        for (int pass = 0; pass < 12 && !done; pass++) {   // 8 key bytes, then 4 id bytes
+        for (int pass = common; pass < 12 && !done; pass++) {   // 8 key bytes, then 4 id bytes
             const bool on_key = pass < 8;
             const int shift = on_key ? 56 - 8 * pass : 24 - 8 * (pass - 8);
             for (int b = tid; b < 256; b += kSelThreads)
