@@ -13,7 +13,8 @@ Prints ONE JSON line.  ``value`` = host->HBM KV gather GB/s over whole steps (8,
 gathered per step / step time).  ``roofline`` is the gather kernel itself (HIP events on the
 launch stream) against the PCIe Gen5 x16 per-direction peak; ``cpu_baseline`` is the CPU
 oracle running the same step on the host cores.  ``--suite`` adds the other workloads
-(one-layer and 32-layer swaps, the small-page kernel/SDMA sweep, tiered prefill).
+(one-layer and 32-layer swaps, the small-page sweep of kernel, DMA-engine and runtime copies,
+tiered prefill).
 """
 from __future__ import annotations
 
@@ -401,6 +402,10 @@ def _median(xs):
     return xs[len(xs) // 2]
 
 
+# the three ways a swap can move pages, as named in the suites' output
+COPY_MODES_SPEC = (("COPY_KERNEL", "kernel"), ("COPY_SDMA", "sdma"), ("COPY_RUNTIME", "runtime"))
+
+
 def _swap_rate(torch, kvt, t, tab, n, direction, mode, nbytes):
     t.start()
     kvt.kvt_swap_blocks(tab[0], tab[1], tab[2], n, direction, mode)
@@ -454,7 +459,7 @@ def suite_one_layer(torch, kvt, synth, dev, peaks, reps=20):
     tab = tb.numpy(np.uint64, (3, 2 * n))
     t = Timer(torch, torch.cuda.current_stream())
     out = {}
-    for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma"), (kvt.COPY_RUNTIME, "runtime")):
+    for mode, mname in [(getattr(kvt, c), n) for c, n in COPY_MODES_SPEC]:
         for direction, dname in ((kvt.H2D, "h2d"), (kvt.D2H, "d2h")):
             rates = []
             for r in range(reps):
@@ -511,7 +516,7 @@ def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
     out = {}
     g = synth.rng(2, synth.P_SKIP)
     for direction, dname in ((kvt.H2D, "h2d"), (kvt.D2H, "d2h")):
-        for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma"), (kvt.COPY_RUNTIME, "runtime")):
+        for mode, mname in [(getattr(kvt, c), n) for c, n in COPY_MODES_SPEC]:
             rates = []
             for r in range(reps):
                 skip = int(g.integers(0, bpc))
@@ -570,7 +575,7 @@ def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
     for size in sizes + [2048]:
         off = 8 if (size == 2048 and len(out["sweep"]) == len(sizes)) else 0
         row = {"page_bytes": size, "host_offset_mod16": off}
-        for mode, mname in ((kvt.COPY_KERNEL, "kernel"), (kvt.COPY_SDMA, "sdma"), (kvt.COPY_RUNTIME, "runtime")):
+        for mode, mname in [(getattr(kvt, c), n) for c, n in COPY_MODES_SPEC]:
             rates = []
             for r in range(reps):
                 src = synth.permutation(synth.rng(3, synth.P_PERM_SRC, r), n)
