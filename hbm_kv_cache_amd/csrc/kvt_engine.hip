@@ -10,14 +10,12 @@
 //
 // The mode is synchronous with respect to the calling thread: it drains the caller's stream,
 // submits the copies, waits for them on this thread and returns, so work queued on the stream
-// afterwards sees them.  It never waits on a runtime thread: the runtime runs stream host
-// functions on the thread that also serves HSA's asynchronous signal handlers, and a copy whose
-// completion goes through such a handler (a copy tracer installs one) would never complete
-// while that thread is blocked.
+// afterwards sees them.  It never waits on a runtime thread.  Ordering the copies with a stream
+// host function that waited inside stalled at the first copy under a memory-copy trace, whose
+// completion handler most likely needs the thread the runtime runs host functions on.
 #include <hsa/hsa.h>
 #include <hsa/hsa_ext_amd.h>
 
-#include <cstdio>
 #include <mutex>
 #include <new>
 
@@ -181,8 +179,9 @@ int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *size
     });
     if (submitted < runs)   // copies never submitted will never count the signal down
         hsa_signal_subtract_screlease(sig, runs - submitted);
-    while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_EQ, 0, UINT64_MAX,
-                                     HSA_WAIT_STATE_BLOCKED) != 0) {
+    // "below 1" rather than "equal to 0": a count taken past zero still ends the wait
+    while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_LT, 1, UINT64_MAX,
+                                     HSA_WAIT_STATE_BLOCKED) >= 1) {
     }
     hsa_signal_destroy(sig);
     if (st != HSA_STATUS_SUCCESS)
