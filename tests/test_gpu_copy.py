@@ -369,3 +369,46 @@ def test_swap_32_layers_full_geometry_sampled(gpu):
     del hbm
     host.free(); tb.free()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", [kvt.COPY_KERNEL, kvt.COPY_AUTO], ids=lambda m: MODE_NAMES[m])
+def test_swap_pages_up_to_512_bytes_mixed(gpu, mode):
+    """Small pages of mixed sizes (0 to 512 bytes) in one batch, an odd count of descriptors (the
+    last group of eight is partial), host pages 16-byte and only 8-byte aligned, in both
+    directions; bit-exact against the oracle's memcpy loop, canaries elsewhere untouched."""
+    n, slot = 1001, 528
+    g = synth.rng(3, synth.P_MISC, 512)
+    sizes = g.choice(np.array([0, 8, 64, 200, 504, 512], np.uint64), size=n)
+    offs = g.choice(np.array([0, 8], np.int64), size=n)   # 16- or only 8-byte aligned bases
+    host = kvt.HostBuffer(n * slot + 64)
+    hb = host.numpy(np.uint8)
+    synth.fill_random_bytes(synth.rng(3, synth.P_K, 512), hb)
+    dev = torch.full((n * slot,), 0x5C, dtype=torch.uint8, device=gpu)
+    src_slot = synth.permutation(synth.rng(3, synth.P_PERM_SRC, 512), n)
+    dst_slot = synth.permutation(synth.rng(3, synth.P_PERM_DST, 512), n)
+    tb, t = _tables(n)
+    t[0] = [host.dev + int(src_slot[i]) * slot + int(offs[i]) for i in range(n)]
+    t[1] = [dev.data_ptr() + int(dst_slot[i]) * slot for i in range(n)]
+    t[2] = sizes
+    kvt.kvt_swap_blocks(t[0], t[1], t[2], n, kvt.H2D, mode)
+    torch.cuda.synchronize()
+    ref = np.full(n * slot, 0x5C, dtype=np.uint8)
+    oracle.swap(np.array([hb.ctypes.data + int(src_slot[i]) * slot + int(offs[i])
+                          for i in range(n)], np.uint64),
+                np.array([ref.ctypes.data + int(dst_slot[i]) * slot for i in range(n)], np.uint64),
+                sizes)
+    assert np.array_equal(dev.cpu().numpy(), ref)
+    # back to a canary-filled host buffer at the source slots, 8 bytes past the slot start
+    back = kvt.HostBuffer(n * slot + 64)
+    bb = back.numpy(np.uint8)
+    bb[:] = 0xA7
+    t[0], t[1] = t[1].copy(), [back.dev + int(src_slot[i]) * slot + 8 for i in range(n)]
+    kvt.kvt_swap_blocks(t[0], t[1], t[2], n, kvt.D2H, mode)
+    torch.cuda.synchronize()
+    want = np.full(n * slot + 64, 0xA7, dtype=np.uint8)
+    oracle.swap(np.array([ref.ctypes.data + int(dst_slot[i]) * slot for i in range(n)], np.uint64),
+                np.array([want.ctypes.data + int(src_slot[i]) * slot + 8 for i in range(n)],
+                         np.uint64), sizes)
+    assert np.array_equal(bb, want)
+    del hb, bb
+    host.free(); back.free(); tb.free()
