@@ -14,7 +14,7 @@ gathered per step / step time).  ``roofline`` is the gather kernel itself (HIP e
 launch stream) against the PCIe Gen5 x16 per-direction peak; ``cpu_baseline`` is the CPU
 oracle running the same step on the host cores.  ``--suite`` adds the other workloads
 (one-layer and 32-layer swaps, the small-page sweep of kernel, DMA-engine and runtime copies,
-tiered prefill).
+tiered prefill, and prefill over a chain of layers with the next layer's first bucket prefetched).
 """
 from __future__ import annotations
 
@@ -45,7 +45,8 @@ def parse():
                    help="host K/V plane layout (block-local head-major, or token-major)")
     p.add_argument("--suite", nargs="?", const="all", default=None,
                    help="also measure the other workloads: all, or a comma list of "
-                        "prefill, swap1, small, swap32, qsa, decode1m, worker, upkeep, rows")
+                        "prefill, chain, swap1, small, swap32, qsa, decode1m, worker, upkeep, "
+                        "rows")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the CPU-oracle baseline's wall time")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -790,6 +791,79 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
     return res
 
 
+def suite_prefill_chain(torch, kvt, synth, dev, peaks, reps=5):
+    """Tiered prefill over a chain of 8 layers with the whole 180,000-token q8_0 cache of each
+    layer in pinned host memory (n_head 0), a 2048-query causal chunk with 32 query heads, 16,384-
+    row buckets: kvt_attn_prefill_pipelined per layer (each waits for its first bucket's copy)
+    against kvt_attn_prefill_chain (each call copies the next layer's first bucket behind its
+    own copies).  Layers alternate between two sets of host planes (K and V swapped) and two
+    arenas."""
+    import numpy as np
+    n_kv, n_q, n_qh, kvh, hd = 180000, 2048, 32, 8, 128
+    n_layers, ch_rows = 8, 2 * 16384
+    t0 = time.time()
+    k = synth.q8_0_rows(synth.rng(5, synth.P_K, n_kv), n_kv, kvh, hd)
+    v = synth.q8_0_rows(synth.rng(5, synth.P_V, n_kv), n_kv, kvh, hd)
+    row = k.shape[1]
+    q_np = synth.f16_normal(synth.rng(5, synth.P_Q, n_kv), (n_q, n_qh, hd))
+    q = torch.from_numpy(q_np.view(np.int16)).to(dev)
+    ch_hosts = []
+    for kk, vv in ((k, v), (v, k)):
+        hbuf = kvt.HostBuffer(2 * n_kv * row)
+        hp = hbuf.numpy(np.uint8, (2, n_kv, row))
+        hp[0], hp[1] = kk, vv
+        del hp
+        ch_hosts.append(hbuf)
+    del k, v
+    ch_arenas = [torch.empty((2, ch_rows, row), dtype=torch.uint8, device=dev) for _ in range(2)]
+    out = torch.empty((n_q, n_qh, hd), dtype=torch.float32, device=dev)
+    state_b = kvt.kvt_attn_prefill_state_bytes(n_q, n_qh, kvh)
+    state = torch.empty(state_b, dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
+    t = Timer(torch, torch.cuda.current_stream())
+    q_pos0 = n_kv - n_q
+    scale = 1 / math.sqrt(hd)
+    log(f"chain inputs ready in {time.time() - t0:.1f}s")
+
+    def chain_ms(prefetch, reps=reps):
+        ms = []
+        for _ in range(reps):
+            t.start()
+            for i in range(n_layers):
+                h, hn = ch_hosts[i % 2], ch_hosts[(i + 1) % 2]
+                a, an = ch_arenas[i % 2], ch_arenas[(i + 1) % 2]
+                kvt.kvt_attn_prefill_chain(
+                    q, n_q, q_pos0, n_qh, kvh, hd, None, None, 0, h.dev, h.dev + n_kv * row,
+                    n_kv, kvt.Q8_0, 1, scale, a[0], a[1], ch_rows,
+                    ch_rows // 2 if prefetch and i > 0 else 0, hn.dev, hn.dev + n_kv * row,
+                    ch_rows // 2 if prefetch and i + 1 < n_layers else 0, an[0], an[1], ch_rows,
+                    state, state_b, out, copy_stream=copy_stream)
+            ms.append(t.stop_ms() / n_layers)
+        return _median(ms)
+
+    # untimed: the first passes over freshly pinned planes run up to ten times slower
+    chain_ms(False, 1)
+    chain_ms(True, 1)
+    plain = chain_ms(False)
+    chained = chain_ms(True)
+    layer_bytes = 2 * n_kv * row
+    res = {
+        "n_kv": n_kv, "n_head": 0, "n_q": n_q, "q_heads": n_qh, "kv_heads": kvh,
+        "layers": n_layers, "bucket_rows": ch_rows // 2, "host_bytes_per_layer": layer_bytes,
+        "pipelined_ms_per_layer": round(plain, 4),
+        "chain_ms_per_layer": round(chained, 4),
+        "chain_link_gbs": round(layer_bytes / (chained * 1e-3) / GB, 2),
+        "prefill_tok_s_pipelined": round(n_q / (plain * 1e-3), 1),
+        "prefill_tok_s_chain": round(n_q / (chained * 1e-3), 1),
+    }
+    log("prefill chain", res)
+    for hbuf in ch_hosts:
+        hbuf.free()
+    del ch_arenas, out, q, state
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_prefill(k, v, ht, q_np, n_head, n_kv, kvh, row, scale, stage_bytes, budget_s=20.0):
     """The oracle's staging (memcpy of the host tail) and fp64 prefill attention over a bounded
     sample of the last query rows (each sees ~180k keys): staging GB/s and attention tok/s."""
@@ -1142,11 +1216,15 @@ def suite_rows(torch, kvt, synth, dev, wl, peaks, row_counts=(1, 16, 64, 128, 25
 
 def run_suite(torch, kvt, synth, dev, wl, args, peaks):
     want = set(args.suite.split(",")) if args.suite != "all" else {
-        "prefill", "swap1", "small", "swap32", "qsa", "decode1m", "worker", "upkeep", "rows"}
+        "prefill", "chain", "swap1", "small", "swap32", "qsa", "decode1m", "worker", "upkeep",
+        "rows"}
     out = {}
     if "prefill" in want:
         log("suite: tiered prefill")
         out["tiered_prefill"] = suite_prefill(torch, kvt, synth, dev, peaks)
+    if "chain" in want:
+        log("suite: tiered prefill over a chain of layers, cache wholly in host memory")
+        out["tiered_prefill_chain"] = suite_prefill_chain(torch, kvt, synth, dev, peaks)
     if "swap1" in want:
         log("suite: one-layer swap")
         out["swap_1_layer"] = suite_one_layer(torch, kvt, synth, dev, peaks)

@@ -560,11 +560,20 @@ void launch_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, in
         launch(prefill_attn<KVT_BF16>);
 }
 
-// Events of the pipelined entry point, created once per thread and device and then reused:
-// [0] start, [1 + slot] slot filled, [3 + slot] slot free.
+// A first bucket copied ahead by one pipelined call for the next call on the same thread: the
+// host rows [0, rows) of the planes at k_host / v_host, now at the start of arena_k / arena_v.
+struct Prefetched {
+    int device = -1;
+    uintptr_t k_host = 0, v_host = 0, arena_k = 0, arena_v = 0;
+    int64_t row_bytes = 0, rows = 0;
+};
+
+// Events of the pipelined entry points, created once per thread and device and then reused:
+// [0] start, [1 + slot] slot filled, [3 + slot] slot free, [5] prefetch done.
 struct PipeEvents {
     int device = -1;
-    hipEvent_t e[5] = {};
+    hipEvent_t e[6] = {};
+    Prefetched pre;   // valid for the next pipelined call on this thread only
 };
 thread_local PipeEvents t_pipe;
 
@@ -579,6 +588,7 @@ int pipe_events(hipEvent_t *&ev)
             x = nullptr;
         }
         t_pipe.device = -1;
+        t_pipe.pre = Prefetched{};
         for (hipEvent_t &x : t_pipe.e)
             KVT_HIP(hipEventCreateWithFlags(&x, hipEventDisableTiming));
         t_pipe.device = dev;
@@ -717,9 +727,192 @@ extern "C" int kvt_attn_prefill_range(const void *q, int64_t n_q, int64_t q_pos0
     return KVT_OK;
 }
 
+namespace {
+
+// The next call's first host rows, copied at the end of this call (rows 0: no prefetch).
+struct NextBucket {
+    uintptr_t k_host = 0, v_host = 0, arena_k = 0, arena_v = 0;
+    int64_t rows = 0, arena_rows = 0;
+};
+
+bool ranges_overlap(uintptr_t a, uint64_t an, uintptr_t b, uint64_t bn)
+{
+    return an && bn && a < b + bn && b < a + an;
+}
+
+// S7+S8 overlapped (llama-T staging, with QSA-KVO's bounded arena and online-softmax fold over
+// buckets, and exl3-DMA's copy of the next layer's first batch while this layer is attended).  The first
+// `staged` host rows of bucket 0 are already in the arena (a previous call's prefetch).
+int prefill_pipeline(const char *fn, const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                     int32_t kvh, int32_t hd, const void *k_head, const void *v_head,
+                     int64_t n_head, const void *k_host, const void *v_host, int64_t n_kv,
+                     int32_t kv_format, int32_t causal, float scale, void *arena_k,
+                     void *arena_v, int64_t arena_rows, int64_t staged, const NextBucket &nx,
+                     void *state, size_t state_bytes_, float *out, void *stream,
+                     void *copy_stream)
+{
+    // whatever this call does, a prefetch left by the previous one is good for it alone
+    const Prefetched got = t_pipe.pre;
+    t_pipe.pre = Prefetched{};
+    int group = 0;
+    int64_t q_tiles = 0;
+    const int rc = check_prefill(fn, q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head,
+                                 k_host, v_host, n_kv, kv_format, scale, out, group, q_tiles);
+    if (rc != KVT_OK)
+        return rc;
+    if (staged < 0 || nx.rows < 0)
+        return kvt::fail(KVT_EINVAL, "%s: negative row count", fn);
+    hipStream_t s = kvt::as_stream(stream), cs = kvt::as_stream(copy_stream);
+    const bool prefetch = nx.rows > 0;
+    if (n_q == 0 && !staged && !prefetch)
+        return KVT_OK;
+    const bool host_rows = n_head < n_kv;
+    const int64_t row_bytes = (int64_t)kvh * head_bytes(kv_format);
+    const uintptr_t ak = reinterpret_cast<uintptr_t>(arena_k);
+    const uintptr_t av = reinterpret_cast<uintptr_t>(arena_v);
+    const uintptr_t hk = reinterpret_cast<uintptr_t>(k_host);
+    const uintptr_t hv = reinterpret_cast<uintptr_t>(v_host);
+    const int64_t slot_keys = arena_rows / 2 / kKT * kKT;
+    const int64_t hb = n_head / kKT * kKT;   // head keys in whole tiles; the rest by bucket
+    if (host_rows) {
+        if (slot_keys < kKT || !arena_k || !arena_v || !kvt::aligned(arena_k, 8) ||
+            !kvt::aligned(arena_v, 8))
+            return kvt::fail(KVT_EINVAL,
+                             "%s: arena of %lld rows (need >= 128, 8-byte aligned K and V)", fn,
+                             (long long)arena_rows);
+        if (!state || state_bytes_ < state_bytes(q_tiles, kvh) || !kvt::aligned(state, 4))
+            return kvt::fail(KVT_EINVAL, "%s: state of %zu bytes, need %zu", fn, state_bytes_,
+                             state_bytes(q_tiles, kvh));
+    }
+    if ((host_rows || prefetch) && cs == s)
+        return kvt::fail(KVT_EINVAL, "%s: copy_stream must differ from stream", fn);
+    if (staged) {
+        // host rows of bucket 0: keys [hb, hb + slot_keys) past the head
+        const int64_t b0 = host_rows ? (hb + slot_keys < n_kv ? hb + slot_keys : n_kv) - n_head
+                                     : 0;
+        if (got.rows != staged || got.k_host != hk || got.v_host != hv || got.arena_k != ak ||
+            got.arena_v != av || got.row_bytes != row_bytes)
+            return kvt::fail(KVT_EINVAL,
+                             "%s: %lld rows said to be staged, but the previous pipelined call "
+                             "on this thread prefetched %lld rows for other planes or arena",
+                             fn, (long long)staged, (long long)got.rows);
+        if (staged > b0)
+            return kvt::fail(KVT_EINVAL, "%s: %lld staged rows, but the first bucket holds %lld "
+                                         "host rows", fn, (long long)staged, (long long)b0);
+    }
+    if (prefetch) {
+        const int64_t nslot = nx.arena_rows / 2 / kKT * kKT;
+        if (nslot < kKT || !nx.arena_k || !nx.arena_v || !nx.k_host || !nx.v_host ||
+            nx.arena_k % 8 || nx.arena_v % 8)
+            return kvt::fail(KVT_EINVAL, "%s: next arena of %lld rows (need >= 128, 8-byte "
+                                         "aligned K and V) and next host planes", fn,
+                             (long long)nx.arena_rows);
+        if (nx.rows > nslot)
+            return kvt::fail(KVT_EINVAL, "%s: %lld rows to prefetch, but a bucket of the next "
+                                         "arena holds %lld", fn, (long long)nx.rows,
+                             (long long)nslot);
+        const uint64_t nb = (uint64_t)nx.rows * (uint64_t)row_bytes;
+        const uint64_t span = host_rows ? 2 * (uint64_t)slot_keys * (uint64_t)row_bytes : 0;
+        if (ranges_overlap(nx.arena_k, nb, ak, span) || ranges_overlap(nx.arena_k, nb, av, span) ||
+            ranges_overlap(nx.arena_v, nb, ak, span) || ranges_overlap(nx.arena_v, nb, av, span) ||
+            ranges_overlap(nx.arena_k, nb, nx.arena_v, nb))
+            return kvt::fail(KVT_EINVAL, "%s: the next arena overlaps this call's arena (or its "
+                                         "K half its V half)", fn);
+    }
+    int dev = 0;
+    KVT_HIP(hipGetDevice(&dev));
+    if (staged && got.device != dev)
+        return kvt::fail(KVT_EINVAL, "%s: the staged rows were prefetched on device %d, not %d",
+                         fn, got.device, dev);
+    hipEvent_t *ev = nullptr;
+    if (pipe_events(ev) != KVT_OK)
+        return KVT_EHIP;
+    float *stf = static_cast<float *>(state);
+
+    // the copies start after everything already on `stream` (the tail's producers, and the
+    // previous calls' passes over this arena and the next one)
+    if (host_rows || prefetch) {
+        KVT_HIP(hipEventRecord(ev[0], s));
+        KVT_HIP(hipStreamWaitEvent(cs, ev[0], 0));
+    }
+    if (n_q > 0 && !host_rows) {   // nothing in host memory
+        launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
+                       nullptr, nullptr, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out,
+                       kv_format, s);
+        KVT_LAUNCHED("prefill_attn");
+    } else if (n_q > 0) {
+        bool started = false;
+        if (hb > 0) {
+            launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
+                           nullptr, nullptr, n_kv, causal, scale, 0, hb, stf, 1, 0, out,
+                           kv_format, s);
+            KVT_LAUNCHED("prefill_attn");
+            started = true;
+        }
+        int b = 0;
+        for (int64_t kb = hb; kb < n_kv; kb += slot_keys, b++) {
+            const int64_t ke = kb + slot_keys < n_kv ? kb + slot_keys : n_kv;
+            const int slot = b & 1;
+            const int64_t r0 = kb > n_head ? kb : n_head;   // first host row of the bucket
+            const int64_t c0 = b == 0 ? r0 + staged : r0;   // first row this call copies
+            const uintptr_t sk = ak + (uintptr_t)(slot * slot_keys * row_bytes);
+            const uintptr_t sv = av + (uintptr_t)(slot * slot_keys * row_bytes);
+            if (c0 < ke) {
+                const size_t bytes = (size_t)(ke - c0) * (size_t)row_bytes;
+                const uintptr_t off = (uintptr_t)((c0 - r0) * row_bytes);
+                if (b >= 2)
+                    KVT_HIP(hipStreamWaitEvent(cs, ev[3 + slot], 0));
+                KVT_HIP(hipMemcpyAsync(
+                    reinterpret_cast<void *>(sk + off),
+                    reinterpret_cast<const void *>(hk + (c0 - n_head) * row_bytes), bytes,
+                    hipMemcpyDefault, cs));
+                KVT_HIP(hipMemcpyAsync(
+                    reinterpret_cast<void *>(sv + off),
+                    reinterpret_cast<const void *>(hv + (c0 - n_head) * row_bytes), bytes,
+                    hipMemcpyDefault, cs));
+                KVT_HIP(hipEventRecord(ev[1 + slot], cs));
+                KVT_HIP(hipStreamWaitEvent(s, ev[1 + slot], 0));
+            }
+            if (b == 0 && staged)
+                KVT_HIP(hipStreamWaitEvent(s, ev[5], 0));
+            // the kernel reads row r >= n_head at tail + (r - n_head)*row_bytes: aim it at the
+            // slot
+            const uintptr_t shift = (uintptr_t)((r0 - n_head) * row_bytes);
+            launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
+                           reinterpret_cast<const void *>(sk - shift),
+                           reinterpret_cast<const void *>(sv - shift), n_kv, causal, scale, kb,
+                           ke, stf, started ? 0 : 1, ke == n_kv ? 1 : 0, out, kv_format, s);
+            KVT_LAUNCHED("prefill_attn");
+            started = true;
+            KVT_HIP(hipEventRecord(ev[3 + slot], s));
+        }
+    }
+    if (prefetch) {   // behind this call's own copies, while its last buckets are attended
+        const size_t nb = (size_t)nx.rows * (size_t)row_bytes;
+        KVT_HIP(hipMemcpyAsync(reinterpret_cast<void *>(nx.arena_k),
+                               reinterpret_cast<const void *>(nx.k_host), nb, hipMemcpyDefault,
+                               cs));
+        KVT_HIP(hipMemcpyAsync(reinterpret_cast<void *>(nx.arena_v),
+                               reinterpret_cast<const void *>(nx.v_host), nb, hipMemcpyDefault,
+                               cs));
+        KVT_HIP(hipEventRecord(ev[5], cs));
+        Prefetched p;
+        p.device = dev;
+        p.k_host = nx.k_host;
+        p.v_host = nx.v_host;
+        p.arena_k = nx.arena_k;
+        p.arena_v = nx.arena_v;
+        p.row_bytes = row_bytes;
+        p.rows = nx.rows;
+        t_pipe.pre = p;
+    }
+    return KVT_OK;
+}
+
+}  // namespace
+
 // S7+S8 overlapped: the host tail crosses the link in arena-sized buckets on copy_stream while
-// stream attends the HBM head and then each staged bucket (llama-T staging, with the pages'
-// bounded arena and online-softmax fold over buckets).
+// stream attends the HBM head and then each staged bucket.
 extern "C" int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_pos0,
                                           int32_t n_qh, int32_t kvh, int32_t hd,
                                           const void *k_head, const void *v_head, int64_t n_head,
@@ -729,86 +922,35 @@ extern "C" int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_
                                           void *state, size_t state_bytes_, float *out,
                                           void *stream, void *copy_stream)
 {
-    int group = 0;
-    int64_t q_tiles = 0;
-    const int rc = check_prefill("kvt_attn_prefill_pipelined", q, n_q, q_pos0, n_qh, kvh, hd,
-                                 k_head, v_head, n_head, k_host, v_host, n_kv, kv_format, scale,
-                                 out, group, q_tiles);
-    if (rc != KVT_OK)
-        return rc;
-    hipStream_t s = kvt::as_stream(stream), cs = kvt::as_stream(copy_stream);
-    if (n_q == 0)
-        return KVT_OK;
-    if (n_head == n_kv) {   // nothing in host memory
-        launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
-                       nullptr, nullptr, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out,
-                       kv_format, s);
-        KVT_LAUNCHED("prefill_attn");
-        return KVT_OK;
-    }
-    const int64_t slot_keys = arena_rows / 2 / kKT * kKT;
-    if (slot_keys < kKT || !arena_k || !arena_v || !kvt::aligned(arena_k, 8) ||
-        !kvt::aligned(arena_v, 8))
-        return kvt::fail(KVT_EINVAL,
-                         "kvt_attn_prefill_pipelined: arena of %lld rows (need >= 128, 8-byte "
-                         "aligned K and V)",
-                         (long long)arena_rows);
-    if (cs == s)
-        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill_pipelined: copy_stream must differ from "
-                                     "stream");
-    if (!state || state_bytes_ < state_bytes(q_tiles, kvh) || !kvt::aligned(state, 4))
-        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill_pipelined: state of %zu bytes, need %zu",
-                         state_bytes_, state_bytes(q_tiles, kvh));
-    hipEvent_t *ev = nullptr;
-    if (pipe_events(ev) != KVT_OK)
-        return KVT_EHIP;
-    const int64_t row_bytes = (int64_t)kvh * head_bytes(kv_format);
-    const uintptr_t ak = reinterpret_cast<uintptr_t>(arena_k);
-    const uintptr_t av = reinterpret_cast<uintptr_t>(arena_v);
-    const uintptr_t hk = reinterpret_cast<uintptr_t>(k_host);
-    const uintptr_t hv = reinterpret_cast<uintptr_t>(v_host);
-    float *stf = static_cast<float *>(state);
+    return prefill_pipeline("kvt_attn_prefill_pipelined", q, n_q, q_pos0, n_qh, kvh, hd, k_head,
+                            v_head, n_head, k_host, v_host, n_kv, kv_format, causal, scale,
+                            arena_k, arena_v, arena_rows, 0, NextBucket{}, state, state_bytes_,
+                            out, stream, copy_stream);
+}
 
-    // the copies start after everything already on `stream` (the tail's producers, and the
-    // previous call's passes over the arena)
-    KVT_HIP(hipEventRecord(ev[0], s));
-    KVT_HIP(hipStreamWaitEvent(cs, ev[0], 0));
-    const int64_t hb = n_head / kKT * kKT;   // head keys in whole tiles; the rest by bucket
-    bool started = false;
-    if (hb > 0) {
-        launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
-                       nullptr, nullptr, n_kv, causal, scale, 0, hb, stf, 1, 0, out, kv_format,
-                       s);
-        KVT_LAUNCHED("prefill_attn");
-        started = true;
-    }
-    int b = 0;
-    for (int64_t kb = hb; kb < n_kv; kb += slot_keys, b++) {
-        const int64_t ke = kb + slot_keys < n_kv ? kb + slot_keys : n_kv;
-        const int slot = b & 1;
-        const int64_t r0 = kb > n_head ? kb : n_head;   // first host row of the bucket
-        const size_t bytes = (size_t)(ke - r0) * (size_t)row_bytes;
-        const uintptr_t sk = ak + (uintptr_t)(slot * slot_keys * row_bytes);
-        const uintptr_t sv = av + (uintptr_t)(slot * slot_keys * row_bytes);
-        if (b >= 2)
-            KVT_HIP(hipStreamWaitEvent(cs, ev[3 + slot], 0));
-        KVT_HIP(hipMemcpyAsync(reinterpret_cast<void *>(sk),
-                               reinterpret_cast<const void *>(hk + (r0 - n_head) * row_bytes),
-                               bytes, hipMemcpyDefault, cs));
-        KVT_HIP(hipMemcpyAsync(reinterpret_cast<void *>(sv),
-                               reinterpret_cast<const void *>(hv + (r0 - n_head) * row_bytes),
-                               bytes, hipMemcpyDefault, cs));
-        KVT_HIP(hipEventRecord(ev[1 + slot], cs));
-        KVT_HIP(hipStreamWaitEvent(s, ev[1 + slot], 0));
-        // the kernel reads row r >= n_head at tail + (r - n_head)*row_bytes: aim it at the slot
-        const uintptr_t shift = (uintptr_t)((r0 - n_head) * row_bytes);
-        launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
-                       reinterpret_cast<const void *>(sk - shift),
-                       reinterpret_cast<const void *>(sv - shift), n_kv, causal, scale, kb, ke,
-                       stf, started ? 0 : 1, ke == n_kv ? 1 : 0, out, kv_format, s);
-        KVT_LAUNCHED("prefill_attn");
-        started = true;
-        KVT_HIP(hipEventRecord(ev[3 + slot], s));
-    }
-    return KVT_OK;
+// The same op in a chain of layers: the first `staged_rows` host rows were prefetched by the
+// previous call, and the next layer's first `next_rows` host rows are copied into its arena
+// behind this call's own copies.
+extern "C" int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                                      int32_t kvh, int32_t hd, const void *k_head,
+                                      const void *v_head, int64_t n_head, const void *k_host,
+                                      const void *v_host, int64_t n_kv, int32_t kv_format,
+                                      int32_t causal, float scale, void *arena_k, void *arena_v,
+                                      int64_t arena_rows, int64_t staged_rows,
+                                      const void *next_k_host, const void *next_v_host,
+                                      int64_t next_rows, void *next_arena_k, void *next_arena_v,
+                                      int64_t next_arena_rows, void *state, size_t state_bytes_,
+                                      float *out, void *stream, void *copy_stream)
+{
+    NextBucket nx;
+    nx.k_host = reinterpret_cast<uintptr_t>(next_k_host);
+    nx.v_host = reinterpret_cast<uintptr_t>(next_v_host);
+    nx.arena_k = reinterpret_cast<uintptr_t>(next_arena_k);
+    nx.arena_v = reinterpret_cast<uintptr_t>(next_arena_v);
+    nx.rows = next_rows;
+    nx.arena_rows = next_arena_rows;
+    return prefill_pipeline("kvt_attn_prefill_chain", q, n_q, q_pos0, n_qh, kvh, hd, k_head,
+                            v_head, n_head, k_host, v_host, n_kv, kv_format, causal, scale,
+                            arena_k, arena_v, arena_rows, staged_rows, nx, state, state_bytes_,
+                            out, stream, copy_stream);
 }

@@ -56,6 +56,10 @@ _SIGNATURES = {
     "kvt_attn_prefill_pipelined": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P,
                                            _P, c_int64, _P, _P, c_int64, c_int32, c_int32,
                                            c_float, _P, _P, c_int64, _P, c_size_t, _P, _P, _P]),
+    "kvt_attn_prefill_chain": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P,
+                                       c_int64, _P, _P, c_int64, c_int32, c_int32, c_float, _P,
+                                       _P, c_int64, c_int64, _P, _P, c_int64, _P, _P, c_int64,
+                                       _P, c_size_t, _P, _P, _P]),
     "kvt_worker_create": (c_int, [c_int32, c_int32, ctypes.POINTER(c_void_p)]),
     "kvt_worker_reserve": (c_int, [_P, c_int32, c_int64]),
     "kvt_worker_submit": (c_int, [_P, c_int64, _P, _P, _P, c_int64, _P]),
@@ -292,6 +296,21 @@ def kvt_attn_prefill_pipelined(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_
         int(n_head), _ptr(k_host), _ptr(v_host), int(n_kv), int(kv_format), int(bool(causal)),
         float(scale), _ptr(arena_k), _ptr(arena_v), int(arena_rows), _ptr(state),
         int(state_bytes), _ptr(out), _stream(stream), _stream(copy_stream)))
+
+
+def kvt_attn_prefill_chain(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_host,
+                           v_host, n_kv, kv_format, causal, scale, arena_k, arena_v, arena_rows,
+                           staged_rows, next_k_host, next_v_host, next_rows, next_arena_k,
+                           next_arena_v, next_arena_rows, state, state_bytes, out, stream=None,
+                           copy_stream=None):
+    """kvt_attn_prefill_pipelined in a chain of layers (next-layer prefetch)."""
+    _check("kvt_attn_prefill_chain", load().kvt_attn_prefill_chain(
+        _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
+        int(n_head), _ptr(k_host), _ptr(v_host), int(n_kv), int(kv_format), int(bool(causal)),
+        float(scale), _ptr(arena_k), _ptr(arena_v), int(arena_rows), int(staged_rows),
+        _ptr(next_k_host), _ptr(next_v_host), int(next_rows), _ptr(next_arena_k),
+        _ptr(next_arena_v), int(next_arena_rows), _ptr(state), int(state_bytes), _ptr(out),
+        _stream(stream), _stream(copy_stream)))
 
 
 def kvt_worker_create(direction, mode=COPY_AUTO) -> int:

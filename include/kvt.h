@@ -18,6 +18,7 @@
  *   kvt_attn_prefill     causal (or full) prefill attention over an HBM head + tail
  *   kvt_attn_prefill_range      the same attention as resumable passes over key ranges
  *   kvt_attn_prefill_pipelined  tail staging in arena buckets overlapped with the attention
+ *   kvt_attn_prefill_chain      the same over a chain of layers, prefetching the next layer
  *   kvt_worker_*         an ordered, event-timed asynchronous transfer queue around the swap
  *   kvt_paged_write      append new K/V (and raw key) rows into paged planes via a block table
  *   kvt_copy_page        duplicate a page's first rows (host planes on the CPU, pooled on device)
@@ -26,6 +27,7 @@
  *   [vLLM-CPU] vLLM fork, "v1/kv_offload/cpu/gpu_worker.py" (CPU offloading worker)
  *   [QSA-KVO]  "QSA KV cache host-RAM offload for ExLlamaV3" (qsa-kv-offload.patch)
  *   [llama-T]  "llama/cuda: tiered KV cache (--kv-vram-cells)", llama.cpp PR #319
+ *   [exl3-DMA] vllm-exl3 patch "vllm-exl3-host-dma.patch" (prefill DMA streaming into VRAM slots)
  *
  * Conventions (all entry points):
  *   - The caller owns every buffer.  The library allocates nothing on the hot path; where an
@@ -55,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 11
+#define KVT_ABI_VERSION 12
 
 /* status codes */
 #define KVT_OK 0
@@ -391,7 +393,7 @@ int kvt_attn_prefill_range(const void *q, int64_t n_q, int64_t q_pos0, int32_t n
  *   stream, copy_stream two different streams; the copies wait for everything enqueued on
  *                       `stream` before the call, and `stream` waits for each copy it reads,
  *                       so the op is ordered on `stream` like any other call.
- * The output equals kvt_attn_prefill's bit for bit.  The library keeps five events per host
+ * The output equals kvt_attn_prefill's bit for bit.  The library keeps six events per host
  * thread (created on the first call on a device, then reused); calls from one thread are
  * ordered through them, so two calls on one thread must use the same `stream`.
  * Limits: as kvt_attn_prefill.
@@ -402,6 +404,39 @@ int kvt_attn_prefill_pipelined(const void *q, int64_t n_q, int64_t q_pos0, int32
                                int64_t n_kv, int32_t kv_format, int32_t causal, float scale,
                                void *arena_k, void *arena_v, int64_t arena_rows, void *state,
                                size_t state_bytes, float *out, void *stream, void *copy_stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S7+S8 overlapped across layers.  [exl3-DMA]'s prefill streaming copies the next layer's
+ * first batches into VRAM slots while the current layer runs.  kvt_attn_prefill_pipelined exposes the
+ * copy of its first bucket whenever the HBM head is too short to hide it; in a chain of calls,
+ * one per layer, each call can copy the next call's first host rows behind its own copies:
+ *   next_k_host, next_v_host, next_arena_k, next_arena_v, next_arena_rows
+ *                       the next call's k_host, v_host, arena_k, arena_v and arena_rows
+ *   next_rows           host rows [0, next_rows) of the next call's planes (its rows
+ *                       n_head ...) to copy into the start of its arena; 0 = no prefetch.
+ *                       At most one bucket of the next arena.  Those rows must be final when
+ *                       this call is enqueued; rows written later (this chunk's own keys, say)
+ *                       are left to the next call.
+ *   staged_rows         how many rows the previous call prefetched for this one (0 = none).
+ *                       Must equal that call's next_rows, with the same planes and arena, and
+ *                       fit this call's first bucket; else KVT_EINVAL and nothing enqueued.
+ * Everything else as kvt_attn_prefill_pipelined, whose calls also take part: each call to
+ * either entry point ends the previous prefetch of its thread, used or not, even when it
+ * fails its checks.  Calls of a chain come from one host thread, in order, on the same
+ * `stream`.  The prefetch waits for everything enqueued on `stream` before this call (the
+ * previous layer's passes over the next arena), so the next arena must not overlap this
+ * call's arena (KVT_EINVAL) and must not be read by anything this call reads: two arenas,
+ * alternating between layers, are enough.  Outputs equal kvt_attn_prefill's bit for bit.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh,
+                           int32_t hd, const void *k_head, const void *v_head, int64_t n_head,
+                           const void *k_host, const void *v_host, int64_t n_kv,
+                           int32_t kv_format, int32_t causal, float scale, void *arena_k,
+                           void *arena_v, int64_t arena_rows, int64_t staged_rows,
+                           const void *next_k_host, const void *next_v_host, int64_t next_rows,
+                           void *next_arena_k, void *next_arena_v, int64_t next_arena_rows,
+                           void *state, size_t state_bytes, float *out, void *stream,
+                           void *copy_stream);
 
 /* ----------------------------------------------------------------------------------------
  * Transfer worker.  [vLLM-CPU] SingleDirectionOffloadingHandler: transfer_async,

@@ -48,7 +48,7 @@ def test_binding_constants_equal_the_header():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 11
+    assert kvt.kvt_abi_version() == 12
 
 
 def test_library_has_gfx950_code_object():
@@ -150,6 +150,20 @@ def test_argument_errors_return_before_any_device_work():
                    dict(arena_k=None)):
         with pytest.raises(kvt.KvtError) as e:
             kvt.kvt_attn_prefill_pipelined(**{**pipe, **change})
+        assert e.value.code == kvt.EINVAL, change
+    chain = dict(pipe, staged_rows=0, next_k_host=16, next_v_host=16, next_rows=64,
+                 next_arena_k=1 << 40, next_arena_v=1 << 41, next_arena_rows=4096)
+    for change in (dict(next_rows=2049),                     # more than one next bucket
+                   dict(next_arena_rows=100),                # next buckets under 64 keys
+                   dict(next_k_host=None), dict(next_arena_v=None),
+                   dict(next_arena_k=1 << 40 | 4),           # misaligned
+                   dict(next_arena_k=16),                    # overlaps this call's arena
+                   dict(next_arena_v=(1 << 40) + 64 * 1088 - 8),   # next K and V overlap
+                   dict(next_rows=-1),
+                   dict(staged_rows=1),                      # nothing was prefetched
+                   dict(copy_stream=0)):
+        with pytest.raises(kvt.KvtError) as e:
+            kvt.kvt_attn_prefill_chain(**{**chain, **change})
         assert e.value.code == kvt.EINVAL, change
     assert kvt.kvt_attn_prefill_state_bytes(2048, 32, 8) == 32 * 8 * 8 * 66 * 64 * 4
     assert kvt.kvt_attn_prefill_state_bytes(10, 12, 1) == 0      # group 12: unsupported

@@ -4,6 +4,7 @@
   the full 180,000-token geometry);
 * bit-identical output whether the cache is all in HBM, split into an HBM head plus a staged
   tail, or split with the tail read in place from host memory (staging off)."""
+import functools
 import math
 
 import numpy as np
@@ -46,6 +47,12 @@ def _prefill(q_np, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, ca
 
 def _dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+@functools.lru_cache(maxsize=1)
+def _full_cache():
+    """The 180,000-row q8_0 cache (8 KV heads) of the full-size tests, generated once."""
+    return _cache(180000, 8, 180000)
 
 
 @pytest.mark.parametrize("n_kv,n_q,n_qh,kvh,causal,n_head", [
@@ -208,7 +215,7 @@ def test_prefill_full_geometry_sampled_rows(gpu):
     host rows into HBM once, run the attention, compare sampled query rows (all heads, all
     dims) with the fp64 oracle; staging on/off and all-HBM agree bit for bit."""
     n_kv, n_head, n_q, n_qh, kvh = 180000, 94208, 2048, 32, 8
-    k, v = _cache(n_kv, kvh, 180000)
+    k, v = _full_cache()
     row = k.shape[1]
     n_tail = n_kv - n_head
     q = synth.f16_normal(synth.rng(5, synth.P_Q, 180000), (n_q, n_qh, 128))
@@ -302,6 +309,165 @@ def test_prefill_pipelined_fp_caches_bit_identical(gpu, fmt):
                      gpu, fmt=fmt)
     assert np.array_equal(got.view(np.uint32), all_hbm.view(np.uint32))
     host.free()
+
+
+class _Chain:
+    """Layers of a kvt_attn_prefill_chain run: per layer a q8_0 cache (K, V rows), queries, host
+    planes holding rows [n_head, n_kv) (K rows then V rows) and an output; two arenas taken in
+    turn."""
+
+    def __init__(self, dev, n_kv, n_q, n_qh, kvh, geo, seed, caches=None):
+        self.dev, self.n_kv, self.n_q, self.n_qh, self.kvh = dev, n_kv, n_q, n_qh, kvh
+        self.geo = geo                       # [(n_head, arena_rows, staged_rows)] per layer
+        self.caches = caches or [_cache(n_kv, kvh, seed + i) for i in range(len(geo))]
+        self.row = self.caches[0][0].shape[1]
+        self.q = [torch.from_numpy(synth.f16_normal(synth.rng(5, synth.P_Q, seed + 50 + i),
+                                                    (n_q, n_qh, 128)).view(np.int16)).to(dev)
+                  for i in range(len(geo))]
+        self.host = []
+        for (n_head, _, _), (k, v) in zip(geo, self.caches):
+            h = kvt.HostBuffer(max(2 * (n_kv - n_head) * self.row, 16))
+            self.host.append(h)
+            if n_kv > n_head:
+                self.planes(len(self.host) - 1)[:] = np.stack([k[n_head:], v[n_head:]])
+        cap = max(a for _, a, _ in geo)
+        self.arena = [torch.full((2, cap, self.row), 0xA5, dtype=torch.uint8, device=dev)
+                      for _ in range(2)]
+        self.heads = [(_dev(k[:max(nh, 1)], dev), _dev(v[:max(nh, 1)], dev))
+                      for (nh, _, _), (k, v) in zip(geo, self.caches)]
+        self.sb = kvt.kvt_attn_prefill_state_bytes(n_q, n_qh, kvh)
+        self.state = torch.empty(self.sb, dtype=torch.uint8, device=dev)
+        self.copy_stream = torch.cuda.Stream()
+        self.out = [torch.empty((n_q, n_qh, 128), dtype=torch.float32, device=dev)
+                    for _ in geo]
+
+    def planes(self, i):
+        n_tail = self.n_kv - self.geo[i][0]
+        return self.host[i].numpy(np.uint8, (2, n_tail, self.row))
+
+    def args(self, i, staged=None, next_rows=None):
+        n_head, arena_rows, st = self.geo[i]
+        j = i + 1
+        nxt = self.geo[j][2] if j < len(self.geo) else 0
+        a, an = self.arena[i % 2], self.arena[j % 2]
+        n_tail = self.n_kv - n_head
+        hd_ = self.host[j].dev if j < len(self.geo) else 0
+        nt_next = self.n_kv - self.geo[j][0] if j < len(self.geo) else 0
+        return dict(q=self.q[i], n_q=self.n_q, q_pos0=self.n_kv - self.n_q, n_qh=self.n_qh,
+                    kvh=self.kvh, hd=128, k_head=self.heads[i][0], v_head=self.heads[i][1],
+                    n_head=n_head, k_host=self.host[i].dev,
+                    v_host=self.host[i].dev + n_tail * self.row, n_kv=self.n_kv,
+                    kv_format=kvt.Q8_0, causal=1, scale=1 / math.sqrt(128), arena_k=a[0],
+                    arena_v=a[1], arena_rows=arena_rows,
+                    staged_rows=st if staged is None else staged,
+                    next_k_host=hd_, next_v_host=hd_ + nt_next * self.row,
+                    next_rows=nxt if next_rows is None else next_rows, next_arena_k=an[0],
+                    next_arena_v=an[1],
+                    next_arena_rows=self.geo[j][1] if j < len(self.geo) else 0,
+                    state=self.state, state_bytes=self.sb, out=self.out[i],
+                    copy_stream=self.copy_stream)
+
+    def call(self, i, **kw):
+        for o in self.out[i:i + 1]:
+            o.fill_(float("nan"))
+        kvt.kvt_attn_prefill_chain(**self.args(i, **kw))
+
+    def expected(self, i):
+        k, v = self.caches[i]
+        kd, vd = _dev(k, self.dev), _dev(v, self.dev)
+        out = torch.full((self.n_q, self.n_qh, 128), float("nan"), dtype=torch.float32,
+                         device=self.dev)
+        kvt.kvt_attn_prefill(self.q[i], self.n_q, self.n_kv - self.n_q, self.n_qh, self.kvh,
+                             128, kd, vd, self.n_kv, None, None, self.n_kv, kvt.Q8_0, 1,
+                             1 / math.sqrt(128), out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def free(self):
+        for h in self.host:
+            h.free()
+
+
+def test_prefill_chain_bit_identical(gpu):
+    """Six layers in a chain, two arenas in turn, each call copying the next layer's first host
+    rows behind its own copies: every layer's output has the bits of the single pass over an
+    all-HBM cache.  Covered: a full and a partial prefetch, a head split mid-tile, a layer with
+    nothing in host memory (which still prefetches for the next), 64-key buckets, and host rows
+    written by the CPU after the prefetching call was enqueued (left to the next call)."""
+    geo = [(0, 1000, 0),         # 448-key buckets from key 0
+           (2100, 1000, 396),    # head split mid-tile; all 396 host rows of bucket 0 prefetched
+           (5000, 128, 0),       # nothing in host memory; prefetches for the next layer
+           (0, 10240, 3000),     # one bucket of 5000 rows, 3000 prefetched, 2000 written later
+           (2048, 128, 64),      # 64-key buckets, the first one prefetched whole
+           (2100, 1000, 200)]    # part of a mid-tile bucket prefetched
+    ch = _Chain(gpu, 5000, 300, 32, 8, geo, 700)
+    want = [ch.expected(i) for i in range(len(geo))]
+    late = ch.planes(3)[:, 3000:].copy()
+    for run in range(2):
+        if run == 0:
+            ch.planes(3)[:, 3000:] = 0xA5     # not final yet when layer 2's call is enqueued
+        for i in range(len(geo)):
+            ch.call(i)
+            if run == 0 and i == 2:
+                ch.planes(3)[:, 3000:] = late   # the CPU writes them before layer 3's call
+        torch.cuda.synchronize()
+        for i in range(len(geo)):
+            got = ch.out[i].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), want[i].view(np.uint32)), (run, i)
+    ch.free()
+
+
+def test_prefill_chain_prefetch_is_for_the_next_call_only(gpu):
+    """A staged_rows that does not match the previous call's prefetch fails with KVT_EINVAL and
+    enqueues nothing: after a plain pipelined call in between, with another row count, with more
+    rows than the first bucket holds, and on the retry after a failure."""
+    geo = [(0, 1000, 0), (2100, 1000, 396)]
+    ch = _Chain(gpu, 5000, 300, 32, 8, geo, 720)
+    want = ch.expected(1)
+
+    def fails(**kw):
+        with pytest.raises(kvt.KvtError) as e:
+            ch.call(1, **kw)
+        assert e.value.code == kvt.EINVAL
+
+    ch.call(0)
+    a = {k_: v_ for k_, v_ in ch.args(0).items()
+         if k_ not in ("staged_rows", "next_k_host", "next_v_host", "next_rows", "next_arena_k",
+                       "next_arena_v", "next_arena_rows")}
+    kvt.kvt_attn_prefill_pipelined(**a)
+    fails()                                  # the pipelined call ended the prefetch
+    ch.call(0)
+    fails(staged=395)                        # another row count
+    fails()                                  # ... and the failure ended it too
+    ch.call(0, next_rows=448)                # a whole next bucket of rows, but bucket 0
+    fails(staged=448)                        # of layer 1 holds only 396 host rows
+    ch.call(0)
+    ch.call(1)                               # the matching call
+    torch.cuda.synchronize()
+    assert np.array_equal(ch.out[1].cpu().numpy().view(np.uint32), want.view(np.uint32))
+    ch.call(1, staged=0)                     # no prefetch: copies its whole first bucket
+    torch.cuda.synchronize()
+    assert np.array_equal(ch.out[1].cpu().numpy().view(np.uint32), want.view(np.uint32))
+    ch.free()
+
+
+def test_prefill_chain_full_geometry(gpu):
+    """Two layers of the 180,000-token q8_0 cache wholly in host memory (n_head 0), 2048 queries x
+    32 heads, 16,384-row buckets, the second layer's first bucket prefetched by the first call
+    (the configuration the benchmark times): each equals the all-HBM single pass bit for bit."""
+    k, v = _full_cache()
+    # the second layer: K and V swapped and rolled, so that a mix-up of layers shows
+    caches = [(k, v), (np.roll(v, 7, axis=0), np.roll(k, 7, axis=0))]
+    geo = [(0, 32768, 0), (0, 32768, 16384)]
+    ch = _Chain(gpu, 180000, 2048, 32, 8, geo, 740, caches=caches)
+    want = [ch.expected(i) for i in range(2)]
+    ch.call(0)
+    ch.call(1)
+    torch.cuda.synchronize()
+    for i in range(2):
+        got = ch.out[i].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want[i].view(np.uint32)), i
+    ch.free()
 
 
 def _splitk(q_np, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, causal, dev,
