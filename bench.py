@@ -516,6 +516,7 @@ def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
     t = Timer(torch, torch.cuda.current_stream())
     out = {}
     g = synth.rng(2, synth.P_SKIP)
+    build_ms = []   # S1 on the host: both sides' tables for all 64 tensors, 128 calls
     for direction, dname in ((kvt.H2D, "h2d"), (kvt.D2H, "d2h")):
         for mode, mname in [(getattr(kvt, c), n) for c, n in COPY_MODES_SPEC]:
             rates = []
@@ -526,11 +527,13 @@ def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
                 gids = synth.permutation(synth.rng(2, synth.P_PERM_DST, r), gblocks)[:n]
                 hrow = tab[0 if direction == kvt.H2D else 1]
                 grow = tab[1 if direction == kvt.H2D else 0]
+                t0 = time.perf_counter()
                 for x in range(tensors):
                     kvt.kvt_sub_block_ptrs(host.dev + x * hrows * stride, stride, page, chunks, nch,
                                            bpc, skip, hrow[x * n:], n)
                     kvt.kvt_sub_block_ptrs(hbm.data_ptr() + x * gblocks * page, page, page, gids,
                                            n, 1, 0, grow[x * n:], n)
+                build_ms.append((time.perf_counter() - t0) * 1e3)
                 tab[2] = page
                 rate, ms = _swap_rate(torch, kvt, t, tab, tensors * n, direction, mode,
                                       tensors * n * page)
@@ -540,6 +543,8 @@ def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
             out[f"{dname}_{mname}_gbs"] = round(_median(rates), 2)
             out[f"{dname}_{mname}_pct_measured_peak"] = round(100 * _median(rates) / peak, 1)
     out["bytes_per_direction"] = tensors * n * page
+    out["table_build_ms"] = round(_median(build_ms[1:]), 3)   # the first build pays page faults
+    out["table_build_descriptors_per_s"] = round(2 * tensors * n / (_median(build_ms[1:]) * 1e-3))
     # CPU baseline on one tensor's load (4096 pages of 32 KiB = 128 MiB), the last ids drawn
     kvt.kvt_sub_block_ptrs(host.dev, stride, page, chunks, nch, bpc, skip, tab[0], n)
     kvt.kvt_sub_block_ptrs(hbm.data_ptr(), page, page, gids, n, 1, 0, tab[1], n)
