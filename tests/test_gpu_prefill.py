@@ -316,10 +316,11 @@ class _Chain:
     planes holding rows [n_head, n_kv) (K rows then V rows) and an output; two arenas taken in
     turn."""
 
-    def __init__(self, dev, n_kv, n_q, n_qh, kvh, geo, seed, caches=None):
+    def __init__(self, dev, n_kv, n_q, n_qh, kvh, geo, seed, caches=None, fmt=kvt.Q8_0):
         self.dev, self.n_kv, self.n_q, self.n_qh, self.kvh = dev, n_kv, n_q, n_qh, kvh
+        self.fmt = fmt
         self.geo = geo                       # [(n_head, arena_rows, staged_rows)] per layer
-        self.caches = caches or [_cache(n_kv, kvh, seed + i) for i in range(len(geo))]
+        self.caches = caches or [_cache(n_kv, kvh, seed + i, fmt) for i in range(len(geo))]
         self.row = self.caches[0][0].shape[1]
         self.q = [torch.from_numpy(synth.f16_normal(synth.rng(5, synth.P_Q, seed + 50 + i),
                                                     (n_q, n_qh, 128)).view(np.int16)).to(dev)
@@ -357,7 +358,7 @@ class _Chain:
                     kvh=self.kvh, hd=128, k_head=self.heads[i][0], v_head=self.heads[i][1],
                     n_head=n_head, k_host=self.host[i].dev,
                     v_host=self.host[i].dev + n_tail * self.row, n_kv=self.n_kv,
-                    kv_format=kvt.Q8_0, causal=1, scale=1 / math.sqrt(128), arena_k=a[0],
+                    kv_format=self.fmt, causal=1, scale=1 / math.sqrt(128), arena_k=a[0],
                     arena_v=a[1], arena_rows=arena_rows,
                     staged_rows=st if staged is None else staged,
                     next_k_host=hd_, next_v_host=hd_ + nt_next * self.row,
@@ -378,7 +379,7 @@ class _Chain:
         out = torch.full((self.n_q, self.n_qh, 128), float("nan"), dtype=torch.float32,
                          device=self.dev)
         kvt.kvt_attn_prefill(self.q[i], self.n_q, self.n_kv - self.n_q, self.n_qh, self.kvh,
-                             128, kd, vd, self.n_kv, None, None, self.n_kv, kvt.Q8_0, 1,
+                             128, kd, vd, self.n_kv, None, None, self.n_kv, self.fmt, 1,
                              1 / math.sqrt(128), out)
         torch.cuda.synchronize()
         return out.cpu().numpy()
@@ -414,6 +415,27 @@ def test_prefill_chain_bit_identical(gpu):
         for i in range(len(geo)):
             got = ch.out[i].cpu().numpy()
             assert np.array_equal(got.view(np.uint32), want[i].view(np.uint32)), (run, i)
+    ch.free()
+
+
+@pytest.mark.parametrize("fmt,n_qh,kvh", [
+    (kvt.F16, 16, 4),     # 256-byte head slices, group 4
+    (kvt.BF16, 8, 8),     # group 1
+    (kvt.Q8_0, 64, 8),    # group 8
+], ids=["f16-g4", "bf16-g1", "q8_0-g8"])
+def test_prefill_chain_formats_and_groups(gpu, fmt, n_qh, kvh):
+    """Three chained layers over fp16, bf16 and q8_0 caches and query groups 1, 4 and 8: a
+    partial and a full prefetch, a head split mid-tile; each output equals the all-HBM single
+    pass bit for bit."""
+    geo = [(1000, 600, 0), (0, 512, 200), (2100, 1000, 396)]
+    ch = _Chain(gpu, 3000, 200, n_qh, kvh, geo, 760 + fmt, fmt=fmt)
+    want = [ch.expected(i) for i in range(len(geo))]
+    for i in range(len(geo)):
+        ch.call(i)
+    torch.cuda.synchronize()
+    for i in range(len(geo)):
+        got = ch.out[i].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want[i].view(np.uint32)), i
     ch.free()
 
 
