@@ -816,8 +816,8 @@ int prefill_pipeline(const char *fn, const void *q, int64_t n_q, int64_t q_pos0,
         if (ranges_overlap(nx.arena_k, nb, ak, span) || ranges_overlap(nx.arena_k, nb, av, span) ||
             ranges_overlap(nx.arena_v, nb, ak, span) || ranges_overlap(nx.arena_v, nb, av, span) ||
             ranges_overlap(nx.arena_k, nb, nx.arena_v, nb))
-            return kvt::fail(KVT_EINVAL, "%s: the next arena overlaps this call's arena (or its "
-                                         "K half its V half)", fn);
+            return kvt::fail(KVT_EINVAL, "%s: the next arena overlaps this call's arena, or its "
+                                         "K rows overlap its V rows", fn);
     }
     int dev = 0;
     KVT_HIP(hipGetDevice(&dev));
