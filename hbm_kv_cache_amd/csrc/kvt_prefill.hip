@@ -13,7 +13,8 @@
 //   * the tile's raw q8_0 head slices (64 keys x 136 bytes per plane, 1088 bytes apart in the
 //     cache rows) are read with coalesced 8-byte loads -- consecutive lanes on consecutive words
 //     of one slice, so a load instruction touches a handful of cache lines rather than one per
-//     lane -- and parked in LDS;
+//     lane -- and parked in LDS (fp16 / bf16 slices of 256 bytes: 16-byte loads when the cache
+//     pointers are 16-byte aligned, else 8-byte ones);
 //   * every thread then owns one q8_0 block of the tile (plane K or V, key = lane, block 0..3)
 //     and dequantises it to fp16 with a magic-number conversion (the int8 byte under 0x64 is
 //     1024 + 128 + q in fp16; subtracting 1152 is exact; times the block scale is the one
@@ -30,6 +31,7 @@
 //     and the V^T operand is read with two 8-byte LDS loads from the same key set.
 // No atomics, one fixed reduction order: the result is deterministic.
 #include <cmath>
+#include <type_traits>
 
 #include "kvt_internal.h"
 
@@ -53,7 +55,14 @@ struct Raw {
     static constexpr int kHeadBytes = head_bytes(F);
     static constexpr int kPlane = kKT * kHeadBytes;                  // one plane's slices of a tile
     static constexpr int kBytes = 2 * kPlane;                        // K and V
-    static constexpr int kWords = kBytes / 8;                        // 8-byte words per tile
+};
+// The raw tile as the loads see it: WB-byte words (8; 16 for fp16 / bf16 slices, which are 256
+// bytes, when the cache pointers are 16-byte aligned).
+template <int F, int WB>
+struct Words {
+    static_assert(WB == 8 || (WB == 16 && F != KVT_Q8_0), "q8_0 slices are 8-byte aligned only");
+    using Word = std::conditional_t<WB == 8, uint64_t, u32x4>;
+    static constexpr int kWords = Raw<F>::kBytes / WB;               // words per tile
     static constexpr int kPerThread = (kWords + kThreads - 1) / kThreads;
 };
 constexpr int kOutPitch = 33;                  // floats per row of the output transpose buffer
@@ -92,16 +101,17 @@ __device__ __forceinline__ void dequant_block(const uint32_t w[9], bool odd, uin
 }
 
 
-// Coalesced 8-byte loads of tile `tile`: word f is plane f / 1088, key (f % 1088) / 17,
-// byte 8 * (f % 17) of that key's 136-byte head slice.
+// Coalesced WB-byte loads of tile `tile`: for q8_0 (WB 8) word f is plane f / 1088, key
+// (f % 1088) / 17, byte 8 * (f % 17) of that key's 136-byte head slice.
 // k_head ... v_tail already point at this workgroup's head slice (offset h * 136 added).
-template <int F>
+template <int F, int WB>
 __device__ __forceinline__ void load_raw(const unsigned char *k_head, const unsigned char *v_head,
                                          const unsigned char *k_tail, const unsigned char *v_tail,
                                          int64_t n_head, int64_t n_kv, int64_t row_bytes, int tile,
-                                         uint64_t (&rq)[Raw<F>::kPerThread])
+                                         typename Words<F, WB>::Word (&rq)[Words<F, WB>::kPerThread])
 {
     using R = Raw<F>;
+    using W = Words<F, WB>;
     // the tile's first key in each tier, as scalar bases; per word only a 32-bit row offset
     const int64_t key0 = (int64_t)tile * kKT;
     const int kmax = (int)((n_kv - 1 - key0) < kKT - 1 ? (n_kv - 1 - key0) : kKT - 1);
@@ -110,31 +120,32 @@ __device__ __forceinline__ void load_raw(const unsigned char *k_head, const unsi
     const unsigned char *tk = k_tail + (key0 - n_head) * row_bytes;
     const unsigned char *tv = v_tail + (key0 - n_head) * row_bytes;
 #pragma unroll
-    for (int u = 0; u < R::kPerThread; u++) {
+    for (int u = 0; u < W::kPerThread; u++) {
         const int f = threadIdx.x + u * kThreads;
-        if (f < R::kWords) {
-            const int plane = f >= R::kWords / 2;
-            const int rem = f - plane * (R::kWords / 2);
-            int kin = rem / (R::kHeadBytes / 8);
-            const int w = rem - kin * (R::kHeadBytes / 8);
+        if (f < W::kWords) {
+            const int plane = f >= W::kWords / 2;
+            const int rem = f - plane * (W::kWords / 2);
+            int kin = rem / (R::kHeadBytes / WB);
+            const int w = rem - kin * (R::kHeadBytes / WB);
             kin = kin < kmax ? kin : kmax;
             const unsigned char *base = kin < khead ? (plane ? hv : hk) : (plane ? tv : tk);
-            const uint32_t off = (uint32_t)kin * (uint32_t)row_bytes + 8u * (uint32_t)w;
-            rq[u] = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(base + off));
+            const uint32_t off = (uint32_t)kin * (uint32_t)row_bytes + (uint32_t)WB * (uint32_t)w;
+            rq[u] = __builtin_nontemporal_load(reinterpret_cast<const typename W::Word *>(base + off));
         }
     }
 }
 
-// Word f goes to byte 8*f: the raw tile in LDS is [plane][key][136 bytes].
-template <int F>
+// Word f goes to byte WB*f: the raw tile in LDS is [plane][key][head slice].
+template <int F, int WB>
 __device__ __forceinline__ void store_raw(unsigned char *rawbuf,
-                                          const uint64_t (&rq)[Raw<F>::kPerThread])
+                                          const typename Words<F, WB>::Word (&rq)[Words<F, WB>::kPerThread])
 {
+    using W = Words<F, WB>;
 #pragma unroll
-    for (int u = 0; u < Raw<F>::kPerThread; u++) {
+    for (int u = 0; u < W::kPerThread; u++) {
         const int f = threadIdx.x + u * kThreads;
-        if (f < Raw<F>::kWords)
-            *reinterpret_cast<uint64_t *>(rawbuf + 8 * f) = rq[u];
+        if (f < W::kWords)
+            *reinterpret_cast<typename W::Word *>(rawbuf + WB * f) = rq[u];
     }
 }
 
@@ -193,7 +204,7 @@ __device__ __forceinline__ void dequant_tile(const unsigned char *rawbuf, unsign
     }
 }
 
-template <int F>
+template <int F, int WB>
 __global__ __launch_bounds__(kThreads) void prefill_attn(
     const _Float16 *__restrict__ q, int64_t n_q, int64_t q_pos0, int n_qh, int kvh, int group,
     const unsigned char *__restrict__ k_head, const unsigned char *__restrict__ v_head,
@@ -279,24 +290,24 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     // the four cache bases, moved to this workgroup's head slice
     const unsigned char *kh = k_head + h * R::kHeadBytes, *vh = v_head + h * R::kHeadBytes;
     const unsigned char *kt = k_tail + h * R::kHeadBytes, *vt = v_tail + h * R::kHeadBytes;
-    uint64_t rq[R::kPerThread];
+    typename Words<F, WB>::Word rq[Words<F, WB>::kPerThread];
 
     // prologue: raw tile b -> LDS; fp16 tile b and raw tile b+1 ready; loads of b+2 in flight
     // (b = tb; buffers are indexed by tile & 1)
     const int b0 = tb;
     if (n_tiles > b0) {
-        load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
-        store_raw<F>(lds_raw + (b0 & 1) * R::kBytes, rq);
+        load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
+        store_raw<F, WB>(lds_raw + (b0 & 1) * R::kBytes, rq);
         if (n_tiles > b0 + 1)
-            load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
+            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
     }
     __syncthreads();
     if (n_tiles > b0) {
         dequant_tile<F>(lds_raw + (b0 & 1) * R::kBytes, lds + (b0 & 1) * kLdsBuf, wave, lane);
         if (n_tiles > b0 + 1)
-            store_raw<F>(lds_raw + ((b0 + 1) & 1) * R::kBytes, rq);
+            store_raw<F, WB>(lds_raw + ((b0 + 1) & 1) * R::kBytes, rq);
         if (n_tiles > b0 + 2)
-            load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 2, rq);
+            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 2, rq);
     }
     __syncthreads();
 
@@ -396,10 +407,10 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
             dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kLdsBuf,
                          wave, lane);
         if (tile + 2 < n_tiles)   // last, so the loads of tile + 2 have had the whole tile
-            store_raw<F>(lds_raw + (tile & 1) * R::kBytes, rq);
+            store_raw<F, WB>(lds_raw + (tile & 1) * R::kBytes, rq);
         __syncthreads();
         if (tile + 3 < n_tiles)
-            load_raw<F>(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 3, rq);
+            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 3, rq);
     }
 
     if (!last) {   // hand the state to the next pass
@@ -552,12 +563,15 @@ void launch_prefill(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, in
                            tile_begin, tile_cap, n_split, tiles_per_split, state, first, last,
                            out);
     };
+    // fp16 / bf16 slices are 256 bytes: 16-byte loads when every cache pointer allows them
+    const bool w16 = kvt::aligned(k_head, 16) && kvt::aligned(v_head, 16) &&
+                     kvt::aligned(k_tail, 16) && kvt::aligned(v_tail, 16);
     if (kv_format == KVT_Q8_0)
-        launch(prefill_attn<KVT_Q8_0>);
+        launch(prefill_attn<KVT_Q8_0, 8>);
     else if (kv_format == KVT_F16)
-        launch(prefill_attn<KVT_F16>);
+        w16 ? launch(prefill_attn<KVT_F16, 16>) : launch(prefill_attn<KVT_F16, 8>);
     else
-        launch(prefill_attn<KVT_BF16>);
+        w16 ? launch(prefill_attn<KVT_BF16, 16>) : launch(prefill_attn<KVT_BF16, 8>);
 }
 
 // A first bucket copied ahead by one pipelined call for the next call on the same thread: the

@@ -492,6 +492,33 @@ def test_prefill_chain_full_geometry(gpu):
     ch.free()
 
 
+@pytest.mark.parametrize("fmt", [kvt.F16, kvt.BF16], ids=["f16", "bf16"])
+def test_prefill_fp_caches_8_byte_aligned_planes(gpu, fmt):
+    """fp16 / bf16 planes that are only 8-byte aligned take the 8-byte raw loads (16-byte ones
+    need every cache pointer 16-byte aligned): the same bits as the aligned planes, head split
+    mid-tile and tail in place."""
+    n_kv, n_q, n_qh, kvh, n_head = 1500, 100, 16, 4, 700
+    k, v = _cache(n_kv, kvh, 31 + fmt, fmt)
+    row = k.shape[1]
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, 31 + fmt), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    aligned = _prefill(q, q_pos0, kvh, kd, vd, n_head, kd[n_head:], vd[n_head:], n_kv, True, gpu,
+                       fmt)
+    # the same rows 8 bytes into a byte buffer
+    buf = torch.zeros((2, n_kv * row + 16), dtype=torch.uint8, device=gpu)
+    buf[0, 8:8 + n_kv * row] = kd.reshape(-1)
+    buf[1, 8:8 + n_kv * row] = vd.reshape(-1)
+    ko, vo = buf[0, 8:8 + n_kv * row], buf[1, 8:8 + n_kv * row]
+    assert ko.data_ptr() % 16 == 8
+    got = _prefill(q, q_pos0, kvh, ko, vo, n_head, ko[n_head * row:], vo[n_head * row:], n_kv,
+                   True, gpu, fmt)
+    assert np.array_equal(got.view(np.uint32), aligned.view(np.uint32))
+    ref = oracle.attn_prefill(q, q_pos0, kvh, k, v, n_kv, None, None, n_kv, ORACLE_FMT[fmt], True,
+                              1 / math.sqrt(128))
+    assert np.max(np.abs(got - ref)) <= TOL
+
+
 def _splitk(q_np, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_kv, causal, dev,
             fmt=kvt.Q8_0):
     n_q, n_qh, hd = q_np.shape
