@@ -18,7 +18,7 @@
 //   * every thread then owns one q8_0 block of the tile (plane K or V, key = lane, block 0..3)
 //     and dequantises it to fp16 with a magic-number conversion (the int8 byte under 0x64 is
 //     1024 + 128 + q in fp16; subtracting 1152 is exact; times the block scale is the one
-//     rounding, to nearest): K as rows [key][d], V transposed [d][key].  Raw and fp16 tiles
+//     rounding, to nearest): K and V as rows [key][d].  Raw and fp16 tiles
 //     are double buffered: tile t+1 is dequantised while tile t is multiplied, one barrier per
 //     tile, with the loads of tiles t+2 and t+3 in flight;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (K from LDS, Q held in registers);
@@ -28,7 +28,8 @@
 //   * O^T += V^T P^T on the same MFMA.  Computing S transposed leaves every lane holding the
 //     16 probabilities of one query row in the MFMA B-operand layout, so P needs no shuffle:
 //     the k-slots of a PV step are the keys {16s + 4g + 0..3, 16s + 8 + 4g + 0..3} (g = lane/32)
-//     and the V^T operand is read with two 8-byte LDS loads from the same key set.
+//     and the V^T operand is read from the row-major V tile with two transposing 8-byte LDS
+//     reads (ds_read_b64_tr_b16) from the same key set.
 // No atomics, one fixed reduction order: the result is deterministic.
 #include <cmath>
 #include <type_traits>
@@ -43,10 +44,13 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlk = 34;                       // q8_0 block: fp16 scale + 32 int8
 constexpr int kKPitch = kHd * 2 + 16;          // LDS bytes per dequantised K row (272)
-constexpr int kVtPitch = kKT * 2 + 8;          // LDS bytes per dequantised V^T row (136)
 constexpr int kLdsK = kKT * kKPitch;
-constexpr int kLdsV = kHd * kVtPitch;
-constexpr int kLdsBuf = kLdsK + kLdsV;         // one tile, K and V^T
+// LDS bytes per dequantised V row: the PV product reads V transposed, each 16-lane group from
+// four rows.  320 puts those rows in disjoint banks and is faster for fp16 / bf16 caches; for
+// q8_0, 272 (as K) measured faster.
+template <int F> constexpr int v_pitch() { return F == KVT_Q8_0 ? kKPitch : kHd * 2 + 64; }
+template <int F> constexpr int lds_buf() { return kLdsK + kKT * v_pitch<F>(); }   // K + V
+constexpr int kLdsBuf = kLdsK + kKT * kKPitch;     // the smallest tile buffer
 // The raw (as stored) tile per cache format: one head's slice of a row is four q8_0 blocks
 // (136 bytes) or 128 fp16 / bf16 values (256 bytes).
 constexpr int head_bytes(int fmt) { return fmt == KVT_Q8_0 ? (kHd / 32) * kBlk : kHd * 2; }
@@ -77,6 +81,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane s reads 4 values and receives value s % 4
+// of the reads of lanes 4e + s / 4, e = 0..3 -- one column of four rows.
+__device__ __forceinline__ f16x4 tr_read(const unsigned char *p)
+{
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) s16x4 *)(p)));
 }
 
 // q8_0 block -> 32 fp16 values (16 dwords, element order).  odd: the block starts 2 bytes
@@ -150,7 +163,7 @@ __device__ __forceinline__ void store_raw(unsigned char *rawbuf,
 }
 
 // Thread (plane = wave / 4, block = wave % 4, key = lane) turns its 32 values of the raw tile
-// into fp16 in the tile used by the MFMA: K as rows [key][d], V transposed [d][key].  q8_0:
+// into fp16 in the tile used by the MFMA: K and V both as rows [key][d].  q8_0:
 // the block's dequantisation; fp16: the values as stored; bf16: each value converted to fp16,
 // which is exact for magnitudes in [2^-17, 65504] (bf16 carries 8 significant bits; below 2^-17
 // the fp16 subnormal spacing of 2^-24 rounds, and beyond 65504 the result is infinite).
@@ -189,19 +202,11 @@ __device__ __forceinline__ void dequant_tile(const unsigned char *rawbuf, unsign
             }
         }
     }
-    if (!is_v) {
-        unsigned char *kdst = buf + lane * kKPitch + blk * 64;
+    unsigned char *dst = buf + (is_v ? kLdsK + lane * v_pitch<F>() : lane * kKPitch) + blk * 64;
 #pragma unroll
-        for (int c = 0; c < 4; c++)
-            *reinterpret_cast<u32x4 *>(kdst + 16 * c) =
-                u32x4{d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]};
-    } else {
-        unsigned char *vdst = buf + kLdsK + (blk * 32) * kVtPitch + lane * 2;
-#pragma unroll
-        for (int e = 0; e < 32; e++)
-            *reinterpret_cast<uint16_t *>(vdst + e * kVtPitch) =
-                (uint16_t)(d[e >> 1] >> ((e & 1) * 16));
-    }
+    for (int c = 0; c < 4; c++)
+        *reinterpret_cast<u32x4 *>(dst + 16 * c) =
+            u32x4{d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]};
 }
 
 template <int F, int WB>
@@ -214,11 +219,14 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     int first, int last, float *__restrict__ out)
 {
     using R = Raw<F>;
-    __shared__ __align__(16) unsigned char lds[2 * kLdsBuf + 2 * R::kBytes];
-    unsigned char *const lds_raw = lds + 2 * kLdsBuf;   // two raw (as stored) tiles
+    constexpr int kBuf = lds_buf<F>();
+    __shared__ __align__(16) unsigned char lds[2 * kBuf + 2 * R::kBytes];
+    unsigned char *const lds_raw = lds + 2 * kBuf;   // two raw (as stored) tiles
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, i = lane & 31;
+    // the lane's share of a transposed V read: row offset and column within a 32-column block
+    const int tr_r = (lane & 15) >> 2, tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     // split-K: gridDim.x = n_split x (query tiles x kvh); split x takes key tiles
     // [x * tiles_per_split, (x + 1) * tiles_per_split) and hands its state on
     const int n_wg = gridDim.x / n_split;
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     }
     __syncthreads();
     if (n_tiles > b0) {
-        dequant_tile<F>(lds_raw + (b0 & 1) * R::kBytes, lds + (b0 & 1) * kLdsBuf, wave, lane);
+        dequant_tile<F>(lds_raw + (b0 & 1) * R::kBytes, lds + (b0 & 1) * kBuf, wave, lane);
         if (n_tiles > b0 + 1)
             store_raw<F, WB>(lds_raw + ((b0 + 1) & 1) * R::kBytes, rq);
         if (n_tiles > b0 + 2)
@@ -316,14 +324,14 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     // then issue the loads of tile+3
     const bool dequant_first = wave >= 4;
     for (int tile = b0; tile < n_tiles; tile++) {
-        const unsigned char *lk = lds + (tile & 1) * kLdsBuf;
+        const unsigned char *lk = lds + (tile & 1) * kBuf;
         const unsigned char *lv = lk + kLdsK;
         const int64_t key0 = (int64_t)tile * kKT;
         // Waves w and w + 4 share a SIMD.  The upper four dequantise the next tile before they
         // multiply this one and the lower four after, so on every SIMD one wave's MFMA work
         // meets the other's VALU work.
         if (dequant_first && tile + 1 < n_tiles)
-            dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kLdsBuf,
+            dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kBuf,
                          wave, lane);
         if (key0 <= wave_last) {
             // S^T tile: rows = keys 32*st + (lane & 31), columns = this wave's 32 query rows
@@ -394,17 +402,19 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
                     f16x8, u32x4{pk[st][r0], pk[st][r0 + 1], pk[st][r0 + 2], pk[st][r0 + 3]});
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++) {
-                    const unsigned char *vrow = lv + (32 * dt + i) * kVtPitch;
-                    const f16x4 lo = *reinterpret_cast<const f16x4 *>(vrow + 2 * (16 * ks + 4 * g));
-                    const f16x4 hi =
-                        *reinterpret_cast<const f16x4 *>(vrow + 2 * (16 * ks + 8 + 4 * g));
+                    // lane L receives V[16ks + 4g + e][32dt + L % 32], e = 0..3 (and keys + 8):
+                    // in its 16-lane group it reads 4 values of row 16ks + 4g + tr_r at column
+                    // 32dt + tr_c, and the read transposes them
+                    const unsigned char *vp = lv + (16 * ks + 4 * g + tr_r) * v_pitch<F>() +
+                                              2 * (32 * dt + tr_c);
+                    const f16x4 lo = tr_read(vp), hi = tr_read(vp + 8 * v_pitch<F>());
                     const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     o[dt] = mfma32(a, pb, o[dt]);
                 }
             }
         }
         if (!dequant_first && tile + 1 < n_tiles)
-            dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kLdsBuf,
+            dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kBuf,
                          wave, lane);
         if (tile + 2 < n_tiles)   // last, so the loads of tile + 2 have had the whole tile
             store_raw<F, WB>(lds_raw + (tile & 1) * R::kBytes, rq);
