@@ -13,12 +13,19 @@
 // afterwards sees them.  It never waits on a runtime thread.  Ordering the copies with a stream
 // host function that waited inside stalled at the first copy under a memory-copy trace, whose
 // completion handler most likely needs the thread the runtime runs host functions on.
+//
+// Every copy has a completion signal of its own with value 1 (kvt_engine_runs.h holds that
+// bookkeeping and its error paths), the form the runtime's own copies take.  One signal
+// counted down once per copy is legal HSA too, but a memory-copy tracer, which completes each
+// copy's signal from its own handler, rejected such a signal's value and the traced process
+// then crashed.
 #include <hsa/hsa.h>
 #include <hsa/hsa_ext_amd.h>
 
 #include <mutex>
 #include <new>
 
+#include "kvt_engine_runs.h"
 #include "kvt_internal.h"
 
 namespace {
@@ -108,32 +115,34 @@ int agents_for(int dev, Agents *out)
     return KVT_OK;
 }
 
-// A run: descriptors i..j-1 with every next one starting where the previous ended, on both
-// sides.  Zero-size descriptors are skipped and end no run.
-template <class F>
-void for_each_run(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
-                  F &&f)
-{
-    int64_t i = 0;
-    while (i < n) {
-        if (!sizes[i]) {
-            i++;
-            continue;
-        }
-        const uint64_t s0 = src[i], d0 = dst[i];
-        uint64_t len = sizes[i];
-        int64_t k = i + 1;
-        for (; k < n; k++) {
-            if (!sizes[k])
-                continue;
-            if (src[k] != s0 + len || dst[k] != d0 + len)
-                break;
-            len += sizes[k];
-        }
-        f(s0, d0, len);
-        i = k;
+// The engine-copy operations of one call (see kvt_engine_runs.h).
+struct HsaOps {
+    hsa_agent_t dst_agent, src_agent;
+    int create(uint64_t *sig)
+    {
+        hsa_signal_t h;
+        const hsa_status_t st = hsa_signal_create(1, 0, nullptr, &h);
+        *sig = h.handle;
+        return st == HSA_STATUS_SUCCESS ? 0 : (int)st;
     }
-}
+    int copy(uint64_t d, uint64_t s, uint64_t len, uint64_t sig)
+    {
+        const hsa_status_t st = hsa_amd_memory_async_copy(
+            reinterpret_cast<void *>(d), dst_agent, reinterpret_cast<const void *>(s), src_agent,
+            len, 0, nullptr, hsa_signal_t{sig});
+        return st == HSA_STATUS_SUCCESS ? 0 : (int)st;
+    }
+    void reset(uint64_t sig) { hsa_signal_store_screlease(hsa_signal_t{sig}, 1); }
+    void wait(uint64_t sig)
+    {
+        while (hsa_signal_wait_scacquire(hsa_signal_t{sig}, HSA_SIGNAL_CONDITION_LT, 1, UINT64_MAX,
+                                         HSA_WAIT_STATE_BLOCKED) >= 1) {
+        }
+    }
+    void destroy(uint64_t sig) { hsa_signal_destroy(hsa_signal_t{sig}); }
+};
+
+constexpr int64_t kSignalWindow = 256;   // copies in flight at most
 
 }  // namespace
 
@@ -156,37 +165,21 @@ int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *size
     const int rc = agents_for(dev, &a);
     if (rc != KVT_OK)
         return rc;
-    const hsa_agent_t dst_agent = dir == KVT_H2D ? a.gpu : a.cpu;
-    const hsa_agent_t src_agent = dir == KVT_H2D ? a.cpu : a.gpu;
-    int64_t runs = 0;
-    for_each_run(src, dst, sizes, n, [&](uint64_t, uint64_t, uint64_t) { runs++; });
-    if (!runs)
+    bool any = false;
+    for (int64_t i = 0; i < n && !any; i++)
+        any = sizes[i] != 0;
+    if (!any)
         return KVT_OK;
     KVT_HIP(hipStreamSynchronize(s));   // the copies come after the stream's earlier work
-    hsa_signal_t sig;
-    hsa_status_t st = hsa_signal_create(runs, 0, nullptr, &sig);
-    if (st != HSA_STATUS_SUCCESS)
-        return fail(KVT_EHIP, "kvt_swap_blocks: hsa_signal_create: status %d", (int)st);
-    int64_t submitted = 0;
-    for_each_run(src, dst, sizes, n, [&](uint64_t sa, uint64_t da, uint64_t len) {
-        if (st != HSA_STATUS_SUCCESS)
-            return;
-        st = hsa_amd_memory_async_copy(reinterpret_cast<void *>(da), dst_agent,
-                                       reinterpret_cast<const void *>(sa), src_agent, len, 0,
-                                       nullptr, sig);
-        if (st == HSA_STATUS_SUCCESS)
-            submitted++;
-    });
-    if (submitted < runs)   // copies never submitted will never count the signal down
-        hsa_signal_subtract_screlease(sig, runs - submitted);
-    // "below 1" rather than "equal to 0": a count taken past zero still ends the wait
-    while (hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_LT, 1, UINT64_MAX,
-                                     HSA_WAIT_STATE_BLOCKED) >= 1) {
-    }
-    hsa_signal_destroy(sig);
-    if (st != HSA_STATUS_SUCCESS)
+    HsaOps ops{dir == KVT_H2D ? a.gpu : a.cpu, dir == KVT_H2D ? a.cpu : a.gpu};
+    const EngineTally t = run_engine_copies(ops, src, dst, sizes, n, kSignalWindow);
+    if (t.failed_at == 1)
+        return fail(KVT_EHIP, "kvt_swap_blocks: hsa_signal_create: status %d (no copy submitted)",
+                    t.status);
+    if (t.failed_at == 2)
         return fail(KVT_EHIP, "kvt_swap_blocks: hsa_amd_memory_async_copy: status %d after %lld "
-                              "of %lld copies", (int)st, (long long)submitted, (long long)runs);
+                              "of %lld copies", t.status, (long long)t.submitted,
+                    (long long)t.runs);
     return KVT_OK;
 }
 

@@ -142,8 +142,9 @@ int64_t kvt_chunks_consumed(int64_t n, int32_t skip, int32_t bpc);
  *   previous one on both sides go as one copy), waits for them and returns, so work queued
  *   afterwards sees them.  Host addresses must be pinned memory from kvt_host_alloc (or
  *   hipHostMalloc).  Not allowed while the stream is being captured into a graph
- *   (KVT_EUNSUPPORTED).  Its copies share one completion signal, which rocprofv3's
- *   memory-copy trace does not support (the traced process fails); kernel traces are fine.
+ *   (KVT_EUNSUPPORTED).  Every engine copy has a completion signal of its own (value 1), at
+ *   most 256 in flight, waited for oldest first.  A signal that cannot be created, or a copy
+ *   that cannot be submitted, returns KVT_EHIP after the copies already submitted are done.
  * Destination ranges must be pairwise disjoint and disjoint from all sources; the order of
  * the copies is unspecified.  Zero sizes are no-ops.  n == 0 enqueues nothing.
  * ---------------------------------------------------------------------------------------- */

@@ -128,13 +128,17 @@ def test_swap_chunked_strided_layers_with_skip(gpu, mode):
         host.free(); tb.free()
 
 
-@pytest.mark.parametrize("page,offset", [(512, 0), (2048, 0), (2048, 8), (8192, 0), (1000, 8)])
+@pytest.mark.parametrize("page,offset", [(512, 0), (2048, 0), (2048, 8), (8192, 0), (1000, 8),
+                                         (16384, 0), (65536, 0)])
 @pytest.mark.parametrize("mode", [kvt.COPY_KERNEL, kvt.COPY_SDMA, kvt.COPY_RUNTIME],
                          ids=lambda m: MODE_NAMES[m])
 def test_swap_small_pages_scattered(gpu, page, offset, mode):
-    """Many small pages in random scattered order host -> HBM; offset 8 puts the host page bases
-    at 8 mod 16 (the 8-byte path); page 1000 is 8-byte aligned but not a multiple of 16."""
-    n = 65536 if page <= 2048 else 8192
+    """Many small pages in random scattered order host -> HBM, every page size the small-page
+    sweep reports; offset 8 puts the host page bases at 8 mod 16 (the 8-byte path); page 1000
+    is 8-byte aligned but not a multiple of 16.  65,536 pages up to 16 KiB (the workload's full
+    count), 16,384 of 64 KiB (1 GiB).  The expected HBM image is the oracle's memcpy loop over
+    its own pointer tables into a zero-filled host replica of the HBM buffer."""
+    n = 65536 if page <= 16384 else 16384
     stride = page + offset
     host = kvt.HostBuffer(n * stride + 64)
     hb = host.numpy(np.uint8, None)[offset:offset + n * stride].reshape(n, stride)
@@ -149,10 +153,14 @@ def test_swap_small_pages_scattered(gpu, page, offset, mode):
     kvt.kvt_swap_blocks(t[0], t[1], t[2], n, kvt.H2D, mode)
     torch.cuda.synchronize()
     ref = np.zeros((n, page), dtype=np.uint8)
-    ref[dst] = hb[src, :page]
+    s = oracle.sub_block_ptrs(hb.ctypes.data, stride, page, src, 1, 0, n)
+    d = oracle.sub_block_ptrs(ref.ctypes.data, page, page, dst, 1, 0, n)
+    oracle.swap(s, d, np.full(n, page, dtype=np.uint64))
     assert np.array_equal(dev.cpu().numpy(), ref)
-    del hb
+    del hb, ref
+    del dev
     host.free(); tb.free()
+    torch.cuda.empty_cache()
 
 
 def test_swap_zero_sizes_and_empty(gpu):
@@ -306,9 +314,11 @@ def test_swap_32_layers_full_geometry_sampled(gpu):
     mode, 262,144 descriptors per direction): 64 tensors of 8192 HBM blocks; host rows of four
     32 KiB pages + 4 KiB pad (2048 rows per tensor, 16.5 GiB pinned); 4096 random blocks per
     tensor with a random skip on the first host chunk.  Every host page carries its own
-    (tensor, row, page) stamp, so a copy from the wrong place cannot match.  Checked on 3000
-    sampled descriptors against the host bytes (the oracle's memcpy, one page at a time),
-    unselected HBM blocks and pads left alone, and the store back as a round trip."""
+    (tensor, row, page) stamp, so a copy from the wrong place cannot match.  The oracle builds
+    its own pointer tables over the host planes, and its memcpy loop copies 3000 sampled
+    descriptors' pages into a host array; the loaded HBM pages must equal them.  Unselected
+    HBM blocks and pads stay untouched, and after the store the oracle's memcpy over the same
+    tables reads back the original bytes (round trip)."""
     tensors, gblocks, bpc, page, pad, n = 64, 8192, 4, 32768, 4096, 4096
     hrows = gblocks // bpc
     stride = bpc * page + pad
@@ -343,8 +353,18 @@ def test_swap_32_layers_full_geometry_sampled(gpu):
 
     pick = synth.rng(2, synth.P_MISC, 99).choice(tensors * n, size=3000, replace=False)
     xs, os_ = pick // n, pick % n
-    rows, js = chunks[(os_ + skip) // bpc], (os_ + skip) % bpc
-    want = np.stack([hb[x, r, j * page:(j + 1) * page] for x, r, j in zip(xs, rows, js)])
+    rows = chunks[(os_ + skip) // bpc]
+    # the oracle's tables over the host planes, and its memcpy of the sampled descriptors
+    osrc = np.concatenate([oracle.sub_block_ptrs(hb[x].ctypes.data, stride, page, chunks, bpc,
+                                                 skip, n) for x in range(tensors)])
+    sizes = np.full(pick.size, page, dtype=np.uint64)
+
+    def oracle_read(out):
+        oracle.swap(osrc[pick], out.ctypes.data + np.arange(pick.size, dtype=np.uint64) * page,
+                    sizes)
+        return out
+
+    want = oracle_read(np.empty((pick.size, page), dtype=np.uint8))
     got = hbm[torch.from_numpy(xs).to(gpu), torch.from_numpy(gids[os_]).to(gpu)].cpu().numpy()
     assert np.array_equal(got, want), "loaded pages differ from their host pages"
     rest = np.setdiff1d(np.arange(gblocks), gids)
@@ -362,7 +382,7 @@ def test_swap_32_layers_full_geometry_sampled(gpu):
     t[0], t[1] = t[1].copy(), t[0].copy()
     kvt.kvt_swap_blocks(t[0], t[1], t[2], tensors * n, kvt.D2H, kvt.COPY_KERNEL)
     torch.cuda.synchronize()
-    back = np.stack([hb[x, r, j * page:(j + 1) * page] for x, r, j in zip(xs, rows, js)])
+    back = oracle_read(np.zeros((pick.size, page), dtype=np.uint8))
     assert np.array_equal(back, want), "round trip changed sampled pages"
     assert np.array_equal(np.stack([hb[x, r, bpc * page:] for x, r in zip(xs, rows)]), pads)
     del hb, flat, got, want, back

@@ -1,7 +1,8 @@
 """GPU parity of the tiered prefill path: tail staging + flash attention over a q8_0 cache.
 
-* within 2e-3 max-abs of the fp64 oracle (every element at small sizes, sampled query rows at
-  the full 180,000-token geometry);
+* within 2e-3 max-abs of the fp64 oracle (every element at small sizes; at the full
+  180,000-token geometry every row of the first, a middle and the last 64-query tile, and one
+  row in each other tile);
 * bit-identical output whether the cache is all in HBM, split into an HBM head plus a staged
   tail, or split with the tail read in place from host memory (staging off)."""
 import functools
@@ -209,17 +210,20 @@ def test_prefill_pipelined_bit_identical(gpu, n_kv, n_head, arena_rows, n_qh, kv
     host.free()
 
 
-def test_prefill_full_geometry_sampled_rows(gpu):
-    """180,000-token context, cells [0, 94208) in HBM and the rest in host memory, q8_0 K/V
-    (8 KV heads x 128), a 2048-query causal chunk at the tail with 32 query heads: stage the
-    host rows into HBM once, run the attention, compare sampled query rows (all heads, all
-    dims) with the fp64 oracle; staging on/off and all-HBM agree bit for bit."""
-    n_kv, n_head, n_q, n_qh, kvh = 180000, 94208, 2048, 32, 8
+C5_NKV, C5_NHEAD, C5_NQ, C5_NQH, C5_KVH = 180000, 94208, 2048, 32, 8
+
+
+@pytest.fixture(scope="module")
+def c5_staged(gpu):
+    """The tiered-prefill workload at full size: 180,000-token q8_0 context (8 KV heads x 128),
+    cells [0, 94208) in HBM and the rest in host memory, a 2048-query causal chunk at the tail
+    with 32 query heads.  The tail is staged into HBM once and the attention runs over head +
+    staging.  Returns (q, output); the oracle comparisons are the tests below."""
+    n_kv, n_head, n_q, n_qh, kvh = C5_NKV, C5_NHEAD, C5_NQ, C5_NQH, C5_KVH
     k, v = _full_cache()
     row = k.shape[1]
     n_tail = n_kv - n_head
     q = synth.f16_normal(synth.rng(5, synth.P_Q, 180000), (n_q, n_qh, 128))
-    q_pos0 = n_kv - n_q
     kd, vd = _dev(k[:n_head], gpu), _dev(v[:n_head], gpu)
     host = kvt.HostBuffer(2 * n_tail * row)
     ht = host.numpy(np.uint8, (2, n_tail, row))
@@ -227,13 +231,62 @@ def test_prefill_full_geometry_sampled_rows(gpu):
     stage = torch.empty((2, n_tail, row), dtype=torch.uint8, device=gpu)
     kvt.kvt_stage_tail(host.dev, row, 0, n_tail, stage[0], kvt.COPY_AUTO)
     kvt.kvt_stage_tail(host.dev + n_tail * row, row, 0, n_tail, stage[1], kvt.COPY_AUTO)
-    staged = _prefill(q, q_pos0, kvh, kd, vd, n_head, stage[0], stage[1], n_kv, True, gpu)
+    staged = _prefill(q, n_kv - n_q, kvh, kd, vd, n_head, stage[0], stage[1], n_kv, True, gpu)
     assert np.array_equal(stage.cpu().numpy().reshape(2, n_tail, row), ht)
-    for rows in ((0, 2), (1023, 1025), (2046, 2048)):
-        ref = oracle.attn_prefill(q, q_pos0, kvh, k, v, n_kv, None, None, n_kv, oracle.Q8_0, True,
-                                  1 / math.sqrt(128), t_begin=rows[0], t_end=rows[1])
-        err = np.max(np.abs(staged[rows[0]:rows[1]] - ref))
-        assert err <= TOL, (rows, err)
+    del ht, stage, kd, vd
+    host.free()
+    torch.cuda.empty_cache()
+    return q, staged
+
+
+def _c5_oracle_rows(q, t_begin, t_end):
+    k, v = _full_cache()
+    return oracle.attn_prefill(q, C5_NKV - C5_NQ, C5_KVH, k, v, C5_NKV, None, None, C5_NKV,
+                               oracle.Q8_0, True, 1 / math.sqrt(128), t_begin=t_begin,
+                               t_end=t_end)
+
+
+@pytest.mark.parametrize("tile", [0, 15, 31], ids=["first", "middle", "last"])
+def test_prefill_full_geometry_whole_query_tile(c5_staged, tile):
+    """Every query row of one 64-query tile (all 32 heads, all 128 dims) at the full 180k
+    geometry, within 2e-3 of the fp64 oracle: covers every wave and head group of the tile."""
+    q, staged = c5_staged
+    t0, t1 = 64 * tile, 64 * tile + 64
+    ref = _c5_oracle_rows(q, t0, t1)
+    got = staged[t0:t1]
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= TOL, (tile, err)
+
+
+def test_prefill_full_geometry_one_row_per_tile(c5_staged):
+    """One query row in each of the other 29 tiles, at offsets that step through the tile
+    (3, 10, 17, ... mod 64: odd and even, every 8-query slice), against the fp64 oracle."""
+    q, staged = c5_staged
+    worst = 0.0
+    for tile in range(32):
+        if tile in (0, 15, 31):
+            continue
+        t = 64 * tile + (7 * tile + 3) % 64
+        ref = _c5_oracle_rows(q, t, t + 1)
+        err = float(np.max(np.abs(staged[t:t + 1] - ref)))
+        assert err <= TOL, (t, err)
+        worst = max(worst, err)
+
+
+def test_prefill_full_geometry_tiers_bit_identical(gpu, c5_staged):
+    """At the full geometry the staged tier, the tail read in place from host memory, the
+    all-HBM cache and the pipelined bucketed staging give the same output bits."""
+    n_kv, n_head, n_q, kvh = C5_NKV, C5_NHEAD, C5_NQ, C5_KVH
+    q, staged = c5_staged
+    k, v = _full_cache()
+    row = k.shape[1]
+    n_tail = n_kv - n_head
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k[:n_head], gpu), _dev(v[:n_head], gpu)
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
     in_place = _prefill(q, q_pos0, kvh, kd, vd, n_head, host.dev, host.dev + n_tail * row, n_kv,
                         True, gpu)
     assert np.array_equal(in_place.view(np.uint32), staged.view(np.uint32))

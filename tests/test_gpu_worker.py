@@ -201,7 +201,8 @@ def test_graph_staging_then_prefill_replays(gpu, mode):
         tail = synth.q8_0_rows(synth.rng(9, synth.P_K, 60 + r), n_kv - n_head, kvh, 128)
         hk[0, n_head:] = tail
         hk[1, n_head:] = tail[::-1]
-        scratch = torch.randn(1 << 20, device=gpu).sum()     # eager work between replays
+        noise = torch.randn(1 << 20, device=gpu)
+        scratch = noise.sum()                    # eager work between replays
         g.replay()
         torch.cuda.synchronize()
         got_out, got_stage = out.clone(), stage.clone()
@@ -212,7 +213,7 @@ def test_graph_staging_then_prefill_replays(gpu, mode):
         assert torch.equal(got_stage[0].cpu(), torch.from_numpy(hk[0, n_head:].copy()))
         assert torch.equal(got_stage, stage), f"replay {r}: staged rows differ"
         assert torch.equal(got_out, out), f"replay {r}: attention differs"
-        assert float(scratch) == float(scratch)
+        assert torch.equal(scratch, noise.sum()), f"replay {r}: eager work was disturbed"
     del g, hk
     torch.cuda.synchronize()
     host.free()
