@@ -14,6 +14,7 @@
 //   max first, then every chunk rescaled by e^(m_c - max) -- the same fold, one rescale each.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "kvt_internal.h"
 
@@ -597,50 +598,54 @@ extern "C" int kvt_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t
     return KVT_OK;
 }
 
-// S5+S6 in one pass: QSA-KVO's decode reads the selected K/V blocks through base pointers and
-// computed offsets; here each chunk's rows cross the host link straight into the wave that
-// attends them (and, when k_out/v_out are given, into the HBM gather buffers as well).
-extern "C" int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd,
-                                      int32_t dtype, const void *k_plane, const void *v_plane,
-                                      int64_t n_blocks, int64_t block_stride, int64_t head_stride,
-                                      int64_t token_stride, const int32_t *block_table, int32_t bt,
-                                      const int32_t *ids, int32_t k, void *k_out, void *v_out,
-                                      float scale, float *out, void *ws, size_t ws_bytes,
-                                      void *stream)
+namespace {
+
+// Argument checks shared by the workspace and the no-allocation forms of the fused decode;
+// returns KVT_OK and the key count, or the failure status.
+int gather_attn_decode_check(const char *who, const void *q, int32_t n_qh, int32_t kvh,
+                             int32_t hd, int32_t dtype, const void *k_plane, const void *v_plane,
+                             int64_t n_blocks, int64_t block_stride, int64_t head_stride,
+                             int64_t token_stride, int32_t bt, const int32_t *ids, int32_t k,
+                             const void *k_out, const void *v_out, const float *out,
+                             int64_t *n_kv)
 {
     if (hd != kHd)
-        return kvt::fail(KVT_EUNSUPPORTED, "kvt_gather_attn_decode: hd=%d (supported: 128)", hd);
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: hd=%d (supported: 128)", who, hd);
     if (dtype != KVT_BF16 && dtype != KVT_F16)
-        return kvt::fail(KVT_EUNSUPPORTED, "kvt_gather_attn_decode: dtype=%d", dtype);
+        return kvt::fail(KVT_EUNSUPPORTED, "%s: dtype=%d", who, dtype);
     if (n_qh < 1 || kvh < 1 || n_qh % kvh || n_qh / kvh > 16 || kvh > 65535 || bt < 1 || k < 1 ||
         n_blocks < 1)
-        return kvt::fail(KVT_EINVAL,
-                         "kvt_gather_attn_decode: n_qh=%d kvh=%d bt=%d k=%d n_blocks=%lld", n_qh,
+        return kvt::fail(KVT_EINVAL, "%s: n_qh=%d kvh=%d bt=%d k=%d n_blocks=%lld", who, n_qh,
                          kvh, bt, k, (long long)n_blocks);
     if ((int64_t)k * bt > 0x7fffffffll - kKeys)
-        return kvt::fail(KVT_ERANGE, "kvt_gather_attn_decode: k*bt too large");
+        return kvt::fail(KVT_ERANGE, "%s: k*bt too large", who);
     if (block_stride % 16 || head_stride % 16 || token_stride % 16 || block_stride < 0 ||
         head_stride < 0 || token_stride < 0)
         return kvt::fail(KVT_EALIGN,
-                         "kvt_gather_attn_decode: strides (%lld, %lld, %lld) must be non-negative "
-                         "multiples of 16",
-                         (long long)block_stride, (long long)head_stride, (long long)token_stride);
+                         "%s: strides (%lld, %lld, %lld) must be non-negative multiples of 16",
+                         who, (long long)block_stride, (long long)head_stride,
+                         (long long)token_stride);
     if (!q || !out || !k_plane || !v_plane || !ids || (!k_out) != (!v_out))
-        return kvt::fail(KVT_EINVAL, "kvt_gather_attn_decode: null pointer (k_out and v_out "
-                                     "are both given or both NULL)");
+        return kvt::fail(KVT_EINVAL, "%s: null pointer (k_out and v_out are both given or both "
+                                     "NULL)", who);
     if (!kvt::aligned(q, 16) || !kvt::aligned(k_plane, 16) || !kvt::aligned(v_plane, 16) ||
         !kvt::aligned(k_out, 16) || !kvt::aligned(v_out, 16))
-        return kvt::fail(KVT_EALIGN, "kvt_gather_attn_decode: q, planes and outputs must be "
-                                     "16-byte aligned");
+        return kvt::fail(KVT_EALIGN, "%s: q, planes and outputs must be 16-byte aligned", who);
+    *n_kv = (int64_t)k * bt;
+    return KVT_OK;
+}
+
+// Enqueues the fused gather + attention with its split partials in `part` (checked already).
+int gather_attn_decode_launch(const void *q, int32_t n_qh, int32_t kvh, int32_t dtype,
+                              const void *k_plane, const void *v_plane, int64_t n_blocks,
+                              int64_t block_stride, int64_t head_stride, int64_t token_stride,
+                              const int32_t *block_table, int32_t bt, const int32_t *ids,
+                              int32_t k, void *k_out, void *v_out, float scale, float *out,
+                              float *part, hipStream_t s)
+{
     const int64_t n_kv = (int64_t)k * bt;
-    const size_t need = kvt_attn_decode_ws_bytes(n_qh, hd, n_kv);
-    if (!ws || ws_bytes < need)
-        return kvt::fail(KVT_EINVAL, "kvt_gather_attn_decode: workspace of %zu bytes, need %zu",
-                         ws_bytes, need);
     const int64_t chunks = (n_kv + kKeys - 1) / kKeys;
-    hipStream_t s = kvt::as_stream(stream);
     const int group = n_qh / kvh;
-    float *part = static_cast<float *>(ws);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
     const SlotMap sm{block_table, n_blocks, n_blocks, block_stride, 1,
                      (int)std::min<int64_t>(n_blocks, 0x7fffffff), 0};
@@ -661,6 +666,110 @@ extern "C" int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, 
     hipLaunchKernelGGL(decode_merge, dim3(n_qh), dim3(kHd), 0, s, part, group, (int)chunks, out);
     KVT_LAUNCHED("decode_merge");
     return KVT_OK;
+}
+
+// The no-allocation form's scratch: the split partials live in this fixed array, one copy per
+// GPU, held until the process ends.  Host code never passes its name to a kernel (on the host
+// the name is a stand-in, not a device address): it uses the address hipGetSymbolAddress
+// returns for each device, taken once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = 4u << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxScratchDevices] = {};
+
+int scratch_for_device(int dev, void **addr)
+{
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_gather_attn_decode_noalloc: device %d out of "
+                                           "range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        int cur = 0;
+        KVT_HIP(hipGetDevice(&cur));
+        KVT_HIP(hipSetDevice(dev));
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return kvt::fail(KVT_EHIP, "kvt_gather_attn_decode_noalloc: hipGetSymbolAddress: %s",
+                             hipGetErrorString(e));
+        if (e2 != hipSuccess)
+            return kvt::fail(KVT_EHIP, "kvt_gather_attn_decode_noalloc: hipSetDevice: %s",
+                             hipGetErrorString(e2));
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return KVT_OK;
+}
+
+}  // namespace
+
+// S5+S6 in one pass: QSA-KVO's decode reads the selected K/V blocks through base pointers and
+// computed offsets; here each chunk's rows cross the host link straight into the wave that
+// attends them (and, when k_out/v_out are given, into the HBM gather buffers as well).
+extern "C" int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd,
+                                      int32_t dtype, const void *k_plane, const void *v_plane,
+                                      int64_t n_blocks, int64_t block_stride, int64_t head_stride,
+                                      int64_t token_stride, const int32_t *block_table, int32_t bt,
+                                      const int32_t *ids, int32_t k, void *k_out, void *v_out,
+                                      float scale, float *out, void *ws, size_t ws_bytes,
+                                      void *stream)
+{
+    int64_t n_kv = 0;
+    const int rc = gather_attn_decode_check("kvt_gather_attn_decode", q, n_qh, kvh, hd, dtype,
+                                            k_plane, v_plane, n_blocks, block_stride,
+                                            head_stride, token_stride, bt, ids, k, k_out, v_out,
+                                            out, &n_kv);
+    if (rc != KVT_OK)
+        return rc;
+    const size_t need = kvt_attn_decode_ws_bytes(n_qh, hd, n_kv);
+    if (!ws || ws_bytes < need)
+        return kvt::fail(KVT_EINVAL, "kvt_gather_attn_decode: workspace of %zu bytes, need %zu",
+                         ws_bytes, need);
+    return gather_attn_decode_launch(q, n_qh, kvh, dtype, k_plane, v_plane, n_blocks,
+                                     block_stride, head_stride, token_stride, block_table, bt,
+                                     ids, k, k_out, v_out, scale, out, static_cast<float *>(ws),
+                                     kvt::as_stream(stream));
+}
+
+// The same pass for callers that cannot allocate: the partials go to the library's fixed
+// per-GPU scratch array instead of a caller workspace (kvt_gather_attn_decode_noalloc in kvt.h).
+extern "C" size_t kvt_gather_attn_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int kvt_gather_attn_decode_noalloc(const void *q, int32_t n_qh, int32_t kvh,
+                                              int32_t hd, int32_t dtype, const void *k_plane,
+                                              const void *v_plane, int64_t n_blocks,
+                                              int64_t block_stride, int64_t head_stride,
+                                              int64_t token_stride, const int32_t *block_table,
+                                              int32_t bt, const int32_t *ids, int32_t k,
+                                              void *k_out, void *v_out, float scale, float *out,
+                                              void *stream)
+{
+    int64_t n_kv = 0;
+    int rc = gather_attn_decode_check("kvt_gather_attn_decode_noalloc", q, n_qh, kvh, hd, dtype,
+                                      k_plane, v_plane, n_blocks, block_stride, head_stride,
+                                      token_stride, bt, ids, k, k_out, v_out, out, &n_kv);
+    if (rc != KVT_OK)
+        return rc;
+    const size_t need = kvt_attn_decode_ws_bytes(n_qh, hd, n_kv);
+    if (need > kNoAllocScratchBytes)
+        return kvt::fail(KVT_ERANGE, "kvt_gather_attn_decode_noalloc: the partials need %zu "
+                                     "bytes, more than the %zu-byte scratch (n_qh * "
+                                     "ceil(k*bt/64) * 130 * 4 bytes)", need,
+                         kNoAllocScratchBytes);
+    hipStream_t s = kvt::as_stream(stream);
+    int dev = 0;
+    KVT_HIP(hipStreamGetDevice(s, &dev));
+    void *part = nullptr;
+    rc = scratch_for_device(dev, &part);
+    if (rc != KVT_OK)
+        return rc;
+    return gather_attn_decode_launch(q, n_qh, kvh, dtype, k_plane, v_plane, n_blocks,
+                                     block_stride, head_stride, token_stride, block_table, bt,
+                                     ids, k, k_out, v_out, scale, out, static_cast<float *>(part),
+                                     s);
 }
 
 // [QSA-KVO] qsa_staging_worthwhile: the direct path reads rows * k_pad positions over the link

@@ -47,6 +47,10 @@ _SIGNATURES = {
     "kvt_gather_attn_decode": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, _P, _P, c_int64,
                                        c_int64, c_int64, c_int64, _P, c_int32, _P, c_int32, _P, _P,
                                        c_float, _P, _P, c_size_t, _P]),
+    "kvt_gather_attn_decode_noalloc_max_bytes": (c_size_t, []),
+    "kvt_gather_attn_decode_noalloc": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, _P, _P,
+                                               c_int64, c_int64, c_int64, c_int64, _P, c_int32,
+                                               _P, c_int32, _P, _P, c_float, _P, _P]),
     "kvt_attn_prefill": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P, c_int64,
                                  _P, _P, c_int64, c_int32, c_int32, c_float, _P, _P]),
     "kvt_attn_prefill_state_bytes": (c_size_t, [c_int64, c_int32, c_int32]),
@@ -232,6 +236,20 @@ def kvt_gather_attn_decode(q, n_qh, kvh, hd, dtype, k_plane, v_plane, n_blocks, 
         int(n_blocks), int(block_stride), int(head_stride), int(token_stride), _ptr(block_table),
         int(bt), _ptr(ids), int(k), _ptr(k_out), _ptr(v_out), float(scale), _ptr(out), _ptr(ws),
         int(ws_bytes), _stream(stream)))
+
+
+def kvt_gather_attn_decode_noalloc_max_bytes():
+    return int(load().kvt_gather_attn_decode_noalloc_max_bytes())
+
+
+def kvt_gather_attn_decode_noalloc(q, n_qh, kvh, hd, dtype, k_plane, v_plane, n_blocks,
+                                   block_stride, head_stride, token_stride, block_table, bt, ids,
+                                   k, k_out, v_out, scale, out, stream=None):
+    _check("kvt_gather_attn_decode_noalloc", load().kvt_gather_attn_decode_noalloc(
+        _ptr(q), int(n_qh), int(kvh), int(hd), int(dtype), _ptr(k_plane), _ptr(v_plane),
+        int(n_blocks), int(block_stride), int(head_stride), int(token_stride), _ptr(block_table),
+        int(bt), _ptr(ids), int(k), _ptr(k_out), _ptr(v_out), float(scale), _ptr(out),
+        _stream(stream)))
 
 
 def kvt_attn_prefill(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_tail, v_tail, n_kv,

@@ -265,6 +265,26 @@ int kvt_gather_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t hd,
                            size_t ws_bytes, void *stream);
 
 /* ----------------------------------------------------------------------------------------
+ * kvt_gather_attn_decode without a workspace, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, results and limits as kvt_gather_attn_decode, minus ws / ws_bytes: the split
+ * partials go to a scratch array inside the library, one per GPU, of
+ * kvt_gather_attn_decode_noalloc_max_bytes() bytes (4 MiB), held until the process ends.
+ * The call allocates nothing.  It needs n_qh * ceil(k*bt / 64) * (hd + 2) * 4 bytes of it
+ * (1.06 MB for 64 query heads and 32 blocks of 64 tokens); more returns KVT_ERANGE and
+ * enqueues nothing.  Every call on one GPU uses the same scratch, and each call writes every
+ * partial it reads, so nothing carries over between calls; but calls that can run at the
+ * same time on one GPU (on different streams) race on it and must be ordered by the caller.
+ * ---------------------------------------------------------------------------------------- */
+size_t kvt_gather_attn_decode_noalloc_max_bytes(void);
+int kvt_gather_attn_decode_noalloc(const void *q, int32_t n_qh, int32_t kvh, int32_t hd,
+                                   int32_t dtype, const void *k_plane, const void *v_plane,
+                                   int64_t n_blocks, int64_t block_stride, int64_t head_stride,
+                                   int64_t token_stride, const int32_t *block_table, int32_t bt,
+                                   const int32_t *ids, int32_t k, void *k_out, void *v_out,
+                                   float scale, float *out, void *stream);
+
+/* ----------------------------------------------------------------------------------------
  * Sparse attention over per-row selections.  [QSA-KVO] qsa_sparse_attend_rows: query row r
  * (R rows of n_qh heads, e.g. the tokens of a prefill chunk) attends the cache positions
  * positions[r][0..k_pad) (logical token positions; -1 pads), the same selection for every
