@@ -367,9 +367,13 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
                     mt = fmaxf(mt, s[st][r]);
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
             const float m_new = fmaxf(m, mt);
-            // every logit is scaled by c > 0, so the max commutes with the scaling
+            // every logit is scaled by c > 0, so the max commutes with the scaling.  An
+            // unchanged max rescales by exactly 1: exp2(m*c - round(m*c)) would be 1 + the
+            // product's rounding error, compounding over thousands of tiles into a drift of
+            // the early keys' weights against the later ones (and rescaling O every tile).
             const float mc = m_new == -INFINITY ? 0.f : m_new * scale_log2;
-            const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m * scale_log2 - mc);
+            const float alpha = m == -INFINITY ? 0.f
+                                : (m_new == m ? 1.f : __builtin_amdgcn_exp2f(m * scale_log2 - mc));
             uint32_t pk[2][8];   // fp16 probabilities, packed in pairs
             float psum = 0.f;
 #pragma unroll
