@@ -21,6 +21,10 @@ Functions and the passages they follow:
 * ``paged_write``      -- QSA KV offload, ``CacheLayer_qsa_offload`` docstring (new rows reach
   the host pages through the paged cache update; the plain block-table rule).
 * ``copy_page``        -- QSA KV offload, ``CacheLayer_qsa_offload.copy_page``.
+* ``pool_rebuild``     -- QSA KV offload, ``CacheLayer_qsa_offload`` docstring (the pool kernel
+  rebuilds the pooled blocks an append touched, reading the raw key plane at the write head).
+  The pooling function is not on the page: the reading taken is the mean of the block's raw
+  key rows, rounded once to fp16 (``f64_to_f16``).
 
 Every function here has at least one pin in ``tests/test_oracle.py`` that does not restate its
 formula (library routines, closed forms, invariants, worked values).
@@ -68,6 +72,9 @@ def _load():
             "orc_attn_prefill": (c_int, [P, c_int64, c_int64, c_int32, c_int32, c_int32, P, P,
                                          c_int64, P, P, c_int64, c_int32, c_int32, c_double,
                                          c_int64, c_int64, P, c_int]),
+            "orc_f64_to_f16": (ctypes.c_uint16, [c_double]),
+            "orc_pool_rebuild": (c_int, [P, P, c_int32, c_int32, c_int32, P, P, c_int32, c_int32,
+                                         c_int32, c_int64]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -356,3 +363,24 @@ def attn_prefill(q_u16, q_pos0, kvh, k_head, v_head, n_head, k_tail, v_tail, n_k
         _ptr(k_tail), _ptr(v_tail), int(n_kv), int(fmt), int(bool(causal)), float(scale),
         int(t_begin), int(t_end), _ptr(out), _threads(threads)))
     return out
+
+
+def f64_to_f16(x):
+    """fp64 -> fp16 bit pattern, round to nearest even (the oracle's own conversion)."""
+    return int(_load().orc_f64_to_f16(float(x)))
+
+
+def pool_rebuild(raw_u16, pooled_u16, cache_seqlens, seq, block_table, page_size, cr):
+    """Rebuild the pooled blocks an append of `seq` tokens at cache_seqlens[b] touched.
+    raw: uint16 fp16 bits [n_pages][page_size][dim]; pooled: uint16 [n_pages][page_size/cr][dim],
+    modified in place and returned.  block_table: int [bsz][pages_per_seq]."""
+    raw = np.ascontiguousarray(raw_u16, dtype=np.uint16)
+    assert pooled_u16.dtype == np.uint16 and pooled_u16.flags.c_contiguous
+    n_pages, ps, dim = raw.shape
+    assert ps == page_size
+    lens = np.ascontiguousarray(cache_seqlens, dtype=np.int32)
+    table = np.ascontiguousarray(block_table, dtype=np.int32)
+    _check("orc_pool_rebuild", _load().orc_pool_rebuild(
+        _ptr(raw), _ptr(pooled_u16), int(dim), int(lens.size), int(seq), _ptr(lens), _ptr(table),
+        int(table.shape[1]), int(page_size), int(cr), int(n_pages)))
+    return pooled_u16

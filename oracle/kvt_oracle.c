@@ -406,3 +406,85 @@ int orc_attn_prefill(const uint16_t *q, int64_t n_q, int64_t q_pos0, int32_t n_q
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Pool rebuild at the write head          [QSA-KVO] CacheLayer_qsa_offload docstring          */
+/* ------------------------------------------------------------------------------------------ */
+/* fp64 -> fp16, rounding to nearest with ties to even, from the definition: for a normal
+ * result the value is scaled so that its 11 significant bits are the integer part, for a
+ * subnormal one it is counted in units of 2^-24; the remainder decides the rounding.  Values
+ * at or beyond 65520 (halfway between 65504 and 65536) round to infinity.  NaN gives 0x7E00. */
+uint16_t orc_f64_to_f16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7E00;
+    if (a >= 65520.0)
+        return (uint16_t)(sign | 0x7C00);
+    int e;
+    (void)frexp(a, &e);                  /* a = f * 2^e, f in [0.5, 1) */
+    int unbiased = e - 1;                /* a in [2^unbiased, 2^(unbiased+1)) */
+    double units;                        /* a in units of the result's last place */
+    int32_t bits_exp;
+    if (a == 0.0 || unbiased < -14) {    /* subnormal (or zero) */
+        units = ldexp(a, 24);
+        bits_exp = 0;
+    } else {
+        units = ldexp(a, 10 - unbiased); /* in [1024, 2048) */
+        bits_exp = unbiased + 15;
+    }
+    double whole = floor(units);
+    double rem = units - whole;          /* exact: both are in a range where doubles are exact */
+    uint32_t q = (uint32_t)whole;
+    if (rem > 0.5 || (rem == 0.5 && (q & 1u)))
+        q++;
+    /* normal: q in [1024, 2048]; the implicit bit goes into the exponent field by addition,
+     * which also carries q == 2048 into the next binade (and 65504 + ulp into infinity) */
+    uint32_t bits = bits_exp == 0 ? q : ((uint32_t)(bits_exp - 1) << 10) + q;
+    return (uint16_t)(sign | bits);
+}
+
+/* After an append of seq tokens to sequence b at positions [len, len + seq), len =
+ * cache_seqlens[b] (len < 0: no such sequence), every pooled block those positions fall in,
+ * j = len/cr ... (len + seq - 1)/cr, is rebuilt from the raw key rows the block holds: rows
+ * [j*cr, min(j*cr + cr, len + seq)).  The pooled key is the mean of those rows, per element:
+ * their sum in fp64 (exact for up to 512 fp16 values), divided by the count, rounded once to
+ * fp16.  A block's rows sit in page block_table[b][(j*cr) / page_size] (cr divides
+ * page_size), rows (j*cr) % page_size.., and its pooled row is row ((j*cr) % page_size) / cr
+ * of the same page in the pooled plane.  Blocks whose table slot or page is out of range are
+ * skipped.  raw: [n_pages][page_size][dim] fp16 bits; pooled: [n_pages][page_size/cr][dim]. */
+int orc_pool_rebuild(const uint16_t *raw, uint16_t *pooled, int32_t dim, int32_t bsz, int32_t seq,
+                     const int32_t *cache_seqlens, const int32_t *block_table,
+                     int32_t pages_per_seq, int32_t page_size, int32_t cr, int64_t n_pages)
+{
+    if (dim < 1 || bsz < 0 || seq < 0 || pages_per_seq < 1 || page_size < 1 || cr < 1 ||
+        cr > 512 || page_size % cr || n_pages < 0)
+        return ORC_EINVAL;
+    const int32_t per_page = page_size / cr;
+    for (int32_t b = 0; b < bsz; b++) {
+        const int64_t len = cache_seqlens[b];
+        if (len < 0 || seq == 0)
+            continue;
+        const int64_t end = len + seq;
+        for (int64_t j = len / cr; j <= (end - 1) / cr; j++) {
+            const int64_t first = j * cr;
+            const int64_t slot = first / page_size;
+            if (slot >= pages_per_seq)
+                continue;
+            const int64_t page = block_table[(int64_t)b * pages_per_seq + slot];
+            if (page < 0 || page >= n_pages)
+                continue;
+            const int64_t rows = (end - first) < cr ? (end - first) : cr;
+            const int64_t row0 = first % page_size;
+            for (int32_t d = 0; d < dim; d++) {
+                double s = 0.0;
+                for (int64_t r = 0; r < rows; r++)
+                    s += orc_f16_to_f64(raw[((size_t)page * page_size + row0 + r) * dim + d]);
+                pooled[((size_t)page * per_page + row0 / cr) * dim + d] =
+                    orc_f64_to_f16(s / (double)rows);
+            }
+        }
+    }
+    return ORC_OK;
+}

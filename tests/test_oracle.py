@@ -606,3 +606,108 @@ def test_staging_worthwhile_page_examples():
     assert not oracle.staging_worthwhile(1, 2080, 4096, 256)
     assert not oracle.staging_worthwhile(1024, 1024, 2048, 256)     # equal: not worthwhile
     assert oracle.staging_worthwhile(1025, 1024, 2048, 256)
+
+
+# ---------------------------------------------------------------------------------------------
+# pool rebuild at the write head (QSA KV offload, CacheLayer_qsa_offload docstring)
+# ---------------------------------------------------------------------------------------------
+
+def test_f64_to_f16_matches_numpy_on_every_midpoint_and_random_values():
+    """The oracle's rounding against numpy's float64 -> float16 cast: every finite fp16 value,
+    every midpoint between neighbours (the ties), values a hair either side of them, and
+    random doubles over all binades, signed."""
+    pos = np.arange(0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2
+    xs = np.concatenate([pos, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf),
+                         [65504.0, 65519.999, 65520.0, 1e9, 2.0 ** -25, 2.0 ** -26]])
+    g = synth.rng(0, synth.P_MISC, 616)
+    xs = np.concatenate([xs, g.standard_normal(20000) * np.exp2(g.integers(-30, 17, 20000))])
+    xs = np.concatenate([xs, -xs])
+    with np.errstate(over="ignore"):
+        want = xs.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f64_to_f16(x) for x in xs], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    assert oracle.f64_to_f16(float("inf")) == 0x7C00 and oracle.f64_to_f16(float("-inf")) == 0xFC00
+    assert oracle.f64_to_f16(float("nan")) & 0x7C00 == 0x7C00
+
+
+def _pool_fixture(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_pool_rebuild_worked_example():
+    w = _pool_fixture("pool_rebuild_worked.json")
+    ps, cr, dim, n_pages = w["page_size"], w["cr"], w["dim"], w["n_pages"]
+    raw = np.zeros((n_pages, ps, dim), dtype=np.float16)
+    for r in w["raw_rows"]:
+        raw[r["page"], r["row"]] = r["values"]
+    pooled = np.full((n_pages, ps // cr, dim), w["pooled_canary_bits"], dtype=np.uint16)
+    oracle.pool_rebuild(raw.view(np.uint16), pooled, w["cache_seqlens"], w["seq"],
+                        w["block_table"], ps, cr)
+    want = np.full_like(pooled, w["pooled_canary_bits"])
+    for e in w["expected_pooled"]:
+        want[e["page"], e["row"]] = e["bits"]
+    assert np.array_equal(pooled, want)
+    # the partial block of three rows
+    pooled[:] = w["pooled_canary_bits"]
+    oracle.pool_rebuild(raw.view(np.uint16), pooled, [-1, 0, -1], 3, w["block_table"], ps, cr)
+    assert list(pooled[1, 0]) == w["partial_three_rows"]["bits"]
+
+
+def test_pool_rebuild_closed_form_on_symmetric_blocks():
+    """Rows c + delta*(-3, -1, 1, 3) (all exact in fp16) average to c exactly, whatever c and
+    delta are; every touched block of every sequence must come out as c."""
+    cr, ps, dim, n_pages = 4, 16, 8, 12
+    g = synth.rng(0, synth.P_MISC, 617)
+    # c: multiples of 2^-4 in [-8, 8]; delta: 2^-4 .. 2^-1.  Every row is then a multiple of
+    # 2^-4 below 10 in magnitude (at most 8 significant bits), exact in fp16
+    c = g.integers(-128, 129, (n_pages, ps // cr, dim)) / 16.0
+    delta = np.exp2(g.integers(-4, 0, (n_pages, ps // cr, dim)))
+    raw = np.empty((n_pages, ps, dim), dtype=np.float16)
+    for k, f in enumerate((-3, -1, 1, 3)):
+        raw[:, k::cr] = (c + f * delta).astype(np.float16)
+    exact = np.array([(c + f * delta).astype(np.float16).astype(np.float64) for f in (-3, -1, 1, 3)])
+    assert np.array_equal(exact.mean(0), c), "construction: rows representable, mean exact"
+    table = synth.permutation(synth.rng(0, synth.P_PERM_DST, 617), n_pages).reshape(4, 3)
+    pooled = np.zeros((n_pages, ps // cr, dim), dtype=np.uint16)
+    # each sequence appends its whole 48-token range: every block complete
+    oracle.pool_rebuild(raw.view(np.uint16), pooled, [0, 0, 0, 0], 48, table, ps, cr)
+    assert np.array_equal(pooled.view(np.float16).astype(np.float64), c)
+
+
+def test_pool_rebuild_equals_numpy_mean_per_touched_block():
+    """Random fp16 keys, sequences at varied lengths (complete and partial write-head
+    blocks, appends that span pages, a -1 table entry, a negative length): every touched
+    block equals numpy's float64 mean of the block's present rows cast to float16; every
+    other pooled row keeps its value."""
+    cr, ps, dim, n_pages, pps = 4, 32, 64, 40, 6
+    g = synth.rng(0, synth.P_MISC, 618)
+    raw = synth.f16_normal(g, (n_pages, ps, dim))
+    table = synth.permutation(synth.rng(0, synth.P_PERM_DST, 618), n_pages)[:5 * pps].reshape(5, pps)
+    table[3, 2] = -1
+    lens = np.array([0, 5, 30, 61, -1], dtype=np.int32)
+    for seq in (1, 3, 7, 40):
+        pooled = synth.f16_normal(synth.rng(0, synth.P_CANARY, seq), (n_pages, ps // cr, dim))
+        before = pooled.copy()
+        oracle.pool_rebuild(raw, pooled, lens, seq, table, ps, cr)
+        want = before.copy()
+        for b, ln in enumerate(lens):
+            if ln < 0:
+                continue
+            for j in range(ln // cr, (ln + seq - 1) // cr + 1):
+                slot = j * cr // ps
+                if slot >= pps or table[b, slot] < 0:
+                    continue
+                page, row0 = table[b, slot], j * cr % ps
+                rows = min(cr, ln + seq - j * cr)
+                vals = raw[page, row0:row0 + rows].view(np.float16).astype(np.float64)
+                want[page, row0 // cr] = vals.mean(0).astype(np.float16).view(np.uint16)
+        assert np.array_equal(pooled, want), seq
+
+
+def test_pool_rebuild_argument_errors():
+    raw = np.zeros((2, 8, 4), dtype=np.uint16)
+    pooled = np.zeros((2, 2, 4), dtype=np.uint16)
+    with pytest.raises(oracle.OracleError):
+        oracle.pool_rebuild(raw, pooled, [0], 1, [[0]], 8, 3)     # cr does not divide page_size
