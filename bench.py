@@ -1086,8 +1086,9 @@ def suite_worker(torch, kvt, synth, dev, wl, peaks, jobs=16, pages_per_job=4096)
 def suite_upkeep(torch, kvt, synth, dev, peaks, reps=20):
     """The write side: a 2048-token prefill chunk appended to host pages (K and V rows of
     8 heads x 128 bf16, raw keys of 128 fp16; 256-token pages at random page ids) and one
-    decode token appended, both through kvt_paged_write; then copy_page of a full page (host
-    memcpy of the three planes after draining the stream, pooled rows on the device)."""
+    decode token appended, both through kvt_paged_write, each followed by the pool rebuild of
+    the blocks it touched (cr 4); then copy_page of a full page (host memcpy of the three
+    planes after draining the stream, pooled rows on the device)."""
     import numpy as np
     ps, n_pages, cr = 256, 1024, 4
     rbs = [8 * 128 * 2, 8 * 128 * 2, 128 * 2]
@@ -1114,6 +1115,22 @@ def suite_upkeep(torch, kvt, synth, dev, peaks, reps=20):
                      "gbs": round(nbytes / (ms * 1e-3) / GB, 2),
                      "pct_measured_d2h": round(100 * nbytes / (ms * 1e-3) / GB /
                                                peaks["d2h_sdma_gbs"], 1)}
+        # the pool kernel at the write head: the touched blocks' pooled keys rebuilt from the
+        # raw key rows just written (read back over the host link), into the HBM pooled plane
+        ptimes = []
+        for r in range(reps):
+            lens = torch.tensor([(r * 4099) % (n_pages * ps - seq)], dtype=torch.int32,
+                                device=dev)
+            kvt.kvt_paged_write(src, [b.dev for b in bufs], rbs, 1, seq, lens, table, pps, ps,
+                                n_pages)
+            t.start()
+            kvt.kvt_pool_rebuild(bufs[2].dev, pooled, 128, 1, seq, lens, table, pps, ps, cr,
+                                 n_pages)
+            ptimes.append(t.stop_ms())
+        pms = _median(ptimes)
+        blocks = (seq + cr - 1) // cr + 1
+        out[name]["pool_rebuild"] = {"blocks_at_most": blocks, "us": round(pms * 1e3, 2),
+                                     "raw_bytes_read_at_most": blocks * cr * rbs[2]}
     host_ms = []
     for r in range(reps):
         t0 = time.perf_counter()

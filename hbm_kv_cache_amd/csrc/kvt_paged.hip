@@ -7,7 +7,9 @@
 // p % page_size of page block_table[b][p / page_size].  copy_page duplicates the first
 // num_tokens rows of a page on the CPU -- the page's reasoning: a host memcpy leaves the host
 // link to the attention gather -- after draining the stream, and copies the page's pooled rows
-// (one per cr tokens, in HBM) on the device.
+// (one per cr tokens, in HBM) on the device.  pool_rebuild_kernel is the pool kernel at the
+// write head: after an append it recomputes the pooled rows of the blocks the new tokens fall
+// in, from the raw key rows those blocks hold.
 #include <algorithm>
 #include <cstring>
 
@@ -58,6 +60,79 @@ __global__ __launch_bounds__(kThreads) void paged_write_kernel(
         const int words = (int)(rb >> 4);
         for (int w = lane; w < words; w += kvt::kWave)
             __builtin_nontemporal_store(s[w], d + w);
+    }
+}
+
+// fp64 -> fp16 bit pattern, rounding to nearest with ties to even, worked on the fp64 bits:
+// keep 10 fraction bits (normal results) or count units of 2^-24 (subnormal ones) and round
+// on the dropped bits.  A carry out of the fraction moves into the exponent field by the
+// addition, which also turns 65504 + half an ulp and more into infinity.  NaN gives 0x7E00.
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double x)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+    const int ex = (int)((u >> 52) & 0x7ff);
+    const uint64_t frac = u & ((1ull << 52) - 1);
+    if (ex == 0x7ff)
+        return frac ? (uint16_t)0x7e00 : (uint16_t)(sign | 0x7c00u);
+    const int e = ex - 1023;   // |x| in [2^e, 2^(e+1)) for normal fp64
+    if (e > 15)
+        return (uint16_t)(sign | 0x7c00u);
+    if (e >= -14) {
+        uint64_t q = frac >> 42;
+        const uint64_t rem = frac & ((1ull << 42) - 1), half = 1ull << 41;
+        q += (rem > half || (rem == half && (q & 1))) ? 1 : 0;
+        return (uint16_t)(sign | (((uint32_t)(e + 15) << 10) + (uint32_t)q));
+    }
+    if (ex == 0)
+        return (uint16_t)sign;                 // fp64 subnormal: far below 2^-25
+    const int shift = 28 - e;                  // |x| / 2^-24 = significand >> shift, shift >= 43
+    if (shift > 53)
+        return (uint16_t)sign;                 // below half of 2^-24
+    const uint64_t sig = (1ull << 52) | frac;
+    uint64_t q = sig >> shift;
+    const uint64_t rem = sig & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+    q += (rem > half || (rem == half && (q & 1))) ? 1 : 0;
+    return (uint16_t)(sign | (uint32_t)q);
+}
+
+// One wave per (sequence, k-th touched block): sequence b's append covers positions
+// [len, len + seq), len = cache_seqlens[b]; block j = len / cr + k holds positions
+// [j*cr, j*cr + cr), of which rows up to the write head exist.  Each lane averages one
+// element over those rows (exact fp64 sum, one division, one rounding to fp16).
+__global__ __launch_bounds__(256) void pool_rebuild_kernel(
+    const uint16_t *__restrict__ raw, uint16_t *__restrict__ pooled, int dim, int bsz, int seq,
+    const int32_t *__restrict__ cache_seqlens, const int32_t *__restrict__ block_table,
+    int pages_per_seq, int page_size, int cr, int64_t n_pages, int blocks_per_seq)
+{
+    const int lane = threadIdx.x & (kvt::kWave - 1);
+    const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t b = w / blocks_per_seq;
+    if (b >= bsz)
+        return;
+    const int64_t len = cache_seqlens[b];
+    if (len < 0)
+        return;
+    const int64_t end = len + seq;
+    const int64_t j = len / cr + (w - b * blocks_per_seq);
+    if (j > (end - 1) / cr)
+        return;
+    const int64_t first = j * cr;
+    const int64_t slot = first / page_size;
+    if (slot >= pages_per_seq)
+        return;
+    const int64_t page = block_table[b * pages_per_seq + slot];
+    if (page < 0 || page >= n_pages)
+        return;
+    const int rows = (int)(end - first < cr ? end - first : cr);
+    const int64_t row0 = first % page_size;
+    const uint16_t *src = raw + (page * page_size + row0) * dim;
+    uint16_t *dst = pooled + (page * (page_size / cr) + row0 / cr) * dim;
+    for (int d = lane; d < dim; d += kvt::kWave) {
+        double s = 0.0;
+        for (int r = 0; r < rows; r++)
+            s += (double)__builtin_bit_cast(_Float16, src[(int64_t)r * dim + d]);
+        dst[d] = f64_to_f16_rne(s / (double)rows);
     }
 }
 
@@ -164,5 +239,39 @@ extern "C" int kvt_copy_page(const void *const *src_host, void *const *dst_host,
             KVT_HIP(hipMemcpyAsync(d, s, (size_t)(nb * pooled_row_bytes),
                                    hipMemcpyDeviceToDevice, kvt::as_stream(stream)));
     }
+    return KVT_OK;
+}
+
+// QSA-KVO, CacheLayer_qsa_offload docstring: the pool kernel at the write head.  Rebuilds the
+// pooled rows of every block an append of seq tokens touched (reading the raw key plane only
+// there) as the mean of the raw rows each block holds, rounded once to fp16.
+extern "C" int kvt_pool_rebuild(const void *raw_k, void *pooled, int32_t dim, int32_t bsz,
+                                int32_t seq, const int32_t *cache_seqlens,
+                                const int32_t *block_table, int32_t pages_per_seq,
+                                int32_t page_size, int32_t cr, int64_t n_pages, void *stream)
+{
+    if (dim < 1 || bsz < 0 || seq < 0 || pages_per_seq < 1 || page_size < 1 || cr < 1 ||
+        cr > 512 || page_size % cr || n_pages < 0)
+        return kvt::fail(KVT_EINVAL, "kvt_pool_rebuild: dim=%d bsz=%d seq=%d pages_per_seq=%d "
+                         "page_size=%d cr=%d (1..512, dividing page_size) n_pages=%lld", dim, bsz,
+                         seq, pages_per_seq, page_size, cr, (long long)n_pages);
+    if (bsz == 0 || seq == 0 || n_pages == 0)
+        return KVT_OK;
+    if (!raw_k || !pooled || !cache_seqlens || !block_table)
+        return kvt::fail(KVT_EINVAL, "kvt_pool_rebuild: null pointer");
+    if (!kvt::aligned(raw_k, 2) || !kvt::aligned(pooled, 2))
+        return kvt::fail(KVT_EALIGN, "kvt_pool_rebuild: planes must be 2-byte aligned");
+    if ((int64_t)page_size * dim > INT64_MAX / n_pages / 2)
+        return kvt::fail(KVT_ERANGE, "kvt_pool_rebuild: planes too large");
+    // a sequence's append touches at most ceil(seq / cr) + 1 blocks (a partial one first)
+    const int64_t blocks_per_seq = ((int64_t)seq + cr - 1) / cr + 1;
+    const int64_t waves = (int64_t)bsz * blocks_per_seq;
+    if (waves > 0x7fffffffll)
+        return kvt::fail(KVT_ERANGE, "kvt_pool_rebuild: bsz x touched blocks too large");
+    hipLaunchKernelGGL(pool_rebuild_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       kvt::as_stream(stream), static_cast<const uint16_t *>(raw_k),
+                       static_cast<uint16_t *>(pooled), dim, bsz, seq, cache_seqlens,
+                       block_table, pages_per_seq, page_size, cr, n_pages, (int)blocks_per_seq);
+    KVT_LAUNCHED("pool_rebuild_kernel");
     return KVT_OK;
 }

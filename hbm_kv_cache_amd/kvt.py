@@ -51,6 +51,8 @@ _SIGNATURES = {
     "kvt_gather_attn_decode_noalloc": (c_int, [_P, c_int32, c_int32, c_int32, c_int32, _P, _P,
                                                c_int64, c_int64, c_int64, c_int64, _P, c_int32,
                                                _P, c_int32, _P, _P, c_float, _P, _P]),
+    "kvt_pool_rebuild": (c_int, [_P, _P, c_int32, c_int32, c_int32, _P, _P, c_int32, c_int32,
+                                 c_int32, c_int64, _P]),
     "kvt_attn_prefill": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P, c_int64,
                                  _P, _P, c_int64, c_int32, c_int32, c_float, _P, _P]),
     "kvt_attn_prefill_state_bytes": (c_size_t, [c_int64, c_int32, c_int32]),
@@ -462,3 +464,11 @@ def kvt_attn_prefill_splitk(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_hea
         _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
         int(n_head), _ptr(k_tail), _ptr(v_tail), int(n_kv), int(kv_format), int(bool(causal)),
         float(scale), _ptr(ws), int(ws_bytes), _ptr(out), _stream(stream)))
+
+
+def kvt_pool_rebuild(raw_k, pooled, dim, bsz, seq, cache_seqlens, block_table, pages_per_seq,
+                     page_size, cr, n_pages, stream=None):
+    _check("kvt_pool_rebuild", load().kvt_pool_rebuild(
+        _ptr(raw_k), _ptr(pooled), int(dim), int(bsz), int(seq), _ptr(cache_seqlens),
+        _ptr(block_table), int(pages_per_seq), int(page_size), int(cr), int(n_pages),
+        _stream(stream)))

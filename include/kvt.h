@@ -22,6 +22,7 @@
  *   kvt_worker_*         an ordered, event-timed asynchronous transfer queue around the swap
  *   kvt_paged_write      append new K/V (and raw key) rows into paged planes via a block table
  *   kvt_copy_page        duplicate a page's first rows (host planes on the CPU, pooled on device)
+ *   kvt_pool_rebuild     recompute the pooled keys of the blocks an append touched
  *
  * Sources (page titles; each entry point names the section it follows):
  *   [vLLM-CPU] vLLM fork, "v1/kv_offload/cpu/gpu_worker.py" (CPU offloading worker)
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 12
+#define KVT_ABI_VERSION 14
 
 /* status codes */
 #define KVT_OK 0
@@ -536,6 +537,28 @@ int kvt_copy_page(const void *const *src_host, void *const *dst_host, const int6
                   int32_t n_planes, int64_t from_page, int64_t to_page, int32_t page_size,
                   int32_t num_tokens, const void *src_pooled, void *dst_pooled,
                   int64_t pooled_row_bytes, int32_t cr, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * Pool rebuild at the write head.  [QSA-KVO] CacheLayer_qsa_offload docstring: the raw key
+ * plane is read only around the write head, where the pool kernel rebuilds the pooled blocks
+ * an append touched.  The page does not give the pooling function; here a block's pooled key
+ * is the mean of the raw key rows it holds, per element: the rows' exact sum (fp64), divided
+ * by their count, rounded once to fp16 (to nearest, ties to even; NaN gives 0x7E00).
+ *   Call after kvt_paged_write has placed the raw rows of an append of seq tokens, with the
+ *   same cache_seqlens (the lengths before the append) and block table.  For sequence b,
+ *   len = cache_seqlens[b] (< 0: skipped); blocks j = len/cr ... (len+seq-1)/cr are rebuilt,
+ *   each from rows [j*cr, min(j*cr + cr, len + seq)) -- the write head's partial block from
+ *   the rows it has so far.  Block j lies in page block_table[b][(j*cr) / page_size]
+ *   (skipped when that slot is past pages_per_seq or the entry is outside [0, n_pages)).
+ *   raw_k   fp16 [n_pages][page_size][dim], device pointer (host-mapped or HBM)
+ *   pooled  fp16 [n_pages][page_size/cr][dim], device pointer (HBM); pooled row
+ *           ((j*cr) % page_size) / cr of the block's page is written, no other
+ * Limits: 1 <= cr <= 512, cr divides page_size; planes 2-byte aligned.  Enqueued on stream.
+ * ---------------------------------------------------------------------------------------- */
+int kvt_pool_rebuild(const void *raw_k, void *pooled, int32_t dim, int32_t bsz, int32_t seq,
+                     const int32_t *cache_seqlens, const int32_t *block_table,
+                     int32_t pages_per_seq, int32_t page_size, int32_t cr, int64_t n_pages,
+                     void *stream);
 
 /* ----------------------------------------------------------------------------------------
  * Workspace sizes by operation: one entry point over the *_ws_bytes / *_state_bytes calls
