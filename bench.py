@@ -26,7 +26,8 @@ import sys
 import time
 
 GB = 1e9
-PCIE5_X16_PEAK_GBS = 64.0   # AMD: PCIe 5.0 x16, 128 GB/s bidirectional -> 64 GB/s per direction
+# PCIe 5.0 x16 per direction: 32 GT/s x 16 lanes x 128/130 (line code) / 8 bits = 63.0 GB/s
+PCIE5_X16_PEAK_GBS = 63.0
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -40,9 +41,10 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--ctx", type=int, default=262144)
-    p.add_argument("--layout", default="block_head_major",
+    p.add_argument("--layout", default="token_major",
                    choices=["block_head_major", "token_major"],
-                   help="host K/V plane layout (block-local head-major, or token-major)")
+                   help="host K/V plane layout: token-major [token][head][dim] as on the pages "
+                        "(default), or block-local head-major")
     p.add_argument("--suite", nargs="?", const="all", default=None,
                    help="also measure the other workloads: all, or a comma list of "
                         "prefill, chain, swap1, small, swap32, qsa, decode1m, worker, upkeep, "
@@ -50,6 +52,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bound on the CPU-oracle baseline's wall time")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the compact per-config figures (one-layer and 32-layer swaps, "
+                        "small pages, decode at 1M, tiered prefill)")
     return p.parse_args()
 
 
@@ -249,19 +254,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PMC_RECORD = os.path.join(ROOT, "profiles", "decode_step_262k_pmc.json")
 
 
-def kernel_traffic(kernel):
-    """Bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE record, each
-    counter scaled by what it read for a plain copy kernel of known size.  None when there is
-    no record, or it was taken on another version of the kernel's source file."""
+def _pmc_record(kernel):
+    """The committed counter record of `kernel`, or None when there is none or it was taken on
+    another version of the kernel's source file."""
     import hashlib
     try:
         rec = json.load(open(PMC_RECORD))["kernels"][kernel]
         src = hashlib.sha256(open(os.path.join(ROOT, rec["source"]), "rb").read()).hexdigest()
     except (OSError, ValueError, KeyError, TypeError):
         return None
-    if rec.get("source_sha256") != src:
-        return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec if rec.get("source_sha256") == src else None
+
+
+def kernel_traffic(kernel):
+    """Bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE record, each
+    counter scaled by what it read for a plain copy kernel of known size."""
+    rec = _pmc_record(kernel)
+    return rec.get("traffic_bytes_per_launch") if rec else None
+
+
+def kernel_traffic_ea(kernel):
+    """Per-launch bytes of `kernel` by destination, from the L2's external-access request
+    counters in the same record: host-link (IO) and HBM (DRAM) reads and writes."""
+    rec = _pmc_record(kernel)
+    return rec.get("ea_counters_per_launch") if rec else None
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        for l in open("/proc/cpuinfo"):
+            if l.lower().startswith("model name"):
+                return l.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(wl, seconds):
@@ -289,7 +316,7 @@ def cpu_baseline(wl, seconds):
             break
     steps_s = n / el
     return {"value": round(wl.gather_bytes * steps_s / GB, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "steps_per_s": round(steps_s, 3),
+            "cpu_model": cpu_model(), "kind": "oracle", "steps_per_s": round(steps_s, 3),
             "sample": f"{n} oracle decode steps at {wl.ctx} ctx (fp64 scoring of {wl.n_blocks} "
                       f"blocks x 8 heads, full-sort top-32, memcpy gather of 8 MiB, fp64 GQA "
                       f"attention over 2048 keys x 64 heads) in {el:.1f}s"}
@@ -377,17 +404,13 @@ def main():
             "decode_tok_s": round(1e3 / r_other["ms_per_step"], 2),
             "gather_attn_gbs": gbs(r_other["part_ms"]["gather_attn"])},
         "link_peaks": peaks,
-        "roofline": {"bound": "pcie",
-                     "kernel": "gather_decode_partial (timed with its decode_merge: "
-                               "kvt_gather_attn_decode)",
-                     "achieved": round(achieved, 3),
-                     "peak": PCIE5_X16_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PCIE5_X16_PEAK_GBS, 4),
-                     "peak_measured_h2d": peaks["h2d_sdma_gbs"],
-                     "frac_measured": round(achieved / peaks["h2d_sdma_gbs"], 4),
+        "roofline": {**_pcie_roofline(achieved, peaks,
+                                      kernel="gather_decode_partial (timed with its "
+                                             "decode_merge: kvt_gather_attn_decode)"),
                      "bytes_per_launch": wl.gather_bytes, "avg_launch_ms": round(kern_ms, 5),
                      "traffic": kernel_traffic("gather_decode_partial"),
-                     "traffic_unit": "bytes per launch"},
+                     "traffic_unit": "bytes per launch",
+                     "traffic_by_destination": kernel_traffic_ea("gather_decode_partial")},
     }
     if args.suite:
         line["suite"] = run_suite(torch, kvt, synth, dev, wl, args, peaks)
@@ -395,6 +418,9 @@ def main():
         log("cpu baseline ...")
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     wl.free()
+    if not args.no_configs:
+        line["configs"] = {"C4_topk_decode_262k": "the headline (value, roofline, cpu_baseline)",
+                           **run_configs(torch, kvt, synth, dev, peaks, args)}
     print(json.dumps(line), flush=True)
 
 
@@ -441,6 +467,7 @@ def cpu_swap_rates(src, dst_dev, dev_base, sizes, reps=3):
             ts.append(time.perf_counter() - t0)
         out[key] = round(nbytes / _median(ts) / GB, 2)
     out["cores"] = _cpu_threads()
+    out["cpu_model"] = cpu_model()
     del buf
     return out
 
@@ -631,10 +658,12 @@ def prefill_flops(n_q, q_pos0, n_qh, hd, n_kv, causal=True):
     return 4 * hd * n_qh * keys
 
 
-def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
+def suite_prefill(torch, kvt, synth, dev, peaks, reps=5, compact=False):
     """Tiered prefill: 180,000-token q8_0 cache (8 KV heads x 128), cells [0, 94208) in HBM and
     the rest in pinned host memory; a 2048-query causal chunk at the tail with 32 query heads.
-    Stage the used host rows into HBM once, then flash attention over head + staging."""
+    Stage the used host rows into HBM once, then flash attention over head + staging.
+    compact: only the staging, the staged attention and the pipelined form (16,384-row
+    arena), with a shorter CPU baseline."""
     import numpy as np
     n_kv, n_head, n_q, n_qh, kvh, hd = 180000, 94208, 2048, 32, 8, 128
     n_tail = n_kv - n_head
@@ -696,6 +725,25 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5):
     st_sdma = stage_ms(kvt.COPY_SDMA)
     st_kernel = stage_ms(kvt.COPY_KERNEL)
     a_staged = attn_ms(k_all, v_all, n_head, stage[0], stage[1])
+    if compact:
+        p_arena = pipe_ms(2 * 16384)
+        st = min(st_sdma, st_kernel)
+        res = {"n_kv": n_kv, "n_head": n_head, "n_q": n_q, "stage_bytes": stage_bytes,
+               "flops": flops, "stage_sdma_ms": round(st_sdma, 4),
+               "stage_kernel_ms": round(st_kernel, 4),
+               "stage_gbs": round(stage_bytes / (st * 1e-3) / GB, 2),
+               "attn_staged_ms": round(a_staged, 4),
+               "attn_tflops": round(flops / (a_staged * 1e-3) / 1e12, 1),
+               "prefill_tok_s_staged": round(n_q / ((st + a_staged) * 1e-3), 1),
+               "pipelined_arena_16384_ms": round(p_arena, 4),
+               "prefill_tok_s_pipelined": round(n_q / (p_arena * 1e-3), 1),
+               "cpu_baseline": cpu_prefill(k, v, ht, q_np, n_head, n_kv, kvh, row, scale,
+                                           stage_bytes, budget_s=8.0)}
+        del ht, k, v
+        host.free()
+        del k_all, v_all, stage, out, q, state
+        torch.cuda.empty_cache()
+        return res
     a_inplace = attn_ms(k_all, v_all, n_head, host.dev, host.dev + n_tail * row)
     a_hbm = attn_ms(k_all, v_all, n_kv, None, None)
     p_one = pipe_ms(2 * n_tail)          # the whole tail in one bucket
@@ -889,7 +937,7 @@ def cpu_prefill(k, v, ht, q_np, n_head, n_kv, kvh, row, scale, stage_bytes, budg
                             threads=threads)
         el += time.perf_counter() - t0
         rows += r
-    return {"kind": "oracle", "cores": threads,
+    return {"kind": "oracle", "cores": threads, "cpu_model": cpu_model(),
             "stage_gbs": round(stage_bytes / st / GB, 2),
             "attn_rows_per_s": round(rows / el, 3),
             "sample": f"staging memcpy of the {n_tail}-row tail; fp64 attention of the last {rows} "
@@ -1234,6 +1282,128 @@ def suite_rows(torch, kvt, synth, dev, wl, peaks, row_counts=(1, 16, 64, 128, 25
     del sk, sv, ws, out
     torch.cuda.empty_cache()
     return res
+
+
+def _pcie_roofline(gbs, peaks, direction="h2d", kernel=None):
+    """A host-link kernel against the PCIe Gen5 x16 per-direction peak (63.0 GB/s nominal) and
+    against the same run's measured DMA-engine peak."""
+    pk = peaks["h2d_sdma_gbs"] if direction == "h2d" else peaks["d2h_sdma_gbs"]
+    r = {"bound": "pcie", "achieved": round(gbs, 3), "peak": PCIE5_X16_PEAK_GBS, "unit": "GB/s",
+         "frac": round(gbs / PCIE5_X16_PEAK_GBS, 4), "peak_measured": pk,
+         "frac_measured": round(gbs / pk, 4)}
+    if kernel:
+        r["kernel"] = kernel
+    return r
+
+
+def run_configs(torch, kvt, synth, dev, peaks, args):
+    """One compact entry per workload besides the headline: its figure, the roofline of its
+    dominant kernel and the CPU oracle's rate on the same data."""
+    cfg = {}
+
+    def timed(name, fn):
+        t0 = time.time()
+        log(f"config: {name}")
+        r = fn()
+        r["wall_s"] = round(time.time() - t0, 1)
+        cfg[name] = r
+        log(f"config {name}: {json.dumps(r)[:400]}")
+
+    def c1():
+        r = suite_one_layer(torch, kvt, synth, dev, peaks)
+        return {"workload": "one layer: K and V planes of 256 x 32 KiB fp16 pages in pinned "
+                            "host memory, 64 random block ids host->HBM (4 MiB), then stored back",
+                "metric": "load GB/s (kernel)", "value": r["h2d_kernel_gbs"], "unit": "GB/s",
+                "store_gbs": r["d2h_kernel_gbs"], "load_sdma_gbs": r["h2d_sdma_gbs"],
+                "load_runtime_gbs": r["h2d_runtime_gbs"],
+                "roofline": _pcie_roofline(r["h2d_kernel_gbs"], peaks, kernel="copy_desc_kernel"),
+                "cpu_baseline": {**r["cpu_baseline"], "value": r["cpu_baseline"]["all_threads_gbs"],
+                                 "unit": "GB/s",
+                                 "sample": "the last load's 128 descriptors of 32 KiB"}}
+
+    def c2():
+        r = suite_32_layers(torch, kvt, synth, dev, peaks, reps=1)
+        return {"workload": "32 layers: 64 tensors of 8192 x 32 KiB bf16 blocks, host rows of 4 "
+                            "pages + 4 KiB pad, 4096 random blocks per tensor with a random skip "
+                            "(262,144 descriptors, 8 GiB a direction)",
+                "metric": "load GB/s (kernel)", "value": r["h2d_kernel_gbs"], "unit": "GB/s",
+                "store_gbs": r["d2h_kernel_gbs"], "load_sdma_gbs": r["h2d_sdma_gbs"],
+                "load_runtime_gbs": r["h2d_runtime_gbs"],
+                "table_build_ms": r["table_build_ms"],
+                "roofline": _pcie_roofline(r["h2d_kernel_gbs"], peaks, kernel="copy_desc_kernel"),
+                "cpu_baseline": {**r["cpu_baseline"],
+                                 "value": r["cpu_baseline"]["all_threads_gbs"], "unit": "GB/s"}}
+
+    def c3():
+        r = suite_small_pages(torch, kvt, synth, dev, peaks, reps=1)
+        row2k = next(x for x in r["sweep"] if x["page_bytes"] == 2048
+                     and x["host_offset_mod16"] == 0)
+        return {"workload": "65,536 scattered pages host->HBM, 512 B .. 64 KiB (kernel, DMA "
+                            "engines, runtime copies); 2 KiB pages at the workload's size",
+                "metric": "2 KiB-page load GB/s (kernel)", "value": row2k["kernel_gbs"],
+                "unit": "GB/s", "sdma_gbs_2k": row2k["sdma_gbs"],
+                "runtime_gbs_2k": row2k["runtime_gbs"],
+                "crossover_bytes_sdma": r["h2d_crossover_bytes"],
+                "crossover_bytes_runtime": r["h2d_crossover_bytes_runtime"],
+                "sweep_kernel_gbs": {str(x["page_bytes"]) + ("@8mod16" if x["host_offset_mod16"]
+                                                              else ""): x["kernel_gbs"]
+                                     for x in r["sweep"]},
+                "roofline": _pcie_roofline(row2k["kernel_gbs"], peaks, kernel="copy_small_kernel"),
+                "cpu_baseline": {"value": r["cpu_baseline"]["512B"]["all_threads_gbs"],
+                                 "unit": "GB/s", "kind": "oracle",
+                                 "cores": r["cpu_baseline"]["512B"]["cores"],
+                                 "cpu_model": cpu_model(),
+                                 "sample": "the memcpy loop over 65,536 pages of 512 B",
+                                 "per_size": r["cpu_baseline"]}}
+
+    def c4():
+        w1m = DecodeWorkload(torch, kvt, synth, dev, 1 << 20, 2 * (args.warmup + args.steps) + 4,
+                             "token_major")
+        rr = w1m.run(args.steps, args.warmup)
+        kern = w1m.gather_bytes / (rr["part_ms"]["gather_attn"] * 1e-3) / GB
+        out = {"workload": "top-k sparse decode step at 1,048,576 tokens (16,384 pooled blocks, "
+                           "2 GiB host planes per K/V), token-major host planes",
+               "metric": "gather GB/s over whole steps", "unit": "GB/s",
+               "value": round(w1m.gather_bytes / (rr["ms_per_step"] * 1e-3) / GB, 3),
+               "decode_tok_s": round(1e3 / rr["ms_per_step"], 2),
+               "part_ms": {k: round(v, 5) for k, v in rr["part_ms"].items()},
+               "roofline": _pcie_roofline(kern, peaks, kernel="gather_decode_partial "
+                                          "(with decode_merge)")}
+        if not args.no_cpu:
+            out["cpu_baseline"] = cpu_baseline(w1m, 5.0)
+        w1m.free()
+        return out
+
+    def c5():
+        r = suite_prefill(torch, kvt, synth, dev, peaks, reps=5, compact=True)
+        tf = r["attn_tflops"]
+        cb = r["cpu_baseline"]
+        return {"workload": "tiered prefill: 180,000-token q8_0 cache, [0, 94208) in HBM and the "
+                            "tail in pinned host memory; 2048 causal queries x 32 heads at the "
+                            "tail; tail staged host->HBM once, then flash attention",
+                "metric": "prefill tok/s (staging overlapped with attention, 16,384-row arena)",
+                "value": r["prefill_tok_s_pipelined"], "unit": "tok/s",
+                "prefill_tok_s_staged": r["prefill_tok_s_staged"],
+                "stage_gbs": r["stage_gbs"], "attn_ms": r["attn_staged_ms"],
+                "attn_tflops": tf,
+                "roofline": {"bound": "mfma", "kernel": "prefill_attn (q8_0)",
+                             "achieved": tf, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                             "flops_per_launch": r["flops"]},
+                "staging_roofline": _pcie_roofline(r["stage_gbs"], peaks,
+                                                   kernel="kvt_stage_tail (DMA engine or "
+                                                          "copy_span_kernel, the faster)"),
+                "cpu_baseline": {"value": cb["attn_rows_per_s"], "unit": "query rows/s",
+                                 "stage_gbs": cb["stage_gbs"], "kind": "oracle",
+                                 "cores": cb["cores"], "cpu_model": cb["cpu_model"],
+                                 "sample": cb["sample"]}}
+
+    timed("C1_swap_1_layer", c1)
+    timed("C3_small_pages", c3)
+    timed("C5_tiered_prefill", c5)
+    timed("C4_topk_decode_1m", c4)
+    timed("C2_swap_32_layers", c2)
+    return cfg
 
 
 def run_suite(torch, kvt, synth, dev, wl, args, peaks):
