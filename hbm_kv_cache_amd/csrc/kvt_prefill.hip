@@ -77,10 +77,45 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// The same product with both operands holding bf16 bit patterns.
+__device__ __forceinline__ f32x16 mfma32_bf16(f16x8 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// x * y rounded on its own: the empty asm hides the product from contraction into a later
+// fused multiply-add.
+__device__ __forceinline__ float mul_rounded(float x, float y)
+{
+    float r = x * y;
+    asm volatile("" : "+v"(r));
+    return r;
+}
+
+// fp32 pairs -> bf16 pairs rounded to nearest even (bit patterns, first value low).
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b)
+{
+    auto rne = [](float x) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, x);
+        return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    };
+    return rne(a) | (rne(b) << 16);
+}
+// A value as the sum of two bf16 values: hi = bf16(x), lo = bf16(x - hi).  For an fp16 x
+// (11 significant bits) the sum is exactly x; for an fp32 x it carries 16 significant bits.
+__device__ __forceinline__ void bf16_split(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    hi = bf16_pair(a, b);
+    const float ha = __builtin_bit_cast(float, hi << 16);
+    const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
+    lo = bf16_pair(a - ha, b - hb);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -163,10 +198,9 @@ __device__ __forceinline__ void store_raw(unsigned char *rawbuf,
 }
 
 // Thread (plane = wave / 4, block = wave % 4, key = lane) turns its 32 values of the raw tile
-// into fp16 in the tile used by the MFMA: K and V both as rows [key][d].  q8_0:
-// the block's dequantisation; fp16: the values as stored; bf16: each value converted to fp16,
-// which is exact for magnitudes in [2^-17, 65504] (bf16 carries 8 significant bits; below 2^-17
-// the fp16 subnormal spacing of 2^-24 rounds, and beyond 65504 the result is infinite).
+// into the 16-bit tile used by the MFMA: K and V both as rows [key][d].  q8_0: the block's
+// dequantisation to fp16; fp16 and bf16: the values as stored (bf16 tiles go to the bf16 MFMA,
+// with the query and the probabilities each split into two bf16 parts).
 template <int F>
 __device__ __forceinline__ void dequant_tile(const unsigned char *rawbuf, unsigned char *buf,
                                              int wave, int lane)
@@ -193,14 +227,7 @@ __device__ __forceinline__ void dequant_tile(const unsigned char *rawbuf, unsign
             for (int e = 0; e < 4; e++)
                 d[4 * c + e] = x[e];
         }
-        if constexpr (F == KVT_BF16) {
-#pragma unroll
-            for (int k = 0; k < 16; k++) {
-                const float lo = __builtin_bit_cast(float, d[k] << 16);
-                const float hi = __builtin_bit_cast(float, d[k] & 0xffff0000u);
-                d[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, h2));
-            }
-        }
+
     }
     unsigned char *dst = buf + (is_v ? kLdsK + lane * kVPitch : lane * kKPitch) + blk * 64;
 #pragma unroll
@@ -262,11 +289,25 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     const int n_tiles = n_tiles_all < tc ? n_tiles_all : tc;
 
     // Q^T as MFMA B operands: column i = query row, k = d = 16*kd + 8*g + 0..7
+    // bf16 caches: the fp16 query as two bf16 halves (qb high parts, qlo low parts), exactly
+    constexpr bool kBf = F == KVT_BF16;
     f16x8 qb[8];
+    f16x8 qlo[kBf ? 8 : 1];
     const _Float16 *qrow = q + (t_ld * n_qh + qh) * kHd + 8 * g;
 #pragma unroll
     for (int kd = 0; kd < 8; kd++)
         qb[kd] = *reinterpret_cast<const f16x8 *>(qrow + 16 * kd);
+    if constexpr (kBf) {
+#pragma unroll
+        for (int kd = 0; kd < 8; kd++) {
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                bf16_split((float)qb[kd][2 * e], (float)qb[kd][2 * e + 1], hi[e], lo[e]);
+            qb[kd] = __builtin_bit_cast(f16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+            qlo[kd] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+        }
+    }
 
     f32x16 o[4];
     float m = -INFINITY, l = 0.f;   // running max (raw logits) and sum
@@ -341,7 +382,12 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
                 for (int st = 0; st < 2; st++) {
                     const f16x8 a = *reinterpret_cast<const f16x8 *>(
                         lk + (32 * st + i) * kKPitch + (16 * kd + 8 * g) * 2);
-                    s[st] = mfma32(a, qb[kd], s[st]);
+                    if constexpr (kBf) {
+                        s[st] = mfma32_bf16(a, qb[kd], s[st]);
+                        s[st] = mfma32_bf16(a, qlo[kd], s[st]);
+                    } else {
+                        s[st] = mfma32(a, qb[kd], s[st]);
+                    }
                 }
             }
             // lane holds S[query i][key0 + 32*st + 8*(r/4) + 4*g + r%4] in s[st][r]
@@ -367,14 +413,21 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
                     mt = fmaxf(mt, s[st][r]);
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
             const float m_new = fmaxf(m, mt);
-            // every logit is scaled by c > 0, so the max commutes with the scaling.  An
-            // unchanged max rescales by exactly 1: exp2(m*c - round(m*c)) would be 1 + the
-            // product's rounding error, compounding over thousands of tiles into a drift of
-            // the early keys' weights against the later ones (and rescaling O every tile).
-            const float mc = m_new == -INFINITY ? 0.f : m_new * scale_log2;
+            // every logit is scaled by c > 0, so the max commutes with the scaling.  The
+            // probabilities are exp2(s*c - mc) with mc = round(m*c), one rounding (an FMA): they
+            // are relative to the rounded reference, so the state carried from earlier tiles
+            // is rebased by exp2(round(m_old*c) - round(m_new*c)) -- exactly 1 when the max is
+            // unchanged.  Rebasing by exp2(m_old*c - round(m_new*c)) instead would be off by
+            // m_old*c's rounding error: a drift over thousands of tiles for ordinary logits,
+            // and factors of 2^4 and more for logits near 1e8.  Both products are kept whole
+            // (mul_rounded: no fused multiply-add).
+            const float mc = m_new == -INFINITY ? 0.f : mul_rounded(m_new, scale_log2);
             const float alpha = m == -INFINITY ? 0.f
-                                : (m_new == m ? 1.f : __builtin_amdgcn_exp2f(m * scale_log2 - mc));
-            uint32_t pk[2][8];   // fp16 probabilities, packed in pairs
+                                : (m_new == m ? 1.f
+                                              : __builtin_amdgcn_exp2f(mul_rounded(m, scale_log2) - mc));
+            // probabilities packed in pairs: fp16; for bf16 caches two bf16 parts, pk + pl
+            uint32_t pk[2][8];
+            uint32_t pl[2][kBf ? 8 : 1];
             float psum = 0.f;
 #pragma unroll
             for (int st = 0; st < 2; st++) {
@@ -383,8 +436,11 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][r], scale_log2, -mc));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][r + 1], scale_log2, -mc));
                     psum += p0 + p1;
-                    pk[st][r >> 1] =
-                        __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, h2));
+                    if constexpr (kBf)
+                        bf16_split(p0, p1, pk[st][r >> 1], pl[st][r >> 1]);
+                    else
+                        pk[st][r >> 1] = __builtin_bit_cast(
+                            uint32_t, __builtin_convertvector(f32x2{p0, p1}, h2));
                 }
             }
             psum += __shfl_xor(psum, 32, 64);
@@ -412,7 +468,14 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
                                               2 * (32 * dt + tr_c);
                     const f16x4 lo = tr_read(vp), hi = tr_read(vp + 8 * kVPitch);
                     const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[dt] = mfma32(a, pb, o[dt]);
+                    if constexpr (kBf) {
+                        const f16x8 pbl = __builtin_bit_cast(
+                            f16x8, u32x4{pl[st][r0], pl[st][r0 + 1], pl[st][r0 + 2], pl[st][r0 + 3]});
+                        o[dt] = mfma32_bf16(a, pb, o[dt]);
+                        o[dt] = mfma32_bf16(a, pbl, o[dt]);
+                    } else {
+                        o[dt] = mfma32(a, pb, o[dt]);
+                    }
                 }
             }
         }
@@ -458,10 +521,10 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
 }
 
 // Split-K merge: one thread per lane of each (workgroup, wave) of the split launch.  The
-// splits' (o, m, l) -- o and l relative to 2^(m*c) -- fold in split order: M = max m_s, then
-// o = sum o_s 2^((m_s - M) c), l = sum l_s 2^((m_s - M) c); a split that saw no key (m = -inf)
-// weighs 0.  The result, o / l, goes to out[t][qh][d] with the kernel's own lane mapping
-// (query row lane % 32, dims 32*dt + 8*(r/4) + 4*(lane/32) + r%4).
+// splits' (o, m, l) -- o and l relative to 2^round(m*c) -- fold in split order: M = max m_s,
+// then o = sum o_s w_s, l = sum l_s w_s with w_s = 2^(round(m_s*c) - round(M*c)); a split that
+// saw no key (m = -inf) weighs 0.  The result, o / l, goes to out[t][qh][d] with the kernel's
+// own lane mapping (query row lane % 32, dims 32*dt + 8*(r/4) + 4*(lane/32) + r%4).
 __global__ __launch_bounds__(64) void prefill_split_merge(const float *__restrict__ state,
                                                           int n_split, int kvh, int group,
                                                           int64_t n_q, int n_qh,
@@ -482,7 +545,10 @@ __global__ __launch_bounds__(64) void prefill_split_merge(const float *__restric
     for (int x = 0; x < n_split; x++) {
         const float *b = base + x * sstride;
         const float mx = b[64 * 64];
-        const float w = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mx - M) * scale_log2);
+        // o_s and l_s are relative to round(m_s * c) (see prefill_attn): rebase by the same
+        const float w = mx == -INFINITY ? 0.f
+                                        : __builtin_amdgcn_exp2f(mul_rounded(mx, scale_log2) -
+                                                                 mul_rounded(M, scale_log2));
         L = fmaf(b[65 * 64], w, L);
 #pragma unroll
         for (int j = 0; j < 64; j++)

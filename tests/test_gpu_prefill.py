@@ -328,8 +328,9 @@ def test_prefill_argument_errors(gpu):
     (600, 50, 16, 2, True, 0),          # group 8, all in the tail
 ])
 def test_prefill_fp_caches_match_oracle(gpu, fmt, n_kv, n_q, n_qh, kvh, causal, n_head):
-    """fp16 and bf16 caches: the values as stored (bf16 converted to fp16, exact at these
-    magnitudes) on the same MFMA path; within 2e-3 of the fp64 oracle."""
+    """fp16 and bf16 caches: the values as stored (fp16 on the fp16 MFMA, bf16 on the bf16
+    MFMA with the query and probabilities split into two bf16 parts); within 2e-3 of the fp64
+    oracle."""
     k, v = _cache(n_kv, kvh, n_kv + n_q + fmt, fmt)
     q = synth.f16_normal(synth.rng(5, synth.P_Q, n_kv + fmt), (n_q, n_qh, 128))
     q_pos0 = n_kv - n_q
@@ -340,6 +341,55 @@ def test_prefill_fp_caches_match_oracle(gpu, fmt, n_kv, n_q, n_qh, kvh, causal, 
                               ORACLE_FMT[fmt], causal, 1 / math.sqrt(128))
     err = np.max(np.abs(got - ref))
     assert np.isfinite(got).all() and err <= TOL, err
+
+
+def _bf16_bits(x):
+    """float32 values -> bf16 bit patterns, rounded to nearest even."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("tiers", ["all_hbm", "head_and_tail"])
+def test_prefill_bf16_cache_beyond_the_fp16_range(gpu, tiers):
+    """A bf16 cache with keys and values far past fp16's range among N(0,1) values: keys with
+    one entry of +-7e4 or +-1e5 (at most one such key per head and dimension, so that large
+    logits stay well apart -- closer ones would need more than fp32 to resolve) and entries of
+    1e-30; values with +-7e4, +-1e5 and +-3e9 entries anywhere.  The values are used as stored,
+    so the output is finite and matches the fp64 oracle within 2e-3 of max(1, sum_j p_j |v_j|)
+    per element, where a conversion to fp16 would give infinities and NaN."""
+    n_kv, n_q, n_qh, kvh = 900, 70, 16, 4
+    g = synth.rng(5, synth.P_MISC, 4242)
+    kf = g.standard_normal((n_kv, kvh, 128)).astype(np.float32)
+    vf = g.standard_normal((n_kv, kvh * 128)).astype(np.float32)
+    for h in range(kvh):     # 100 keys per head, each with one large entry in its own column
+        keys = g.choice(n_kv, size=100, replace=False)
+        cols = g.choice(128, size=100, replace=False)
+        kf[keys, h, cols] = g.choice(np.array([7e4, -7e4, 1e5, -1e5], np.float32), size=100)
+    tiny = g.choice(kf.size, size=300, replace=False)
+    kf.reshape(-1)[tiny] = np.float32(1e-30)
+    kf = kf.reshape(n_kv, kvh * 128)
+    idx = g.choice(vf.size, size=600, replace=False)
+    vf.reshape(-1)[idx] = g.choice(np.array([7e4, -7e4, 1e5, -1e5, 3e9, -3e9], np.float32),
+                                   size=600)
+    k = _bf16_bits(kf).view(np.uint8).reshape(n_kv, -1)
+    v = _bf16_bits(vf).view(np.uint8).reshape(n_kv, -1)
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, 4242), (n_q, n_qh, 128))
+    n_head = n_kv if tiers == "all_hbm" else 333
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    got = _prefill(q, n_kv - n_q, kvh, kd, vd, n_head, kd[n_head:], vd[n_head:], n_kv, True, gpu,
+                   kvt.BF16)
+    ref = oracle.attn_prefill(q, n_kv - n_q, kvh, k, v, n_head, k[n_head:], v[n_head:], n_kv,
+                              oracle.BF16, True, 1 / math.sqrt(128))
+    # the size of the terms each output sums: sum_j p_j |v_j| (the oracle over |V|).  Where
+    # terms of +-3e9 cancel, the output is small but its rounding error scales with the terms
+    v_abs = (v.view(np.uint16) & np.uint16(0x7FFF)).view(np.uint8)
+    mag = oracle.attn_prefill(q, n_kv - n_q, kvh, k, v_abs, n_head, k[n_head:], v_abs[n_head:],
+                              n_kv, oracle.BF16, True, 1 / math.sqrt(128))
+    assert np.isfinite(ref).all()
+    assert np.isfinite(got).all(), "non-finite output"
+    err = np.max(np.abs(got - ref) / np.maximum(1.0, mag))
+    assert err <= TOL, err
+    assert np.abs(ref).max() > 65504, "the case must reach past the fp16 range"
 
 
 @pytest.mark.parametrize("fmt", [kvt.F16, kvt.BF16], ids=FMT_IDS.get)
