@@ -588,27 +588,30 @@ def suite_32_layers(torch, kvt, synth, dev, peaks, reps=3):
 
 def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
     """65,536 pages in random scattered order host -> HBM, page sizes 512 B .. 64 KiB, kernel
-    loads vs the copy engines and vs the runtime's copy calls; plus 2 KiB pages at 8 mod 16
+    loads vs the copy engines and vs the runtime's copy calls; then 4 GiB of 128 KiB .. 1 MiB
+    pages, where the engines close in on the kernel; plus 2 KiB pages at 8 mod 16
     alignment."""
     import numpy as np
-    n = 65536
-    sizes = [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536]
-    host = kvt.HostBuffer(n * sizes[-1] + 64)
+    span = 65536 * 65536
+    sizes = [512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144, 524288, 1048576]
+    host = kvt.HostBuffer(span + 64)
     hb = host.numpy(np.uint8)
     synth.fill_random_bytes(synth.rng(3, synth.P_K), hb[:1 << 28])
     for o in range(1 << 28, hb.size, 1 << 28):
         m = min(1 << 28, hb.size - o)
         hb[o:o + m] = hb[:m]
-    hbm = torch.empty(n * sizes[-1], dtype=torch.uint8, device=dev)
+    n = 65536
+    hbm = torch.empty(span, dtype=torch.uint8, device=dev)
     tb = kvt.HostBuffer(3 * 8 * n)
     tab = tb.numpy(np.uint64, (3, n))
     t = Timer(torch, torch.cuda.current_stream())
     out = {"pages": n, "sweep": []}
     cross = cross_rt = None
     for size in sizes + [2048]:
+        n = min(65536, span // size)
         off = 8 if (size == 2048 and len(out["sweep"]) == len(sizes)) else 0
-        row = {"page_bytes": size, "host_offset_mod16": off}
-        for mode, mname in [(getattr(kvt, c), n) for c, n in COPY_MODES_SPEC]:
+        row = {"page_bytes": size, "pages": n, "host_offset_mod16": off}
+        for mode, mname in [(getattr(kvt, c), nm) for c, nm in COPY_MODES_SPEC]:
             rates = []
             for r in range(reps):
                 src = synth.permutation(synth.rng(3, synth.P_PERM_SRC, r), n)
@@ -629,6 +632,7 @@ def suite_small_pages(torch, kvt, synth, dev, peaks, reps=3):
     out["h2d_crossover_bytes"] = cross
     out["h2d_crossover_bytes_runtime"] = cross_rt
     # CPU baseline: 512-byte pages (all 65,536) and 64 KiB pages (the first 4096 descriptors)
+    n = 65536
     cpu = {}
     for size, m in ((512, n), (65536, 4096)):
         src = synth.permutation(synth.rng(3, synth.P_PERM_SRC, 0), n)[:m]
@@ -722,15 +726,16 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5, compact=False):
         del arena
         return _median(ms)
 
+    st_runtime = stage_ms(kvt.COPY_RUNTIME)
     st_sdma = stage_ms(kvt.COPY_SDMA)
     st_kernel = stage_ms(kvt.COPY_KERNEL)
     a_staged = attn_ms(k_all, v_all, n_head, stage[0], stage[1])
     if compact:
         p_arena = pipe_ms(2 * 16384)
-        st = min(st_sdma, st_kernel)
+        st = min(st_runtime, st_sdma, st_kernel)
         res = {"n_kv": n_kv, "n_head": n_head, "n_q": n_q, "stage_bytes": stage_bytes,
-               "flops": flops, "stage_sdma_ms": round(st_sdma, 4),
-               "stage_kernel_ms": round(st_kernel, 4),
+               "flops": flops, "stage_runtime_ms": round(st_runtime, 4),
+               "stage_sdma_ms": round(st_sdma, 4), "stage_kernel_ms": round(st_kernel, 4),
                "stage_gbs": round(stage_bytes / (st * 1e-3) / GB, 2),
                "attn_staged_ms": round(a_staged, 4),
                "attn_tflops": round(flops / (a_staged * 1e-3) / 1e12, 1),
@@ -748,28 +753,47 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5, compact=False):
     a_hbm = attn_ms(k_all, v_all, n_kv, None, None)
     p_one = pipe_ms(2 * n_tail)          # the whole tail in one bucket
     p_arena = pipe_ms(2 * 16384)         # bounded arena: buckets of 16,384 rows (17.8 MB/plane)
-    st = min(st_sdma, st_kernel)
+    st = min(st_runtime, st_sdma, st_kernel)
     # short chunks (one token = a decode step over the tiered cache): the split-K form, staged
     # (stage + attend) and with the tail read in place, against the single pass -- whether the
     # staging pays below some chunk length, as the page streaming cold weights keeps chunks
     # under 65 tokens zero-copy
     cutoff = {}
-    ws_b = kvt.kvt_attn_prefill_splitk_ws_bytes(1, n_qh, kvh, n_kv)
+    ws_b = max(kvt.kvt_attn_prefill_splitk_ws_bytes(1, n_qh, kvh, n_kv),
+               kvt.kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv))
     ws_sk = torch.empty(max(ws_b, 16), dtype=torch.uint8, device=dev)
-    for nq in (1, 16, 64, 256, 1024):
+    arena_p = torch.empty((2, 2 * 16384, row), dtype=torch.uint8, device=dev)
+    for nq in (1, 16, 64, 256, 512, 1024, 2048):
         qs = q[n_q - nq:]
         outs = out[:nq]
         wb = kvt.kvt_attn_prefill_splitk_ws_bytes(nq, n_qh, kvh, n_kv)
-        assert wb <= ws_sk.numel()
+        wa = kvt.kvt_attn_prefill_auto_ws_bytes(nq, n_qh, kvh, n_kv)
+        assert wb <= ws_sk.numel() and wa <= ws_sk.numel()
+        plan = None
 
         def run(kind):
+            nonlocal plan
             ms = []
             for _ in range(reps):
                 t.start()
+                if kind == "auto":
+                    plan = kvt.kvt_attn_prefill_auto(
+                        qs, nq, n_kv - nq, n_qh, kvh, hd, k_all, v_all, n_head, host.dev,
+                        host.dev + n_tail * row, n_kv, kvt.Q8_0, 1, scale, stage[0], stage[1],
+                        n_tail, ws_sk, wa, outs, copy_stream=copy_stream)
+                    ms.append(t.stop_ms())
+                    continue
+                if kind == "pipelined":
+                    kvt.kvt_attn_prefill_pipelined(
+                        qs, nq, n_kv - nq, n_qh, kvh, hd, k_all, v_all, n_head, host.dev,
+                        host.dev + n_tail * row, n_kv, kvt.Q8_0, 1, scale, arena_p[0],
+                        arena_p[1], arena_p.shape[1], ws_sk, wa, outs, copy_stream=copy_stream)
+                    ms.append(t.stop_ms())
+                    continue
                 if kind == "staged":
-                    kvt.kvt_stage_tail(host.dev, row, 0, n_tail, stage[0], kvt.COPY_SDMA)
+                    kvt.kvt_stage_tail(host.dev, row, 0, n_tail, stage[0], kvt.COPY_AUTO)
                     kvt.kvt_stage_tail(host.dev + n_tail * row, row, 0, n_tail, stage[1],
-                                       kvt.COPY_SDMA)
+                                       kvt.COPY_AUTO)
                     kt_, vt_ = stage[0], stage[1]
                 else:
                     kt_, vt_ = host.dev, host.dev + n_tail * row
@@ -783,10 +807,11 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5, compact=False):
                 ms.append(t.stop_ms())
             return _median(ms)
         cutoff[str(nq)] = {k_: round(run(k_), 3) for k_ in
-                           ("staged", "in_place", "single_pass_in_place")}
+                           ("staged", "in_place", "single_pass_in_place", "pipelined", "auto")}
         cutoff[str(nq)]["splits"] = (wb // kvt.kvt_attn_prefill_state_bytes(nq, n_qh, kvh)
                                      if wb else 1)
-    del ws_sk
+        cutoff[str(nq)]["auto_plan"] = ("in_place", "staged", "pipelined")[plan]
+    del ws_sk, arena_p
     log("prefill staging cutoff", cutoff)
     # an fp16 GEMM probe (hipBLASLt through torch, 8192^3) for the measured MFMA rate
     a = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
@@ -816,7 +841,8 @@ def suite_prefill(torch, kvt, synth, dev, peaks, reps=5, compact=False):
     res = {
         "n_kv": n_kv, "n_head": n_head, "n_q": n_q, "q_heads": n_qh, "kv_heads": kvh,
         "stage_bytes": stage_bytes, "flops": flops,
-        "stage_sdma_ms": round(st_sdma, 4), "stage_kernel_ms": round(st_kernel, 4),
+        "stage_runtime_ms": round(st_runtime, 4), "stage_sdma_ms": round(st_sdma, 4),
+        "stage_kernel_ms": round(st_kernel, 4),
         "stage_gbs": round(stage_bytes / (st * 1e-3) / GB, 2),
         "stage_pct_measured_h2d_peak": round(100 * stage_bytes / (st * 1e-3) / GB / peaks["h2d_sdma_gbs"], 1),
         "attn_staged_ms": round(a_staged, 4),
@@ -1338,8 +1364,9 @@ def run_configs(torch, kvt, synth, dev, peaks, args):
         r = suite_small_pages(torch, kvt, synth, dev, peaks, reps=1)
         row2k = next(x for x in r["sweep"] if x["page_bytes"] == 2048
                      and x["host_offset_mod16"] == 0)
-        return {"workload": "65,536 scattered pages host->HBM, 512 B .. 64 KiB (kernel, DMA "
-                            "engines, runtime copies); 2 KiB pages at the workload's size",
+        return {"workload": "65,536 scattered pages host->HBM, 512 B .. 64 KiB, then 4 GiB of "
+                            "128 KiB .. 1 MiB pages (kernel, DMA engines, runtime copies); "
+                            "2 KiB pages at the workload's size",
                 "metric": "2 KiB-page load GB/s (kernel)", "value": row2k["kernel_gbs"],
                 "unit": "GB/s", "sdma_gbs_2k": row2k["sdma_gbs"],
                 "runtime_gbs_2k": row2k["runtime_gbs"],
@@ -1348,6 +1375,9 @@ def run_configs(torch, kvt, synth, dev, peaks, args):
                 "sweep_kernel_gbs": {str(x["page_bytes"]) + ("@8mod16" if x["host_offset_mod16"]
                                                               else ""): x["kernel_gbs"]
                                      for x in r["sweep"]},
+                "sweep_sdma_gbs": {str(x["page_bytes"]): x["sdma_gbs"] for x in r["sweep"]
+                                   if not x["host_offset_mod16"]},
+                "sdma_engines": kvt.kvt_copy_engines(kvt.H2D),
                 "roofline": _pcie_roofline(row2k["kernel_gbs"], peaks, kernel="copy_small_kernel"),
                 "cpu_baseline": {"value": r["cpu_baseline"]["512B"]["all_threads_gbs"],
                                  "unit": "GB/s", "kind": "oracle",

@@ -12,8 +12,9 @@
 //   * RUNTIME: HIP's copy calls -- hipMemcpyBatchAsync (one submission for the batch), else one
 //     hipMemcpyAsync per descriptor -- which choose the engine per copy themselves: a kernel
 //     trace shows page-sized copies running as the runtime's blit kernel.
-// kvt_stage_tail (llama-T tail staging) is one contiguous range: one hipMemcpyAsync, which the
-// runtime runs on a copy engine at staging sizes, or the same wide-load kernel over one span.
+// kvt_stage_tail (llama-T tail staging) is one contiguous range: one hipMemcpyAsync (AUTO and
+// RUNTIME), which the runtime runs on a copy engine at staging sizes; one engine copy driven
+// through HSA (SDMA, as in kvt_swap_blocks); or the same wide-load kernel over one span.
 #include <dlfcn.h>
 
 #include <algorithm>
@@ -256,7 +257,7 @@ extern "C" int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const u
     bool use_kernel = mode == KVT_COPY_KERNEL ||
                       (mode == KVT_COPY_AUTO && kernel_ok && max_size < g_threshold[dir].load());
     if (mode == KVT_COPY_SDMA)
-        return kvt::engine_copies(src, dst, sizes, n, dir, s);
+        return kvt::engine_copies("kvt_swap_blocks", src, dst, sizes, n, dir, s);
     if (!use_kernel)
         return runtime_copies(src, dst, sizes, n, s);
 
@@ -298,6 +299,8 @@ extern "C" int kvt_stage_tail(const void *plane, int64_t row_bytes, int64_t row_
     hipStream_t s = kvt::as_stream(stream);
     const uint64_t src = reinterpret_cast<uint64_t>(plane) + (uint64_t)row_begin * row_bytes;
     const uint64_t dst = reinterpret_cast<uint64_t>(staging);
+    if (mode == KVT_COPY_SDMA)
+        return kvt::engine_copies("kvt_stage_tail", &src, &dst, &bytes, 1, KVT_H2D, s);
     if (mode != KVT_COPY_KERNEL) {
         KVT_HIP(hipMemcpyAsync(staging, reinterpret_cast<const void *>(src), bytes,
                                hipMemcpyDefault, s));

@@ -1,12 +1,22 @@
-// kvt_engine.hip -- S2 batched swap on the DMA (SDMA) copy engines, driven through HSA.
+// kvt_engine.hip -- S2 batched swap and S7 tail staging on the DMA (SDMA) copy engines,
+// driven through HSA.
 //
 // vLLM-CPU chooses between the copy engines and a kernel that reads host pointers.  Through
 // HIP's copy calls that choice is not ours to make: the runtime picks an engine per copy, and
 // on MI355X a kernel trace shows every page-sized pinned<->HBM copy of a batch
 // (hipMemcpyBatchAsync or hipMemcpyAsync) running as one dispatch of the runtime's blit kernel;
-// only large copies reach the DMA engines.  So the SDMA mode of kvt_swap_blocks drives the
-// engines itself: hsa_amd_memory_async_copy between the GPU agent and a CPU agent is a DMA
-// engine copy, one per run of adjacent descriptors (a run is contiguous on both sides).
+// only large copies reach the DMA engines.  So the SDMA mode drives the engines itself:
+// hsa_amd_memory_async_copy_on_engine between the GPU agent and a CPU agent is a DMA engine
+// copy, one per run of adjacent descriptors (a run is contiguous on both sides), runs longer
+// than 4 MiB cut into 4 MiB pieces.
+//
+// Engines.  MI355X reports 16 engines for each direction between host and device.  One engine
+// takes about 10 us per copy whatever its size (2 KiB and 32 KiB copies alike), while a
+// submission costs the calling thread about 0.4 us, so one engine moves 32 KiB pages at
+// ~2.9 GB/s and the engines, not the thread, set the rate.  Copies therefore go round-robin
+// over every engine the runtime reports available for the direction (32 KiB pages: ~29 GB/s
+// from one thread over 16 engines); several submitting threads gained nothing over that.
+// Descriptors write disjoint ranges, so copies may complete in any order.
 //
 // The mode is synchronous with respect to the calling thread: it drains the caller's stream,
 // submits the copies, waits for them on this thread and returns, so work queued on the stream
@@ -32,10 +42,13 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+constexpr int kMaxEngines = 16;
+
 struct Agents {
     bool probed = false;
     int status = KVT_OK;
     hsa_agent_t gpu{}, cpu{};
+    uint32_t engines[2] = {0, 0};   // available engine masks: [KVT_H2D], [KVT_D2H]
 };
 
 std::mutex g_mu;
@@ -107,6 +120,14 @@ int agents_for(int dev, Agents *out)
             pr.cpu = near;
         a.gpu = pr.gpu;
         a.cpu = pr.cpu;
+        // engines the runtime reports for each direction; none reported: it picks per copy
+        for (int d = 0; d < 2; d++) {
+            uint32_t m = 0;
+            if (hsa_amd_memory_copy_engine_status(d == KVT_H2D ? pr.gpu : pr.cpu,
+                                                  d == KVT_H2D ? pr.cpu : pr.gpu,
+                                                  &m) == HSA_STATUS_SUCCESS)
+                a.engines[d] = m & ((1u << kMaxEngines) - 1);
+        }
         a.status = KVT_OK;
     }
     if (a.status != KVT_OK)
@@ -115,9 +136,20 @@ int agents_for(int dev, Agents *out)
     return KVT_OK;
 }
 
-// The engine-copy operations of one call (see kvt_engine_runs.h).
+// The engine-copy operations of one call (see kvt_engine_runs.h): copies go round-robin over
+// the engines in `engine` (n_engines of them; none: the runtime's own choice per copy).
 struct HsaOps {
     hsa_agent_t dst_agent, src_agent;
+    hsa_amd_sdma_engine_id_t engine[kMaxEngines];
+    int n_engines = 0;
+    int64_t next = 0;
+
+    HsaOps(hsa_agent_t d, hsa_agent_t s, uint32_t mask) : dst_agent(d), src_agent(s)
+    {
+        for (int b = 0; b < kMaxEngines; b++)
+            if (mask & (1u << b))
+                engine[n_engines++] = static_cast<hsa_amd_sdma_engine_id_t>(1u << b);
+    }
     int create(uint64_t *sig)
     {
         hsa_signal_t h;
@@ -127,9 +159,14 @@ struct HsaOps {
     }
     int copy(uint64_t d, uint64_t s, uint64_t len, uint64_t sig)
     {
-        const hsa_status_t st = hsa_amd_memory_async_copy(
-            reinterpret_cast<void *>(d), dst_agent, reinterpret_cast<const void *>(s), src_agent,
-            len, 0, nullptr, hsa_signal_t{sig});
+        void *dp = reinterpret_cast<void *>(d);
+        const void *sp = reinterpret_cast<const void *>(s);
+        const hsa_status_t st =
+            n_engines ? hsa_amd_memory_async_copy_on_engine(dp, dst_agent, sp, src_agent, len, 0,
+                                                            nullptr, hsa_signal_t{sig},
+                                                            engine[next++ % n_engines], false)
+                      : hsa_amd_memory_async_copy(dp, dst_agent, sp, src_agent, len, 0, nullptr,
+                                                  hsa_signal_t{sig});
         return st == HSA_STATUS_SUCCESS ? 0 : (int)st;
     }
     void reset(uint64_t sig) { hsa_signal_store_screlease(hsa_signal_t{sig}, 1); }
@@ -142,7 +179,8 @@ struct HsaOps {
     void destroy(uint64_t sig) { hsa_signal_destroy(hsa_signal_t{sig}); }
 };
 
-constexpr int64_t kSignalWindow = 256;   // copies in flight at most
+constexpr int64_t kSignalWindow = 256;        // copies in flight at most
+constexpr uint64_t kMaxRun = (uint64_t)4 << 20;   // longer runs are cut, to use more engines
 
 }  // namespace
 
@@ -150,15 +188,15 @@ namespace kvt {
 
 // The n descriptor copies on the DMA engines, after everything queued on stream s; returns
 // once they are done (see the file comment).  dir KVT_H2D: src is host memory, dst device
-// memory; KVT_D2H the reverse.
-int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
-                  int32_t dir, hipStream_t s)
+// memory; KVT_D2H the reverse.  fn names the entry point in error messages.
+int engine_copies(const char *fn, const uint64_t *src, const uint64_t *dst,
+                  const uint64_t *sizes, int64_t n, int32_t dir, hipStream_t s)
 {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     KVT_HIP(hipStreamIsCapturing(s, &cs));
     if (cs != hipStreamCaptureStatusNone)
-        return fail(KVT_EUNSUPPORTED, "kvt_swap_blocks: the SDMA mode waits on the host and "
-                                      "cannot be captured in a graph");
+        return fail(KVT_EUNSUPPORTED, "%s: the SDMA mode waits on the host and cannot be "
+                                      "captured in a graph", fn);
     int dev = 0;
     KVT_HIP(hipStreamGetDevice(s, &dev));
     Agents a;
@@ -171,16 +209,37 @@ int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *size
     if (!any)
         return KVT_OK;
     KVT_HIP(hipStreamSynchronize(s));   // the copies come after the stream's earlier work
-    HsaOps ops{dir == KVT_H2D ? a.gpu : a.cpu, dir == KVT_H2D ? a.cpu : a.gpu};
-    const EngineTally t = run_engine_copies(ops, src, dst, sizes, n, kSignalWindow);
+    HsaOps ops(dir == KVT_H2D ? a.gpu : a.cpu, dir == KVT_H2D ? a.cpu : a.gpu,
+               a.engines[dir == KVT_H2D ? KVT_H2D : KVT_D2H]);
+    const EngineTally t = run_engine_copies(ops, src, dst, sizes, n, kSignalWindow, kMaxRun);
     if (t.failed_at == 1)
-        return fail(KVT_EHIP, "kvt_swap_blocks: hsa_signal_create: status %d (no copy submitted)",
+        return fail(KVT_EHIP, "%s: hsa_signal_create: status %d (no copy submitted)", fn,
                     t.status);
     if (t.failed_at == 2)
-        return fail(KVT_EHIP, "kvt_swap_blocks: hsa_amd_memory_async_copy: status %d after %lld "
-                              "of %lld copies", t.status, (long long)t.submitted,
-                    (long long)t.runs);
+        return fail(KVT_EHIP, "%s: engine copy submission: status %d after %lld of %lld copies",
+                    fn, t.status, (long long)t.submitted, (long long)t.runs);
     return KVT_OK;
 }
 
+// Engines the SDMA mode spreads its copies over for direction dir on device dev (0: the
+// runtime picks per copy), or a negative status.
+int engine_count(int dev, int32_t dir)
+{
+    Agents a;
+    const int rc = agents_for(dev, &a);
+    if (rc != KVT_OK)
+        return rc;
+    return __builtin_popcount(a.engines[dir == KVT_H2D ? KVT_H2D : KVT_D2H]);
+}
+
 }  // namespace kvt
+
+// The number of engines the SDMA mode uses on the current device for direction dir.
+extern "C" int kvt_copy_engines(int32_t dir)
+{
+    if (dir != KVT_H2D && dir != KVT_D2H)
+        return kvt::fail(KVT_EINVAL, "kvt_copy_engines: dir=%d", dir);
+    int dev = 0;
+    KVT_HIP(hipGetDevice(&dev));
+    return kvt::engine_count(dev, dir);
+}

@@ -2,7 +2,8 @@
 // HSA calls it drives, so that host code alone can check it.
 //
 // The mode submits one engine copy per run of adjacent descriptors (vLLM-CPU's batched swap,
-// `transfer_async` -> `swap_blocks_batch`).  Every copy gets a completion signal of its own,
+// `transfer_async` -> `swap_blocks_batch`), a long run cut into pieces of at most max_run
+// bytes.  Every copy gets a completion signal of its own,
 // created with value 1, which the engine counts down to 0 when the copy is done: the form the
 // runtime's own copies use, and the one a memory-copy tracer that wraps each copy's signal
 // expects.  A window of at most `window` signals is reused: before copy i takes the signal of
@@ -30,16 +31,18 @@ namespace kvt {
 struct EngineTally {
     int status = 0;            // 0, or the first failing create / copy status
     int failed_at = 0;         // 0 none, 1 signal creation, 2 copy submission
-    int64_t runs = 0;          // copies the descriptors call for
+    int64_t runs = 0;          // copies the descriptors call for (runs, or their pieces)
     int64_t created = 0, submitted = 0, waited = 0, destroyed = 0;
 };
 
 // A run: descriptors i..j-1 with every next one starting where the previous ended, on both
-// sides.  Zero-size descriptors are skipped and end no run.
+// sides.  Zero-size descriptors are skipped and end no run.  Each run goes to f in pieces of at
+// most max_run bytes (0: whole), so that one long range can be spread over several engines.
 template <class F>
 void for_each_engine_run(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes,
-                         int64_t n, F &&f)
+                         int64_t n, uint64_t max_run, F &&f)
 {
+    const uint64_t cut = max_run ? max_run : ~(uint64_t)0;
     int64_t i = 0;
     while (i < n) {
         if (!sizes[i]) {
@@ -56,17 +59,19 @@ void for_each_engine_run(const uint64_t *src, const uint64_t *dst, const uint64_
                 break;
             len += sizes[k];
         }
-        f(s0, d0, len);
+        for (uint64_t off = 0; off < len; off += cut)
+            f(s0 + off, d0 + off, len - off < cut ? len - off : cut);
         i = k;
     }
 }
 
 template <class Ops>
 EngineTally run_engine_copies(Ops &ops, const uint64_t *src, const uint64_t *dst,
-                              const uint64_t *sizes, int64_t n, int64_t window)
+                              const uint64_t *sizes, int64_t n, int64_t window, uint64_t max_run)
 {
     EngineTally t;
-    for_each_engine_run(src, dst, sizes, n, [&](uint64_t, uint64_t, uint64_t) { t.runs++; });
+    for_each_engine_run(src, dst, sizes, n, max_run,
+                        [&](uint64_t, uint64_t, uint64_t) { t.runs++; });
     if (!t.runs)
         return t;
     const int64_t w = t.runs < window ? t.runs : (window > 0 ? window : 1);
@@ -81,7 +86,8 @@ EngineTally run_engine_copies(Ops &ops, const uint64_t *src, const uint64_t *dst
         }
     }
     if (!t.status) {
-        for_each_engine_run(src, dst, sizes, n, [&](uint64_t s, uint64_t d, uint64_t len) {
+        for_each_engine_run(src, dst, sizes, n, max_run, [&](uint64_t s, uint64_t d,
+                                                             uint64_t len) {
             if (t.status)
                 return;
             const size_t slot = (size_t)(t.submitted % w);

@@ -37,11 +37,13 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
-// kvt_swap_blocks' SDMA mode: n descriptor copies on the DMA engines after the work queued on
-// stream s, waited for on the calling thread (kvt_engine.hip).  dir KVT_H2D: src host, dst
-// device; KVT_D2H the reverse.
-int engine_copies(const uint64_t *src, const uint64_t *dst, const uint64_t *sizes, int64_t n,
-                  int32_t dir, hipStream_t s);
+// The SDMA copy mode: n descriptor copies on the DMA engines after the work queued on stream
+// s, waited for on the calling thread (kvt_engine.hip).  dir KVT_H2D: src host, dst device;
+// KVT_D2H the reverse.  fn names the entry point in error messages.
+int engine_copies(const char *fn, const uint64_t *src, const uint64_t *dst,
+                  const uint64_t *sizes, int64_t n, int32_t dir, hipStream_t s);
+// Engines that mode spreads its copies over on device dev (0: the runtime picks per copy).
+int engine_count(int dev, int32_t dir);
 
 }  // namespace kvt
 

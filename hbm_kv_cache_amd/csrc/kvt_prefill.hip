@@ -1047,3 +1047,120 @@ extern "C" int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0
                             arena_k, arena_v, arena_rows, staged_rows, nx, state, state_bytes_,
                             out, stream, copy_stream);
 }
+
+namespace {
+
+// The auto plan's time model: the host link at the rate contiguous staging copies reach on
+// MI355X (56 GB/s), and the prefill kernel's attention rate per cache format when its
+// workgroups fill the chip (measured over a 180,000-key cache: q8_0 0.80, fp16 0.73, bf16 0.50
+// PFLOP/s).
+constexpr double kLinkBytesPerUs = 56.0e3;
+
+double attn_flop_per_us(int32_t fmt)
+{
+    return fmt == KVT_Q8_0 ? 8.0e8 : fmt == KVT_F16 ? 7.3e8 : 5.0e8;
+}
+
+// (query, key) pairs the attention visits: row t sees min(n_kv, q_pos0 + t + 1) keys when
+// causal, all n_kv otherwise.
+double key_pairs(int64_t n_q, int64_t q_pos0, int64_t n_kv, int32_t causal)
+{
+    if (!causal)
+        return (double)n_q * (double)n_kv;
+    int64_t lin = n_kv - q_pos0;   // rows t < lin see q_pos0 + t + 1 keys, the rest n_kv
+    lin = lin < 0 ? 0 : (lin > n_q ? n_q : lin);
+    const double l = (double)lin;
+    return l * (double)(q_pos0 + 1) + l * (l - 1) / 2 + (double)(n_q - lin) * (double)n_kv;
+}
+
+}  // namespace
+
+// S7+S8 with the stage-or-read-in-place choice made from the chunk's shape.
+extern "C" int kvt_attn_prefill_plan(int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh,
+                                     int64_t n_head, int64_t n_kv, int32_t kv_format,
+                                     int32_t causal, int64_t arena_rows, int32_t two_streams)
+{
+    if (kv_format != KVT_Q8_0 && kv_format != KVT_F16 && kv_format != KVT_BF16)
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_prefill_plan: kv_format=%d", kv_format);
+    if (kvh < 1 || n_qh < 1 || n_qh % kvh)
+        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill_plan: n_qh=%d kvh=%d", n_qh, kvh);
+    const int group = n_qh / kvh;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return kvt::fail(KVT_EUNSUPPORTED, "kvt_attn_prefill_plan: group %d", group);
+    if (n_q < 0 || q_pos0 < 0 || n_head < 0 || n_head > n_kv || arena_rows < 0)
+        return kvt::fail(KVT_EINVAL, "kvt_attn_prefill_plan: n_q=%lld q_pos0=%lld n_head=%lld "
+                                     "n_kv=%lld arena_rows=%lld", (long long)n_q,
+                         (long long)q_pos0, (long long)n_head, (long long)n_kv,
+                         (long long)arena_rows);
+    const int64_t tail = n_kv - n_head;
+    if (n_q == 0 || tail == 0)
+        return KVT_PREFILL_IN_PLACE;   // nothing crosses the link
+    const int qpw = 32 * (kWaves / group);
+    const int64_t q_tiles = (n_q + qpw - 1) / qpw;
+    int n_split = 1, tps = 0;
+    split_plan(q_tiles * kvh, (n_kv + kKT - 1) / kKT, n_split, tps);
+    if (n_split == 1)   // the chunk fills the chip: hide the copies behind the attention
+        return two_streams && arena_rows / 2 / kKT * kKT >= kKT ? KVT_PREFILL_PIPELINED
+                                                                 : KVT_PREFILL_IN_PLACE;
+    // a short chunk: in place, its few workgroups wait on scattered head slices across the
+    // link; staged, the tail crosses once, contiguously, before an attention that is short
+    const double row_bytes = (double)kvh * head_bytes(kv_format);
+    const double stage_us = 2.0 * (double)tail * row_bytes / kLinkBytesPerUs;
+    const double attn_us =
+        4.0 * kHd * n_qh * key_pairs(n_q, q_pos0, n_kv, causal) / attn_flop_per_us(kv_format);
+    return arena_rows >= tail && attn_us < stage_us ? KVT_PREFILL_STAGED : KVT_PREFILL_IN_PLACE;
+}
+
+extern "C" size_t kvt_attn_prefill_auto_ws_bytes(int64_t n_q, int32_t n_qh, int32_t kvh,
+                                                 int64_t n_kv)
+{
+    const size_t a = kvt_attn_prefill_splitk_ws_bytes(n_q, n_qh, kvh, n_kv);
+    const size_t b = kvt_attn_prefill_state_bytes(n_q, n_qh, kvh);
+    return a > b ? a : b;
+}
+
+extern "C" int kvt_attn_prefill_auto(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh,
+                                     int32_t kvh, int32_t hd, const void *k_head,
+                                     const void *v_head, int64_t n_head, const void *k_host,
+                                     const void *v_host, int64_t n_kv, int32_t kv_format,
+                                     int32_t causal, float scale, void *arena_k, void *arena_v,
+                                     int64_t arena_rows, void *ws, size_t ws_bytes, float *out,
+                                     int32_t *plan, void *stream, void *copy_stream)
+{
+    int group = 0;
+    int64_t q_tiles = 0;
+    int rc = check_prefill("kvt_attn_prefill_auto", q, n_q, q_pos0, n_qh, kvh, hd, k_head,
+                           v_head, n_head, k_host, v_host, n_kv, kv_format, scale, out, group,
+                           q_tiles);
+    if (rc != KVT_OK)
+        return rc;
+    const bool arena = arena_k && arena_v;
+    const bool two = kvt::as_stream(stream) != kvt::as_stream(copy_stream);
+    const int p = kvt_attn_prefill_plan(n_q, q_pos0, n_qh, kvh, n_head, n_kv, kv_format, causal,
+                                        arena ? arena_rows : 0, two ? 1 : 0);
+    if (p < 0)
+        return p;
+    if (plan)
+        *plan = p;
+    if (n_q == 0)
+        return KVT_OK;
+    const int64_t tail = n_kv - n_head;
+    if (p == KVT_PREFILL_PIPELINED)
+        return kvt_attn_prefill_pipelined(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head,
+                                          k_host, v_host, n_kv, kv_format, causal, scale,
+                                          arena_k, arena_v, arena_rows, ws, ws_bytes, out, stream,
+                                          copy_stream);
+    const void *kt = k_host, *vt = v_host;
+    if (p == KVT_PREFILL_STAGED) {
+        const int64_t row_bytes = (int64_t)kvh * head_bytes(kv_format);
+        rc = kvt_stage_tail(k_host, row_bytes, 0, tail, arena_k, KVT_COPY_AUTO, stream);
+        if (rc == KVT_OK)
+            rc = kvt_stage_tail(v_host, row_bytes, 0, tail, arena_v, KVT_COPY_AUTO, stream);
+        if (rc != KVT_OK)
+            return rc;
+        kt = arena_k;
+        vt = arena_v;
+    }
+    return kvt_attn_prefill_splitk(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, kt, vt,
+                                   n_kv, kv_format, causal, scale, ws, ws_bytes, out, stream);
+}

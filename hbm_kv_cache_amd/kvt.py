@@ -21,6 +21,7 @@ H2D, D2H = 0, 1
 COPY_AUTO, COPY_KERNEL, COPY_SDMA, COPY_RUNTIME = 0, 1, 2, 3
 F16, BF16, Q8_0 = 1, 2, 3
 HOST_COHERENT, HOST_NONCOHERENT, HOST_WRITECOMBINED = 0, 1, 2
+PREFILL_IN_PLACE, PREFILL_STAGED, PREFILL_PIPELINED = 0, 1, 2
 OP_NONE_NEEDED, OP_INDEX_TOPK, OP_ATTN_DECODE, OP_SPARSE_ROWS, OP_PREFILL_STATE = 0, 1, 2, 3, 4
 
 _P = c_void_p
@@ -88,6 +89,14 @@ _SIGNATURES = {
     "kvt_attn_prefill_splitk": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P,
                                         c_int64, _P, _P, c_int64, c_int32, c_int32, c_float, _P,
                                         c_size_t, _P, _P]),
+    "kvt_copy_engines": (c_int, [c_int32]),
+    "kvt_attn_prefill_plan": (c_int, [c_int64, c_int64, c_int32, c_int32, c_int64, c_int64,
+                                      c_int32, c_int32, c_int64, c_int32]),
+    "kvt_attn_prefill_auto_ws_bytes": (c_size_t, [c_int64, c_int32, c_int32, c_int64]),
+    "kvt_attn_prefill_auto": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P,
+                                      c_int64, _P, _P, c_int64, c_int32, c_int32, c_float, _P,
+                                      _P, c_int64, _P, c_size_t, _P, ctypes.POINTER(c_int32),
+                                      _P, _P]),
     "kvt_paged_write": (c_int, [_P, _P, _P, c_int32, c_int32, c_int32, _P, _P, c_int32, c_int32,
                                 c_int64, _P]),
     "kvt_copy_page": (c_int, [_P, _P, _P, c_int32, c_int64, c_int64, c_int32, c_int32, _P, _P,
@@ -464,6 +473,46 @@ def kvt_attn_prefill_splitk(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_hea
         _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
         int(n_head), _ptr(k_tail), _ptr(v_tail), int(n_kv), int(kv_format), int(bool(causal)),
         float(scale), _ptr(ws), int(ws_bytes), _ptr(out), _stream(stream)))
+
+
+def kvt_copy_engines(direction) -> int:
+    """DMA engines KVT_COPY_SDMA spreads its copies over on the current device (0: the runtime
+    picks per copy)."""
+    rc = load().kvt_copy_engines(int(direction))
+    if rc < 0:
+        _check("kvt_copy_engines", rc)
+    return int(rc)
+
+
+def kvt_attn_prefill_plan(n_q, q_pos0, n_qh, kvh, n_head, n_kv, kv_format, causal, arena_rows,
+                          two_streams) -> int:
+    """The plan kvt_attn_prefill_auto takes (PREFILL_*); host only."""
+    rc = load().kvt_attn_prefill_plan(int(n_q), int(q_pos0), int(n_qh), int(kvh), int(n_head),
+                                      int(n_kv), int(kv_format), int(bool(causal)),
+                                      int(arena_rows), int(bool(two_streams)))
+    if rc < 0:
+        _check("kvt_attn_prefill_plan", rc)
+    return int(rc)
+
+
+def kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv) -> int:
+    return int(load().kvt_attn_prefill_auto_ws_bytes(int(n_q), int(n_qh), int(kvh), int(n_kv)))
+
+
+def kvt_attn_prefill_auto(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_host, v_host,
+                          n_kv, kv_format, causal, scale, arena_k, arena_v, arena_rows, ws,
+                          ws_bytes, out, stream=None, copy_stream=None) -> int:
+    """Runs the plan kvt_attn_prefill_plan picks and returns it.  copy_stream None: no second
+    stream, so no pipelining."""
+    plan = c_int32(-1)
+    s = _stream(stream)
+    cs = s if copy_stream is None else _stream(copy_stream)
+    _check("kvt_attn_prefill_auto", load().kvt_attn_prefill_auto(
+        _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
+        int(n_head), _ptr(k_host), _ptr(v_host), int(n_kv), int(kv_format), int(bool(causal)),
+        float(scale), _ptr(arena_k), _ptr(arena_v), int(arena_rows), _ptr(ws), int(ws_bytes),
+        _ptr(out), ctypes.byref(plan), s, cs))
+    return int(plan.value)
 
 
 def kvt_pool_rebuild(raw_k, pooled, dim, bsz, seq, cache_seqlens, block_table, pages_per_seq,

@@ -19,6 +19,7 @@
  *   kvt_attn_prefill_range      the same attention as resumable passes over key ranges
  *   kvt_attn_prefill_pipelined  tail staging in arena buckets overlapped with the attention
  *   kvt_attn_prefill_chain      the same over a chain of layers, prefetching the next layer
+ *   kvt_attn_prefill_auto       stage the tail, pipeline it or read it in place, by a time model
  *   kvt_worker_*         an ordered, event-timed asynchronous transfer queue around the swap
  *   kvt_paged_write      append new K/V (and raw key) rows into paged planes via a block table
  *   kvt_copy_page        duplicate a page's first rows (host planes on the CPU, pooled on device)
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 14
+#define KVT_ABI_VERSION 15
 
 /* status codes */
 #define KVT_OK 0
@@ -76,9 +77,10 @@ extern "C" {
 #define KVT_COPY_AUTO 0    /* the kernel when sizes are multiples of 8 and pages are below the
                              threshold (default: no limit), else RUNTIME */
 #define KVT_COPY_KERNEL 1  /* wavefront loads/stores through the host mapping */
-#define KVT_COPY_SDMA 2    /* the DMA copy engines, one engine copy per run of adjacent
-                             descriptors, driven through HSA; waits on the calling thread
-                             (kvt_swap_blocks; see there) */
+#define KVT_COPY_SDMA 2    /* the DMA copy engines driven through HSA, one engine copy per
+                             run of adjacent descriptors (<= 4 MiB pieces), round-robin over
+                             the engines; waits on the calling thread (kvt_swap_blocks and
+                             kvt_stage_tail; see kvt_swap_blocks) */
 #define KVT_COPY_RUNTIME 3 /* HIP's copy calls (hipMemcpyBatchAsync, else hipMemcpyAsync per
                              descriptor); the runtime picks the engine per copy and serves
                              page-sized copies with its blit kernel */
@@ -140,7 +142,8 @@ int64_t kvt_chunks_consumed(int64_t n, int32_t skip, int32_t bpc);
  *   aligned ones an 8-byte path, anything else a byte path.
  *   SDMA is synchronous with respect to the calling thread: the call waits for the work
  *   already queued on the stream, submits the engine copies (descriptors that continue the
- *   previous one on both sides go as one copy), waits for them and returns, so work queued
+ *   previous one on both sides go as one copy, cut into pieces of at most 4 MiB), round-robin
+ *   over the engines kvt_copy_engines(dir) counts, waits for them and returns, so work queued
  *   afterwards sees them.  Host addresses must be pinned memory from kvt_host_alloc (or
  *   hipHostMalloc).  Not allowed while the stream is being captured into a graph
  *   (KVT_EUNSUPPORTED).  Every engine copy has a completion signal of its own (value 1), at
@@ -153,6 +156,10 @@ int kvt_swap_blocks(const uint64_t *src, const uint64_t *dst, const uint64_t *si
                     int32_t dir, int32_t mode, void *stream);
 /* AUTO switches to RUNTIME at pages >= threshold bytes (per direction); returns the old value. */
 uint64_t kvt_set_copy_threshold(int32_t dir, uint64_t bytes);
+/* The number of DMA engines KVT_COPY_SDMA spreads its copies over on the current device for
+ * direction dir (those the runtime reports available; 0: none reported, the runtime then
+ * picks an engine per copy), or a negative status. */
+int kvt_copy_engines(int32_t dir);
 
 /* ----------------------------------------------------------------------------------------
  * S3+S4  index scoring and top-k selection.  [QSA-KVO] CacheLayer_qsa_offload docstring and
@@ -217,8 +224,10 @@ int kvt_gather_blocks(const void *k_plane, const void *v_plane, int64_t n_blocks
  * used host rows are copied into a VRAM staging buffer once per op, and the op reads that.
  *   staging[(r - row_begin)*row_bytes ...] = plane[r*row_bytes ...]  for r in [row_begin, row_end)
  *   plane: device pointer (host-mapped), staging: device (HBM); mode KVT_COPY_*: KERNEL is
- *   the wide-load kernel over one span; AUTO, SDMA and RUNTIME are one hipMemcpyAsync, which
- *   the runtime runs on a copy engine at staging sizes (and which graph capture records).
+ *   the wide-load kernel over one span; AUTO and RUNTIME are one hipMemcpyAsync, which the
+ *   runtime runs on a copy engine at staging sizes (and which graph capture records); SDMA
+ *   is the engine mode of kvt_swap_blocks over the one range (4 MiB pieces round-robin over
+ *   the engines, synchronous with respect to the calling thread, not capturable).
  * ---------------------------------------------------------------------------------------- */
 int kvt_stage_tail(const void *plane, int64_t row_bytes, int64_t row_begin, int64_t row_end,
                    void *staging, int32_t mode, void *stream);
@@ -346,9 +355,11 @@ int kvt_sparse_attend_rows_auto(const void *q, int32_t rows, int32_t n_qh, int32
  *          (KVT_Q8_0: hd/32 blocks of 34 bytes per head, head-major)
  *   causal nonzero: row t sees keys j <= q_pos0 + t (j < n_kv); zero: all n_kv keys
  *   out    device fp32 [n_q][n_qh][hd]
- *   kv_format KVT_Q8_0, KVT_F16 or KVT_BF16.  Products run on fp16 MFMA: q8_0 values are
- *          dequantised to fp16 (one rounding), fp16 values are used as stored, bf16 values are
- *          converted to fp16 (exact for magnitudes in [2^-17, 65504]; larger ones overflow).
+ *   kv_format KVT_Q8_0, KVT_F16 or KVT_BF16.  q8_0 values are dequantised to fp16 (one
+ *          rounding) and fp16 values used as stored, on fp16 MFMA.  bf16 values are used as
+ *          stored, on bf16 MFMA, over their whole range: the fp16 query is split into two
+ *          bf16 parts whose sum is exact, and the fp32 probabilities into two bf16 parts
+ *          (16 significant bits), so each product is taken twice (about 1.6x the time).
  * Limits: hd == 128, n_qh/kvh in {1, 2, 4, 8}, scale > 0; q and out 16-byte aligned,
  * K/V pointers 8-byte aligned.  Deterministic: the same inputs give the same bits, however
  * the rows are split between head and tail.
@@ -459,6 +470,53 @@ int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0, int32_t n
                            void *next_arena_k, void *next_arena_v, int64_t next_arena_rows,
                            void *state, size_t state_bytes, float *out, void *stream,
                            void *copy_stream);
+
+/* ----------------------------------------------------------------------------------------
+ * S7+S8 with the choice made by the library.  [exl3-DMA] decides per chunk whether host
+ * memory is read in place or copied over first, by the chunk's token count (its minimum-token
+ * rule for the DMA path); [llama-T] stages the tail once per op.  For attention over a tiered
+ * cache the deciding quantity is time, not tokens: a short chunk has few workgroups, which
+ * wait on scattered head slices across the link when reading in place, while the attention
+ * itself is short, so copying the tail first (contiguously, at the link rate) pays; a long
+ * chunk hides in-place reads or bucket copies behind its attention.
+ *
+ * kvt_attn_prefill_plan (host only, no device work) returns the plan, or a negative status:
+ *   KVT_PREFILL_IN_PLACE   the tail is read where it lies (through the host mapping)
+ *   KVT_PREFILL_STAGED     the whole tail is first copied into the arena (kvt_stage_tail,
+ *                          mode AUTO, on `stream`), then attended from HBM
+ *   KVT_PREFILL_PIPELINED  kvt_attn_prefill_pipelined over the arena
+ * Rule.  Let s be the number of key splits kvt_attn_prefill_splitk takes for (n_q, n_qh, kvh,
+ * n_kv).  No tail rows, or n_q == 0: IN_PLACE.  s == 1 (the chunk's own workgroups fill the
+ * chip): PIPELINED when two_streams is nonzero and arena_rows >= 128, else IN_PLACE.  s > 1:
+ * STAGED when arena_rows >= n_kv - n_head and the modelled attention time is below the
+ * modelled staging time, else IN_PLACE; both through the split-K form.  The model:
+ * staging 2*(n_kv - n_head)*row_bytes at 56 GB/s; attention 4*hd*n_qh*pairs flop at 0.80
+ * (q8_0), 0.73 (fp16) or 0.50 (bf16) PFLOP/s, pairs being the (query, key) pairs visited
+ * (causal: row t sees min(n_kv, q_pos0 + t + 1) keys).
+ *
+ * kvt_attn_prefill_auto: computes the plan (two_streams = stream and copy_stream differ;
+ * arena_rows counts as 0 when arena_k or arena_v is NULL), writes it to *plan (optional,
+ * host) and runs it.  Arguments as kvt_attn_prefill_pipelined, with ws (device,
+ * kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv) bytes, 4-byte aligned) serving as the
+ * split-K workspace or the pipelined state; arena_k / arena_v may be NULL (no staging).
+ * Output: with s == 1 it equals kvt_attn_prefill's bits, with s > 1 kvt_attn_prefill_splitk's,
+ * whichever plan is taken and however the rows are split between head and tail.  A PIPELINED
+ * plan carries kvt_attn_prefill_pipelined's thread rules (one stream per thread; it ends a
+ * pending chain prefetch).  Limits: as kvt_attn_prefill.
+ * ---------------------------------------------------------------------------------------- */
+#define KVT_PREFILL_IN_PLACE 0
+#define KVT_PREFILL_STAGED 1
+#define KVT_PREFILL_PIPELINED 2
+int kvt_attn_prefill_plan(int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh, int64_t n_head,
+                          int64_t n_kv, int32_t kv_format, int32_t causal, int64_t arena_rows,
+                          int32_t two_streams);
+size_t kvt_attn_prefill_auto_ws_bytes(int64_t n_q, int32_t n_qh, int32_t kvh, int64_t n_kv);
+int kvt_attn_prefill_auto(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh,
+                          int32_t hd, const void *k_head, const void *v_head, int64_t n_head,
+                          const void *k_host, const void *v_host, int64_t n_kv,
+                          int32_t kv_format, int32_t causal, float scale, void *arena_k,
+                          void *arena_v, int64_t arena_rows, void *ws, size_t ws_bytes,
+                          float *out, int32_t *plan, void *stream, void *copy_stream);
 
 /* ----------------------------------------------------------------------------------------
  * Transfer worker.  [vLLM-CPU] SingleDirectionOffloadingHandler: transfer_async,

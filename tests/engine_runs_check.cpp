@@ -1,7 +1,7 @@
 // Host-only driver for the engine-copy bookkeeping (kvt_engine_runs.h) with fake signal and
 // copy operations.  Built and run by tests/test_engine_bookkeeping.py; no HIP, no HSA, no GPU.
 //
-// stdin:  n window fail_create_at fail_copy_at        (-1 = never fail)
+// stdin:  n window fail_create_at fail_copy_at max_run   (-1 = never fail; max_run 0 = whole)
 //         n lines "src dst size"
 // stdout: "T status failed_at runs created submitted waited destroyed"
 //         one "C dst src len" line per submitted copy, in submission order
@@ -108,7 +108,8 @@ struct FakeOps {
 int main()
 {
     long long n = 0, window = 0, fc = -1, fp = -1;
-    if (scanf("%lld %lld %lld %lld", &n, &window, &fc, &fp) != 4)
+    unsigned long long max_run = 0;
+    if (scanf("%lld %lld %lld %lld %llu", &n, &window, &fc, &fp, &max_run) != 5)
         return 2;
     std::vector<uint64_t> src(n), dst(n), sz(n);
     for (long long i = 0; i < n; i++) {
@@ -123,7 +124,7 @@ int main()
     ops.fail_create_at = fc;
     ops.fail_copy_at = fp;
     const kvt::EngineTally t = kvt::run_engine_copies(ops, src.data(), dst.data(), sz.data(), n,
-                                                      window);
+                                                      window, max_run);
     for (auto &kv : ops.sigs)
         if (kv.second.alive)
             ops.bad("signal left alive");

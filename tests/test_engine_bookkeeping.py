@@ -1,8 +1,9 @@
 """CPU-only checks of the engine (SDMA) mode's bookkeeping, with the HSA calls replaced by fakes.
 
-kvt_swap_blocks' engine mode submits one DMA-engine copy per run of adjacent descriptors, each
-with a completion signal of its own (value 1), at most `window` in flight, waited for oldest
-first; every signal is destroyed at the end.  tests/engine_runs_check.cpp drives that code
+The engine (SDMA) mode of kvt_swap_blocks and kvt_stage_tail submits one DMA-engine copy per
+run of adjacent descriptors (a long run cut into pieces of at most max_run bytes), each with a
+completion signal of its own (value 1), at most `window` in flight, waited for oldest first;
+every signal is destroyed at the end.  tests/engine_runs_check.cpp drives that code
 (hbm_kv_cache_amd/csrc/kvt_engine_runs.h, compiled with g++) against fake operations that
 report any rule broken: a copy given a signal whose value is not 1, a wait on a signal with
 no copy in flight (which would never return on an engine), a reset or destroy while a copy
@@ -30,8 +31,8 @@ def driver(tmp_path_factory):
     return exe
 
 
-def _run(exe, src, dst, sizes, window, fail_create=-1, fail_copy=-1):
-    lines = [f"{len(src)} {window} {fail_create} {fail_copy}"]
+def _run(exe, src, dst, sizes, window, fail_create=-1, fail_copy=-1, max_run=0):
+    lines = [f"{len(src)} {window} {fail_create} {fail_copy} {max_run}"]
     lines += [f"{int(a)} {int(b)} {int(c)}" for a, b, c in zip(src, dst, sizes)]
     out = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True,
                          check=True).stdout.splitlines()
@@ -130,3 +131,29 @@ def test_engine_bookkeeping_signal_creation_fails(driver, fail_create):
     assert tally["status"] == 7 and tally["failed_at"] == 1
     assert tally["created"] == tally["destroyed"] == fail_create
     assert tally["submitted"] == tally["waited"] == 0
+
+
+@pytest.mark.parametrize("sizes,max_run,pieces", [
+    ([10 << 20], 4 << 20, [4 << 20, 4 << 20, 2 << 20]),     # one range cut in three
+    ([4 << 20], 4 << 20, [4 << 20]),                         # exactly one piece
+    ([3 << 20, 0, 3 << 20], 4 << 20, [4 << 20, 2 << 20]),    # an adjacent run, then cut
+    ([1000, 24], 512, [512, 512]),                           # the cut ignores descriptor ends
+    ([10 << 20], 0, [10 << 20]),                             # 0: runs stay whole
+])
+def test_engine_runs_cut_into_pieces(driver, sizes, max_run, pieces):
+    """Runs longer than max_run go as consecutive pieces of max_run bytes and a remainder; the
+    pieces cover the run exactly, in order, and equal the oracle's copy."""
+    off = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
+    dst_off = off + np.uint64(64)
+    tally, copies, bad = _run(driver, off, dst_off, np.array(sizes, np.uint64), 256,
+                              max_run=max_run)
+    assert bad == [] and tally["status"] == 0
+    assert [c[2] for c in copies] == pieces
+    pos = 0
+    for d, s_, ln in copies:
+        assert s_ == pos and d == pos + 64
+        pos += ln
+    total = int(sum(sizes)) + 64
+    mem = synth.random_bytes(synth.rng(0, synth.P_K, len(sizes)), total)
+    assert np.array_equal(_apply(copies, mem, total),
+                          _oracle(off, dst_off, np.array(sizes, np.uint64), mem, total))

@@ -709,3 +709,85 @@ def test_prefill_splitk_decode_token_at_full_geometry(gpu):
     assert np.max(np.abs(got - ref)) <= TOL
     del ht
     host.free()
+
+
+@pytest.mark.parametrize("n_q,n_head,arena_rows,two_streams,plan", [
+    (1, 3000, 5192, False, kvt.PREFILL_STAGED),         # decode token: the tail is staged
+    (1, 3000, 5191, True, kvt.PREFILL_IN_PLACE),        # the arena is one row short
+    (7, 3000, 0, False, kvt.PREFILL_IN_PLACE),          # no arena at all
+    (1024, 7000, 8192, True, kvt.PREFILL_IN_PLACE),     # 2 splits; attention outlasts staging
+    (1024, 3000, 8192, False, kvt.PREFILL_STAGED),      # 2 splits; staging is longer
+    (2048, 3000, 4096, True, kvt.PREFILL_PIPELINED),    # one split: buckets overlapped
+    (2048, 3000, 4096, False, kvt.PREFILL_IN_PLACE),    # one split, one stream
+    (300, 8192, 4096, True, kvt.PREFILL_IN_PLACE),      # all in HBM
+])
+def test_prefill_auto_plans_bit_identical(gpu, n_q, n_head, arena_rows, two_streams, plan):
+    """kvt_attn_prefill_auto takes the plan kvt_attn_prefill_plan names and gives the bits of
+    the split-K form over the all-HBM cache (the single pass when one split is taken), on two
+    calls in a row."""
+    n_kv, n_qh, kvh = 8192, 32, 8
+    k, v = _cache(n_kv, kvh, 8192 + n_q)
+    row = k.shape[1]
+    q_np = synth.f16_normal(synth.rng(5, synth.P_Q, 8192 + n_q), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    ref, _ = _splitk(q_np, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    assert kvt.kvt_attn_prefill_plan(n_q, q_pos0, n_qh, kvh, n_head, n_kv, kvt.Q8_0, True,
+                                     arena_rows, two_streams) == plan
+    n_tail = n_kv - n_head
+    host = kvt.HostBuffer(max(2 * n_tail * row, 16))
+    if n_tail:
+        ht = host.numpy(np.uint8, (2, n_tail, row))
+        ht[0], ht[1] = k[n_head:], v[n_head:]
+        del ht
+    q = torch.from_numpy(q_np.view(np.int16)).to(gpu)
+    wb = kvt.kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=gpu)
+    arena = torch.full((2, max(arena_rows, 1), row), 0xA5, dtype=torch.uint8, device=gpu)
+    copy_stream = torch.cuda.Stream() if two_streams else None
+    for _ in range(2):
+        out = torch.full((n_q, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
+        got_plan = kvt.kvt_attn_prefill_auto(
+            q, n_q, q_pos0, n_qh, kvh, 128, kd, vd, n_head, host.dev if n_tail else None,
+            host.dev + n_tail * row if n_tail else None, n_kv, kvt.Q8_0, True,
+            1 / math.sqrt(128), arena[0] if arena_rows else None,
+            arena[1] if arena_rows else None, arena_rows, ws, wb, out, copy_stream=copy_stream)
+        torch.cuda.synchronize()
+        assert got_plan == plan
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    host.free()
+
+
+def test_prefill_auto_staged_decode_token_matches_oracle(gpu):
+    """The staged plan for one decode token, against the fp64 oracle, and the argument checks
+    (workspace too small)."""
+    n_kv, n_head, n_qh, kvh = 6000, 2500, 32, 8
+    k, v = _cache(n_kv, kvh, 6001)
+    row = k.shape[1]
+    q_np = synth.f16_normal(synth.rng(5, synth.P_Q, 6001), (1, n_qh, 128))
+    kd, vd = _dev(k[:n_head], gpu), _dev(v[:n_head], gpu)
+    n_tail = n_kv - n_head
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    q = torch.from_numpy(q_np.view(np.int16)).to(gpu)
+    wb = kvt.kvt_attn_prefill_auto_ws_bytes(1, n_qh, kvh, n_kv)
+    ws = torch.empty(wb, dtype=torch.uint8, device=gpu)
+    arena = torch.empty((2, n_tail, row), dtype=torch.uint8, device=gpu)
+    out = torch.full((1, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
+    plan = kvt.kvt_attn_prefill_auto(q, 1, n_kv - 1, n_qh, kvh, 128, kd, vd, n_head, host.dev,
+                                     host.dev + n_tail * row, n_kv, kvt.Q8_0, True,
+                                     1 / math.sqrt(128), arena[0], arena[1], n_tail, ws, wb, out)
+    torch.cuda.synchronize()
+    assert plan == kvt.PREFILL_STAGED
+    assert np.array_equal(arena[0].cpu().numpy(), k[n_head:])
+    ref = oracle.attn_prefill(q_np, n_kv - 1, kvh, k, v, n_head, k[n_head:], v[n_head:], n_kv,
+                              oracle.Q8_0, True, 1 / math.sqrt(128))
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL
+    with pytest.raises(kvt.KvtError) as e:
+        kvt.kvt_attn_prefill_auto(q, 1, n_kv - 1, n_qh, kvh, 128, kd, vd, n_head, host.dev,
+                                  host.dev + n_tail * row, n_kv, kvt.Q8_0, True, 0.1, arena[0],
+                                  arena[1], n_tail, ws, wb - 4, out)
+    assert e.value.code == kvt.EINVAL
+    del ht
+    host.free()
