@@ -294,14 +294,19 @@ def test_sdma_refused_under_graph_capture(gpu):
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     code = None
+    code_tail = None
     with torch.cuda.graph(g, stream=s):
         try:
             kvt.kvt_swap_blocks(t[0], t[1], t[2], 1, kvt.H2D, kvt.COPY_SDMA,
                                 stream=s.cuda_stream)
         except kvt.KvtError as e:
             code = e.code
+        try:   # the staging copy's SDMA mode is the same engine path
+            kvt.kvt_stage_tail(host.dev, 4096, 0, 1, dev, kvt.COPY_SDMA, stream=s.cuda_stream)
+        except kvt.KvtError as e:
+            code_tail = e.code
         dev.add_(1)
-    assert code == kvt.EUNSUPPORTED
+    assert code == kvt.EUNSUPPORTED and code_tail == kvt.EUNSUPPORTED
     g.replay()
     torch.cuda.synchronize()
     assert (dev.cpu() == 1).all()

@@ -114,7 +114,7 @@ def test_prefill_three_way_bit_identity(gpu, fmt):
     ht[0], ht[1] = k[n_head:], v[n_head:]
     all_hbm = _prefill(q, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu, fmt)
     stage = torch.empty((2, n_kv - n_head, row), dtype=torch.uint8, device=gpu)
-    for mode in (kvt.COPY_SDMA, kvt.COPY_KERNEL):
+    for mode in (kvt.COPY_RUNTIME, kvt.COPY_SDMA, kvt.COPY_KERNEL):
         stage.zero_()
         kvt.kvt_stage_tail(host.dev, row, 0, n_kv - n_head, stage[0], mode)
         kvt.kvt_stage_tail(host.dev + (n_kv - n_head) * row, row, 0, n_kv - n_head, stage[1], mode)

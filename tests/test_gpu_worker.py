@@ -162,10 +162,12 @@ def test_worker_errors_and_destroy_drains(gpu):
     host.free()
 
 
-@pytest.mark.parametrize("mode", [kvt.COPY_SDMA, kvt.COPY_KERNEL], ids=["sdma", "kernel"])
+@pytest.mark.parametrize("mode", [kvt.COPY_RUNTIME, kvt.COPY_KERNEL], ids=["runtime", "kernel"])
 def test_graph_staging_then_prefill_replays(gpu, mode):
     """Tail staging (K and V) + prefill attention captured once, replayed three times with the
-    host tail rewritten and eager work in between: each replay equals an eager run."""
+    host tail rewritten and eager work in between: each replay equals an eager run.  The
+    runtime mode is one hipMemcpyAsync, which the runtime runs on a copy engine at this size;
+    the library-driven engine mode waits on the host and refuses capture."""
     n_kv, n_head, n_q, n_qh, kvh = 3000, 1100, 64, 16, 4
     k = synth.q8_0_rows(synth.rng(9, synth.P_K, 50), n_kv, kvh, 128)
     v = synth.q8_0_rows(synth.rng(9, synth.P_V, 50), n_kv, kvh, 128)
