@@ -253,8 +253,11 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     const int g = lane >> 5, i = lane & 31;
     // the lane's share of a transposed V read: row offset and column within a 32-column block
     const int tr_r = (lane & 15) >> 2, tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    // split-K: gridDim.x = n_split x (query tiles x kvh); split x takes key tiles
-    // [x * tiles_per_split, (x + 1) * tiles_per_split) and hands its state on
+    // split-K: gridDim.x = n_split x (query tiles x kvh); split x owns key tiles
+    // [x * tiles_per_split, (x + 1) * tiles_per_split) and hands its state on.  A pass over
+    // tiles [tile_begin, tile_cap) takes the part of each split's tiles inside it; the split's
+    // state starts in the pass that holds its first tile, and a split with no tile in the pass
+    // leaves its state alone.
     const int n_wg = gridDim.x / n_split;
     const int split = blockIdx.x / n_wg;
     const int wg = blockIdx.x - split * n_wg;
@@ -262,8 +265,12 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     const int64_t qt = wg / kvh;
     int tb = tile_begin, tc = tile_cap;
     if (n_split > 1) {
-        tb = split * tiles_per_split;
-        tc = tb + tiles_per_split < tile_cap ? tb + tiles_per_split : tile_cap;
+        const int s0 = split * tiles_per_split;
+        tb = s0 > tile_begin ? s0 : tile_begin;
+        tc = s0 + tiles_per_split < tile_cap ? s0 + tiles_per_split : tile_cap;
+        if (tb >= tc)
+            return;
+        first = tb == s0;
     }
     const int qpw = 32 * (kWaves / group);         // queries per workgroup
     const int64_t q_base = qt * qpw;
@@ -842,7 +849,7 @@ int prefill_pipeline(const char *fn, const void *q, int64_t n_q, int64_t q_pos0,
                      int32_t kv_format, int32_t causal, float scale, void *arena_k,
                      void *arena_v, int64_t arena_rows, int64_t staged, const NextBucket &nx,
                      void *state, size_t state_bytes_, float *out, void *stream,
-                     void *copy_stream)
+                     void *copy_stream, bool split_k = false)
 {
     // whatever this call does, a prefetch left by the previous one is good for it alone
     const Prefetched got = t_pipe.pre;
@@ -867,16 +874,25 @@ int prefill_pipeline(const char *fn, const void *q, int64_t n_q, int64_t q_pos0,
     const uintptr_t hv = reinterpret_cast<uintptr_t>(v_host);
     const int64_t slot_keys = arena_rows / 2 / kKT * kKT;
     const int64_t hb = n_head / kKT * kKT;   // head keys in whole tiles; the rest by bucket
+    // split_k: every pass runs in kvt_attn_prefill_splitk's key splits, each split's state
+    // carried from bucket to bucket, and one merge at the end (its bits, not the single pass's)
+    int n_split = 1, tps = 0;
+    if (split_k)
+        split_plan(q_tiles * kvh, (n_kv + kKT - 1) / kKT, n_split, tps);
+    if (n_split > 1 && q_tiles * kvh * n_split > 0x7fffffffll)
+        return kvt::fail(KVT_ERANGE, "%s: too many workgroups", fn);
+    const size_t need_state = (size_t)n_split * state_bytes(q_tiles, kvh);
     if (host_rows) {
         if (slot_keys < kKT || !arena_k || !arena_v || !kvt::aligned(arena_k, 8) ||
             !kvt::aligned(arena_v, 8))
             return kvt::fail(KVT_EINVAL,
                              "%s: arena of %lld rows (need >= 128, 8-byte aligned K and V)", fn,
                              (long long)arena_rows);
-        if (!state || state_bytes_ < state_bytes(q_tiles, kvh) || !kvt::aligned(state, 4))
-            return kvt::fail(KVT_EINVAL, "%s: state of %zu bytes, need %zu", fn, state_bytes_,
-                             state_bytes(q_tiles, kvh));
     }
+    if ((host_rows || n_split > 1) && n_q > 0 &&
+        (!state || state_bytes_ < need_state || !kvt::aligned(state, 4)))
+        return kvt::fail(KVT_EINVAL, "%s: state of %zu bytes, need %zu", fn, state_bytes_,
+                         need_state);
     if ((host_rows || prefetch) && cs == s)
         return kvt::fail(KVT_EINVAL, "%s: copy_stream must differ from stream", fn);
     if (staged) {
@@ -928,17 +944,18 @@ int prefill_pipeline(const char *fn, const void *q, int64_t n_q, int64_t q_pos0,
         KVT_HIP(hipEventRecord(ev[0], s));
         KVT_HIP(hipStreamWaitEvent(cs, ev[0], 0));
     }
+    const int fin = n_split > 1 ? 0 : 1;   // split passes always hand their state on
     if (n_q > 0 && !host_rows) {   // nothing in host memory
         launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
-                       nullptr, nullptr, n_kv, causal, scale, 0, n_kv, nullptr, 1, 1, out,
-                       kv_format, s);
+                       nullptr, nullptr, n_kv, causal, scale, 0, n_kv,
+                       n_split > 1 ? stf : nullptr, 1, fin, out, kv_format, s, n_split, tps);
         KVT_LAUNCHED("prefill_attn");
     } else if (n_q > 0) {
         bool started = false;
         if (hb > 0) {
             launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
                            nullptr, nullptr, n_kv, causal, scale, 0, hb, stf, 1, 0, out,
-                           kv_format, s);
+                           kv_format, s, n_split, tps);
             KVT_LAUNCHED("prefill_attn");
             started = true;
         }
@@ -974,11 +991,18 @@ int prefill_pipeline(const char *fn, const void *q, int64_t n_q, int64_t q_pos0,
             launch_prefill(q, n_q, q_pos0, n_qh, kvh, group, q_tiles, k_head, v_head, n_head,
                            reinterpret_cast<const void *>(sk - shift),
                            reinterpret_cast<const void *>(sv - shift), n_kv, causal, scale, kb,
-                           ke, stf, started ? 0 : 1, ke == n_kv ? 1 : 0, out, kv_format, s);
+                           ke, stf, started ? 0 : 1, ke == n_kv ? fin : 0, out, kv_format, s,
+                           n_split, tps);
             KVT_LAUNCHED("prefill_attn");
             started = true;
             KVT_HIP(hipEventRecord(ev[3 + slot], s));
         }
+    }
+    if (n_q > 0 && n_split > 1) {
+        hipLaunchKernelGGL(prefill_split_merge, dim3((unsigned)(q_tiles * kvh), kWaves), dim3(64),
+                           0, s, stf, n_split, (int)kvh, group, n_q, (int)n_qh,
+                           (float)((double)scale * 1.4426950408889634), out);
+        KVT_LAUNCHED("prefill_split_merge");
     }
     if (prefetch) {   // behind this call's own copies, while its last buckets are attended
         const size_t nb = (size_t)nx.rows * (size_t)row_bytes;
@@ -1095,20 +1119,21 @@ extern "C" int kvt_attn_prefill_plan(int64_t n_q, int64_t q_pos0, int32_t n_qh, 
     const int64_t tail = n_kv - n_head;
     if (n_q == 0 || tail == 0)
         return KVT_PREFILL_IN_PLACE;   // nothing crosses the link
-    const int qpw = 32 * (kWaves / group);
-    const int64_t q_tiles = (n_q + qpw - 1) / qpw;
-    int n_split = 1, tps = 0;
-    split_plan(q_tiles * kvh, (n_kv + kKT - 1) / kKT, n_split, tps);
-    if (n_split == 1)   // the chunk fills the chip: hide the copies behind the attention
-        return two_streams && arena_rows / 2 / kKT * kKT >= kKT ? KVT_PREFILL_PIPELINED
-                                                                 : KVT_PREFILL_IN_PLACE;
-    // a short chunk: in place, its few workgroups wait on scattered head slices across the
-    // link; staged, the tail crosses once, contiguously, before an attention that is short
     const double row_bytes = (double)kvh * head_bytes(kv_format);
     const double stage_us = 2.0 * (double)tail * row_bytes / kLinkBytesPerUs;
     const double attn_us =
         4.0 * kHd * n_qh * key_pairs(n_q, q_pos0, n_kv, causal) / attn_flop_per_us(kv_format);
-    return arena_rows >= tail && attn_us < stage_us ? KVT_PREFILL_STAGED : KVT_PREFILL_IN_PLACE;
+    const bool fits = arena_rows >= tail;
+    // with a second stream and an arena, the copies of one bucket run beside the attention of
+    // the last (in key splits when the chunk is short), so the op takes about the longer of
+    // the two -- unless the attention is so short (under a quarter of the copy) that hiding
+    // it gains less than the extra passes cost, and the whole tail can be staged instead
+    if (two_streams && arena_rows / 2 / kKT * kKT >= kKT)
+        return fits && 4.0 * attn_us < stage_us ? KVT_PREFILL_STAGED : KVT_PREFILL_PIPELINED;
+    // one stream: staged, the tail crosses once at the link rate and then the attention runs;
+    // in place, reading scattered head slices takes about twice the copy, beside the
+    // attention.  Staging is the shorter when the attention is shorter than the copy.
+    return fits && attn_us < stage_us ? KVT_PREFILL_STAGED : KVT_PREFILL_IN_PLACE;
 }
 
 extern "C" size_t kvt_attn_prefill_auto_ws_bytes(int64_t n_q, int32_t n_qh, int32_t kvh,
@@ -1145,11 +1170,11 @@ extern "C" int kvt_attn_prefill_auto(const void *q, int64_t n_q, int64_t q_pos0,
     if (n_q == 0)
         return KVT_OK;
     const int64_t tail = n_kv - n_head;
-    if (p == KVT_PREFILL_PIPELINED)
-        return kvt_attn_prefill_pipelined(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head,
-                                          k_host, v_host, n_kv, kv_format, causal, scale,
-                                          arena_k, arena_v, arena_rows, ws, ws_bytes, out, stream,
-                                          copy_stream);
+    if (p == KVT_PREFILL_PIPELINED)   // in key splits when the chunk is short
+        return prefill_pipeline("kvt_attn_prefill_auto", q, n_q, q_pos0, n_qh, kvh, hd, k_head,
+                                v_head, n_head, k_host, v_host, n_kv, kv_format, causal, scale,
+                                arena_k, arena_v, arena_rows, 0, NextBucket{}, ws, ws_bytes, out,
+                                stream, copy_stream, true);
     const void *kt = k_host, *vt = v_host;
     if (p == KVT_PREFILL_STAGED) {
         const int64_t row_bytes = (int64_t)kvh * head_bytes(kv_format);

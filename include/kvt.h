@@ -484,25 +484,29 @@ int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0, int32_t n
  *   KVT_PREFILL_IN_PLACE   the tail is read where it lies (through the host mapping)
  *   KVT_PREFILL_STAGED     the whole tail is first copied into the arena (kvt_stage_tail,
  *                          mode AUTO, on `stream`), then attended from HBM
- *   KVT_PREFILL_PIPELINED  kvt_attn_prefill_pipelined over the arena
- * Rule.  Let s be the number of key splits kvt_attn_prefill_splitk takes for (n_q, n_qh, kvh,
- * n_kv).  No tail rows, or n_q == 0: IN_PLACE.  s == 1 (the chunk's own workgroups fill the
- * chip): PIPELINED when two_streams is nonzero and arena_rows >= 128, else IN_PLACE.  s > 1:
+ *   KVT_PREFILL_PIPELINED  the tail copied in arena buckets on copy_stream while the previous
+ *                          bucket is attended, as kvt_attn_prefill_pipelined
+ * Rule.  No tail rows, or n_q == 0: IN_PLACE.  With two_streams nonzero and arena_rows >= 128:
+ * STAGED when arena_rows >= n_kv - n_head and the modelled attention time is below a quarter
+ * of the modelled staging time (too short to hide much), else PIPELINED.  With one stream:
  * STAGED when arena_rows >= n_kv - n_head and the modelled attention time is below the
- * modelled staging time, else IN_PLACE; both through the split-K form.  The model:
- * staging 2*(n_kv - n_head)*row_bytes at 56 GB/s; attention 4*hd*n_qh*pairs flop at 0.80
- * (q8_0), 0.73 (fp16) or 0.50 (bf16) PFLOP/s, pairs being the (query, key) pairs visited
- * (causal: row t sees min(n_kv, q_pos0 + t + 1) keys).
+ * modelled staging time, else IN_PLACE.  The model: staging
+ * 2*(n_kv - n_head)*row_bytes at 56 GB/s; attention 4*hd*n_qh*pairs flop at 0.80 (q8_0), 0.73
+ * (fp16) or 0.50 (bf16) PFLOP/s, pairs being the (query, key) pairs visited (causal: row t
+ * sees min(n_kv, q_pos0 + t + 1) keys).  Every plan runs the attention in the key splits
+ * kvt_attn_prefill_splitk takes for (n_q, n_qh, kvh, n_kv) -- s of them, one when the chunk's
+ * own workgroups fill the chip; the pipelined plan carries each split's state from bucket to
+ * bucket and merges the splits after the last.
  *
  * kvt_attn_prefill_auto: computes the plan (two_streams = stream and copy_stream differ;
  * arena_rows counts as 0 when arena_k or arena_v is NULL), writes it to *plan (optional,
  * host) and runs it.  Arguments as kvt_attn_prefill_pipelined, with ws (device,
  * kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv) bytes, 4-byte aligned) serving as the
  * split-K workspace or the pipelined state; arena_k / arena_v may be NULL (no staging).
- * Output: with s == 1 it equals kvt_attn_prefill's bits, with s > 1 kvt_attn_prefill_splitk's,
- * whichever plan is taken and however the rows are split between head and tail.  A PIPELINED
- * plan carries kvt_attn_prefill_pipelined's thread rules (one stream per thread; it ends a
- * pending chain prefetch).  Limits: as kvt_attn_prefill.
+ * Output: kvt_attn_prefill_splitk's bits (kvt_attn_prefill's when s == 1), whichever plan is
+ * taken and however the rows are split between head and tail.  A PIPELINED plan carries
+ * kvt_attn_prefill_pipelined's thread rules (one stream per thread; it ends a pending chain
+ * prefetch).  Limits: as kvt_attn_prefill.
  * ---------------------------------------------------------------------------------------- */
 #define KVT_PREFILL_IN_PLACE 0
 #define KVT_PREFILL_STAGED 1

@@ -288,18 +288,28 @@ def test_workspace_bytes_dispatches_to_the_per_op_sizes():
 
 # Chunk length against the stage-or-read-in-place choice over a 180,000-key q8_0 cache with
 # 94,208 rows in HBM (8 KV heads, 32 query heads, causal chunk at the end), as measured on
-# MI355X in ms (split-K form, staged / in place): 16 tokens 3.55 / 6.80, 64: 3.60 / 6.78,
-# 256: 4.39 / 6.86, 1024: 7.90 / 7.03; at 2048 tokens the pipelined form took 7.0 ms against
-# 10.8 staged and 11.3 in place.
+# MI355X in ms (split-K form, staged / in place): 1 token 3.52 / 6.92, 16: 3.54 / 6.91,
+# 64: 3.60 / 6.91, 256: 4.31 / 6.93, 512: 5.34 / 7.25, 1024: 7.49 / 7.60, 2048 (one split,
+# the single pass): 11.34 / 11.41.  Without a second stream the rule stages up to 512 tokens
+# and reads in place from 1024, where the two are within 2%.
 @pytest.mark.parametrize("n_q,plan", [(1, kvt.PREFILL_STAGED), (16, kvt.PREFILL_STAGED),
                                       (64, kvt.PREFILL_STAGED), (256, kvt.PREFILL_STAGED),
+                                      (512, kvt.PREFILL_STAGED),
                                       (1024, kvt.PREFILL_IN_PLACE),
-                                      (2048, kvt.PREFILL_PIPELINED)])
+                                      (2048, kvt.PREFILL_IN_PLACE)])
 def test_prefill_plan_follows_the_measured_crossover(n_q, plan):
     n_kv, n_head = 180000, 94208
     got = kvt.kvt_attn_prefill_plan(n_q, n_kv - n_q, 32, 8, n_head, n_kv, kvt.Q8_0, True,
-                                    n_kv - n_head, True)
+                                    n_kv - n_head, False)
     assert got == plan
+    # with a second stream and an arena smaller than the tail every chunk length pipelines;
+    # with an arena that holds the tail, chunks whose attention is under a quarter of the copy
+    # (up to 64 tokens here: 3.52-3.59 ms staged against 3.60-3.65 pipelined) stage instead
+    assert kvt.kvt_attn_prefill_plan(n_q, n_kv - n_q, 32, 8, n_head, n_kv, kvt.Q8_0, True,
+                                     2 * 16384, True) == kvt.PREFILL_PIPELINED
+    assert kvt.kvt_attn_prefill_plan(n_q, n_kv - n_q, 32, 8, n_head, n_kv, kvt.Q8_0, True,
+                                     n_kv - n_head, True) == (
+        kvt.PREFILL_STAGED if n_q <= 64 else kvt.PREFILL_PIPELINED)
 
 
 def test_prefill_plan_rules():
@@ -308,32 +318,40 @@ def test_prefill_plan_rules():
     # nothing in host memory, or no queries: in place (nothing to move)
     assert P(1, n_kv - 1, 32, 8, n_kv, n_kv, kvt.Q8_0, True, 1 << 20, True) == kvt.PREFILL_IN_PLACE
     assert P(0, 0, 32, 8, n_head, n_kv, kvt.Q8_0, True, 1 << 20, True) == kvt.PREFILL_IN_PLACE
-    # a short chunk stages only into an arena that holds the whole tail, whatever the streams
-    for two in (False, True):
-        assert P(1, n_kv - 1, 32, 8, n_head, n_kv, kvt.Q8_0, True, n_kv - n_head,
-                 two) == kvt.PREFILL_STAGED
-        assert P(1, n_kv - 1, 32, 8, n_head, n_kv, kvt.Q8_0, True, n_kv - n_head - 1,
-                 two) == kvt.PREFILL_IN_PLACE
-    # a chunk that fills the chip pipelines with two streams and an arena of >= 128 rows
-    assert P(2048, n_kv - 2048, 32, 8, n_head, n_kv, kvt.Q8_0, True, 128,
-             True) == kvt.PREFILL_PIPELINED
-    assert P(2048, n_kv - 2048, 32, 8, n_head, n_kv, kvt.Q8_0, True, 127,
-             True) == kvt.PREFILL_IN_PLACE
-    assert P(2048, n_kv - 2048, 32, 8, n_head, n_kv, kvt.Q8_0, True, 1 << 20,
-             False) == kvt.PREFILL_IN_PLACE
-    # the time model: with 2 splits, 1024 causal queries over 8192 keys take ~161 us of
-    # attention; staging 5192 or 1192 tail rows takes ~202 or ~46 us
-    assert P(1024, n_kv - 1024, 32, 8, 3000, n_kv, kvt.Q8_0, True, 1 << 20,
+    # a second stream and an arena of >= 128 rows (smaller than the tail): pipelined, for
+    # short and long chunks
+    for n_q in (1, 1024, 2048):
+        assert P(n_q, n_kv - n_q, 32, 8, n_head, n_kv, kvt.Q8_0, True, 128,
+                 True) == kvt.PREFILL_PIPELINED
+        assert P(n_q, n_kv - n_q, 32, 8, n_head, n_kv, kvt.Q8_0, True, 127,
+                 True) != kvt.PREFILL_PIPELINED
+    # an arena that holds the tail, two streams: one token's attention (~0.2 us) is far under
+    # a quarter of the copy (~202 us): staged; 1024 queries (~161 us) pipeline
+    assert P(1, n_kv - 1, 32, 8, n_head, n_kv, kvt.Q8_0, True, n_kv - n_head,
              True) == kvt.PREFILL_STAGED
+    assert P(1024, n_kv - 1024, 32, 8, n_head, n_kv, kvt.Q8_0, True, n_kv - n_head,
+             True) == kvt.PREFILL_PIPELINED
+    # one stream: a short chunk stages only into an arena that holds the whole tail
+    assert P(1, n_kv - 1, 32, 8, n_head, n_kv, kvt.Q8_0, True, n_kv - n_head,
+             False) == kvt.PREFILL_STAGED
+    assert P(1, n_kv - 1, 32, 8, n_head, n_kv, kvt.Q8_0, True, n_kv - n_head - 1,
+             False) == kvt.PREFILL_IN_PLACE
+    # the time model: 1024 causal queries over 8192 keys take ~161 us of attention; staging
+    # 5192 or 1192 tail rows takes ~202 or ~46 us
+    assert P(1024, n_kv - 1024, 32, 8, 3000, n_kv, kvt.Q8_0, True, 1 << 20,
+             False) == kvt.PREFILL_STAGED
     assert P(1024, n_kv - 1024, 32, 8, 7000, n_kv, kvt.Q8_0, True, 1 << 20,
-             True) == kvt.PREFILL_IN_PLACE
-    # bf16: the same attention at 0.50 PFLOP/s is ~258 us, staging 2 x 5192 rows of 2048
+             False) == kvt.PREFILL_IN_PLACE
+    # 2048 queries (~301 us) against 5192 rows (~202 us): in place
+    assert P(2048, n_kv - 2048, 32, 8, 3000, n_kv, kvt.Q8_0, True, 1 << 20,
+             False) == kvt.PREFILL_IN_PLACE
+    # bf16: the same 1024 queries at 0.50 PFLOP/s take ~258 us, staging 2 x 5192 rows of 2048
     # bytes ~380 us
     assert P(1024, n_kv - 1024, 32, 8, 3000, n_kv, kvt.BF16, True, 1 << 20,
-             True) == kvt.PREFILL_STAGED
+             False) == kvt.PREFILL_STAGED
     # non-causal chunks visit every key: 1024 x 8192 pairs is ~172 us against ~46 us staging
     assert P(1024, 0, 32, 8, 7000, n_kv, kvt.Q8_0, False, 1 << 20,
-             True) == kvt.PREFILL_IN_PLACE
+             False) == kvt.PREFILL_IN_PLACE
     for bad in [dict(kvh=3), dict(n_head=n_kv + 1), dict(n_q=-1), dict(fmt=9), dict(arena=-1)]:
         a = dict(n_q=1, kvh=8, n_head=n_head, fmt=kvt.Q8_0, arena=0)
         a.update(bad)

@@ -711,28 +711,35 @@ def test_prefill_splitk_decode_token_at_full_geometry(gpu):
     host.free()
 
 
-@pytest.mark.parametrize("n_q,n_head,arena_rows,two_streams,plan", [
-    (1, 3000, 5192, False, kvt.PREFILL_STAGED),         # decode token: the tail is staged
-    (1, 3000, 5191, True, kvt.PREFILL_IN_PLACE),        # the arena is one row short
-    (7, 3000, 0, False, kvt.PREFILL_IN_PLACE),          # no arena at all
-    (1024, 7000, 8192, True, kvt.PREFILL_IN_PLACE),     # 2 splits; attention outlasts staging
-    (1024, 3000, 8192, False, kvt.PREFILL_STAGED),      # 2 splits; staging is longer
-    (2048, 3000, 4096, True, kvt.PREFILL_PIPELINED),    # one split: buckets overlapped
-    (2048, 3000, 4096, False, kvt.PREFILL_IN_PLACE),    # one split, one stream
-    (300, 8192, 4096, True, kvt.PREFILL_IN_PLACE),      # all in HBM
+@pytest.mark.parametrize("n_q,n_head,arena_rows,two_streams,plan,causal", [
+    (1, 3000, 5192, False, kvt.PREFILL_STAGED, True),       # decode token: the tail is staged
+    (1, 3000, 5191, False, kvt.PREFILL_IN_PLACE, True),     # the arena is one row short
+    (7, 3000, 0, True, kvt.PREFILL_IN_PLACE, True),         # no arena at all
+    (1024, 7000, 8192, False, kvt.PREFILL_IN_PLACE, True),  # 2 splits; attention outlasts staging
+    (1024, 3000, 8192, False, kvt.PREFILL_STAGED, True),    # 2 splits; staging is longer
+    (2048, 3000, 4096, False, kvt.PREFILL_IN_PLACE, True),  # one split, one stream
+    (300, 8192, 4096, True, kvt.PREFILL_IN_PLACE, True),    # all in HBM
+    (2048, 3000, 4096, True, kvt.PREFILL_PIPELINED, True),  # one split: buckets overlapped
+    (1024, 7000, 8192, True, kvt.PREFILL_PIPELINED, True),  # 2 splits carried across buckets
+    (1, 3000, 128, True, kvt.PREFILL_PIPELINED, True),      # 16 splits, 64-key buckets
+    (7, 0, 1000, True, kvt.PREFILL_PIPELINED, True),        # no head: buckets from key 0
+    (300, 2100, 700, True, kvt.PREFILL_PIPELINED, True),    # 7 splits of 19 tiles, 5-tile buckets
+    (64, 2000, 1000, True, kvt.PREFILL_PIPELINED, False),   # non-causal
 ])
-def test_prefill_auto_plans_bit_identical(gpu, n_q, n_head, arena_rows, two_streams, plan):
+def test_prefill_auto_plans_bit_identical(gpu, n_q, n_head, arena_rows, two_streams, plan,
+                                          causal):
     """kvt_attn_prefill_auto takes the plan kvt_attn_prefill_plan names and gives the bits of
     the split-K form over the all-HBM cache (the single pass when one split is taken), on two
-    calls in a row."""
+    calls in a row.  The pipelined plan carries each key split's state across buckets that
+    start and end inside the splits."""
     n_kv, n_qh, kvh = 8192, 32, 8
     k, v = _cache(n_kv, kvh, 8192 + n_q)
     row = k.shape[1]
     q_np = synth.f16_normal(synth.rng(5, synth.P_Q, 8192 + n_q), (n_q, n_qh, 128))
     q_pos0 = n_kv - n_q
     kd, vd = _dev(k, gpu), _dev(v, gpu)
-    ref, _ = _splitk(q_np, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
-    assert kvt.kvt_attn_prefill_plan(n_q, q_pos0, n_qh, kvh, n_head, n_kv, kvt.Q8_0, True,
+    ref, _ = _splitk(q_np, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, causal, gpu)
+    assert kvt.kvt_attn_prefill_plan(n_q, q_pos0, n_qh, kvh, n_head, n_kv, kvt.Q8_0, causal,
                                      arena_rows, two_streams) == plan
     n_tail = n_kv - n_head
     host = kvt.HostBuffer(max(2 * n_tail * row, 16))
@@ -749,7 +756,7 @@ def test_prefill_auto_plans_bit_identical(gpu, n_q, n_head, arena_rows, two_stre
         out = torch.full((n_q, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
         got_plan = kvt.kvt_attn_prefill_auto(
             q, n_q, q_pos0, n_qh, kvh, 128, kd, vd, n_head, host.dev if n_tail else None,
-            host.dev + n_tail * row if n_tail else None, n_kv, kvt.Q8_0, True,
+            host.dev + n_tail * row if n_tail else None, n_kv, kvt.Q8_0, causal,
             1 / math.sqrt(128), arena[0] if arena_rows else None,
             arena[1] if arena_rows else None, arena_rows, ws, wb, out, copy_stream=copy_stream)
         torch.cuda.synchronize()
