@@ -197,6 +197,28 @@ __device__ __forceinline__ void store_raw(unsigned char *rawbuf,
     }
 }
 
+// fp16 and bf16 tiles need no conversion: word f (plane, key, WB-byte column) goes straight to
+// its place in the 16-bit tile, K rows kKPitch and V rows kVPitch bytes apart.
+template <int F, int WB>
+__device__ __forceinline__ void store_direct(unsigned char *buf,
+                                             const typename Words<F, WB>::Word (&rq)[Words<F, WB>::kPerThread])
+{
+    using R = Raw<F>;
+    using W = Words<F, WB>;
+    constexpr int kPerRow = R::kHeadBytes / WB;
+#pragma unroll
+    for (int u = 0; u < W::kPerThread; u++) {
+        const int f = threadIdx.x + u * kThreads;
+        if (f < W::kWords) {
+            const int plane = f >= W::kWords / 2;
+            const int rem = f - plane * (W::kWords / 2);
+            const int key = rem / kPerRow, w = rem - key * kPerRow;
+            unsigned char *dst = buf + (plane ? kLdsK + key * kVPitch : key * kKPitch) + WB * w;
+            *reinterpret_cast<typename W::Word *>(dst) = rq[u];
+        }
+    }
+}
+
 // Thread (plane = wave / 4, block = wave % 4, key = lane) turns its 32 values of the raw tile
 // into the 16-bit tile used by the MFMA: K and V both as rows [key][d].  q8_0: the block's
 // dequantisation to fp16; fp16 and bf16: the values as stored (bf16 tiles go to the bf16 MFMA,
@@ -246,8 +268,11 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     int first, int last, float *__restrict__ out)
 {
     using R = Raw<F>;
-    __shared__ __align__(16) unsigned char lds[2 * kLdsBuf + 2 * R::kBytes];
-    unsigned char *const lds_raw = lds + 2 * kLdsBuf;   // two raw (as stored) tiles
+    // q8_0 tiles go through raw (as stored) buffers and a dequantisation; fp16 and bf16 tiles
+    // are stored from the load registers straight into the 16-bit tiles
+    constexpr bool kDirect = F != KVT_Q8_0;
+    __shared__ __align__(16) unsigned char lds[2 * kLdsBuf + (kDirect ? 0 : 2 * R::kBytes)];
+    unsigned char *const lds_raw = lds + 2 * kLdsBuf;   // two raw tiles (q8_0)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, i = lane & 31;
@@ -350,21 +375,32 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     // prologue: raw tile b -> LDS; fp16 tile b and raw tile b+1 ready; loads of b+2 in flight
     // (b = tb; buffers are indexed by tile & 1)
     const int b0 = tb;
-    if (n_tiles > b0) {
-        load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
-        store_raw<F, WB>(lds_raw + (b0 & 1) * R::kBytes, rq);
-        if (n_tiles > b0 + 1)
-            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
+    if constexpr (kDirect) {
+        // 16-bit tile b in buffer b & 1; the registers hold tile b + 1
+        if (n_tiles > b0) {
+            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
+            store_direct<F, WB>(lds + (b0 & 1) * kLdsBuf, rq);
+            if (n_tiles > b0 + 1)
+                load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
+        }
+        __syncthreads();
+    } else {
+        if (n_tiles > b0) {
+            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
+            store_raw<F, WB>(lds_raw + (b0 & 1) * R::kBytes, rq);
+            if (n_tiles > b0 + 1)
+                load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
+        }
+        __syncthreads();
+        if (n_tiles > b0) {
+            dequant_tile<F>(lds_raw + (b0 & 1) * R::kBytes, lds + (b0 & 1) * kLdsBuf, wave, lane);
+            if (n_tiles > b0 + 1)
+                store_raw<F, WB>(lds_raw + ((b0 + 1) & 1) * R::kBytes, rq);
+            if (n_tiles > b0 + 2)
+                load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 2, rq);
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    if (n_tiles > b0) {
-        dequant_tile<F>(lds_raw + (b0 & 1) * R::kBytes, lds + (b0 & 1) * kLdsBuf, wave, lane);
-        if (n_tiles > b0 + 1)
-            store_raw<F, WB>(lds_raw + ((b0 + 1) & 1) * R::kBytes, rq);
-        if (n_tiles > b0 + 2)
-            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 2, rq);
-    }
-    __syncthreads();
 
     // per tile: multiply fp16 buffer (tile & 1); dequantise raw tile+1 into the other fp16
     // buffer; move the registers of tile+2 into the raw buffer tile+1 just left; one barrier;
@@ -377,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
         // Waves w and w + 4 share a SIMD.  The upper four dequantise the next tile before they
         // multiply this one and the lower four after, so on every SIMD one wave's MFMA work
         // meets the other's VALU work.
-        if (dequant_first && tile + 1 < n_tiles)
+        if (!kDirect && dequant_first && tile + 1 < n_tiles)
             dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kLdsBuf,
                          wave, lane);
         if (key0 <= wave_last) {
@@ -486,14 +522,24 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
                 }
             }
         }
-        if (!dequant_first && tile + 1 < n_tiles)
-            dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kLdsBuf,
-                         wave, lane);
-        if (tile + 2 < n_tiles)   // last, so the loads of tile + 2 have had the whole tile
-            store_raw<F, WB>(lds_raw + (tile & 1) * R::kBytes, rq);
-        __syncthreads();
-        if (tile + 3 < n_tiles)
-            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 3, rq);
+        if constexpr (kDirect) {
+            // the loads of tile + 1 have had the whole tile; its buffer was last read for tile
+            // - 1, before the previous barrier
+            if (tile + 1 < n_tiles)
+                store_direct<F, WB>(lds + ((tile + 1) & 1) * kLdsBuf, rq);
+            __syncthreads();
+            if (tile + 2 < n_tiles)
+                load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 2, rq);
+        } else {
+            if (!dequant_first && tile + 1 < n_tiles)
+                dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes,
+                                lds + ((tile + 1) & 1) * kLdsBuf, wave, lane);
+            if (tile + 2 < n_tiles)   // last, so the loads of tile + 2 have had the whole tile
+                store_raw<F, WB>(lds_raw + (tile & 1) * R::kBytes, rq);
+            __syncthreads();
+            if (tile + 3 < n_tiles)
+                load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 3, rq);
+        }
     }
 
     if (!last) {   // hand the state to the next pass
