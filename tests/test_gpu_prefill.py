@@ -798,3 +798,42 @@ def test_prefill_auto_staged_decode_token_matches_oracle(gpu):
     assert e.value.code == kvt.EINVAL
     del ht
     host.free()
+
+
+@pytest.mark.parametrize("n_q", [1, 512, 2048])
+def test_prefill_auto_full_geometry(gpu, n_q):
+    """The auto plan over the 180,000-token tiered q8_0 cache (94,208 rows in HBM, the tail in
+    host memory) with two streams and a 2 x 16,384-row arena -- pipelined in 32, 4 and 1 key
+    splits -- equals the split-K form over the all-HBM cache bit for bit; its last query row
+    is within 2e-3 of the fp64 oracle."""
+    n_kv, n_head, n_qh, kvh = C5_NKV, C5_NHEAD, C5_NQH, C5_KVH
+    k, v = _full_cache()
+    row = k.shape[1]
+    n_tail = n_kv - n_head
+    q_np = synth.f16_normal(synth.rng(5, synth.P_Q, 180000 + n_q), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    ref, _ = _splitk(q_np, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu)
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    q = torch.from_numpy(q_np.view(np.int16)).to(gpu)
+    wb = kvt.kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=gpu)
+    arena = torch.empty((2, 2 * 16384, row), dtype=torch.uint8, device=gpu)
+    out = torch.full((n_q, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
+    plan = kvt.kvt_attn_prefill_auto(q, n_q, q_pos0, n_qh, kvh, 128, kd[:n_head], vd[:n_head],
+                                     n_head, host.dev, host.dev + n_tail * row, n_kv, kvt.Q8_0,
+                                     True, 1 / math.sqrt(128), arena[0], arena[1], 2 * 16384, ws,
+                                     wb, out, copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert plan == kvt.PREFILL_PIPELINED
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    last = oracle.attn_prefill(q_np[n_q - 1:], n_kv - 1, kvh, k, v, n_head, k[n_head:],
+                               v[n_head:], n_kv, oracle.Q8_0, True, 1 / math.sqrt(128))
+    assert np.max(np.abs(got[n_q - 1:] - last)) <= TOL
+    del ht
+    host.free()
+    del kd, vd, arena, ws
+    torch.cuda.empty_cache()
