@@ -93,10 +93,11 @@ _SIGNATURES = {
     "kvt_attn_prefill_plan": (c_int, [c_int64, c_int64, c_int32, c_int32, c_int64, c_int64,
                                       c_int32, c_int32, c_int64, c_int32]),
     "kvt_attn_prefill_auto_ws_bytes": (c_size_t, [c_int64, c_int32, c_int32, c_int64]),
+    "kvt_attn_prefill_conv_bytes": (c_size_t, [c_int64, c_int32, c_int64, c_int32]),
     "kvt_attn_prefill_auto": (c_int, [_P, c_int64, c_int64, c_int32, c_int32, c_int32, _P, _P,
                                       c_int64, _P, _P, c_int64, c_int32, c_int32, c_float, _P,
-                                      _P, c_int64, _P, c_size_t, _P, ctypes.POINTER(c_int32),
-                                      _P, _P]),
+                                      _P, c_int64, _P, c_size_t, _P, c_size_t, _P,
+                                      ctypes.POINTER(c_int32), _P, _P]),
     "kvt_paged_write": (c_int, [_P, _P, _P, c_int32, c_int32, c_int32, _P, _P, c_int32, c_int32,
                                 c_int64, _P]),
     "kvt_copy_page": (c_int, [_P, _P, _P, c_int32, c_int64, c_int64, c_int32, c_int32, _P, _P,
@@ -499,11 +500,17 @@ def kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv) -> int:
     return int(load().kvt_attn_prefill_auto_ws_bytes(int(n_q), int(n_qh), int(kvh), int(n_kv)))
 
 
+def kvt_attn_prefill_conv_bytes(n_head, kvh, arena_rows, kv_format) -> int:
+    return int(load().kvt_attn_prefill_conv_bytes(int(n_head), int(kvh), int(arena_rows),
+                                                  int(kv_format)))
+
+
 def kvt_attn_prefill_auto(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head, k_host, v_host,
                           n_kv, kv_format, causal, scale, arena_k, arena_v, arena_rows, ws,
-                          ws_bytes, out, stream=None, copy_stream=None) -> int:
+                          ws_bytes, out, stream=None, copy_stream=None, conv=None,
+                          conv_bytes=0) -> int:
     """Runs the plan kvt_attn_prefill_plan picks and returns it.  copy_stream None: no second
-    stream, so no pipelining."""
+    stream, so no pipelining.  conv: the optional fp16 conversion buffer."""
     plan = c_int32(-1)
     s = _stream(stream)
     cs = s if copy_stream is None else _stream(copy_stream)
@@ -511,7 +518,7 @@ def kvt_attn_prefill_auto(q, n_q, q_pos0, n_qh, kvh, hd, k_head, v_head, n_head,
         _ptr(q), int(n_q), int(q_pos0), int(n_qh), int(kvh), int(hd), _ptr(k_head), _ptr(v_head),
         int(n_head), _ptr(k_host), _ptr(v_host), int(n_kv), int(kv_format), int(bool(causal)),
         float(scale), _ptr(arena_k), _ptr(arena_v), int(arena_rows), _ptr(ws), int(ws_bytes),
-        _ptr(out), ctypes.byref(plan), s, cs))
+        _ptr(conv), int(conv_bytes), _ptr(out), ctypes.byref(plan), s, cs))
     return int(plan.value)
 
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KVT_ABI_VERSION 15
+#define KVT_ABI_VERSION 16
 
 /* status codes */
 #define KVT_OK 0
@@ -503,6 +503,14 @@ int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0, int32_t n
  * host) and runs it.  Arguments as kvt_attn_prefill_pipelined, with ws (device,
  * kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv) bytes, 4-byte aligned) serving as the
  * split-K workspace or the pipelined state; arena_k / arena_v may be NULL (no staging).
+ *   conv, conv_bytes  optional (NULL, 0): device, 16-byte aligned, at least
+ *          kvt_attn_prefill_conv_bytes(n_head, kvh, arena_rows, kv_format) bytes (0 unless
+ *          the cache is q8_0).  Given that, a q8_0 cache on the pipelined plan has its rows
+ *          converted to fp16 once -- the head at the start, each bucket as it lands in the
+ *          arena -- and every pass runs on fp16 rows, when the modelled attention is long
+ *          enough for the faster fp16 passes to repay the conversion (about 11 times the
+ *          time the conversion moves the cache's bytes at 4 TB/s).  The fp16 values are the
+ *          ones the q8_0 kernel dequantises to, so the output is the same either way.
  * Output: kvt_attn_prefill_splitk's bits (kvt_attn_prefill's when s == 1), whichever plan is
  * taken and however the rows are split between head and tail.  A PIPELINED plan carries
  * kvt_attn_prefill_pipelined's thread rules (one stream per thread; it ends a pending chain
@@ -515,12 +523,15 @@ int kvt_attn_prefill_plan(int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh
                           int64_t n_kv, int32_t kv_format, int32_t causal, int64_t arena_rows,
                           int32_t two_streams);
 size_t kvt_attn_prefill_auto_ws_bytes(int64_t n_q, int32_t n_qh, int32_t kvh, int64_t n_kv);
+size_t kvt_attn_prefill_conv_bytes(int64_t n_head, int32_t kvh, int64_t arena_rows,
+                                   int32_t kv_format);
 int kvt_attn_prefill_auto(const void *q, int64_t n_q, int64_t q_pos0, int32_t n_qh, int32_t kvh,
                           int32_t hd, const void *k_head, const void *v_head, int64_t n_head,
                           const void *k_host, const void *v_host, int64_t n_kv,
                           int32_t kv_format, int32_t causal, float scale, void *arena_k,
                           void *arena_v, int64_t arena_rows, void *ws, size_t ws_bytes,
-                          float *out, int32_t *plan, void *stream, void *copy_stream);
+                          void *conv, size_t conv_bytes, float *out, int32_t *plan,
+                          void *stream, void *copy_stream);
 
 /* ----------------------------------------------------------------------------------------
  * Transfer worker.  [vLLM-CPU] SingleDirectionOffloadingHandler: transfer_async,

@@ -48,7 +48,7 @@ def test_binding_constants_equal_the_header():
 
 
 def test_abi_version():
-    assert kvt.kvt_abi_version() == 15
+    assert kvt.kvt_abi_version() == 16
 
 
 def test_library_has_gfx950_code_object():

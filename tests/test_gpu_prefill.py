@@ -752,16 +752,21 @@ def test_prefill_auto_plans_bit_identical(gpu, n_q, n_head, arena_rows, two_stre
     ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=gpu)
     arena = torch.full((2, max(arena_rows, 1), row), 0xA5, dtype=torch.uint8, device=gpu)
     copy_stream = torch.cuda.Stream() if two_streams else None
-    for _ in range(2):
+    cb = kvt.kvt_attn_prefill_conv_bytes(n_head, kvh, arena_rows, kvt.Q8_0)
+    conv = torch.full((max(cb, 16),), 0x5A, dtype=torch.uint8, device=gpu)
+    # without and with the fp16 conversion buffer (taken on the pipelined plan when the
+    # attention repays it: here at 1024 and 2048 queries)
+    for use_conv in (False, True, True):
         out = torch.full((n_q, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
         got_plan = kvt.kvt_attn_prefill_auto(
             q, n_q, q_pos0, n_qh, kvh, 128, kd, vd, n_head, host.dev if n_tail else None,
             host.dev + n_tail * row if n_tail else None, n_kv, kvt.Q8_0, causal,
             1 / math.sqrt(128), arena[0] if arena_rows else None,
-            arena[1] if arena_rows else None, arena_rows, ws, wb, out, copy_stream=copy_stream)
+            arena[1] if arena_rows else None, arena_rows, ws, wb, out, copy_stream=copy_stream,
+            conv=conv if use_conv else None, conv_bytes=cb if use_conv else 0)
         torch.cuda.synchronize()
         assert got_plan == plan
-        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), use_conv
     host.free()
 
 
@@ -804,8 +809,8 @@ def test_prefill_auto_staged_decode_token_matches_oracle(gpu):
 def test_prefill_auto_full_geometry(gpu, n_q):
     """The auto plan over the 180,000-token tiered q8_0 cache (94,208 rows in HBM, the tail in
     host memory) with two streams and a 2 x 16,384-row arena -- pipelined in 32, 4 and 1 key
-    splits -- equals the split-K form over the all-HBM cache bit for bit; its last query row
-    is within 2e-3 of the fp64 oracle."""
+    splits, the last on rows converted to fp16 -- equals the split-K form over the all-HBM
+    cache bit for bit; its last query row is within 2e-3 of the fp64 oracle."""
     n_kv, n_head, n_qh, kvh = C5_NKV, C5_NHEAD, C5_NQH, C5_KVH
     k, v = _full_cache()
     row = k.shape[1]
@@ -822,10 +827,13 @@ def test_prefill_auto_full_geometry(gpu, n_q):
     ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=gpu)
     arena = torch.empty((2, 2 * 16384, row), dtype=torch.uint8, device=gpu)
     out = torch.full((n_q, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
+    cb = kvt.kvt_attn_prefill_conv_bytes(n_head, kvh, 2 * 16384, kvt.Q8_0)
+    conv = torch.empty(cb, dtype=torch.uint8, device=gpu)   # taken at 2048 queries
     plan = kvt.kvt_attn_prefill_auto(q, n_q, q_pos0, n_qh, kvh, 128, kd[:n_head], vd[:n_head],
                                      n_head, host.dev, host.dev + n_tail * row, n_kv, kvt.Q8_0,
                                      True, 1 / math.sqrt(128), arena[0], arena[1], 2 * 16384, ws,
-                                     wb, out, copy_stream=torch.cuda.Stream())
+                                     wb, out, copy_stream=torch.cuda.Stream(), conv=conv,
+                                     conv_bytes=cb)
     torch.cuda.synchronize()
     assert plan == kvt.PREFILL_PIPELINED
     got = out.cpu().numpy()
@@ -835,5 +843,5 @@ def test_prefill_auto_full_geometry(gpu, n_q):
     assert np.max(np.abs(got[n_q - 1:] - last)) <= TOL
     del ht
     host.free()
-    del kd, vd, arena, ws
+    del kd, vd, arena, ws, conv
     torch.cuda.empty_cache()
