@@ -479,3 +479,51 @@ def test_sdma_long_ranges_cut_over_engines(gpu):
     del hb, t
     tabs.free()
     host.free()
+
+
+def test_sdma_from_two_threads_at_once(gpu):
+    """Two host threads drive the engine mode at the same time, each on its own stream with its
+    own tables and buffers (every engine carries copies of both): each result is bit-exact
+    against the oracle's memcpy loop."""
+    import threading
+    page, n = 16384, 2048
+    jobs = []
+    for j in range(2):
+        host = kvt.HostBuffer(n * page)
+        hb = host.numpy(np.uint8, (n, page))
+        synth.fill_random_bytes(synth.rng(3, synth.P_K, 90 + j), hb)
+        dev = torch.zeros((n, page), dtype=torch.uint8, device=gpu)
+        src = synth.permutation(synth.rng(3, synth.P_PERM_SRC, 90 + j), n)
+        dst = synth.permutation(synth.rng(3, synth.P_PERM_DST, 90 + j), n)
+        tb, t = _tables(n)
+        kvt.kvt_sub_block_ptrs(host.dev, page, page, src, n, 1, 0, t[0], n)
+        kvt.kvt_sub_block_ptrs(_dev_addr(dev), page, page, dst, n, 1, 0, t[1], n)
+        t[2] = page
+        jobs.append(dict(host=host, hb=hb, dev=dev, src=src, dst=dst, tb=tb, t=t,
+                         stream=torch.cuda.Stream(), err=None))
+
+    def run(job):
+        try:
+            for _ in range(3):
+                kvt.kvt_swap_blocks(job["t"][0], job["t"][1], job["t"][2], n, kvt.H2D,
+                                    kvt.COPY_SDMA, stream=job["stream"])
+        except Exception as e:   # reported by the main thread
+            job["err"] = e
+
+    threads = [threading.Thread(target=run, args=(j,)) for j in jobs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    for job in jobs:
+        assert job["err"] is None, job["err"]
+        ref = np.zeros((n, page), dtype=np.uint8)
+        s = oracle.sub_block_ptrs(job["hb"].ctypes.data, page, page, job["src"], 1, 0, n)
+        d = oracle.sub_block_ptrs(ref.ctypes.data, page, page, job["dst"], 1, 0, n)
+        oracle.swap(s, d, np.full(n, page, dtype=np.uint64))
+        assert np.array_equal(job["dev"].cpu().numpy(), ref)
+    for job in jobs:
+        del job["hb"], job["t"]
+        job["host"].free()
+        job["tb"].free()
