@@ -845,3 +845,38 @@ def test_prefill_auto_full_geometry(gpu, n_q):
     host.free()
     del kd, vd, arena, ws, conv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", [kvt.F16, kvt.BF16], ids=FMT_IDS.get)
+@pytest.mark.parametrize("n_q,arena_rows,two_streams", [(1, 128, True), (1024, 4096, True),
+                                                        (2048, 4096, True), (1, 6000, False)])
+def test_prefill_auto_fp_caches(gpu, fmt, n_q, arena_rows, two_streams):
+    """The auto plan over fp16 and bf16 caches (pipelined in key splits, pipelined in one pass,
+    staged) gives the split-K form's bits over the all-HBM cache; the conversion buffer is
+    sized 0 for them and never used."""
+    n_kv, n_head, n_qh, kvh = 6000, 2100, 32, 8
+    k, v = _cache(n_kv, kvh, 6000 + n_q, fmt)
+    row = k.shape[1]
+    q_np = synth.f16_normal(synth.rng(5, synth.P_Q, 6000 + n_q), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    ref, _ = _splitk(q_np, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu, fmt)
+    assert kvt.kvt_attn_prefill_conv_bytes(n_head, kvh, arena_rows, fmt) == 0
+    n_tail = n_kv - n_head
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    q = torch.from_numpy(q_np.view(np.int16)).to(gpu)
+    wb = kvt.kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=gpu)
+    arena = torch.empty((2, arena_rows, row), dtype=torch.uint8, device=gpu)
+    out = torch.full((n_q, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
+    plan = kvt.kvt_attn_prefill_auto(q, n_q, q_pos0, n_qh, kvh, 128, kd, vd, n_head, host.dev,
+                                     host.dev + n_tail * row, n_kv, fmt, True,
+                                     1 / math.sqrt(128), arena[0], arena[1], arena_rows, ws, wb,
+                                     out, copy_stream=torch.cuda.Stream() if two_streams else None)
+    torch.cuda.synchronize()
+    assert plan == (kvt.PREFILL_PIPELINED if two_streams else kvt.PREFILL_STAGED)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    del ht
+    host.free()
