@@ -880,3 +880,32 @@ def test_prefill_auto_fp_caches(gpu, fmt, n_q, arena_rows, two_streams):
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
     del ht
     host.free()
+
+
+@pytest.mark.parametrize("fmt", [kvt.F16, kvt.BF16], ids=FMT_IDS.get)
+def test_prefill_fp_caches_full_geometry(gpu, fmt):
+    """fp16 and bf16 caches at the full 180,000-token geometry (2048 causal queries x 32
+    heads): the all-HBM cache and the HBM head with the tail read in place from host memory
+    give the same bits; the first and last query rows are within 2e-3 of the fp64 oracle."""
+    n_kv, n_head, n_q, n_qh, kvh = C5_NKV, C5_NHEAD, C5_NQ, C5_NQH, C5_KVH
+    k, v = _cache(n_kv, kvh, 180002, fmt)
+    row = k.shape[1]
+    n_tail = n_kv - n_head
+    q = synth.f16_normal(synth.rng(5, synth.P_Q, 180002), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    all_hbm = _prefill(q, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, True, gpu, fmt)
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    in_place = _prefill(q, q_pos0, kvh, kd, vd, n_head, host.dev, host.dev + n_tail * row, n_kv,
+                        True, gpu, fmt)
+    assert np.array_equal(in_place.view(np.uint32), all_hbm.view(np.uint32))
+    for t in (0, n_q - 1):
+        ref = oracle.attn_prefill(q, q_pos0, kvh, k, v, n_kv, None, None, n_kv, ORACLE_FMT[fmt],
+                                  True, 1 / math.sqrt(128), t_begin=t, t_end=t + 1)
+        assert np.max(np.abs(all_hbm[t:t + 1] - ref)) <= TOL, t
+    del ht
+    host.free()
+    del kd, vd
+    torch.cuda.empty_cache()
