@@ -7,14 +7,14 @@
 // so the value is fully determined and the selection is reproducible bit for bit.
 //
 // Wavefront path (k <= 32, the decode case):
-//   score_wave_topk -- a workgroup stages 64 pooled rows and the index queries in LDS; lane l
-//     of a wave scores row l for one head, so a head's 64 candidates sit one per lane and a
-//     64-lane bitonic sort over cross-lane shuffles (no LDS, no barriers) leaves the best k in
+//   score_wave_topk -- a workgroup stages 64 pooled rows and two heads' index queries in LDS;
+//     lane l of a wave scores row l for one head, so a head's 64 candidates sit one per lane
+//     and a 64-lane bitonic sort over cross-lane shuffles (no barriers) leaves the best k in
 //     lanes 0..k-1, written out as a sorted candidate list.
-//   merge_wave_topk -- one workgroup per head; each wave folds candidate lists into its running
-//     best-32 (the running list in lanes 0..31, the incoming list reversed in lanes 32..63:
-//     a bitonic sequence, cleaned in six shuffle steps), then the 16 waves fold pairwise
-//     through LDS, and the winners' ids are sorted ascending by one more lane sort.
+//   merge_wave_topk -- one workgroup per head; each half-wave folds candidate lists into its
+//     running best-32 (each incoming list read in reverse order, so the better entry of every
+//     lane pair is a bitonic sequence, cleaned in five shuffle steps), then the halves and the
+//     16 waves fold pairwise, and the winners' ids are sorted ascending by one more lane sort.
 // Selection path (32 < k <= 2048):
 //   score_wave_topk<true> -- the same scoring, writing every rank key;  select_level -- exact
 //     selection by bisection over the (key, id) composite, per segment of up to 4096 keys, then
@@ -133,42 +133,65 @@ __device__ __forceinline__ void wave_sort_best_first(uint64_t &key, uint32_t &id
             wave_cx(key, id, lane, stride, size == 64 || (lane & size) == 0);
 }
 
-// running best-32 (lanes 0..31, best first) merged with a list (lanes 0..31, best first)
-__device__ __forceinline__ void wave_merge32(uint64_t &ck, uint32_t &ci, uint64_t lk, uint32_t li,
+// Each 32-lane half of a wave merges on its own: a running best-32 (slot = lane & 31, best
+// first) and a list held reversed (slot 31 - (lane & 31) of a best-first list).  The better of
+// the two in every lane is the best 32 of both, as a bitonic sequence (falling, then rising),
+// which five compare-exchange steps inside the half sort best first.  A list is reversed by
+// the address its lanes read, so a merge costs one compare and five steps on half a wave.
+__device__ __forceinline__ void half_merge32(uint64_t &ck, uint32_t &ci, uint64_t rk, uint32_t ri,
                                              int lane)
 {
-    const uint64_t rk = shfl_u64(lk, 63 - lane);
-    const uint32_t ri = __shfl(li, 63 - lane, 64);
-    if (lane >= 32) {
+    if (better(rk, ri, ck, ci)) {
         ck = rk;
         ci = ri;
     }
 #pragma unroll
-    for (int stride = 32; stride > 0; stride >>= 1)
+    for (int stride = 16; stride > 0; stride >>= 1)
         wave_cx(ck, ci, lane, stride, true);
 }
 
-// grid.x = ceil(n_blocks / 64), kWaveThreads threads (a wave per head).  LDS: 64 padded rows
-// + queries as fp64.
-constexpr int kWaveThreads = 512;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// The exact product of two fp16 values in fp32 (11-bit significands give at most 22 bits, and
+// the exponents stay inside fp32's normal range), as one v_fma_mix_f32 that adds `zero`.  The
+// zero is 0.0f passed in from the host, so the compiler keeps the mixed-precision FMA instead
+// of converting both operands first.  Adding it to the fp64 sum is then exactly the fp64 FMA
+// of the two values.
+__device__ __forceinline__ float f16_product(_Float16 a, _Float16 b, float zero)
+{
+    return __builtin_fmaf((float)a, (float)b, zero);
+}
+
+// A scoring workgroup takes 64 pooled rows and kScoreHeads heads, a wave per head: the
+// scoring chains and sorts then spread over four times as many CUs as with every head in one
+// workgroup (the loop is VALU-bound, and one wave per SIMD leaves it to the chain's latency).
+constexpr int kScoreHeads = 2;
+constexpr int kWaveThreads = kScoreHeads * 64;
+// grid.x = n_rg * ceil(n_sel / kScoreHeads) with n_rg = ceil(n_blocks / 64): row group
+// blockIdx.x % n_rg, head group blockIdx.x / n_rg.  Workgroups go to the eight XCDs in turn, so
+// with n_rg a multiple of 8 every head group of a row group runs on one XCD and its rows come
+// from HBM once.  LDS: 64 padded rows + the group's index queries (fp16).
 // kKeysOnly: write every row's rank key to cand_key[h][n_blocks] (ids implicit) instead of the
-// sorted best-k candidate lists -- the input of the selection path.
+// sorted best-k candidate lists [h][n_rg][k] -- the input of the selection path.
 template <bool kKeysOnly>
 __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
     const uint16_t *__restrict__ pooled, int64_t n_blocks, int dim,
     const uint16_t *__restrict__ q_idx, int n_sel, int k, uint64_t *__restrict__ cand_key,
-    uint32_t *__restrict__ cand_id, double *__restrict__ scores_out)
+    uint32_t *__restrict__ cand_id, double *__restrict__ scores_out, float zero)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     const int pitch = dim * 2 + 16;
     unsigned char *rows = lds;
-    double *qd = reinterpret_cast<double *>(lds + kWaveRows * pitch);
-    const int64_t b0 = (int64_t)blockIdx.x * kWaveRows;
+    uint16_t *qs = reinterpret_cast<uint16_t *>(lds + kWaveRows * pitch);
+    const unsigned n_rg = (unsigned)((n_blocks + kWaveRows - 1) / kWaveRows);
+    const unsigned rg = blockIdx.x % n_rg;
+    const int h0 = (int)(blockIdx.x / n_rg) * kScoreHeads;
+    const int64_t b0 = (int64_t)rg * kWaveRows;
     const int nrows = (int)std::min<int64_t>(kWaveRows, n_blocks - b0);
     const int wpr = dim / 8;
 
     // every load is issued unconditionally (tail rows re-read the last valid row)
-    constexpr int kMaxWordsPerThread = kWaveRows * (256 / 8) / kWaveThreads;   // 4
+    constexpr int kMaxWordsPerThread = kWaveRows * (256 / 8) / kWaveThreads;   // 16
     u32x4 v[kMaxWordsPerThread];
 #pragma unroll
     for (int u = 0; u < kMaxWordsPerThread; u++) {
@@ -183,24 +206,42 @@ __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
         if (w < kWaveRows * wpr)
             *reinterpret_cast<u32x4 *>(rows + (w / wpr) * pitch + (w % wpr) * 16) = v[u];
     }
-    for (int e = threadIdx.x; e < n_sel * dim; e += kWaveThreads)
-        qd[e] = (double)f16_bits_to_f32(q_idx[e]);
+    const int nh = std::min(kScoreHeads, n_sel - h0);
+    for (int e = threadIdx.x; e < nh * dim; e += kWaveThreads)
+        qs[e] = q_idx[h0 * dim + e];
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool valid = lane < nrows;
     const unsigned char *my_row = rows + lane * pitch;
-    // one head per wave: lane l scores row l, one fp64 chain in index order
-    for (int h = wave; h < n_sel; h += kWaveThreads / 64) {
-        const double *qh = qd + h * dim;
+    // one head per wave: lane l scores row l, one fp64 chain in index order.  Up to 128
+    // elements of the row and the query are read into registers at once, so the chain waits on
+    // LDS once per 128 elements.
+    if (wave < nh) {
+        const int h = h0 + wave;
+        const unsigned char *q_row = reinterpret_cast<const unsigned char *>(qs + wave * dim);
         double acc = 0.0;
-        for (int c = 0; c < wpr; c++) {
-            const u32x4 w4 = *reinterpret_cast<const u32x4 *>(my_row + c * 16);
+        for (int c0 = 0; c0 < wpr; c0 += 16) {
+            u32x4 kw[16], qw[16];
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const uint16_t bits = (uint16_t)(w4[e >> 1] >> ((e & 1) * 16));
-                acc = fma(qh[c * 8 + e], (double)f16_bits_to_f32(bits), acc);
+            for (int j = 0; j < 16; j++) {   // words past the row re-read its last word, unused
+                const int c = min(c0 + j, wpr - 1);
+                kw[j] = *reinterpret_cast<const u32x4 *>(my_row + c * 16);
+                qw[j] = *reinterpret_cast<const u32x4 *>(q_row + c * 16);
             }
+#pragma unroll
+            for (int j = 0; j < 16; j++)
+                if (c0 + j < wpr)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {   // word e: elements 2e (low half), 2e + 1
+                        // (the words are copied out first: clang's bit_cast of a vector
+                        // element subscript reads element 0 whatever the index)
+                        const uint32_t kv = kw[j][e], qv = qw[j][e];
+                        const half2_t kx = __builtin_bit_cast(half2_t, kv);
+                        const half2_t qx = __builtin_bit_cast(half2_t, qv);
+                        acc += (double)f16_product(qx[0], kx[0], zero);
+                        acc += (double)f16_product(qx[1], kx[1], zero);
+                    }
         }
         uint64_t key = valid ? rank_key(acc) : 0;
         uint32_t id = valid ? (uint32_t)(b0 + lane) : kNoId;
@@ -209,11 +250,11 @@ __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
         if (kKeysOnly) {
             if (valid)
                 cand_key[(int64_t)h * n_blocks + b0 + lane] = key;
-            continue;
+            return;
         }
         wave_sort_best_first(key, id, lane);
         if (lane < k) {
-            const int64_t o = ((int64_t)h * gridDim.x + blockIdx.x) * k + lane;
+            const int64_t o = ((int64_t)h * n_rg + rg) * k + lane;
             cand_key[o] = key;
             cand_id[o] = id;
         }
@@ -221,62 +262,67 @@ __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
 }
 
 // grid.x = n_sel, kMergeWaves*64 threads.  Lists of k sorted candidates: [h][n_lists][k].
+// Half-wave hw (2 * wave + upper half) keeps a running best-32 over lists hw, hw + 32, ...;
+// then the upper half of each wave folds into the lower, and the waves fold pairwise through
+// LDS.  Slots past a list's k entries, and lists past n_lists, are empty (key 0, id kNoId):
+// merging an empty list leaves a sorted list as it is.
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
     const uint64_t *__restrict__ cand_key, const uint32_t *__restrict__ cand_id, int n_lists,
     int k, int32_t *__restrict__ ids)
 {
+    constexpr int kHalves = 2 * kMergeWaves;
     __shared__ uint64_t skey[kMergeWaves][kWaveK];
     __shared__ uint32_t sid[kMergeWaves][kWaveK];
     const int h = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = lane & 31, hw = 2 * wave + (lane >> 5);
     const uint64_t *hk = cand_key + (int64_t)h * n_lists * k;
     const uint32_t *hi = cand_id + (int64_t)h * n_lists * k;
-    const int li = min(lane, k - 1);
-    uint64_t ck = 0;
-    uint32_t ci = kNoId;
-    // prefetch one list ahead: the loads of list L+16 are in flight while L merges
-    int L = wave;
-    uint64_t nk = 0;
-    uint32_t ni = kNoId;
-    if (L < n_lists) {
-        nk = hk[(int64_t)L * k + li];
-        ni = hi[(int64_t)L * k + li];
+    auto load = [&](int L, int sl, uint64_t &key, uint32_t &id) {
+        const bool in = L < n_lists && sl < k;
+        key = in ? hk[(int64_t)L * k + sl] : 0;
+        id = in ? hi[(int64_t)L * k + sl] : kNoId;
+    };
+    uint64_t ck, nk;
+    uint32_t ci, ni;
+    load(hw, slot, ck, ci);
+    // one list ahead: the loads of round r + 1 are in flight while round r merges
+    const int rounds = (n_lists + kHalves - 1) / kHalves;
+    load(hw + kHalves, 31 - slot, nk, ni);
+    for (int r = 1; r < rounds; r++) {
+        const uint64_t lk = nk;
+        const uint32_t lid = ni;
+        load(hw + (r + 1) * kHalves, 31 - slot, nk, ni);
+        half_merge32(ck, ci, lk, lid, lane);
     }
-    while (L < n_lists) {
-        uint64_t lk = lane < k ? nk : 0;
-        uint32_t lid = lane < k ? ni : kNoId;
-        const int Ln = L + kMergeWaves;
-        if (Ln < n_lists) {
-            nk = hk[(int64_t)Ln * k + li];
-            ni = hi[(int64_t)Ln * k + li];
-        }
-        wave_merge32(ck, ci, lk, lid, lane);
-        L = Ln;
+    // the upper half's list, reversed, into the lower half (lane l < 32 reads lane 63 - l)
+    {
+        const uint64_t rk = shfl_u64(ck, 63 - lane);
+        const uint32_t ri = __shfl(ci, 63 - lane, 64);
+        half_merge32(ck, ci, rk, ri, lane);
     }
-    // pairwise fold of the waves' lists through LDS
+    // pairwise fold of the waves' lists (lanes 0..31) through LDS, read back reversed
     for (int active = kMergeWaves / 2; active >= 1; active >>= 1) {
         if (wave >= active && wave < 2 * active && lane < kWaveK) {
             skey[wave][lane] = ck;
             sid[wave][lane] = ci;
         }
         __syncthreads();
-        if (wave < active) {
-            const uint64_t lk = skey[wave + active][lane & 31];
-            const uint32_t lid = sid[wave + active][lane & 31];
-            wave_merge32(ck, ci, lane < kWaveK ? lk : 0, lane < kWaveK ? lid : kNoId, lane);
-        }
+        if (wave < active)
+            half_merge32(ck, ci, skey[wave + active][31 - slot], sid[wave + active][31 - slot], lane);
         __syncthreads();
     }
     if (wave == 0) {
-        // the k winners' ids in ascending order; empty slots (kNoId) sort last and become -1
+        // the k winners' ids in ascending order (a sort inside each half; the lower half's is
+        // used); empty slots (kNoId) sort last and become -1
         uint32_t id = lane < k ? ci : kNoId;
 #pragma unroll
-        for (int size = 2; size <= 64; size <<= 1)
+        for (int size = 2; size <= 32; size <<= 1)
 #pragma unroll
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
                 const uint32_t p = xor_lane_dyn(id, lane, stride);
                 const bool lower = (lane & stride) == 0;
-                const bool up = size == 64 || (lane & size) == 0;
+                const bool up = size == 32 || (lane & size) == 0;
                 const bool mine_first = id < p;
                 if ((lower == up) != mine_first && id != p)
                     id = p;
@@ -578,10 +624,11 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
         uint64_t *ck = reinterpret_cast<uint64_t *>(w);
         uint32_t *ci = reinterpret_cast<uint32_t *>(w + round_up(c * 8, 256));
         if (n_wg > 0) {
-            const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)n_sel * dim * 8;
-            hipLaunchKernelGGL(score_wave_topk<false>, dim3((unsigned)n_wg), dim3(kWaveThreads), lds, s,
+            const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)kScoreHeads * dim * 2;
+            const unsigned grid = (unsigned)n_wg * (unsigned)((n_sel + kScoreHeads - 1) / kScoreHeads);
+            hipLaunchKernelGGL(score_wave_topk<false>, dim3(grid), dim3(kWaveThreads), lds, s,
                                static_cast<const uint16_t *>(pooled), n_blocks, dim,
-                               static_cast<const uint16_t *>(q_idx), n_sel, k, ck, ci, scores);
+                               static_cast<const uint16_t *>(q_idx), n_sel, k, ck, ci, scores, 0.0f);
             KVT_LAUNCHED("score_wave_topk");
         }
         hipLaunchKernelGGL(merge_wave_topk, dim3(n_sel), dim3(kMergeWaves * 64), 0, s, ck, ci,
@@ -601,11 +648,12 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
     uint32_t *b_id = reinterpret_cast<uint32_t *>(w);
     if (n_blocks > 0) {
         const int64_t n_wg = (n_blocks + kWaveRows - 1) / kWaveRows;
-        const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)n_sel * dim * 8;
-        hipLaunchKernelGGL(score_wave_topk<true>, dim3((unsigned)n_wg), dim3(kWaveThreads), lds, s,
+        const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)kScoreHeads * dim * 2;
+        const unsigned grid = (unsigned)n_wg * (unsigned)((n_sel + kScoreHeads - 1) / kScoreHeads);
+        hipLaunchKernelGGL(score_wave_topk<true>, dim3(grid), dim3(kWaveThreads), lds, s,
                            static_cast<const uint16_t *>(pooled), n_blocks, dim,
                            static_cast<const uint16_t *>(q_idx), n_sel, k, all_key, nullptr,
-                           scores);
+                           scores, 0.0f);
         KVT_LAUNCHED("score_wave_topk");
     }
     const uint64_t *in_key = all_key;
