@@ -14,7 +14,7 @@
 //   merge_wave_topk -- one workgroup per head; each half-wave folds candidate lists into its
 //     running best-32 (each incoming list read in reverse order, so the better entry of every
 //     lane pair is a bitonic sequence, cleaned in five shuffle steps), then the halves and the
-//     16 waves fold pairwise, and the winners' ids are sorted ascending by one more lane sort.
+//     8 or 16 waves fold pairwise, and the winners' ids are sorted ascending by one more lane sort.
 // Selection path (32 < k <= 2048):
 //   score_wave_topk<true> -- the same scoring, writing every rank key;  select_level -- exact
 //     selection by bisection over the (key, id) composite, per segment of up to 4096 keys, then
@@ -53,7 +53,6 @@ __device__ __forceinline__ bool better(uint64_t ka, uint32_t ia, uint64_t kb, ui
 // ---------------------------------------------------------------------------------------------
 constexpr int kWaveRows = 64;        // pooled rows per scoring workgroup: one per lane
 constexpr int kWaveK = 32;           // largest k of this path
-constexpr int kMergeWaves = 16;
 
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src)
 {
@@ -162,15 +161,17 @@ __device__ __forceinline__ float f16_product(_Float16 a, _Float16 b, float zero)
     return __builtin_fmaf((float)a, (float)b, zero);
 }
 
-// A scoring workgroup takes 64 pooled rows and kScoreHeads heads, a wave per head: the
-// scoring chains and sorts then spread over four times as many CUs as with every head in one
-// workgroup (the loop is VALU-bound, and one wave per SIMD leaves it to the chain's latency).
+// A scoring workgroup takes 128 pooled rows and kScoreHeads heads, two waves per head (rows
+// 0..63 and 64..127), four waves in all: the scoring chains and sorts spread over many CUs at
+// one wave per SIMD (the loop is VALU-bound).  The two waves of a head merge their best-32
+// lists in LDS, so the merge kernel reads one list per 128 rows.
+constexpr int kScoreRows = 2 * kWaveRows;
 constexpr int kScoreHeads = 2;
-constexpr int kWaveThreads = kScoreHeads * 64;
-// grid.x = n_rg * ceil(n_sel / kScoreHeads) with n_rg = ceil(n_blocks / 64): row group
+constexpr int kWaveThreads = kScoreHeads * 2 * 64;
+// grid.x = n_rg * ceil(n_sel / kScoreHeads) with n_rg = ceil(n_blocks / 128): row group
 // blockIdx.x % n_rg, head group blockIdx.x / n_rg.  Workgroups go to the eight XCDs in turn, so
 // with n_rg a multiple of 8 every head group of a row group runs on one XCD and its rows come
-// from HBM once.  LDS: 64 padded rows + the group's index queries (fp16).
+// from HBM once.  LDS: 128 padded rows, the group's index queries (fp16), the upper waves' lists.
 // kKeysOnly: write every row's rank key to cand_key[h][n_blocks] (ids implicit) instead of the
 // sorted best-k candidate lists [h][n_rg][k] -- the input of the selection path.
 template <bool kKeysOnly>
@@ -182,28 +183,30 @@ __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
     extern __shared__ __align__(16) unsigned char lds[];
     const int pitch = dim * 2 + 16;
     unsigned char *rows = lds;
-    uint16_t *qs = reinterpret_cast<uint16_t *>(lds + kWaveRows * pitch);
-    const unsigned n_rg = (unsigned)((n_blocks + kWaveRows - 1) / kWaveRows);
+    uint16_t *qs = reinterpret_cast<uint16_t *>(lds + kScoreRows * pitch);
+    uint64_t *list_key = reinterpret_cast<uint64_t *>(lds + kScoreRows * pitch + kScoreHeads * dim * 2);
+    uint32_t *list_id = reinterpret_cast<uint32_t *>(list_key + kScoreHeads * kWaveK);
+    const unsigned n_rg = (unsigned)((n_blocks + kScoreRows - 1) / kScoreRows);
     const unsigned rg = blockIdx.x % n_rg;
     const int h0 = (int)(blockIdx.x / n_rg) * kScoreHeads;
-    const int64_t b0 = (int64_t)rg * kWaveRows;
-    const int nrows = (int)std::min<int64_t>(kWaveRows, n_blocks - b0);
+    const int64_t b0 = (int64_t)rg * kScoreRows;
+    const int nrows = (int)std::min<int64_t>(kScoreRows, n_blocks - b0);
     const int wpr = dim / 8;
 
     // every load is issued unconditionally (tail rows re-read the last valid row)
-    constexpr int kMaxWordsPerThread = kWaveRows * (256 / 8) / kWaveThreads;   // 16
+    constexpr int kMaxWordsPerThread = kScoreRows * (256 / 8) / kWaveThreads;   // 16
     u32x4 v[kMaxWordsPerThread];
 #pragma unroll
     for (int u = 0; u < kMaxWordsPerThread; u++) {
         const int w = threadIdx.x + u * kWaveThreads;
         const int r = min(w / wpr, nrows - 1), c = w % wpr;
-        if (w < kWaveRows * wpr)
+        if (w < kScoreRows * wpr)
             v[u] = *reinterpret_cast<const u32x4 *>(pooled + (b0 + r) * dim + c * 8);
     }
 #pragma unroll
     for (int u = 0; u < kMaxWordsPerThread; u++) {
         const int w = threadIdx.x + u * kWaveThreads;
-        if (w < kWaveRows * wpr)
+        if (w < kScoreRows * wpr)
             *reinterpret_cast<u32x4 *>(rows + (w / wpr) * pitch + (w % wpr) * 16) = v[u];
     }
     const int nh = std::min(kScoreHeads, n_sel - h0);
@@ -212,14 +215,18 @@ __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const bool valid = lane < nrows;
-    const unsigned char *my_row = rows + lane * pitch;
-    // one head per wave: lane l scores row l, one fp64 chain in index order.  Up to 128
+    const int hl = wave >> 1, part = wave & 1;   // head in the group, row half
+    const int row = part * kWaveRows + lane;
+    const bool valid = row < nrows;
+    const unsigned char *my_row = rows + row * pitch;
+    uint64_t key = 0;
+    uint32_t id = kNoId;
+    // lane l of a wave scores its row for one head, one fp64 chain in index order.  Up to 128
     // elements of the row and the query are read into registers at once, so the chain waits on
     // LDS once per 128 elements.
-    if (wave < nh) {
-        const int h = h0 + wave;
-        const unsigned char *q_row = reinterpret_cast<const unsigned char *>(qs + wave * dim);
+    if (hl < nh) {
+        const int h = h0 + hl;
+        const unsigned char *q_row = reinterpret_cast<const unsigned char *>(qs + hl * dim);
         double acc = 0.0;
         for (int c0 = 0; c0 < wpr; c0 += 16) {
             u32x4 kw[16], qw[16];
@@ -243,29 +250,43 @@ __global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
                         acc += (double)f16_product(qx[1], kx[1], zero);
                     }
         }
-        uint64_t key = valid ? rank_key(acc) : 0;
-        uint32_t id = valid ? (uint32_t)(b0 + lane) : kNoId;
+        key = valid ? rank_key(acc) : 0;
+        id = valid ? (uint32_t)(b0 + row) : kNoId;
         if (scores_out && valid)
-            scores_out[(int64_t)h * n_blocks + b0 + lane] = acc;
+            scores_out[(int64_t)h * n_blocks + b0 + row] = acc;
         if (kKeysOnly) {
             if (valid)
-                cand_key[(int64_t)h * n_blocks + b0 + lane] = key;
-            return;
+                cand_key[(int64_t)h * n_blocks + b0 + row] = key;
+        } else {
+            wave_sort_best_first(key, id, lane);
+            if (part == 1 && lane < kWaveK) {
+                list_key[hl * kWaveK + lane] = key;
+                list_id[hl * kWaveK + lane] = id;
+            }
         }
-        wave_sort_best_first(key, id, lane);
-        if (lane < k) {
-            const int64_t o = ((int64_t)h * n_rg + rg) * k + lane;
-            cand_key[o] = key;
-            cand_id[o] = id;
+    }
+    if constexpr (!kKeysOnly) {
+        __syncthreads();
+        // the lower wave takes the upper wave's best 32, read in reverse order
+        if (hl < nh && part == 0) {
+            const int sl = kWaveK - 1 - (lane & 31);
+            half_merge32(key, id, list_key[hl * kWaveK + sl], list_id[hl * kWaveK + sl], lane);
+            if (lane < k) {
+                const int64_t o = ((int64_t)(h0 + hl) * n_rg + rg) * k + lane;
+                cand_key[o] = key;
+                cand_id[o] = id;
+            }
         }
     }
 }
 
 // grid.x = n_sel, kMergeWaves*64 threads.  Lists of k sorted candidates: [h][n_lists][k].
-// Half-wave hw (2 * wave + upper half) keeps a running best-32 over lists hw, hw + 32, ...;
+// Half-wave hw (2 * wave + upper half) keeps a running best-32 over lists hw, hw + 2W, ...;
 // then the upper half of each wave folds into the lower, and the waves fold pairwise through
 // LDS.  Slots past a list's k entries, and lists past n_lists, are empty (key 0, id kNoId):
-// merging an empty list leaves a sorted list as it is.
+// merging an empty list leaves a sorted list as it is.  A fold level costs about two merge
+// rounds, so few lists take 8 waves and many take 16.
+template <int kMergeWaves>
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
     const uint64_t *__restrict__ cand_key, const uint32_t *__restrict__ cand_id, int n_lists,
     int k, int32_t *__restrict__ ids)
@@ -301,7 +322,10 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
         const uint32_t ri = __shfl(ci, 63 - lane, 64);
         half_merge32(ck, ci, rk, ri, lane);
     }
-    // pairwise fold of the waves' lists (lanes 0..31) through LDS, read back reversed
+    // pairwise fold of the waves' lists (lanes 0..31) through LDS, read back reversed.  A wave
+    // writes its slot once, at the level where it hands its list on, so one barrier a level
+    // orders every write before its read.
+#pragma unroll
     for (int active = kMergeWaves / 2; active >= 1; active >>= 1) {
         if (wave >= active && wave < 2 * active && lane < kWaveK) {
             skey[wave][lane] = ck;
@@ -310,7 +334,6 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_wave_topk(
         __syncthreads();
         if (wave < active)
             half_merge32(ck, ci, skey[wave + active][31 - slot], sid[wave + active][31 - slot], lane);
-        __syncthreads();
     }
     if (wave == 0) {
         // the k winners' ids in ascending order (a sort inside each half; the lower half's is
@@ -586,7 +609,7 @@ extern "C" size_t kvt_index_topk_ws_bytes(int64_t n_blocks, int32_t n_sel, int32
     if (n_blocks < 0 || n_sel < 1 || k < 1)
         return 0;
     if (k <= kWaveK) {
-        const size_t c = (size_t)n_sel * (size_t)std::max<int64_t>((n_blocks + kWaveRows - 1) / kWaveRows, 1) * k;
+        const size_t c = (size_t)n_sel * (size_t)std::max<int64_t>((n_blocks + kScoreRows - 1) / kScoreRows, 1) * k;
         return round_up(c * 8, 256) + round_up(c * 4, 256) + 256;
     }
     // rank keys of every block, then two ping-pong candidate buffers (key + id)
@@ -618,21 +641,26 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
                          ws_bytes, need);
     hipStream_t s = kvt::as_stream(stream);
     if (k <= kWaveK) {
-        const int64_t n_wg = (n_blocks + kWaveRows - 1) / kWaveRows;
+        const int64_t n_wg = (n_blocks + kScoreRows - 1) / kScoreRows;   // one list per head each
         const size_t c = (size_t)n_sel * (size_t)std::max<int64_t>(n_wg, 1) * k;
         uintptr_t w = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
         uint64_t *ck = reinterpret_cast<uint64_t *>(w);
         uint32_t *ci = reinterpret_cast<uint32_t *>(w + round_up(c * 8, 256));
         if (n_wg > 0) {
-            const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)kScoreHeads * dim * 2;
+            const size_t lds = (size_t)kScoreRows * (dim * 2 + 16) + (size_t)kScoreHeads * dim * 2 +
+                               (size_t)kScoreHeads * kWaveK * 12;
             const unsigned grid = (unsigned)n_wg * (unsigned)((n_sel + kScoreHeads - 1) / kScoreHeads);
             hipLaunchKernelGGL(score_wave_topk<false>, dim3(grid), dim3(kWaveThreads), lds, s,
                                static_cast<const uint16_t *>(pooled), n_blocks, dim,
                                static_cast<const uint16_t *>(q_idx), n_sel, k, ck, ci, scores, 0.0f);
             KVT_LAUNCHED("score_wave_topk");
         }
-        hipLaunchKernelGGL(merge_wave_topk, dim3(n_sel), dim3(kMergeWaves * 64), 0, s, ck, ci,
-                           (int)n_wg, k, ids);
+        if (n_wg <= 32)
+            hipLaunchKernelGGL(merge_wave_topk<8>, dim3(n_sel), dim3(8 * 64), 0, s, ck, ci,
+                               (int)n_wg, k, ids);
+        else
+            hipLaunchKernelGGL(merge_wave_topk<16>, dim3(n_sel), dim3(16 * 64), 0, s, ck, ci,
+                               (int)n_wg, k, ids);
         KVT_LAUNCHED("merge_wave_topk");
         return KVT_OK;
     }
@@ -647,8 +675,9 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
     uint64_t *b_key = reinterpret_cast<uint64_t *>(w); w += round_up((size_t)n_sel * nb * 8, 256);
     uint32_t *b_id = reinterpret_cast<uint32_t *>(w);
     if (n_blocks > 0) {
-        const int64_t n_wg = (n_blocks + kWaveRows - 1) / kWaveRows;
-        const size_t lds = (size_t)kWaveRows * (dim * 2 + 16) + (size_t)kScoreHeads * dim * 2;
+        const int64_t n_wg = (n_blocks + kScoreRows - 1) / kScoreRows;
+        const size_t lds = (size_t)kScoreRows * (dim * 2 + 16) + (size_t)kScoreHeads * dim * 2 +
+                           (size_t)kScoreHeads * kWaveK * 12;
         const unsigned grid = (unsigned)n_wg * (unsigned)((n_sel + kScoreHeads - 1) / kScoreHeads);
         hipLaunchKernelGGL(score_wave_topk<true>, dim3(grid), dim3(kWaveThreads), lds, s,
                            static_cast<const uint16_t *>(pooled), n_blocks, dim,
