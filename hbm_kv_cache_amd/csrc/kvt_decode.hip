@@ -12,6 +12,8 @@
 //   the probabilities in fp32 avoids rounding them to 16 bits.
 // decode_merge: one thread per (query head, dim) folds the chunks in index order: the global
 //   max first, then every chunk rescaled by e^(m_c - max) -- the same fold, one rescale each.
+//   Its loads are all issued before the max is reduced, one memory round trip for the step's
+//   32 chunks.
 #include <algorithm>
 #include <cmath>
 #include <mutex>
@@ -513,30 +515,85 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
                   part + (((int64_t)row * kvh + h) * n_split + x) * group * (kHd + 2), lane);
 }
 
-// grid = (n_qh, rows), block = kHd.  Two passes over the chunks (global max, then the weighted
-// sums), each with independent loads, in chunk order: deterministic.
+// grid = (n_qh, rows), block = kHd.  The global max of the chunks' m, then the weighted sums
+// in chunk order: deterministic.  Every load of the first kMergeBatch chunks (this thread's
+// output element of each, the m and l of chunk threadIdx.x) is issued before the max is
+// reduced, so up to kMergeBatch chunks take one memory round trip; the weights and l's of a
+// batch of kHd chunks go through LDS.
+constexpr int kMergeBatch = 32;
 __global__ __launch_bounds__(kHd) void decode_merge(const float *__restrict__ part, int group,
                                                     int n_chunks, float *__restrict__ out)
 {
+    __shared__ float s_w[kHd], s_l[kHd], s_max[kHd / 64];
     const int qh = blockIdx.x, d = threadIdx.x, n_qh = gridDim.x;
     const int h = qh / group, r = qh % group;
     part += (int64_t)blockIdx.y * n_qh * n_chunks * (kHd + 2);
     out += (int64_t)blockIdx.y * n_qh * kHd;
+    if (n_chunks <= 0) {
+        out[(int64_t)qh * kHd + d] = 0.f;
+        return;
+    }
     const float *base = part + ((int64_t)h * n_chunks * group + r) * (kHd + 2);
     const int64_t cstride = (int64_t)group * (kHd + 2);
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int c = 0; c < n_chunks; c++)
+    // chunk indices are clamped, so every load is unconditional; the empty asm takes the
+    // values as operands, which keeps the loads here, ahead of the reduction (the compiler
+    // would otherwise sink them, read-only as they are, to their uses after the barrier)
+    float v[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; j++)
+        v[j] = base[min(j, n_chunks - 1) * cstride + d];
+    const int cd = min(d, n_chunks - 1);
+    float mc = base[cd * cstride + kHd], lc = base[cd * cstride + kHd + 1];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; j++)
+        asm volatile("" : "+v"(v[j]));
+    if (d >= n_chunks) {
+        mc = -INFINITY;
+        lc = 0.f;
+    }
+    float M = fmaxf(-INFINITY, mc);
+    for (int c = d + kHd; c < n_chunks; c += kHd)
         M = fmaxf(M, base[c * cstride + kHd]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        M = fmaxf(M, __shfl_xor(M, o, 64));
+    if ((d & 63) == 0)
+        s_max[d >> 6] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kHd / 64; w++)
+        M = fmaxf(M, s_max[w]);
     float acc = 0.f, l = 0.f;
     if (M != -INFINITY) {
-#pragma unroll 8
-        for (int c = 0; c < n_chunks; c++) {
-            const float *pb = base + c * cstride;
-            const float mc = pb[kHd];
-            const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-            acc = fmaf(pb[d], w, acc);
-            l = fmaf(pb[kHd + 1], w, l);
+        for (int c0 = 0; c0 < n_chunks; c0 += kHd) {
+            const int c = c0 + d;
+            if (c0 > 0) {
+                mc = -INFINITY;
+                lc = 0.f;
+                if (c < n_chunks) {
+                    mc = base[c * cstride + kHd];
+                    lc = base[c * cstride + kHd + 1];
+                }
+            }
+            s_w[d] = c < n_chunks && mc != -INFINITY ? __builtin_amdgcn_exp2f(mc - M) : 0.f;
+            s_l[d] = lc;
+            __syncthreads();
+            const int nb = min(kHd, n_chunks - c0);
+            for (int j0 = 0; j0 < nb; j0 += kMergeBatch) {
+                if (c0 + j0 > 0) {
+#pragma unroll
+                    for (int j = 0; j < kMergeBatch; j++)
+                        v[j] = base[(c0 + j0 + min(j, nb - j0 - 1)) * cstride + d];
+                }
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; j++)
+                    if (j0 + j < nb) {
+                        const float w = s_w[j0 + j];
+                        acc = fmaf(v[j], w, acc);
+                        l = fmaf(s_l[j0 + j], w, l);
+                    }
+            }
+            __syncthreads();
         }
     }
     out[(int64_t)qh * kHd + d] = l > 0.f ? acc / l : 0.f;
