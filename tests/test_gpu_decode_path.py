@@ -45,6 +45,22 @@ def test_index_topk_bit_exact(gpu, n_blocks, k):
     assert np.array_equal(ids, oracle.topk(ref_scores, k))
 
 
+@pytest.mark.parametrize("dim,n_sel,n_blocks,k", [(8, 5, 300, 32), (64, 32, 1000, 32),
+                                                   (136, 7, 257, 32), (256, 3, 2000, 32),
+                                                   (256, 5, 3000, 100), (136, 1, 129, 7)])
+def test_index_topk_other_dims_and_head_counts(gpu, dim, n_sel, n_blocks, k):
+    """Row widths that take one, a partial or two 128-element register batches of the scoring
+    chain; head counts that leave a scoring workgroup's second head empty; both selection
+    paths."""
+    g = synth.rng(4, synth.P_POOLED, 1000 * dim + n_sel)
+    pooled = synth.f16_normal(g, (n_blocks, dim))
+    q_idx = synth.f16_normal(synth.rng(4, synth.P_QIDX, dim), (n_sel, dim))
+    ids, scores = _run_topk(pooled, q_idx, k, gpu)
+    ref_scores = oracle.index_scores(pooled, q_idx)
+    assert np.array_equal(scores, ref_scores)
+    assert np.array_equal(ids, oracle.topk(ref_scores, k))
+
+
 def test_index_topk_ties_nans_and_duplicates(gpu):
     g = synth.rng(4, synth.P_MISC, 1)
     n_blocks = 3000
