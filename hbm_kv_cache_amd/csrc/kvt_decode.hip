@@ -515,8 +515,8 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
                   part + (((int64_t)row * kvh + h) * n_split + x) * group * (kHd + 2), lane);
 }
 
-// grid = (n_qh, rows), block = kHd.  The global max of the chunks' m, then the weighted sums
-// in chunk order: deterministic.  Every load of the first kMergeBatch chunks (this thread's
+// grid = (n_qh, 1), block = kHd (one row: few workgroups, latency-bound).  The global max of the
+// chunks' m, then the weighted sums in chunk order: deterministic.  Every load of the first kMergeBatch chunks (this thread's
 // output element of each, the m and l of chunk threadIdx.x) is issued before the max is
 // reduced, so up to kMergeBatch chunks take one memory round trip; the weights and l's of a
 // batch of kHd chunks go through LDS.
@@ -535,13 +535,13 @@ __global__ __launch_bounds__(kHd) void decode_merge(const float *__restrict__ pa
     }
     const float *base = part + ((int64_t)h * n_chunks * group + r) * (kHd + 2);
     const int64_t cstride = (int64_t)group * (kHd + 2);
-    // chunk indices are clamped, so every load is unconditional; the empty asm takes the
+    // the loads past the last chunk are skipped (a uniform condition); the empty asm takes the
     // values as operands, which keeps the loads here, ahead of the reduction (the compiler
     // would otherwise sink them, read-only as they are, to their uses after the barrier)
     float v[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; j++)
-        v[j] = base[min(j, n_chunks - 1) * cstride + d];
+        v[j] = j < n_chunks ? base[j * cstride + d] : 0.f;
     const int cd = min(d, n_chunks - 1);
     float mc = base[cd * cstride + kHd], lc = base[cd * cstride + kHd + 1];
 #pragma unroll
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(kHd) void decode_merge(const float *__restrict__ pa
                 if (c0 + j0 > 0) {
 #pragma unroll
                     for (int j = 0; j < kMergeBatch; j++)
-                        v[j] = base[(c0 + j0 + min(j, nb - j0 - 1)) * cstride + d];
+                        v[j] = j0 + j < nb ? base[(c0 + j0 + j) * cstride + d] : 0.f;
                 }
 #pragma unroll
                 for (int j = 0; j < kMergeBatch; j++)
@@ -594,6 +594,38 @@ __global__ __launch_bounds__(kHd) void decode_merge(const float *__restrict__ pa
                     }
             }
             __syncthreads();
+        }
+    }
+    out[(int64_t)qh * kHd + d] = l > 0.f ? acc / l : 0.f;
+}
+
+// grid = (n_qh, rows) with many rows, block = kHd: the same fold as decode_merge in two
+// streaming passes over the chunks (global max, then the weighted sums, eight loads in flight),
+// with no barrier: many workgroups share each CU, so this form keeps fewer instructions per
+// output instead of taking one round trip per workgroup.  Same operations in the same order as
+// decode_merge: the two give the same bits.
+__global__ __launch_bounds__(kHd) void decode_merge_rows(const float *__restrict__ part, int group,
+                                                    int n_chunks, float *__restrict__ out)
+{
+    const int qh = blockIdx.x, d = threadIdx.x, n_qh = gridDim.x;
+    const int h = qh / group, r = qh % group;
+    part += (int64_t)blockIdx.y * n_qh * n_chunks * (kHd + 2);
+    out += (int64_t)blockIdx.y * n_qh * kHd;
+    const float *base = part + ((int64_t)h * n_chunks * group + r) * (kHd + 2);
+    const int64_t cstride = (int64_t)group * (kHd + 2);
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int c = 0; c < n_chunks; c++)
+        M = fmaxf(M, base[c * cstride + kHd]);
+    float acc = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+        for (int c = 0; c < n_chunks; c++) {
+            const float *pb = base + c * cstride;
+            const float mc = pb[kHd];
+            const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+            acc = fmaf(pb[d], w, acc);
+            l = fmaf(pb[kHd + 1], w, l);
         }
     }
     out[(int64_t)qh * kHd + d] = l > 0.f ? acc / l : 0.f;
@@ -954,8 +986,12 @@ int launch_rows(const char *fn, const RowsArgs &a, const void *kp, const void *v
                : launch(gather_decode_partial<false, true, false>);
     }
     KVT_LAUNCHED("gather_decode_partial");
-    hipLaunchKernelGGL(decode_merge, dim3(a.n_qh, a.rows), dim3(kHd), 0, s, part, group, splits,
-                       a.out);
+    if (a.rows == 1)
+        hipLaunchKernelGGL(decode_merge, dim3(a.n_qh, 1), dim3(kHd), 0, s, part, group, splits,
+                           a.out);
+    else
+        hipLaunchKernelGGL(decode_merge_rows, dim3(a.n_qh, a.rows), dim3(kHd), 0, s, part, group,
+                           splits, a.out);
     KVT_LAUNCHED("decode_merge");
     (void)fn;
     return KVT_OK;

@@ -161,83 +161,103 @@ __device__ __forceinline__ float f16_product(_Float16 a, _Float16 b, float zero)
     return __builtin_fmaf((float)a, (float)b, zero);
 }
 
-// A scoring workgroup takes 128 pooled rows and kScoreHeads heads, two waves per head (rows
-// 0..63 and 64..127), four waves in all: the scoring chains and sorts spread over many CUs at
-// one wave per SIMD (the loop is VALU-bound).  The two waves of a head merge their best-32
-// lists in LDS, so the merge kernel reads one list per 128 rows.
-constexpr int kScoreRows = 2 * kWaveRows;
-constexpr int kScoreHeads = 2;
-constexpr int kWaveThreads = kScoreHeads * 2 * 64;
-// grid.x = n_rg * ceil(n_sel / kScoreHeads) with n_rg = ceil(n_blocks / 128): row group
+// Scoring workgroup shapes.  The list path (k <= 32) takes 128 pooled rows and two heads, two
+// waves per head (rows 0..63 and 64..127), four waves in all: the scoring chains and sorts
+// spread over many CUs at one wave per SIMD (the loop is VALU-bound), and the two waves of a
+// head merge their best-32 lists in LDS, so the merge kernel reads one list per 128 rows.  The
+// keys-only path (the selection path's input) has no lists to merge: 64 rows and eight heads,
+// a wave per head, so each staged row serves eight chains.
+template <bool kKeysOnly>
+struct ScoreShape {
+    static constexpr int kParts = kKeysOnly ? 1 : 2;       // waves per head, 64 rows each
+    static constexpr int kHeads = kKeysOnly ? 8 : 2;       // heads per workgroup
+    static constexpr int kRows = kParts * kWaveRows;
+    static constexpr int kThreads = kHeads * kParts * 64;
+    // 16-byte words of the row and the query held in registers per batch of the scoring chain:
+    // the list path runs one workgroup per CU at a time and takes 128 elements a batch; the
+    // keys-only path runs many workgroups per CU and keeps to fewer registers
+    static constexpr int kBatch = kKeysOnly ? 8 : 16;
+    static size_t lds_bytes(int dim)
+    {
+        return (size_t)kRows * (dim * 2 + 16) + (size_t)kHeads * dim * 2 +
+               (kKeysOnly ? 0 : (size_t)kHeads * kWaveK * 12);
+    }
+};
+constexpr int kScoreRows = ScoreShape<false>::kRows;   // rows per candidate list
+// grid.x = n_rg * ceil(n_sel / kHeads) with n_rg = ceil(n_blocks / kRows): row group
 // blockIdx.x % n_rg, head group blockIdx.x / n_rg.  Workgroups go to the eight XCDs in turn, so
 // with n_rg a multiple of 8 every head group of a row group runs on one XCD and its rows come
-// from HBM once.  LDS: 128 padded rows, the group's index queries (fp16), the upper waves' lists.
+// from HBM once.  LDS: the padded rows, the group's index queries (fp16), the upper waves' lists.
 // kKeysOnly: write every row's rank key to cand_key[h][n_blocks] (ids implicit) instead of the
 // sorted best-k candidate lists [h][n_rg][k] -- the input of the selection path.
 template <bool kKeysOnly>
-__global__ __launch_bounds__(kWaveThreads) void score_wave_topk(
+__global__ __launch_bounds__(ScoreShape<kKeysOnly>::kThreads) void score_wave_topk(
     const uint16_t *__restrict__ pooled, int64_t n_blocks, int dim,
     const uint16_t *__restrict__ q_idx, int n_sel, int k, uint64_t *__restrict__ cand_key,
     uint32_t *__restrict__ cand_id, double *__restrict__ scores_out, float zero)
 {
+    using Sh = ScoreShape<kKeysOnly>;
+    constexpr int kRows = Sh::kRows, kHeads = Sh::kHeads, kParts = Sh::kParts;
+    constexpr int kThreads = Sh::kThreads;
     extern __shared__ __align__(16) unsigned char lds[];
     const int pitch = dim * 2 + 16;
     unsigned char *rows = lds;
-    uint16_t *qs = reinterpret_cast<uint16_t *>(lds + kScoreRows * pitch);
-    uint64_t *list_key = reinterpret_cast<uint64_t *>(lds + kScoreRows * pitch + kScoreHeads * dim * 2);
-    uint32_t *list_id = reinterpret_cast<uint32_t *>(list_key + kScoreHeads * kWaveK);
-    const unsigned n_rg = (unsigned)((n_blocks + kScoreRows - 1) / kScoreRows);
+    uint16_t *qs = reinterpret_cast<uint16_t *>(lds + kRows * pitch);
+    uint64_t *list_key = reinterpret_cast<uint64_t *>(lds + kRows * pitch + kHeads * dim * 2);
+    uint32_t *list_id = reinterpret_cast<uint32_t *>(list_key + kHeads * kWaveK);
+    const unsigned n_rg = (unsigned)((n_blocks + kRows - 1) / kRows);
     const unsigned rg = blockIdx.x % n_rg;
-    const int h0 = (int)(blockIdx.x / n_rg) * kScoreHeads;
-    const int64_t b0 = (int64_t)rg * kScoreRows;
-    const int nrows = (int)std::min<int64_t>(kScoreRows, n_blocks - b0);
+    const int h0 = (int)(blockIdx.x / n_rg) * kHeads;
+    const int64_t b0 = (int64_t)rg * kRows;
+    const int nrows = (int)std::min<int64_t>(kRows, n_blocks - b0);
     const int wpr = dim / 8;
 
     // every load is issued unconditionally (tail rows re-read the last valid row)
-    constexpr int kMaxWordsPerThread = kScoreRows * (256 / 8) / kWaveThreads;   // 16
+    constexpr int kMaxWordsPerThread = kRows * (256 / 8) / kThreads;   // 16 or 4
     u32x4 v[kMaxWordsPerThread];
 #pragma unroll
     for (int u = 0; u < kMaxWordsPerThread; u++) {
-        const int w = threadIdx.x + u * kWaveThreads;
+        const int w = threadIdx.x + u * kThreads;
         const int r = min(w / wpr, nrows - 1), c = w % wpr;
-        if (w < kScoreRows * wpr)
+        if (w < kRows * wpr)
             v[u] = *reinterpret_cast<const u32x4 *>(pooled + (b0 + r) * dim + c * 8);
     }
 #pragma unroll
     for (int u = 0; u < kMaxWordsPerThread; u++) {
-        const int w = threadIdx.x + u * kWaveThreads;
-        if (w < kScoreRows * wpr)
+        const int w = threadIdx.x + u * kThreads;
+        if (w < kRows * wpr)
             *reinterpret_cast<u32x4 *>(rows + (w / wpr) * pitch + (w % wpr) * 16) = v[u];
     }
-    const int nh = std::min(kScoreHeads, n_sel - h0);
-    for (int e = threadIdx.x; e < nh * dim; e += kWaveThreads)
+    const int nh = std::min(kHeads, n_sel - h0);
+    for (int e = threadIdx.x; e < nh * dim; e += kThreads)
         qs[e] = q_idx[h0 * dim + e];
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int hl = wave >> 1, part = wave & 1;   // head in the group, row half
+    const int hl = wave / kParts, part = wave % kParts;   // head in the group, row half
     const int row = part * kWaveRows + lane;
     const bool valid = row < nrows;
     const unsigned char *my_row = rows + row * pitch;
     uint64_t key = 0;
     uint32_t id = kNoId;
-    // lane l of a wave scores its row for one head, one fp64 chain in index order.  Up to 128
-    // elements of the row and the query are read into registers at once, so the chain waits on
-    // LDS once per 128 elements.
+    // lane l of a wave scores its row for one head, one fp64 chain in index order.  kBatch words
+    // (8 elements each) of the row and the query are read into registers at once, so the chain
+    // waits on LDS once per batch.
     if (hl < nh) {
         const int h = h0 + hl;
         const unsigned char *q_row = reinterpret_cast<const unsigned char *>(qs + hl * dim);
         double acc = 0.0;
-        for (int c0 = 0; c0 < wpr; c0 += 16) {
-            u32x4 kw[16], qw[16];
+        constexpr int kBatch = Sh::kBatch;
+        for (int c0 = 0; c0 < wpr; c0 += kBatch) {
+            u32x4 kw[kBatch], qw[kBatch];
 #pragma unroll
-            for (int j = 0; j < 16; j++) {   // words past the row re-read its last word, unused
+            for (int j = 0; j < kBatch; j++) {   // words past the row re-read its last word, unused
                 const int c = min(c0 + j, wpr - 1);
                 kw[j] = *reinterpret_cast<const u32x4 *>(my_row + c * 16);
                 qw[j] = *reinterpret_cast<const u32x4 *>(q_row + c * 16);
             }
 #pragma unroll
-            for (int j = 0; j < 16; j++)
+            for (int j = 0; j < kBatch; j++)
                 if (c0 + j < wpr)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {   // word e: elements 2e (low half), 2e + 1
@@ -647,10 +667,9 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
         uint64_t *ck = reinterpret_cast<uint64_t *>(w);
         uint32_t *ci = reinterpret_cast<uint32_t *>(w + round_up(c * 8, 256));
         if (n_wg > 0) {
-            const size_t lds = (size_t)kScoreRows * (dim * 2 + 16) + (size_t)kScoreHeads * dim * 2 +
-                               (size_t)kScoreHeads * kWaveK * 12;
-            const unsigned grid = (unsigned)n_wg * (unsigned)((n_sel + kScoreHeads - 1) / kScoreHeads);
-            hipLaunchKernelGGL(score_wave_topk<false>, dim3(grid), dim3(kWaveThreads), lds, s,
+            using Sh = ScoreShape<false>;
+            const unsigned grid = (unsigned)n_wg * (unsigned)((n_sel + Sh::kHeads - 1) / Sh::kHeads);
+            hipLaunchKernelGGL(score_wave_topk<false>, dim3(grid), dim3(Sh::kThreads), Sh::lds_bytes(dim), s,
                                static_cast<const uint16_t *>(pooled), n_blocks, dim,
                                static_cast<const uint16_t *>(q_idx), n_sel, k, ck, ci, scores, 0.0f);
             KVT_LAUNCHED("score_wave_topk");
@@ -675,11 +694,10 @@ extern "C" int kvt_index_topk(const void *pooled, int64_t n_blocks, int32_t dim,
     uint64_t *b_key = reinterpret_cast<uint64_t *>(w); w += round_up((size_t)n_sel * nb * 8, 256);
     uint32_t *b_id = reinterpret_cast<uint32_t *>(w);
     if (n_blocks > 0) {
-        const int64_t n_wg = (n_blocks + kScoreRows - 1) / kScoreRows;
-        const size_t lds = (size_t)kScoreRows * (dim * 2 + 16) + (size_t)kScoreHeads * dim * 2 +
-                           (size_t)kScoreHeads * kWaveK * 12;
-        const unsigned grid = (unsigned)n_wg * (unsigned)((n_sel + kScoreHeads - 1) / kScoreHeads);
-        hipLaunchKernelGGL(score_wave_topk<true>, dim3(grid), dim3(kWaveThreads), lds, s,
+        using Sh = ScoreShape<true>;
+        const int64_t n_wg = (n_blocks + Sh::kRows - 1) / Sh::kRows;
+        const unsigned grid = (unsigned)n_wg * (unsigned)((n_sel + Sh::kHeads - 1) / Sh::kHeads);
+        hipLaunchKernelGGL(score_wave_topk<true>, dim3(grid), dim3(Sh::kThreads), Sh::lds_bytes(dim), s,
                            static_cast<const uint16_t *>(pooled), n_blocks, dim,
                            static_cast<const uint16_t *>(q_idx), n_sel, k, all_key, nullptr,
                            scores, 0.0f);

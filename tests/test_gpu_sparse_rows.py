@@ -79,6 +79,25 @@ def test_sparse_rows_match_oracle(gpu, fmt, R, n_qh, kvh, k_pad, per_row):
     host.free()
 
 
+@pytest.mark.parametrize("fmt", [kvt.BF16, kvt.F16], ids=["bf16", "f16"])
+def test_single_row_merge_equals_multi_row_merge(gpu, fmt):
+    """One row folds its chunk partials in the one-row merge kernel, several rows in the
+    streaming merge kernel: with the same chunk split (few rows, one chunk per workgroup) each
+    row of a multi-row call equals the same row computed alone, bit for bit."""
+    kvh, ps, R, n_qh, k_pad = 8, 16, 3, 64, 2080     # 33 chunks: a second batch of one chunk
+    host, planes, q, table, pos, n_rows, row, cols = _setup(gpu, 256, ps, kvh, R, n_qh, k_pad,
+                                                            3000, fmt, 91)
+    pos[1, :] = -1                                   # an empty row
+    many = _run(gpu, host, q, table, pos, n_rows, row, cols, kvh, ps, fmt)
+    for r in range(R):
+        one = _run(gpu, host, q[r:r + 1], table[r:r + 1], pos[r:r + 1], n_rows, row, cols, kvh,
+                   ps, fmt)
+        assert np.array_equal(one[0], many[r]), r
+    assert (many[1] == 0).all()
+    del planes
+    host.free()
+
+
 def test_sparse_rows_without_table(gpu):
     kvh, ps, R, n_qh, k_pad = 4, 16, 5, 16, 100
     host, planes, q, _, pos, n_rows, row, _ = _setup(gpu, 64, ps, kvh, R, n_qh, k_pad, 1024,
