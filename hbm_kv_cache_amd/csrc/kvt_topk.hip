@@ -7,16 +7,18 @@
 // so the value is fully determined and the selection is reproducible bit for bit.
 //
 // Wavefront path (k <= 32, the decode case):
-//   score_wave_topk -- a workgroup stages 64 pooled rows and two heads' index queries in LDS;
-//     lane l of a wave scores row l for one head, so a head's 64 candidates sit one per lane
-//     and a 64-lane bitonic sort over cross-lane shuffles (no barriers) leaves the best k in
-//     lanes 0..k-1, written out as a sorted candidate list.
+//   score_wave_topk -- a workgroup stages 128 pooled rows and two heads' index queries in LDS;
+//     lane l of a wave scores one row for one head, so 64 of a head's candidates sit one per
+//     lane and a 64-lane bitonic sort over cross-lane shuffles (no barriers) leaves the best 32
+//     in lanes 0..31; the head's two waves merge their lists in LDS and write the best k as a
+//     sorted candidate list.
 //   merge_wave_topk -- one workgroup per head; each half-wave folds candidate lists into its
 //     running best-32 (each incoming list read in reverse order, so the better entry of every
 //     lane pair is a bitonic sequence, cleaned in five shuffle steps), then the halves and the
 //     8 or 16 waves fold pairwise, and the winners' ids are sorted ascending by one more lane sort.
 // Selection path (32 < k <= 2048):
-//   score_wave_topk<true> -- the same scoring, writing every rank key;  select_level -- exact
+//   score_wave_topk<true> -- the same scoring (64 rows, eight heads per workgroup), writing
+//     every rank key;  select_level -- exact
 //     selection by bisection over the (key, id) composite, per segment of up to 4096 keys, then
 //     once more over the survivors (up to 8192), whose output is already in id order.
 //
