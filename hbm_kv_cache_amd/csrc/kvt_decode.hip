@@ -4,7 +4,7 @@
 // yields a partial (o, m, l) and the partials are folded with the online-softmax rule
 // (m' = max, alpha = e^(m - m'), beta = e^(m_c - m'), a chunk with m = -inf contributes 0).
 //
-// decode_partial: one wavefront per (64-key chunk, KV head).  All of the chunk's K (as MFMA B
+// decode_partial: one wavefront per (64-key chunk, KV head, block of four query rows).  All of the chunk's K (as MFMA B
 //   operands, straight from HBM) and V (staged in LDS) loads are issued up front.  The group's
 //   query heads (padded to 16 rows) times K^T run on v_mfma_f32_16x16x32_{bf16,f16}: bf16/f16
 //   products are exact in fp32, accumulation is fp32.  Softmax and P*V stay in fp32 on the
@@ -71,12 +71,15 @@ __device__ __forceinline__ void state_init(ChunkState &st)
 }
 
 // kb: sub-tile t's K as MFMA B operands (lane (g, col): key 16t + col, dims ks*32 + 8g ..);
-// vs: the chunk's V rows in LDS; ps [16][16] and as [16]: per-sub-tile LDS scratch.
+// vs: the chunk's V rows in LDS; ps [16][16] and as [16]: per-sub-tile LDS scratch.  The output
+// rows kept (rescaled and accumulated) are the blocks of four [4*q4_lo, 4*q4_hi); every row's
+// arithmetic is its own, so a wave may keep a part of the group's rows.
 template <bool kBf16>
 __device__ __forceinline__ void subtile_attend(int t, const uint4 (&qa)[4], const uint4 (&kb)[4],
                                                uint64_t valid, int group, float scale_log2,
                                                const unsigned char *vs, float (*ps)[16],
-                                               float *as, ChunkState &st, int lane)
+                                               float *as, ChunkState &st, int lane,
+                                               int q4_lo = 0, int q4_hi = 4)
 {
     const int g = lane >> 4, col = lane & 15;
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -122,10 +125,10 @@ __device__ __forceinline__ void subtile_attend(int t, const uint4 (&qa)[4], cons
     }
     __syncthreads();   // ps, as visible to the whole wave
 
-    const int nq4 = (group + 3) >> 2;   // float4 groups of rows actually used
+    const int nq4 = min((group + 3) >> 2, q4_hi);   // float4 groups of rows kept
 #pragma unroll
     for (int q4 = 0; q4 < 4; q4++) {
-        if (q4 < nq4) {
+        if (q4 >= q4_lo && q4 < nq4) {
             const float4 a = *reinterpret_cast<const float4 *>(&as[4 * q4]);
             const float ar[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
@@ -143,7 +146,7 @@ __device__ __forceinline__ void subtile_attend(int t, const uint4 (&qa)[4], cons
         const float v1 = to_f32((uint16_t)(pair >> 16), kBf16);
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
-            if (q4 < nq4) {
+            if (q4 >= q4_lo && q4 < nq4) {
                 const float4 p = *reinterpret_cast<const float4 *>(&ps[key][4 * q4]);
                 const float pr[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
@@ -156,18 +159,18 @@ __device__ __forceinline__ void subtile_attend(int t, const uint4 (&qa)[4], cons
     }
 }
 
-// the chunk's partial (o, m, l) for the group's query rows
+// the chunk's partial (o, m, l) for the group's query rows [4*q4_lo, 4*q4_hi)
 __device__ __forceinline__ void write_partial(const ChunkState &st, int group, float *pb,
-                                              int lane)
+                                              int lane, int q4_lo = 0, int q4_hi = 4)
 {
     const int g = lane >> 4, col = lane & 15;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-        if (r < group)
+        if (r < group && r >= 4 * q4_lo && r < 4 * q4_hi)
             *reinterpret_cast<float2 *>(pb + r * (kHd + 2) + 2 * lane) =
                 make_float2(st.o[r][0], st.o[r][1]);
     }
-    if (col == 0) {
+    if (col == 0 && g >= q4_lo && g < q4_hi) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int r = 4 * g + i;
@@ -191,7 +194,10 @@ __device__ __forceinline__ void load_q(const uint16_t *__restrict__ q, int h, in
         qa[ks] = *reinterpret_cast<const uint4 *>(qh + ks * 32);
 }
 
-// part layout: [kvh][n_chunks][group][kHd + 2]  (o[kHd], m, l); m, l in the log2 domain
+// part layout: [kvh][n_chunks][group][kHd + 2]  (o[kHd], m, l); m, l in the log2 domain.
+// grid = (chunks, kvh, ceil(group / 4)): the query rows of a KV head are split over waves in
+// blocks of four (each wave loads the chunk's K and V, the later ones from L2), which divides
+// the VALU work of the PV product -- the wave's critical path once its loads have landed.
 template <bool kBf16>
 __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict__ q, int group,
                                                      const uint16_t *__restrict__ k,
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
     __shared__ __align__(16) float ps[16][16];   // a sub-tile's probabilities, key-major
     __shared__ __align__(16) float as[16];       // a sub-tile's rescale factors per row
     const int lane = threadIdx.x;
-    const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x;
+    const int c = blockIdx.x, h = blockIdx.y, n_chunks = gridDim.x, q4 = blockIdx.z;
     const int64_t key0 = (int64_t)c * kKeys;
     const int g = lane >> 4, col = lane & 15;
 
@@ -250,9 +256,11 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
 #pragma unroll
     for (int t = 0; t < 4; t++) {
         __syncthreads();   // V rows (t = 0) / the previous sub-tile's ps, as reads are done
-        subtile_attend<kBf16>(t, qa, kb[t], valid, group, scale_log2, vs, ps, as, st, lane);
+        subtile_attend<kBf16>(t, qa, kb[t], valid, group, scale_log2, vs, ps, as, st, lane, q4,
+                              q4 + 1);
     }
-    write_partial(st, group, part + ((int64_t)h * n_chunks + c) * group * (kHd + 2), lane);
+    write_partial(st, group, part + ((int64_t)h * n_chunks + c) * group * (kHd + 2), lane, q4,
+                  q4 + 1);
 }
 
 // How a selected slot id becomes the byte offset of its block (token_stride apart rows).
@@ -670,13 +678,14 @@ extern "C" int kvt_attn_decode(const void *q, int32_t n_qh, int32_t kvh, int32_t
     float *part = static_cast<float *>(ws);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
     if (chunks > 0) {
+        const dim3 grid((unsigned)chunks, kvh, (group + 3) / 4);
         if (dtype == KVT_BF16)
-            hipLaunchKernelGGL(decode_partial<true>, dim3((unsigned)chunks, kvh), dim3(64), 0, s,
+            hipLaunchKernelGGL(decode_partial<true>, grid, dim3(64), 0, s,
                                static_cast<const uint16_t *>(q), group,
                                static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
                                n_kv, n_valid, scale_log2, part);
         else
-            hipLaunchKernelGGL(decode_partial<false>, dim3((unsigned)chunks, kvh), dim3(64), 0, s,
+            hipLaunchKernelGGL(decode_partial<false>, grid, dim3(64), 0, s,
                                static_cast<const uint16_t *>(q), group,
                                static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
                                n_kv, n_valid, scale_log2, part);
