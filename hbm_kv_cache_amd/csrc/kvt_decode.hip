@@ -70,6 +70,32 @@ __device__ __forceinline__ void state_init(ChunkState &st)
         st.o[r][0] = st.o[r][1] = 0.f;
 }
 
+// The value lane ^ off holds, for off = 1, 2, 4, 8 (inside a row of 16 lanes), by DPP: quad
+// permutes for 1 and 2, row shifts up or down by off for 4 and 8.  The same values as
+// __shfl_xor, without the LDS permute and its latency.
+__device__ __forceinline__ float xor16(float v, int off, int lane)
+{
+    const int x = __builtin_bit_cast(int, v);
+    int r;
+    switch (off) {
+    case 1: r = __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false); break;   // [1,0,3,2]
+    case 2: r = __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false); break;   // [2,3,0,1]
+    case 4: {
+        const int up = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0xF, false);  // lane + 4
+        const int dn = __builtin_amdgcn_update_dpp(x, x, 0x114, 0xF, 0xF, false);  // lane - 4
+        r = (lane & 4) ? dn : up;
+        break;
+    }
+    default: {
+        const int up = __builtin_amdgcn_update_dpp(x, x, 0x108, 0xF, 0xF, false);  // lane + 8
+        const int dn = __builtin_amdgcn_update_dpp(x, x, 0x118, 0xF, 0xF, false);  // lane - 8
+        r = (lane & 8) ? dn : up;
+        break;
+    }
+    }
+    return __builtin_bit_cast(float, r);
+}
+
 // kb: sub-tile t's K as MFMA B operands (lane (g, col): key 16t + col, dims ks*32 + 8g ..);
 // vs: the chunk's V rows in LDS; ps [16][16] and as [16]: per-sub-tile LDS scratch.  The output
 // rows kept (rescaled and accumulated) are the blocks of four [4*q4_lo, 4*q4_hi); every row's
@@ -99,7 +125,7 @@ __device__ __forceinline__ void subtile_attend(int t, const uint4 (&qa)[4], cons
     for (int off = 1; off < 16; off <<= 1)
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            mt[i] = fmaxf(mt[i], __shfl_xor(mt[i], off, 64));
+            mt[i] = fmaxf(mt[i], xor16(mt[i], off, lane));
     float alpha[4], ls[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -114,7 +140,7 @@ __device__ __forceinline__ void subtile_attend(int t, const uint4 (&qa)[4], cons
     for (int off = 1; off < 16; off <<= 1)
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            ls[i] += __shfl_xor(ls[i], off, 64);
+            ls[i] += xor16(ls[i], off, lane);
 #pragma unroll
     for (int i = 0; i < 4; i++)
         st.l[i] = fmaf(st.l[i], alpha[i], ls[i]);
@@ -138,21 +164,32 @@ __device__ __forceinline__ void subtile_attend(int t, const uint4 (&qa)[4], cons
             }
         }
     }
-#pragma unroll 4
-    for (int key = 0; key < 16; key++) {
-        const uint32_t pair =
-            *reinterpret_cast<const uint32_t *>(vs + (16 * t + key) * kVPitch + lane * 4);
-        const float v0 = to_f32((uint16_t)(pair & 0xffff), kBf16);
-        const float v1 = to_f32((uint16_t)(pair >> 16), kBf16);
+    // P*V: the sub-tile's 16 V pairs of this lane's two dims, and eight keys' probability vectors
+    // of a row block at a time, are read before the FMAs that use them (a read per FMA group
+    // would wait on LDS each time); every output still sums its keys in order.
+    uint32_t pair[16];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; q4++) {
-            if (q4 >= q4_lo && q4 < nq4) {
-                const float4 p = *reinterpret_cast<const float4 *>(&ps[key][4 * q4]);
-                const float pr[4] = {p.x, p.y, p.z, p.w};
+    for (int key = 0; key < 16; key++)
+        pair[key] = *reinterpret_cast<const uint32_t *>(vs + (16 * t + key) * kVPitch + lane * 4);
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    st.o[4 * q4 + e][0] = fmaf(pr[e], v0, st.o[4 * q4 + e][0]);
-                    st.o[4 * q4 + e][1] = fmaf(pr[e], v1, st.o[4 * q4 + e][1]);
+    for (int q4 = 0; q4 < 4; q4++) {
+        if (q4 >= q4_lo && q4 < nq4) {
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += 8) {
+                float4 p[8];
+#pragma unroll
+                for (int kk = 0; kk < 8; kk++)
+                    p[kk] = *reinterpret_cast<const float4 *>(&ps[k0 + kk][4 * q4]);
+#pragma unroll
+                for (int kk = 0; kk < 8; kk++) {
+                    const float v0 = to_f32((uint16_t)(pair[k0 + kk] & 0xffff), kBf16);
+                    const float v1 = to_f32((uint16_t)(pair[k0 + kk] >> 16), kBf16);
+                    const float pr[4] = {p[kk].x, p[kk].y, p[kk].z, p[kk].w};
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        st.o[4 * q4 + e][0] = fmaf(pr[e], v0, st.o[4 * q4 + e][0]);
+                        st.o[4 * q4 + e][1] = fmaf(pr[e], v1, st.o[4 * q4 + e][1]);
+                    }
                 }
             }
         }
@@ -214,40 +251,35 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
     const int g = lane >> 4, col = lane & 15;
 
     // Every load below is unconditional, from a clamped (always valid) address, so all of them
-    // are in flight together; out-of-range rows are zeroed or masked afterwards.
+    // are in flight together; out-of-range rows are zeroed or masked afterwards.  They are issued
+    // sub-tile by sub-tile (its K operands, then its V rows), so a sub-tile is attended as soon as
+    // its own loads have landed while the later ones are still in flight (loads complete in issue
+    // order for the wait counter); the query and n_valid go first for the same reason.
     uint4 qa[4];
     load_q(q, h, group, lane, qa);
+    int64_t nv = n_valid ? (int64_t)n_valid[h] : n_kv;
     const uint16_t *kh = k + (int64_t)h * n_kv * kHd;
+    const uint16_t *vh = v + (int64_t)h * n_kv * kHd;
     uint4 kb[4][4];
+    uint4 vr[16];
 #pragma unroll
     for (int nt = 0; nt < 4; nt++) {
         const int64_t key = min(key0 + nt * 16 + col, n_kv - 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
             kb[nt][ks] = *reinterpret_cast<const uint4 *>(kh + key * kHd + ks * 32 + 8 * g);
-    }
-    const uint16_t *vh = v + (int64_t)h * n_kv * kHd;
-    uint4 vr[16];
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
-        const int64_t key = min(key0 + row, n_kv - 1);
-        vr[j] = *reinterpret_cast<const uint4 *>(vh + key * kHd + cw * 8);
+        for (int j = 4 * nt; j < 4 * nt + 4; j++) {   // V rows 16 nt .. 16 nt + 15
+            const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
+            const int64_t vkey = min(key0 + row, n_kv - 1);
+            vr[j] = *reinterpret_cast<const uint4 *>(vh + vkey * kHd + cw * 8);
+        }
     }
-    int64_t nv = n_valid ? (int64_t)n_valid[h] : n_kv;
     nv = nv < n_kv ? nv : n_kv;
     if (col >= group) {
 #pragma unroll
         for (int ks = 0; ks < 4; ks++)
             qa[ks] = make_uint4(0, 0, 0, 0);
-    }
-    // V rows of keys that take no part are zeroed: their probability is 0, but 0 * NaN is not
-    // (rows past n_valid may hold anything, e.g. slots a gather skipped)
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
-        const uint4 val = key0 + row < nv ? vr[j] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(vs + row * kVPitch + cw * 16) = val;
     }
     const int64_t nvc = nv - key0;   // keys of this chunk that take part: the first nvc
     const uint64_t valid = nvc >= kKeys ? ~0ull : nvc <= 0 ? 0ull : (1ull << nvc) - 1;
@@ -255,7 +287,15 @@ __global__ __launch_bounds__(64) void decode_partial(const uint16_t *__restrict_
     state_init(st);
 #pragma unroll
     for (int t = 0; t < 4; t++) {
-        __syncthreads();   // V rows (t = 0) / the previous sub-tile's ps, as reads are done
+        // V rows of keys that take no part are zeroed: their probability is 0, but 0 * NaN is
+        // not (rows past n_valid may hold anything, e.g. slots a gather skipped)
+#pragma unroll
+        for (int j = 4 * t; j < 4 * t + 4; j++) {
+            const int w = lane + 64 * j, row = w >> 4, cw = w & 15;
+            const uint4 val = key0 + row < nv ? vr[j] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(vs + row * kVPitch + cw * 16) = val;
+        }
+        __syncthreads();   // the sub-tile's V rows / the previous sub-tile's ps, as reads are done
         subtile_attend<kBf16>(t, qa, kb[t], valid, group, scale_log2, vs, ps, as, st, lane, q4,
                               q4 + 1);
     }
