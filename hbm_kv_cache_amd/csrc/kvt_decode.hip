@@ -4,16 +4,17 @@
 // yields a partial (o, m, l) and the partials are folded with the online-softmax rule
 // (m' = max, alpha = e^(m - m'), beta = e^(m_c - m'), a chunk with m = -inf contributes 0).
 //
-// decode_partial: one wavefront per (64-key chunk, KV head, block of four query rows).  All of the chunk's K (as MFMA B
-//   operands, straight from HBM) and V (staged in LDS) loads are issued up front.  The group's
-//   query heads (padded to 16 rows) times K^T run on v_mfma_f32_16x16x32_{bf16,f16}: bf16/f16
-//   products are exact in fp32, accumulation is fp32.  Softmax and P*V stay in fp32 on the
-//   vector ALUs: with at most 16 query rows per KV head the PV product is tiny, and keeping
-//   the probabilities in fp32 avoids rounding them to 16 bits.
+// decode_partial: one wavefront per (64-key chunk, KV head, block of four query rows).  All of
+//   the chunk's K (as MFMA B operands, straight from HBM) and V (staged in LDS) loads are
+//   issued up front, sub-tile by sub-tile.  The group's query heads (padded to 16 rows) times
+//   K^T run on v_mfma_f32_16x16x32_{bf16,f16}: bf16/f16 products are exact in fp32,
+//   accumulation is fp32.  Softmax and P*V stay in fp32 on the vector ALUs: with at most 16
+//   query rows per KV head the PV product is tiny, and keeping the probabilities in fp32 avoids
+//   rounding them to 16 bits.
 // decode_merge: one thread per (query head, dim) folds the chunks in index order: the global
 //   max first, then every chunk rescaled by e^(m_c - max) -- the same fold, one rescale each.
-//   Its loads are all issued before the max is reduced, one memory round trip for the step's
-//   32 chunks.
+//   One row issues all its loads before the max is reduced (one memory round trip for the
+//   step's 32 chunks); many rows stream (decode_merge_rows), with the same arithmetic.
 #include <algorithm>
 #include <cmath>
 #include <mutex>
@@ -564,10 +565,10 @@ __global__ __launch_bounds__(64) void gather_decode_partial(
 }
 
 // grid = (n_qh, 1), block = kHd (one row: few workgroups, latency-bound).  The global max of the
-// chunks' m, then the weighted sums in chunk order: deterministic.  Every load of the first kMergeBatch chunks (this thread's
-// output element of each, the m and l of chunk threadIdx.x) is issued before the max is
-// reduced, so up to kMergeBatch chunks take one memory round trip; the weights and l's of a
-// batch of kHd chunks go through LDS.
+// chunks' m, then the weighted sums in chunk order: deterministic.  Every load of the first
+// kMergeBatch chunks (this thread's output element of each, the m and l of chunk threadIdx.x)
+// is issued before the max is reduced, so up to kMergeBatch chunks take one memory round trip;
+// the weights and l's of a batch of kHd chunks go through LDS.
 constexpr int kMergeBatch = 32;
 __global__ __launch_bounds__(kHd) void decode_merge(const float *__restrict__ part, int group,
                                                     int n_chunks, float *__restrict__ out)
