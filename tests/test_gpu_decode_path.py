@@ -34,7 +34,8 @@ def _run_topk(pooled, q_idx, k, dev, want_scores=True):
 
 @pytest.mark.parametrize("n_blocks,k", [(4096, 32), (16384, 32), (5000, 32), (129, 32), (100, 32),
                                         (1, 32), (32, 32), (70000, 32), (3000, 200), (5, 1),
-                                        (65536, 512), (70000, 1000), (5000, 2048), (300, 512)])
+                                        (65536, 512), (70000, 1000), (5000, 2048), (300, 512),
+                                        (65535, 2048), (20000, 1024)])
 def test_index_topk_bit_exact(gpu, n_blocks, k):
     g = synth.rng(4, synth.P_POOLED, n_blocks + k)
     pooled = synth.f16_normal(g, (n_blocks, 128))
