@@ -187,7 +187,8 @@ def _run_decode(q, k, v, fmt, dev, n_valid=None, scale=None):
 @pytest.mark.parametrize("n_qh,kvh,n_kv,fmt", [(64, 8, 2048, kvt.BF16), (64, 8, 2000, kvt.BF16),
                                                (64, 8, 2048, kvt.F16), (8, 8, 300, kvt.BF16),
                                                (32, 2, 1000, kvt.F16), (12, 4, 64, kvt.BF16),
-                                               (16, 1, 4096, kvt.BF16)])
+                                               (16, 1, 4096, kvt.BF16),
+                                               (16, 2, 9000, kvt.F16)])   # 141 chunks to merge
 def test_decode_attention_within_tolerance(gpu, n_qh, kvh, n_kv, fmt):
     q, k, v = _decode_inputs(n_qh, kvh, n_kv, fmt, n_qh * 7 + n_kv)
     got, ref = _run_decode(q, k, v, fmt, gpu)
