@@ -21,6 +21,12 @@
 //     rounding, to nearest): K and V as rows [key][d].  Raw and fp16 tiles
 //     are double buffered: tile t+1 is dequantised while tile t is multiplied, one barrier per
 //     tile, with the loads of tiles t+2 and t+3 in flight;
+//   * fp16 and bf16 slices need no conversion and take another schedule: the waves run as two
+//     groups in alternating phases (waves w and w + 4 share a SIMD).  Waves 0-3 move the K
+//     plane of each tile and lead; waves 4-7 move the V plane and trail by one phase.  A wave's
+//     MFMA phase holds the V P product of the previous tile and the S product of this one, its
+//     VALU phase the softmax step and its plane's store and next load, so on every SIMD one
+//     wave multiplies while the other exponentiates;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (K from LDS, Q held in registers);
 //   * online softmax in fp32 in the log2 domain: p = exp2(s*c - m*c) with the scale c folded
 //     into one FMA and the exponential on the bare v_exp_f32 (results below 2^-126 flush to
@@ -116,6 +122,18 @@ __device__ __forceinline__ void bf16_split(float a, float b, uint32_t &hi, uint3
     const float ha = __builtin_bit_cast(float, hi << 16);
     const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
     lo = bf16_pair(a - ha, b - hb);
+}
+
+// x of lanes 0-31 and of lanes 32-63, each in all 64 lanes, from one v_permlane32_swap (a VALU
+// exchange; no LDS round trip): lo[L] = x[L % 32], hi[L] = x[32 + L % 32].
+__device__ __forceinline__ void wave_halves(float x, float &lo, float &hi)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    // scalar copies first: a bit_cast of a vector element subscript reads element 0
+    const uint32_t a = r[0], b = r[1];
+    lo = __builtin_bit_cast(float, a);
+    hi = __builtin_bit_cast(float, b);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -251,6 +269,76 @@ __device__ __forceinline__ void store_direct(unsigned char *buf,
             unsigned char *dst = buf + (plane ? kLdsK + key * kVPitch : key * kKPitch) + WB * w;
             *reinterpret_cast<typename W::Word *>(dst) = rq[u];
         }
+    }
+}
+
+// One plane (0: K, 1: V) of tile `tile` by the 256 threads of one wave group (gi = thread index
+// in the group): the same coalesced WB-byte words as load_raw, consecutive threads on
+// consecutive words of a head slice.  p_head / p_tail point at this workgroup's head slice.
+// off0: the thread's word offset within a tile, (gi / words per row) * row_bytes + WB * (gi % words
+// per row).  A tile wholly inside one tier and inside the cache takes a scalar base and the fixed
+// per-thread offsets; only the tile that straddles the tiers or the end is addressed row by row.
+template <int F, int WB>
+__device__ __forceinline__ void load_plane(const unsigned char *p_head, const unsigned char *p_tail,
+                                           int64_t n_head, int64_t n_kv, int64_t row_bytes, int tile,
+                                           int gi, uint32_t off0,
+                                           typename Words<F, WB>::Word (&rq)[Words<F, WB>::kPerThread])
+{
+    using R = Raw<F>;
+    using W = Words<F, WB>;
+    constexpr int kPerRow = R::kHeadBytes / WB;
+    constexpr int kRowsPerU = 256 / kPerRow;
+    static_assert(W::kWords / 2 == 256 * W::kPerThread, "a plane is 256 threads' words");
+    const int64_t key0 = (int64_t)tile * kKT;
+    if (key0 + kKT <= n_kv && (key0 + kKT <= n_head || key0 >= n_head)) {
+        // buffer loads: the tile's base in a scalar descriptor, the row step as a scalar offset
+        // and off0 as the only per-thread term (offsets stay below 64 rows, far under the
+        // descriptor's 2^31-byte range)
+        const unsigned char *base = key0 < n_head ? p_head + key0 * row_bytes
+                                                  : p_tail + (key0 - n_head) * row_bytes;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < W::kPerThread; u++) {
+            const int soff = (int)(u * kRowsPerU * row_bytes);
+            if constexpr (WB == 16) {
+                rq[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off0, soff, 2);   // nt
+            } else {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off0, soff, 2);
+                rq[u] = __builtin_bit_cast(uint64_t, x);
+            }
+        }
+        return;
+    }
+    const int kmax = (int)((n_kv - 1 - key0) < kKT - 1 ? (n_kv - 1 - key0) : kKT - 1);
+    const int khead = (int)((n_head - key0) < kKT ? (n_head - key0) : kKT);
+    const unsigned char *hp = p_head + key0 * row_bytes, *tp = p_tail + (key0 - n_head) * row_bytes;
+#pragma unroll
+    for (int u = 0; u < W::kPerThread; u++) {
+        const int f = gi + 256 * u;
+        int kin = f / kPerRow;
+        const int w = f - kin * kPerRow;
+        kin = kin < kmax ? kin : kmax;
+        const uint32_t off = (uint32_t)kin * (uint32_t)row_bytes + (uint32_t)WB * (uint32_t)w;
+        rq[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const typename W::Word *>((kin < khead ? hp : tp) + off));
+    }
+}
+
+// The words of load_plane into their rows of the 16-bit tile in `buf`.
+template <int F, int WB>
+__device__ __forceinline__ void store_plane(unsigned char *buf, int plane, int gi,
+                                            const typename Words<F, WB>::Word (&rq)[Words<F, WB>::kPerThread])
+{
+    using W = Words<F, WB>;
+    constexpr int kPerRow = Raw<F>::kHeadBytes / WB;
+    unsigned char *const base = buf + (plane ? kLdsK : 0);
+    const int pitch = plane ? kVPitch : kKPitch;
+#pragma unroll
+    for (int u = 0; u < W::kPerThread; u++) {
+        const int f = gi + 256 * u;
+        const int key = f / kPerRow, w = f - key * kPerRow;
+        *reinterpret_cast<typename W::Word *>(base + key * pitch + WB * w) = rq[u];
     }
 }
 
@@ -407,19 +495,193 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
     const unsigned char *kt = k_tail + h * R::kHeadBytes, *vt = v_tail + h * R::kHeadBytes;
     typename Words<F, WB>::Word rq[Words<F, WB>::kPerThread];
 
-    // prologue: raw tile b -> LDS; fp16 tile b and raw tile b+1 ready; loads of b+2 in flight
-    // (b = tb; buffers are indexed by tile & 1)
+    // The tile arithmetic, in three steps per tile: S = the tile's logits (MFMA), the online
+    // softmax step (VALU), and O += V P (MFMA).  s carries a tile's logits from the first step to
+    // the second, pk / pl its probabilities from the second to the third.
+    f32x16 s[2];
+    uint32_t pk[2][8];
+    uint32_t pl[2][kBf ? 8 : 1];
+    // S^T tile: rows = keys 32*st + (lane & 31), columns = this wave's 32 query rows
+    auto s_product = [&](const unsigned char *lk) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int kd = 0; kd < 8; kd++) {
+#pragma unroll
+            for (int st = 0; st < 2; st++) {
+                const f16x8 a = *reinterpret_cast<const f16x8 *>(
+                    lk + (32 * st + i) * kKPitch + (16 * kd + 8 * g) * 2);
+                if constexpr (kBf) {
+                    s[st] = mfma32_bf16(a, qb[kd], s[st]);
+                    s[st] = mfma32_bf16(a, qlo[kd], s[st]);
+                } else {
+                    s[st] = mfma32(a, qb[kd], s[st]);
+                }
+            }
+        }
+    };
+    // lane holds S[query i][key0 + 32*st + 8*(r/4) + 4*g + r%4] in s[st][r]
+    auto softmax_step = [&](int64_t key0) {
+        const bool need_mask = key0 + kKT - 1 > (causal ? pos_first : n_kv - 1) ||
+                               key0 + kKT > n_kv;
+        if (need_mask) {
+            // last visible key of this lane's query, relative to the tile, in [-1, 64]
+            int64_t lim = (causal && pos_i < n_kv - 1 ? pos_i : n_kv - 1) - key0;
+            lim = lim < -1 ? -1 : (lim > kKT ? kKT : lim);
+            // the lane's part of the key index (4g) moved to the limit, so each comparison is
+            // against an inline constant rather than a per-element index held in a register
+            const int rel = (int)lim - 4 * g;
+#pragma unroll
+            for (int st = 0; st < 2; st++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    if (32 * st + 8 * (r >> 2) + (r & 3) > rel)
+                        s[st][r] = -INFINITY;
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; st++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                mt = fmaxf(mt, s[st][r]);
+        {
+            float lo, hi;
+            wave_halves(mt, lo, hi);
+            mt = fmaxf(lo, hi);
+        }
+        const float m_new = fmaxf(m, mt);
+        // every logit is scaled by c > 0, so the max commutes with the scaling.  The
+        // probabilities are exp2(s*c - mc) with mc = round(m*c), one rounding (an FMA): they
+        // are relative to the rounded reference, so the state carried from earlier tiles
+        // is rebased by exp2(round(m_old*c) - round(m_new*c)) -- exactly 1 when the max is
+        // unchanged.  Rebasing by exp2(m_old*c - round(m_new*c)) instead would be off by
+        // m_old*c's rounding error: a drift over thousands of tiles for ordinary logits,
+        // and factors of 2^4 and more for logits near 1e8.  Both products are kept whole
+        // (mul_rounded: no fused multiply-add).
+        // alpha without branches: for an unchanged max the exponent is exactly 0 and alpha 1
+        const float mc = m_new == -INFINITY ? 0.f : mul_rounded(m_new, scale_log2);
+        const float ea = __builtin_amdgcn_exp2f(mul_rounded(m, scale_log2) - mc);
+        const float alpha = m == -INFINITY ? 0.f : ea;
+        // probabilities packed in pairs: fp16; for bf16 caches two bf16 parts, pk + pl
+        float psum = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][r], scale_log2, -mc));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][r + 1], scale_log2, -mc));
+                psum += p0 + p1;
+                if constexpr (kBf)
+                    bf16_split(p0, p1, pk[st][r >> 1], pl[st][r >> 1]);
+                else
+                    pk[st][r >> 1] = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector(f32x2{p0, p1}, h2));
+            }
+        }
+        {
+            float lo, hi;
+            wave_halves(psum, lo, hi);
+            psum = lo + hi;   // this lane's sum plus lane (L ^ 32)'s, in either order
+        }
+        l = l * alpha + psum;
+        m = m_new;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    o[dt][r] *= alpha;
+        }
+    };
+    // O^T[d][query] += V^T[d][keys] P^T[keys][query], 16 keys per step
+    auto pv_product = [&](const unsigned char *lv) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            const int st = ks >> 1, r0 = 4 * (ks & 1);
+            const f16x8 pb = __builtin_bit_cast(
+                f16x8, u32x4{pk[st][r0], pk[st][r0 + 1], pk[st][r0 + 2], pk[st][r0 + 3]});
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) {
+                // lane L receives V[16ks + 4g + e][32dt + L % 32], e = 0..3 (and keys + 8):
+                // in its 16-lane group it reads 4 values of row 16ks + 4g + tr_r at column
+                // 32dt + tr_c, and the read transposes them
+                const unsigned char *vp = lv + (16 * ks + 4 * g + tr_r) * kVPitch +
+                                          2 * (32 * dt + tr_c);
+                const f16x4 lo = tr_read(vp), hi = tr_read(vp + 8 * kVPitch);
+                const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                if constexpr (kBf) {
+                    const f16x8 pbl = __builtin_bit_cast(
+                        f16x8, u32x4{pl[st][r0], pl[st][r0 + 1], pl[st][r0 + 2], pl[st][r0 + 3]});
+                    o[dt] = mfma32_bf16(a, pb, o[dt]);
+                    o[dt] = mfma32_bf16(a, pbl, o[dt]);
+                } else {
+                    o[dt] = mfma32(a, pb, o[dt]);
+                }
+            }
+        }
+    };
+
     const int b0 = tb;
     if constexpr (kDirect) {
-        // 16-bit tile b in buffer b & 1; the registers hold tile b + 1
+        // fp16 and bf16 tiles: two wave groups in alternating phases.  Waves w and w + 4 share a
+        // SIMD; waves 0-3 (group 0) move the K plane of every tile and lead, waves 4-7 (group 1)
+        // move the V plane and trail by one phase.  Each tile takes two phases per wave, each
+        // ended by a workgroup barrier:
+        //   MFMA phase of tile t: O += V P for tile t - 1, then S for tile t;
+        //   VALU phase of tile t: the softmax step of tile t; the group's plane of tile t + 1
+        //                         stored from the registers into buffer (t + 1) & 1; the loads
+        //                         of its plane of tile t + 2 issued.
+        // So on every SIMD one wave multiplies while the other runs its softmax step.  Barrier
+        // by barrier: group 0 runs tile t's MFMA phase in interval 2t and its VALU phase in
+        // 2t + 1, group 1 one interval later.  K(t) is read in intervals 2t and 2t + 1 and
+        // K(t + 2) stored into its buffer in 2t + 3; V(t) is stored in 2t and read in 2t + 2
+        // and 2t + 3, V(t + 2) stored in 2t + 4.  Double buffering suffices for both planes.
+        // the group is uniform in a wave: readfirstlane makes its branches scalar, so a wave of
+        // the other group jumps over the extra barriers rather than meeting them with no lanes on
+        const int grp = __builtin_amdgcn_readfirstlane(wave >> 2), gi = threadIdx.x & 255;
+        const unsigned char *ph = grp ? vh : kh, *pt = grp ? vt : kt;
+        constexpr int kPerRow = R::kHeadBytes / WB;
+        const uint32_t off0 = (uint32_t)(gi / kPerRow) * (uint32_t)row_bytes + (uint32_t)(WB * (gi % kPerRow));
         if (n_tiles > b0) {
-            load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
-            store_direct<F, WB>(lds + (b0 & 1) * kLdsBuf, rq);
-            if (n_tiles > b0 + 1)
-                load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 1, rq);
+            load_plane<F, WB>(ph, pt, n_head, n_kv, row_bytes, b0, gi, off0, rq);
+            if (grp == 0) {
+                store_plane<F, WB>(lds + (b0 & 1) * kLdsBuf, 0, gi, rq);
+                if (n_tiles > b0 + 1)
+                    load_plane<F, WB>(ph, pt, n_head, n_kv, row_bytes, b0 + 1, gi, off0, rq);
+            }
         }
         __syncthreads();
+        if (grp == 1) {   // the trailing group's VALU phase of tile b0 - 1: only the moves
+            if (n_tiles > b0) {
+                store_plane<F, WB>(lds + (b0 & 1) * kLdsBuf, 1, gi, rq);
+                if (n_tiles > b0 + 1)
+                    load_plane<F, WB>(ph, pt, n_head, n_kv, row_bytes, b0 + 1, gi, off0, rq);
+            }
+            __syncthreads();
+        }
+        for (int tile = b0; tile < n_tiles; tile++) {
+            const int64_t key0 = (int64_t)tile * kKT;
+            if (tile > b0 && key0 - kKT <= wave_last)
+                pv_product(lds + ((tile - 1) & 1) * kLdsBuf + kLdsK);
+            if (key0 <= wave_last)
+                s_product(lds + (tile & 1) * kLdsBuf);
+            __syncthreads();
+            if (key0 <= wave_last)
+                softmax_step(key0);
+            if (tile + 1 < n_tiles)
+                store_plane<F, WB>(lds + ((tile + 1) & 1) * kLdsBuf, grp, gi, rq);
+            if (tile + 2 < n_tiles)
+                load_plane<F, WB>(ph, pt, n_head, n_kv, row_bytes, tile + 2, gi, off0, rq);
+            __syncthreads();
+        }
+        if (n_tiles > b0 && (int64_t)(n_tiles - 1) * kKT <= wave_last)
+            pv_product(lds + ((n_tiles - 1) & 1) * kLdsBuf + kLdsK);
+        if (grp == 0)   // the leading group matches the trailing group's extra barrier
+            __syncthreads();
+        __syncthreads();   // every product done before the output staging reuses the tiles
     } else {
+        // q8_0: raw tile b -> LDS; fp16 tile b and raw tile b+1 ready; loads of b+2 in flight
+        // (b = tb; buffers are indexed by tile & 1)
         if (n_tiles > b0) {
             load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0, rq);
             store_raw<F, WB>(lds_raw + (b0 & 1) * R::kBytes, rq);
@@ -435,137 +697,25 @@ __global__ __launch_bounds__(kThreads) void prefill_attn(
                 load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, b0 + 2, rq);
         }
         __syncthreads();
-    }
 
-    // per tile: multiply fp16 buffer (tile & 1); dequantise raw tile+1 into the other fp16
-    // buffer; move the registers of tile+2 into the raw buffer tile+1 just left; one barrier;
-    // then issue the loads of tile+3
-    const bool dequant_first = wave >= 4;
-    for (int tile = b0; tile < n_tiles; tile++) {
-        const unsigned char *lk = lds + (tile & 1) * kLdsBuf;
-        const unsigned char *lv = lk + kLdsK;
-        const int64_t key0 = (int64_t)tile * kKT;
-        // Waves w and w + 4 share a SIMD.  The upper four dequantise the next tile before they
-        // multiply this one and the lower four after, so on every SIMD one wave's MFMA work
-        // meets the other's VALU work.
-        if (!kDirect && dequant_first && tile + 1 < n_tiles)
-            dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes, lds + ((tile + 1) & 1) * kLdsBuf,
-                         wave, lane);
-        if (key0 <= wave_last) {
-            // S^T tile: rows = keys 32*st + (lane & 31), columns = this wave's 32 query rows
-            f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int kd = 0; kd < 8; kd++) {
-#pragma unroll
-                for (int st = 0; st < 2; st++) {
-                    const f16x8 a = *reinterpret_cast<const f16x8 *>(
-                        lk + (32 * st + i) * kKPitch + (16 * kd + 8 * g) * 2);
-                    if constexpr (kBf) {
-                        s[st] = mfma32_bf16(a, qb[kd], s[st]);
-                        s[st] = mfma32_bf16(a, qlo[kd], s[st]);
-                    } else {
-                        s[st] = mfma32(a, qb[kd], s[st]);
-                    }
-                }
+        // per tile: multiply fp16 buffer (tile & 1); dequantise raw tile+1 into the other fp16
+        // buffer; move the registers of tile+2 into the raw buffer tile+1 just left; one
+        // barrier; then issue the loads of tile+3
+        const bool dequant_first = wave >= 4;
+        for (int tile = b0; tile < n_tiles; tile++) {
+            const unsigned char *lk = lds + (tile & 1) * kLdsBuf;
+            const int64_t key0 = (int64_t)tile * kKT;
+            // Waves w and w + 4 share a SIMD.  The upper four dequantise the next tile before
+            // they multiply this one and the lower four after, so on every SIMD one wave's MFMA
+            // work meets the other's VALU work.
+            if (dequant_first && tile + 1 < n_tiles)
+                dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes,
+                                lds + ((tile + 1) & 1) * kLdsBuf, wave, lane);
+            if (key0 <= wave_last) {
+                s_product(lk);
+                softmax_step(key0);
+                pv_product(lk + kLdsK);
             }
-            // lane holds S[query i][key0 + 32*st + 8*(r/4) + 4*g + r%4] in s[st][r]
-            const bool need_mask = key0 + kKT - 1 > (causal ? pos_first : n_kv - 1) ||
-                                   key0 + kKT > n_kv;
-            if (need_mask) {
-                // last visible key of this lane's query, relative to the tile, in [-1, 64]
-                int64_t lim = (causal && pos_i < n_kv - 1 ? pos_i : n_kv - 1) - key0;
-                lim = lim < -1 ? -1 : (lim > kKT ? kKT : lim);
-                const int lim32 = (int)lim;
-#pragma unroll
-                for (int st = 0; st < 2; st++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        if (32 * st + 8 * (r >> 2) + 4 * g + (r & 3) > lim32)
-                            s[st][r] = -INFINITY;
-            }
-            float mt = -INFINITY;
-#pragma unroll
-            for (int st = 0; st < 2; st++)
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    mt = fmaxf(mt, s[st][r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float m_new = fmaxf(m, mt);
-            // every logit is scaled by c > 0, so the max commutes with the scaling.  The
-            // probabilities are exp2(s*c - mc) with mc = round(m*c), one rounding (an FMA): they
-            // are relative to the rounded reference, so the state carried from earlier tiles
-            // is rebased by exp2(round(m_old*c) - round(m_new*c)) -- exactly 1 when the max is
-            // unchanged.  Rebasing by exp2(m_old*c - round(m_new*c)) instead would be off by
-            // m_old*c's rounding error: a drift over thousands of tiles for ordinary logits,
-            // and factors of 2^4 and more for logits near 1e8.  Both products are kept whole
-            // (mul_rounded: no fused multiply-add).
-            const float mc = m_new == -INFINITY ? 0.f : mul_rounded(m_new, scale_log2);
-            const float alpha = m == -INFINITY ? 0.f
-                                : (m_new == m ? 1.f
-                                              : __builtin_amdgcn_exp2f(mul_rounded(m, scale_log2) - mc));
-            // probabilities packed in pairs: fp16; for bf16 caches two bf16 parts, pk + pl
-            uint32_t pk[2][8];
-            uint32_t pl[2][kBf ? 8 : 1];
-            float psum = 0.f;
-#pragma unroll
-            for (int st = 0; st < 2; st++) {
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st][r], scale_log2, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st][r + 1], scale_log2, -mc));
-                    psum += p0 + p1;
-                    if constexpr (kBf)
-                        bf16_split(p0, p1, pk[st][r >> 1], pl[st][r >> 1]);
-                    else
-                        pk[st][r >> 1] = __builtin_bit_cast(
-                            uint32_t, __builtin_convertvector(f32x2{p0, p1}, h2));
-                }
-            }
-            psum += __shfl_xor(psum, 32, 64);
-            l = l * alpha + psum;
-            m = m_new;
-            if (__any(alpha != 1.f)) {
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        o[dt][r] *= alpha;
-            }
-            // O^T[d][query] += V^T[d][keys] P^T[keys][query], 16 keys per step
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) {
-                const int st = ks >> 1, r0 = 4 * (ks & 1);
-                const f16x8 pb = __builtin_bit_cast(
-                    f16x8, u32x4{pk[st][r0], pk[st][r0 + 1], pk[st][r0 + 2], pk[st][r0 + 3]});
-#pragma unroll
-                for (int dt = 0; dt < 4; dt++) {
-                    // lane L receives V[16ks + 4g + e][32dt + L % 32], e = 0..3 (and keys + 8):
-                    // in its 16-lane group it reads 4 values of row 16ks + 4g + tr_r at column
-                    // 32dt + tr_c, and the read transposes them
-                    const unsigned char *vp = lv + (16 * ks + 4 * g + tr_r) * kVPitch +
-                                              2 * (32 * dt + tr_c);
-                    const f16x4 lo = tr_read(vp), hi = tr_read(vp + 8 * kVPitch);
-                    const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    if constexpr (kBf) {
-                        const f16x8 pbl = __builtin_bit_cast(
-                            f16x8, u32x4{pl[st][r0], pl[st][r0 + 1], pl[st][r0 + 2], pl[st][r0 + 3]});
-                        o[dt] = mfma32_bf16(a, pb, o[dt]);
-                        o[dt] = mfma32_bf16(a, pbl, o[dt]);
-                    } else {
-                        o[dt] = mfma32(a, pb, o[dt]);
-                    }
-                }
-            }
-        }
-        if constexpr (kDirect) {
-            // the loads of tile + 1 have had the whole tile; its buffer was last read for tile
-            // - 1, before the previous barrier
-            if (tile + 1 < n_tiles)
-                store_direct<F, WB>(lds + ((tile + 1) & 1) * kLdsBuf, rq);
-            __syncthreads();
-            if (tile + 2 < n_tiles)
-                load_raw<F, WB>(kh, vh, kt, vt, n_head, n_kv, row_bytes, tile + 2, rq);
-        } else {
             if (!dequant_first && tile + 1 < n_tiles)
                 dequant_tile<F>(lds_raw + ((tile + 1) & 1) * R::kBytes,
                                 lds + ((tile + 1) & 1) * kLdsBuf, wave, lane);
