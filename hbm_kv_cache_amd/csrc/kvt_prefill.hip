@@ -170,13 +170,18 @@ __device__ __forceinline__ void dequant_block(const uint32_t w[9], bool odd, uin
 // q8_0 rows -> fp16 rows ([row][head][d], 256 bytes a head): the values dequant_block gives
 // inside prefill_attn, so the fp16 kernel over converted rows computes what the q8_0 kernel
 // computes over the originals.  Each workgroup reads `rows_per_group` consecutive rows into LDS
-// with coalesced 8-byte loads, then each thread converts 34-byte blocks from there.
-__global__ __launch_bounds__(256) void q8_0_to_f16_rows(const unsigned char *__restrict__ src,
+// with coalesced 8-byte loads, then each thread converts 34-byte blocks from there.  blockIdx.y
+// picks the plane: (src0, dst0) or (src1, dst1).
+__global__ __launch_bounds__(256) void q8_0_to_f16_rows(const unsigned char *__restrict__ src0,
+                                                        const unsigned char *__restrict__ src1,
                                                         int64_t n_rows, int kvh,
                                                         int rows_per_group,
-                                                        unsigned char *__restrict__ dst)
+                                                        unsigned char *__restrict__ dst0,
+                                                        unsigned char *__restrict__ dst1)
 {
     extern __shared__ __align__(16) unsigned char conv_lds[];
+    const unsigned char *const src = blockIdx.y ? src1 : src0;
+    unsigned char *const dst = blockIdx.y ? dst1 : dst0;
     const int64_t row_bytes = (int64_t)kvh * (kHd / 32) * kBlk;
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_group;
     const int n = (int)(n_rows - r0 < rows_per_group ? n_rows - r0 : rows_per_group);
@@ -1073,17 +1078,20 @@ struct Conv {
     unsigned char *head_k = nullptr, *head_v = nullptr, *slot_k = nullptr, *slot_v = nullptr;
 };
 
-// rows [0, n) of q8_0 rows at src -> fp16 rows at dst, on stream s
-void convert_rows(const void *src, int64_t n, int kvh, void *dst, hipStream_t s)
+// rows [0, n) of two planes of q8_0 rows (src_k, src_v) -> fp16 rows (dst_k, dst_v), one
+// launch on stream s
+void convert_rows(const void *src_k, const void *src_v, int64_t n, int kvh, void *dst_k,
+                  void *dst_v, hipStream_t s)
 {
     if (n <= 0)
         return;
     const int64_t row_bytes = (int64_t)kvh * (kHd / 32) * kBlk;
     const int rpg = (int)std::max<int64_t>(1, std::min<int64_t>(64, 32768 / row_bytes));
-    hipLaunchKernelGGL(q8_0_to_f16_rows, dim3((unsigned)((n + rpg - 1) / rpg)), dim3(256),
+    hipLaunchKernelGGL(q8_0_to_f16_rows, dim3((unsigned)((n + rpg - 1) / rpg), 2), dim3(256),
                        (size_t)(rpg * row_bytes + 16), s,
-                       static_cast<const unsigned char *>(src), n, kvh, rpg,
-                       static_cast<unsigned char *>(dst));
+                       static_cast<const unsigned char *>(src_k),
+                       static_cast<const unsigned char *>(src_v), n, kvh, rpg,
+                       static_cast<unsigned char *>(dst_k), static_cast<unsigned char *>(dst_v));
 }
 
 bool ranges_overlap(uintptr_t a, uint64_t an, uintptr_t b, uint64_t bn)
@@ -1203,8 +1211,7 @@ int prefill_pipeline(const char *fn, const void *q, int64_t n_q, int64_t q_pos0,
     const int64_t row16 = (int64_t)kvh * kHd * 2;
     const void *ph_k = cv ? conv->head_k : k_head, *ph_v = cv ? conv->head_v : v_head;
     if (cv && n_head > 0) {
-        convert_rows(k_head, n_head, kvh, conv->head_k, s);
-        convert_rows(v_head, n_head, kvh, conv->head_v, s);
+        convert_rows(k_head, v_head, n_head, kvh, conv->head_k, conv->head_v, s);
         KVT_LAUNCHED("q8_0_to_f16_rows");
     }
     if (n_q > 0 && !host_rows) {   // nothing in host memory
@@ -1256,9 +1263,8 @@ int prefill_pipeline(const char *fn, const void *q, int64_t n_q, int64_t q_pos0,
                                      (uintptr_t)(slot * slot_keys * row16);
                 const uintptr_t cvv = reinterpret_cast<uintptr_t>(conv->slot_v) +
                                       (uintptr_t)(slot * slot_keys * row16);
-                convert_rows(reinterpret_cast<const void *>(sk), ke - r0, kvh,
-                             reinterpret_cast<void *>(ck), s);
-                convert_rows(reinterpret_cast<const void *>(sv), ke - r0, kvh,
+                convert_rows(reinterpret_cast<const void *>(sk), reinterpret_cast<const void *>(sv),
+                             ke - r0, kvh, reinterpret_cast<void *>(ck),
                              reinterpret_cast<void *>(cvv), s);
                 KVT_LAUNCHED("q8_0_to_f16_rows");
                 KVT_HIP(hipEventRecord(ev[3 + slot], s));
