@@ -190,20 +190,34 @@ __global__ __launch_bounds__(256) void q8_0_to_f16_rows(const unsigned char *__r
     for (int w = threadIdx.x; w < words; w += 256)
         reinterpret_cast<uint64_t *>(conv_lds)[w] = __builtin_nontemporal_load(s8 + w);
     __syncthreads();
-    const int per_row = kvh * (kHd / 32);
-    for (int b = threadIdx.x; b < n * per_row; b += 256) {
-        const int row = b / per_row, br = b - row * per_row;
-        const int off = (int)(row * row_bytes) + kBlk * br;   // head br / 4, block br % 4
+    // one 16-byte output chunk per thread and step, consecutive threads on consecutive chunks
+    // (coalesced stores): chunk c of a row is quarter c % 4 of block c / 4 (head c / 16), the
+    // block's values 8 * (c % 4) .. + 7, dequantised as dequant_block does
+    const int per_row = kvh * (kHd / 32) * 4;
+    unsigned char *const d0 = dst + r0 * (int64_t)kvh * kHd * 2;
+    for (int c = threadIdx.x; c < n * per_row; c += 256) {
+        const int row = c / per_row, cc = c - row * per_row;
+        const int br = cc >> 2, qt = cc & 3;
+        const int off = (int)(row * row_bytes) + kBlk * br;
         const uint32_t *w32 = reinterpret_cast<const uint32_t *>(conv_lds + (off & ~3));
-        uint32_t w[9], d[16];
+        const bool odd = (off & 2) != 0;
+        const uint32_t w0 = w32[0], wa = w32[2 * qt], wb = w32[2 * qt + 1], wc = w32[2 * qt + 2];
+        const uint16_t sbits = odd ? (uint16_t)(w0 >> 16) : (uint16_t)(w0 & 0xffff);
+        const _Float16 sc = __builtin_bit_cast(_Float16, sbits);
+        const h2 s2 = {sc, sc};
+        const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+        uint32_t o[4];
 #pragma unroll
-        for (int k = 0; k < 9; k++)
-            w[k] = w32[k];
-        dequant_block(w, (off & 2) != 0, d);
-        u32x4 *o = reinterpret_cast<u32x4 *>(dst + (r0 + row) * (int64_t)kvh * kHd * 2 + 64 * br);
-#pragma unroll
-        for (int c = 0; c < 4; c++)
-            o[c] = u32x4{d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]};
+        for (int k = 0; k < 2; k++) {
+            const uint32_t q = odd ? (k ? wc : wb)
+                                   : __builtin_amdgcn_alignbyte(k ? wc : wb, k ? wb : wa, 2);
+            const uint32_t u = q ^ 0x80808080u;
+            const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+            const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+            o[2 * k] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2, lo) - bias) * s2);
+            o[2 * k + 1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2, hi) - bias) * s2);
+        }
+        *reinterpret_cast<u32x4 *>(d0 + 16 * (int64_t)c) = u32x4{o[0], o[1], o[2], o[3]};
     }
 }
 
