@@ -770,6 +770,49 @@ def test_prefill_auto_plans_bit_identical(gpu, n_q, n_head, arena_rows, two_stre
     host.free()
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("kvh,n_head,arena_rows", [(1, 3000, 4096), (2, 2900, 1000),
+                                                   (4, 3003, 4096), (16, 1000, 2048)])
+def test_prefill_auto_conversion_other_head_counts(gpu, kvh, n_head, arena_rows):
+    """The pipelined plan with the q8_0 -> fp16 row conversion at 1, 2, 4 and 16 KV heads (rows
+    of 136 to 2176 bytes, so the conversion's rows per workgroup and 16-byte chunks per row
+    differ from the 8-head case), head and buckets of row counts that are not multiples of a
+    workgroup's rows: bit-identical to the split-K form over the all-HBM q8_0 cache."""
+    n_kv, n_q = 8192, 2048
+    n_qh = 4 * kvh
+    k, v = _cache(n_kv, kvh, 9000 + kvh)
+    row = k.shape[1]
+    q_np = synth.f16_normal(synth.rng(5, synth.P_Q, 9000 + kvh), (n_q, n_qh, 128))
+    q_pos0 = n_kv - n_q
+    kd, vd = _dev(k, gpu), _dev(v, gpu)
+    ref, _ = _splitk(q_np, q_pos0, kvh, kd, vd, n_kv, None, None, n_kv, 1, gpu)
+    assert kvt.kvt_attn_prefill_plan(n_q, q_pos0, n_qh, kvh, n_head, n_kv, kvt.Q8_0, 1,
+                                     arena_rows, 1) == kvt.PREFILL_PIPELINED
+    n_tail = n_kv - n_head
+    host = kvt.HostBuffer(2 * n_tail * row)
+    ht = host.numpy(np.uint8, (2, n_tail, row))
+    ht[0], ht[1] = k[n_head:], v[n_head:]
+    del ht
+    q = torch.from_numpy(q_np.view(np.int16)).to(gpu)
+    wb = kvt.kvt_attn_prefill_auto_ws_bytes(n_q, n_qh, kvh, n_kv)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device=gpu)
+    arena = torch.full((2, arena_rows, row), 0xA5, dtype=torch.uint8, device=gpu)
+    cb = kvt.kvt_attn_prefill_conv_bytes(n_head, kvh, arena_rows, kvt.Q8_0)
+    assert cb > 0
+    conv = torch.full((cb,), 0x5A, dtype=torch.uint8, device=gpu)
+    out = torch.full((n_q, n_qh, 128), float("nan"), dtype=torch.float32, device=gpu)
+    plan = kvt.kvt_attn_prefill_auto(q, n_q, q_pos0, n_qh, kvh, 128, kd, vd, n_head, host.dev,
+                                     host.dev + n_tail * row, n_kv, kvt.Q8_0, 1,
+                                     1 / math.sqrt(128), arena[0], arena[1], arena_rows, ws, wb,
+                                     out, copy_stream=torch.cuda.Stream(), conv=conv,
+                                     conv_bytes=cb)
+    torch.cuda.synchronize()
+    assert plan == kvt.PREFILL_PIPELINED
+    assert not bool(torch.all(conv == 0x5A))   # the conversion ran
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    host.free()
+
+
 def test_prefill_auto_staged_decode_token_matches_oracle(gpu):
     """The staged plan for one decode token, against the fp64 oracle, and the argument checks
     (workspace too small)."""
