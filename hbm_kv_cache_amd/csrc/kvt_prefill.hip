@@ -1376,13 +1376,13 @@ namespace {
 
 // The auto plan's time model: the host link at the rate contiguous staging copies reach on
 // MI355X (56 GB/s), and the prefill kernel's attention rate per cache format when its
-// workgroups fill the chip (measured over a 180,000-key cache: q8_0 0.80, fp16 0.73, bf16 0.50
+// workgroups fill the chip (measured over a 180,000-key cache: q8_0 0.85, fp16 0.98, bf16 0.61
 // PFLOP/s).
 constexpr double kLinkBytesPerUs = 56.0e3;
 
 double attn_flop_per_us(int32_t fmt)
 {
-    return fmt == KVT_Q8_0 ? 8.0e8 : fmt == KVT_F16 ? 7.3e8 : 5.0e8;
+    return fmt == KVT_Q8_0 ? 8.5e8 : fmt == KVT_F16 ? 9.8e8 : 6.1e8;
 }
 
 // (query, key) pairs the attention visits: row t sees min(n_kv, q_pos0 + t + 1) keys when
@@ -1485,7 +1485,7 @@ extern "C" int kvt_attn_prefill_auto(const void *q, int64_t n_q, int64_t q_pos0,
     if (p == KVT_PREFILL_PIPELINED) {   // in key splits when the chunk is short
         // q8_0: convert every row to fp16 once (the head here, each bucket as it lands) and
         // run the passes on the fp16 kernel -- when the buffer is given and the attention is
-        // long enough to repay the conversion (the fp16 kernel is ~9% faster; the conversion
+        // long enough to repay the conversion (the fp16 kernel is ~13% faster; the conversion
         // moves the cache's bytes once more at ~4 TB/s)
         Conv cvb;
         const size_t need = kvt_attn_prefill_conv_bytes(n_head, kvh, arena_rows, kv_format);
@@ -1494,7 +1494,7 @@ extern "C" int kvt_attn_prefill_auto(const void *q, int64_t n_q, int64_t q_pos0,
             const double conv_us = (double)n_kv * 2.0 * (row_bytes + kvh * kHd * 2) / 4.0e6;
             const double attn_us = 4.0 * kHd * n_qh * key_pairs(n_q, q_pos0, n_kv, causal) /
                                    attn_flop_per_us(kv_format);
-            if (0.09 * attn_us > conv_us) {
+            if (0.13 * attn_us > conv_us) {
                 const int64_t slot_keys = arena_rows / 2 / kKT * kKT;
                 const int64_t row16 = (int64_t)kvh * kHd * 2;
                 unsigned char *c = static_cast<unsigned char *>(conv);

@@ -491,8 +491,8 @@ int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0, int32_t n
  * of the modelled staging time (too short to hide much), else PIPELINED.  With one stream:
  * STAGED when arena_rows >= n_kv - n_head and the modelled attention time is below the
  * modelled staging time, else IN_PLACE.  The model: staging
- * 2*(n_kv - n_head)*row_bytes at 56 GB/s; attention 4*hd*n_qh*pairs flop at 0.80 (q8_0), 0.73
- * (fp16) or 0.50 (bf16) PFLOP/s, pairs being the (query, key) pairs visited (causal: row t
+ * 2*(n_kv - n_head)*row_bytes at 56 GB/s; attention 4*hd*n_qh*pairs flop at 0.85 (q8_0), 0.98
+ * (fp16) or 0.61 (bf16) PFLOP/s, pairs being the (query, key) pairs visited (causal: row t
  * sees min(n_kv, q_pos0 + t + 1) keys).  Every plan runs the attention in the key splits
  * kvt_attn_prefill_splitk takes for (n_q, n_qh, kvh, n_kv) -- s of them, one when the chunk's
  * own workgroups fill the chip; the pipelined plan carries each split's state from bucket to
@@ -508,7 +508,7 @@ int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0, int32_t n
  *          the cache is q8_0).  Given that, a q8_0 cache on the pipelined plan has its rows
  *          converted to fp16 once -- the head at the start, each bucket as it lands in the
  *          arena -- and every pass runs on fp16 rows, when the modelled attention is long
- *          enough for the faster fp16 passes to repay the conversion (about 11 times the
+ *          enough for the faster fp16 passes to repay the conversion (about 7.7 times the
  *          time the conversion moves the cache's bytes at 4 TB/s).  The fp16 values are the
  *          ones the q8_0 kernel dequantises to, so the output is the same either way.
  * Output: kvt_attn_prefill_splitk's bits (kvt_attn_prefill's when s == 1), whichever plan is
