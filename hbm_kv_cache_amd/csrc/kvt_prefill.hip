@@ -269,28 +269,6 @@ __device__ __forceinline__ void store_raw(unsigned char *rawbuf,
     }
 }
 
-// fp16 and bf16 tiles need no conversion: word f (plane, key, WB-byte column) goes straight to
-// its place in the 16-bit tile, K rows kKPitch and V rows kVPitch bytes apart.
-template <int F, int WB>
-__device__ __forceinline__ void store_direct(unsigned char *buf,
-                                             const typename Words<F, WB>::Word (&rq)[Words<F, WB>::kPerThread])
-{
-    using R = Raw<F>;
-    using W = Words<F, WB>;
-    constexpr int kPerRow = R::kHeadBytes / WB;
-#pragma unroll
-    for (int u = 0; u < W::kPerThread; u++) {
-        const int f = threadIdx.x + u * kThreads;
-        if (f < W::kWords) {
-            const int plane = f >= W::kWords / 2;
-            const int rem = f - plane * (W::kWords / 2);
-            const int key = rem / kPerRow, w = rem - key * kPerRow;
-            unsigned char *dst = buf + (plane ? kLdsK + key * kVPitch : key * kKPitch) + WB * w;
-            *reinterpret_cast<typename W::Word *>(dst) = rq[u];
-        }
-    }
-}
-
 // One plane (0: K, 1: V) of tile `tile` by the 256 threads of one wave group (gi = thread index
 // in the group): the same coalesced WB-byte words as load_raw, consecutive threads on
 // consecutive words of a head slice.  p_head / p_tail point at this workgroup's head slice.
@@ -361,38 +339,25 @@ __device__ __forceinline__ void store_plane(unsigned char *buf, int plane, int g
     }
 }
 
-// Thread (plane = wave / 4, block = wave % 4, key = lane) turns its 32 values of the raw tile
-// into the 16-bit tile used by the MFMA: K and V both as rows [key][d].  q8_0: the block's
-// dequantisation to fp16; fp16 and bf16: the values as stored (bf16 tiles go to the bf16 MFMA,
-// with the query and the probabilities each split into two bf16 parts).
+// Thread (plane = wave / 4, block = wave % 4, key = lane) turns its 32 values of the raw q8_0
+// tile into the fp16 tile used by the MFMA: the block's dequantisation, K and V both as rows
+// [key][d].  (fp16 and bf16 tiles are stored from the load registers as they are.)
 template <int F>
 __device__ __forceinline__ void dequant_tile(const unsigned char *rawbuf, unsigned char *buf,
                                              int wave, int lane)
 {
+    static_assert(F == KVT_Q8_0, "only q8_0 tiles go through a raw buffer");
     using R = Raw<F>;
     const bool is_v = wave >= 4;
     const int blk = wave & 3;
     uint32_t d[16];
-    if constexpr (F == KVT_Q8_0) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(
-            rawbuf + (is_v ? R::kPlane : 0) + lane * R::kHeadBytes + 4 * ((kBlk * blk) >> 2));
-        uint32_t w[9];
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(
+        rawbuf + (is_v ? R::kPlane : 0) + lane * R::kHeadBytes + 4 * ((kBlk * blk) >> 2));
+    uint32_t w[9];
 #pragma unroll
-        for (int k = 0; k < 9; k++)
-            w[k] = src[k];
-        dequant_block(w, blk & 1, d);
-    } else {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(
-            rawbuf + (is_v ? R::kPlane : 0) + lane * R::kHeadBytes + blk * 64);
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const u32x4 x = src[c];
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-                d[4 * c + e] = x[e];
-        }
-
-    }
+    for (int k = 0; k < 9; k++)
+        w[k] = src[k];
+    dequant_block(w, blk & 1, d);
     unsigned char *dst = buf + (is_v ? kLdsK + lane * kVPitch : lane * kKPitch) + blk * 64;
 #pragma unroll
     for (int c = 0; c < 4; c++)
