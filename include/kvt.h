@@ -507,9 +507,8 @@ int kvt_attn_prefill_chain(const void *q, int64_t n_q, int64_t q_pos0, int32_t n
  *          kvt_attn_prefill_conv_bytes(n_head, kvh, arena_rows, kv_format) bytes (0 unless
  *          the cache is q8_0).  Given that, a q8_0 cache on the pipelined plan has its rows
  *          converted to fp16 once -- the head at the start, each bucket as it lands in the
- *          arena -- and every pass runs on fp16 rows, when the modelled attention is long
- *          enough for the faster fp16 passes to repay the conversion (about 7.7 times the
- *          time the conversion moves the cache's bytes at 4 TB/s).  The fp16 values are the
+ *          arena -- and every pass runs on fp16 rows, when the modelled attention outlasts
+ *          the conversion (the time it moves the cache's bytes at 4 TB/s).  The fp16 values are the
  *          ones the q8_0 kernel dequantises to, so the output is the same either way.
  * Output: kvt_attn_prefill_splitk's bits (kvt_attn_prefill's when s == 1), whichever plan is
  * taken and however the rows are split between head and tail.  A PIPELINED plan carries

@@ -852,7 +852,7 @@ def test_prefill_auto_staged_decode_token_matches_oracle(gpu):
 def test_prefill_auto_full_geometry(gpu, n_q):
     """The auto plan over the 180,000-token tiered q8_0 cache (94,208 rows in HBM, the tail in
     host memory) with two streams and a 2 x 16,384-row arena -- pipelined in 32, 4 and 1 key
-    splits, the last on rows converted to fp16 -- equals the split-K form over the all-HBM
+    splits, the last two on rows converted to fp16 -- equals the split-K form over the all-HBM
     cache bit for bit; its last query row is within 2e-3 of the fp64 oracle."""
     n_kv, n_head, n_qh, kvh = C5_NKV, C5_NHEAD, C5_NQH, C5_KVH
     k, v = _full_cache()
